@@ -1,0 +1,465 @@
+"""Plain fp64 CPU oracle of the looped Recurrent Block forward.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It
+shares no code with the HIP path and the HIP path never calls it.
+
+It computes the block step by step in the order the pages give, in float64,
+with NumPy's matmul as the only library primitive and explicit decisions.
+Where floating point decides an integer (the router's top-k, the ACT halting
+test) the decision is taken in float32, the precision the kernels decide in.
+
+Pages cited (title, then section):
+  [ZS] "OpenMythos 분석: Mythos Preview의 장기 추론 성능과 OpenMythos의 계산 모델링"
+       (zero.shotlearni.ng)
+  [RC] "OpenMythos" (runchr.com, Korean copy of the project README)
+
+Readings of what the pages leave open (listed again in the design doc):
+  * h0 = e: the recurrent stage receives the prelude output both as its state
+    and as the frozen anchor ([ZS §Core Structure]).
+  * loop-index embedding: frequencies theta^(-2j/loop_dim) for
+    j < loop_dim/2, sin half then cos half, added to the first loop_dim
+    channels of h only; t counts from 0 ([ZS §Repeating the parameter
+    reduces expressiveness]).
+  * pre-norm block: x1 = c + Attn(RMSNorm(c)), tau = x1 + MoE(RMSNorm(x1)).
+  * RMSNorm y = x / sqrt(mean(x^2) + eps) * g.
+  * RoPE: adjacent channel pairs rotated as complex numbers by p * theta_i,
+    theta_i = base^(-2i/rot_dim), p = start_pos + i ([ZS §RoPE & generation
+    cache]).
+  * attention: no biases; scale 1/sqrt(d_qk); query head h reads KV head
+    floor(h / (H / Hkv)); causal on absolute positions.
+  * MLA (DeepSeek-V2 form): RMSNorm on the q and kv latents, per-head
+    [nope | rope] for q and k, [nope | v] for the kv up-projection, one
+    shared rotated k_rope for all heads; cache = (c_kv before its norm,
+    k_rope after RoPE).
+  * router: no bias on the linear map; softmax over all experts; top-k on
+    logits + router_bias, descending, ties to the lower expert index; gates
+    from the unbiased softmax renormalised over the k chosen ([ZS §MoE]).
+  * dropless routing; SwiGLU experts without biases; shared experts have the
+    routed experts' width and are added with weight 1.
+  * depth-wise LoRA acts on the block output with scale row min(t, L-1).
+  * A and B are diagonal; rho(A) = max_i A_i.
+  * ACT: cum starts at 0; a running position halts at the first loop where
+    cum + p >= threshold, or at the last loop, and takes the remainder
+    1 - cum as its weight there; every position keeps running the block
+    after it halts (halting only zeroes its weight); threshold 0 = ACT off,
+    output = final h.
+"""
+
+import math
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# dtype helpers
+# --------------------------------------------------------------------------
+
+def as_f64(x):
+    """Exact upcast: uint16 arrays are bfloat16 bit patterns."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+class Params:
+    """Block parameters as float64, upcast on first use.
+
+    ``arrays`` maps names to numpy arrays (bf16 bit patterns or floats).
+    Stacked expert tensors may instead come from ``expert_loader(name, e)``,
+    so the largest configs never hold every expert in float64 at once.
+    """
+
+    def __init__(self, arrays, expert_loader=None):
+        self.arrays = arrays
+        self.expert_loader = expert_loader
+        self._cache = {}
+
+    def __getitem__(self, name):
+        if name not in self._cache:
+            self._cache[name] = as_f64(self.arrays[name])
+        return self._cache[name]
+
+    def expert(self, name, e):
+        if name in self.arrays:
+            return as_f64(self.arrays[name][e])
+        return as_f64(self.expert_loader(name, e))
+
+
+# --------------------------------------------------------------------------
+# single steps
+# --------------------------------------------------------------------------
+
+def loop_index_embedding(t, loop_dim, dim, theta):
+    """Signal of the loop index t on the first ``loop_dim`` channels.
+
+    [ZS §Repeating the parameter reduces expressiveness]: angles t*freq, the
+    sines then the cosines, written into the leading channels and zero
+    elsewhere.  Frequencies follow the sinusoidal rule of RoPE, as the
+    loop-index hypothesis of [RC] calls it RoPE-like.
+    """
+    half = loop_dim // 2
+    freqs = np.array([theta ** (-2.0 * j / loop_dim) for j in range(half)], dtype=np.float64)
+    angles = float(t) * freqs
+    emb = np.zeros(dim, dtype=np.float64)
+    emb[:half] = np.sin(angles)
+    emb[half:loop_dim] = np.cos(angles)
+    return emb
+
+
+def rms_norm(x, g, eps):
+    """Root-mean-square normalisation over the last axis, then the gain."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def rope_cos_sin(positions, rot_dim, theta):
+    """cos/sin of p * theta^(-2i/rot_dim) for each position p and pair i."""
+    i = np.arange(rot_dim // 2, dtype=np.float64)
+    inv = theta ** (-2.0 * i / rot_dim)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def apply_rope(x, cos, sin):
+    """Rotate adjacent channel pairs (2i, 2i+1) as the complex number
+    x[2i] + j x[2i+1] times exp(j * angle) ([ZS §RoPE & generation cache]).
+
+    x: [..., P, rot_dim]; cos, sin: [P, rot_dim/2].
+    """
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * cos - x1 * sin
+    out[..., 1::2] = x0 * sin + x1 * cos
+    return out
+
+
+def attend(q, k, v, q_pos, k_pos, scale):
+    """Explicit causal softmax attention for one head.
+
+    q [Tq, d], k [Tk, d], v [Tk, dv]; key j is visible to query i when
+    k_pos[j] <= q_pos[i].
+    """
+    s = (q @ k.T) * scale
+    visible = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
+    s = np.where(visible, s, -np.inf)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return p @ v
+
+
+def gqa_attention(cfg, P, a, start_pos, cache, rows):
+    """Grouped-query attention with RoPE, output projection included.
+
+    [RC §Attention 구현]: fewer KV heads than query heads, RoPE applied to q
+    and k before they are cached.  ``a`` is [B, T, D]; ``rows`` lists the
+    (b, i) query rows to produce.  ``cache`` (or None) is a dict with 'k',
+    'v' arrays [B, Hkv, capacity, dh] that this call fills at positions
+    start_pos .. start_pos+T-1 and then reads from position 0.
+    """
+    B, T, D = a.shape
+    H, G, dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    pos = start_pos + np.arange(T)
+    cos, sin = rope_cos_sin(pos, dh, cfg["rope_theta"])
+    k = (a @ P["wk"].T).reshape(B, T, G, dh).transpose(0, 2, 1, 3)
+    v = (a @ P["wv"].T).reshape(B, T, G, dh).transpose(0, 2, 1, 3)
+    k = apply_rope(k, cos, sin)
+    if cache is not None:
+        cache["k"][:, :, start_pos:start_pos + T] = k
+        cache["v"][:, :, start_pos:start_pos + T] = v
+        kk, vv = cache["k"], cache["v"]
+        k_pos = np.arange(start_pos + T)
+    else:
+        kk, vv = k, v
+        k_pos = pos
+    rep = H // G
+    out = {}
+    by_b = {}
+    for (b, i) in rows:
+        by_b.setdefault(b, []).append(i)
+    for b, idx in by_b.items():
+        idx = np.asarray(idx)
+        q = (a[b, idx] @ P["wq"].T).reshape(len(idx), H, dh)
+        q = np.stack([apply_rope(q[:, h], cos[idx], sin[idx]) for h in range(H)], axis=1)
+        o = np.empty((len(idx), H, dh))
+        for h in range(H):
+            g = h // rep
+            o[:, h] = attend(q[:, h], as_f64(kk[b, g, :len(k_pos)]), as_f64(vv[b, g, :len(k_pos)]),
+                             pos[idx], k_pos, 1.0 / math.sqrt(dh))
+        y = o.reshape(len(idx), H * dh) @ P["wo"].T
+        for n, i in enumerate(idx):
+            out[(b, i)] = y[n]
+    return out
+
+
+def mla_attention(cfg, P, a, start_pos, cache, rows):
+    """Multi-latent attention (DeepSeek-V2 form) with RoPE on the rope part.
+
+    [ZS §MLA]: the kv down-projection splits into the latent c_kv
+    (kv_lora_rank wide) and one k_rope shared by all heads, which is
+    rotated; c_kv and k_rope are what the cache holds; k_nope and v are
+    rebuilt from c_kv.  Queries go through the q latent (q_lora_rank).
+    """
+    B, T, D = a.shape
+    H = cfg["n_heads"]
+    kvl, rope, nope, vd = cfg["kv_lora_rank"], cfg["qk_rope_head_dim"], cfg["qk_nope_head_dim"], cfg["v_head_dim"]
+    eps = cfg["norm_eps"]
+    pos = start_pos + np.arange(T)
+    cos, sin = rope_cos_sin(pos, rope, cfg["rope_theta"])
+    kv_raw = a @ P["wdkv"].T                       # [B, T, kvl + rope]
+    c_kv = kv_raw[..., :kvl]
+    k_rope = apply_rope(kv_raw[..., kvl:], cos, sin)
+    if cache is not None:
+        cache["c_kv"][:, start_pos:start_pos + T] = c_kv
+        cache["k_rope"][:, start_pos:start_pos + T] = k_rope
+        all_ckv = as_f64(cache["c_kv"][:, :start_pos + T])
+        all_kr = as_f64(cache["k_rope"][:, :start_pos + T])
+        k_pos = np.arange(start_pos + T)
+    else:
+        all_ckv, all_kr, k_pos = c_kv, k_rope, pos
+    kv = (rms_norm(all_ckv, P["gkv"], eps) @ P["wukv"].T).reshape(B, len(k_pos), H, nope + vd)
+    out = {}
+    by_b = {}
+    for (b, i) in rows:
+        by_b.setdefault(b, []).append(i)
+    for b, idx in by_b.items():
+        idx = np.asarray(idx)
+        c_q = rms_norm(a[b, idx] @ P["wdq"].T, P["gq"], eps)
+        q = (c_q @ P["wuq"].T).reshape(len(idx), H, nope + rope)
+        o = np.empty((len(idx), H, vd))
+        for h in range(H):
+            qh = np.concatenate([q[:, h, :nope], apply_rope(q[:, h, nope:], cos[idx], sin[idx])], axis=-1)
+            kh = np.concatenate([kv[b, :, h, :nope], all_kr[b]], axis=-1)
+            o[:, h] = attend(qh, kh, kv[b, :, h, nope:], pos[idx], k_pos, 1.0 / math.sqrt(nope + rope))
+        y = o.reshape(len(idx), H * vd) @ P["wo"].T
+        for n, i in enumerate(idx):
+            out[(b, i)] = y[n]
+    return out
+
+
+def topk_desc_lowest_index(values, k):
+    """Indices of the k largest entries per row, largest first, equal values
+    ordered by ascending index (a stable sort of the negated values)."""
+    return np.argsort(-values, axis=-1, kind="stable")[:, :k]
+
+
+def router(cfg, P, f):
+    """Top-k softmax router with a selection-only bias ([ZS §MoE]).
+
+    Returns logits z (float64), the chosen experts, their renormalised
+    gates, and the float64 margin between the k-th and (k+1)-th biased
+    logit.  The choice itself is made on float32 logits + float32 bias, as
+    the kernel makes it.
+    """
+    k = cfg["top_k"]
+    z = f @ P["router_w"].T                                   # [n, E]
+    s = np.exp(z - z.max(axis=-1, keepdims=True))
+    s = s / s.sum(axis=-1, keepdims=True)
+    bias32 = np.asarray(P.arrays["router_bias"], dtype=np.float32)
+    biased32 = (z.astype(np.float32) + bias32).astype(np.float32)
+    sel = topk_desc_lowest_index(biased32, k)
+    gate = np.take_along_axis(s, sel, axis=-1)
+    gate = gate / gate.sum(axis=-1, keepdims=True)
+    b64 = z + bias32.astype(np.float64)
+    srt = -np.sort(-b64, axis=-1)
+    margin = srt[:, k - 1] - srt[:, k] if k < b64.shape[1] else np.full(len(z), np.inf)
+    return z, sel, gate, margin
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def swiglu(x, wg, wu, wd):
+    """Expert feed-forward: down( silu(gate x) * (up x) ), no biases."""
+    return (silu(x @ wg.T) * (x @ wu.T)) @ wd.T
+
+
+def moe_ffn(cfg, P, f, sel, gate):
+    """Routed experts weighted by their gates, plus the shared experts.
+
+    f [n, D]; sel, gate [n, k].  Each routed expert runs on exactly the rows
+    that chose it (dropless); shared experts run on every row.
+    """
+    n, D = f.shape
+    y = np.zeros((n, D))
+    for e in range(cfg["n_experts"]):
+        hit = np.nonzero(sel == e)
+        if len(hit[0]) == 0:
+            continue
+        r, j = hit
+        out = swiglu(f[r], P.expert("w_gate", e), P.expert("w_up", e), P.expert("w_down", e))
+        y[r] += gate[r, j][:, None] * out
+    for s in range(cfg["n_shared_experts"]):
+        y += swiglu(f, P.expert("s_gate", s), P.expert("s_up", s), P.expert("s_down", s))
+    return y
+
+
+def depthwise_lora(cfg, P, x, t):
+    """Loop-dependent low-rank term: (down(x) * scale[t']) @ B_lora, with the
+    scale row t' = min(t, max_loop_iters-1) ([ZS §Repeating the parameter
+    reduces expressiveness])."""
+    ti = min(t, cfg["max_loop_iters"] - 1)
+    return ((x @ P["lora_down"].T) * P["lora_scale"][ti]) @ P["lora_B"]
+
+
+def lti_A(P):
+    """Diagonal of A = exp(-exp(clamp(log_dt + log_A, -20, 20))), every entry
+    in (0, 1) ([ZS §latent reasoning]; [RC §해결책])."""
+    return np.exp(-np.exp(np.clip(P["log_dt"][0] + P["log_A"], -20.0, 20.0)))
+
+
+def lti_injection(P, h, e, trans_out):
+    """h_next = A*h + B*e + Transformer(h, e) ([RC §아키텍처])."""
+    return lti_A(P) * h + P["B"] * e + trans_out
+
+
+def halting_probability(P, h):
+    """p = sigmoid(h . w_halt + b_halt) per position ([ZS §ACT])."""
+    z = h @ P["halt_w"] + P["halt_b"][0]
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+# --------------------------------------------------------------------------
+# one loop and the full loop
+# --------------------------------------------------------------------------
+
+def run_loop(cfg, P, h, e, t, start_pos=0, cache=None, rows=None, route_hook=None):
+    """One pass of the recurrent block at loop index t ([ZS §Recurrent Block]).
+
+    h, e: [B, T, D] float64.  Returns the new state for ``rows`` (all rows
+    when None) and the intermediates callers check.  ``route_hook(sel,
+    margin, rows)`` may return a replacement expert choice (used by the
+    tie-adoption protocol); the gates are then taken for that choice.
+    """
+    B, T, D = h.shape
+    eps = cfg["norm_eps"]
+    if rows is None:
+        rows = [(b, i) for b in range(B) for i in range(T)]
+    u = h + loop_index_embedding(t, cfg["loop_dim"], D, cfg["loop_theta"])
+    c = rms_norm(u + e, P["g_rec"], eps)
+    a = rms_norm(c, P["g_attn"], eps)
+    attn = gqa_attention if cfg["attn"] == "gqa" else mla_attention
+    o = attn(cfg, P, a, start_pos, cache, rows)
+    ridx = tuple(np.array(rows).T)
+    x1 = c[ridx] + np.stack([o[r] for r in rows])
+    f = rms_norm(x1, P["g_ffn"], eps)
+    z, sel, gate, margin = router(cfg, P, f)
+    if route_hook is not None:
+        new_sel = route_hook(sel, margin, rows)
+        if new_sel is not None and not np.array_equal(new_sel, sel):
+            sel = np.asarray(new_sel)
+            s = np.exp(z - z.max(axis=-1, keepdims=True))
+            s = s / s.sum(axis=-1, keepdims=True)
+            gate = np.take_along_axis(s, sel, axis=-1)
+            gate = gate / gate.sum(axis=-1, keepdims=True)
+    tau = x1 + moe_ffn(cfg, P, f, sel, gate)
+    tau = tau + depthwise_lora(cfg, P, tau, t)
+    h_new = lti_injection(P, h[ridx], e[ridx], tau)
+    return dict(h=h_new, rows=rows, sel=sel, gate=gate, margin=margin, z=z, f=f, x1=x1, c=c, a=a)
+
+
+def new_cache(cfg, batch, capacity, n_loops):
+    """Empty per-loop caches (float64), one per loop index."""
+    if cfg["attn"] == "gqa":
+        G, dh = cfg["n_kv_heads"], cfg["head_dim"]
+        return [dict(k=np.zeros((batch, G, capacity, dh)), v=np.zeros((batch, G, capacity, dh)))
+                for _ in range(n_loops)]
+    return [dict(c_kv=np.zeros((batch, capacity, cfg["kv_lora_rank"])),
+                 k_rope=np.zeros((batch, capacity, cfg["qk_rope_head_dim"])))
+            for _ in range(n_loops)]
+
+
+class Adoption:
+    """Decisions recorded by another implementation, taken where the
+    oracle's own decision is within rounding of a tie.
+
+    sel: [n_loops, N, k] chosen experts; halt_counts: [N] 1-based halting
+    loop.  A router choice is adopted where the oracle's top-k margin is
+    below eps_route; a halting decision where |cum + p - threshold| is
+    below eps_halt.  Everything else must agree, and is counted when not.
+    """
+
+    def __init__(self, sel=None, halt_counts=None, eps_route=0.0, eps_halt=0.0):
+        self.sel = sel
+        self.halt_counts = halt_counts
+        self.eps_route = eps_route
+        self.eps_halt = eps_halt
+        self.route_adopted = 0
+        self.route_disagree = 0
+        self.halt_adopted = 0
+        self.halt_disagree = 0
+
+
+def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=None,
+                      adopt=None, record=False):
+    """The looped Recurrent Block ([ZS §Recurrent Block]; [RC §아키텍처]).
+
+    e, h0: [B, T, D].  Returns dict(out=[B, T, D] float64, halt_counts=[B, T]
+    int, and per-loop records when ``record``).  With act_threshold == 0 the
+    output is the final state; otherwise the ACT-weighted sum of the states.
+    """
+    e = as_f64(e)
+    h = as_f64(h0)
+    B, T, D = h.shape
+    N = B * T
+    act = act_threshold > 0
+    thr32 = np.float32(act_threshold)
+    h_out = np.zeros_like(h)
+    cum = np.zeros(N)
+    cum32 = np.zeros(N, dtype=np.float32)
+    halted = np.zeros(N, dtype=bool)
+    counts = np.full(N, n_loops, dtype=np.int64)
+    rec = dict(h=[], sel=[], margin=[], p=[], weight=[])
+    for t in range(n_loops):
+        hook = None
+        if adopt is not None and adopt.sel is not None:
+            gpu = np.asarray(adopt.sel[t]).reshape(N, -1)
+
+            def hook(sel, margin, rows, gpu=gpu):
+                out = sel.copy()
+                for n in range(len(rows)):
+                    if not np.array_equal(sel[n], gpu[n]):
+                        if margin[n] < adopt.eps_route:
+                            out[n] = gpu[n]
+                            adopt.route_adopted += 1
+                        else:
+                            adopt.route_disagree += 1
+                return out
+        step = run_loop(cfg, P, h, e, t, start_pos, None if cache is None else cache[t], route_hook=hook)
+        h = step["h"].reshape(B, T, D)
+        if act:
+            p = halting_probability(P, h.reshape(N, D))
+            p32 = p.astype(np.float32)
+            running = ~halted
+            reach = (cum32 + p32).astype(np.float32) >= thr32
+            halt_now = running & (reach | (t == n_loops - 1))
+            if adopt is not None and adopt.halt_counts is not None:
+                gpu_halt = np.asarray(adopt.halt_counts).reshape(N) == t + 1
+                near = running & (np.abs((cum32 + p32).astype(np.float64) - float(thr32)) < adopt.eps_halt) \
+                    & (t != n_loops - 1)
+                diff = running & (gpu_halt != halt_now)
+                adopt.halt_adopted += int(np.sum(diff & near))
+                adopt.halt_disagree += int(np.sum(diff & ~near))
+                halt_now = np.where(near, gpu_halt & running, halt_now)
+            weight = np.where(halt_now, np.maximum(1.0 - cum, 0.0), p) * running
+            h_out += weight.reshape(B, T, 1) * h
+            cum = cum + p * running
+            cum32 = np.where(running, (cum32 + p32).astype(np.float32), cum32)
+            counts[halt_now] = t + 1
+            halted |= halt_now
+            if record:
+                rec["p"].append(p)
+                rec["weight"].append(weight)
+        if record:
+            rec["h"].append(h.copy())
+            rec["sel"].append(step["sel"].copy())
+            rec["margin"].append(step["margin"].copy())
+    out = h_out if act else h
+    res = dict(out=out, halt_counts=counts.reshape(B, T), state=h)
+    if record:
+        res["record"] = rec
+    return res

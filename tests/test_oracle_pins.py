@@ -1,0 +1,387 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Each test ties one oracle function to a closed form, an invariant the pages
+state, brute force on tiny inputs, or an independent library routine
+(PyTorch CPU: rms_norm, complex multiplication, scaled_dot_product_attention),
+so that a dropped term, a wrong sign or index, or a transposed operand in the
+oracle fails at least one of them.
+
+Pages: [ZS] "OpenMythos 분석: …의 계산 모델링" (zero.shotlearni.ng);
+[RC] "OpenMythos" (runchr.com).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import rdt_oracle as O
+from workloads import configs, generate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _setup(name, scales=None, **over):
+    cfg = configs.get(name, **over)
+    W = generate.make_weights(cfg, scales=scales)
+    e, h0 = generate.make_inputs(cfg)
+    return cfg, W, O.Params(W), e, h0
+
+
+# ---------------------------------------------------------------- injection
+
+def test_A_matches_zoh_discretisation_and_clamp():
+    """[RC §해결책]: A = exp(dt * A_c) with A_c = -exp(log_A), dt = exp(log_dt)
+    (zero-order hold of a negative diagonal); [ZS §latent reasoning] clamps
+    log_dt + log_A to [-20, 20].  Values from tests/golden/lti_A.json."""
+    gold = json.load(open(os.path.join(GOLDEN, "lti_A.json")))
+    for case in gold["cases"]:
+        P = O.Params({"log_A": np.array(case["log_A"]), "log_dt": np.array([case["log_dt"]])})
+        A = O.lti_A(P)
+        # inside the clamp: the ZOH form, written independently
+        for la, a in zip(case["log_A"], A):
+            s = case["log_dt"] + la
+            if -20 <= s <= 20:
+                ref = math.exp(math.exp(case["log_dt"]) * -math.exp(la))
+                assert a == pytest.approx(ref, rel=1e-14, abs=0)
+        np.testing.assert_allclose(A, case["expected"], rtol=1e-12, atol=0)
+
+
+def test_transformer_term_zero_gives_closed_form_lti():
+    """With the recurrent norm gain at 0 the block input is 0, so attention,
+    experts and LoRA all return 0 and the loop is the pure LTI recurrence
+    h_t = A^t h0 + (1 - A^t)/(1 - A) * B * e ([RC §동적 시스템 관점])."""
+    cfg, W, P, e, h0 = _setup("tiny_gqa")
+    W = dict(W)
+    W["g_rec"] = np.zeros_like(W["g_rec"])
+    P = O.Params(W)
+    A = O.lti_A(P)
+    Bv = O.as_f64(W["B"])
+    e64, h64 = e.astype(np.float64), h0.astype(np.float64) * 0.5 + 0.3   # h0 != e on purpose
+    for n in (1, 3, 6):
+        r = O.recurrent_forward(cfg, P, e64, h64, n, 0.0)
+        ref = A ** n * h64 + (1 - A ** n) / (1 - A) * Bv * e64
+        np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_lti_fixed_point_after_5000_loops():
+    """rho(A) < 1 makes h converge to (I - A)^-1 B e for any start."""
+    cfg, W, P, e, h0 = _setup("tiny_gqa")
+    e64 = e.astype(np.float64)
+    h = np.full_like(e64, 7.0)
+    for _ in range(5000):
+        h = O.lti_injection(P, h, e64, 0.0)
+    fixed = O.as_f64(W["B"]) * e64 / (1.0 - O.lti_A(P))
+    np.testing.assert_allclose(h, fixed, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", ["tiny_gqa", "tiny_mla", "small_bf16", "mythos_1b", "mythos_3b", "mythos_10b_decode"])
+def test_spectral_radius_below_one(name):
+    """[RC §사용법] checks rho(A) < 1; A diagonal so rho = max A_i.  Also in
+    fp32, where exp(-exp(x)) rounds to 1 for x below about -17."""
+    cfg = configs.get(name)
+    W = generate.make_weights(cfg, names={"log_A", "log_dt"})
+    A = O.lti_A(O.Params(W))
+    assert A.max() < 1.0 and A.min() > 0.0
+    assert np.float32(A.max()) <= np.float32(1.0 - 2.0 ** -24)
+
+
+# ---------------------------------------------------------------- loop index
+
+def test_loop_index_embedding_closed_form():
+    """[ZS §Repeating the parameter reduces expressiveness]: sin then cos of
+    t * freq on the leading channels, zero elsewhere."""
+    emb0 = O.loop_index_embedding(0, 8, 16, 10000.0)
+    np.testing.assert_array_equal(emb0, [0, 0, 0, 0, 1, 1, 1, 1] + [0] * 8)
+    emb = O.loop_index_embedding(3, 8, 16, 10000.0)
+    freqs = [1.0, 0.1, 0.01, 0.001]          # 10000^(-2j/8)
+    np.testing.assert_allclose(emb[:4], [math.sin(3 * f) for f in freqs], rtol=1e-15, atol=1e-16)
+    np.testing.assert_allclose(emb[4:8], [math.cos(3 * f) for f in freqs], rtol=1e-15)
+    assert np.all(emb[8:] == 0)
+    pairs = emb[:4] ** 2 + emb[4:8] ** 2
+    np.testing.assert_allclose(pairs, 1.0, rtol=1e-15)
+
+
+# ---------------------------------------------------------------- norms, rope
+
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 64))
+    g = rng.standard_normal(64)
+    ref = F.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rms_norm(x, g, 1e-6), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_rope_matches_complex_rotation_and_is_relative():
+    """[ZS §RoPE & generation cache]: adjacent pairs are complex numbers
+    rotated by position.  Checked against torch complex arithmetic, norm
+    preservation, and q_m . k_n depending only on m - n."""
+    rng = np.random.default_rng(1)
+    d, theta = 16, 10000.0
+    x = rng.standard_normal((7, d))
+    pos = np.arange(3, 10)
+    cos, sin = O.rope_cos_sin(pos, d, theta)
+    got = O.apply_rope(x, cos, sin)
+    xc = torch.view_as_complex(torch.from_numpy(x).reshape(7, d // 2, 2).contiguous())
+    inv = theta ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
+    ph = torch.polar(torch.ones(7, d // 2, dtype=torch.float64), torch.from_numpy(pos).double()[:, None] * inv)
+    ref = torch.view_as_real(xc * ph).reshape(7, d).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(np.linalg.norm(got, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    def score(m, n):
+        cm, sm = O.rope_cos_sin([m], d, theta)
+        cn, sn = O.rope_cos_sin([n], d, theta)
+        return O.apply_rope(q[None], cm, sm)[0] @ O.apply_rope(k[None], cn, sn)[0]
+    assert score(9, 4) == pytest.approx(score(105, 100), rel=1e-10)
+    assert score(9, 4) != pytest.approx(score(9, 5), rel=1e-3)
+
+
+# ---------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("H,G", [(8, 2), (4, 4), (6, 3)])
+def test_attention_matches_sdpa(H, G):
+    """Oracle causal attention with GQA head mapping == torch SDPA
+    (enable_gqa); H == G is plain multi-head attention."""
+    rng = np.random.default_rng(H * 10 + G)
+    T, d = 11, 16
+    q = rng.standard_normal((H, T, d))
+    k = rng.standard_normal((G, T, d))
+    v = rng.standard_normal((G, T, d))
+    pos = np.arange(T)
+    got = np.stack([O.attend(q[h], k[h // (H // G)], v[h // (H // G)], pos, pos, 1 / math.sqrt(d)) for h in range(H)])
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q)[None], torch.from_numpy(k)[None],
+                                         torch.from_numpy(v)[None], is_causal=True, enable_gqa=True)[0].numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- router / MoE
+
+def test_topk_matches_brute_force_sort():
+    rng = np.random.default_rng(2)
+    v = rng.integers(0, 4, size=(50, 9)).astype(np.float32)   # many exact ties
+    got = O.topk_desc_lowest_index(v, 3)
+    for n in range(50):
+        ref = sorted(range(9), key=lambda j: (-v[n, j], j))[:3]
+        assert list(got[n]) == ref
+
+
+def test_router_gates_use_unbiased_scores():
+    """[ZS §MoE]: the bias steers selection only; gates come from the
+    unbiased softmax renormalised over the chosen experts."""
+    cfg, W, P, e, h0 = _setup("tiny_gqa")
+    rng = np.random.default_rng(3)
+    f = rng.standard_normal((20, cfg["dim"]))
+    W2 = dict(W)
+    bias = np.zeros(cfg["n_experts"], dtype=np.float32)
+    bias[5] = 1e3
+    W2["router_bias"] = bias
+    z, sel, gate, _ = O.router(cfg, O.Params(W2), f)
+    assert np.all(sel[:, 0] == 5)
+    s = np.exp(z) / np.exp(z).sum(1, keepdims=True)
+    np.testing.assert_allclose(s.sum(1), 1.0, rtol=1e-14)
+    for n in range(20):
+        ref = s[n, sel[n]] / s[n, sel[n]].sum()
+        np.testing.assert_allclose(gate[n], ref, rtol=1e-14)
+    np.testing.assert_allclose(gate.sum(1), 1.0, rtol=1e-14)
+
+
+def test_moe_equals_dense_masked_sum():
+    """Top-k MoE == every expert on every row, weighted by a gate matrix that
+    is zero outside the chosen set (brute force), plus the shared expert."""
+    cfg, W, P, e, h0 = _setup("tiny_gqa", n_shared_experts=2)
+    rng = np.random.default_rng(4)
+    f = rng.standard_normal((24, cfg["dim"]))
+    z, sel, gate, _ = O.router(cfg, P, f)
+    got = O.moe_ffn(cfg, P, f, sel, gate)
+    ft = torch.from_numpy(f)
+    def expert(wg, wu, wd):
+        return F.linear(F.silu(F.linear(ft, torch.from_numpy(O.as_f64(wg)))) * F.linear(ft, torch.from_numpy(O.as_f64(wu))),
+                        torch.from_numpy(O.as_f64(wd)))
+    dense = torch.stack([expert(W["w_gate"][x], W["w_up"][x], W["w_down"][x]) for x in range(cfg["n_experts"])], 1)
+    mask = torch.zeros(24, cfg["n_experts"], dtype=torch.float64)
+    for n in range(24):
+        for j in range(cfg["top_k"]):
+            mask[n, sel[n, j]] += gate[n, j]
+    ref = (dense * mask[:, :, None]).sum(1)
+    for s_ in range(2):
+        ref = ref + expert(W["s_gate"][s_], W["s_up"][s_], W["s_down"][s_])
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-11, atol=1e-14)
+
+
+# ---------------------------------------------------------------- LoRA
+
+def test_depthwise_lora_closed_form_and_clamp():
+    """With basis-vector down/B rows the LoRA term is x_j * scale[t', j] on the
+    first r channels; t' = min(t, L - 1) ([ZS §Repeating the parameter
+    reduces expressiveness]); scale 0 is a no-op."""
+    D, r, L = 12, 3, 4
+    cfg = dict(max_loop_iters=L)
+    eye = np.eye(r, D)
+    scale = np.arange(1, L * r + 1, dtype=np.float64).reshape(L, r)
+    P = O.Params({"lora_down": eye, "lora_B": eye * 2.0, "lora_scale": scale})
+    x = np.random.default_rng(5).standard_normal((4, D))
+    for t in range(7):
+        ti = min(t, L - 1)
+        ref = np.zeros_like(x)
+        ref[:, :r] = x[:, :r] * scale[ti] * 2.0
+        np.testing.assert_allclose(O.depthwise_lora(cfg, P, x, t), ref, rtol=1e-15)
+    P0 = O.Params({"lora_down": eye, "lora_B": eye, "lora_scale": np.zeros((L, r))})
+    assert np.all(O.depthwise_lora(cfg, P0, x, 2) == 0)
+
+
+# ---------------------------------------------------------------- ACT
+
+@pytest.mark.parametrize("name", ["tiny_gqa", "tiny_mla", "small_f32"])
+def test_act_weights_sum_to_one_and_first_crossing(name):
+    """Halting weights sum to 1 per position; the halt count is the first
+    loop where the float32 running sum of p reaches the threshold (or the
+    last loop), recomputed by brute force from the recorded p; and halting
+    leaves the h trajectory unchanged (it only weights the output)."""
+    scales = {"halt_w": 0.05, "halt_b": -0.8}
+    cfg, W, P, e, h0 = _setup(name, scales=scales)
+    n = cfg["n_loops"]
+    on = O.recurrent_forward(cfg, P, e, h0, n, cfg["act_threshold"], record=True)
+    off = O.recurrent_forward(cfg, P, e, h0, n, 0.0, record=True)
+    wsum = np.sum(on["record"]["weight"], axis=0)
+    np.testing.assert_allclose(wsum, 1.0, rtol=0, atol=1e-12)
+    for a, b in zip(on["record"]["h"], off["record"]["h"]):
+        np.testing.assert_array_equal(a, b)
+    ps = np.array(on["record"]["p"])              # [loops, N]
+    thr = np.float32(cfg["act_threshold"])
+    counts = on["halt_counts"].ravel()
+    for pos in range(ps.shape[1]):
+        cum = np.float32(0)
+        want = n
+        for t in range(n):
+            if np.float32(cum + np.float32(ps[t, pos])) >= thr:
+                want = t + 1
+                break
+            cum = np.float32(cum + np.float32(ps[t, pos]))
+        assert counts[pos] == want
+    assert len(np.unique(counts)) > 1, "halting is not spread; the pin would be weak"
+    # the output is the weighted sum of the recorded states
+    ref = sum(w.reshape(e.shape[0], e.shape[1], 1) * h for w, h in zip(on["record"]["weight"], on["record"]["h"]))
+    np.testing.assert_allclose(on["out"], ref, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- whole block
+
+def _torch_one_loop(cfg, W, h, e, t, start_pos=0):
+    """One loop written independently with torch CPU library routines:
+    F.rms_norm, complex-number RoPE, SDPA with GQA, a dense masked MoE."""
+    T64 = lambda a: torch.from_numpy(O.as_f64(a))
+    h, e = torch.from_numpy(h), torch.from_numpy(e)
+    B, T, D = h.shape
+    eps = cfg["norm_eps"]
+    half = cfg["loop_dim"] // 2
+    fr = cfg["loop_theta"] ** (-torch.arange(0, cfg["loop_dim"], 2, dtype=torch.float64) / cfg["loop_dim"])
+    emb = torch.zeros(D, dtype=torch.float64)
+    emb[:half], emb[half:2 * half] = torch.sin(t * fr), torch.cos(t * fr)
+    c = F.rms_norm(h + emb + e, (D,), T64(W["g_rec"]), eps)
+    a = F.rms_norm(c, (D,), T64(W["g_attn"]), eps)
+
+    def rot(x, d):                                 # x [B, T, heads, d]
+        inv = cfg["rope_theta"] ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
+        ang = (start_pos + torch.arange(T, dtype=torch.float64))[:, None] * inv
+        xc = torch.view_as_complex(x.reshape(*x.shape[:-1], d // 2, 2).contiguous())
+        return torch.view_as_real(xc * torch.polar(torch.ones_like(ang), ang)[None, :, None]).reshape(x.shape)
+
+    H = cfg["n_heads"]
+    if cfg["attn"] == "gqa":
+        G, dh = cfg["n_kv_heads"], cfg["head_dim"]
+        q = rot(F.linear(a, T64(W["wq"])).reshape(B, T, H, dh), dh).transpose(1, 2)
+        k = rot(F.linear(a, T64(W["wk"])).reshape(B, T, G, dh), dh).transpose(1, 2)
+        v = F.linear(a, T64(W["wv"])).reshape(B, T, G, dh).transpose(1, 2)
+        o = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+    else:
+        kvl, rp, nope, vd = cfg["kv_lora_rank"], cfg["qk_rope_head_dim"], cfg["qk_nope_head_dim"], cfg["v_head_dim"]
+        cq = F.rms_norm(F.linear(a, T64(W["wdq"])), (cfg["q_lora_rank"],), T64(W["gq"]), eps)
+        q = F.linear(cq, T64(W["wuq"])).reshape(B, T, H, nope + rp)
+        q = torch.cat([q[..., :nope], rot(q[..., nope:], rp)], -1)
+        raw = F.linear(a, T64(W["wdkv"]))
+        kr = rot(raw[..., kvl:].reshape(B, T, 1, rp), rp).expand(B, T, H, rp)
+        kv = F.linear(F.rms_norm(raw[..., :kvl], (kvl,), T64(W["gkv"]), eps), T64(W["wukv"])).reshape(B, T, H, nope + vd)
+        k = torch.cat([kv[..., :nope], kr], -1)
+        v = kv[..., nope:]
+        o = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), is_causal=True)
+    x1 = c + F.linear(o.transpose(1, 2).reshape(B, T, -1), T64(W["wo"]))
+    f = F.rms_norm(x1, (D,), T64(W["g_ffn"]), eps).reshape(B * T, D)
+    z = F.linear(f, T64(W["router_w"]))
+    s = torch.softmax(z, -1)
+    sel = torch.topk(z + T64(W["router_bias"]), cfg["top_k"], -1).indices
+    g = torch.gather(s, 1, sel)
+    g = g / g.sum(-1, keepdim=True)
+    mask = torch.zeros_like(s).scatter_add_(1, sel, g)
+
+    def ex(wg, wu, wd, x):
+        return F.linear(F.silu(F.linear(x, T64(wg))) * F.linear(x, T64(wu)), T64(wd))
+    y = sum(mask[:, x_:x_ + 1] * ex(W["w_gate"][x_], W["w_up"][x_], W["w_down"][x_], f) for x_ in range(cfg["n_experts"]))
+    y = y + sum(ex(W["s_gate"][s_], W["s_up"][s_], W["s_down"][s_], f) for s_ in range(cfg["n_shared_experts"]))
+    tau = x1.reshape(B * T, D) + y
+    ti = min(t, cfg["max_loop_iters"] - 1)
+    tau = tau + (F.linear(tau, T64(W["lora_down"])) * T64(W["lora_scale"])[ti]) @ T64(W["lora_B"])
+    A = torch.exp(-torch.exp(torch.clamp(T64(W["log_dt"]) + T64(W["log_A"]), -20, 20)))
+    return (A * h.reshape(B * T, D) + T64(W["B"]) * e.reshape(B * T, D) + tau).reshape(B, T, D).numpy()
+
+
+BIG = {"lora_scale": 1.0, "lora_B": 0.3, "wo": 0.1, "w_down": 0.1, "s_down": 0.1}
+
+
+@pytest.mark.parametrize("name", ["tiny_gqa", "tiny_mla", "small_f32", "small_bf16_k3"])
+def test_single_loop_matches_independent_torch_block(name):
+    """n_loops = 1 equals one application of the block, written independently
+    with library routines (north star special case).  Larger LoRA / output
+    scales keep every term visible above the tolerance."""
+    cfg, W, P, e, h0 = _setup(name, scales=BIG)
+    e64 = e.astype(np.float64)
+    h = e64 * 0.7 + 0.1
+    got = O.recurrent_forward(cfg, P, e64, h, 1, 0.0)["out"]
+    ref = _torch_one_loop(cfg, W, h, e64, 0)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+    # a later loop index exercises the loop embedding and LoRA clamp
+    t = cfg["max_loop_iters"] + 1
+    got5 = O.run_loop(cfg, P, h, e64, t)["h"].reshape(h.shape)
+    np.testing.assert_allclose(got5, _torch_one_loop(cfg, W, h, e64, t), rtol=1e-10, atol=1e-11)
+
+
+def test_n_loops_is_repeated_single_loop():
+    cfg, W, P, e, h0 = _setup("tiny_gqa")
+    e64 = e.astype(np.float64)
+    h = e64.copy()
+    for t in range(3):
+        h = O.run_loop(cfg, P, h, e64, t)["h"].reshape(h.shape)
+    np.testing.assert_array_equal(O.recurrent_forward(cfg, P, e64, e64, 3, 0.0)["out"], h)
+
+
+@pytest.mark.parametrize("name", ["tiny_gqa", "tiny_mla"])
+def test_decode_equals_last_row_of_prefill(name):
+    """[ZS §RoPE & generation cache]: with the per-loop caches of a prefill of
+    positions 0..P-1, a one-token step at start_pos P gives the row P of a
+    prefill of 0..P, in every loop (attention is causal in every loop)."""
+    cfg, W, P, e, h0 = _setup(name, scales=BIG)
+    B, T = e.shape[:2]
+    n = 3
+    full = O.recurrent_forward(cfg, P, e, h0, n, 0.0)["out"]
+    cache = O.new_cache(cfg, B, T, n)
+    O.recurrent_forward(cfg, P, e[:, :T - 1], h0[:, :T - 1], n, 0.0, start_pos=0, cache=cache)
+    step = O.recurrent_forward(cfg, P, e[:, T - 1:], h0[:, T - 1:], n, 0.0, start_pos=T - 1, cache=cache)["out"]
+    np.testing.assert_allclose(step[:, 0], full[:, T - 1], rtol=1e-11, atol=1e-12)
+
+
+def test_row_subset_equals_full_loop():
+    """The sampled-row mode used at full sizes returns exactly the rows of
+    the all-rows pass (attention still reads every earlier position)."""
+    cfg, W, P, e, h0 = _setup("small_f32")
+    e64 = e.astype(np.float64)
+    full = O.run_loop(cfg, P, e64, e64, 2)
+    rows = [(0, 0), (0, 149), (1, 77), (1, 3)]
+    part = O.run_loop(cfg, P, e64, e64, 2, rows=rows)
+    T = e.shape[1]
+    idx = [b * T + i for b, i in rows]
+    np.testing.assert_allclose(part["h"], full["h"][idx], rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(part["sel"], full["sel"][idx])
