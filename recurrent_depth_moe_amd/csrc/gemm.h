@@ -1,0 +1,62 @@
+// Grouped GEMM C[m, n] = sum_k A[row(m), k] * W[group(m)][n, k] with fused
+// epilogues, for every matrix product of the recurrent block.
+#pragma once
+
+#include "common.h"
+
+enum EpiKind {
+  EPI_STORE = 0,   // out[m, n] = acc                         (type TO)
+  EPI_RESID = 1,   // out[m, n] = resid[m, n] + acc           (fp32)
+  EPI_QKV = 2,     // RoPE on q and k, scatter to q / K / V^T (type TO)
+  EPI_SWIGLU = 3,  // dual B: out[m, n] = silu(acc0) * acc1   (type TO)
+  EPI_MLA_Q = 4,   // MLA query: RoPE on the rope part of each head
+  EPI_MLA_KV = 5,  // MLA kv up-projection: k_nope -> K, v -> V^T
+};
+
+struct EpiParams {
+  void* out;
+  int64_t ldo;
+  const float* resid;
+  void* q;
+  void* k;
+  void* vt;
+  int T;      // rows per sequence (query rows, or key rows for EPI_MLA_KV)
+  int H, G;   // query heads, kv heads
+  int dq;     // q/k head width (GQA: head_dim; MLA: nope + rope)
+  int dv;     // v head width
+  int nope;   // MLA: width of the no-RoPE part
+  int cap;    // K / V^T buffer capacity (positions per (b, head))
+  int kbase;  // buffer index of this call's first position
+  int start_pos;
+  const float* rcos;  // RoPE tables [position][rot_half]
+  const float* rsin;
+  int rot_half;
+};
+
+struct GemmParams {
+  const void* A;
+  int64_t lda;
+  const int32_t* a_rows;   // logical row -> row of A (null: identity)
+  const void* W0;
+  const void* W1;          // second B matrix for EPI_SWIGLU
+  int64_t w_stride;        // elements between consecutive groups of W
+  int M, N, K;
+  // grouped schedule (routed experts), all device arrays; null = one group
+  const int32_t* mt_start;   // [E+1] first m-tile of each group
+  const int32_t* tile_row0;  // [m-tiles] first logical row of the m-tile
+  const int32_t* tile_grp;   // [m-tiles] group of the m-tile
+  const int32_t* grp_end;    // [E+1] offsets: rows of group e are [grp_end[e], grp_end[e+1])
+  int n_groups;
+  int dense_gm;              // dense raster: m-tiles per group of the tile order
+  EpiParams epi;
+};
+
+// Launch helpers (stream-ordered, no sync).  `bm` selects the m-tile height
+// that the grouped schedule was built for.
+void launch_gemm_bf16(const GemmParams& p, int epi, bool dual, int bm, int out_is_bf16, int n_cu, hipStream_t s);
+void launch_gemm_f32(const GemmParams& p, int epi, bool dual, int n_cu, hipStream_t s);
+
+// m-tile heights the kernels are built with (the dispatch builds schedules
+// for exactly these)
+#define RDT_BM_LARGE 128
+#define RDT_BM_F32 64

@@ -1,0 +1,69 @@
+// Row-wise (HBM-bound) kernels of the recurrent block and the router/dispatch.
+#pragma once
+
+#include "common.h"
+
+#define RDT_DISP_TILE 256
+#define RDT_MAX_EXPERTS 512
+#define RDT_MAX_LORA 32
+
+// tables: RoPE cos/sin [max_seq][rot/2] for each rotary width, loop-index
+// embedding [n_loops_max][loop_dim], A [D]
+void launch_make_tables(float* rope_cos, float* rope_sin, int max_seq, int rot_dim, double theta, hipStream_t s);
+void launch_make_loop_table(float* emb, int n_loops_max, int loop_dim, double theta, hipStream_t s);
+void launch_make_A(const float* log_A, const float* log_dt, float* A, int D, hipStream_t s);
+
+// c = RMSNorm(h + emb_t + e) * g_rec (fp32); a = RMSNorm(c) * g_attn (bf16 or fp32)
+void launch_loop_head(int act_bf16, const float* h, const float* e, const float* emb_t, int loop_dim,
+                      const float* g_rec, const float* g_attn, float eps, float* c, void* a, int N, int D,
+                      hipStream_t s);
+// out[r] = RMSNorm(x[r]) * g for rows r < rows; x fp32 with row stride ldx,
+// out (bf16 or fp32) with stride ldo
+void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, float eps, void* out, int64_t ldo,
+                    int rows, int D, hipStream_t s);
+
+// softmax over E logits, top-k of logits + bias (descending, ties to the
+// lower index), gates renormalised over the chosen experts
+void launch_router_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* sel, float* gate,
+                        int32_t* cap_sel, hipStream_t s);
+// dropless dispatch: stable order (token, slot) inside each expert
+void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,
+                     int32_t* mt_start, int32_t* tile_row0, int32_t* tile_grp, int32_t* perm_src, int32_t* inv,
+                     hipStream_t s);
+
+struct TailArgs {
+  const float* x1;        // [N][D]
+  const float* y;         // routed expert outputs in dispatch order [NK][D]
+  const int32_t* inv;     // [N*k] slot -> dispatch row
+  const float* gate;      // [N*k]
+  const float* y_s;       // shared expert outputs [S][N][D]
+  int S;
+  const void* lora_down;  // [r][D] weight dtype
+  const void* lora_B;     // [r][D]
+  const float* lora_scale_row;  // [r] row min(t, L-1)
+  int r;
+  const float* A;         // [D]
+  const float* Bv;        // [D]
+  const float* e;         // [N][D]
+  const float* h_prev;    // [N][D]
+  float* h_next;          // [N][D]
+  const float* halt_w;    // [D]
+  const float* halt_b;    // [1]
+  float act_threshold;    // 0 = off
+  float* h_out;           // [N][D]
+  float* cum;             // [N]
+  int32_t* halt_counts;   // [N]
+  int t, n_loops, N, D, k;
+  float* cap_h;           // [N][D] slice of loop t, or null
+  float* cap_p;           // [N] slice of loop t, or null
+  int w_bf16;
+};
+void launch_loop_tail(const TailArgs& a, hipStream_t s);
+
+// MLA glue (see attention.hip for buffer layouts)
+void launch_mla_latent(int act_bf16, const float* kv_raw, const float* cq_raw, const float* gq, float eps, int N,
+                       int T, int ql, int kvl, int rope, int start_pos, const float* rcos, const float* rsin,
+                       void* cq_norm, void* lat_ckv, void* lat_krope, int lat_cap, int kbase, hipStream_t s);
+void launch_mla_kv_prep(int act_bf16, const void* lat_ckv, const void* lat_krope, int lat_cap, const float* gkv,
+                        float eps, int B, int kvlen, int kvl, int rope, int H, int dq, void* ckv_norm, void* K,
+                        hipStream_t s);

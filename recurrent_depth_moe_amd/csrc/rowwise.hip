@@ -1,0 +1,566 @@
+// Row-wise kernels of the recurrent block: tables, loop head (loop-index
+// embedding + re-injection + two RMSNorms), RMSNorm, router top-k, dropless
+// dispatch, loop tail (combine + depth-wise LoRA + LTI injection + ACT) and
+// the MLA latent glue.  All are HBM-bound: one block streams one row with
+// 16-byte accesses and keeps it in registers between its passes.
+//
+// Pages: [ZS] "OpenMythos 분석: …의 계산 모델링" (zero.shotlearni.ng);
+//        [RC] "OpenMythos" (runchr.com).
+#include "rowwise.h"
+
+namespace {
+
+constexpr int RB = 256;   // threads per row block
+constexpr int MAXV4 = 8;  // float4 per thread: D <= 8192
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 ld4(const bf16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ void st4(float* p, float4 v) { *(float4*)p = v; }
+__device__ __forceinline__ void st4(bf16_t* p, float4 v) {
+  uint2 u;
+  u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+  u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+  *(uint2*)p = u;
+}
+__device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+__device__ __forceinline__ float4 fma4(float s, float4 a, float4 b) {
+  return make_float4(fmaf(s, a.x, b.x), fmaf(s, a.y, b.y), fmaf(s, a.z, b.z), fmaf(s, a.w, b.w));
+}
+
+// ------------------------------------------------------------ tables
+
+__global__ void make_rope_kernel(float* c, float* s, int max_seq, int half, int rot, double theta) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= max_seq * half) return;
+  const int p = idx / half, i = idx - p * half;
+  const double ang = (double)p * pow(theta, -2.0 * i / rot);
+  c[idx] = (float)cos(ang);
+  s[idx] = (float)sin(ang);
+}
+
+// loop-index signal: sin(t w_j) on channel j, cos(t w_j) on channel half + j,
+// w_j = theta^(-2j/loop_dim) ([ZS §Repeating the parameter reduces
+// expressiveness]: sin and cos halves on the leading channels)
+__global__ void make_loop_kernel(float* emb, int n_loops, int loop_dim, double theta) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_loops * loop_dim) return;
+  const int t = idx / loop_dim, d = idx - t * loop_dim, half = loop_dim / 2;
+  const int j = d < half ? d : d - half;
+  const double ang = (double)t * pow(theta, -2.0 * j / loop_dim);
+  emb[idx] = (float)(d < half ? sin(ang) : cos(ang));
+}
+
+// A = exp(-exp(clamp(log_dt + log_A, -20, 20))) ([ZS §latent reasoning])
+__global__ void make_A_kernel(const float* log_A, const float* log_dt, float* A, int D) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= D) return;
+  double x = (double)log_dt[0] + (double)log_A[d];
+  x = x < -20.0 ? -20.0 : (x > 20.0 ? 20.0 : x);
+  A[d] = (float)exp(-exp(x));
+}
+
+// ------------------------------------------------------------ loop head
+
+template <typename TA>
+__global__ __launch_bounds__(RB) void loop_head_kernel(const float* __restrict__ h, const float* __restrict__ e,
+                                                       const float* __restrict__ emb, int loop_dim,
+                                                       const float* __restrict__ g_rec,
+                                                       const float* __restrict__ g_attn, float eps,
+                                                       float* __restrict__ c, TA* __restrict__ a, int D) {
+  __shared__ float red[RB / 64];
+  const int64_t base = (int64_t)blockIdx.x * D;
+  const int D4 = D >> 2;
+  float4 v[MAXV4];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (i4 < D4) {
+      const int d = i4 * 4;
+      float4 x = ld4(h + base + d);
+      const float4 y = ld4(e + base + d);
+      if (d < loop_dim) {
+        const float4 m = ld4(emb + d);
+        x.x += m.x; x.y += m.y; x.z += m.z; x.w += m.w;
+      }
+      x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      v[j] = x;
+      ss += dot4(x, x);
+    }
+  }
+  const float r1 = 1.0f / sqrtf(block_sum(ss, red) / D + eps);
+  ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (i4 < D4) {
+      const int d = i4 * 4;
+      const float4 g = ld4(g_rec + d);
+      float4 x = v[j];
+      x = make_float4(x.x * r1 * g.x, x.y * r1 * g.y, x.z * r1 * g.z, x.w * r1 * g.w);
+      st4(c + base + d, x);
+      v[j] = x;
+      ss += dot4(x, x);
+    }
+  }
+  const float r2 = 1.0f / sqrtf(block_sum(ss, red) / D + eps);
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (i4 < D4) {
+      const int d = i4 * 4;
+      const float4 g = ld4(g_attn + d);
+      const float4 x = v[j];
+      st4(a + base + d, make_float4(x.x * r2 * g.x, x.y * r2 * g.y, x.z * r2 * g.z, x.w * r2 * g.w));
+    }
+  }
+}
+
+template <typename TO>
+__global__ __launch_bounds__(RB) void rmsnorm_kernel(const float* __restrict__ x, int64_t ldx,
+                                                     const float* __restrict__ g, float eps, TO* __restrict__ out,
+                                                     int64_t ldo, int D) {
+  __shared__ float red[RB / 64];
+  const float* xr = x + (int64_t)blockIdx.x * ldx;
+  TO* orow = out + (int64_t)blockIdx.x * ldo;
+  const int D4 = D >> 2;
+  float4 v[MAXV4];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (i4 < D4) {
+      v[j] = ld4(xr + i4 * 4);
+      ss += dot4(v[j], v[j]);
+    }
+  }
+  const float r = 1.0f / sqrtf(block_sum(ss, red) / D + eps);
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (i4 < D4) {
+      const float4 gg = ld4(g + i4 * 4);
+      const float4 y = v[j];
+      st4(orow + i4 * 4, make_float4(y.x * r * gg.x, y.y * r * gg.y, y.z * r * gg.z, y.w * r * gg.w));
+    }
+  }
+}
+
+// ------------------------------------------------------------ router
+// One wave per token.  [ZS §MoE]: softmax scores over all experts; top-k
+// taken on logits + router_bias; gates = chosen scores renormalised.
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          const float* __restrict__ bias, int N, int E, int k,
+                                                          int32_t* __restrict__ sel, float* __restrict__ gate,
+                                                          int32_t* __restrict__ cap_sel) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const float* z = logits + (int64_t)row * E;
+  float zv[4], bv[4];
+  unsigned taken = 0;
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ex = lane + 64 * j;
+    if (ex < E) {
+      zv[j] = z[ex];
+      const float b = zv[j] + bias[ex];
+      bv[j] = (b != b) ? -INFINITY : b;
+      m = fmaxf(m, zv[j]);
+    } else {
+      zv[j] = 0.f;
+      bv[j] = -INFINITY;
+      taken |= 1u << j;
+    }
+  }
+  m = wave_max(m);
+  float num[8];
+  int idx[8];
+  float den = 0.f;
+  for (int kk = 0; kk < k; ++kk) {
+    float best = -INFINITY, bz = 0.f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ex = lane + 64 * j;
+      if (!((taken >> j) & 1u) && (bv[j] > best || (bv[j] == best && ex < bi))) {
+        best = bv[j];
+        bi = ex;
+        bz = zv[j];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ob = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      const float oz = __shfl_xor(bz, o, 64);
+      if (ob > best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+        bz = oz;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    num[kk] = expf(bz - m);
+    idx[kk] = bi;
+    den += num[kk];
+  }
+  if (lane == 0) {
+    for (int kk = 0; kk < k; ++kk) {
+      sel[(int64_t)row * k + kk] = idx[kk];
+      gate[(int64_t)row * k + kk] = num[kk] / den;
+      if (cap_sel) cap_sel[(int64_t)row * k + kk] = idx[kk];
+    }
+  }
+}
+
+// ------------------------------------------------------------ dispatch
+// counts per expert for each tile of 256 (token, slot) assignments
+__global__ __launch_bounds__(RDT_DISP_TILE) void dispatch_count_kernel(const int32_t* __restrict__ sel, int NK,
+                                                                       int E, int32_t* __restrict__ tile_counts) {
+  __shared__ int cnt[RDT_MAX_EXPERTS];
+  for (int i = threadIdx.x; i < E; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int a = blockIdx.x * RDT_DISP_TILE + threadIdx.x;
+  if (a < NK) atomicAdd(&cnt[sel[a]], 1);
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += blockDim.x) tile_counts[(int64_t)blockIdx.x * E + i] = cnt[i];
+}
+
+// per expert: exclusive scan over tiles (tile base), totals -> offsets,
+// m-tile schedule of height bm
+__global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t* __restrict__ tile_counts,
+                                                                        int ntiles, int E, int bm,
+                                                                        int32_t* __restrict__ offsets,
+                                                                        int32_t* __restrict__ mt_start,
+                                                                        int32_t* __restrict__ tile_row0,
+                                                                        int32_t* __restrict__ tile_grp) {
+  __shared__ int tot[RDT_MAX_EXPERTS];
+  __shared__ int off[RDT_MAX_EXPERTS + 1];
+  __shared__ int mts[RDT_MAX_EXPERTS + 1];
+  const int ex = threadIdx.x;
+  if (ex < E) {
+    int run = 0;
+    for (int t = 0; t < ntiles; ++t) {
+      const int c = tile_counts[(int64_t)t * E + ex];
+      tile_counts[(int64_t)t * E + ex] = run;
+      run += c;
+    }
+    tot[ex] = run;
+  }
+  __syncthreads();
+  if (ex == 0) {
+    int o = 0, m = 0;
+    for (int i = 0; i < E; ++i) {
+      off[i] = o;
+      mts[i] = m;
+      o += tot[i];
+      m += (tot[i] + bm - 1) / bm;
+    }
+    off[E] = o;
+    mts[E] = m;
+  }
+  __syncthreads();
+  if (ex <= E) {
+    offsets[ex] = off[ex];
+    mt_start[ex] = mts[ex];
+  }
+  if (ex < E) {
+    for (int t = 0; t < ntiles; ++t) tile_counts[(int64_t)t * E + ex] += off[ex];
+    const int nt = mts[ex + 1] - mts[ex];
+    for (int i = 0; i < nt; ++i) {
+      tile_grp[mts[ex] + i] = ex;
+      tile_row0[mts[ex] + i] = off[ex] + i * bm;
+    }
+  }
+}
+
+// rank of each assignment among equal experts inside its tile, in
+// (token, slot) order; destination = tile base + rank
+__global__ __launch_bounds__(RDT_DISP_TILE) void dispatch_scatter_kernel(const int32_t* __restrict__ sel, int NK,
+                                                                         int k, int E,
+                                                                         const int32_t* __restrict__ tile_base,
+                                                                         int32_t* __restrict__ perm_src,
+                                                                         int32_t* __restrict__ inv) {
+  __shared__ int wcnt[RDT_DISP_TILE / 64][RDT_MAX_EXPERTS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < (RDT_DISP_TILE / 64) * RDT_MAX_EXPERTS; i += blockDim.x) (&wcnt[0][0])[i] = 0;
+  const int a = blockIdx.x * RDT_DISP_TILE + threadIdx.x;
+  const bool valid = a < NK;
+  const int ex = valid ? sel[a] : 0;
+  uint64_t same = __ballot(valid);
+  for (int bit = 0; (1 << bit) < E; ++bit) {
+    const bool on = (ex >> bit) & 1;
+    const uint64_t bal = __ballot(on);
+    same &= on ? bal : ~bal;
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(same & lt);
+  __syncthreads();
+  if (valid && (same >> lane) == 1ull) wcnt[w][ex] = __popcll(same);
+  __syncthreads();
+  if (valid) {
+    int r = rank;
+    for (int ww = 0; ww < w; ++ww) r += wcnt[ww][ex];
+    const int dest = tile_base[(int64_t)blockIdx.x * E + ex] + r;
+    perm_src[dest] = a / k;
+    inv[a] = dest;
+  }
+}
+
+// ------------------------------------------------------------ loop tail
+// tau = x1 + sum_j gate_j y_j + sum_s y_s; tau += ((tau Wd^T) * scale_t) B;
+// h = A h + B e + tau ([RC §아키텍처]); p = sigmoid(h . w + b) and the ACT
+// update ([ZS §ACT], [ZS §Recurrent Block]).
+template <typename TW>
+__global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
+  __shared__ float red[RDT_MAX_LORA + 1][RB / 64];
+  const int n = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int D = a.D, D4 = D >> 2;
+  const int64_t base = (int64_t)n * D;
+  const TW* Wd = (const TW*)a.lora_down;
+  const TW* Wb = (const TW*)a.lora_B;
+
+  int drow[8];
+  float gw[8];
+  for (int j = 0; j < a.k; ++j) {
+    drow[j] = a.inv[(int64_t)n * a.k + j];
+    gw[j] = a.gate[(int64_t)n * a.k + j];
+  }
+  float4 tau[MAXV4];
+  float part[RDT_MAX_LORA];
+#pragma unroll
+  for (int r = 0; r < RDT_MAX_LORA; ++r) part[r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (i4 < D4) {
+      const int d = i4 * 4;
+      float4 x = ld4(a.x1 + base + d);
+      for (int s = 0; s < a.k; ++s) x = fma4(gw[s], ld4(a.y + (int64_t)drow[s] * D + d), x);
+      for (int s = 0; s < a.S; ++s) {
+        const float4 ys = ld4(a.y_s + (int64_t)s * a.N * D + base + d);
+        x.x += ys.x; x.y += ys.y; x.z += ys.z; x.w += ys.w;
+      }
+      tau[j] = x;
+#pragma unroll
+      for (int r = 0; r < RDT_MAX_LORA; ++r)
+        if (r < a.r) part[r] += dot4(x, ld4(Wd + (int64_t)r * D + d));
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RDT_MAX_LORA; ++r)
+    if (r < a.r) {
+      const float v = wave_sum(part[r]);
+      if (lane == 0) red[r][w] = v;
+    }
+  __syncthreads();
+  float lo[RDT_MAX_LORA];
+#pragma unroll
+  for (int r = 0; r < RDT_MAX_LORA; ++r) {
+    lo[r] = 0.f;
+    if (r < a.r) {
+      float v = 0.f;
+      for (int ww = 0; ww < RB / 64; ++ww) v += red[r][ww];
+      lo[r] = v * a.lora_scale_row[r];
+    }
+  }
+  float zs = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (i4 < D4) {
+      const int d = i4 * 4;
+      float4 x = tau[j];
+#pragma unroll
+      for (int r = 0; r < RDT_MAX_LORA; ++r)
+        if (r < a.r) x = fma4(lo[r], ld4(Wb + (int64_t)r * D + d), x);
+      const float4 A = ld4(a.A + d), Bv = ld4(a.Bv + d), hp = ld4(a.h_prev + base + d), ee = ld4(a.e + base + d);
+      float4 hn;
+      hn.x = A.x * hp.x + Bv.x * ee.x + x.x;
+      hn.y = A.y * hp.y + Bv.y * ee.y + x.y;
+      hn.z = A.z * hp.z + Bv.z * ee.z + x.z;
+      hn.w = A.w * hp.w + Bv.w * ee.w + x.w;
+      tau[j] = hn;
+      st4(a.h_next + base + d, hn);
+      if (a.cap_h) st4(a.cap_h + base + d, hn);
+      zs += dot4(hn, ld4(a.halt_w + d));
+    }
+  }
+  const bool act = a.act_threshold > 0.f;
+  const bool last = a.t == a.n_loops - 1;
+  if (!act) {
+    if (last) {
+#pragma unroll
+      for (int j = 0; j < MAXV4; ++j) {
+        const int i4 = threadIdx.x + j * RB;
+        if (i4 < D4) st4(a.h_out + base + i4 * 4, tau[j]);
+      }
+    }
+    if (threadIdx.x == 0) a.halt_counts[n] = a.t + 1;
+    return;
+  }
+  const float z = block_sum(zs, &red[RDT_MAX_LORA][0]) + a.halt_b[0];
+  const float p = sigmoid_f(z);
+  const float cum = a.t == 0 ? 0.f : a.cum[n];
+  const int hc = a.t == 0 ? 0 : a.halt_counts[n];
+  const bool running = hc == 0;
+  float wgt = 0.f;
+  bool halt_now = false;
+  if (running) {
+    const float s = cum + p;
+    halt_now = (s >= a.act_threshold) || last;
+    wgt = halt_now ? fmaxf(1.0f - cum, 0.f) : p;
+  }
+  if (a.t == 0 || running) {
+#pragma unroll
+    for (int j = 0; j < MAXV4; ++j) {
+      const int i4 = threadIdx.x + j * RB;
+      if (i4 < D4) {
+        const int d = i4 * 4;
+        const float4 prev = a.t == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : ld4(a.h_out + base + d);
+        st4(a.h_out + base + d, fma4(wgt, tau[j], prev));
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    a.cum[n] = running ? cum + p : cum;
+    a.halt_counts[n] = halt_now ? a.t + 1 : hc;
+    if (a.cap_p) a.cap_p[n] = p;
+  }
+}
+
+// ------------------------------------------------------------ MLA glue
+// [ZS §MLA]: the kv down-projection splits into the latent c_kv and one
+// shared k_rope, which is rotated; both are what the cache holds.  The q
+// latent and the kv latent are RMS-normalised (DeepSeek-V2 form).
+template <typename TA>
+__global__ __launch_bounds__(64) void mla_latent_kernel(const float* __restrict__ kv_raw,
+                                                        const float* __restrict__ cq_raw,
+                                                        const float* __restrict__ gq, float eps, int T, int ql,
+                                                        int kvl, int rope, int start_pos,
+                                                        const float* __restrict__ rcos,
+                                                        const float* __restrict__ rsin, TA* __restrict__ cq_norm,
+                                                        TA* __restrict__ lat_ckv, TA* __restrict__ lat_krope,
+                                                        int lat_cap, int kbase) {
+  const int n = blockIdx.x, b = n / T, i = n - b * T, lane = threadIdx.x;
+  const float* cq = cq_raw + (int64_t)n * ql;
+  float ss = 0.f;
+  for (int d = lane; d < ql; d += 64) ss += cq[d] * cq[d];
+  const float r = 1.0f / sqrtf(wave_sum(ss) / ql + eps);
+  for (int d = lane; d < ql; d += 64) St<TA>::st(cq_norm + (int64_t)n * ql + d, cq[d] * r * gq[d]);
+  const float* kv = kv_raw + (int64_t)n * (kvl + rope);
+  const int64_t slot = (int64_t)b * lat_cap + kbase + i;
+  for (int d = lane; d < kvl; d += 64) St<TA>::st(lat_ckv + slot * kvl + d, kv[d]);
+  const int half = rope / 2, pos = start_pos + i;
+  for (int j = lane; j < half; j += 64) {
+    const float x0 = kv[kvl + 2 * j], x1 = kv[kvl + 2 * j + 1];
+    const float c = rcos[(int64_t)pos * half + j], s = rsin[(int64_t)pos * half + j];
+    St<TA>::st(lat_krope + slot * rope + 2 * j, x0 * c - x1 * s);
+    St<TA>::st(lat_krope + slot * rope + 2 * j + 1, x0 * s + x1 * c);
+  }
+}
+
+template <typename TA>
+__global__ __launch_bounds__(64) void mla_kv_prep_kernel(const TA* __restrict__ lat_ckv,
+                                                         const TA* __restrict__ lat_krope, int lat_cap,
+                                                         const float* __restrict__ gkv, float eps, int kvlen,
+                                                         int kvl, int rope, int H, int dq,
+                                                         TA* __restrict__ ckv_norm, TA* __restrict__ K) {
+  const int m = blockIdx.x, b = m / kvlen, j = m - b * kvlen, lane = threadIdx.x;
+  const TA* c = lat_ckv + ((int64_t)b * lat_cap + j) * kvl;
+  float ss = 0.f;
+  for (int d = lane; d < kvl; d += 64) {
+    const float x = St<TA>::ld(c + d);
+    ss += x * x;
+  }
+  const float r = 1.0f / sqrtf(wave_sum(ss) / kvl + eps);
+  for (int d = lane; d < kvl; d += 64) St<TA>::st(ckv_norm + (int64_t)m * kvl + d, St<TA>::ld(c + d) * r * gkv[d]);
+  const TA* kr = lat_krope + ((int64_t)b * lat_cap + j) * rope;
+  const int nope = dq - rope;
+  for (int x = lane; x < H * rope; x += 64) {
+    const int h = x / rope, d = x - h * rope;
+    K[(((int64_t)(b * H + h)) * kvlen + j) * dq + nope + d] = kr[d];
+  }
+}
+
+}  // namespace
+
+void launch_make_tables(float* rope_cos, float* rope_sin, int max_seq, int rot_dim, double theta, hipStream_t s) {
+  const int n = max_seq * (rot_dim / 2);
+  make_rope_kernel<<<(n + 255) / 256, 256, 0, s>>>(rope_cos, rope_sin, max_seq, rot_dim / 2, rot_dim, theta);
+}
+void launch_make_loop_table(float* emb, int n_loops_max, int loop_dim, double theta, hipStream_t s) {
+  const int n = n_loops_max * loop_dim;
+  make_loop_kernel<<<(n + 255) / 256, 256, 0, s>>>(emb, n_loops_max, loop_dim, theta);
+}
+void launch_make_A(const float* log_A, const float* log_dt, float* A, int D, hipStream_t s) {
+  make_A_kernel<<<(D + 255) / 256, 256, 0, s>>>(log_A, log_dt, A, D);
+}
+
+void launch_loop_head(int act_bf16, const float* h, const float* e, const float* emb_t, int loop_dim,
+                      const float* g_rec, const float* g_attn, float eps, float* c, void* a, int N, int D,
+                      hipStream_t s) {
+  if (act_bf16)
+    loop_head_kernel<bf16_t><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (bf16_t*)a, D);
+  else
+    loop_head_kernel<float><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (float*)a, D);
+}
+
+void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, float eps, void* out, int64_t ldo,
+                    int rows, int D, hipStream_t s) {
+  if (rows <= 0) return;
+  if (out_bf16) rmsnorm_kernel<bf16_t><<<rows, RB, 0, s>>>(x, ldx, g, eps, (bf16_t*)out, ldo, D);
+  else rmsnorm_kernel<float><<<rows, RB, 0, s>>>(x, ldx, g, eps, (float*)out, ldo, D);
+}
+
+void launch_router_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* sel, float* gate,
+                        int32_t* cap_sel, hipStream_t s) {
+  router_topk_kernel<<<(N + 3) / 4, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel);
+}
+
+void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,
+                     int32_t* mt_start, int32_t* tile_row0, int32_t* tile_grp, int32_t* perm_src, int32_t* inv,
+                     hipStream_t s) {
+  const int ntiles = (NK + RDT_DISP_TILE - 1) / RDT_DISP_TILE;
+  dispatch_count_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, E, tile_counts);
+  dispatch_scan_kernel<<<1, RDT_MAX_EXPERTS, 0, s>>>(tile_counts, ntiles, E, bm, offsets, mt_start, tile_row0,
+                                                     tile_grp);
+  dispatch_scatter_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, k, E, tile_counts, perm_src, inv);
+}
+
+void launch_loop_tail(const TailArgs& a, hipStream_t s) {
+  if (a.w_bf16) loop_tail_kernel<bf16_t><<<a.N, RB, 0, s>>>(a);
+  else loop_tail_kernel<float><<<a.N, RB, 0, s>>>(a);
+}
+
+void launch_mla_latent(int act_bf16, const float* kv_raw, const float* cq_raw, const float* gq, float eps, int N,
+                       int T, int ql, int kvl, int rope, int start_pos, const float* rcos, const float* rsin,
+                       void* cq_norm, void* lat_ckv, void* lat_krope, int lat_cap, int kbase, hipStream_t s) {
+  if (act_bf16)
+    mla_latent_kernel<bf16_t><<<N, 64, 0, s>>>(kv_raw, cq_raw, gq, eps, T, ql, kvl, rope, start_pos, rcos, rsin,
+                                               (bf16_t*)cq_norm, (bf16_t*)lat_ckv, (bf16_t*)lat_krope, lat_cap,
+                                               kbase);
+  else
+    mla_latent_kernel<float><<<N, 64, 0, s>>>(kv_raw, cq_raw, gq, eps, T, ql, kvl, rope, start_pos, rcos, rsin,
+                                              (float*)cq_norm, (float*)lat_ckv, (float*)lat_krope, lat_cap, kbase);
+}
+
+void launch_mla_kv_prep(int act_bf16, const void* lat_ckv, const void* lat_krope, int lat_cap, const float* gkv,
+                        float eps, int B, int kvlen, int kvl, int rope, int H, int dq, void* ckv_norm, void* K,
+                        hipStream_t s) {
+  if (act_bf16)
+    mla_kv_prep_kernel<bf16_t><<<B * kvlen, 64, 0, s>>>((const bf16_t*)lat_ckv, (const bf16_t*)lat_krope, lat_cap,
+                                                        gkv, eps, kvlen, kvl, rope, H, dq, (bf16_t*)ckv_norm,
+                                                        (bf16_t*)K);
+  else
+    mla_kv_prep_kernel<float><<<B * kvlen, 64, 0, s>>>((const float*)lat_ckv, (const float*)lat_krope, lat_cap,
+                                                       gkv, eps, kvlen, kvl, rope, H, dq, (float*)ckv_norm,
+                                                       (float*)K);
+}

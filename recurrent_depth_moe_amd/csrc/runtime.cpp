@@ -1,0 +1,760 @@
+// Host runtime behind include/rdt.h: argument checks, the handle (weights
+// and tables), workspace carving and the per-loop launch sequence.
+//
+// Pages: [ZS] "OpenMythos 분석: …의 계산 모델링" (zero.shotlearni.ng);
+//        [RC] "OpenMythos" (runchr.com).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/rdt.h"
+#include "attention.h"
+#include "gemm.h"
+#include "rowwise.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+rdt_status fail(rdt_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define HIP_TRY(x)                                                                    \
+  do {                                                                                \
+    hipError_t _e = (x);                                                              \
+    if (_e != hipSuccess) return fail(RDT_E_HIP, "%s: %s", #x, hipGetErrorString(_e)); \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+size_t esize(const rdt_config& c) { return c.weight_dtype == RDT_BF16 ? 2 : 4; }
+
+bool is_gqa(const rdt_config& c) { return c.attn == RDT_ATTN_GQA; }
+
+int qk_dim(const rdt_config& c) { return is_gqa(c) ? c.head_dim : c.qk_nope_head_dim + c.qk_rope_head_dim; }
+int v_dim(const rdt_config& c) { return is_gqa(c) ? c.head_dim : c.v_head_dim; }
+int kv_heads(const rdt_config& c) { return is_gqa(c) ? c.n_kv_heads : c.n_heads; }
+int rot_dim(const rdt_config& c) { return is_gqa(c) ? c.head_dim : c.qk_rope_head_dim; }
+
+rdt_status check_config(const rdt_config* c) {
+  if (!c) return fail(RDT_E_INVALID_ARG, "config is NULL");
+  if (c->weight_dtype != RDT_F32 && c->weight_dtype != RDT_BF16) return fail(RDT_E_INVALID_ARG, "weight_dtype");
+  if (c->attn != RDT_ATTN_GQA && c->attn != RDT_ATTN_MLA) return fail(RDT_E_INVALID_ARG, "attn type");
+  if (c->dim < 4 || c->dim % 4) return fail(RDT_E_INVALID_ARG, "dim %d must be a positive multiple of 4", c->dim);
+  if (c->dim > 8192) return fail(RDT_E_UNSUPPORTED, "dim %d above 8192", c->dim);
+  if (c->n_heads < 1) return fail(RDT_E_INVALID_ARG, "n_heads");
+  if (is_gqa(*c)) {
+    if (c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return fail(RDT_E_INVALID_ARG, "n_kv_heads must divide n_heads");
+    if (c->head_dim < 2 || c->head_dim % 2) return fail(RDT_E_INVALID_ARG, "head_dim must be even");
+    if (c->dim != c->n_heads * c->head_dim) return fail(RDT_E_INVALID_ARG, "dim != n_heads * head_dim");
+    if (c->weight_dtype == RDT_BF16 && c->head_dim != 128)
+      return fail(RDT_E_UNSUPPORTED, "bf16 attention is built for head_dim 128 (got %d)", c->head_dim);
+    if (c->weight_dtype == RDT_F32 && c->head_dim > 128) return fail(RDT_E_UNSUPPORTED, "head_dim above 128");
+  } else {
+    if (c->weight_dtype != RDT_F32) return fail(RDT_E_UNSUPPORTED, "MLA is built for fp32 only");
+    if (c->q_lora_rank < 1 || c->kv_lora_rank < 1 || c->qk_rope_head_dim < 2 || c->qk_rope_head_dim % 2 ||
+        c->qk_nope_head_dim < 0 || c->v_head_dim < 1)
+      return fail(RDT_E_INVALID_ARG, "MLA ranks / head widths");
+    if (c->qk_nope_head_dim % 2) return fail(RDT_E_INVALID_ARG, "qk_nope_head_dim must be even");
+    if (qk_dim(*c) > 128 || c->v_head_dim > 128) return fail(RDT_E_UNSUPPORTED, "MLA head width above 128");
+    if (c->q_lora_rank % 4 || c->kv_lora_rank % 4 || (c->n_heads * c->v_head_dim) % 4)
+      return fail(RDT_E_UNSUPPORTED, "MLA ranks must be multiples of 4");
+  }
+  if (c->n_experts < 1 || c->n_experts > 256) return fail(RDT_E_INVALID_ARG, "n_experts must be in [1, 256]");
+  if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts) return fail(RDT_E_INVALID_ARG, "top_k must be in [1, min(8, n_experts)]");
+  if (c->n_shared_experts < 0 || c->n_shared_experts > 8) return fail(RDT_E_INVALID_ARG, "n_shared_experts");
+  if (c->expert_dim < 4) return fail(RDT_E_INVALID_ARG, "expert_dim");
+  const int kmul = c->weight_dtype == RDT_BF16 ? 8 : 4;
+  if (c->dim % kmul || c->expert_dim % kmul)
+    return fail(RDT_E_UNSUPPORTED, "dim and expert_dim must be multiples of %d", kmul);
+  if (c->lora_rank < 1 || c->lora_rank > RDT_MAX_LORA) return fail(RDT_E_INVALID_ARG, "lora_rank must be in [1, %d]", RDT_MAX_LORA);
+  if (c->max_loop_iters < 1) return fail(RDT_E_INVALID_ARG, "max_loop_iters");
+  if (c->loop_dim < 0 || c->loop_dim > c->dim || c->loop_dim % 4)
+    return fail(RDT_E_INVALID_ARG, "loop_dim must be a multiple of 4 in [0, dim]");
+  if (c->max_seq_len < 1) return fail(RDT_E_INVALID_ARG, "max_seq_len");
+  if (!(c->norm_eps > 0.f) || !(c->rope_theta > 0.f) || !(c->loop_theta > 0.f))
+    return fail(RDT_E_INVALID_ARG, "norm_eps, rope_theta and loop_theta must be positive");
+  return RDT_OK;
+}
+
+// ------------------------------------------------------------ workspace plan
+
+enum WsId {
+  WS_H, WS_C, WS_A, WS_Q, WS_K, WS_VT, WS_O, WS_X1, WS_F, WS_LOGITS, WS_SEL, WS_GATE, WS_TILECNT, WS_OFFSETS,
+  WS_MTSTART, WS_TROW0, WS_TGRP, WS_PERM, WS_INV, WS_ACT, WS_Y, WS_ACTS, WS_YS, WS_CUM,
+  WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_COUNT
+};
+const char* kWsNames[WS_COUNT] = {"h", "c", "a", "q", "k", "vt", "o", "x1", "f", "logits", "sel", "gate",
+                                  "tile_counts", "offsets", "mt_start", "tile_row0", "tile_grp", "perm", "inv",
+                                  "act", "y", "act_s", "y_s", "cum", "kv_raw", "cq_raw", "cq_norm", "lat_ckv",
+                                  "lat_krope", "ckv_norm"};
+
+struct Plan {
+  int B, T, N, NK, kvcap, kvlen_max, bm, max_mt, disp_tiles;
+  size_t off[WS_COUNT], size[WS_COUNT], total;
+};
+
+int bm_for(const rdt_config& c) { return c.weight_dtype == RDT_BF16 ? RDT_BM_LARGE : RDT_BM_F32; }
+
+Plan make_plan(const rdt_config& c, int B, int T) {
+  Plan p{};
+  p.B = B;
+  p.T = T;
+  p.N = B * T;
+  p.NK = p.N * c.top_k;
+  p.kvcap = round_up(T, 64);
+  p.kvlen_max = c.max_seq_len;
+  p.bm = bm_for(c);
+  p.max_mt = (p.NK + p.bm - 1) / p.bm + c.n_experts;
+  p.disp_tiles = (p.NK + RDT_DISP_TILE - 1) / RDT_DISP_TILE;
+  const size_t es = esize(c), D = c.dim, N = p.N, NK = p.NK, F = c.expert_dim, E = c.n_experts;
+  const size_t H = c.n_heads, G = kv_heads(c), dq = qk_dim(c), dv = v_dim(c);
+  size_t* s = p.size;
+  s[WS_H] = N * D * 4;
+  s[WS_C] = N * D * 4;
+  s[WS_A] = N * D * es;
+  s[WS_Q] = N * H * dq * es;
+  if (is_gqa(c)) {
+    s[WS_K] = (size_t)B * G * p.kvcap * dq * es;
+    s[WS_VT] = (size_t)B * G * dv * p.kvcap * es;
+  } else {
+    // MLA rebuilds per-head K / V^T for every visible key position
+    s[WS_K] = (size_t)B * H * p.kvlen_max * dq * es;
+    s[WS_VT] = (size_t)B * H * dv * p.kvlen_max * es;
+  }
+  s[WS_O] = N * H * dv * es;
+  s[WS_X1] = N * D * 4;
+  s[WS_F] = N * D * es;
+  s[WS_LOGITS] = N * E * 4;
+  s[WS_SEL] = NK * 4;
+  s[WS_GATE] = NK * 4;
+  s[WS_TILECNT] = (size_t)p.disp_tiles * E * 4;
+  s[WS_OFFSETS] = (E + 1) * 4;
+  s[WS_MTSTART] = (E + 1) * 4;
+  s[WS_TROW0] = (size_t)p.max_mt * 4;
+  s[WS_TGRP] = (size_t)p.max_mt * 4;
+  s[WS_PERM] = NK * 4;
+  s[WS_INV] = NK * 4;
+  s[WS_ACT] = NK * F * es;
+  s[WS_Y] = NK * D * 4;
+  s[WS_ACTS] = N * F * es;
+  s[WS_YS] = (size_t)c.n_shared_experts * N * D * 4;
+  s[WS_CUM] = N * 4;
+  if (!is_gqa(c)) {
+    const size_t ql = c.q_lora_rank, kvl = c.kv_lora_rank, rope = c.qk_rope_head_dim;
+    s[WS_KVRAW] = N * (kvl + rope) * 4;
+    s[WS_CQRAW] = N * ql * 4;
+    s[WS_CQN] = N * ql * es;
+    s[WS_LATC] = N * kvl * es;
+    s[WS_LATR] = N * rope * es;
+    s[WS_CKVN] = (size_t)B * p.kvlen_max * kvl * es;
+  }
+  size_t o = 0;
+  for (int i = 0; i < WS_COUNT; ++i) {
+    p.off[i] = o;
+    o += align256(s[i]);
+  }
+  p.total = o;
+  return p;
+}
+
+size_t kv_slot_bytes(const rdt_config& c, int B, int capacity) {
+  const size_t cp = round_up(capacity, 64);
+  if (is_gqa(c)) return 2 * (size_t)B * c.n_kv_heads * cp * c.head_dim * esize(c);
+  return (size_t)B * cp * (c.kv_lora_rank + c.qk_rope_head_dim) * esize(c);
+}
+
+rdt_status check_call(const rdt_config& c, const void* e, const void* h0, int B, int T, int start_pos, int n_loops,
+                      float thr, const void* kv, int kv_capacity, size_t kv_bytes, const void* ws, size_t ws_bytes,
+                      const void* h_out, const void* hc, bool decode) {
+  if (!e || !h0 || !h_out || !hc) return fail(RDT_E_INVALID_ARG, "e, h0, h_out and halt_counts must be non-NULL");
+  if (B < 1 || T < 1) return fail(RDT_E_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
+  if (n_loops < 1 || n_loops > RDT_MAX_LOOPS) return fail(RDT_E_INVALID_ARG, "n_loops must be in [1, %d]", RDT_MAX_LOOPS);
+  if (!(thr == 0.f || (thr > 0.f && thr <= 1.f))) return fail(RDT_E_INVALID_ARG, "act_threshold must be 0 or in (0, 1]");
+  if (start_pos < 0) return fail(RDT_E_INVALID_ARG, "start_pos < 0");
+  if ((int64_t)start_pos + T > c.max_seq_len)
+    return fail(RDT_E_INVALID_ARG, "start_pos + T = %lld exceeds max_seq_len %d", (long long)start_pos + T, c.max_seq_len);
+  if (decode && !kv) return fail(RDT_E_BAD_STATE, "decode needs a KV cache");
+  if (kv) {
+    if ((int64_t)start_pos + T > kv_capacity)
+      return fail(RDT_E_INVALID_ARG, "start_pos + T exceeds kv_capacity %d", kv_capacity);
+    const size_t need = kv_slot_bytes(c, B, kv_capacity) * (size_t)n_loops;
+    if (kv_bytes < need) {
+      return fail(decode ? RDT_E_BAD_STATE : RDT_E_INVALID_ARG,
+                  "kv cache holds %zu bytes, %d loop slots need %zu", kv_bytes, n_loops, need);
+    }
+  }
+  if (!ws) return fail(RDT_E_INVALID_ARG, "workspace is NULL");
+  const Plan p = make_plan(c, B, T);
+  if (ws_bytes < p.total) return fail(RDT_E_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, p.total);
+  if (((uintptr_t)ws) & 255) return fail(RDT_E_INVALID_ARG, "workspace must be 256-byte aligned");
+  return RDT_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ handle
+
+struct rdt_block {
+  rdt_config cfg;
+  int n_cu = 0;
+  int64_t params = 0;
+  char* mem = nullptr;
+  size_t mem_bytes = 0;
+  // weights (device, handle-owned)
+  const float *g_rec, *g_attn, *g_ffn, *gq, *gkv, *router_bias, *lora_scale, *log_A, *log_dt, *Bv, *halt_w, *halt_b;
+  const void *wqkv, *wo, *wdq, *wuq, *wdkv, *wukv, *router, *w_gate, *w_up, *w_down, *s_gate, *s_up, *s_down,
+      *lora_down, *lora_B;
+  // tables
+  float *A, *rope_cos, *rope_sin, *loop_emb;
+  // capture
+  float* cap_h = nullptr;
+  int32_t* cap_sel = nullptr;
+  float* cap_p = nullptr;
+  int cap_loops = 0;
+};
+
+namespace {
+
+struct TensorDesc {
+  int id;
+  size_t numel;
+  bool matrix;  // stored in weight_dtype; vectors are fp32
+};
+
+void tensor_list(const rdt_config& c, TensorDesc* out, int* n) {
+  const size_t D = c.dim, E = c.n_experts, F = c.expert_dim, S = c.n_shared_experts, r = c.lora_rank,
+               L = c.max_loop_iters, H = c.n_heads;
+  int i = 0;
+  auto add = [&](int id, size_t numel, bool m) { out[i++] = TensorDesc{id, numel, m}; };
+  add(RDT_W_G_REC, D, false);
+  add(RDT_W_G_ATTN, D, false);
+  add(RDT_W_G_FFN, D, false);
+  if (is_gqa(c)) {
+    const size_t dh = c.head_dim, G = c.n_kv_heads;
+    add(RDT_W_WQ, H * dh * D, true);
+    add(RDT_W_WK, G * dh * D, true);
+    add(RDT_W_WV, G * dh * D, true);
+    add(RDT_W_WO, D * H * dh, true);
+  } else {
+    const size_t ql = c.q_lora_rank, kvl = c.kv_lora_rank, rope = c.qk_rope_head_dim, nope = c.qk_nope_head_dim,
+                 vd = c.v_head_dim;
+    add(RDT_W_WDQ, ql * D, true);
+    add(RDT_W_GQ, ql, false);
+    add(RDT_W_WUQ, H * (nope + rope) * ql, true);
+    add(RDT_W_WDKV, (kvl + rope) * D, true);
+    add(RDT_W_GKV, kvl, false);
+    add(RDT_W_WUKV, H * (nope + vd) * kvl, true);
+    add(RDT_W_WO, D * H * vd, true);
+  }
+  add(RDT_W_ROUTER, E * D, true);
+  add(RDT_W_ROUTER_BIAS, E, false);
+  add(RDT_W_GATE, E * F * D, true);
+  add(RDT_W_UP, E * F * D, true);
+  add(RDT_W_DOWN, E * D * F, true);
+  if (S) {
+    add(RDT_W_S_GATE, S * F * D, true);
+    add(RDT_W_S_UP, S * F * D, true);
+    add(RDT_W_S_DOWN, S * D * F, true);
+  }
+  add(RDT_W_LORA_DOWN, r * D, true);
+  add(RDT_W_LORA_B, r * D, true);
+  add(RDT_W_LORA_SCALE, L * r, false);
+  add(RDT_W_LOG_A, D, false);
+  add(RDT_W_LOG_DT, 1, false);
+  add(RDT_W_B, D, false);
+  add(RDT_W_HALT_W, D, false);
+  add(RDT_W_HALT_B, 1, false);
+  *n = i;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t rdt_abi_version(void) { return RDT_ABI_VERSION; }
+
+const char* rdt_status_string(rdt_status s) {
+  switch (s) {
+    case RDT_OK: return "ok";
+    case RDT_E_INVALID_ARG: return "invalid argument";
+    case RDT_E_UNSUPPORTED: return "unsupported";
+    case RDT_E_OUT_OF_MEMORY: return "out of device memory";
+    case RDT_E_HIP: return "HIP runtime error";
+    case RDT_E_BAD_STATE: return "bad state";
+    case RDT_E_WORKSPACE_TOO_SMALL: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* rdt_last_error(void) { return g_err.c_str(); }
+
+rdt_status rdt_check_config(const rdt_config* cfg) {
+  g_err.clear();
+  return check_config(cfg);
+}
+
+rdt_status rdt_workspace_bytes_cfg(const rdt_config* cfg, int32_t B, int32_t T, size_t* bytes) {
+  rdt_status st = check_config(cfg);
+  if (st) return st;
+  if (!bytes) return fail(RDT_E_INVALID_ARG, "bytes is NULL");
+  if (B < 1 || T < 1) return fail(RDT_E_INVALID_ARG, "B and T must be >= 1");
+  *bytes = make_plan(*cfg, B, T).total;
+  return RDT_OK;
+}
+
+rdt_status rdt_kv_cache_bytes_cfg(const rdt_config* cfg, int32_t B, int32_t capacity, int32_t n_loops,
+                                  size_t* bytes) {
+  rdt_status st = check_config(cfg);
+  if (st) return st;
+  if (!bytes) return fail(RDT_E_INVALID_ARG, "bytes is NULL");
+  if (B < 1 || capacity < 1 || n_loops < 1) return fail(RDT_E_INVALID_ARG, "B, capacity and n_loops must be >= 1");
+  *bytes = kv_slot_bytes(*cfg, B, capacity) * (size_t)n_loops;
+  return RDT_OK;
+}
+
+rdt_status rdt_workspace_offset_cfg(const rdt_config* cfg, int32_t B, int32_t T, const char* name, size_t* offset,
+                                    size_t* bytes) {
+  rdt_status st = check_config(cfg);
+  if (st) return st;
+  if (!name || !offset || !bytes) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  if (B < 1 || T < 1) return fail(RDT_E_INVALID_ARG, "B and T must be >= 1");
+  const Plan p = make_plan(*cfg, B, T);
+  for (int i = 0; i < WS_COUNT; ++i)
+    if (!strcmp(name, kWsNames[i])) {
+      *offset = p.off[i];
+      *bytes = p.size[i];
+      return RDT_OK;
+    }
+  return fail(RDT_E_INVALID_ARG, "unknown workspace buffer '%s'", name);
+}
+
+rdt_status rdt_check_call(const rdt_config* cfg, int32_t B, int32_t T, int32_t start_pos, int32_t n_loops,
+                          float act_threshold, int32_t has_kv, int32_t kv_capacity, size_t kv_bytes,
+                          size_t ws_bytes, int32_t decode) {
+  rdt_status st = check_config(cfg);
+  if (st) return st;
+  // stand-in non-NULL pointers: only shapes and sizes are checked here
+  static char dummy[256] __attribute__((aligned(256)));
+  return check_call(*cfg, dummy, dummy, B, T, start_pos, n_loops, act_threshold, has_kv ? dummy : nullptr,
+                    kv_capacity, kv_bytes, dummy, ws_bytes, dummy, dummy, decode != 0);
+}
+
+rdt_status rdt_block_create(const rdt_config* cfg, const void* const* weights, void* stream, rdt_block** out) {
+  g_err.clear();
+  if (!out) return fail(RDT_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  rdt_status st = check_config(cfg);
+  if (st) return st;
+  if (!weights) return fail(RDT_E_INVALID_ARG, "weights is NULL");
+  const rdt_config& c = *cfg;
+  TensorDesc td[RDT_W_COUNT];
+  int nt = 0;
+  tensor_list(c, td, &nt);
+  for (int i = 0; i < nt; ++i)
+    if (!weights[td[i].id]) return fail(RDT_E_INVALID_ARG, "weight tensor %d is NULL", td[i].id);
+
+  const size_t es = esize(c);
+  size_t off[RDT_W_COUNT] = {0};
+  size_t o = 0;
+  int64_t params = 0;
+  // q, k, v are placed back to back: one [(H + 2G) * dh, D] matrix
+  for (int i = 0; i < nt; ++i) {
+    const size_t bytes = td[i].numel * (td[i].matrix ? es : 4);
+    const bool packed = td[i].id == RDT_W_WK || td[i].id == RDT_W_WV;
+    off[td[i].id] = packed ? o : (o = align256(o), o);
+    o += bytes;
+    params += (int64_t)td[i].numel;
+  }
+  o = align256(o);
+  const int rot = rot_dim(c);
+  const size_t rope_off = o;
+  o += align256((size_t)c.max_seq_len * (rot / 2) * 4) * 2;
+  const size_t loop_off = o;
+  o += align256((size_t)RDT_MAX_LOOPS * (c.loop_dim > 0 ? c.loop_dim : 1) * 4);
+  const size_t A_off = o;
+  o += align256((size_t)c.dim * 4);
+
+  const char* fa = getenv("RDT_FAULT_ALLOC");
+  if (fa && atoi(fa) == 1) return fail(RDT_E_OUT_OF_MEMORY, "allocation failure injected by RDT_FAULT_ALLOC=1");
+
+  hipStream_t s = (hipStream_t)stream;
+  rdt_block* b = new rdt_block();
+  b->cfg = c;
+  b->params = params;
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he == hipSuccess) he = hipDeviceGetAttribute(&b->n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (he != hipSuccess) {
+    delete b;
+    return fail(RDT_E_HIP, "hipGetDevice/hipDeviceGetAttribute: %s", hipGetErrorString(he));
+  }
+  he = hipMalloc((void**)&b->mem, o);
+  if (he != hipSuccess) {
+    delete b;
+    return fail(he == hipErrorOutOfMemory ? RDT_E_OUT_OF_MEMORY : RDT_E_HIP, "hipMalloc(%zu): %s", o,
+                hipGetErrorString(he));
+  }
+  b->mem_bytes = o;
+  for (int i = 0; i < nt; ++i) {
+    const size_t bytes = td[i].numel * (td[i].matrix ? es : 4);
+    he = hipMemcpyAsync(b->mem + off[td[i].id], weights[td[i].id], bytes, hipMemcpyDeviceToDevice, s);
+    if (he != hipSuccess) break;
+  }
+  auto P = [&](int id) -> const void* { return b->mem + off[id]; };
+  auto PF = [&](int id) -> const float* { return (const float*)(b->mem + off[id]); };
+  b->g_rec = PF(RDT_W_G_REC);
+  b->g_attn = PF(RDT_W_G_ATTN);
+  b->g_ffn = PF(RDT_W_G_FFN);
+  if (is_gqa(c)) {
+    b->wqkv = P(RDT_W_WQ);
+  } else {
+    b->wdq = P(RDT_W_WDQ);
+    b->gq = PF(RDT_W_GQ);
+    b->wuq = P(RDT_W_WUQ);
+    b->wdkv = P(RDT_W_WDKV);
+    b->gkv = PF(RDT_W_GKV);
+    b->wukv = P(RDT_W_WUKV);
+  }
+  b->wo = P(RDT_W_WO);
+  b->router = P(RDT_W_ROUTER);
+  b->router_bias = PF(RDT_W_ROUTER_BIAS);
+  b->w_gate = P(RDT_W_GATE);
+  b->w_up = P(RDT_W_UP);
+  b->w_down = P(RDT_W_DOWN);
+  if (c.n_shared_experts) {
+    b->s_gate = P(RDT_W_S_GATE);
+    b->s_up = P(RDT_W_S_UP);
+    b->s_down = P(RDT_W_S_DOWN);
+  }
+  b->lora_down = P(RDT_W_LORA_DOWN);
+  b->lora_B = P(RDT_W_LORA_B);
+  b->lora_scale = PF(RDT_W_LORA_SCALE);
+  b->log_A = PF(RDT_W_LOG_A);
+  b->log_dt = PF(RDT_W_LOG_DT);
+  b->Bv = PF(RDT_W_B);
+  b->halt_w = PF(RDT_W_HALT_W);
+  b->halt_b = PF(RDT_W_HALT_B);
+  b->rope_cos = (float*)(b->mem + rope_off);
+  b->rope_sin = (float*)(b->mem + rope_off + align256((size_t)c.max_seq_len * (rot / 2) * 4));
+  b->loop_emb = (float*)(b->mem + loop_off);
+  b->A = (float*)(b->mem + A_off);
+  if (he == hipSuccess) {
+    launch_make_tables(b->rope_cos, b->rope_sin, c.max_seq_len, rot, (double)c.rope_theta, s);
+    if (c.loop_dim > 0) launch_make_loop_table(b->loop_emb, RDT_MAX_LOOPS, c.loop_dim, (double)c.loop_theta, s);
+    launch_make_A(b->log_A, b->log_dt, b->A, c.dim, s);
+    he = hipGetLastError();
+  }
+  if (he == hipSuccess) he = hipStreamSynchronize(s);
+  if (he != hipSuccess) {
+    (void)hipFree(b->mem);
+    delete b;
+    return fail(RDT_E_HIP, "create: %s", hipGetErrorString(he));
+  }
+  *out = b;
+  return RDT_OK;
+}
+
+rdt_status rdt_block_destroy(rdt_block* b) {
+  if (!b) return RDT_OK;
+  hipError_t he = hipDeviceSynchronize();
+  if (b->mem) (void)hipFree(b->mem);
+  delete b;
+  if (he != hipSuccess) return fail(RDT_E_HIP, "destroy: %s", hipGetErrorString(he));
+  return RDT_OK;
+}
+
+rdt_status rdt_param_count(const rdt_block* b, int64_t* count) {
+  if (!b || !count) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  *count = b->params;
+  return RDT_OK;
+}
+
+rdt_status rdt_workspace_bytes(const rdt_block* b, int32_t B, int32_t T, size_t* bytes) {
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  return rdt_workspace_bytes_cfg(&b->cfg, B, T, bytes);
+}
+
+rdt_status rdt_kv_cache_bytes(const rdt_block* b, int32_t B, int32_t capacity, int32_t n_loops, size_t* bytes) {
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  return rdt_kv_cache_bytes_cfg(&b->cfg, B, capacity, n_loops, bytes);
+}
+
+rdt_status rdt_workspace_offset(const rdt_block* b, int32_t B, int32_t T, const char* name, size_t* offset,
+                                size_t* bytes) {
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  return rdt_workspace_offset_cfg(&b->cfg, B, T, name, offset, bytes);
+}
+
+rdt_status rdt_get_A(const rdt_block* b, float* A_host) {
+  if (!b || !A_host) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  HIP_TRY(hipMemcpy(A_host, b->A, (size_t)b->cfg.dim * 4, hipMemcpyDeviceToHost));
+  return RDT_OK;
+}
+
+rdt_status rdt_set_capture(rdt_block* b, float* h_loops, int32_t* sel_loops, float* p_loops, int32_t max_loops) {
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  if ((h_loops || sel_loops || p_loops) && max_loops < 1) return fail(RDT_E_INVALID_ARG, "max_loops must be >= 1");
+  b->cap_h = h_loops;
+  b->cap_sel = sel_loops;
+  b->cap_p = p_loops;
+  b->cap_loops = (h_loops || sel_loops || p_loops) ? max_loops : 0;
+  return RDT_OK;
+}
+
+static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int T, int start_pos, int n_loops,
+                      float thr, void* kv, int kv_capacity, size_t kv_bytes, void* ws, size_t ws_bytes,
+                      float* h_out, int32_t* halt_counts, void* stream, bool decode) {
+  g_err.clear();
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  const rdt_config& c = b->cfg;
+  rdt_status st = check_call(c, e, h0, B, T, start_pos, n_loops, thr, kv, kv_capacity, kv_bytes, ws, ws_bytes,
+                             h_out, halt_counts, decode);
+  if (st) return st;
+  if (b->cap_loops && n_loops > b->cap_loops)
+    return fail(RDT_E_INVALID_ARG, "n_loops %d exceeds the capture buffers (%d loops)", n_loops, b->cap_loops);
+  hipStream_t s = (hipStream_t)stream;
+  const Plan p = make_plan(c, B, T);
+  char* w = (char*)ws;
+  auto W = [&](int id) -> void* { return w + p.off[id]; };
+  auto WF = [&](int id) -> float* { return (float*)(w + p.off[id]); };
+  auto WI = [&](int id) -> int32_t* { return (int32_t*)(w + p.off[id]); };
+  const bool bf = c.weight_dtype == RDT_BF16;
+  const int N = p.N, D = c.dim, E = c.n_experts, F = c.expert_dim, k = c.top_k, H = c.n_heads;
+  const int G = kv_heads(c), dq = qk_dim(c), dv = v_dim(c);
+  const size_t es = esize(c);
+  const int cap_pad = round_up(kv_capacity > 0 ? kv_capacity : 1, 64);
+  const size_t slot = kv ? kv_slot_bytes(c, B, kv_capacity) : 0;
+  const float scale = 1.0f / sqrtf((float)dq);
+
+  auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16) {
+    if (bf) launch_gemm_bf16(gp, epi, dual, p.bm, out_bf16, b->n_cu, s);
+    else launch_gemm_f32(gp, epi, dual, b->n_cu, s);
+  };
+  auto dense = [&](const void* A, int64_t lda, const void* W0, const void* W1, int M, int Nn, int K) {
+    GemmParams gp{};
+    gp.A = A;
+    gp.lda = lda;
+    gp.W0 = W0;
+    gp.W1 = W1;
+    gp.M = M;
+    gp.N = Nn;
+    gp.K = K;
+    gp.dense_gm = 4;
+    return gp;
+  };
+
+  for (int t = 0; t < n_loops; ++t) {
+    const float* hp = t == 0 ? h0 : WF(WS_H);
+    // a1-a3: loop-index embedding, re-injection of e, RMSNorms
+    launch_loop_head(bf, hp, e, b->loop_emb + (size_t)t * c.loop_dim, c.loop_dim, b->g_rec, b->g_attn, c.norm_eps,
+                     WF(WS_C), W(WS_A), N, D, s);
+    // a4-a6: attention
+    char* kslot = kv ? (char*)kv + slot * t : nullptr;
+    if (is_gqa(c)) {
+      void* K = kv ? (void*)kslot : W(WS_K);
+      void* VT = kv ? (void*)(kslot + (size_t)B * G * cap_pad * dq * es) : W(WS_VT);
+      const int cap = kv ? cap_pad : p.kvcap;
+      const int kbase = kv ? start_pos : 0;
+      GemmParams gp = dense(W(WS_A), D, b->wqkv, nullptr, N, (H + 2 * G) * dq, D);
+      EpiParams& ep = gp.epi;
+      ep.q = W(WS_Q);
+      ep.k = K;
+      ep.vt = VT;
+      ep.T = T;
+      ep.H = H;
+      ep.G = G;
+      ep.dq = dq;
+      ep.dv = dv;
+      ep.cap = cap;
+      ep.kbase = kbase;
+      ep.start_pos = start_pos;
+      ep.rcos = b->rope_cos;
+      ep.rsin = b->rope_sin;
+      ep.rot_half = dq / 2;
+      gemm(gp, EPI_QKV, false, bf);
+      if (bf && T > 1)
+        launch_attn_flash_bf16(W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, kbase, scale, s);
+      else
+        launch_attn_generic(bf, W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, dq, dv, kbase, scale, s);
+    } else {
+      const int ql = c.q_lora_rank, kvl = c.kv_lora_rank, rope = c.qk_rope_head_dim, nope = c.qk_nope_head_dim;
+      const int lat_cap = kv ? cap_pad : T;
+      const int kbase = kv ? start_pos : 0;
+      const int kvlen = kbase + T;
+      void* lat_c = kv ? (void*)kslot : W(WS_LATC);
+      void* lat_r = kv ? (void*)(kslot + (size_t)B * cap_pad * kvl * es) : W(WS_LATR);
+      GemmParams g1 = dense(W(WS_A), D, b->wdkv, nullptr, N, kvl + rope, D);
+      g1.epi.out = W(WS_KVRAW);
+      g1.epi.ldo = kvl + rope;
+      gemm(g1, EPI_STORE, false, 0);
+      GemmParams g2 = dense(W(WS_A), D, b->wdq, nullptr, N, ql, D);
+      g2.epi.out = W(WS_CQRAW);
+      g2.epi.ldo = ql;
+      gemm(g2, EPI_STORE, false, 0);
+      launch_mla_latent(bf, WF(WS_KVRAW), WF(WS_CQRAW), b->gq, c.norm_eps, N, T, ql, kvl, rope, start_pos,
+                        b->rope_cos, b->rope_sin, W(WS_CQN), lat_c, lat_r, lat_cap, kbase, s);
+      GemmParams g3 = dense(W(WS_CQN), ql, b->wuq, nullptr, N, H * dq, ql);
+      g3.epi.q = W(WS_Q);
+      g3.epi.T = T;
+      g3.epi.H = H;
+      g3.epi.dq = dq;
+      g3.epi.nope = nope;
+      g3.epi.start_pos = start_pos;
+      g3.epi.rcos = b->rope_cos;
+      g3.epi.rsin = b->rope_sin;
+      g3.epi.rot_half = rope / 2;
+      gemm(g3, EPI_MLA_Q, false, bf);
+      launch_mla_kv_prep(bf, lat_c, lat_r, lat_cap, b->gkv, c.norm_eps, B, kvlen, kvl, rope, H, dq, W(WS_CKVN),
+                         W(WS_K), s);
+      GemmParams g4 = dense(W(WS_CKVN), kvl, b->wukv, nullptr, B * kvlen, H * (nope + dv), kvl);
+      g4.epi.k = W(WS_K);
+      g4.epi.vt = W(WS_VT);
+      g4.epi.T = kvlen;
+      g4.epi.H = H;
+      g4.epi.dq = dq;
+      g4.epi.dv = dv;
+      g4.epi.nope = nope;
+      g4.epi.cap = kvlen;
+      gemm(g4, EPI_MLA_KV, false, bf);
+      launch_attn_generic(bf, W(WS_Q), W(WS_K), W(WS_VT), W(WS_O), B, H, H, T, kvlen, dq, dv, kbase, scale, s);
+    }
+    // a7: x1 = c + o Wo^T
+    {
+      GemmParams gp = dense(W(WS_O), (int64_t)H * dv, b->wo, nullptr, N, D, H * dv);
+      gp.epi.out = W(WS_X1);
+      gp.epi.ldo = D;
+      gp.epi.resid = WF(WS_C);
+      gemm(gp, EPI_RESID, false, 0);
+    }
+    // a8: f = RMSNorm(x1) * g_ffn
+    launch_rmsnorm(bf, WF(WS_X1), D, b->g_ffn, c.norm_eps, W(WS_F), D, N, D, s);
+    // a9: router logits, softmax, top-k
+    {
+      GemmParams gp = dense(W(WS_F), D, b->router, nullptr, N, E, D);
+      gp.epi.out = W(WS_LOGITS);
+      gp.epi.ldo = E;
+      gemm(gp, EPI_STORE, false, 0);
+      launch_router_topk(WF(WS_LOGITS), b->router_bias, N, E, k, WI(WS_SEL), WF(WS_GATE),
+                         b->cap_sel ? b->cap_sel + (size_t)t * N * k : nullptr, s);
+    }
+    // a10: dispatch
+    launch_dispatch(WI(WS_SEL), p.NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART), WI(WS_TROW0),
+                    WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), s);
+    // a11: routed gate|up + SwiGLU, rows gathered from f
+    {
+      GemmParams gp{};
+      gp.A = W(WS_F);
+      gp.lda = D;
+      gp.a_rows = WI(WS_PERM);
+      gp.W0 = b->w_gate;
+      gp.W1 = b->w_up;
+      gp.w_stride = (int64_t)F * D;
+      gp.M = p.NK;
+      gp.N = F;
+      gp.K = D;
+      gp.mt_start = WI(WS_MTSTART);
+      gp.tile_row0 = WI(WS_TROW0);
+      gp.tile_grp = WI(WS_TGRP);
+      gp.grp_end = WI(WS_OFFSETS);
+      gp.n_groups = E;
+      gp.epi.out = W(WS_ACT);
+      gp.epi.ldo = F;
+      gemm(gp, EPI_SWIGLU, true, bf);
+      // a12: routed down
+      GemmParams gd = gp;
+      gd.A = W(WS_ACT);
+      gd.lda = F;
+      gd.a_rows = nullptr;
+      gd.W0 = b->w_down;
+      gd.W1 = nullptr;
+      gd.w_stride = (int64_t)D * F;
+      gd.N = D;
+      gd.K = F;
+      gd.epi = EpiParams{};
+      gd.epi.out = W(WS_Y);
+      gd.epi.ldo = D;
+      gemm(gd, EPI_STORE, false, 0);
+    }
+    // a13: shared experts on every row
+    for (int si = 0; si < c.n_shared_experts; ++si) {
+      GemmParams gp = dense(W(WS_F), D, (const char*)b->s_gate + (size_t)si * F * D * es,
+                            (const char*)b->s_up + (size_t)si * F * D * es, N, F, D);
+      gp.epi.out = W(WS_ACTS);
+      gp.epi.ldo = F;
+      gemm(gp, EPI_SWIGLU, true, bf);
+      GemmParams gd = dense(W(WS_ACTS), F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, N, D, F);
+      gd.epi.out = WF(WS_YS) + (size_t)si * N * D;
+      gd.epi.ldo = D;
+      gemm(gd, EPI_STORE, false, 0);
+    }
+    // a14-a17: combine, depth-wise LoRA, LTI injection, ACT
+    {
+      TailArgs ta{};
+      ta.x1 = WF(WS_X1);
+      ta.y = WF(WS_Y);
+      ta.inv = WI(WS_INV);
+      ta.gate = WF(WS_GATE);
+      ta.y_s = WF(WS_YS);
+      ta.S = c.n_shared_experts;
+      ta.lora_down = b->lora_down;
+      ta.lora_B = b->lora_B;
+      ta.lora_scale_row = b->lora_scale + (size_t)(t < c.max_loop_iters ? t : c.max_loop_iters - 1) * c.lora_rank;
+      ta.r = c.lora_rank;
+      ta.A = b->A;
+      ta.Bv = b->Bv;
+      ta.e = e;
+      ta.h_prev = hp;
+      ta.h_next = WF(WS_H);
+      ta.halt_w = b->halt_w;
+      ta.halt_b = b->halt_b;
+      ta.act_threshold = thr;
+      ta.h_out = h_out;
+      ta.cum = WF(WS_CUM);
+      ta.halt_counts = halt_counts;
+      ta.t = t;
+      ta.n_loops = n_loops;
+      ta.N = N;
+      ta.D = D;
+      ta.k = k;
+      ta.cap_h = b->cap_h ? b->cap_h + (size_t)t * N * D : nullptr;
+      ta.cap_p = (b->cap_p && thr > 0.f) ? b->cap_p + (size_t)t * N : nullptr;
+      ta.w_bf16 = bf;
+      launch_loop_tail(ta, s);
+    }
+  }
+  hipError_t he = hipGetLastError();
+  if (he != hipSuccess) return fail(RDT_E_HIP, "kernel launch: %s", hipGetErrorString(he));
+  return RDT_OK;
+}
+
+rdt_status rdt_recurrent_forward(rdt_block* b, const float* e, const float* h0, int32_t B, int32_t T,
+                                 int32_t start_pos, int32_t n_loops, float act_threshold, void* kv_cache,
+                                 int32_t kv_capacity, size_t kv_bytes, void* workspace, size_t ws_bytes,
+                                 float* h_out, int32_t* halt_counts, void* stream) {
+  return run(b, e, h0, B, T, start_pos, n_loops, act_threshold, kv_cache, kv_capacity, kv_bytes, workspace,
+             ws_bytes, h_out, halt_counts, stream, false);
+}
+
+rdt_status rdt_decode_step(rdt_block* b, const float* e_new, const float* h0_new, int32_t B, int32_t start_pos,
+                           int32_t n_loops, float act_threshold, void* kv_cache, int32_t kv_capacity,
+                           size_t kv_bytes, void* workspace, size_t ws_bytes, float* h_out, int32_t* halt_counts,
+                           void* stream) {
+  return run(b, e_new, h0_new, B, 1, start_pos, n_loops, act_threshold, kv_cache, kv_capacity, kv_bytes, workspace,
+             ws_bytes, h_out, halt_counts, stream, true);
+}
+
+}  // extern "C"
