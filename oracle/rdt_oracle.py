@@ -249,10 +249,12 @@ def topk_desc_lowest_index(values, k):
 def router(cfg, P, f):
     """Top-k softmax router with a selection-only bias ([ZS §MoE]).
 
-    Returns logits z (float64), the chosen experts, their renormalised
-    gates, and the float64 margin between the k-th and (k+1)-th biased
-    logit.  The choice itself is made on float32 logits + float32 bias, as
-    the kernel makes it.
+    Returns logits z (float64), the chosen experts (an ordered list,
+    largest first), their renormalised gates, and the float64 decision
+    margin: the smallest gap between consecutive values among the k+1
+    largest biased logits, since a near-tie anywhere there (inside the
+    top-k order or at its edge) makes two answers correct.  The choice
+    itself is made on float32 logits + float32 bias, as the kernel makes it.
     """
     k = cfg["top_k"]
     z = f @ P["router_w"].T                                   # [n, E]
@@ -265,7 +267,8 @@ def router(cfg, P, f):
     gate = gate / gate.sum(axis=-1, keepdims=True)
     b64 = z + bias32.astype(np.float64)
     srt = -np.sort(-b64, axis=-1)
-    margin = srt[:, k - 1] - srt[:, k] if k < b64.shape[1] else np.full(len(z), np.inf)
+    top = srt[:, :min(k + 1, b64.shape[1])]
+    margin = np.min(top[:, :-1] - top[:, 1:], axis=-1) if top.shape[1] > 1 else np.full(len(z), np.inf)
     return z, sel, gate, margin
 
 
@@ -392,6 +395,7 @@ class Adoption:
         self.route_disagree = 0
         self.halt_adopted = 0
         self.halt_disagree = 0
+        self.disagree_rows = []     # (loop, row, oracle margin) of route disagreements
 
 
 def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=None,
@@ -419,7 +423,7 @@ def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=
         if adopt is not None and adopt.sel is not None:
             gpu = np.asarray(adopt.sel[t]).reshape(N, -1)
 
-            def hook(sel, margin, rows, gpu=gpu):
+            def hook(sel, margin, rows, gpu=gpu, t=t):
                 out = sel.copy()
                 for n in range(len(rows)):
                     if not np.array_equal(sel[n], gpu[n]):
@@ -428,6 +432,7 @@ def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=
                             adopt.route_adopted += 1
                         else:
                             adopt.route_disagree += 1
+                            adopt.disagree_rows.append((t, n, float(margin[n])))
                 return out
         step = run_loop(cfg, P, h, e, t, start_pos, None if cache is None else cache[t], route_hook=hook)
         h = step["h"].reshape(B, T, D)

@@ -36,12 +36,18 @@ def _e2e(cfg, W, e, h0, **kw):
     print(f"[e2e] {cfg['name']} B={cfg['batch']} T={cfg['seq']} loops={cfg['n_loops']} thr={cfg['act_threshold']}",
           flush=True)
     g = GpuRun(cfg, W, e, h0, **kw).np()
+    N = e.shape[0] * e.shape[1]
     dt = cfg["dtype"]
     adopt = O.Adoption(sel=g["sel"], halt_counts=g["halt"], eps_route=EPS_ROUTE[dt], eps_halt=EPS_HALT[dt])
     ref = O.recurrent_forward(cfg, O.Params(W), e, h0, cfg["n_loops"], cfg["act_threshold"],
                               adopt=adopt, record=True)
     print(f"  adopted route={adopt.route_adopted} halt={adopt.halt_adopted}; "
           f"disagree route={adopt.route_disagree} halt={adopt.halt_disagree}", flush=True)
+    if adopt.disagree_rows:
+        T = e.shape[1]
+        for (t, n, m) in adopt.disagree_rows[:10]:
+            print(f"  disagree loop {t} row {n} (b={n // T}, i={n % T}) margin {m:.3e}: "
+                  f"gpu {g['sel'][t].reshape(N, -1)[n]}", flush=True)
     assert adopt.route_disagree == 0
     assert adopt.halt_disagree == 0
     N = e.shape[0] * e.shape[1]

@@ -143,3 +143,19 @@ def get(name, **overrides):
 
 def tokens_x_loops(cfg):
     return cfg["batch"] * cfg["seq"] * cfg["n_loops"]
+
+
+def _apply_calibration():
+    """mythos_3b's halting-head bias comes from workloads/calibrate_halt.py
+    (an oracle run), stored in calibration.json beside this file."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "calibration.json")
+    if os.path.exists(path):
+        cal = json.load(open(path))
+        for name, vals in cal.items():
+            if name in CONFIGS:
+                CONFIGS[name]["halt_b"] = float(vals["halt_b"])
+
+
+_apply_calibration()
