@@ -1,0 +1,188 @@
+"""Benchmark of the looped Recurrent-Block forward on one MI355X.
+
+Workload (default): the mythos_3b-shaped block, bf16 prefill, batch 2 x
+4096 tokens, 16 loops, ACT at 0.99, synthetic seeded weights and inputs
+(workloads.generate).  A step is one rdt_recurrent_forward call: every loop
+of the whole block over the batch.  Inputs are resident in HBM before the
+timed region.
+
+Prints ONE JSON line: token*loops/s, the roofline of the dominant kernel
+(routed expert gate|up grouped GEMM, timed live with HIP events recorded by
+the library on the launch stream) and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mythos_3b]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "recurrent-block token·loops/sec (1 GPU) + % bf16 MFMA peak / % HBM peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_work(cfg):
+    """Algorithmic flops and bytes of one launch of each stage (per loop)."""
+    B, T, D = cfg["batch"], cfg["seq"], cfg["dim"]
+    N = B * T
+    H, G, dh, E, F, k, S = (cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["n_experts"],
+                            cfg["expert_dim"], cfg["top_k"], cfg["n_shared_experts"])
+    sp = cfg["start_pos"]
+    NK = N * k
+    w = {}
+    w["qkv"] = dict(flops=2.0 * N * D * (H + 2 * G) * dh)
+    w["attention"] = dict(flops=4.0 * B * H * dh * sum(sp + i + 1 for i in range(T)))
+    w["o_proj"] = dict(flops=2.0 * N * D * H * dh)
+    w["router"] = dict(flops=2.0 * N * D * E)
+    w["expert_gate_up"] = dict(flops=2.0 * NK * 2 * F * D, bytes=2.0 * E * 2 * F * D + 2.0 * NK * D + 2.0 * NK * F)
+    w["expert_down"] = dict(flops=2.0 * NK * F * D, bytes=2.0 * E * F * D + 2.0 * NK * F + 4.0 * NK * D)
+    w["shared_gate_up"] = dict(flops=2.0 * N * 2 * F * D * S)
+    w["shared_down"] = dict(flops=2.0 * N * F * D * S)
+    # row-wise kernels: each tensor read / written once at its stored width
+    w["loop_head"] = dict(bytes=N * D * (4 + 4 + 4 + 2))             # h, e in; c fp32, a bf16 out
+    w["ffn_norm"] = dict(bytes=N * D * (4 + 2))                       # x1 in, f out
+    w["tail"] = dict(bytes=N * D * (4 + 4 * k + 4 * S + 4 + 4 + 4 + 4))   # x1, y (k rows), y_s, h, e in; h, h_out
+    return w
+
+
+def cpu_baseline(cfg, W, e, h0, prefix):
+    """The fp64 oracle as it stands, on the first `prefix` tokens of each
+    sequence for one loop (causal attention and per-token routing make this
+    exactly the first rows of the full workload's first loop)."""
+    import numpy as np
+    from oracle import rdt_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    P = O.Params(W)
+    sub = dict(cfg, seq=prefix)
+    t0 = time.perf_counter()
+    O.recurrent_forward(sub, P, e[:, :prefix], h0[:, :prefix], 1, cfg["act_threshold"])
+    dt = time.perf_counter() - t0
+    return dict(value=round(cfg["batch"] * prefix / dt, 3), unit="token·loops/s", cores=cores, kind="oracle",
+                sample=f"1 loop over the first {prefix} tokens of each of the {cfg['batch']} sequences "
+                       f"({cfg['batch'] * prefix} token-loops, {dt:.1f} s)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="mythos_3b")
+    ap.add_argument("--cpu-prefix", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU recurrent-block forward; runs on more than one GPU are not "
+              "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from recurrent_depth_moe_amd import binding
+    from workloads import configs, generate
+
+    cfg = configs.get(args.config)
+    B, T, D, n_loops, thr = cfg["batch"], cfg["seq"], cfg["dim"], cfg["n_loops"], cfg["act_threshold"]
+    t0 = time.time()
+    W = generate.make_weights(cfg)
+    e, h0 = generate.make_inputs(cfg)
+    log(f"[bench] {args.config}: inputs generated in {time.time() - t0:.1f}s")
+    blk = binding.Block(cfg, binding.weights_to_device(W))
+    et = torch.from_numpy(e).cuda()
+    ht = torch.from_numpy(h0).cuda()
+    ws = blk.new_workspace(B, T)
+    h_out = torch.empty_like(et)
+    hc = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    kv = None
+    cap = 0
+    if cfg["use_cache"]:
+        cap = cfg["start_pos"] + T
+        kv = torch.zeros(blk.kv_cache_bytes(B, cap, n_loops), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        blk.forward(et, ht, n_loops, thr, cfg["start_pos"], kv, cap, ws, h_out, hc)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    blk.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stages = blk.read_timing()
+    blk.set_timing(False)
+    log(f"[bench] {args.steps} timed steps in {elapsed:.3f}s")
+
+    halt = hc.cpu().numpy()
+    loops_exec = n_loops          # every loop runs (halting only weights the output)
+    ms_step = elapsed / args.steps * 1e3
+    value = B * T * loops_exec * args.steps / elapsed
+
+    work = stage_work(cfg)
+    kernels = {}
+    for name, (ms, n) in stages.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        ent = dict(avg_ms=round(avg, 4), launches=n, share=round(ms / max(1e-9, sum(v[0] for v in stages.values())), 4))
+        wk = work.get(name, {})
+        if "flops" in wk:
+            ent["tflops"] = round(wk["flops"] / (avg * 1e-3) / 1e12, 2)
+            ent["mfma_frac"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if "bytes" in wk:
+            ent["gbs"] = round(wk["bytes"] / (avg * 1e-3) / 1e9, 1)
+            ent["hbm_frac"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[name] = ent
+    for name, ent in kernels.items():
+        log(f"  {name:16s} {ent}")
+    dom = "expert_gate_up"
+    d = kernels.get(dom, {})
+    roof = dict(kernel="routed expert gate|up grouped GEMM (SwiGLU epilogue)", bound="mfma",
+                achieved=d.get("tflops"), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=d.get("mfma_frac"), traffic=None,
+                per_launch_flops=work[dom]["flops"], avg_launch_ms=d.get("avg_ms"))
+    if thr > 0:
+        hist = np.bincount(halt.ravel(), minlength=n_loops + 1)[1:]
+        log(f"[bench] halt-count histogram (loops 1..{n_loops}): {hist.tolist()}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, W, e, h0, min(args.cpu_prefix, T))
+        log(f"[bench] cpu baseline: {cpu}")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "token·loops/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
+        "data": "synthetic (seeded N(0,0.02) weights, RMS-normalised N(0,1) inputs)",
+        "config": {"workload": f"{args.config}-shaped recurrent block, {cfg['dtype']} "
+                               f"{'decode' if cfg['use_cache'] else 'prefill'}, batch {B} x seq {T}, "
+                               f"{n_loops} loops, ACT {'off' if thr == 0 else thr}",
+                   "dim": D, "heads": cfg["n_heads"], "kv_heads": cfg["n_kv_heads"], "experts": cfg["n_experts"],
+                   "expert_dim": cfg["expert_dim"], "top_k": cfg["top_k"], "loops_executed": loops_exec},
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -182,6 +182,19 @@ rdt_status rdt_set_capture(rdt_block* blk, float* h_loops, int32_t* sel_loops, f
 rdt_status rdt_workspace_offset(const rdt_block* blk, int32_t B, int32_t T, const char* name,
                                 size_t* offset, size_t* bytes);
 
+/* Per-stage kernel timing with HIP events recorded on the call's stream
+ * around each stage's launches (for benchmarks; off by default, and a small
+ * host-side cost per launch when on).  rdt_set_timing(1) clears the totals;
+ * rdt_read_timing waits for the recorded events and returns, per stage, the
+ * summed milliseconds and the number of timed launches since then. */
+enum rdt_stage {
+  RDT_STAGE_LOOP_HEAD = 0, RDT_STAGE_QKV, RDT_STAGE_ATTN, RDT_STAGE_OPROJ, RDT_STAGE_FFN_NORM,
+  RDT_STAGE_ROUTER, RDT_STAGE_DISPATCH, RDT_STAGE_EXPERT_GATEUP, RDT_STAGE_EXPERT_DOWN,
+  RDT_STAGE_SHARED_GATEUP, RDT_STAGE_SHARED_DOWN, RDT_STAGE_TAIL, RDT_STAGE_COUNT
+};
+rdt_status rdt_set_timing(rdt_block* blk, int32_t enable);
+rdt_status rdt_read_timing(rdt_block* blk, double* total_ms, int64_t* launches);
+
 /* Host-only variants that take the configuration instead of a handle, so a
  * caller can size buffers (and tests can check arguments) before any device
  * work.  rdt_check_config validates a configuration; rdt_check_call returns

@@ -19,6 +19,9 @@ RDT_ATTN_GQA, RDT_ATTN_MLA = 0, 1
 STATUS = {0: "RDT_OK", 1: "RDT_E_INVALID_ARG", 2: "RDT_E_UNSUPPORTED", 3: "RDT_E_OUT_OF_MEMORY",
           4: "RDT_E_HIP", 5: "RDT_E_BAD_STATE", 6: "RDT_E_WORKSPACE_TOO_SMALL"}
 
+STAGES = ["loop_head", "qkv", "attention", "o_proj", "ffn_norm", "router", "dispatch", "expert_gate_up",
+          "expert_down", "shared_gate_up", "shared_down", "tail"]
+
 WEIGHT_NAMES = ["g_rec", "g_attn", "g_ffn", "wq", "wk", "wv", "wo", "wdq", "gq", "wuq", "wdkv", "gkv", "wukv",
                 "router_w", "router_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
                 "lora_down", "lora_B", "lora_scale", "log_A", "log_dt", "B", "halt_w", "halt_b"]
@@ -72,6 +75,8 @@ def lib():
         "rdt_decode_step": ([vp, vp, vp, i32, i32, i32, f32, vp, i32, sz, vp, sz, vp, vp, vp], i32),
         "rdt_get_A": ([vp, vp], i32),
         "rdt_set_capture": ([vp, vp, vp, vp, i32], i32),
+        "rdt_set_timing": ([vp, i32], i32),
+        "rdt_read_timing": ([vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -189,6 +194,16 @@ class Block:
     def set_capture(self, h_loops=None, sel_loops=None, p_loops=None, max_loops=0):
         check(lib().rdt_set_capture(self._h, _ptr(h_loops), _ptr(sel_loops), _ptr(p_loops), max_loops))
         self._capture = (h_loops, sel_loops, p_loops)
+
+    def set_timing(self, enable=True):
+        check(lib().rdt_set_timing(self._h, 1 if enable else 0))
+
+    def read_timing(self):
+        """{stage: (total_ms, launches)} since set_timing(True)."""
+        ms = (ctypes.c_double * len(STAGES))()
+        n = (ctypes.c_int64 * len(STAGES))()
+        check(lib().rdt_read_timing(self._h, ms, n))
+        return {st: (ms[i], n[i]) for i, st in enumerate(STAGES)}
 
     def forward(self, e, h0, n_loops, act_threshold, start_pos=0, kv_cache=None, kv_capacity=0,
                 workspace=None, h_out=None, halt_counts=None, stream=None):

@@ -8,6 +8,7 @@ typedef uint16_t bf16_t;  // bfloat16 storage (bit pattern)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 #define RDT_WAVE 64
 #define RDT_NUM_XCD 8

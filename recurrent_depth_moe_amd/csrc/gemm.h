@@ -54,9 +54,13 @@ struct GemmParams {
 // Launch helpers (stream-ordered, no sync).  `bm` selects the m-tile height
 // that the grouped schedule was built for.
 void launch_gemm_bf16(const GemmParams& p, int epi, bool dual, int bm, int out_is_bf16, int n_cu, hipStream_t s);
+// 256x256 tiles, direct-to-LDS loads; K must be a multiple of 64 and a
+// grouped schedule must be built with m-tile height RDT_BM_BIG
+void launch_gemm_bf16_big(const GemmParams& p, int epi, bool dual, int out_is_bf16, int n_cu, hipStream_t s);
 void launch_gemm_f32(const GemmParams& p, int epi, bool dual, int n_cu, hipStream_t s);
 
 // m-tile heights the kernels are built with (the dispatch builds schedules
 // for exactly these)
 #define RDT_BM_LARGE 128
+#define RDT_BM_BIG 256
 #define RDT_BM_F32 64

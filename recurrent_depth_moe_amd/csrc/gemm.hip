@@ -2,103 +2,18 @@
 //
 // bf16 path: 128x128x64 block tiles (or 128x64 per matrix for the fused
 // gate|up product), four wave64s in 2x2, v_mfma_f32_16x16x32_bf16 with fp32
-// accumulation, double-buffered LDS with an XOR swizzle of 16-byte chunks so
-// the fragment reads of 16 consecutive rows land in distinct banks.
+// accumulation, double-buffered LDS with an XOR swizzle of the 16-byte
+// chunks of each 128-byte row (chunk ^ ((row >> 1) & 7)) so the fragment
+// reads of 16 consecutive rows land in distinct banks.
 // fp32 path (fp32 configs): 64x64x16 tiles, 4x4 fp32 FMA micro-tiles.
 //
 // Both run a persistent, XCD-aware tile loop: the tile list is cut into
 // eight contiguous chunks, one per XCD (workgroup i runs on XCD i % 8), so
 // the m-tiles that share an expert's weight panel, and the n-tiles that
 // share a group's activation rows, meet in the same L2.
-#include "gemm.h"
+#include "gemm_device.h"
 
 namespace {
-
-template <int EPI, typename TO>
-__device__ __forceinline__ void epi_store(const EpiParams& e, int m, int n, float v, float v2) {
-  if constexpr (EPI == EPI_STORE) {
-    St<TO>::st((TO*)e.out + (int64_t)m * e.ldo + n, v);
-  } else if constexpr (EPI == EPI_RESID) {
-    const int64_t i = (int64_t)m * e.ldo + n;
-    ((float*)e.out)[i] = e.resid[i] + v;
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    St<TO>::st((TO*)e.out + (int64_t)m * e.ldo + n, silu_f(v) * v2);
-  } else if constexpr (EPI == EPI_QKV) {
-    const int b = m / e.T, i = m - b * e.T;
-    const int hq = e.H * e.dq, hk = e.G * e.dq;
-    if (n < hq + hk) {
-      // adjacent channels (2j, 2j+1) are one complex number; v2 holds the
-      // other member of the pair
-      const int d = n % e.dq;
-      const int64_t ti = (int64_t)(e.start_pos + i) * e.rot_half + (d >> 1);
-      const float c = e.rcos[ti], s = e.rsin[ti];
-      const float r = (d & 1) ? (v2 * s + v * c) : (v * c - v2 * s);
-      if (n < hq) {
-        const int h = n / e.dq;
-        St<TO>::st((TO*)e.q + (((int64_t)(b * e.H + h) * e.T + i) * e.dq + d), r);
-      } else {
-        const int g = (n - hq) / e.dq;
-        St<TO>::st((TO*)e.k + (((int64_t)(b * e.G + g) * e.cap + e.kbase + i) * e.dq + d), r);
-      }
-    } else {
-      const int nn = n - hq - hk, g = nn / e.dv, d = nn - g * e.dv;
-      St<TO>::st((TO*)e.vt + (((int64_t)(b * e.G + g) * e.dv + d) * e.cap + e.kbase + i), v);
-    }
-  } else if constexpr (EPI == EPI_MLA_Q) {
-    const int b = m / e.T, i = m - b * e.T;
-    const int h = n / e.dq, d = n - h * e.dq;
-    float r = v;
-    if (d >= e.nope) {
-      const int64_t ti = (int64_t)(e.start_pos + i) * e.rot_half + ((d - e.nope) >> 1);
-      const float c = e.rcos[ti], s = e.rsin[ti];
-      r = ((d - e.nope) & 1) ? (v2 * s + v * c) : (v * c - v2 * s);
-    }
-    St<TO>::st((TO*)e.q + (((int64_t)(b * e.H + h) * e.T + i) * e.dq + d), r);
-  } else if constexpr (EPI == EPI_MLA_KV) {
-    const int b = m / e.T, j = m - b * e.T;
-    const int w = e.nope + e.dv, h = n / w, d = n - h * w;
-    if (d < e.nope)
-      St<TO>::st((TO*)e.k + (((int64_t)(b * e.H + h) * e.cap + j) * e.dq + d), v);
-    else
-      St<TO>::st((TO*)e.vt + (((int64_t)(b * e.H + h) * e.dv + (d - e.nope)) * e.cap + j), v);
-  }
-}
-
-// Tile index -> (m-tile, n-tile).  Grouped: groups in order, inside a group
-// the n-tile is the slow index, so the m-tiles that share a weight panel are
-// consecutive.  Dense: raster groups of `dense_gm` m-tiles.
-__device__ __forceinline__ void tile_coords(const GemmParams& p, int L, int ntn, int n_mt, int& mt, int& nt) {
-  if (p.mt_start) {
-    int lo = 0, hi = p.n_groups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.mt_start[mid] * ntn <= L) lo = mid; else hi = mid - 1;
-    }
-    const int s0 = p.mt_start[lo], ne = p.mt_start[lo + 1] - s0;
-    const int local = L - s0 * ntn;
-    nt = local / ne;
-    mt = s0 + (local - nt * ne);
-  } else {
-    const int GM = p.dense_gm;
-    const int mt0 = (L / (GM * ntn)) * GM;
-    const int gm = min(GM, n_mt - mt0);
-    const int local = L - mt0 * ntn;
-    nt = local / gm;
-    mt = mt0 + (local - nt * gm);
-  }
-}
-
-__device__ __forceinline__ void tile_rows(const GemmParams& p, int mt, int bm, int& row0, int& rows, int& grp) {
-  if (p.mt_start) {
-    grp = p.tile_grp[mt];
-    row0 = p.tile_row0[mt];
-    rows = min(bm, p.grp_end[grp + 1] - row0);
-  } else {
-    grp = 0;
-    row0 = mt * bm;
-    rows = min(bm, p.M - row0);
-  }
-}
 
 // ------------------------------------------------------------ bf16 MFMA
 
@@ -180,13 +95,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < A_LD; ++j) {
         const int idx = tid + j * 256, r = idx >> 3, c = idx & 7;
-        sA[buf][r * 8 + (c ^ (r & 7))] = ra[j];
+        sA[buf][r * 8 + (c ^ ((r >> 1) & 7))] = ra[j];
       }
 #pragma unroll
       for (int j = 0; j < B_LD; ++j) {
         const int idx = tid + j * 256, r = idx >> 3, c = idx & 7;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) sB[buf][b][r * 8 + (c ^ (r & 7))] = rb[b][j];
+        for (int b = 0; b < NB; ++b) sB[buf][b][r * 8 + (c ^ ((r >> 1) & 7))] = rb[b][j];
       }
     };
 
@@ -204,14 +119,14 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int r = wm * WM + i * 16 + (lane & 15);
-          af[i] = __builtin_bit_cast(bf16x8_t, sA[buf][r * 8 + (c ^ (r & 7))]);
+          af[i] = __builtin_bit_cast(bf16x8_t, sA[buf][r * 8 + (c ^ ((r >> 1) & 7))]);
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const int r = wn * WN + j * 16 + (lane & 15);
-            bfr[b][j] = __builtin_bit_cast(bf16x8_t, sB[buf][b][r * 8 + (c ^ (r & 7))]);
+            bfr[b][j] = __builtin_bit_cast(bf16x8_t, sB[buf][b][r * 8 + (c ^ ((r >> 1) & 7))]);
           }
 #pragma unroll
         for (int b = 0; b < NB; ++b)

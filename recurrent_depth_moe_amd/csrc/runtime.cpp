@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/rdt.h"
 #include "attention.h"
@@ -77,7 +78,7 @@ rdt_status check_config(const rdt_config* c) {
   if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts) return fail(RDT_E_INVALID_ARG, "top_k must be in [1, min(8, n_experts)]");
   if (c->n_shared_experts < 0 || c->n_shared_experts > 8) return fail(RDT_E_INVALID_ARG, "n_shared_experts");
   if (c->expert_dim < 4) return fail(RDT_E_INVALID_ARG, "expert_dim");
-  const int kmul = c->weight_dtype == RDT_BF16 ? 8 : 4;
+  const int kmul = c->weight_dtype == RDT_BF16 ? 64 : 4;
   if (c->dim % kmul || c->expert_dim % kmul)
     return fail(RDT_E_UNSUPPORTED, "dim and expert_dim must be multiples of %d", kmul);
   if (c->lora_rank < 1 || c->lora_rank > RDT_MAX_LORA) return fail(RDT_E_INVALID_ARG, "lora_rank must be in [1, %d]", RDT_MAX_LORA);
@@ -107,7 +108,12 @@ struct Plan {
   size_t off[WS_COUNT], size[WS_COUNT], total;
 };
 
-int bm_for(const rdt_config& c) { return c.weight_dtype == RDT_BF16 ? RDT_BM_LARGE : RDT_BM_F32; }
+// m-tile height of the routed-expert schedule: the 256-row kernel for bf16
+// prefill, the 128-row kernel for single-token steps, 64 for fp32
+int bm_for(const rdt_config& c, int T) {
+  if (c.weight_dtype != RDT_BF16) return RDT_BM_F32;
+  return T > 1 ? RDT_BM_BIG : RDT_BM_LARGE;
+}
 
 Plan make_plan(const rdt_config& c, int B, int T) {
   Plan p{};
@@ -117,7 +123,7 @@ Plan make_plan(const rdt_config& c, int B, int T) {
   p.NK = p.N * c.top_k;
   p.kvcap = round_up(T, 64);
   p.kvlen_max = c.max_seq_len;
-  p.bm = bm_for(c);
+  p.bm = bm_for(c, T);
   p.max_mt = (p.NK + p.bm - 1) / p.bm + c.n_experts;
   p.disp_tiles = (p.NK + RDT_DISP_TILE - 1) / RDT_DISP_TILE;
   const size_t es = esize(c), D = c.dim, N = p.N, NK = p.NK, F = c.expert_dim, E = c.n_experts;
@@ -225,7 +231,48 @@ struct rdt_block {
   int32_t* cap_sel = nullptr;
   float* cap_p = nullptr;
   int cap_loops = 0;
+  // stage timing
+  bool timing = false;
+  struct Pending {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> free_events;
+  double stage_ms[RDT_STAGE_COUNT] = {0};
+  int64_t stage_n[RDT_STAGE_COUNT] = {0};
 };
+
+namespace {
+
+hipEvent_t take_event(rdt_block* b) {
+  if (!b->free_events.empty()) {
+    hipEvent_t e = b->free_events.back();
+    b->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one stage's launches with events on the stream when timing is on.
+struct StageTimer {
+  rdt_block* b;
+  hipStream_t s;
+  int stage;
+  hipEvent_t a = nullptr;
+  StageTimer(rdt_block* b_, hipStream_t s_, int st) : b(b_), s(s_), stage(st) {
+    if (b->timing && (a = take_event(b)) != nullptr && hipEventRecord(a, s) != hipSuccess) a = nullptr;
+  }
+  ~StageTimer() {
+    if (!a) return;
+    hipEvent_t e = take_event(b);
+    if (e && hipEventRecord(e, s) == hipSuccess) b->pending.push_back({stage, a, e});
+  }
+};
+
+}  // namespace
 
 namespace {
 
@@ -471,6 +518,11 @@ rdt_status rdt_block_create(const rdt_config* cfg, const void* const* weights, v
 rdt_status rdt_block_destroy(rdt_block* b) {
   if (!b) return RDT_OK;
   hipError_t he = hipDeviceSynchronize();
+  for (auto& p : b->pending) {
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
+  }
+  for (auto e : b->free_events) (void)hipEventDestroy(e);
   if (b->mem) (void)hipFree(b->mem);
   delete b;
   if (he != hipSuccess) return fail(RDT_E_HIP, "destroy: %s", hipGetErrorString(he));
@@ -515,6 +567,40 @@ rdt_status rdt_set_capture(rdt_block* b, float* h_loops, int32_t* sel_loops, flo
   return RDT_OK;
 }
 
+rdt_status rdt_set_timing(rdt_block* b, int32_t enable) {
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  b->timing = enable != 0;
+  for (int i = 0; i < RDT_STAGE_COUNT; ++i) {
+    b->stage_ms[i] = 0.0;
+    b->stage_n[i] = 0;
+  }
+  for (auto& p : b->pending) {
+    b->free_events.push_back(p.a);
+    b->free_events.push_back(p.b);
+  }
+  b->pending.clear();
+  return RDT_OK;
+}
+
+rdt_status rdt_read_timing(rdt_block* b, double* total_ms, int64_t* launches) {
+  if (!b || !total_ms || !launches) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  for (auto& p : b->pending) {
+    HIP_TRY(hipEventSynchronize(p.b));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, p.a, p.b));
+    b->stage_ms[p.stage] += ms;
+    b->stage_n[p.stage] += 1;
+    b->free_events.push_back(p.a);
+    b->free_events.push_back(p.b);
+  }
+  b->pending.clear();
+  for (int i = 0; i < RDT_STAGE_COUNT; ++i) {
+    total_ms[i] = b->stage_ms[i];
+    launches[i] = b->stage_n[i];
+  }
+  return RDT_OK;
+}
+
 static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int T, int start_pos, int n_loops,
                       float thr, void* kv, int kv_capacity, size_t kv_bytes, void* ws, size_t ws_bytes,
                       float* h_out, int32_t* halt_counts, void* stream, bool decode) {
@@ -540,9 +626,17 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   const size_t slot = kv ? kv_slot_bytes(c, B, kv_capacity) : 0;
   const float scale = 1.0f / sqrtf((float)dq);
 
+  // bf16: the 256x256 kernel for wide products in prefill, the 128x128
+  // kernel for narrow outputs (router) and single-token steps
   auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16) {
-    if (bf) launch_gemm_bf16(gp, epi, dual, p.bm, out_bf16, b->n_cu, s);
-    else launch_gemm_f32(gp, epi, dual, b->n_cu, s);
+    if (!bf) {
+      launch_gemm_f32(gp, epi, dual, b->n_cu, s);
+      return;
+    }
+    const bool grouped = gp.mt_start != nullptr;
+    const bool big = grouped ? p.bm == RDT_BM_BIG : (T > 1 && gp.N > 128);
+    if (big) launch_gemm_bf16_big(gp, epi, dual, out_bf16, b->n_cu, s);
+    else launch_gemm_bf16(gp, epi, dual, RDT_BM_LARGE, out_bf16, b->n_cu, s);
   };
   auto dense = [&](const void* A, int64_t lda, const void* W0, const void* W1, int M, int Nn, int K) {
     GemmParams gp{};
@@ -560,8 +654,11 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   for (int t = 0; t < n_loops; ++t) {
     const float* hp = t == 0 ? h0 : WF(WS_H);
     // a1-a3: loop-index embedding, re-injection of e, RMSNorms
-    launch_loop_head(bf, hp, e, b->loop_emb + (size_t)t * c.loop_dim, c.loop_dim, b->g_rec, b->g_attn, c.norm_eps,
+    {
+      StageTimer st_(b, s, RDT_STAGE_LOOP_HEAD);
+      launch_loop_head(bf, hp, e, b->loop_emb + (size_t)t * c.loop_dim, c.loop_dim, b->g_rec, b->g_attn, c.norm_eps,
                      WF(WS_C), W(WS_A), N, D, s);
+    }
     // a4-a6: attention
     char* kslot = kv ? (char*)kv + slot * t : nullptr;
     if (is_gqa(c)) {
@@ -585,12 +682,17 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       ep.rcos = b->rope_cos;
       ep.rsin = b->rope_sin;
       ep.rot_half = dq / 2;
-      gemm(gp, EPI_QKV, false, bf);
+      {
+        StageTimer st_(b, s, RDT_STAGE_QKV);
+        gemm(gp, EPI_QKV, false, bf);
+      }
+      StageTimer st_(b, s, RDT_STAGE_ATTN);
       if (bf && T > 1)
         launch_attn_flash_bf16(W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, kbase, scale, s);
       else
         launch_attn_generic(bf, W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, dq, dv, kbase, scale, s);
     } else {
+      StageTimer st_(b, s, RDT_STAGE_ATTN);
       const int ql = c.q_lora_rank, kvl = c.kv_lora_rank, rope = c.qk_rope_head_dim, nope = c.qk_nope_head_dim;
       const int lat_cap = kv ? cap_pad : T;
       const int kbase = kv ? start_pos : 0;
@@ -634,6 +736,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     }
     // a7: x1 = c + o Wo^T
     {
+      StageTimer st_(b, s, RDT_STAGE_OPROJ);
       GemmParams gp = dense(W(WS_O), (int64_t)H * dv, b->wo, nullptr, N, D, H * dv);
       gp.epi.out = W(WS_X1);
       gp.epi.ldo = D;
@@ -641,9 +744,13 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gemm(gp, EPI_RESID, false, 0);
     }
     // a8: f = RMSNorm(x1) * g_ffn
-    launch_rmsnorm(bf, WF(WS_X1), D, b->g_ffn, c.norm_eps, W(WS_F), D, N, D, s);
+    {
+      StageTimer st_(b, s, RDT_STAGE_FFN_NORM);
+      launch_rmsnorm(bf, WF(WS_X1), D, b->g_ffn, c.norm_eps, W(WS_F), D, N, D, s);
+    }
     // a9: router logits, softmax, top-k
     {
+      StageTimer st_(b, s, RDT_STAGE_ROUTER);
       GemmParams gp = dense(W(WS_F), D, b->router, nullptr, N, E, D);
       gp.epi.out = W(WS_LOGITS);
       gp.epi.ldo = E;
@@ -652,8 +759,11 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
                          b->cap_sel ? b->cap_sel + (size_t)t * N * k : nullptr, s);
     }
     // a10: dispatch
-    launch_dispatch(WI(WS_SEL), p.NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART), WI(WS_TROW0),
-                    WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), s);
+    {
+      StageTimer st_(b, s, RDT_STAGE_DISPATCH);
+      launch_dispatch(WI(WS_SEL), p.NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART),
+                      WI(WS_TROW0), WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), s);
+    }
     // a11: routed gate|up + SwiGLU, rows gathered from f
     {
       GemmParams gp{};
@@ -673,7 +783,10 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gp.n_groups = E;
       gp.epi.out = W(WS_ACT);
       gp.epi.ldo = F;
-      gemm(gp, EPI_SWIGLU, true, bf);
+      {
+        StageTimer st_(b, s, RDT_STAGE_EXPERT_GATEUP);
+        gemm(gp, EPI_SWIGLU, true, bf);
+      }
       // a12: routed down
       GemmParams gd = gp;
       gd.A = W(WS_ACT);
@@ -687,6 +800,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gd.epi = EpiParams{};
       gd.epi.out = W(WS_Y);
       gd.epi.ldo = D;
+      StageTimer st_(b, s, RDT_STAGE_EXPERT_DOWN);
       gemm(gd, EPI_STORE, false, 0);
     }
     // a13: shared experts on every row
@@ -695,10 +809,14 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
                             (const char*)b->s_up + (size_t)si * F * D * es, N, F, D);
       gp.epi.out = W(WS_ACTS);
       gp.epi.ldo = F;
-      gemm(gp, EPI_SWIGLU, true, bf);
+      {
+        StageTimer st_(b, s, RDT_STAGE_SHARED_GATEUP);
+        gemm(gp, EPI_SWIGLU, true, bf);
+      }
       GemmParams gd = dense(W(WS_ACTS), F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, N, D, F);
       gd.epi.out = WF(WS_YS) + (size_t)si * N * D;
       gd.epi.ldo = D;
+      StageTimer st_(b, s, RDT_STAGE_SHARED_DOWN);
       gemm(gd, EPI_STORE, false, 0);
     }
     // a14-a17: combine, depth-wise LoRA, LTI injection, ACT
@@ -733,6 +851,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       ta.cap_h = b->cap_h ? b->cap_h + (size_t)t * N * D : nullptr;
       ta.cap_p = (b->cap_p && thr > 0.f) ? b->cap_p + (size_t)t * N : nullptr;
       ta.w_bf16 = bf;
+      StageTimer st_(b, s, RDT_STAGE_TAIL);
       launch_loop_tail(ta, s);
     }
   }
