@@ -179,21 +179,25 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    // masked scores are -inf: with a finite reference they give exp2 = 0;
+    // a row with nothing visible yet uses reference 0 so no NaN appears
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float psum = 0.f;
     bf16x8_t pf[4];   // key steps of 16: (kb2, elements 0..7) and (kb2, 8..15)
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        bf16_t pv[8];
+        float p[8];
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
-          const float p = (m_new == -INFINITY) ? 0.f : exp2f(s[kb2][hh * 8 + x] - m_new);
-          psum += p;
-          pv[x] = f2bf(p);
+          p[x] = __builtin_amdgcn_exp2f(s[kb2][hh * 8 + x] - m_use);
+          psum += p[x];
         }
-        pf[kb2 * 2 + hh] = __builtin_bit_cast(bf16x8_t, *(const uint4*)pv);
+        const uint4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                          pack_bf16x2(p[6], p[7])};
+        pf[kb2 * 2 + hh] = __builtin_bit_cast(bf16x8_t, pk);
       }
     psum += __shfl_xor(psum, 32, 64);
     l_run = l_run * alpha + psum;
@@ -234,10 +238,9 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        bf16_t ov[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ov[r] = f2bf(oacc[db][e4 * 4 + r] * inv);
-        *(uint2*)(orow + db * 32 + 8 * e4 + 4 * half) = *(const uint2*)ov;
+        const uint2 ov = {pack_bf16x2(oacc[db][e4 * 4] * inv, oacc[db][e4 * 4 + 1] * inv),
+                          pack_bf16x2(oacc[db][e4 * 4 + 2] * inv, oacc[db][e4 * 4 + 3] * inv)};
+        *(uint2*)(orow + db * 32 + 8 * e4 + 4 * half) = ov;
       }
   }
 }

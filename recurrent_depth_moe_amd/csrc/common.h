@@ -15,12 +15,14 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Round-to-nearest-even float -> bfloat16; NaN stays NaN (quiet bit set).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  return (bf16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+// two floats -> two packed bfloat16 (low half = a), round to nearest even,
+// NaN stays NaN: the gfx950 conversion instruction v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2_t));
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
 // Storage-type traits: activations are float (fp32 configs) or bf16.
 template <typename T> struct St;

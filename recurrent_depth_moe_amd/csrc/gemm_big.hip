@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
           __builtin_amdgcn_wave_barrier();
           if constexpr (DUAL) {
             // 64 output columns: gate at patch columns 0..63, up at 64..127
-#pragma unroll
+#pragma unroll 1
             for (int it = 0; it < 4; ++it) {
               const int rl = it * 8 + (lane >> 3), c8 = (lane & 7) * 8;
               const int ml = wm * WTM + pass * 32 + rl;
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
               if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + wn * 64 + c8, g, u);
             }
           } else {
-#pragma unroll
+#pragma unroll 1
             for (int it = 0; it < 8; ++it) {
               const int rl = it * 4 + (lane >> 4), c8 = (lane & 15) * 8;
               const int ml = wm * WTM + pass * 32 + rl;

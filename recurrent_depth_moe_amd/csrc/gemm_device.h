@@ -97,11 +97,8 @@ static __device__ __forceinline__ void tile_rows(const GemmParams& p, int mt, in
 template <int EPI, typename TO>
 static __device__ __forceinline__ void store8(TO* p, const float* v) {
   if constexpr (sizeof(TO) == 2) {
-    uint4 u;
-    u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-    u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-    u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+    const uint4 u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7])};
     *(uint4*)p = u;
   } else {
     *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);

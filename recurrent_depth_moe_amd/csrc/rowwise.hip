@@ -21,9 +21,7 @@ __device__ __forceinline__ float4 ld4(const bf16_t* p) {
 }
 __device__ __forceinline__ void st4(float* p, float4 v) { *(float4*)p = v; }
 __device__ __forceinline__ void st4(bf16_t* p, float4 v) {
-  uint2 u;
-  u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
-  u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+  const uint2 u = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
   *(uint2*)p = u;
 }
 __device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
@@ -436,6 +434,175 @@ __global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
   }
 }
 
+// Same step for R rows per block: the LoRA matrices (r x D each) are read
+// once per block instead of once per row, which is what bounds the one-row
+// form (2 r D bytes of L2 traffic per row).  Thread t owns float4 column t
+// (+256 j) of every row.
+template <typename TW, int R, int NJ, int LR>
+__global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
+  __shared__ float red[RB / 64][LR * R + R];
+  const int n0 = blockIdx.x * R, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int D = a.D, D4 = D >> 2;
+  const TW* Wd = (const TW*)a.lora_down;
+  const TW* Wb = (const TW*)a.lora_B;
+  float4 tau[R][NJ];
+  float part[LR][R];
+#pragma unroll
+  for (int r = 0; r < LR; ++r)
+#pragma unroll
+    for (int i = 0; i < R; ++i) part[r][i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int n = n0 + i;
+    int drow[8];
+    float gw[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < a.k) {
+        drow[s] = a.inv[(int64_t)n * a.k + s];
+        gw[s] = a.gate[(int64_t)n * a.k + s];
+      }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int i4 = threadIdx.x + j * RB;
+      if (i4 < D4) {
+        const int d = i4 * 4;
+        float4 x = ld4(a.x1 + (int64_t)n * D + d);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          if (s < a.k) x = fma4(gw[s], ld4(a.y + (int64_t)drow[s] * D + d), x);
+        for (int s = 0; s < a.S; ++s) {
+          const float4 ys = ld4(a.y_s + ((int64_t)s * a.N + n) * D + d);
+          x.x += ys.x; x.y += ys.y; x.z += ys.z; x.w += ys.w;
+        }
+        tau[i][j] = x;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (i4 < D4) {
+#pragma unroll
+      for (int r = 0; r < LR; ++r)
+        if (r < a.r) {
+          const float4 wv = ld4(Wd + (int64_t)r * D + i4 * 4);
+#pragma unroll
+          for (int i = 0; i < R; ++i) part[r][i] += dot4(tau[i][j], wv);
+        }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < LR; ++r)
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (r < a.r) {
+        const float v = wave_sum(part[r][i]);
+        if (lane == 0) red[w][r * R + i] = v;
+      }
+  __syncthreads();
+  float lo[LR][R];
+#pragma unroll
+  for (int r = 0; r < LR; ++r)
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float v = 0.f;
+      if (r < a.r) {
+        for (int ww = 0; ww < RB / 64; ++ww) v += red[ww][r * R + i];
+        v *= a.lora_scale_row[r];
+      }
+      lo[r][i] = v;
+    }
+  float zs[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) zs[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (i4 < D4) {
+      const int d = i4 * 4;
+#pragma unroll
+      for (int r = 0; r < LR; ++r)
+        if (r < a.r) {
+          const float4 bv = ld4(Wb + (int64_t)r * D + d);
+#pragma unroll
+          for (int i = 0; i < R; ++i) tau[i][j] = fma4(lo[r][i], bv, tau[i][j]);
+        }
+      const float4 A = ld4(a.A + d), Bv = ld4(a.Bv + d), hw = ld4(a.halt_w + d);
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int64_t off = (int64_t)(n0 + i) * D + d;
+        const float4 hp = ld4(a.h_prev + off), ee = ld4(a.e + off), x = tau[i][j];
+        float4 hn;
+        hn.x = A.x * hp.x + Bv.x * ee.x + x.x;
+        hn.y = A.y * hp.y + Bv.y * ee.y + x.y;
+        hn.z = A.z * hp.z + Bv.z * ee.z + x.z;
+        hn.w = A.w * hp.w + Bv.w * ee.w + x.w;
+        tau[i][j] = hn;
+        st4(a.h_next + off, hn);
+        if (a.cap_h) st4(a.cap_h + off, hn);
+        zs[i] += dot4(hn, hw);
+      }
+    }
+  }
+  const bool act = a.act_threshold > 0.f;
+  const bool last = a.t == a.n_loops - 1;
+  if (!act) {
+    if (last) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int i4 = threadIdx.x + j * RB;
+          if (i4 < D4) st4(a.h_out + (int64_t)(n0 + i) * D + i4 * 4, tau[i][j]);
+        }
+    }
+    if (threadIdx.x < R) a.halt_counts[n0 + threadIdx.x] = a.t + 1;
+    return;
+  }
+  __syncthreads();   // red reused
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const float v = wave_sum(zs[i]);
+    if (lane == 0) red[w][LR * R + i] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int n = n0 + i;
+    float z = a.halt_b[0];
+    for (int ww = 0; ww < RB / 64; ++ww) z += red[ww][LR * R + i];
+    const float p = sigmoid_f(z);
+    const float cum = a.t == 0 ? 0.f : a.cum[n];
+    const int hc = a.t == 0 ? 0 : a.halt_counts[n];
+    const bool running = hc == 0;
+    float wgt = 0.f;
+    bool halt_now = false;
+    if (running) {
+      const float sum = cum + p;
+      halt_now = (sum >= a.act_threshold) || last;
+      wgt = halt_now ? fmaxf(1.0f - cum, 0.f) : p;
+    }
+    if (a.t == 0 || running) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int i4 = threadIdx.x + j * RB;
+        if (i4 < D4) {
+          const int64_t off = (int64_t)n * D + i4 * 4;
+          const float4 prev = a.t == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : ld4(a.h_out + off);
+          st4(a.h_out + off, fma4(wgt, tau[i][j], prev));
+        }
+      }
+    }
+    __syncthreads();   // every thread has read cum / halt_counts of row n
+    if (threadIdx.x == 0) {
+      a.cum[n] = running ? cum + p : cum;
+      a.halt_counts[n] = halt_now ? a.t + 1 : hc;
+      if (a.cap_p) a.cap_p[n] = p;
+    }
+  }
+}
+
 // ------------------------------------------------------------ MLA glue
 // [ZS §MLA]: the kv down-projection splits into the latent c_kv and one
 // shared k_rope, which is rotated; both are what the cache holds.  The q
@@ -535,7 +702,26 @@ void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* 
   dispatch_scatter_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, k, E, tile_counts, perm_src, inv);
 }
 
+template <typename TW, int LR>
+static void launch_tail_rows(const TailArgs& a, int nj, hipStream_t s) {
+  constexpr int R = 4;
+  const int grid = a.N / R;
+  switch (nj) {
+    case 1: loop_tail_rows_kernel<TW, R, 1, LR><<<grid, RB, 0, s>>>(a); break;
+    case 2: loop_tail_rows_kernel<TW, R, 2, LR><<<grid, RB, 0, s>>>(a); break;
+    case 3: loop_tail_rows_kernel<TW, R, 3, LR><<<grid, RB, 0, s>>>(a); break;
+    default: loop_tail_rows_kernel<TW, R, 4, LR><<<grid, RB, 0, s>>>(a); break;
+  }
+}
+
 void launch_loop_tail(const TailArgs& a, hipStream_t s) {
+  // R-row blocks when the rows split evenly, D <= 4096 and rank <= 16
+  const int nj = (a.D / 4 + RB - 1) / RB;
+  if (a.N % 4 == 0 && nj <= 4 && a.r <= 16) {
+    if (a.w_bf16) launch_tail_rows<bf16_t, 16>(a, nj, s);
+    else launch_tail_rows<float, 16>(a, nj, s);
+    return;
+  }
   if (a.w_bf16) loop_tail_kernel<bf16_t><<<a.N, RB, 0, s>>>(a);
   else loop_tail_kernel<float><<<a.N, RB, 0, s>>>(a);
 }
