@@ -79,9 +79,21 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="mythos_3b")
-    ap.add_argument("--cpu-prefix", type=int, default=256)
+    ap.add_argument("--cpu-prefix", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run plain device copies of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        import torch
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 4}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the single-GPU recurrent-block forward; runs on more than one GPU are not "
               "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
