@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "librdt.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["runtime.cpp", "gemm.hip", "gemm_big.hip", "attention.hip", "rowwise.hip"]
+SOURCES = ["runtime.cpp", "gemm.hip", "gemm_big.hip", "gemm_skinny.hip", "attention.hip", "rowwise.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -48,19 +48,22 @@ struct GemmParams {
   const int32_t* grp_end;    // [E+1] offsets: rows of group e are [grp_end[e], grp_end[e+1])
   int n_groups;
   int dense_gm;              // dense raster: m-tiles per group of the tile order
+  int skinny_mt_cap;         // skinny kernel: m-tiles its grid is sized for
   EpiParams epi;
 };
 
-// Launch helpers (stream-ordered, no sync).  `bm` selects the m-tile height
-// that the grouped schedule was built for.
-void launch_gemm_bf16(const GemmParams& p, int epi, bool dual, int bm, int out_is_bf16, int n_cu, hipStream_t s);
+// Launch helpers (stream-ordered, no sync).
 // 256x256 tiles, direct-to-LDS loads; K must be a multiple of 64 and a
 // grouped schedule must be built with m-tile height RDT_BM_BIG
 void launch_gemm_bf16_big(const GemmParams& p, int epi, bool dual, int out_is_bf16, int n_cu, hipStream_t s);
+// at most 32 rows per m-tile (grouped schedules built with RDT_BM_SKINNY),
+// nc = 32 or 64 output columns per block; mt_cap bounds the m-tile count
+void launch_gemm_bf16_skinny(const GemmParams& p, int epi, bool dual, int out_is_bf16, int mt_cap, int nc,
+                             hipStream_t s);
 void launch_gemm_f32(const GemmParams& p, int epi, bool dual, int n_cu, hipStream_t s);
 
 // m-tile heights the kernels are built with (the dispatch builds schedules
 // for exactly these)
-#define RDT_BM_LARGE 128
 #define RDT_BM_BIG 256
+#define RDT_BM_SKINNY 32
 #define RDT_BM_F32 64

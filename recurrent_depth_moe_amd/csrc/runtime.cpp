@@ -109,10 +109,10 @@ struct Plan {
 };
 
 // m-tile height of the routed-expert schedule: the 256-row kernel for bf16
-// prefill, the 128-row kernel for single-token steps, 64 for fp32
+// prefill, the 32-row skinny kernel for single-token steps, 64 for fp32
 int bm_for(const rdt_config& c, int T) {
   if (c.weight_dtype != RDT_BF16) return RDT_BM_F32;
-  return T > 1 ? RDT_BM_BIG : RDT_BM_LARGE;
+  return T > 1 ? RDT_BM_BIG : RDT_BM_SKINNY;
 }
 
 Plan make_plan(const rdt_config& c, int B, int T) {
@@ -626,17 +626,20 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   const size_t slot = kv ? kv_slot_bytes(c, B, kv_capacity) : 0;
   const float scale = 1.0f / sqrtf((float)dq);
 
-  // bf16: the 256x256 kernel for wide products in prefill, the 128x128
-  // kernel for narrow outputs (router) and single-token steps
-  auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16) {
+  // bf16: the 256x256 kernel for prefill products, the skinny kernel for
+  // single-token steps and for narrow outputs (router logits)
+  auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16, bool narrow = false) {
     if (!bf) {
       launch_gemm_f32(gp, epi, dual, b->n_cu, s);
       return;
     }
     const bool grouped = gp.mt_start != nullptr;
-    const bool big = grouped ? p.bm == RDT_BM_BIG : (T > 1 && gp.N > 128);
-    if (big) launch_gemm_bf16_big(gp, epi, dual, out_bf16, b->n_cu, s);
-    else launch_gemm_bf16(gp, epi, dual, RDT_BM_LARGE, out_bf16, b->n_cu, s);
+    if (T == 1 || narrow) {
+      const int cap = grouped ? p.max_mt : (gp.M + RDT_BM_SKINNY - 1) / RDT_BM_SKINNY;
+      launch_gemm_bf16_skinny(gp, epi, dual, out_bf16, cap, narrow ? 64 : 32, s);
+    } else {
+      launch_gemm_bf16_big(gp, epi, dual, out_bf16, b->n_cu, s);
+    }
   };
   auto dense = [&](const void* A, int64_t lda, const void* W0, const void* W1, int M, int Nn, int K) {
     GemmParams gp{};
@@ -754,7 +757,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       GemmParams gp = dense(W(WS_F), D, b->router, nullptr, N, E, D);
       gp.epi.out = W(WS_LOGITS);
       gp.epi.ldo = E;
-      gemm(gp, EPI_STORE, false, 0);
+      gemm(gp, EPI_STORE, false, 0, true);
       launch_router_topk(WF(WS_LOGITS), b->router_bias, N, E, k, WI(WS_SEL), WF(WS_GATE),
                          b->cap_sel ? b->cap_sel + (size_t)t * N * k : nullptr, s);
     }
