@@ -330,6 +330,22 @@ def halting_probability(P, h):
 # one loop and the full loop
 # --------------------------------------------------------------------------
 
+def act_halts(cum32, running, p, t, n_loops, threshold):
+    """Positions that halt at loop t ([ZS §ACT]): running ones whose
+    cumulative halting probability reaches the threshold (the running sum
+    and the comparison in float32, as the kernel keeps them), and every
+    running one at the last loop."""
+    p32 = np.asarray(p).astype(np.float32)
+    reach = (cum32 + p32).astype(np.float32) >= np.float32(threshold)
+    return running & (reach | (t == n_loops - 1))
+
+
+def act_weights(cum, running, p, halt_now):
+    """Weight of this loop's state in the output: the remainder 1 - cum on
+    the halting loop, p on earlier loops, 0 once halted."""
+    return np.where(halt_now, np.maximum(1.0 - cum, 0.0), p) * running
+
+
 def run_loop(cfg, P, h, e, t, start_pos=0, cache=None, rows=None, route_hook=None):
     """One pass of the recurrent block at loop index t ([ZS §Recurrent Block]).
 
@@ -440,8 +456,7 @@ def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=
             p = halting_probability(P, h.reshape(N, D))
             p32 = p.astype(np.float32)
             running = ~halted
-            reach = (cum32 + p32).astype(np.float32) >= thr32
-            halt_now = running & (reach | (t == n_loops - 1))
+            halt_now = act_halts(cum32, running, p, t, n_loops, act_threshold)
             if adopt is not None and adopt.halt_counts is not None:
                 gpu_halt = np.asarray(adopt.halt_counts).reshape(N) == t + 1
                 near = running & (np.abs((cum32 + p32).astype(np.float64) - float(thr32)) < adopt.eps_halt) \
@@ -450,7 +465,7 @@ def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=
                 adopt.halt_adopted += int(np.sum(diff & near))
                 adopt.halt_disagree += int(np.sum(diff & ~near))
                 halt_now = np.where(near, gpu_halt & running, halt_now)
-            weight = np.where(halt_now, np.maximum(1.0 - cum, 0.0), p) * running
+            weight = act_weights(cum, running, p, halt_now)
             h_out += weight.reshape(B, T, 1) * h
             cum = cum + p * running
             cum32 = np.where(running, (cum32 + p32).astype(np.float32), cum32)
