@@ -10,3 +10,12 @@ void launch_attn_generic(int dtype_bf16, const void* q, const void* k, const voi
 // multiple of 8.
 void launch_attn_flash_bf16(const void* q, const void* k, const void* vt, void* o, int B, int H, int G, int Tq,
                             int cap, int kbase, float scale, hipStream_t s);
+// bf16, head width 128, one query per sequence against the cache (decode
+// step), H / G <= 16, cap >= 4.  Keys are split over blocks of 512; `part`
+// is fp32 scratch of attn_decode_part_floats(B, H, nk) floats.
+int attn_decode_blocks(int nk);
+inline size_t attn_decode_part_floats(int B, int H, int nk) {
+  return (size_t)B * H * attn_decode_blocks(nk) * (128 + 2);
+}
+void launch_attn_decode_bf16(const void* q, const void* k, const void* vt, void* o, float* part, int B, int H, int G,
+                             int cap, int nk, float scale, hipStream_t s);

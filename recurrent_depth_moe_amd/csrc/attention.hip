@@ -245,6 +245,184 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
   }
 }
 
+
+// ------------------------------------------------------------ split-KV decode, bf16, d=128
+// One query per sequence (a decode step against the cache).  The visible
+// keys of each (b, kv head) are cut into blocks of DEC_BLK; a block is four
+// wave64s, each owning DEC_U consecutive keys and ALL query heads of the kv
+// group at once (up to 16), so every cached K / V byte is read from HBM
+// exactly once.  Both products run on v_mfma_f32_16x16x32_bf16 with the K
+// and V^T fragments loaded straight from global memory (each fragment is
+// used once; LDS staging would only add a copy):
+//   S^T = K Q^T : A = 16 keys x 32 dims, B = Q^T (heads on the column axis),
+//                 lane l gets keys 4*(l/16)+i of the 16-key group for head l%16;
+//   O   = P V   : A = P with lane l holding head l%16 at the eight keys it
+//                 already scored in two adjacent groups, B = V read from V^T
+//                 in that same key order (two 8-byte pieces per lane).
+// Each wave takes an exact softmax over its keys (scores stay in registers),
+// the four waves merge through LDS, and the block leaves one partial
+// (max, sum, unnormalised o) per head; a second kernel merges the partials
+// of a row in block order, so the result does not depend on timing.
+constexpr int DEC_U = 128, DEC_BLK = 4 * DEC_U, DEC_D = 128, DEC_MAXREP = 16;
+
+__device__ __forceinline__ uint32_t keep_keys(uint32_t pair, int key, int nk) {
+  // zero the bf16 halves of keys >= nk (the cache past the last position
+  // holds whatever the caller left there)
+  const uint32_t lo = key < nk ? 0xffffu : 0u, hi = key + 1 < nk ? 0xffff0000u : 0u;
+  return pair & (lo | hi);
+}
+
+__global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16_t* __restrict__ q,
+                                                                 const bf16_t* __restrict__ k,
+                                                                 const bf16_t* __restrict__ vt,
+                                                                 float* __restrict__ part_o,
+                                                                 float* __restrict__ part_ml, int H, int G,
+                                                                 int cap, int nk, float scale_log2) {
+  __shared__ float sO[4][DEC_MAXREP][DEC_D + 4];
+  __shared__ float sM[4][DEC_MAXREP], sL[4][DEC_MAXREP];
+  const int nblk = gridDim.x, blk = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / G, g = bg - b * G, rep = H / G;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, qd = lane >> 4, c16 = lane & 15;
+  const int j0 = blk * DEC_BLK + w * DEC_U;
+  const bf16_t* kb = k + (int64_t)bg * cap * DEC_D;
+  const bf16_t* vb = vt + (int64_t)bg * DEC_D * cap;
+
+  // Q^T as the B operand: lane l holds head c16 of this group, dims 32 ds + 8 qd .. +7
+  bf16x8_t qf[4];
+  {
+    const bool hv = c16 < rep;
+    const bf16_t* qr = q + (int64_t)(b * H + g * rep + (hv ? c16 : 0)) * DEC_D + 8 * qd;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      uint4 v = *(const uint4*)(qr + 32 * ds);
+      if (!hv) v = uint4{0u, 0u, 0u, 0u};
+      qf[ds] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // scores of 8 groups of 16 keys; element i of group gi is key j0 + 16 gi + 4 qd + i
+  floatx4_t sc[8];
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi) {
+    const int key = min(j0 + 16 * gi + c16, cap - 1);
+    const bf16_t* kr = kb + (int64_t)key * DEC_D + 8 * qd;
+    uint4 kv4[4];
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) kv4[ds] = *(const uint4*)(kr + 32 * ds);
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv4[ds]), qf[ds], acc, 0, 0, 0);
+    sc[gi] = acc;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = (j0 + 16 * gi + 4 * qd + i < nk) ? sc[gi][i] * scale_log2 : -INFINITY;
+      sc[gi][i] = v;
+      m = fmaxf(m, v);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  const float mu = m == -INFINITY ? 0.f : m;   // a wave past the last key keeps p = 0
+  float l = 0.f;
+  bf16x8_t pf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sc[2 * c][i] - mu);
+      pv[4 + i] = __builtin_amdgcn_exp2f(sc[2 * c + 1][i] - mu);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l += pv[i];
+    uint4 u;
+    u.x = pack_bf16x2(pv[0], pv[1]);
+    u.y = pack_bf16x2(pv[2], pv[3]);
+    u.z = pack_bf16x2(pv[4], pv[5]);
+    u.w = pack_bf16x2(pv[6], pv[7]);
+    pf[c] = __builtin_bit_cast(bf16x8_t, u);
+  }
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+
+  // O = P V over 4 blocks of 32 keys x 8 blocks of 16 dims
+  floatx4_t o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int k1 = j0 + 32 * c + 4 * qd, k2 = k1 + 16;
+    const int a1 = min(k1, cap - 4), a2 = min(k2, cap - 4);
+    uint2 vv[8][2];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16_t* vr = vb + (int64_t)(16 * db + c16) * cap;
+      vv[db][0] = *(const uint2*)(vr + a1);
+      vv[db][1] = *(const uint2*)(vr + a2);
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      uint4 u;
+      u.x = keep_keys(vv[db][0].x, k1, nk);
+      u.y = keep_keys(vv[db][0].y, k1 + 2, nk);
+      u.z = keep_keys(vv[db][1].x, k2, nk);
+      u.w = keep_keys(vv[db][1].y, k2 + 2, nk);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[c], __builtin_bit_cast(bf16x8_t, u), o[db], 0, 0, 0);
+    }
+  }
+
+  // merge the four waves: o[db][i] is head 4 qd + i, dim 16 db + c16
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sO[w][4 * qd + i][16 * db + c16] = o[db][i];
+  if (qd == 0) {
+    sM[w][c16] = m;
+    sL[w][c16] = l;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rep * DEC_D; idx += 256) {
+    const int hh = idx / DEC_D, d = idx - hh * DEC_D;
+    float M = sM[0][hh];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, sM[ww][hh]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float f = sM[ww][hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sM[ww][hh] - M);
+      L += f * sL[ww][hh];
+      acc += f * sO[ww][hh][d];
+    }
+    const int64_t row = (int64_t)(b * H + g * rep + hh) * nblk + blk;
+    part_o[row * DEC_D + d] = acc;
+    if (d == 0) {
+      part_ml[row * 2] = M;
+      part_ml[row * 2 + 1] = L;
+    }
+  }
+}
+
+// merge the per-block partials of one (b, head) in block order
+__global__ __launch_bounds__(DEC_D) void attn_decode_merge_kernel(const float* __restrict__ part_o,
+                                                                   const float* __restrict__ part_ml,
+                                                                   bf16_t* __restrict__ o, int nblk) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* ml = part_ml + (int64_t)bh * nblk * 2;
+  float M = -INFINITY;
+  for (int j = 0; j < nblk; ++j) M = fmaxf(M, ml[2 * j]);
+  float L = 0.f, acc = 0.f;
+  for (int j = 0; j < nblk; ++j) {
+    const float f = __builtin_amdgcn_exp2f(ml[2 * j] - M);
+    L += f * ml[2 * j + 1];
+    acc += f * part_o[((int64_t)bh * nblk + j) * DEC_D + d];
+  }
+  o[(int64_t)bh * DEC_D + d] = f2bf(acc / L);
+}
+
 }  // namespace
 
 void launch_attn_generic(int dtype_bf16, const void* q, const void* k, const void* vt, void* o, int B, int H,
@@ -265,4 +443,17 @@ void launch_attn_flash_bf16(const void* q, const void* k, const void* vt, void* 
   const float scale_log2 = scale * 1.4426950408889634f;
   attn_flash_bf16_kernel<<<grid, block, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt, (bf16_t*)o,
                                                 H, G, Tq, cap, kbase, scale_log2);
+}
+
+int attn_decode_blocks(int nk) { return (nk + DEC_BLK - 1) / DEC_BLK; }
+
+void launch_attn_decode_bf16(const void* q, const void* k, const void* vt, void* o, float* part, int B, int H, int G,
+                             int cap, int nk, float scale, hipStream_t s) {
+  const int nblk = attn_decode_blocks(nk);
+  float* part_o = part;
+  float* part_ml = part + (size_t)B * H * nblk * DEC_D;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  attn_decode_split_kernel<<<dim3(nblk, B * G), 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
+                                                              part_o, part_ml, H, G, cap, nk, scale_log2);
+  attn_decode_merge_kernel<<<B * H, DEC_D, 0, s>>>(part_o, part_ml, (bf16_t*)o, nblk);
 }

@@ -96,12 +96,12 @@ rdt_status check_config(const rdt_config* c) {
 enum WsId {
   WS_H, WS_C, WS_A, WS_Q, WS_K, WS_VT, WS_O, WS_X1, WS_F, WS_LOGITS, WS_SEL, WS_GATE, WS_TILECNT, WS_OFFSETS,
   WS_MTSTART, WS_TROW0, WS_TGRP, WS_PERM, WS_INV, WS_ACT, WS_Y, WS_ACTS, WS_YS, WS_CUM,
-  WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_COUNT
+  WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_DPART, WS_COUNT
 };
 const char* kWsNames[WS_COUNT] = {"h", "c", "a", "q", "k", "vt", "o", "x1", "f", "logits", "sel", "gate",
                                   "tile_counts", "offsets", "mt_start", "tile_row0", "tile_grp", "perm", "inv",
                                   "act", "y", "act_s", "y_s", "cum", "kv_raw", "cq_raw", "cq_norm", "lat_ckv",
-                                  "lat_krope", "ckv_norm"};
+                                  "lat_krope", "ckv_norm", "attn_part"};
 
 struct Plan {
   int B, T, N, NK, kvcap, kvlen_max, bm, max_mt, disp_tiles;
@@ -113,6 +113,13 @@ struct Plan {
 int bm_for(const rdt_config& c, int T) {
   if (c.weight_dtype != RDT_BF16) return RDT_BM_F32;
   return T > 1 ? RDT_BM_BIG : RDT_BM_SKINNY;
+}
+
+// single-token steps of bf16 GQA with 128-wide heads use the split-KV
+// decode kernel (when they attend a cache)
+bool use_decode_attn(const rdt_config& c, int T) {
+  return c.weight_dtype == RDT_BF16 && is_gqa(c) && T == 1 && c.head_dim == 128 &&
+         c.n_heads / kv_heads(c) <= 16;
 }
 
 Plan make_plan(const rdt_config& c, int B, int T) {
@@ -168,6 +175,7 @@ Plan make_plan(const rdt_config& c, int B, int T) {
     s[WS_LATR] = N * rope * es;
     s[WS_CKVN] = (size_t)B * p.kvlen_max * kvl * es;
   }
+  if (use_decode_attn(c, T)) s[WS_DPART] = attn_decode_part_floats(B, c.n_heads, p.kvlen_max) * 4;
   size_t o = 0;
   for (int i = 0; i < WS_COUNT; ++i) {
     p.off[i] = o;
@@ -692,6 +700,8 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       StageTimer st_(b, s, RDT_STAGE_ATTN);
       if (bf && T > 1)
         launch_attn_flash_bf16(W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, kbase, scale, s);
+      else if (kv && use_decode_attn(c, T))
+        launch_attn_decode_bf16(W(WS_Q), K, VT, W(WS_O), WF(WS_DPART), B, H, G, cap, kbase + 1, scale, s);
       else
         launch_attn_generic(bf, W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, dq, dv, kbase, scale, s);
     } else {
