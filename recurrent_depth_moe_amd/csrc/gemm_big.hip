@@ -7,11 +7,18 @@
 // SIMD, where 16x16x32 needs many more independent chains).  Tiles reach
 // LDS with global_load_lds_dwordx4 (no register staging): lane i of a load
 // fills 16-byte LDS slot i of its 1 KB window, so the XOR swizzle of the
-// 16-byte chunks inside a row (chunk ^ ((row >> 2) & 3)) is applied on the source
-// side by choosing which global chunk each lane fetches.  Four LDS stages of
-// 32 deep (32 KB each): while a wave runs the 64 MFMAs of stage k from
-// registers, the fragments of stage k+1 are being read from LDS and stages
-// k+2, k+3 are loading from memory; a wave waits only for its oldest stage.
+// 16-byte chunks inside a row (chunk ^ ((row >> 1) & 7)) is applied on the
+// source side by choosing which global chunk each lane fetches.
+//
+// The k loop runs over 64-deep stages, so every load takes whole 128-byte
+// lines of A and B (a 32-deep stage would touch each line twice, and the
+// measured L2->LDS throughput halves); two stages of 64 KB alternate.  A
+// stage is consumed in two 32-deep halves from registers: while the MFMAs
+// of one half run, the fragments of the next half are read from LDS, and
+// the load of stage k+2 is issued once every wave has finished reading
+// stage k (one barrier per stage).  Loads and fragment reads are spread
+// between the MFMAs (sched_group_barrier), since with one wave per SIMD no
+// other wave fills the issue slots.
 //
 // For the fused gate|up product the B tile holds 128 gate rows and the same
 // 128 up rows, interleaved per wave column (gate 0-63, up 0-63, gate 64-127,
@@ -25,8 +32,34 @@
 
 namespace {
 
-constexpr int BK = 32;                               // k depth of one LDS stage
-constexpr int NSTAGE = 4;                            // stages in flight
+// Issue order of the first half of a stage: a fragment read of the second
+// half after each of the first 16 MFMAs.
+__device__ __forceinline__ void interleave_first_half() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+}
+// Second half: the 16 global->LDS loads of stage k+2 first (their latency
+// is what the pipeline must hide), then the reads of the next stage's first
+// half, one after each MFMA.
+__device__ __forceinline__ void interleave_second_half() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+  }
+}
+
+constexpr int BK = 64;                               // k depth of one LDS stage
+constexpr int NSTAGE = 2;                            // LDS stages
 constexpr int LDS_BYTES = NSTAGE * (256 + 256) * BK * 2;
 constexpr int EP_LD = 128 + 4;                      // epilogue patch row stride (floats)
 static_assert(4 * 32 * EP_LD * 4 <= LDS_BYTES, "epilogue patches fit in the tile LDS");
@@ -37,29 +70,27 @@ __device__ __forceinline__ void g2lds(const void* src, uint4* lds_slot0) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_slot0, 16, 0, 0);
 }
 
-// One 64-deep stage of the wave's 128 x 128 tile (FMV row fragments).
-// Straight-line code, so the fragment reads can be issued ahead of the
-// MFMAs that use them.
-// Fragments of one 32-deep stage for this wave, for v_mfma_f32_32x32x16_bf16
-// (two 16-deep k-steps): 4 A fragments (32 rows each) and 4 B fragments (32
-// columns each) per k-step; lane l holds row/column l % 32 and k values
-// 8 * (l / 32) .. +7 of the k-step.  Rows hold 4 chunks of 8 k (64 bytes);
-// chunk c of row r sits at position c ^ ((r >> 2) & 3), so 16 consecutive
-// rows read the same chunk from distinct banks.
-__device__ __forceinline__ void read_frags(const uint4* sA, const uint4* sB, int wm, int wn, int lane,
+// Fragments of one 32-deep half (hh = 0, 1) of a 64-deep stage for this
+// wave, for v_mfma_f32_32x32x16_bf16 (two 16-deep k-steps): 4 A fragments
+// (32 rows each) and 4 B fragments (32 columns each) per k-step; lane l
+// holds row/column l % 32 and k values 8 * (l / 32) .. +7 of the k-step.
+// Rows hold 8 chunks of 8 k (128 bytes); chunk c of row r sits at position
+// c ^ ((r >> 1) & 7), so the 8 rows a quarter-wave reads land in distinct
+// banks.
+__device__ __forceinline__ void read_frags(const uint4* sA, const uint4* sB, int wm, int wn, int lane, int hh,
                                            bf16x8_t (&af)[8], bf16x8_t (&bf)[8]) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int c = 2 * s + (lane >> 5);
+    const int c = 4 * hh + 2 * s + (lane >> 5);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 128 + j * 32 + (lane & 31);
-      bf[s * 4 + j] = __builtin_bit_cast(bf16x8_t, sB[r * 4 + (c ^ ((r >> 2) & 3))]);
+      bf[s * 4 + j] = __builtin_bit_cast(bf16x8_t, sB[r * 8 + (c ^ ((r >> 1) & 7))]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + i * 32 + (lane & 31);
-      af[s * 4 + i] = __builtin_bit_cast(bf16x8_t, sA[r * 4 + (c ^ ((r >> 2) & 3))]);
+      af[s * 4 + i] = __builtin_bit_cast(bf16x8_t, sA[r * 8 + (c ^ ((r >> 1) & 7))]);
     }
   }
 }
@@ -114,12 +145,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     const bf16_t* W1 = DUAL ? (const bf16_t*)p.W1 + (int64_t)grp * p.w_stride : W0;
 
     // source pointers of this thread's chunks (k offset added per stage):
-    // LDS slot s = (j*4 + w)*64 + lane holds row s/4, logical chunk
-    // (s%4) ^ ((row >> 2) & 3)
+    // LDS slot s = (j*4 + w)*64 + lane holds row s/8, logical chunk
+    // (s%8) ^ ((row >> 1) & 7)
     const bf16_t* asrc[A_IT];
 #pragma unroll
     for (int j = 0; j < A_IT; ++j) {
-      const int s = (j * 4 + w) * 64 + lane, r = s >> 2, c = (s & 3) ^ ((r >> 2) & 3);
+      const int s = (j * 4 + w) * 64 + lane, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
       const int m = row0 + (r < rows ? r : 0);
       const int arow = p.a_rows ? p.a_rows[m] : m;
       asrc[j] = Abase + (int64_t)arow * p.lda + c * 8;
@@ -127,7 +158,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     const bf16_t* bsrc[B_IT];
 #pragma unroll
     for (int j = 0; j < B_IT; ++j) {
-      const int s = (j * 4 + w) * 64 + lane, r = s >> 2, c = (s & 3) ^ ((r >> 2) & 3);
+      const int s = (j * 4 + w) * 64 + lane, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
       const bf16_t* Wsel = W0;
       int col;
       if constexpr (DUAL) {
@@ -159,36 +190,38 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     // 32-row fragments of this wave that hold at least one valid row
     const int fm_valid = max(0, min(4, (rows - wm * WTM + 31) / 32));
 
-    // prologue: stages 0 .. NSTAGE-2 in flight, fragments of stage 0 read
-    // (KT >= 2 and even: K is a multiple of 64)
-#pragma unroll
-    for (int st = 0; st < NSTAGE - 1; ++st) issue(st, min(st, KT - 1) * BK);
+    // prologue: stages 0 and 1 in flight, first half of stage 0 read (past
+    // the end of K, loads repeat the last stage into a buffer nobody reads)
+    issue(0, 0);
+    issue(1, min(1, KT - 1) * BK);
     bf16x8_t fa0[8], fb0[8], fa1[8], fb1[8];
-    wait_vm(2 * (A_IT + B_IT));
+    wait_vm(A_IT + B_IT);
     __syncthreads();
-    read_frags(smem, smem + A_CH, wm, wn, lane, fa0, fb0);
-    // Step kt, branch-free: make stage kt+1 visible, start loading stage
-    // kt+3 into the buffer stage kt-1 used (past the end: a harmless reload
-    // of the last stage into a buffer nobody reads again), read stage kt+1's
-    // fragments into the spare registers (past the end: unused), then run
-    // stage kt's 64 MFMAs while those reads land.
-#define RDT_GEMM_STEP(KT_, CA, CB, NA, NB)                                        \
-  {                                                                               \
-    const int kt_ = (KT_);                                                        \
-    wait_vm(A_IT + B_IT);                                                         \
-    __syncthreads();                                                              \
-    issue((kt_ + NSTAGE - 1) % NSTAGE, min(kt_ + NSTAGE - 1, KT - 1) * BK);       \
-    const uint4* sA_ = smem + ((kt_ + 1) % NSTAGE) * (A_CH + B_CH);               \
-    read_frags(sA_, sA_ + A_CH, wm, wn, lane, NA, NB);                            \
-    __builtin_amdgcn_sched_barrier(0);                                            \
-    mfma_stage(CA, CB, acc);                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                            \
-  }
-    for (int kt = 0; kt < KT; kt += 2) {
-      RDT_GEMM_STEP(kt, fa0, fb0, fa1, fb1)
-      RDT_GEMM_STEP(kt + 1, fa1, fb1, fa0, fb0)
+    read_frags(smem, smem + A_CH, wm, wn, lane, 0, fa0, fb0);
+    for (int kt = 0; kt < KT; ++kt) {
+      {
+        // first half of stage kt (registers fa0/fb0); read its second half
+        const uint4* sb = smem + (kt & 1) * (A_CH + B_CH);
+        read_frags(sb, sb + A_CH, wm, wn, lane, 1, fa1, fb1);
+        mfma_stage(fa0, fb0, acc);
+        interleave_first_half();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        // second half: stage kt+1 landed and every wave is done reading
+        // stage kt, so its buffer takes stage kt+2; read stage kt+1's
+        // first half (past the end: unused)
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt & 1, min(kt + 2, KT - 1) * BK);
+        const uint4* sb = smem + ((kt + 1) & 1) * (A_CH + B_CH);
+        read_frags(sb, sb + A_CH, wm, wn, lane, 0, fa0, fb0);
+        mfma_stage(fa1, fb1, acc);
+        interleave_second_half();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-#undef RDT_GEMM_STEP
     wait_vm(0);   // the trailing reloads land before the epilogue reuses LDS
     __syncthreads();   // every wave done with the stages before the epilogue reuses LDS
 
