@@ -170,6 +170,13 @@ def main():
                 achieved=d.get("tflops"), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=d.get("mfma_frac"), traffic=None,
                 per_launch_flops=work[dom]["flops"], avg_launch_ms=d.get("avg_ms"))
+    E = cfg["n_experts"]
+    offs = blk.workspace_view(ws, B, T, "offsets", torch.int32, (E + 1,)).cpu().numpy()
+    counts = np.diff(offs)
+    tiles = int(np.sum((counts + 255) // 256)) if T > 1 else int(np.sum((counts + 31) // 32))
+    log(f"[bench] routed rows per expert (last loop): min {counts.min()} mean {counts.mean():.1f} "
+        f"max {counts.max()}, experts touched {int(np.sum(counts > 0))}, m-tiles {tiles}, "
+        f"tails <= 64 rows {int(np.sum((counts % 256 > 0) & (counts % 256 <= 64)))}")
     if thr > 0:
         hist = np.bincount(halt.ravel(), minlength=n_loops + 1)[1:]
         log(f"[bench] halt-count histogram (loops 1..{n_loops}): {hist.tolist()}")

@@ -60,7 +60,7 @@ __device__ __forceinline__ void interleave_second_half() {
 
 constexpr int BK = 64;                               // k depth of one LDS stage
 constexpr int NSTAGE = 2;                            // LDS stages
-constexpr int LDS_BYTES = NSTAGE * (256 + 256) * BK * 2;
+constexpr int LDS_BYTES = 160 * 1024;                // two 64 KB stages; short tiles use it all
 constexpr int EP_LD = 128 + 4;                      // epilogue patch row stride (floats)
 static_assert(4 * 32 * EP_LD * 4 <= LDS_BYTES, "epilogue patches fit in the tile LDS");
 
@@ -112,6 +112,142 @@ __device__ __forceinline__ void wait_vm(int n) {
   if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);
   else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
   else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at max
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// A tile with at most SR (64 or 128) valid rows: the tail of a routed
+// expert's rows, or the last rows of a dense product.  Only A rows 0..SR-1
+// are loaded and each wave computes those rows for a quarter of the
+// columns (for gate|up: 32 gate and the matching 32 up columns), so the
+// tile costs SR/256 of a full tile's MFMAs.  With so little math per stage
+// the loads set the pace, so the smaller stages (A 8 or 16 KB + B 32 KB)
+// run in a deeper ring: 4 stages for 64 rows, 3 for 128.
+template <int SR, bool DUAL, int EPI, typename TO>
+__device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, const bf16_t* const (&asrc)[8],
+                                           const bf16_t* const (&bsrc)[8], int w, int lane, int rows, int row0,
+                                           int n0, int KT) {
+  constexpr int FM = SR / 32;                  // 32-row fragments
+  constexpr int SA_IT = SR / 32;               // A rows 0..SR-1 sit in LDS slots 0..SR*8-1
+  constexpr int B_IT = 8;
+  constexpr int IT = SA_IT + B_IT;             // loads per thread and stage
+  constexpr int SA_CH = SR * 8, STG = SA_CH + 2048;
+  constexpr int NS = SR == 64 ? 4 : 3;
+  static_assert(NS * STG * 16 <= LDS_BYTES, "stages fit in LDS");
+  auto issue = [&](int stage, int k0) {
+    uint4* base = smem + stage * STG;
+#pragma unroll
+    for (int j = 0; j < SA_IT; ++j) g2lds(asrc[j] + k0, base + (j * 4 + w) * 64);
+#pragma unroll
+    for (int j = 0; j < B_IT; ++j) g2lds(bsrc[j] + k0, base + SA_CH + (j * 4 + w) * 64);
+  };
+  const int brow0 = DUAL ? (w >> 1) * 128 + (w & 1) * 32 : 64 * w;
+  const int brow1 = DUAL ? brow0 + 64 : brow0 + 32;
+  auto read = [&](int stage, int hh, bf16x8_t (&af)[2 * FM], bf16x8_t (&bf)[4]) {
+    const uint4* sA = smem + stage * STG;
+    const uint4* sB = sA + SA_CH;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 4 * hh + 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = i * 32 + (lane & 31);
+        af[s * FM + i] = __builtin_bit_cast(bf16x8_t, sA[r * 8 + (c ^ ((r >> 1) & 7))]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rb = (j ? brow1 : brow0) + (lane & 31);
+        bf[s * 2 + j] = __builtin_bit_cast(bf16x8_t, sB[rb * 8 + (c ^ ((rb >> 1) & 7))]);
+      }
+    }
+  };
+  floatx16_t acc[FM][2];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  auto mfma = [&](const bf16x8_t (&af)[2 * FM], const bf16x8_t (&bf)[4]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s * FM + i], bf[s * 2 + j], acc[i][j], 0, 0, 0);
+  };
+  // every buffer loading (past the end of K: repeats of the last stage)
+#pragma unroll
+  for (int st = 0; st < NS; ++st) issue(st, min(st, KT - 1) * BK);
+  bf16x8_t a0[2 * FM], b0[4], a1[2 * FM], b1[4];
+  wait_vmcnt<(NS - 1) * IT>();
+  __syncthreads();
+  read(0, 0, a0, b0);
+  for (int kt = 0; kt < KT; ++kt) {
+    read(kt % NS, 1, a1, b1);
+    mfma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage kt+1 landed; every wave is done with stage kt, whose buffer
+    // takes stage kt+NS
+    wait_vmcnt<(NS - 2) * IT>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt % NS, min(kt + NS, KT - 1) * BK);
+    read((kt + 1) % NS, 0, a0, b0);
+    mfma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  // epilogue: FM passes of 32 rows through a 32 x 64 patch per wave
+  float* ep = (float*)smem + w * (32 * EP_LD);
+#pragma unroll
+  for (int pass = 0; pass < FM; ++pass) {
+    if (pass * 32 < rows) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = acc[pass][j][e];
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      if constexpr (DUAL) {
+        // 32 output columns: gate at patch columns 0..31, up at 32..63
+#pragma unroll 1
+        for (int it = 0; it < 2; ++it) {
+          const int rl = it * 16 + (lane >> 2), c8 = (lane & 3) * 8;
+          const int ml = pass * 32 + rl;
+          float g[8], u[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            g[x] = ep[rl * EP_LD + c8 + x];
+            u[x] = ep[rl * EP_LD + 32 + c8 + x];
+          }
+          if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + 32 * w + c8, g, u);
+        }
+      } else {
+#pragma unroll 1
+        for (int it = 0; it < 4; ++it) {
+          const int rl = it * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+          const int ml = pass * 32 + rl;
+          float val[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) val[x] = ep[rl * EP_LD + c8 + x];
+          if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + 64 * w + c8, val, val);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();   // the next tile's loads reuse this LDS
 }
 
 template <bool DUAL, int EPI, typename TO>
@@ -172,13 +308,31 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       bsrc[j] = Wsel + (int64_t)n * p.K + c * 8;
     }
 
-    auto issue = [&](int stage, int k0) {
-      uint4* base = smem + stage * (A_CH + B_CH);
+    // LDS: A stages in a ring of 2 (A rows are shared by every n-tile of
+    // the rows, so they come from L2), B stages in a ring of 3 (a routed
+    // expert's weights stream from HBM, so they are requested one stage
+    // earlier)
+    uint4* const sAbuf = smem;
+    uint4* const sBbuf = smem + 2 * A_CH;
+    auto issueA = [&](int buf, int k0) {
 #pragma unroll
-      for (int j = 0; j < A_IT; ++j) g2lds(asrc[j] + k0, base + (j * 4 + w) * 64);
-#pragma unroll
-      for (int j = 0; j < B_IT; ++j) g2lds(bsrc[j] + k0, base + A_CH + (j * 4 + w) * 64);
+      for (int j = 0; j < A_IT; ++j) g2lds(asrc[j] + k0, sAbuf + buf * A_CH + (j * 4 + w) * 64);
     };
+    auto issueB = [&](int buf, int k0) {
+#pragma unroll
+      for (int j = 0; j < B_IT; ++j) g2lds(bsrc[j] + k0, sBbuf + buf * B_CH + (j * 4 + w) * 64);
+    };
+
+    if constexpr (EPI != EPI_QKV) {   // (QKV rows come in full tiles but the last; its epilogue is the heaviest)
+      if (rows <= 64) {
+        small_tile<64, DUAL, EPI, TO>(p, smem, asrc, bsrc, w, lane, rows, row0, n0, KT);
+        continue;
+      }
+      if (rows <= 128) {
+        small_tile<128, DUAL, EPI, TO>(p, smem, asrc, bsrc, w, lane, rows, row0, n0, KT);
+        continue;
+      }
+    }
 
     floatx16_t acc[4][4];
 #pragma unroll
@@ -190,37 +344,45 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     // 32-row fragments of this wave that hold at least one valid row
     const int fm_valid = max(0, min(4, (rows - wm * WTM + 31) / 32));
 
-    // prologue: stages 0 and 1 in flight, first half of stage 0 read (past
-    // the end of K, loads repeat the last stage into a buffer nobody reads)
-    issue(0, 0);
-    issue(1, min(1, KT - 1) * BK);
+    // prologue: A stages 0, 1 and B stages 0, 1, 2 in flight, first half
+    // of stage 0 read (past the end of K, loads repeat the last stage into
+    // a buffer nobody reads)
+    issueA(0, 0);
+    issueB(0, 0);
+    issueA(1, min(1, KT - 1) * BK);
+    issueB(1, min(1, KT - 1) * BK);
+    issueB(2, min(2, KT - 1) * BK);
     bf16x8_t fa0[8], fb0[8], fa1[8], fb1[8];
-    wait_vm(A_IT + B_IT);
+    wait_vmcnt<A_IT + 2 * B_IT>();
     __syncthreads();
-    read_frags(smem, smem + A_CH, wm, wn, lane, 0, fa0, fb0);
+    read_frags(sAbuf, sBbuf, wm, wn, lane, 0, fa0, fb0);
+    int b3 = 0;   // kt % 3
     for (int kt = 0; kt < KT; ++kt) {
+      const int b3n = b3 == 2 ? 0 : b3 + 1;
       {
         // first half of stage kt (registers fa0/fb0); read its second half
-        const uint4* sb = smem + (kt & 1) * (A_CH + B_CH);
-        read_frags(sb, sb + A_CH, wm, wn, lane, 1, fa1, fb1);
+        read_frags(sAbuf + (kt & 1) * A_CH, sBbuf + b3 * B_CH, wm, wn, lane, 1, fa1, fb1);
         mfma_stage(fa0, fb0, acc);
         interleave_first_half();
         __builtin_amdgcn_sched_barrier(0);
       }
       {
-        // second half: stage kt+1 landed and every wave is done reading
-        // stage kt, so its buffer takes stage kt+2; read stage kt+1's
-        // first half (past the end: unused)
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        // second half: stage kt+1 landed (only B of stage kt+2 may still be
+        // in flight) and every wave is done reading stage kt, so its
+        // buffers take A of stage kt+2 and B of stage kt+3; read stage
+        // kt+1's first half (past the end: unused)
+        wait_vmcnt<B_IT>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        issue(kt & 1, min(kt + 2, KT - 1) * BK);
-        const uint4* sb = smem + ((kt + 1) & 1) * (A_CH + B_CH);
-        read_frags(sb, sb + A_CH, wm, wn, lane, 0, fa0, fb0);
+        issueA(kt & 1, min(kt + 2, KT - 1) * BK);
+        issueB(b3, min(kt + 3, KT - 1) * BK);
+        read_frags(sAbuf + ((kt + 1) & 1) * A_CH, sBbuf + b3n * B_CH, wm, wn, lane, 0, fa0, fb0);
         mfma_stage(fa1, fb1, acc);
         interleave_second_half();
         __builtin_amdgcn_sched_barrier(0);
       }
+      b3 = b3n;
     }
     wait_vm(0);   // the trailing reloads land before the epilogue reuses LDS
     __syncthreads();   // every wave done with the stages before the epilogue reuses LDS
