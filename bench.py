@@ -32,21 +32,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_work(cfg):
-    """Algorithmic flops and bytes of one launch of each stage (per loop)."""
+def stage_work(cfg, touched=None):
+    """Algorithmic flops and bytes of one launch of each stage (per loop).
+    Expert weight bytes count the experts that received rows (``touched``,
+    all of them when None)."""
     B, T, D = cfg["batch"], cfg["seq"], cfg["dim"]
     N = B * T
     H, G, dh, E, F, k, S = (cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["n_experts"],
                             cfg["expert_dim"], cfg["top_k"], cfg["n_shared_experts"])
     sp = cfg["start_pos"]
     NK = N * k
+    Et = E if touched is None else touched
     w = {}
     w["qkv"] = dict(flops=2.0 * N * D * (H + 2 * G) * dh)
     w["attention"] = dict(flops=4.0 * B * H * dh * sum(sp + i + 1 for i in range(T)))
     w["o_proj"] = dict(flops=2.0 * N * D * H * dh)
     w["router"] = dict(flops=2.0 * N * D * E)
-    w["expert_gate_up"] = dict(flops=2.0 * NK * 2 * F * D, bytes=2.0 * E * 2 * F * D + 2.0 * NK * D + 2.0 * NK * F)
-    w["expert_down"] = dict(flops=2.0 * NK * F * D, bytes=2.0 * E * F * D + 2.0 * NK * F + 4.0 * NK * D)
+    w["expert_gate_up"] = dict(flops=2.0 * NK * 2 * F * D, bytes=2.0 * Et * 2 * F * D + 2.0 * NK * D + 2.0 * NK * F)
+    w["expert_down"] = dict(flops=2.0 * NK * F * D, bytes=2.0 * Et * F * D + 2.0 * NK * F + 4.0 * NK * D)
     w["shared_gate_up"] = dict(flops=2.0 * N * 2 * F * D * S)
     w["shared_down"] = dict(flops=2.0 * N * F * D * S)
     # row-wise kernels: each tensor read / written once at its stored width
@@ -54,6 +57,39 @@ def stage_work(cfg):
     w["ffn_norm"] = dict(bytes=N * D * (4 + 2))                       # x1 in, f out
     w["tail"] = dict(bytes=N * D * (4 + 4 * k + 4 * S + 4 + 4 + 4 + 4))   # x1, y (k rows), y_s, h, e in; h, h_out
     return w
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_expert_gate_up_mythos_3b.md")
+GEMM_SOURCES = ["gemm_big.hip", "gemm_device.h", "gemm.h", "common.h"]
+
+
+def gemm_source_hash():
+    import hashlib
+    hsh = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "recurrent_depth_moe_amd", "csrc", name), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the routed gate|up kernel from the committed
+    rocprofv3 counter summary, or None when that summary was taken on
+    another workload or on a different kernel source."""
+    if config != "mythos_3b" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_PROFILE) as f:
+        for line in f:
+            if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("kernel_source_sha256") != gemm_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, W, e, h0, prefix):
@@ -79,7 +115,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="mythos_3b")
-    ap.add_argument("--cpu-prefix", type=int, default=1024)
+    ap.add_argument("--cpu-prefix", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run plain device copies of this many MiB (calibrates HBM byte counters)")
@@ -147,7 +183,11 @@ def main():
     ms_step = elapsed / args.steps * 1e3
     value = B * T * loops_exec * args.steps / elapsed
 
-    work = stage_work(cfg)
+    E = cfg["n_experts"]
+    offs = blk.workspace_view(ws, B, T, "offsets", torch.int32, (E + 1,)).cpu().numpy()
+    counts = np.diff(offs)
+    touched = int(np.sum(counts > 0))
+    work = stage_work(cfg, touched)
     kernels = {}
     for name, (ms, n) in stages.items():
         if n == 0:
@@ -164,15 +204,25 @@ def main():
         kernels[name] = ent
     for name, ent in kernels.items():
         log(f"  {name:16s} {ent}")
+    # roofline of the dominant kernel: whichever of MFMA time and HBM time
+    # of its algorithmic work is longer bounds it
     dom = "expert_gate_up"
     d = kernels.get(dom, {})
-    roof = dict(kernel="routed expert gate|up grouped GEMM (SwiGLU epilogue)", bound="mfma",
-                achieved=d.get("tflops"), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=d.get("mfma_frac"), traffic=None,
-                per_launch_flops=work[dom]["flops"], avg_launch_ms=d.get("avg_ms"))
-    E = cfg["n_experts"]
-    offs = blk.workspace_view(ws, B, T, "offsets", torch.int32, (E + 1,)).cpu().numpy()
-    counts = np.diff(offs)
+    wk = work[dom]
+    t_mfma = wk["flops"] / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = wk["bytes"] / (PEAK_HBM_GBS * 1e9)
+    avg_s = d["avg_ms"] * 1e-3 if d else None
+    if t_hbm >= t_mfma:
+        roof = dict(bound="hbm", achieved=round(wk["bytes"] / avg_s / 1e9, 1) if avg_s else None,
+                    peak=PEAK_HBM_GBS, unit="GB/s")
+    else:
+        roof = dict(bound="mfma", achieved=round(wk["flops"] / avg_s / 1e12, 2) if avg_s else None,
+                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4) if roof["achieved"] else None
+    roof["traffic"] = measured_traffic(args.config)
+    roof.update(kernel="routed expert gate|up grouped GEMM (SwiGLU epilogue)",
+                per_launch_flops=wk["flops"], per_launch_bytes=wk["bytes"], avg_launch_ms=d.get("avg_ms"),
+                mfma_frac=d.get("mfma_frac"))
     tiles = int(np.sum((counts + 255) // 256)) if T > 1 else int(np.sum((counts + 31) // 32))
     log(f"[bench] routed rows per expert (last loop): min {counts.min()} mean {counts.mean():.1f} "
         f"max {counts.max()}, experts touched {int(np.sum(counts > 0))}, m-tiles {tiles}, "
