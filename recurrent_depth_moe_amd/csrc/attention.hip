@@ -65,10 +65,10 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
 // whole kernel and the softmax statistics never leave the lane pair l,
 // l ^ 32), online softmax in fp32, then O^T += V^T P^T with P packed from the
 // S^T accumulators straight into the B operand.  A 32x32 accumulator holds,
-// in lane l and element e, row 8*(e/4) + 4*(l/32) + e%4 and column l%32, so
-// elements 0..7 of a 32-key block cover keys {4g..4g+3, 8+4g..8+4g+3}
-// (g = l/32) -- together with the other lane half, keys 0..15 -- and the
-// V^T fragment is read with the same key order.
+// in lane l and element e, row 8*(e/4) + 4*(l/32) + e%4 and column l%32;
+// the K rows are fed to the MFMA in the order that maps those rows of lane
+// half g to the keys 16g .. 16g+15 of each 32-key block, so the V^T
+// fragment of a P V key step is one 16-byte LDS read per lane.
 constexpr int FD = 128, FBQ = 128, FBK = 64;
 
 __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* __restrict__ q,
@@ -131,104 +131,128 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
     }
   };
 
+  // The tile holding the end of the keys gets its V^T entries past kv_valid
+  // zeroed in LDS once (the buffers past the last position hold whatever
+  // the caller or an earlier call left there), so the P V reads need no
+  // per-element masking; the scores of those keys are masked to -inf.
+  auto zero_v_tail = [&](int buf, int k0) {
+    const int nvalid = kv_valid - k0;
+    unsigned short* sv = (unsigned short*)&sV[buf][0];
+    for (int idx = tid; idx < FD * FBK; idx += 256) {
+      const int d = idx >> 6, key = idx & (FBK - 1);
+      if (key >= nvalid) sv[(d * 8 + ((key >> 3) ^ ((d >> 1) & 7))) * 8 + (key & 7)] = 0;
+    }
+  };
   if (ntiles > 0) issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (ntiles > 0 && FBK > kv_valid) {
+    zero_v_tail(0, 0);
+    __syncthreads();
+  }
   const int qlim = kbase + myq;      // last visible key of this lane's query
+  // K row this lane feeds into S^T: accumulator row r holds key
+  // 16 ((r >> 2) & 1) + 4 (r >> 3) + r % 4 of each 32-key block, so lane
+  // half g ends up with the 16 consecutive keys 16 g .. 16 g + 15 (element
+  // e = key 16 g + e) and each P V key step reads whole V^T chunks
+  const int kperm = 16 * (((lane & 31) >> 2) & 1) + 4 * ((lane & 31) >> 3) + (lane & 3);
+  const int wfirst = kbase + qt * FBQ + w * 32;   // last key every query of this wave sees
+  const int wlast = wfirst + 31;                  // last key any query of this wave sees
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) issue(buf ^ 1, t + 1);
-    // S^T for two key blocks of 32: 8 chained k-steps of 16 d each
-    floatx16_t s[2];
+    if (t * FBK <= wlast) {   // else every key of the tile is past this wave's queries
+      // S^T for two key blocks of 32: 8 chained k-steps of 16 d each
+      floatx16_t s[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb2][e] = 0.f;
-    // K fragments in two batches of 8 reads, each batch in flight before
-    // its MFMAs
+        for (int e = 0; e < 16; ++e) s[kb2][e] = 0.f;
+      // K fragments in two batches of 8 reads, each batch in flight before
+      // its MFMAs
 #pragma unroll
-    for (int dh2 = 0; dh2 < 2; ++dh2) {
-      bf16x8_t kf[4][2];
+      for (int dh2 = 0; dh2 < 2; ++dh2) {
+        bf16x8_t kf[4][2];
 #pragma unroll
-      for (int dd = 0; dd < 4; ++dd)
+        for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const int kr = kb2 * 32 + (lane & 31);
-          const int ch = (dh2 * 4 + dd) * 2 + half;
-          kf[dd][kb2] = __builtin_bit_cast(bf16x8_t, sK[buf][kr * 16 + (ch ^ (kr & 15))]);
-        }
-      __builtin_amdgcn_sched_barrier(0);
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int kr = kb2 * 32 + kperm;
+            const int ch = (dh2 * 4 + dd) * 2 + half;
+            kf[dd][kb2] = __builtin_bit_cast(bf16x8_t, sK[buf][kr * 16 + (ch ^ (kr & 15))]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dd = 0; dd < 4; ++dd)
+        for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+            s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dd][kb2], qf[dh2 * 4 + dd], s[kb2], 0, 0, 0);
+      }
+      // mask (only a tile that crosses this wave's diagonal or the key end),
+      // then online softmax in units of log2: p = 2^(s c - m c)
+      const int k0 = t * FBK;
+      if (k0 + FBK - 1 > wfirst || k0 + FBK > kv_valid) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
-          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dd][kb2], qf[dh2 * 4 + dd], s[kb2], 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + kb2 * 32 + 16 * half + e;
+            if (key > qlim || key >= kv_valid) s[kb2][e] = -INFINITY;
+          }
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[kb2][e]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      // masked scores are -inf: with a finite reference they give exp2 = 0;
+      // a row with nothing visible yet uses reference 0 so no NaN appears
+      const float mc = (m_new == -INFINITY) ? 0.f : m_new * scale_log2;
+      const float alpha = __builtin_amdgcn_exp2f(m_run * scale_log2 - mc);
+      float psum = 0.f;
+      bf16x8_t pf[4];   // key steps of 16: (kb2, elements 0..7) and (kb2, 8..15)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float p[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            p[x] = __builtin_amdgcn_exp2f(fmaf(s[kb2][hh * 8 + x], scale_log2, -mc));
+            psum += p[x];
+          }
+          const uint4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                            pack_bf16x2(p[6], p[7])};
+          pf[kb2 * 2 + hh] = __builtin_bit_cast(bf16x8_t, pk);
+        }
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {   // the running max moved for some query of the wave
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
+      }
+      // O^T[d][q] += V^T[d][keys] P^T[keys][q]; key step ks = 2 kb2 + hh
+      // takes, from lane half g, keys 32 kb2 + 16 g + 8 hh .. +7: one
+      // 16-byte chunk of the V^T row
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = db * 32 + (lane & 31);
+          const int ch = 4 * (ks >> 1) + 2 * half + (ks & 1);
+          const uint4 vv = sV[buf][d * 8 + (ch ^ ((d >> 1) & 7))];
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[ks], oacc[db], 0, 0, 0);
+        }
     }
-    // mask + online softmax
-    const int k0 = t * FBK;
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + kb2 * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-        float v = s[kb2][e] * scale_log2;
-        if (key > qlim || key >= kv_valid) v = -INFINITY;
-        s[kb2][e] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    // masked scores are -inf: with a finite reference they give exp2 = 0;
-    // a row with nothing visible yet uses reference 0 so no NaN appears
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.f;
-    bf16x8_t pf[4];   // key steps of 16: (kb2, elements 0..7) and (kb2, 8..15)
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float p[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          p[x] = __builtin_amdgcn_exp2f(s[kb2][hh * 8 + x] - m_use);
-          psum += p[x];
-        }
-        const uint4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                          pack_bf16x2(p[6], p[7])};
-        pf[kb2 * 2 + hh] = __builtin_bit_cast(bf16x8_t, pk);
-      }
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
-    // O^T[d][q] += V^T[d][keys] P^T[keys][q]; key step ks covers keys
-    // 16 ks .. 16 ks + 15 in the slot order of pf
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = db * 32 + (lane & 31);
-        const int key_a = ks * 16 + 4 * half;        // slots 0..3
-        const int key_b = ks * 16 + 8 + 4 * half;    // slots 4..7
-        const uint2* row = (const uint2*)&sV[buf][d * 8];
-        const int sw = (d >> 1) & 7;
-        uint2 va = row[(((key_a >> 3) ^ sw) << 1) + ((key_a >> 2) & 1)];
-        uint2 vb2 = row[(((key_b >> 3) ^ sw) << 1) + ((key_b >> 2) & 1)];
-        if (k0 + FBK > kv_valid) {   // zero V past the buffer's valid keys
-          const int ka = k0 + key_a, kb_ = k0 + key_b;
-          va.x = (ka + 1 < kv_valid) ? va.x : (ka < kv_valid ? (va.x & 0xffffu) : 0u);
-          va.y = (ka + 3 < kv_valid) ? va.y : (ka + 2 < kv_valid ? (va.y & 0xffffu) : 0u);
-          vb2.x = (kb_ + 1 < kv_valid) ? vb2.x : (kb_ < kv_valid ? (vb2.x & 0xffffu) : 0u);
-          vb2.y = (kb_ + 3 < kv_valid) ? vb2.y : (kb_ + 2 < kv_valid ? (vb2.y & 0xffffu) : 0u);
-        }
-        const uint4 vv = {va.x, va.y, vb2.x, vb2.y};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[ks], oacc[db], 0, 0, 0);
-      }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (t + 1 < ntiles && (t + 2) * FBK > kv_valid) {
+      zero_v_tail(buf ^ 1, (t + 1) * FBK);
+      __syncthreads();
+    }
   }
   if (myq < Tq) {
     const float inv = 1.0f / l_run;
