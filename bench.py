@@ -26,6 +26,10 @@ sys.path.insert(0, ROOT)
 METRIC = "recurrent-block token·loops/sec (1 GPU) + % bf16 MFMA peak / % HBM peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+# token-loops/s each workload would reach at the spec peaks: per loop the
+# larger of its MFMA time (algorithmic flops) and its HBM time (touched
+# expert weights once + the other tensors once per fused kernel)
+ROOFLINE_TOKEN_LOOPS = {"mythos_1b": 10.9e6, "mythos_3b": 6.26e6, "mythos_10b_decode": 30.8e3}
 
 
 def log(*a):
@@ -246,6 +250,9 @@ def main():
                                f"{n_loops} loops, ACT {'off' if thr == 0 else thr}",
                    "dim": D, "heads": cfg["n_heads"], "kv_heads": cfg["n_kv_heads"], "experts": cfg["n_experts"],
                    "expert_dim": cfg["expert_dim"], "top_k": cfg["top_k"], "loops_executed": loops_exec},
+        "useful_token_loops_per_s": round(float(halt.sum()) * args.steps / elapsed, 1),
+        "frac_of_workload_roofline": (round(value / ROOFLINE_TOKEN_LOOPS[args.config], 4)
+                                      if args.config in ROOFLINE_TOKEN_LOOPS else None),
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -47,7 +47,8 @@ def build(verbose=False):
         if rc:
             raise RuntimeError(f"hipcc failed on {src}")
     tmp = OUT + ".tmp"
-    rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [r[1] for r in results])
+    rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp]
+                   + [r[1] for r in results])
     if rc:
         print(out, file=sys.stderr)
         raise RuntimeError("link of librdt.so failed")
