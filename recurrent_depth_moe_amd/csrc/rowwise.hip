@@ -446,11 +446,6 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
   const TW* Wd = (const TW*)a.lora_down;
   const TW* Wb = (const TW*)a.lora_B;
   float4 tau[R][NJ];
-  float part[LR][R];
-#pragma unroll
-  for (int r = 0; r < LR; ++r)
-#pragma unroll
-    for (int i = 0; i < R; ++i) part[r][i] = 0.f;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int n = n0 + i;
@@ -479,40 +474,52 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
       }
     }
   }
+  // LoRA down-projection, one rank at a time (few live partial sums)
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int i4 = threadIdx.x + j * RB;
-    if (i4 < D4) {
+  for (int r = 0; r < LR; ++r) {
+    if (r < a.r) {
+      float pr[R];
 #pragma unroll
-      for (int r = 0; r < LR; ++r)
-        if (r < a.r) {
+      for (int i = 0; i < R; ++i) pr[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int i4 = threadIdx.x + j * RB;
+        if (i4 < D4) {
           const float4 wv = ld4(Wd + (int64_t)r * D + i4 * 4);
 #pragma unroll
-          for (int i = 0; i < R; ++i) part[r][i] += dot4(tau[i][j], wv);
+          for (int i = 0; i < R; ++i) pr[i] += dot4(tau[i][j], wv);
         }
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float s = wave_sum(pr[i]);
+        if (lane == 0) red[w][r * R + i] = s;
+      }
     }
   }
-#pragma unroll
-  for (int r = 0; r < LR; ++r)
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-      if (r < a.r) {
-        const float v = wave_sum(part[r][i]);
-        if (lane == 0) red[w][r * R + i] = v;
-      }
   __syncthreads();
-  float lo[LR][R];
+  // LoRA up-projection, one rank at a time (same per-element order over r)
 #pragma unroll
-  for (int r = 0; r < LR; ++r)
+  for (int r = 0; r < LR; ++r) {
+    if (r < a.r) {
+      float lo[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      float v = 0.f;
-      if (r < a.r) {
+      for (int i = 0; i < R; ++i) {
+        float v = 0.f;
         for (int ww = 0; ww < RB / 64; ++ww) v += red[ww][r * R + i];
-        v *= a.lora_scale_row[r];
+        lo[i] = v * a.lora_scale_row[r];
       }
-      lo[r][i] = v;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int i4 = threadIdx.x + j * RB;
+        if (i4 < D4) {
+          const float4 bv = ld4(Wb + (int64_t)r * D + i4 * 4);
+#pragma unroll
+          for (int i = 0; i < R; ++i) tau[i][j] = fma4(lo[i], bv, tau[i][j]);
+        }
+      }
     }
+  }
   float zs[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) zs[i] = 0.f;
@@ -521,13 +528,6 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
     const int i4 = threadIdx.x + j * RB;
     if (i4 < D4) {
       const int d = i4 * 4;
-#pragma unroll
-      for (int r = 0; r < LR; ++r)
-        if (r < a.r) {
-          const float4 bv = ld4(Wb + (int64_t)r * D + d);
-#pragma unroll
-          for (int i = 0; i < R; ++i) tau[i][j] = fma4(lo[r][i], bv, tau[i][j]);
-        }
       const float4 A = ld4(a.A + d), Bv = ld4(a.Bv + d), hw = ld4(a.halt_w + d);
 #pragma unroll
       for (int i = 0; i < R; ++i) {
