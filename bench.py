@@ -183,7 +183,9 @@ def main():
     log(f"[bench] {args.steps} timed steps in {elapsed:.3f}s")
 
     halt = hc.cpu().numpy()
-    loops_exec = n_loops          # every loop runs (halting only weights the output)
+    # loops actually run: with ACT on and no cache the block stops once every
+    # position has halted, i.e. after max(halt_counts) loops
+    loops_exec = int(halt.max()) if (thr > 0 and not cfg["use_cache"]) else n_loops
     ms_step = elapsed / args.steps * 1e3
     value = B * T * loops_exec * args.steps / elapsed
 

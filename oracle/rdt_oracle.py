@@ -415,12 +415,15 @@ class Adoption:
 
 
 def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=None,
-                      adopt=None, record=False):
+                      adopt=None, record=False, stop_when_halted=True):
     """The looped Recurrent Block ([ZS §Recurrent Block]; [RC §아키텍처]).
 
     e, h0: [B, T, D].  Returns dict(out=[B, T, D] float64, halt_counts=[B, T]
-    int, and per-loop records when ``record``).  With act_threshold == 0 the
-    output is the final state; otherwise the ACT-weighted sum of the states.
+    int, loops_run, and per-loop records when ``record``).  With
+    act_threshold == 0 the output is the final state; otherwise the
+    ACT-weighted sum of the states, and the loop stops once every position
+    has halted (nothing returned can change after that) unless a cache is
+    being filled or ``stop_when_halted`` is False.
     """
     e = as_f64(e)
     h = as_f64(h0)
@@ -478,8 +481,11 @@ def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=
             rec["h"].append(h.copy())
             rec["sel"].append(step["sel"].copy())
             rec["margin"].append(step["margin"].copy())
+        loops_run = t + 1
+        if act and stop_when_halted and cache is None and halted.all():
+            break
     out = h_out if act else h
-    res = dict(out=out, halt_counts=counts.reshape(B, T), state=h)
+    res = dict(out=out, halt_counts=counts.reshape(B, T), state=h, loops_run=loops_run)
     if record:
         res["record"] = rec
     return res

@@ -4,12 +4,15 @@
 #include "common.h"
 
 // Any head widths (dq, dv <= 128), fp32 or bf16 storage.
+// `live` (nullable): skip the launch when it points to 0 (every position
+// halted in the previous loop).
 void launch_attn_generic(int dtype_bf16, const void* q, const void* k, const void* vt, void* o, int B, int H,
-                         int G, int Tq, int cap, int dq, int dv, int kbase, float scale, hipStream_t s);
+                         int G, int Tq, int cap, int dq, int dv, int kbase, float scale, hipStream_t s,
+                         const int32_t* live = nullptr);
 // bf16, head width 128, MFMA flash kernel (prefill).  `cap` must be a
 // multiple of 8.
 void launch_attn_flash_bf16(const void* q, const void* k, const void* vt, void* o, int B, int H, int G, int Tq,
-                            int cap, int kbase, float scale, hipStream_t s);
+                            int cap, int kbase, float scale, hipStream_t s, const int32_t* live = nullptr);
 // bf16, head width 128, one query per sequence against the cache (decode
 // step), H / G <= 16, cap >= 4.  Keys are split over blocks of 512; `part`
 // is fp32 scratch of attn_decode_part_floats(B, H, nk) floats.

@@ -17,7 +17,8 @@ template <typename T>
 __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                           const T* __restrict__ vt, T* __restrict__ o,
                                                           int H, int G, int Tq, int cap, int dq, int dv,
-                                                          int kbase, float scale) {
+                                                          int kbase, float scale, const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
   extern __shared__ float sm[];
   float* qs = sm;          // [dq]
   float* sc = sm + 128;    // [nk]
@@ -75,7 +76,9 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
                                                                   const bf16_t* __restrict__ k,
                                                                   const bf16_t* __restrict__ vt,
                                                                   bf16_t* __restrict__ o, int H, int G, int Tq,
-                                                                  int cap, int kbase, float scale_log2) {
+                                                                  int cap, int kbase, float scale_log2,
+                                                                  const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
   __shared__ uint4 sK[2][FBK * 16];   // [key][16 chunks of 8 d], chunk ^ (key & 15)
   __shared__ uint4 sV[2][FD * 8];     // [d][8 chunks of 8 keys], chunk ^ ((d >> 1) & 7)
   const int nqt = (Tq + FBQ - 1) / FBQ;
@@ -450,23 +453,24 @@ __global__ __launch_bounds__(DEC_D) void attn_decode_merge_kernel(const float* _
 }  // namespace
 
 void launch_attn_generic(int dtype_bf16, const void* q, const void* k, const void* vt, void* o, int B, int H,
-                         int G, int Tq, int cap, int dq, int dv, int kbase, float scale, hipStream_t s) {
+                         int G, int Tq, int cap, int dq, int dv, int kbase, float scale, hipStream_t s,
+                         const int32_t* live) {
   const dim3 grid(Tq, B * H), block(64);
   const size_t shm = (128 + (size_t)(kbase + Tq)) * sizeof(float);
   if (dtype_bf16)
     attn_generic_kernel<bf16_t><<<grid, block, shm, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
-                                                         (bf16_t*)o, H, G, Tq, cap, dq, dv, kbase, scale);
+                                                         (bf16_t*)o, H, G, Tq, cap, dq, dv, kbase, scale, live);
   else
     attn_generic_kernel<float><<<grid, block, shm, s>>>((const float*)q, (const float*)k, (const float*)vt,
-                                                        (float*)o, H, G, Tq, cap, dq, dv, kbase, scale);
+                                                        (float*)o, H, G, Tq, cap, dq, dv, kbase, scale, live);
 }
 
 void launch_attn_flash_bf16(const void* q, const void* k, const void* vt, void* o, int B, int H, int G, int Tq,
-                            int cap, int kbase, float scale, hipStream_t s) {
+                            int cap, int kbase, float scale, hipStream_t s, const int32_t* live) {
   const dim3 grid((Tq + FBQ - 1) / FBQ, B * H), block(256);
   const float scale_log2 = scale * 1.4426950408889634f;
   attn_flash_bf16_kernel<<<grid, block, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt, (bf16_t*)o,
-                                                H, G, Tq, cap, kbase, scale_log2);
+                                                H, G, Tq, cap, kbase, scale_log2, live);
 }
 
 int attn_decode_blocks(int nk) { return (nk + DEC_BLK - 1) / DEC_BLK; }

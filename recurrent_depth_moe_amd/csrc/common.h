@@ -35,6 +35,14 @@ template <> struct St<bf16_t> {
   static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
 };
 
+// Loop skipping (ACT on, no cache to fill): every kernel of loop t > 0 gets
+// the count of positions still running after loop t-1 and returns at once
+// when it is 0, since no output can change any more.
+#define RDT_SKIP_IF_ALL_HALTED(live)                  \
+  do {                                                \
+    if ((live) != nullptr && *(live) == 0) return;    \
+  } while (0)
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -49,6 +49,7 @@ struct GemmParams {
   int n_groups;
   int dense_gm;              // dense raster: m-tiles per group of the tile order
   int skinny_mt_cap;         // skinny kernel: m-tiles its grid is sized for
+  const int32_t* live;       // running positions after the previous loop (null: always run)
   EpiParams epi;
 };
 

@@ -13,6 +13,7 @@ namespace {
 
 template <bool DUAL, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
+  RDT_SKIP_IF_ALL_HALTED(p.live);
   constexpr int BM = 64, BN = 64, BK = 16, NB = DUAL ? 2 : 1;
   __shared__ float sA[BK][BM + 4];
   __shared__ float sB[NB][BK][BN + 4];

@@ -252,6 +252,7 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, con
 
 template <bool DUAL, int EPI, typename TO>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
+  RDT_SKIP_IF_ALL_HALTED(p.live);
   constexpr int BM = 256, BN = 256;
   constexpr int WTM = 128, WTN = 128;
   constexpr int A_CH = BM * (BK / 8), B_CH = BN * (BK / 8);   // 16-byte chunks per stage

@@ -16,6 +16,7 @@ namespace {
 
 template <int NC, bool DUAL, int EPI, typename TO>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
+  RDT_SKIP_IF_ALL_HALTED(p.live);
   constexpr int NF = NC / 32, NB = DUAL ? 2 : 1, NA = NB * NF;
   __shared__ float red[4][NA][16 * 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;

@@ -16,20 +16,20 @@ void launch_make_A(const float* log_A, const float* log_dt, float* A, int D, hip
 // c = RMSNorm(h + emb_t + e) * g_rec (fp32); a = RMSNorm(c) * g_attn (bf16 or fp32)
 void launch_loop_head(int act_bf16, const float* h, const float* e, const float* emb_t, int loop_dim,
                       const float* g_rec, const float* g_attn, float eps, float* c, void* a, int N, int D,
-                      hipStream_t s);
+                      hipStream_t s, const int32_t* live_prev = nullptr, int32_t* live_cur = nullptr);
 // out[r] = RMSNorm(x[r]) * g for rows r < rows; x fp32 with row stride ldx,
 // out (bf16 or fp32) with stride ldo
 void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, float eps, void* out, int64_t ldo,
-                    int rows, int D, hipStream_t s);
+                    int rows, int D, hipStream_t s, const int32_t* live = nullptr);
 
 // softmax over E logits, top-k of logits + bias (descending, ties to the
 // lower index), gates renormalised over the chosen experts
 void launch_router_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* sel, float* gate,
-                        int32_t* cap_sel, hipStream_t s);
+                        int32_t* cap_sel, hipStream_t s, const int32_t* live = nullptr);
 // dropless dispatch: stable order (token, slot) inside each expert
 void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,
                      int32_t* mt_start, int32_t* tile_row0, int32_t* tile_grp, int32_t* perm_src, int32_t* inv,
-                     hipStream_t s);
+                     hipStream_t s, const int32_t* live = nullptr);
 
 struct TailArgs {
   const float* x1;        // [N][D]
@@ -57,13 +57,16 @@ struct TailArgs {
   float* cap_h;           // [N][D] slice of loop t, or null
   float* cap_p;           // [N] slice of loop t, or null
   int w_bf16;
+  const int32_t* live_prev;  // running positions after loop t-1, or null (never skip)
+  int32_t* live_cur;         // running positions after this loop are added here, or null
 };
 void launch_loop_tail(const TailArgs& a, hipStream_t s);
 
 // MLA glue (see attention.hip for buffer layouts)
 void launch_mla_latent(int act_bf16, const float* kv_raw, const float* cq_raw, const float* gq, float eps, int N,
                        int T, int ql, int kvl, int rope, int start_pos, const float* rcos, const float* rsin,
-                       void* cq_norm, void* lat_ckv, void* lat_krope, int lat_cap, int kbase, hipStream_t s);
+                       void* cq_norm, void* lat_ckv, void* lat_krope, int lat_cap, int kbase, hipStream_t s,
+                       const int32_t* live = nullptr);
 void launch_mla_kv_prep(int act_bf16, const void* lat_ckv, const void* lat_krope, int lat_cap, const float* gkv,
                         float eps, int B, int kvlen, int kvl, int rope, int H, int dq, void* ckv_norm, void* K,
-                        hipStream_t s);
+                        hipStream_t s, const int32_t* live = nullptr);

@@ -68,7 +68,12 @@ __global__ __launch_bounds__(RB) void loop_head_kernel(const float* __restrict__
                                                        const float* __restrict__ emb, int loop_dim,
                                                        const float* __restrict__ g_rec,
                                                        const float* __restrict__ g_attn, float eps,
-                                                       float* __restrict__ c, TA* __restrict__ a, int D) {
+                                                       float* __restrict__ c, TA* __restrict__ a, int D,
+                                                       const int32_t* live_prev, int32_t* live_cur) {
+  // this loop's running count starts at 0 (the tail adds to it), also when
+  // the loop itself is skipped, so a skip carries on to every later loop
+  if (live_cur && blockIdx.x == 0 && threadIdx.x == 0) *live_cur = 0;
+  RDT_SKIP_IF_ALL_HALTED(live_prev);
   __shared__ float red[RB / 64];
   const int64_t base = (int64_t)blockIdx.x * D;
   const int D4 = D >> 2;
@@ -121,7 +126,8 @@ __global__ __launch_bounds__(RB) void loop_head_kernel(const float* __restrict__
 template <typename TO>
 __global__ __launch_bounds__(RB) void rmsnorm_kernel(const float* __restrict__ x, int64_t ldx,
                                                      const float* __restrict__ g, float eps, TO* __restrict__ out,
-                                                     int64_t ldo, int D) {
+                                                     int64_t ldo, int D, const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
   __shared__ float red[RB / 64];
   const float* xr = x + (int64_t)blockIdx.x * ldx;
   TO* orow = out + (int64_t)blockIdx.x * ldo;
@@ -154,7 +160,8 @@ __global__ __launch_bounds__(RB) void rmsnorm_kernel(const float* __restrict__ x
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
                                                           const float* __restrict__ bias, int N, int E, int k,
                                                           int32_t* __restrict__ sel, float* __restrict__ gate,
-                                                          int32_t* __restrict__ cap_sel) {
+                                                          int32_t* __restrict__ cap_sel, const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= N) return;
@@ -220,7 +227,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 // ------------------------------------------------------------ dispatch
 // counts per expert for each tile of 256 (token, slot) assignments
 __global__ __launch_bounds__(RDT_DISP_TILE) void dispatch_count_kernel(const int32_t* __restrict__ sel, int NK,
-                                                                       int E, int32_t* __restrict__ tile_counts) {
+                                                                       int E, int32_t* __restrict__ tile_counts,
+                                                                       const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
   __shared__ int cnt[RDT_MAX_EXPERTS];
   for (int i = threadIdx.x; i < E; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
@@ -237,7 +246,9 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
                                                                         int32_t* __restrict__ offsets,
                                                                         int32_t* __restrict__ mt_start,
                                                                         int32_t* __restrict__ tile_row0,
-                                                                        int32_t* __restrict__ tile_grp) {
+                                                                        int32_t* __restrict__ tile_grp,
+                                                                        const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
   __shared__ int tot[RDT_MAX_EXPERTS];
   __shared__ int off[RDT_MAX_EXPERTS + 1];
   __shared__ int mts[RDT_MAX_EXPERTS + 1];
@@ -284,7 +295,9 @@ __global__ __launch_bounds__(RDT_DISP_TILE) void dispatch_scatter_kernel(const i
                                                                          int k, int E,
                                                                          const int32_t* __restrict__ tile_base,
                                                                          int32_t* __restrict__ perm_src,
-                                                                         int32_t* __restrict__ inv) {
+                                                                         int32_t* __restrict__ inv,
+                                                                         const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
   __shared__ int wcnt[RDT_DISP_TILE / 64][RDT_MAX_EXPERTS];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < (RDT_DISP_TILE / 64) * RDT_MAX_EXPERTS; i += blockDim.x) (&wcnt[0][0])[i] = 0;
@@ -317,6 +330,7 @@ __global__ __launch_bounds__(RDT_DISP_TILE) void dispatch_scatter_kernel(const i
 // update ([ZS §ACT], [ZS §Recurrent Block]).
 template <typename TW>
 __global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
+  RDT_SKIP_IF_ALL_HALTED(a.live_prev);
   __shared__ float red[RDT_MAX_LORA + 1][RB / 64];
   const int n = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int D = a.D, D4 = D >> 2;
@@ -431,6 +445,7 @@ __global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
     a.cum[n] = running ? cum + p : cum;
     a.halt_counts[n] = halt_now ? a.t + 1 : hc;
     if (a.cap_p) a.cap_p[n] = p;
+    if (a.live_cur && running && !halt_now) atomicAdd(a.live_cur, 1);
   }
 }
 
@@ -440,6 +455,7 @@ __global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
 // (+256 j) of every row.
 template <typename TW, int R, int NJ, int LR>
 __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
+  RDT_SKIP_IF_ALL_HALTED(a.live_prev);
   __shared__ float red[RB / 64][LR * R + R];
   const int n0 = blockIdx.x * R, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int D = a.D, D4 = D >> 2;
@@ -567,6 +583,7 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
     if (lane == 0) red[w][LR * R + i] = v;
   }
   __syncthreads();
+  int still = 0;   // rows of this block still running after this loop
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int n = n0 + i;
@@ -600,7 +617,9 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
       a.halt_counts[n] = halt_now ? a.t + 1 : hc;
       if (a.cap_p) a.cap_p[n] = p;
     }
+    still += (running && !halt_now) ? 1 : 0;
   }
+  if (a.live_cur && threadIdx.x == 0 && still > 0) atomicAdd(a.live_cur, still);
 }
 
 // ------------------------------------------------------------ MLA glue
@@ -615,7 +634,8 @@ __global__ __launch_bounds__(64) void mla_latent_kernel(const float* __restrict_
                                                         const float* __restrict__ rcos,
                                                         const float* __restrict__ rsin, TA* __restrict__ cq_norm,
                                                         TA* __restrict__ lat_ckv, TA* __restrict__ lat_krope,
-                                                        int lat_cap, int kbase) {
+                                                        int lat_cap, int kbase, const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
   const int n = blockIdx.x, b = n / T, i = n - b * T, lane = threadIdx.x;
   const float* cq = cq_raw + (int64_t)n * ql;
   float ss = 0.f;
@@ -639,7 +659,9 @@ __global__ __launch_bounds__(64) void mla_kv_prep_kernel(const TA* __restrict__ 
                                                          const TA* __restrict__ lat_krope, int lat_cap,
                                                          const float* __restrict__ gkv, float eps, int kvlen,
                                                          int kvl, int rope, int H, int dq,
-                                                         TA* __restrict__ ckv_norm, TA* __restrict__ K) {
+                                                         TA* __restrict__ ckv_norm, TA* __restrict__ K,
+                                                         const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
   const int m = blockIdx.x, b = m / kvlen, j = m - b * kvlen, lane = threadIdx.x;
   const TA* c = lat_ckv + ((int64_t)b * lat_cap + j) * kvl;
   float ss = 0.f;
@@ -673,33 +695,35 @@ void launch_make_A(const float* log_A, const float* log_dt, float* A, int D, hip
 
 void launch_loop_head(int act_bf16, const float* h, const float* e, const float* emb_t, int loop_dim,
                       const float* g_rec, const float* g_attn, float eps, float* c, void* a, int N, int D,
-                      hipStream_t s) {
+                      hipStream_t s, const int32_t* live_prev, int32_t* live_cur) {
   if (act_bf16)
-    loop_head_kernel<bf16_t><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (bf16_t*)a, D);
+    loop_head_kernel<bf16_t><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (bf16_t*)a, D, live_prev,
+                                              live_cur);
   else
-    loop_head_kernel<float><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (float*)a, D);
+    loop_head_kernel<float><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (float*)a, D, live_prev,
+                                             live_cur);
 }
 
 void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, float eps, void* out, int64_t ldo,
-                    int rows, int D, hipStream_t s) {
+                    int rows, int D, hipStream_t s, const int32_t* live) {
   if (rows <= 0) return;
-  if (out_bf16) rmsnorm_kernel<bf16_t><<<rows, RB, 0, s>>>(x, ldx, g, eps, (bf16_t*)out, ldo, D);
-  else rmsnorm_kernel<float><<<rows, RB, 0, s>>>(x, ldx, g, eps, (float*)out, ldo, D);
+  if (out_bf16) rmsnorm_kernel<bf16_t><<<rows, RB, 0, s>>>(x, ldx, g, eps, (bf16_t*)out, ldo, D, live);
+  else rmsnorm_kernel<float><<<rows, RB, 0, s>>>(x, ldx, g, eps, (float*)out, ldo, D, live);
 }
 
 void launch_router_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* sel, float* gate,
-                        int32_t* cap_sel, hipStream_t s) {
-  router_topk_kernel<<<(N + 3) / 4, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel);
+                        int32_t* cap_sel, hipStream_t s, const int32_t* live) {
+  router_topk_kernel<<<(N + 3) / 4, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
 }
 
 void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,
                      int32_t* mt_start, int32_t* tile_row0, int32_t* tile_grp, int32_t* perm_src, int32_t* inv,
-                     hipStream_t s) {
+                     hipStream_t s, const int32_t* live) {
   const int ntiles = (NK + RDT_DISP_TILE - 1) / RDT_DISP_TILE;
-  dispatch_count_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, E, tile_counts);
+  dispatch_count_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, E, tile_counts, live);
   dispatch_scan_kernel<<<1, RDT_MAX_EXPERTS, 0, s>>>(tile_counts, ntiles, E, bm, offsets, mt_start, tile_row0,
-                                                     tile_grp);
-  dispatch_scatter_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, k, E, tile_counts, perm_src, inv);
+                                                     tile_grp, live);
+  dispatch_scatter_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, k, E, tile_counts, perm_src, inv, live);
 }
 
 template <typename TW, int LR>
@@ -728,25 +752,27 @@ void launch_loop_tail(const TailArgs& a, hipStream_t s) {
 
 void launch_mla_latent(int act_bf16, const float* kv_raw, const float* cq_raw, const float* gq, float eps, int N,
                        int T, int ql, int kvl, int rope, int start_pos, const float* rcos, const float* rsin,
-                       void* cq_norm, void* lat_ckv, void* lat_krope, int lat_cap, int kbase, hipStream_t s) {
+                       void* cq_norm, void* lat_ckv, void* lat_krope, int lat_cap, int kbase, hipStream_t s,
+                       const int32_t* live) {
   if (act_bf16)
     mla_latent_kernel<bf16_t><<<N, 64, 0, s>>>(kv_raw, cq_raw, gq, eps, T, ql, kvl, rope, start_pos, rcos, rsin,
                                                (bf16_t*)cq_norm, (bf16_t*)lat_ckv, (bf16_t*)lat_krope, lat_cap,
-                                               kbase);
+                                               kbase, live);
   else
     mla_latent_kernel<float><<<N, 64, 0, s>>>(kv_raw, cq_raw, gq, eps, T, ql, kvl, rope, start_pos, rcos, rsin,
-                                              (float*)cq_norm, (float*)lat_ckv, (float*)lat_krope, lat_cap, kbase);
+                                              (float*)cq_norm, (float*)lat_ckv, (float*)lat_krope, lat_cap, kbase,
+                                              live);
 }
 
 void launch_mla_kv_prep(int act_bf16, const void* lat_ckv, const void* lat_krope, int lat_cap, const float* gkv,
                         float eps, int B, int kvlen, int kvl, int rope, int H, int dq, void* ckv_norm, void* K,
-                        hipStream_t s) {
+                        hipStream_t s, const int32_t* live) {
   if (act_bf16)
     mla_kv_prep_kernel<bf16_t><<<B * kvlen, 64, 0, s>>>((const bf16_t*)lat_ckv, (const bf16_t*)lat_krope, lat_cap,
                                                         gkv, eps, kvlen, kvl, rope, H, dq, (bf16_t*)ckv_norm,
-                                                        (bf16_t*)K);
+                                                        (bf16_t*)K, live);
   else
     mla_kv_prep_kernel<float><<<B * kvlen, 64, 0, s>>>((const float*)lat_ckv, (const float*)lat_krope, lat_cap,
                                                        gkv, eps, kvlen, kvl, rope, H, dq, (float*)ckv_norm,
-                                                       (float*)K);
+                                                       (float*)K, live);
 }

@@ -96,12 +96,12 @@ rdt_status check_config(const rdt_config* c) {
 enum WsId {
   WS_H, WS_C, WS_A, WS_Q, WS_K, WS_VT, WS_O, WS_X1, WS_F, WS_LOGITS, WS_SEL, WS_GATE, WS_TILECNT, WS_OFFSETS,
   WS_MTSTART, WS_TROW0, WS_TGRP, WS_PERM, WS_INV, WS_ACT, WS_Y, WS_ACTS, WS_YS, WS_CUM,
-  WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_DPART, WS_COUNT
+  WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_DPART, WS_LIVE, WS_COUNT
 };
 const char* kWsNames[WS_COUNT] = {"h", "c", "a", "q", "k", "vt", "o", "x1", "f", "logits", "sel", "gate",
                                   "tile_counts", "offsets", "mt_start", "tile_row0", "tile_grp", "perm", "inv",
                                   "act", "y", "act_s", "y_s", "cum", "kv_raw", "cq_raw", "cq_norm", "lat_ckv",
-                                  "lat_krope", "ckv_norm", "attn_part"};
+                                  "lat_krope", "ckv_norm", "attn_part", "live"};
 
 struct Plan {
   int B, T, N, NK, kvcap, kvlen_max, bm, max_mt, disp_tiles;
@@ -176,6 +176,7 @@ Plan make_plan(const rdt_config& c, int B, int T) {
     s[WS_CKVN] = (size_t)B * p.kvlen_max * kvl * es;
   }
   if (use_decode_attn(c, T)) s[WS_DPART] = attn_decode_part_floats(B, c.n_heads, p.kvlen_max) * 4;
+  s[WS_LIVE] = 2 * 4;   // running-position counts of the previous and the current loop
   size_t o = 0;
   for (int i = 0; i < WS_COUNT; ++i) {
     p.off[i] = o;
@@ -633,10 +634,18 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   const int cap_pad = round_up(kv_capacity > 0 ? kv_capacity : 1, 64);
   const size_t slot = kv ? kv_slot_bytes(c, B, kv_capacity) : 0;
   const float scale = 1.0f / sqrtf((float)dq);
+  // Once every position has halted nothing the call returns can change, so
+  // with ACT on and no cache to fill every kernel of the later loops exits
+  // at once: loop t's kernels read the count of positions still running
+  // after loop t-1 (two alternating counters in the workspace).
+  int32_t* const live_buf = (thr > 0.f && !kv) ? WI(WS_LIVE) : nullptr;
+  const int32_t* live_prev = nullptr;
+  int32_t* live_cur = nullptr;
 
   // bf16: the 256x256 kernel for prefill products, the skinny kernel for
   // single-token steps and for narrow outputs (router logits)
   auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16, bool narrow = false) {
+    gp.live = live_prev;
     if (!bf) {
       launch_gemm_f32(gp, epi, dual, b->n_cu, s);
       return;
@@ -664,11 +673,13 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
 
   for (int t = 0; t < n_loops; ++t) {
     const float* hp = t == 0 ? h0 : WF(WS_H);
+    live_prev = (live_buf && t > 0) ? live_buf + ((t - 1) & 1) : nullptr;
+    live_cur = live_buf ? live_buf + (t & 1) : nullptr;
     // a1-a3: loop-index embedding, re-injection of e, RMSNorms
     {
       StageTimer st_(b, s, RDT_STAGE_LOOP_HEAD);
       launch_loop_head(bf, hp, e, b->loop_emb + (size_t)t * c.loop_dim, c.loop_dim, b->g_rec, b->g_attn, c.norm_eps,
-                     WF(WS_C), W(WS_A), N, D, s);
+                     WF(WS_C), W(WS_A), N, D, s, live_prev, live_cur);
     }
     // a4-a6: attention
     char* kslot = kv ? (char*)kv + slot * t : nullptr;
@@ -699,11 +710,11 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       }
       StageTimer st_(b, s, RDT_STAGE_ATTN);
       if (bf && T > 1)
-        launch_attn_flash_bf16(W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, kbase, scale, s);
+        launch_attn_flash_bf16(W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, kbase, scale, s, live_prev);
       else if (kv && use_decode_attn(c, T))
         launch_attn_decode_bf16(W(WS_Q), K, VT, W(WS_O), WF(WS_DPART), B, H, G, cap, kbase + 1, scale, s);
       else
-        launch_attn_generic(bf, W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, dq, dv, kbase, scale, s);
+        launch_attn_generic(bf, W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, dq, dv, kbase, scale, s, live_prev);
     } else {
       StageTimer st_(b, s, RDT_STAGE_ATTN);
       const int ql = c.q_lora_rank, kvl = c.kv_lora_rank, rope = c.qk_rope_head_dim, nope = c.qk_nope_head_dim;
@@ -721,7 +732,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       g2.epi.ldo = ql;
       gemm(g2, EPI_STORE, false, 0);
       launch_mla_latent(bf, WF(WS_KVRAW), WF(WS_CQRAW), b->gq, c.norm_eps, N, T, ql, kvl, rope, start_pos,
-                        b->rope_cos, b->rope_sin, W(WS_CQN), lat_c, lat_r, lat_cap, kbase, s);
+                        b->rope_cos, b->rope_sin, W(WS_CQN), lat_c, lat_r, lat_cap, kbase, s, live_prev);
       GemmParams g3 = dense(W(WS_CQN), ql, b->wuq, nullptr, N, H * dq, ql);
       g3.epi.q = W(WS_Q);
       g3.epi.T = T;
@@ -734,7 +745,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       g3.epi.rot_half = rope / 2;
       gemm(g3, EPI_MLA_Q, false, bf);
       launch_mla_kv_prep(bf, lat_c, lat_r, lat_cap, b->gkv, c.norm_eps, B, kvlen, kvl, rope, H, dq, W(WS_CKVN),
-                         W(WS_K), s);
+                         W(WS_K), s, live_prev);
       GemmParams g4 = dense(W(WS_CKVN), kvl, b->wukv, nullptr, B * kvlen, H * (nope + dv), kvl);
       g4.epi.k = W(WS_K);
       g4.epi.vt = W(WS_VT);
@@ -745,7 +756,8 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       g4.epi.nope = nope;
       g4.epi.cap = kvlen;
       gemm(g4, EPI_MLA_KV, false, bf);
-      launch_attn_generic(bf, W(WS_Q), W(WS_K), W(WS_VT), W(WS_O), B, H, H, T, kvlen, dq, dv, kbase, scale, s);
+      launch_attn_generic(bf, W(WS_Q), W(WS_K), W(WS_VT), W(WS_O), B, H, H, T, kvlen, dq, dv, kbase, scale, s,
+                          live_prev);
     }
     // a7: x1 = c + o Wo^T
     {
@@ -759,7 +771,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     // a8: f = RMSNorm(x1) * g_ffn
     {
       StageTimer st_(b, s, RDT_STAGE_FFN_NORM);
-      launch_rmsnorm(bf, WF(WS_X1), D, b->g_ffn, c.norm_eps, W(WS_F), D, N, D, s);
+      launch_rmsnorm(bf, WF(WS_X1), D, b->g_ffn, c.norm_eps, W(WS_F), D, N, D, s, live_prev);
     }
     // a9: router logits, softmax, top-k
     {
@@ -769,13 +781,13 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gp.epi.ldo = E;
       gemm(gp, EPI_STORE, false, 0, true);
       launch_router_topk(WF(WS_LOGITS), b->router_bias, N, E, k, WI(WS_SEL), WF(WS_GATE),
-                         b->cap_sel ? b->cap_sel + (size_t)t * N * k : nullptr, s);
+                         b->cap_sel ? b->cap_sel + (size_t)t * N * k : nullptr, s, live_prev);
     }
     // a10: dispatch
     {
       StageTimer st_(b, s, RDT_STAGE_DISPATCH);
       launch_dispatch(WI(WS_SEL), p.NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART),
-                      WI(WS_TROW0), WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), s);
+                      WI(WS_TROW0), WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), s, live_prev);
     }
     // a11: routed gate|up + SwiGLU, rows gathered from f
     {
@@ -864,6 +876,8 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       ta.cap_h = b->cap_h ? b->cap_h + (size_t)t * N * D : nullptr;
       ta.cap_p = (b->cap_p && thr > 0.f) ? b->cap_p + (size_t)t * N : nullptr;
       ta.w_bf16 = bf;
+      ta.live_prev = live_prev;
+      ta.live_cur = live_cur;
       StageTimer st_(b, s, RDT_STAGE_TAIL);
       launch_loop_tail(ta, s);
     }

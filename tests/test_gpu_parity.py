@@ -51,8 +51,11 @@ def _e2e(cfg, W, e, h0, **kw):
     assert adopt.route_disagree == 0
     assert adopt.halt_disagree == 0
     N = e.shape[0] * e.shape[1]
-    for t in range(cfg["n_loops"]):
+    for t in range(ref["loops_run"]):
         np.testing.assert_array_equal(ref["record"]["sel"][t], g["sel"][t].reshape(N, -1))
+    # loops after every position halted are skipped on both sides: their capture slots stay untouched
+    for t in range(ref["loops_run"], cfg["n_loops"]):
+        assert np.all(g["sel"][t] == -1)
     np.testing.assert_array_equal(ref["halt_counts"], g["halt"])
     err = rel_err(g["out"], ref["out"])
     print(f"  max|d|/rms = {err:.3e} (tol {TOL[dt]})", flush=True)
@@ -76,6 +79,17 @@ def test_end_to_end_large_terms(name):
     g, ref = _e2e(cfg, W, e, h0)
     if cfg["act_threshold"] > 0:
         assert len(np.unique(g["halt"])) > 1
+
+
+@pytest.mark.parametrize("name", ["tiny_gqa", "tiny_mla", "small_bf16"])
+def test_end_to_end_stops_once_all_halted(name):
+    """Every position halts by loop 2: the remaining loops are skipped on the
+    GPU (their capture slots stay untouched) and on the oracle, with the
+    same output and halt counts."""
+    cfg, W, e, h0 = _inputs(name, scales={"halt_w": 0.005, "halt_b": 3.0})
+    g, ref = _e2e(cfg, W, e, h0)
+    assert ref["loops_run"] < cfg["n_loops"]
+    assert g["halt"].max() == ref["loops_run"]
 
 
 @pytest.mark.parametrize("name", ["tiny_gqa", "small_bf16"])
@@ -223,3 +237,30 @@ def test_prefill_then_decode_matches_full_prefill(name):
     assert rel_err(g["out"][:, 0], full["out"][:, T - 1]) < tol
     ref = O.recurrent_forward(cfg, O.Params(W), e, h0, n, 0.0)["out"]
     assert rel_err(g["out"][:, 0], ref[:, T - 1]) < tol
+
+
+@pytest.mark.parametrize("name,act", [("tiny_gqa", True), ("tiny_mla", True), ("small_bf16", False)])
+def test_chained_decode_steps_match_full_prefill(name, act):
+    """Prefill of positions 0..T-5, then four chained decode steps at
+    T-4 .. T-1, each appending to the same per-loop caches, reproduce the
+    last four rows of a full prefill, ACT output and halt counts included
+    ([ZS §RoPE & generation cache])."""
+    import torch
+    from recurrent_depth_moe_amd import binding
+    over = {} if act else {"act_threshold": 0.0}
+    cfg, W, e, h0 = _inputs(name, **over)
+    B, T, n = cfg["batch"], cfg["seq"], cfg["n_loops"]
+    steps = 4
+    cfgc = dict(cfg, start_pos=0)
+    kv = torch.zeros(binding.kv_cache_bytes(cfg, B, T, n), dtype=torch.uint8, device="cuda")
+    full = GpuRun(cfg, W, e, h0).np()
+    P0 = T - steps
+    GpuRun(dict(cfgc, seq=P0), W, e[:, :P0].copy(), h0[:, :P0].copy(), kv=kv, start_pos=0, capture=False, kv_cap=T)
+    tol = TOL[cfg["dtype"]]
+    for i in range(P0, T):
+        g = GpuRun(dict(cfgc, seq=1, start_pos=i), W, e[:, i:i + 1].copy(), h0[:, i:i + 1].copy(), kv=kv,
+                   decode=True, kv_cap=T).np()
+        print(f"[chained decode] {name} position {i}: max|d|/rms {rel_err(g['out'][:, 0], full['out'][:, i]):.2e}",
+              flush=True)
+        assert rel_err(g["out"][:, 0], full["out"][:, i]) < tol
+        np.testing.assert_array_equal(g["halt"][:, 0], full["halt"][:, i])

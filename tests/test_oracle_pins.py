@@ -236,6 +236,24 @@ def test_depthwise_lora_closed_form_and_clamp():
 
 # ---------------------------------------------------------------- ACT
 
+def test_stop_once_all_halted_changes_nothing():
+    """With every position halted by loop 2, stopping there returns the same
+    output and halt counts as running all loops (the later loops only move
+    h, which the ACT output no longer weights)."""
+    scales = {"halt_w": 0.02, "halt_b": 1.0}
+    cfg, W, P, e, h0 = _setup("tiny_gqa", scales=scales)
+    n = 4
+    stop = O.recurrent_forward(cfg, P, e, h0, n, cfg["act_threshold"])
+    full = O.recurrent_forward(cfg, P, e, h0, n, cfg["act_threshold"], stop_when_halted=False)
+    assert stop["loops_run"] < n and full["loops_run"] == n
+    np.testing.assert_array_equal(stop["out"], full["out"])
+    np.testing.assert_array_equal(stop["halt_counts"], full["halt_counts"])
+    assert stop["halt_counts"].max() == stop["loops_run"]
+    # with a cache being filled every loop runs
+    cache = O.new_cache(cfg, cfg["batch"], cfg["seq"], n)
+    assert O.recurrent_forward(cfg, P, e, h0, n, cfg["act_threshold"], cache=cache)["loops_run"] == n
+
+
 @pytest.mark.parametrize("name", ["tiny_gqa", "tiny_mla", "small_f32"])
 def test_act_weights_sum_to_one_and_first_crossing(name):
     """Halting weights sum to 1 per position; the halt count is the first
@@ -245,7 +263,7 @@ def test_act_weights_sum_to_one_and_first_crossing(name):
     scales = {"halt_w": 0.05, "halt_b": -0.8}
     cfg, W, P, e, h0 = _setup(name, scales=scales)
     n = cfg["n_loops"]
-    on = O.recurrent_forward(cfg, P, e, h0, n, cfg["act_threshold"], record=True)
+    on = O.recurrent_forward(cfg, P, e, h0, n, cfg["act_threshold"], record=True, stop_when_halted=False)
     off = O.recurrent_forward(cfg, P, e, h0, n, 0.0, record=True)
     wsum = np.sum(on["record"]["weight"], axis=0)
     np.testing.assert_allclose(wsum, 1.0, rtol=0, atol=1e-12)
