@@ -133,7 +133,10 @@ rdt_status rdt_kv_cache_bytes(const rdt_block* blk, int32_t B, int32_t capacity,
  * start_pos:  absolute position of token 0 (RoPE and causal mask).
  * act_threshold: 0 = ACT off (h_out = final h, halt_counts = n_loops);
  *             in (0, 1] = ACT on (h_out = sum_t weight_t * h_t, halt_counts
- *             = 1-based loop of each position's remainder step).
+ *             = 1-based loop of each position's remainder step).  With ACT
+ *             on and no cache, the loops after every position has halted
+ *             are skipped on the device (nothing returned can change; the
+ *             per-loop capture slots of skipped loops are left untouched).
  * kv_cache:   NULL, or a cache of kv_bytes bytes with `kv_capacity`
  *             positions per slot; positions [start_pos, start_pos+T) of the
  *             first n_loops slots are written and attention reads [0, pos].
@@ -177,8 +180,10 @@ rdt_status rdt_set_capture(rdt_block* blk, float* h_loops, int32_t* sel_loops, f
  * last loop run (for stage-level tests).  Names: "c", "a", "q", "k", "vt",
  * "o", "x1", "f", "logits", "sel", "gate", "tile_counts", "offsets",
  * "mt_start", "tile_row0", "tile_grp", "perm", "inv", "act", "y", "act_s",
- * "y_s", "h", "cum" (and for MLA "kv_raw", "cq_raw", "cq_norm", "lat_ckv",
- * "lat_krope", "ckv_norm").  INVALID_ARG for other names. */
+ * "y_s", "h", "cum", "live" (running-position counts of the last two loops
+ * when ACT is on without a cache), "attn_part" (split-KV partials of a bf16
+ * decode step; 0 bytes otherwise) and for MLA "kv_raw", "cq_raw", "cq_norm",
+ * "lat_ckv", "lat_krope", "ckv_norm".  INVALID_ARG for other names. */
 rdt_status rdt_workspace_offset(const rdt_block* blk, int32_t B, int32_t T, const char* name,
                                 size_t* offset, size_t* bytes);
 
