@@ -33,29 +33,32 @@
 namespace {
 
 // Issue order of the first half of a stage: a fragment read of the second
-// half after each of the first 16 MFMAs.
+// half after each of the first MFMAs (NM MFMAs, ND fragment reads).
+template <int NM, int ND>
 __device__ __forceinline__ void interleave_first_half() {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < ND; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - ND, 0);
 }
-// Second half: the 16 global->LDS loads of stage k+2 first (their latency
-// is what the pipeline must hide), then the reads of the next stage's first
-// half, one after each MFMA.
+// Second half: the NV global->LDS loads of the next stages first (their
+// latency is what the pipeline must hide), then the reads of the next
+// stage's first half, one after each MFMA.
+template <int NM, int ND, int NV>
 __device__ __forceinline__ void interleave_second_half() {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NV; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < ND; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
   }
+  if constexpr (NM > NV + ND) __builtin_amdgcn_sched_group_barrier(0x008, NM - NV - ND, 0);
 }
 
 constexpr int BK = 64;                               // k depth of one LDS stage
@@ -77,15 +80,16 @@ __device__ __forceinline__ void g2lds(const void* src, uint4* lds_slot0) {
 // Rows hold 8 chunks of 8 k (128 bytes); chunk c of row r sits at position
 // c ^ ((r >> 1) & 7), so the 8 rows a quarter-wave reads land in distinct
 // banks.
+template <int WNF>
 __device__ __forceinline__ void read_frags(const uint4* sA, const uint4* sB, int wm, int wn, int lane, int hh,
-                                           bf16x8_t (&af)[8], bf16x8_t (&bf)[8]) {
+                                           bf16x8_t (&af)[8], bf16x8_t (&bf)[2 * WNF]) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int c = 4 * hh + 2 * s + (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 128 + j * 32 + (lane & 31);
-      bf[s * 4 + j] = __builtin_bit_cast(bf16x8_t, sB[r * 8 + (c ^ ((r >> 1) & 7))]);
+    for (int j = 0; j < WNF; ++j) {
+      const int r = wn * (32 * WNF) + j * 32 + (lane & 31);
+      bf[s * WNF + j] = __builtin_bit_cast(bf16x8_t, sB[r * 8 + (c ^ ((r >> 1) & 7))]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -95,15 +99,16 @@ __device__ __forceinline__ void read_frags(const uint4* sA, const uint4* sB, int
   }
 }
 
-__device__ __forceinline__ void mfma_stage(const bf16x8_t (&af)[8], const bf16x8_t (&bf)[8],
-                                           floatx16_t (&acc)[4][4]) {
+template <int WNF>
+__device__ __forceinline__ void mfma_stage(const bf16x8_t (&af)[8], const bf16x8_t (&bf)[2 * WNF],
+                                           floatx16_t (&acc)[4][WNF]) {
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s * 4 + i], bf[s * 4 + j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < WNF; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s * 4 + i], bf[s * WNF + j], acc[i][j], 0, 0, 0);
 }
 
 // wait until at most `n` direct-to-LDS loads of this wave are in flight
@@ -250,11 +255,15 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, con
   __syncthreads();   // the next tile's loads reuse this LDS
 }
 
-template <bool DUAL, int EPI, typename TO>
+// WNF = 32-column fragments per wave: 4 (256-column tiles) or 3 (192, for
+// dense products whose 256-column tile count leaves the last round of CUs
+// half idle)
+template <bool DUAL, int EPI, typename TO, int WNF>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
+  static_assert(WNF == 4 || (WNF == 3 && !DUAL), "gate|up tiles are 256 columns wide");
   RDT_SKIP_IF_ALL_HALTED(p.live);
-  constexpr int BM = 256, BN = 256;
-  constexpr int WTM = 128, WTN = 128;
+  constexpr int BM = 256, BN = 64 * WNF;
+  constexpr int WTM = 128, WTN = 32 * WNF;
   constexpr int A_CH = BM * (BK / 8), B_CH = BN * (BK / 8);   // 16-byte chunks per stage
   constexpr int A_IT = A_CH / 256, B_IT = B_CH / 256;
   constexpr int NCOL = DUAL ? BN / 2 : BN;       // output columns per tile
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       for (int j = 0; j < B_IT; ++j) g2lds(bsrc[j] + k0, sBbuf + buf * B_CH + (j * 4 + w) * 64);
     };
 
-    if constexpr (EPI != EPI_QKV) {   // (QKV rows come in full tiles but the last; its epilogue is the heaviest)
+    if constexpr (EPI != EPI_QKV && WNF == 4) {   // (QKV rows come in full tiles but the last; its epilogue is the heaviest)
       if (rows <= 64) {
         small_tile<64, DUAL, EPI, TO>(p, smem, asrc, bsrc, w, lane, rows, row0, n0, KT);
         continue;
@@ -335,11 +344,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       }
     }
 
-    floatx16_t acc[4][4];
+    floatx16_t acc[4][WNF];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < WNF; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     // 32-row fragments of this wave that hold at least one valid row
@@ -353,18 +362,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     issueA(1, min(1, KT - 1) * BK);
     issueB(1, min(1, KT - 1) * BK);
     issueB(2, min(2, KT - 1) * BK);
-    bf16x8_t fa0[8], fb0[8], fa1[8], fb1[8];
+    bf16x8_t fa0[8], fb0[2 * WNF], fa1[8], fb1[2 * WNF];
     wait_vmcnt<A_IT + 2 * B_IT>();
     __syncthreads();
-    read_frags(sAbuf, sBbuf, wm, wn, lane, 0, fa0, fb0);
+    read_frags<WNF>(sAbuf, sBbuf, wm, wn, lane, 0, fa0, fb0);
     int b3 = 0;   // kt % 3
     for (int kt = 0; kt < KT; ++kt) {
       const int b3n = b3 == 2 ? 0 : b3 + 1;
       {
         // first half of stage kt (registers fa0/fb0); read its second half
-        read_frags(sAbuf + (kt & 1) * A_CH, sBbuf + b3 * B_CH, wm, wn, lane, 1, fa1, fb1);
-        mfma_stage(fa0, fb0, acc);
-        interleave_first_half();
+        read_frags<WNF>(sAbuf + (kt & 1) * A_CH, sBbuf + b3 * B_CH, wm, wn, lane, 1, fa1, fb1);
+        mfma_stage<WNF>(fa0, fb0, acc);
+        interleave_first_half<8 * WNF, 8 + 2 * WNF>();
         __builtin_amdgcn_sched_barrier(0);
       }
       {
@@ -378,9 +387,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);
         issueA(kt & 1, min(kt + 2, KT - 1) * BK);
         issueB(b3, min(kt + 3, KT - 1) * BK);
-        read_frags(sAbuf + ((kt + 1) & 1) * A_CH, sBbuf + b3n * B_CH, wm, wn, lane, 0, fa0, fb0);
-        mfma_stage(fa1, fb1, acc);
-        interleave_second_half();
+        read_frags<WNF>(sAbuf + ((kt + 1) & 1) * A_CH, sBbuf + b3n * B_CH, wm, wn, lane, 0, fa0, fb0);
+        mfma_stage<WNF>(fa1, fb1, acc);
+        interleave_second_half<8 * WNF, 8 + 2 * WNF, A_IT + B_IT>();
         __builtin_amdgcn_sched_barrier(0);
       }
       b3 = b3n;
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       for (int pass = 0; pass < 4; ++pass) {
         if (pass < fm_valid) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < WNF; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
               ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = acc[pass][j][e];
@@ -421,9 +430,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
               if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + wn * 64 + c8, g, u);
             }
           } else {
+            // 32 rows x WTN columns in groups of 8 columns, one group per lane
+            constexpr int CG = WTN / 8;
 #pragma unroll 1
-            for (int it = 0; it < 8; ++it) {
-              const int rl = it * 4 + (lane >> 4), c8 = (lane & 15) * 8;
+            for (int it = 0; it < 32 * CG / 64; ++it) {
+              const int idx = it * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
               const int ml = wm * WTM + pass * 32 + rl;
               float v[8];
 #pragma unroll
@@ -440,27 +451,33 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
   }
 }
 
-template <bool DUAL, int EPI, typename TO>
+template <bool DUAL, int EPI, typename TO, int WNF = 4>
 void launch_big(const GemmParams& p, int n_cu, hipStream_t s) {
   // the 128 KB of dynamic LDS must be allowed once per kernel and device
   static bool configured[64] = {false};
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev < 0 || dev >= 64 || !configured[dev]) {
-    (void)hipFuncSetAttribute((const void*)gemm_bf16_big_kernel<DUAL, EPI, TO>,
+    (void)hipFuncSetAttribute((const void*)gemm_bf16_big_kernel<DUAL, EPI, TO, WNF>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (dev >= 0 && dev < 64) configured[dev] = true;
   }
   const int grid = ((n_cu + RDT_NUM_XCD - 1) / RDT_NUM_XCD) * RDT_NUM_XCD;
-  gemm_bf16_big_kernel<DUAL, EPI, TO><<<grid, 256, LDS_BYTES, s>>>(p);
+  gemm_bf16_big_kernel<DUAL, EPI, TO, WNF><<<grid, 256, LDS_BYTES, s>>>(p);
 }
 
 }  // namespace
 
-void launch_gemm_bf16_big(const GemmParams& p, int epi, bool dual, int out_is_bf16, int n_cu, hipStream_t s) {
+void launch_gemm_bf16_big(const GemmParams& p, int epi, bool dual, int out_is_bf16, int n_cu, hipStream_t s,
+                          int bn) {
   if (dual) {
     if (out_is_bf16) launch_big<true, EPI_SWIGLU, bf16_t>(p, n_cu, s);
     else launch_big<true, EPI_SWIGLU, float>(p, n_cu, s);
+    return;
+  }
+  if (bn == 192 && ((epi == EPI_STORE && !out_is_bf16) || epi == EPI_RESID)) {
+    if (epi == EPI_RESID) launch_big<false, EPI_RESID, float, 3>(p, n_cu, s);
+    else launch_big<false, EPI_STORE, float, 3>(p, n_cu, s);
     return;
   }
   switch (epi) {

@@ -655,7 +655,19 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       const int cap = grouped ? p.max_mt : (gp.M + RDT_BM_SKINNY - 1) / RDT_BM_SKINNY;
       launch_gemm_bf16_skinny(gp, epi, dual, out_bf16, cap, narrow ? 64 : 32, s);
     } else {
-      launch_gemm_bf16_big(gp, epi, dual, out_bf16, b->n_cu, s);
+      // dense products: 192-column tiles when they fill the rounds of CUs
+      // markedly better than 256-column ones (e.g. N = 3072 on 256 CUs)
+      int bn = 256;
+      if (!grouped && !dual && gp.N % 192 == 0 && !(epi == EPI_STORE && out_bf16) &&
+          (epi == EPI_STORE || epi == EPI_RESID)) {
+        const int mt = (gp.M + 255) / 256;
+        auto eff = [&](int tiles) {
+          const int rounds = (tiles + b->n_cu - 1) / b->n_cu;
+          return (double)tiles / ((double)rounds * b->n_cu);
+        };
+        if (eff(mt * (gp.N / 192)) > eff(mt * ((gp.N + 255) / 256)) + 0.05) bn = 192;
+      }
+      launch_gemm_bf16_big(gp, epi, dual, out_bf16, b->n_cu, s, bn);
     }
   };
   auto dense = [&](const void* A, int64_t lda, const void* W0, const void* W1, int M, int Nn, int K) {
