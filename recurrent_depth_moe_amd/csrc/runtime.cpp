@@ -655,10 +655,14 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       const int cap = grouped ? p.max_mt : (gp.M + RDT_BM_SKINNY - 1) / RDT_BM_SKINNY;
       launch_gemm_bf16_skinny(gp, epi, dual, out_bf16, cap, narrow ? 64 : 32, s);
     } else {
-      // dense products: 192-column tiles when they fill the rounds of CUs
-      // markedly better than 256-column ones (e.g. N = 3072 on 256 CUs)
+      // 192-column tiles where they fill the rounds of CUs markedly better
+      // than 256-column ones (e.g. dense N = 3072 on 256 CUs)
       int bn = 256;
-      if (!grouped && !dual && gp.N % 192 == 0 && !(epi == EPI_STORE && out_bf16) &&
+      if (grouped && !dual && gp.N % 192 == 0 && epi == EPI_STORE && !out_bf16) {
+        // routed down projection: its m-tile count is only known on the
+        // device; a third more (narrower) tiles levels the rounds of CUs
+        bn = 192;
+      } else if (!grouped && !dual && gp.N % 192 == 0 && !(epi == EPI_STORE && out_bf16) &&
           (epi == EPI_STORE || epi == EPI_RESID)) {
         const int mt = (gp.M + 255) / 256;
         auto eff = [&](int tiles) {
