@@ -182,7 +182,8 @@ rdt_status rdt_set_capture(rdt_block* blk, float* h_loops, int32_t* sel_loops, f
  * "mt_start", "tile_row0", "tile_grp", "perm", "inv", "act", "y", "act_s",
  * "y_s", "h", "cum", "live" (running-position counts of the last two loops
  * when ACT is on without a cache), "attn_part" (split-KV partials of a bf16
- * decode step; 0 bytes otherwise) and for MLA "kv_raw", "cq_raw", "cq_norm",
+ * decode step; 0 bytes otherwise), "tile_claim" (tile-claim counters of the
+ * routed products, zeroed by each loop's dispatch) and for MLA "kv_raw", "cq_raw", "cq_norm",
  * "lat_ckv", "lat_krope", "ckv_norm".  INVALID_ARG for other names. */
 rdt_status rdt_workspace_offset(const rdt_block* blk, int32_t B, int32_t T, const char* name,
                                 size_t* offset, size_t* bytes);

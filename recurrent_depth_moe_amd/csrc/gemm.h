@@ -50,6 +50,9 @@ struct GemmParams {
   int dense_gm;              // dense raster: m-tiles per group of the tile order
   int skinny_mt_cap;         // skinny kernel: m-tiles its grid is sized for
   const int32_t* live;       // running positions after the previous loop (null: always run)
+  // big kernel, grouped products: RDT_NUM_XCD tile-claim counters, zero at
+  // launch (null: static round-robin over each XCD's share of the tiles)
+  int32_t* tile_ctr;
   EpiParams epi;
 };
 

@@ -282,7 +282,40 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
   const bf16_t* Abase = (const bf16_t*)p.A;
   const int KT = p.K / BK;
 
-  for (int L = xcd * chunk + slot; L < t_end; L += per_xcd) {
+  // XCD x owns tiles [x * chunk, (x + 1) * chunk), so tiles that share an
+  // A or B panel meet in one L2.  Static order: slot s of the XCD takes
+  // every per_xcd-th tile of its share.  Claimed order (tile_ctr): blocks
+  // take their XCD's tiles one at a time from its counter, then help the
+  // other XCDs in turn, so tiles of unequal cost (the short tail tiles of
+  // routed experts) level out over the CUs.  The claimed tile index passes
+  // through LDS word 0, which no tile uses between its closing barrier and
+  // the next tile's first load.
+  int src = xcd;   // claimed order: the share thread 0 currently draws from
+  auto next_tile = [&](int L) -> int {
+    if (p.tile_ctr == nullptr) {
+      L = L < 0 ? xcd * chunk + slot : L + per_xcd;
+      return L < t_end ? L : -1;
+    }
+    int* const bc = (int*)smem;
+    if (tid == 0) {
+      int got = -1;
+      for (int tries = 0; tries < RDT_NUM_XCD && got < 0; ++tries) {
+        const int c0 = src * chunk, c1 = min(total, c0 + chunk);
+        if (c0 < c1) {
+          const int i = atomicAdd(p.tile_ctr + src, 1);
+          if (c0 + i < c1) got = c0 + i;
+        }
+        if (got < 0) src = src + 1 == RDT_NUM_XCD ? 0 : src + 1;
+      }
+      *bc = got;
+    }
+    __syncthreads();
+    const int got = __builtin_amdgcn_readfirstlane(*(volatile int*)bc);
+    __syncthreads();
+    return got;
+  };
+
+  for (int L = next_tile(-1); L >= 0; L = next_tile(L)) {
     int mt, nt, row0, rows, grp;
     tile_coords(p, L, ntn, n_mt, mt, nt);
     tile_rows(p, mt, BM, row0, rows, grp);

@@ -27,9 +27,11 @@ void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, f
 void launch_router_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* sel, float* gate,
                         int32_t* cap_sel, hipStream_t s, const int32_t* live = nullptr);
 // dropless dispatch: stable order (token, slot) inside each expert
+// (also zeroes the n_claim tile-claim counters the grouped products of the
+// same loop draw from, n_claim <= RDT_MAX_EXPERTS)
 void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,
                      int32_t* mt_start, int32_t* tile_row0, int32_t* tile_grp, int32_t* perm_src, int32_t* inv,
-                     hipStream_t s, const int32_t* live = nullptr);
+                     int32_t* tile_claim, int n_claim, hipStream_t s, const int32_t* live = nullptr);
 
 struct TailArgs {
   const float* x1;        // [N][D]

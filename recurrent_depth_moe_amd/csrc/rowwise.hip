@@ -247,8 +247,10 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
                                                                         int32_t* __restrict__ mt_start,
                                                                         int32_t* __restrict__ tile_row0,
                                                                         int32_t* __restrict__ tile_grp,
-                                                                        const int32_t* live) {
+                                                                        int32_t* __restrict__ tile_claim,
+                                                                        int n_claim, const int32_t* live) {
   RDT_SKIP_IF_ALL_HALTED(live);
+  if ((int)threadIdx.x < n_claim) tile_claim[threadIdx.x] = 0;
   __shared__ int tot[RDT_MAX_EXPERTS];
   __shared__ int off[RDT_MAX_EXPERTS + 1];
   __shared__ int mts[RDT_MAX_EXPERTS + 1];
@@ -718,11 +720,11 @@ void launch_router_topk(const float* logits, const float* bias, int N, int E, in
 
 void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,
                      int32_t* mt_start, int32_t* tile_row0, int32_t* tile_grp, int32_t* perm_src, int32_t* inv,
-                     hipStream_t s, const int32_t* live) {
+                     int32_t* tile_claim, int n_claim, hipStream_t s, const int32_t* live) {
   const int ntiles = (NK + RDT_DISP_TILE - 1) / RDT_DISP_TILE;
   dispatch_count_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, E, tile_counts, live);
   dispatch_scan_kernel<<<1, RDT_MAX_EXPERTS, 0, s>>>(tile_counts, ntiles, E, bm, offsets, mt_start, tile_row0,
-                                                     tile_grp, live);
+                                                     tile_grp, tile_claim, n_claim, live);
   dispatch_scatter_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, k, E, tile_counts, perm_src, inv, live);
 }
 

@@ -96,12 +96,13 @@ rdt_status check_config(const rdt_config* c) {
 enum WsId {
   WS_H, WS_C, WS_A, WS_Q, WS_K, WS_VT, WS_O, WS_X1, WS_F, WS_LOGITS, WS_SEL, WS_GATE, WS_TILECNT, WS_OFFSETS,
   WS_MTSTART, WS_TROW0, WS_TGRP, WS_PERM, WS_INV, WS_ACT, WS_Y, WS_ACTS, WS_YS, WS_CUM,
-  WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_DPART, WS_LIVE, WS_COUNT
+  WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_DPART, WS_LIVE, WS_TCLAIM, WS_COUNT
 };
 const char* kWsNames[WS_COUNT] = {"h", "c", "a", "q", "k", "vt", "o", "x1", "f", "logits", "sel", "gate",
                                   "tile_counts", "offsets", "mt_start", "tile_row0", "tile_grp", "perm", "inv",
                                   "act", "y", "act_s", "y_s", "cum", "kv_raw", "cq_raw", "cq_norm", "lat_ckv",
-                                  "lat_krope", "ckv_norm", "attn_part", "live"};
+                                  "lat_krope", "ckv_norm", "attn_part", "live",
+                                  "tile_claim"};
 
 struct Plan {
   int B, T, N, NK, kvcap, kvlen_max, bm, max_mt, disp_tiles;
@@ -177,6 +178,7 @@ Plan make_plan(const rdt_config& c, int B, int T) {
   }
   if (use_decode_attn(c, T)) s[WS_DPART] = attn_decode_part_floats(B, c.n_heads, p.kvlen_max) * 4;
   s[WS_LIVE] = 2 * 4;   // running-position counts of the previous and the current loop
+  s[WS_TCLAIM] = 2 * RDT_NUM_XCD * 4;   // tile-claim counters of the two routed products
   size_t o = 0;
   for (int i = 0; i < WS_COUNT; ++i) {
     p.off[i] = o;
@@ -803,7 +805,8 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     {
       StageTimer st_(b, s, RDT_STAGE_DISPATCH);
       launch_dispatch(WI(WS_SEL), p.NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART),
-                      WI(WS_TROW0), WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), s, live_prev);
+                      WI(WS_TROW0), WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), WI(WS_TCLAIM), 2 * RDT_NUM_XCD, s,
+                      live_prev);
     }
     // a11: routed gate|up + SwiGLU, rows gathered from f
     {
@@ -822,6 +825,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gp.tile_grp = WI(WS_TGRP);
       gp.grp_end = WI(WS_OFFSETS);
       gp.n_groups = E;
+      gp.tile_ctr = WI(WS_TCLAIM);
       gp.epi.out = W(WS_ACT);
       gp.epi.ldo = F;
       {
@@ -836,6 +840,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gd.W0 = b->w_down;
       gd.W1 = nullptr;
       gd.w_stride = (int64_t)D * F;
+      gd.tile_ctr = WI(WS_TCLAIM) + RDT_NUM_XCD;
       gd.N = D;
       gd.K = F;
       gd.epi = EpiParams{};
