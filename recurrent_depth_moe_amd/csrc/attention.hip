@@ -6,9 +6,20 @@
 // [0, kbase + i]; query head h reads KV head h / (H / G).
 #include "attention.h"
 
+#include <type_traits>
+
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// global -> LDS copy of 16 bytes per lane into the 1 KB window at lds (lane
+// i fills bytes 16 i .. 16 i + 15), written as asm so the compiler does not
+// add its own vmcnt wait before every later LDS read: the caller waits
+// explicitly before reading the window.
+__device__ __forceinline__ void dma16(const void* src, const void* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m) : "memory", "m0");
+}
 
 // ------------------------------------------------------------ generic
 // One wave per (query, head): scores to LDS, exact softmax, then P.V.
@@ -72,6 +83,12 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
 // fragment of a P V key step is one 16-byte LDS read per lane.
 constexpr int FD = 128, FBQ = 128, FBK = 64;
 
+// K tile row kr keeps its 16-byte chunk c at position c ^ kswz(kr).  The
+// 16 lanes of a quarter-wave read rows {r..r+3, r+16..r+19, r+4..r+7,
+// r+20..r+23} (r a multiple of 8, see kperm), which kswz sends to 16
+// distinct positions: one 256-byte bank sweep, no conflicts.
+__device__ __forceinline__ int kswz(int kr) { return (kr & 7) | (((kr >> 4) & 1) << 3); }
+
 __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* __restrict__ q,
                                                                   const bf16_t* __restrict__ k,
                                                                   const bf16_t* __restrict__ vt,
@@ -81,9 +98,29 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
   RDT_SKIP_IF_ALL_HALTED(live);
   __shared__ uint4 sK[2][FBK * 16];   // [key][16 chunks of 8 d], chunk ^ (key & 15)
   __shared__ uint4 sV[2][FD * 8];     // [d][8 chunks of 8 keys], chunk ^ ((d >> 1) & 7)
-  const int nqt = (Tq + FBQ - 1) / FBQ;
-  const int qt = nqt - 1 - blockIdx.x;   // longest tiles first
-  const int bh = blockIdx.y, b = bh / H, h = bh - b * H, g = h / (H / G);
+  // Block order: longest query tiles first.  When the (b, kv head) groups
+  // split evenly over the XCDs, each XCD takes its own groups (blocks go to
+  // XCDs round-robin by linear index), so the K / V tiles its blocks stream
+  // stay in that XCD's L2.
+  const int nqt = (Tq + FBQ - 1) / FBQ, rep = H / G;
+  int qt, b, h;
+  {
+    const int L = blockIdx.x, BG = gridDim.x / (nqt * rep);
+    if (BG % RDT_NUM_XCD == 0) {
+      const int ppc = BG / RDT_NUM_XCD, xcd = L % RDT_NUM_XCD, j = L / RDT_NUM_XCD;
+      const int rank = j / (ppc * rep), rest = j - rank * (ppc * rep);
+      const int bg = xcd * ppc + rest / rep;
+      qt = nqt - 1 - rank;
+      b = bg / G;
+      h = (bg - b * G) * rep + (rest % rep);
+    } else {
+      const int rank = L / (BG * rep), bh = L - rank * (BG * rep);
+      qt = nqt - 1 - rank;
+      b = bh / H;
+      h = bh - b * H;
+    }
+  }
+  const int g = h / rep;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5;            // which 4-row group of each 8 the lane holds
   const int myq = qt * FBQ + w * 32 + (lane & 31);
@@ -110,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float l_run = 0.f;
 
   // Direct-to-LDS tile loads: lane i of each load fills 16-byte slot i of
   // a 1 KB window, so the swizzles are applied by choosing the source chunk.
@@ -121,16 +158,14 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int sl = (j * 4 + w) * 64 + lane;            // K slot: row sl/16, position sl%16
-      const int kr = sl >> 4, kc = (sl & 15) ^ (kr & 15);
-      __builtin_amdgcn_global_load_lds((const void*)(kb + (int64_t)(k0 + kr) * FD + kc * 8),
-                                       (lds_void_t*)&sK[buf][(j * 4 + w) * 64], 16, 0, 0);
+      const int kr = sl >> 4, kc = (sl & 15) ^ kswz(kr);
+      dma16(kb + (int64_t)(k0 + kr) * FD + kc * 8, &sK[buf][(j * 4 + w) * 64]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int sl = (j * 4 + w) * 64 + lane;            // V^T slot: row sl/8, position sl%8
       const int vd = sl >> 3, vc = (sl & 7) ^ ((vd >> 1) & 7);
-      __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)vd * cap + k0 + vc * 8),
-                                       (lds_void_t*)&sV[buf][(j * 4 + w) * 64], 16, 0, 0);
+      dma16(vb + (int64_t)vd * cap + k0 + vc * 8, &sV[buf][(j * 4 + w) * 64]);
     }
   };
 
@@ -161,94 +196,109 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
   const int kperm = 16 * (((lane & 31) >> 2) & 1) + 4 * ((lane & 31) >> 3) + (lane & 3);
   const int wfirst = kbase + qt * FBQ + w * 32;   // last key every query of this wave sees
   const int wlast = wfirst + 31;                  // last key any query of this wave sees
+  // Softmax reference: m_ref trails the running maximum and is moved (with
+  // O and l rescaled) only when some query of the wave would otherwise get
+  // p above 2^8; O / l does not depend on the reference, and p <= 256 is
+  // exact enough in bf16 and far from overflow in the fp32 sums.
+  float m_ref = -INFINITY;
+  const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  auto tile = [&](auto masked, int t, int buf) {
+    // S^T for two key blocks of 32: 8 chained k-steps of 16 d each
+    floatx16_t s[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb2][e] = 0.f;
+    // K fragments in two batches of 8 reads, each batch in flight before
+    // its MFMAs
+#pragma unroll
+    for (int dh2 = 0; dh2 < 2; ++dh2) {
+      bf16x8_t kf[4][2];
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const int kr = kb2 * 32 + kperm;
+          const int ch = (dh2 * 4 + dd) * 2 + half;
+          kf[dd][kb2] = __builtin_bit_cast(bf16x8_t, sK[buf][kr * 16 + (ch ^ kswz(kr))]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dd][kb2], qf[dh2 * 4 + dd], s[kb2], 0, 0, 0);
+    }
+    const int k0 = t * FBK;
+    if constexpr (decltype(masked)::value) {
+      // a tile that crosses this wave's diagonal or the key end
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + kb2 * 32 + 16 * half + e;
+          if (key > qlim || key >= kv_valid) s[kb2][e] = -INFINITY;
+        }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[kb2][e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_ref, tmax);
+    if (__any((m_new - m_ref) * scale_log2 > 8.f)) {
+      // (kept a real branch: the rescale is rare and 64 multiplies long)
+      asm volatile("" ::: "memory");
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * scale_log2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
+      l_run *= alpha;
+      m_ref = m_new;
+    }
+    // masked scores are -inf: with a finite reference they give exp2 = 0;
+    // a row with nothing visible yet uses reference 0 so no NaN appears
+    const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * scale_log2;
+    float psum = 0.f;
+    bf16x8_t pf[4];   // key steps of 16: (kb2, elements 0..7) and (kb2, 8..15)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float p[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) p[x] = __builtin_amdgcn_exp2f(fmaf(s[kb2][hh * 8 + x], scale_log2, -mc));
+        const uint4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                          pack_bf16x2(p[6], p[7])};
+        // l sums the bf16 values the P V product uses
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk.x), ones2, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk.y), ones2, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk.z), ones2, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk.w), ones2, psum, false);
+        pf[kb2 * 2 + hh] = __builtin_bit_cast(bf16x8_t, pk);
+      }
+    psum += __shfl_xor(psum, 32, 64);
+    l_run += psum;
+    // O^T[d][q] += V^T[d][keys] P^T[keys][q]; key step ks = 2 kb2 + hh
+    // takes, from lane half g, keys 32 kb2 + 16 g + 8 hh .. +7: one
+    // 16-byte chunk of the V^T row
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int d = db * 32 + (lane & 31);
+        const int ch = 4 * (ks >> 1) + 2 * half + (ks & 1);
+        const uint4 vv = sV[buf][d * 8 + (ch ^ ((d >> 1) & 7))];
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[ks], oacc[db], 0, 0, 0);
+      }
+  };
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) issue(buf ^ 1, t + 1);
     if (t * FBK <= wlast) {   // else every key of the tile is past this wave's queries
-      // S^T for two key blocks of 32: 8 chained k-steps of 16 d each
-      floatx16_t s[2];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb2][e] = 0.f;
-      // K fragments in two batches of 8 reads, each batch in flight before
-      // its MFMAs
-#pragma unroll
-      for (int dh2 = 0; dh2 < 2; ++dh2) {
-        bf16x8_t kf[4][2];
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2) {
-            const int kr = kb2 * 32 + kperm;
-            const int ch = (dh2 * 4 + dd) * 2 + half;
-            kf[dd][kb2] = __builtin_bit_cast(bf16x8_t, sK[buf][kr * 16 + (ch ^ (kr & 15))]);
-          }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-            s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dd][kb2], qf[dh2 * 4 + dd], s[kb2], 0, 0, 0);
-      }
-      // mask (only a tile that crosses this wave's diagonal or the key end),
-      // then online softmax in units of log2: p = 2^(s c - m c)
       const int k0 = t * FBK;
-      if (k0 + FBK - 1 > wfirst || k0 + FBK > kv_valid) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = k0 + kb2 * 32 + 16 * half + e;
-            if (key > qlim || key >= kv_valid) s[kb2][e] = -INFINITY;
-          }
-      }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[kb2][e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      // masked scores are -inf: with a finite reference they give exp2 = 0;
-      // a row with nothing visible yet uses reference 0 so no NaN appears
-      const float mc = (m_new == -INFINITY) ? 0.f : m_new * scale_log2;
-      const float alpha = __builtin_amdgcn_exp2f(m_run * scale_log2 - mc);
-      float psum = 0.f;
-      bf16x8_t pf[4];   // key steps of 16: (kb2, elements 0..7) and (kb2, 8..15)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          float p[8];
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            p[x] = __builtin_amdgcn_exp2f(fmaf(s[kb2][hh * 8 + x], scale_log2, -mc));
-            psum += p[x];
-          }
-          const uint4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                            pack_bf16x2(p[6], p[7])};
-          pf[kb2 * 2 + hh] = __builtin_bit_cast(bf16x8_t, pk);
-        }
-      psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {   // the running max moved for some query of the wave
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
-      }
-      // O^T[d][q] += V^T[d][keys] P^T[keys][q]; key step ks = 2 kb2 + hh
-      // takes, from lane half g, keys 32 kb2 + 16 g + 8 hh .. +7: one
-      // 16-byte chunk of the V^T row
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int d = db * 32 + (lane & 31);
-          const int ch = 4 * (ks >> 1) + 2 * half + (ks & 1);
-          const uint4 vv = sV[buf][d * 8 + (ch ^ ((d >> 1) & 7))];
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[ks], oacc[db], 0, 0, 0);
-        }
+      if (k0 + FBK - 1 > wfirst || k0 + FBK > kv_valid) tile(std::true_type{}, t, buf);
+      else tile(std::false_type{}, t, buf);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -467,7 +517,7 @@ void launch_attn_generic(int dtype_bf16, const void* q, const void* k, const voi
 
 void launch_attn_flash_bf16(const void* q, const void* k, const void* vt, void* o, int B, int H, int G, int Tq,
                             int cap, int kbase, float scale, hipStream_t s, const int32_t* live) {
-  const dim3 grid((Tq + FBQ - 1) / FBQ, B * H), block(256);
+  const dim3 grid((Tq + FBQ - 1) / FBQ * B * H), block(256);
   const float scale_log2 = scale * 1.4426950408889634f;
   attn_flash_bf16_kernel<<<grid, block, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt, (bf16_t*)o,
                                                 H, G, Tq, cap, kbase, scale_log2, live);
