@@ -624,6 +624,196 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
   if (a.live_cur && threadIdx.x == 0 && still > 0) atomicAdd(a.live_cur, still);
 }
 
+// Same step, bf16 LoRA weights, for the shapes the large configurations
+// have: D a multiple of 4 * RB (every thread owns NJ whole float4 columns
+// of every row), NS = k + S summed rows per output row, rank a multiple of
+// four.  Every memory access is unconditional and batched so loads overlap:
+// a row's x1 and NS source rows are all requested before they are summed,
+// the LoRA rows four ranks at a time, a row's h_prev and e before its state
+// update; wave sums use DPP (no LDS round trips).  Same
+// per-element order as the generic form: x1, routed slots in slot order,
+// shared experts in order; ranks in order.
+template <int R, int NJ, int NS>
+__global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
+  RDT_SKIP_IF_ALL_HALTED(a.live_prev);
+  constexpr int RG = 4;   // ranks per LoRA group
+  __shared__ float red[RB / 64][RDT_MAX_LORA * R + R];
+  const int n0 = blockIdx.x * R, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int D = a.D, k = a.k;
+  const bf16_t* Wd = (const bf16_t*)a.lora_down;
+  const bf16_t* Wb = (const bf16_t*)a.lora_B;
+  // source rows: the k routed slots (gate-weighted), then the S shared experts
+  const float* src[R][NS];
+  float wt[R][NS];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int n = n0 + i;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      if (q < k) {
+        src[i][q] = a.y + (int64_t)a.inv[(int64_t)n * k + q] * D;
+        wt[i][q] = a.gate[(int64_t)n * k + q];
+      } else {
+        src[i][q] = a.y_s + ((int64_t)(q - k) * a.N + n) * D;
+        wt[i][q] = 1.f;
+      }
+    }
+  }
+  float4 tau[R][NJ];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float4 v[NJ][NS + 1];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int d = (threadIdx.x + j * RB) * 4;
+      v[j][0] = ld4(a.x1 + (int64_t)(n0 + i) * D + d);
+#pragma unroll
+      for (int q = 0; q < NS; ++q) v[j][q + 1] = ld4(src[i][q] + d);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float4 x = v[j][0];
+#pragma unroll
+      for (int q = 0; q < NS; ++q) x = fma4(wt[i][q], v[j][q + 1], x);
+      tau[i][j] = x;
+    }
+  }
+  // LoRA down-projection, RG ranks per group
+  const int ng = a.r / RG;
+#pragma unroll 1
+  for (int g = 0; g < ng; ++g) {
+    float4 wv[RG][NJ];
+#pragma unroll
+    for (int rr = 0; rr < RG; ++rr)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) wv[rr][j] = ld4(Wd + (int64_t)(g * RG + rr) * D + (threadIdx.x + j * RB) * 4);
+#pragma unroll
+    for (int rr = 0; rr < RG; ++rr)
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        float pr = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) pr += dot4(tau[i][j], wv[rr][j]);
+        const float s = wave_sum_dpp(pr);
+        if (lane == 0) red[w][(g * RG + rr) * R + i] = s;
+      }
+  }
+  __syncthreads();
+  // LoRA up-projection, ranks in order
+#pragma unroll 1
+  for (int g = 0; g < ng; ++g) {
+    float4 bv[RG][NJ];
+#pragma unroll
+    for (int rr = 0; rr < RG; ++rr)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bv[rr][j] = ld4(Wb + (int64_t)(g * RG + rr) * D + (threadIdx.x + j * RB) * 4);
+#pragma unroll
+    for (int rr = 0; rr < RG; ++rr) {
+      const float sc = a.lora_scale_row[g * RG + rr];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        float v = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < RB / 64; ++ww) v += red[ww][(g * RG + rr) * R + i];
+        const float lo = v * sc;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) tau[i][j] = fma4(lo, bv[rr][j], tau[i][j]);
+      }
+    }
+  }
+  // state update h_{t+1} = A h_t + B e + tau
+  float zs[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    zs[i] = 0.f;
+    float4 hp[NJ], ee[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t off = (int64_t)(n0 + i) * D + (threadIdx.x + j * RB) * 4;
+      hp[j] = ld4(a.h_prev + off);
+      ee[j] = ld4(a.e + off);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int d = (threadIdx.x + j * RB) * 4;
+      const int64_t off = (int64_t)(n0 + i) * D + d;
+      const float4 A = ld4(a.A + d), Bv = ld4(a.Bv + d), x = tau[i][j];
+      float4 hn;
+      hn.x = A.x * hp[j].x + Bv.x * ee[j].x + x.x;
+      hn.y = A.y * hp[j].y + Bv.y * ee[j].y + x.y;
+      hn.z = A.z * hp[j].z + Bv.z * ee[j].z + x.z;
+      hn.w = A.w * hp[j].w + Bv.w * ee[j].w + x.w;
+      tau[i][j] = hn;
+      st4(a.h_next + off, hn);
+      if (a.cap_h) st4(a.cap_h + off, hn);
+      zs[i] += dot4(hn, ld4(a.halt_w + d));
+    }
+  }
+  const bool act = a.act_threshold > 0.f;
+  const bool last = a.t == a.n_loops - 1;
+  if (!act) {
+    if (last) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          st4(a.h_out + (int64_t)(n0 + i) * D + (threadIdx.x + j * RB) * 4, tau[i][j]);
+    }
+    if (threadIdx.x < R) a.halt_counts[n0 + threadIdx.x] = a.t + 1;
+    return;
+  }
+  // ACT: halting logit of every row (block sum), then the decisions
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const float v = wave_sum_dpp(zs[i]);
+    if (lane == 0) red[w][RDT_MAX_LORA * R + i] = v;
+  }
+  __syncthreads();
+  float pv[R], cumv[R];
+  int hcv[R];
+  bool run[R], halt[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int n = n0 + i;
+    float z = a.halt_b[0];
+#pragma unroll
+    for (int ww = 0; ww < RB / 64; ++ww) z += red[ww][RDT_MAX_LORA * R + i];
+    pv[i] = sigmoid_f(z);
+    cumv[i] = a.t == 0 ? 0.f : a.cum[n];
+    hcv[i] = a.t == 0 ? 0 : a.halt_counts[n];
+    run[i] = hcv[i] == 0;
+    halt[i] = false;
+    float wgt = 0.f;
+    if (run[i]) {
+      halt[i] = (cumv[i] + pv[i] >= a.act_threshold) || last;
+      wgt = halt[i] ? fmaxf(1.0f - cumv[i], 0.f) : pv[i];
+    }
+    if (run[i]) {
+      float4 prev[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        prev[j] = a.t == 0 ? make_float4(0.f, 0.f, 0.f, 0.f)
+                           : ld4(a.h_out + (int64_t)n * D + (threadIdx.x + j * RB) * 4);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        st4(a.h_out + (int64_t)n * D + (threadIdx.x + j * RB) * 4, fma4(wgt, tau[i][j], prev[j]));
+    }
+  }
+  __syncthreads();   // every thread has read cum / halt_counts before they change
+  int still = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (threadIdx.x == i) {
+      const int n = n0 + i;
+      a.cum[n] = run[i] ? cumv[i] + pv[i] : cumv[i];
+      a.halt_counts[n] = halt[i] ? a.t + 1 : hcv[i];
+      if (a.cap_p) a.cap_p[n] = pv[i];
+    }
+    still += (run[i] && !halt[i]) ? 1 : 0;
+  }
+  if (a.live_cur && threadIdx.x == 0 && still > 0) atomicAdd(a.live_cur, still);
+}
+
 // ------------------------------------------------------------ MLA glue
 // [ZS §MLA]: the kv down-projection splits into the latent c_kv and one
 // shared k_rope, which is rotated; both are what the cache holds.  The q
@@ -740,7 +930,35 @@ static void launch_tail_rows(const TailArgs& a, int nj, hipStream_t s) {
   }
 }
 
+template <int NJ>
+static bool launch_tail_fast_nj(const TailArgs& a, int ns, hipStream_t s) {
+  constexpr int R = 4;
+  const int grid = a.N / R;
+  switch (ns) {
+    case 1: loop_tail_fast_kernel<R, NJ, 1><<<grid, RB, 0, s>>>(a); return true;
+    case 2: loop_tail_fast_kernel<R, NJ, 2><<<grid, RB, 0, s>>>(a); return true;
+    case 3: loop_tail_fast_kernel<R, NJ, 3><<<grid, RB, 0, s>>>(a); return true;
+    case 4: loop_tail_fast_kernel<R, NJ, 4><<<grid, RB, 0, s>>>(a); return true;
+    default: return false;
+  }
+}
+
 void launch_loop_tail(const TailArgs& a, hipStream_t s) {
+  // batched form: bf16 LoRA, whole float4 columns per thread (D a multiple
+  // of 4 RB, at most 4 of them), 4-row blocks, k + S <= 4, rank a multiple
+  // of 4 up to 16
+  if (a.w_bf16 && a.N % 4 == 0 && a.D % (4 * RB) == 0 && a.D <= 16 * RB && a.r % 4 == 0 && a.r <= 16 &&
+      a.r > 0) {
+    const int ns = a.k + a.S;
+    bool ok = false;
+    switch (a.D / (4 * RB)) {
+      case 1: ok = launch_tail_fast_nj<1>(a, ns, s); break;
+      case 2: ok = launch_tail_fast_nj<2>(a, ns, s); break;
+      case 3: ok = launch_tail_fast_nj<3>(a, ns, s); break;
+      default: ok = launch_tail_fast_nj<4>(a, ns, s); break;
+    }
+    if (ok) return;
+  }
   // R-row blocks when the rows split evenly, D <= 4096 and rank <= 16
   const int nj = (a.D / 4 + RB - 1) / RB;
   if (a.N % 4 == 0 && nj <= 4 && a.r <= 16) {
