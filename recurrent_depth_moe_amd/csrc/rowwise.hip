@@ -256,11 +256,18 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
   __shared__ int mts[RDT_MAX_EXPERTS + 1];
   const int ex = threadIdx.x;
   if (ex < E) {
+    // exclusive scan down the tiles, 16 counts loaded before any is used
+    // (the loads are independent; one at a time they would serialise)
     int run = 0;
-    for (int t = 0; t < ntiles; ++t) {
-      const int c = tile_counts[(int64_t)t * E + ex];
-      tile_counts[(int64_t)t * E + ex] = run;
-      run += c;
+    for (int t0 = 0; t0 < ntiles; t0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = t0 + u < ntiles ? tile_counts[(int64_t)(t0 + u) * E + ex] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (t0 + u < ntiles) tile_counts[(int64_t)(t0 + u) * E + ex] = run;
+        run += c[u];
+      }
     }
     tot[ex] = run;
   }
@@ -282,7 +289,14 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
     mt_start[ex] = mts[ex];
   }
   if (ex < E) {
-    for (int t = 0; t < ntiles; ++t) tile_counts[(int64_t)t * E + ex] += off[ex];
+    for (int t0 = 0; t0 < ntiles; t0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = t0 + u < ntiles ? tile_counts[(int64_t)(t0 + u) * E + ex] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (t0 + u < ntiles) tile_counts[(int64_t)(t0 + u) * E + ex] = c[u] + off[ex];
+    }
     const int nt = mts[ex + 1] - mts[ex];
     for (int i = 0; i < nt; ++i) {
       tile_grp[mts[ex] + i] = ex;

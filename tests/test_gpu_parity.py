@@ -81,6 +81,20 @@ def test_end_to_end_large_terms(name):
         assert len(np.unique(g["halt"])) > 1
 
 
+@pytest.mark.parametrize("act", [0.99, 0.0])
+def test_end_to_end_wide_rows(act):
+    """dim 1024 with rank-16 LoRA, top-2 plus one shared expert: the batched
+    loop-tail form the large configurations run, end to end, with O(1)
+    LoRA / output / halting terms."""
+    scales = {"lora_scale": 1.0, "lora_B": 0.3, "wo": 0.1, "w_down": 0.1, "s_down": 0.1,
+              "halt_w": 0.05, "halt_b": -0.8}
+    cfg, W, e, h0 = _inputs("small_bf16", scales=scales, dim=1024, n_heads=8, n_kv_heads=2, loop_dim=128,
+                            lora_rank=16, seq=96, act_threshold=act)
+    g, ref = _e2e(cfg, W, e, h0)
+    if act > 0:
+        assert len(np.unique(g["halt"])) > 1
+
+
 @pytest.mark.parametrize("name", ["tiny_gqa", "tiny_mla", "small_bf16"])
 def test_end_to_end_stops_once_all_halted(name):
     """Every position halts by loop 2: the remaining loops are skipped on the
