@@ -462,6 +462,34 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
               }
               if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + wn * 64 + c8, g, u);
             }
+          } else if (EPI == EPI_QKV && n0 + wn * WTN >= p.epi.H * p.epi.dq + p.epi.G * p.epi.dq) {
+            // every column of this wave is a V channel, stored transposed
+            // (V^T [b][g][d][position]): a lane takes 8 consecutive rows of
+            // one column and stores them as one 16-byte run of positions
+            const EpiParams& e = p.epi;
+            const int hqk = e.H * e.dq + e.G * e.dq;
+#pragma unroll 1
+            for (int it = 0; it < 32 * WTN / (8 * 64); ++it) {
+              const int idx = it * 64 + lane, c = idx % WTN, rg = idx / WTN;
+              const int ml = wm * WTM + pass * 32 + rg * 8;
+              const int n = n0 + wn * WTN + c;
+              if (ml >= rows || n >= p.N) continue;
+              const int m = row0 + ml, b = m / e.T, i = m - b * e.T;
+              const int nn = n - hqk, g = nn / e.dv, d = nn - g * e.dv;
+              TO* col = (TO*)e.vt + ((int64_t)(b * e.G + g) * e.dv + d) * e.cap + e.kbase + i;
+              float v[8];
+#pragma unroll
+              for (int x = 0; x < 8; ++x) v[x] = ep[(rg * 8 + x) * EP_LD + c];
+              if (ml + 8 <= rows && i + 8 <= e.T && ((e.kbase + i) & 7) == 0) {
+                store8<EPI, TO>(col, v);
+              } else {
+                // rows past the tile, a sequence boundary or an unaligned run
+                for (int x = 0; x < 8 && ml + x < rows; ++x) {
+                  const int mx = m + x, bx = mx / e.T, ix = mx - bx * e.T;
+                  St<TO>::st((TO*)e.vt + ((int64_t)(bx * e.G + g) * e.dv + d) * e.cap + e.kbase + ix, v[x]);
+                }
+              }
+            }
           } else {
             // 32 rows x WTN columns in groups of 8 columns, one group per lane
             constexpr int CG = WTN / 8;
