@@ -156,7 +156,10 @@ rdt_status rdt_recurrent_forward(rdt_block* blk, const float* e, const float* h0
  * cache]): each of B sequences brings one new token at absolute position
  * start_pos; in every loop slot its K/V are appended at start_pos and
  * attention reads positions [0, start_pos].  Same outputs as
- * rdt_recurrent_forward with T = 1.  BAD_STATE if kv_cache is NULL or holds
+ * rdt_recurrent_forward with T = 1 (with MLA both attend over the cached
+ * latent c_kv | k_rope with the k_nope / v up-projections folded into the
+ * query and the output instead of rebuilding per-head K / V, [ZS §MLA];
+ * equal in exact arithmetic).  BAD_STATE if kv_cache is NULL or holds
  * fewer than n_loops slots. */
 rdt_status rdt_decode_step(rdt_block* blk, const float* e_new, const float* h0_new, int32_t B,
                            int32_t start_pos, int32_t n_loops, float act_threshold,
@@ -183,8 +186,11 @@ rdt_status rdt_set_capture(rdt_block* blk, float* h_loops, int32_t* sel_loops, f
  * "y_s", "h", "cum", "live" (running-position counts of the last two loops
  * when ACT is on without a cache), "attn_part" (split-KV partials of a bf16
  * decode step; 0 bytes otherwise), "tile_claim" (tile-claim counters of the
- * routed products, zeroed by each loop's dispatch) and for MLA "kv_raw", "cq_raw", "cq_norm",
- * "lat_ckv", "lat_krope", "ckv_norm".  INVALID_ARG for other names. */
+ * routed products, zeroed by each loop's dispatch) and for MLA "kv_raw",
+ * "cq_raw", "cq_norm", "lat_ckv", "lat_krope", "ckv_norm", plus for MLA
+ * decode steps (T = 1, attention over the latent with absorbed
+ * up-projections) "q_lat", "k_lat", "vt_lat", "o_lat" (0 bytes otherwise).
+ * INVALID_ARG for other names. */
 rdt_status rdt_workspace_offset(const rdt_block* blk, int32_t B, int32_t T, const char* name,
                                 size_t* offset, size_t* bytes);
 

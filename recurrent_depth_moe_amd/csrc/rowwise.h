@@ -69,6 +69,17 @@ void launch_mla_latent(int act_bf16, const float* kv_raw, const float* cq_raw, c
                        int T, int ql, int kvl, int rope, int start_pos, const float* rcos, const float* rsin,
                        void* cq_norm, void* lat_ckv, void* lat_krope, int lat_cap, int kbase, hipStream_t s,
                        const int32_t* live = nullptr);
+// MLA decode step (one query per sequence, fp32) with absorbed
+// up-projections: latent keys k_lat [B][kvlen][kvl + rope] and values
+// vt_lat [B][kvl][kvlen] from the cached latent, queries q_lat
+// [B][H][kvl + rope] from q [B][H][nope + rope]; after attention over the
+// latent (one key head), o [B][H * vd] = W_v,h o_lat [B][H][kvl].
+void launch_mla_absorbed_decode_prep(const float* lat_ckv, const float* lat_krope, int lat_cap, const float* gkv,
+                                     float eps, int B, int kvlen, int kvl, int rope, const float* q,
+                                     const float* wukv, int H, int nope, int vd, float* k_lat, float* vt_lat,
+                                     float* q_lat, hipStream_t s, const int32_t* live = nullptr);
+void launch_mla_absorb_o(const float* o_lat, const float* wukv, int B, int H, int nope, int vd, int kvl, float* o,
+                         hipStream_t s, const int32_t* live = nullptr);
 void launch_mla_kv_prep(int act_bf16, const void* lat_ckv, const void* lat_krope, int lat_cap, const float* gkv,
                         float eps, int B, int kvlen, int kvl, int rope, int H, int dq, void* ckv_norm, void* K,
                         hipStream_t s, const int32_t* live = nullptr);

@@ -885,7 +885,90 @@ __global__ __launch_bounds__(64) void mla_kv_prep_kernel(const TA* __restrict__ 
   }
 }
 
+// MLA decode step with the up-projections absorbed ([ZS §MLA] rebuilds
+// k_nope and v from the cached latent; the products are regrouped here, an
+// exact identity in real arithmetic): with W_k,h / W_v,h the k_nope / v rows
+// of head h in W_ukv and n_j = RMSNorm(c_kv,j) * g_kv,
+//   q_nope,h . (W_k,h n_j) = (W_k,h^T q_nope,h) . n_j     and
+//   sum_j p_j (W_v,h n_j)  = W_v,h (sum_j p_j n_j),
+// so attention runs once over the latent keys [n_j | k_rope,j] and values
+// n_j (one key head shared by all query heads), without rebuilding
+// per-head K / V for every cached position.
+
+// latent keys [B][kvlen][kvl + rope] and values transposed [B][kvl][kvlen]
+template <typename TA>
+__global__ __launch_bounds__(64) void mla_latent_kv_kernel(const TA* __restrict__ lat_ckv,
+                                                           const TA* __restrict__ lat_krope, int lat_cap,
+                                                           const float* __restrict__ gkv, float eps, int kvlen,
+                                                           int kvl, int rope, TA* __restrict__ k_lat,
+                                                           TA* __restrict__ vt_lat, const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
+  const int m = blockIdx.x, b = m / kvlen, j = m - b * kvlen, lane = threadIdx.x, dl = kvl + rope;
+  const TA* c = lat_ckv + ((int64_t)b * lat_cap + j) * kvl;
+  float ss = 0.f;
+  for (int d = lane; d < kvl; d += 64) {
+    const float x = St<TA>::ld(c + d);
+    ss += x * x;
+  }
+  const float r = 1.0f / sqrtf(wave_sum(ss) / kvl + eps);
+  for (int d = lane; d < kvl; d += 64) {
+    const float x = St<TA>::ld(c + d) * r * gkv[d];
+    St<TA>::st(k_lat + (int64_t)m * dl + d, x);
+    St<TA>::st(vt_lat + ((int64_t)b * kvl + d) * kvlen + j, x);
+  }
+  const TA* kr = lat_krope + ((int64_t)b * lat_cap + j) * rope;
+  for (int d = lane; d < rope; d += 64) k_lat[(int64_t)m * dl + kvl + d] = kr[d];
+}
+
+// q_lat[b][h] = [W_k,h^T q_nope,h | q_rope,h] (one query per sequence)
+template <typename TA>
+__global__ __launch_bounds__(64) void mla_absorb_q_kernel(const TA* __restrict__ q, const TA* __restrict__ wukv,
+                                                          int H, int nope, int rope, int vd, int kvl,
+                                                          TA* __restrict__ q_lat, const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
+  const int bh = blockIdx.x, h = bh % H, lane = threadIdx.x;
+  const TA* qr = q + (int64_t)bh * (nope + rope);
+  TA* out = q_lat + (int64_t)bh * (kvl + rope);
+  const TA* wk = wukv + (int64_t)h * (nope + vd) * kvl;
+  for (int c = lane; c < kvl; c += 64) {
+    float acc = 0.f;
+    for (int d = 0; d < nope; ++d) acc = fmaf(St<TA>::ld(qr + d), St<TA>::ld(wk + (int64_t)d * kvl + c), acc);
+    St<TA>::st(out + c, acc);
+  }
+  for (int r = lane; r < rope; r += 64) St<TA>::st(out + kvl + r, St<TA>::ld(qr + nope + r));
+}
+
+// o[b][h] = W_v,h o_lat[b][h]  (the O-projection input [B][H * vd])
+template <typename TA>
+__global__ __launch_bounds__(64) void mla_absorb_o_kernel(const TA* __restrict__ o_lat, const TA* __restrict__ wukv,
+                                                          int H, int nope, int vd, int kvl, TA* __restrict__ o,
+                                                          const int32_t* live) {
+  RDT_SKIP_IF_ALL_HALTED(live);
+  const int bh = blockIdx.x, h = bh % H, lane = threadIdx.x;
+  const TA* ol = o_lat + (int64_t)bh * kvl;
+  const TA* wv = wukv + ((int64_t)h * (nope + vd) + nope) * kvl;
+  for (int e = lane; e < vd; e += 64) {
+    float acc = 0.f;
+    for (int c = 0; c < kvl; ++c) acc = fmaf(St<TA>::ld(ol + c), St<TA>::ld(wv + (int64_t)e * kvl + c), acc);
+    St<TA>::st(o + (int64_t)bh * vd + e, acc);
+  }
+}
+
 }  // namespace
+
+void launch_mla_absorbed_decode_prep(const float* lat_ckv, const float* lat_krope, int lat_cap, const float* gkv,
+                                     float eps, int B, int kvlen, int kvl, int rope, const float* q,
+                                     const float* wukv, int H, int nope, int vd, float* k_lat, float* vt_lat,
+                                     float* q_lat, hipStream_t s, const int32_t* live) {
+  mla_latent_kv_kernel<float><<<B * kvlen, 64, 0, s>>>(lat_ckv, lat_krope, lat_cap, gkv, eps, kvlen, kvl, rope,
+                                                       k_lat, vt_lat, live);
+  mla_absorb_q_kernel<float><<<B * H, 64, 0, s>>>(q, wukv, H, nope, rope, vd, kvl, q_lat, live);
+}
+
+void launch_mla_absorb_o(const float* o_lat, const float* wukv, int B, int H, int nope, int vd, int kvl, float* o,
+                         hipStream_t s, const int32_t* live) {
+  mla_absorb_o_kernel<float><<<B * H, 64, 0, s>>>(o_lat, wukv, H, nope, vd, kvl, o, live);
+}
 
 void launch_make_tables(float* rope_cos, float* rope_sin, int max_seq, int rot_dim, double theta, hipStream_t s) {
   const int n = max_seq * (rot_dim / 2);

@@ -96,13 +96,14 @@ rdt_status check_config(const rdt_config* c) {
 enum WsId {
   WS_H, WS_C, WS_A, WS_Q, WS_K, WS_VT, WS_O, WS_X1, WS_F, WS_LOGITS, WS_SEL, WS_GATE, WS_TILECNT, WS_OFFSETS,
   WS_MTSTART, WS_TROW0, WS_TGRP, WS_PERM, WS_INV, WS_ACT, WS_Y, WS_ACTS, WS_YS, WS_CUM,
-  WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_DPART, WS_LIVE, WS_TCLAIM, WS_COUNT
+  WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_DPART, WS_LIVE, WS_TCLAIM,
+  WS_QLAT, WS_KLAT, WS_VLAT, WS_OLAT, WS_COUNT
 };
 const char* kWsNames[WS_COUNT] = {"h", "c", "a", "q", "k", "vt", "o", "x1", "f", "logits", "sel", "gate",
                                   "tile_counts", "offsets", "mt_start", "tile_row0", "tile_grp", "perm", "inv",
                                   "act", "y", "act_s", "y_s", "cum", "kv_raw", "cq_raw", "cq_norm", "lat_ckv",
                                   "lat_krope", "ckv_norm", "attn_part", "live",
-                                  "tile_claim"};
+                                  "tile_claim", "q_lat", "k_lat", "vt_lat", "o_lat"};
 
 struct Plan {
   int B, T, N, NK, kvcap, kvlen_max, bm, max_mt, disp_tiles;
@@ -175,6 +176,12 @@ Plan make_plan(const rdt_config& c, int B, int T) {
     s[WS_LATC] = N * kvl * es;
     s[WS_LATR] = N * rope * es;
     s[WS_CKVN] = (size_t)B * p.kvlen_max * kvl * es;
+    if (T == 1) {   // decode steps attend over the latent (absorbed up-projections)
+      s[WS_QLAT] = N * H * (kvl + rope) * es;
+      s[WS_KLAT] = (size_t)B * p.kvlen_max * (kvl + rope) * es;
+      s[WS_VLAT] = (size_t)B * kvl * p.kvlen_max * es;
+      s[WS_OLAT] = N * H * kvl * es;
+    }
   }
   if (use_decode_attn(c, T)) s[WS_DPART] = attn_decode_part_floats(B, c.n_heads, p.kvlen_max) * 4;
   s[WS_LIVE] = 2 * 4;   // running-position counts of the previous and the current loop
@@ -762,20 +769,32 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       g3.epi.rsin = b->rope_sin;
       g3.epi.rot_half = rope / 2;
       gemm(g3, EPI_MLA_Q, false, bf);
-      launch_mla_kv_prep(bf, lat_c, lat_r, lat_cap, b->gkv, c.norm_eps, B, kvlen, kvl, rope, H, dq, W(WS_CKVN),
-                         W(WS_K), s, live_prev);
-      GemmParams g4 = dense(W(WS_CKVN), kvl, b->wukv, nullptr, B * kvlen, H * (nope + dv), kvl);
-      g4.epi.k = W(WS_K);
-      g4.epi.vt = W(WS_VT);
-      g4.epi.T = kvlen;
-      g4.epi.H = H;
-      g4.epi.dq = dq;
-      g4.epi.dv = dv;
-      g4.epi.nope = nope;
-      g4.epi.cap = kvlen;
-      gemm(g4, EPI_MLA_KV, false, bf);
-      launch_attn_generic(bf, W(WS_Q), W(WS_K), W(WS_VT), W(WS_O), B, H, H, T, kvlen, dq, dv, kbase, scale, s,
-                          live_prev);
+      if (T == 1 && kv) {
+        // decode step: attention over the cached latent, up-projections
+        // absorbed into the query and the output
+        launch_mla_absorbed_decode_prep((const float*)lat_c, (const float*)lat_r, lat_cap, b->gkv, c.norm_eps, B,
+                                        kvlen, kvl, rope, WF(WS_Q), (const float*)b->wukv, H, nope, dv,
+                                        WF(WS_KLAT), WF(WS_VLAT), WF(WS_QLAT), s, live_prev);
+        launch_attn_generic(bf, W(WS_QLAT), W(WS_KLAT), W(WS_VLAT), W(WS_OLAT), B, H, 1, T, kvlen, kvl + rope, kvl,
+                            kbase, scale, s, live_prev);
+        launch_mla_absorb_o(WF(WS_OLAT), (const float*)b->wukv, B, H, nope, dv, kvl, WF(WS_O), s, live_prev);
+      } else {
+        // prefill: rebuild k_nope and v of every visible position from the latent
+        launch_mla_kv_prep(bf, lat_c, lat_r, lat_cap, b->gkv, c.norm_eps, B, kvlen, kvl, rope, H, dq, W(WS_CKVN),
+                           W(WS_K), s, live_prev);
+        GemmParams g4 = dense(W(WS_CKVN), kvl, b->wukv, nullptr, B * kvlen, H * (nope + dv), kvl);
+        g4.epi.k = W(WS_K);
+        g4.epi.vt = W(WS_VT);
+        g4.epi.T = kvlen;
+        g4.epi.H = H;
+        g4.epi.dq = dq;
+        g4.epi.dv = dv;
+        g4.epi.nope = nope;
+        g4.epi.cap = kvlen;
+        gemm(g4, EPI_MLA_KV, false, bf);
+        launch_attn_generic(bf, W(WS_Q), W(WS_K), W(WS_VT), W(WS_O), B, H, H, T, kvlen, dq, dv, kbase, scale, s,
+                            live_prev);
+      }
     }
     // a7: x1 = c + o Wo^T
     {

@@ -114,6 +114,20 @@ def test_workspace_layout_is_disjoint_and_aligned():
         binding.workspace_offset(cfg, 2, 4096, "nope")
 
 
+def test_mla_decode_plan_has_latent_buffers():
+    """MLA decode steps (T = 1) attend over the cached latent: the plan
+    carries the latent query / key / value / output buffers, sized from the
+    ranks, and a prefill plan does not."""
+    from recurrent_depth_moe_amd import binding
+    cfg = configs.get("tiny_mla")
+    B, H, kvl, rope = 3, cfg["n_heads"], cfg["kv_lora_rank"], cfg["qk_rope_head_dim"]
+    P = cfg["max_seq_len"]
+    want = {"q_lat": B * H * (kvl + rope), "k_lat": B * P * (kvl + rope), "vt_lat": B * kvl * P, "o_lat": B * H * kvl}
+    for name, n in want.items():
+        assert binding.workspace_offset(cfg, B, 1, name)[1] == 4 * n
+        assert binding.workspace_offset(cfg, B, 8, name)[1] == 0
+
+
 def test_kv_cache_size_formula():
     from recurrent_depth_moe_amd import binding
     cfg = configs.get("mythos_10b_decode")

@@ -187,6 +187,45 @@ def _oracle_cache(cfg, n_loops, B, cap):
     return O.new_cache(cfg, B, cap, n_loops)
 
 
+@pytest.mark.parametrize("start_pos", [1, 100])
+def test_mla_decode_against_random_latent_cache(start_pos):
+    """MLA decode step (attention over the cached latent with absorbed
+    up-projections) of 3 sequences at ``start_pos`` against caches holding
+    N(0,1) latents c_kv / k_rope at positions 0..start_pos-1 in every loop
+    slot and NaN past them; the oracle rebuilds per-head K / V from the same
+    latents."""
+    import torch
+    from recurrent_depth_moe_amd import binding
+    cfg, W, e, h0 = _inputs("tiny_mla", batch=3, seq=1, start_pos=start_pos, n_loops=5, use_cache=True)
+    B, P, n = cfg["batch"], cfg["start_pos"], cfg["n_loops"]
+    kvl, rope = cfg["kv_lora_rank"], cfg["qk_rope_head_dim"]
+    cap = kv_capacity(cfg)
+    Pp = (cap + 63) // 64 * 64
+    kv = torch.full((binding.kv_cache_bytes(cfg, B, cap, n),), 0xFF, dtype=torch.uint8, device="cuda")
+    slot = kv.numel() // n
+    oc = O.new_cache(cfg, B, cap, n)
+    for t in range(n):
+        ckv = generate.draw(cfg["seed"], f"cache_ckv_{t}", (B, P, kvl), "normal", 1.0)
+        kr = generate.draw(cfg["seed"], f"cache_krope_{t}", (B, P, rope), "normal", 1.0)
+        ckv, kr = ckv.reshape(B, P, kvl), kr.reshape(B, P, rope)
+        base = kv[t * slot:(t + 1) * slot].view(torch.float32)
+        base[:B * Pp * kvl].view(B, Pp, kvl)[:, :P] = torch.from_numpy(ckv).cuda()
+        base[B * Pp * kvl:B * Pp * (kvl + rope)].view(B, Pp, rope)[:, :P] = torch.from_numpy(kr).cuda()
+        oc[t]["c_kv"][:, :P] = ckv
+        oc[t]["k_rope"][:, :P] = kr
+    print(f"[mla decode] B={B} pos={P} loops={n}", flush=True)
+    g = GpuRun(cfg, W, e, h0, kv=kv, decode=True).np()
+    assert np.all(np.isfinite(g["out"]))
+    thr = cfg["act_threshold"]
+    adopt = O.Adoption(sel=g["sel"], halt_counts=g["halt"], eps_route=EPS_ROUTE["f32"], eps_halt=EPS_HALT["f32"])
+    ref = O.recurrent_forward(cfg, O.Params(W), e, h0, n, thr, start_pos=P, cache=oc, adopt=adopt, record=True)
+    assert adopt.route_disagree == 0 and adopt.halt_disagree == 0
+    np.testing.assert_array_equal(ref["halt_counts"], g["halt"])
+    err = rel_err(g["out"], ref["out"])
+    print(f"  max|d|/rms = {err:.3e}", flush=True)
+    assert err <= TOL["f32"]
+
+
 @pytest.mark.parametrize("start_pos,kv_heads,nan_past_end", [
     (300, 2, False),      # one key block, ragged
     (511, 1, True),       # exactly one full block of 512 keys; cache past the end holds NaN
