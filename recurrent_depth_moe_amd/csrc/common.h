@@ -74,6 +74,18 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Block-wide sum through wave_sum_dpp, otherwise as block_sum below.
+__device__ __forceinline__ float block_sum_dpp(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum_dpp(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
 // Block-wide sum for blockDim.x a multiple of 64 (<= 1024).  Every thread
 // gets the total.  `red` must hold blockDim.x/64 floats.
 __device__ __forceinline__ float block_sum(float v, float* red) {

@@ -63,7 +63,9 @@ __global__ void make_A_kernel(const float* log_A, const float* log_dt, float* A,
 
 // ------------------------------------------------------------ loop head
 
-template <typename TA>
+// NJ > 0: D = 4 RB NJ, every thread owns NJ whole float4 columns and all
+// loads are unconditional (issued together); NJ = 0: any D <= 4 RB MAXV4.
+template <typename TA, int NJ>
 __global__ __launch_bounds__(RB) void loop_head_kernel(const float* __restrict__ h, const float* __restrict__ e,
                                                        const float* __restrict__ emb, int loop_dim,
                                                        const float* __restrict__ g_rec,
@@ -77,30 +79,41 @@ __global__ __launch_bounds__(RB) void loop_head_kernel(const float* __restrict__
   __shared__ float red[RB / 64];
   const int64_t base = (int64_t)blockIdx.x * D;
   const int D4 = D >> 2;
-  float4 v[MAXV4];
+  float4 v[MAXV4], y[MAXV4], m[MAXV4];
+  // every load first (the loop embedding from a clamped, always valid
+  // address, added only on its channels), then the arithmetic
+#pragma unroll
+  for (int j = 0; j < (NJ ? NJ : MAXV4); ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (NJ || i4 < D4) {
+      const int d = i4 * 4;
+      v[j] = ld4(h + base + d);
+      y[j] = ld4(e + base + d);
+      if (loop_dim > 0) m[j] = ld4(emb + min(d, loop_dim - 4));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < MAXV4; ++j) {
+  for (int j = 0; j < (NJ ? NJ : MAXV4); ++j) {
     const int i4 = threadIdx.x + j * RB;
-    if (i4 < D4) {
+    if (NJ || i4 < D4) {
       const int d = i4 * 4;
-      float4 x = ld4(h + base + d);
-      const float4 y = ld4(e + base + d);
+      float4 x = v[j];
       if (d < loop_dim) {
-        const float4 m = ld4(emb + d);
-        x.x += m.x; x.y += m.y; x.z += m.z; x.w += m.w;
+        x.x += m[j].x; x.y += m[j].y; x.z += m[j].z; x.w += m[j].w;
       }
-      x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      x.x += y[j].x; x.y += y[j].y; x.z += y[j].z; x.w += y[j].w;
       v[j] = x;
       ss += dot4(x, x);
     }
   }
-  const float r1 = 1.0f / sqrtf(block_sum(ss, red) / D + eps);
+  const float r1 = 1.0f / sqrtf(block_sum_dpp(ss, red) / D + eps);
   ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < MAXV4; ++j) {
+  for (int j = 0; j < (NJ ? NJ : MAXV4); ++j) {
     const int i4 = threadIdx.x + j * RB;
-    if (i4 < D4) {
+    if (NJ || i4 < D4) {
       const int d = i4 * 4;
       const float4 g = ld4(g_rec + d);
       float4 x = v[j];
@@ -110,11 +123,11 @@ __global__ __launch_bounds__(RB) void loop_head_kernel(const float* __restrict__
       ss += dot4(x, x);
     }
   }
-  const float r2 = 1.0f / sqrtf(block_sum(ss, red) / D + eps);
+  const float r2 = 1.0f / sqrtf(block_sum_dpp(ss, red) / D + eps);
 #pragma unroll
-  for (int j = 0; j < MAXV4; ++j) {
+  for (int j = 0; j < (NJ ? NJ : MAXV4); ++j) {
     const int i4 = threadIdx.x + j * RB;
-    if (i4 < D4) {
+    if (NJ || i4 < D4) {
       const int d = i4 * 4;
       const float4 g = ld4(g_attn + d);
       const float4 x = v[j];
@@ -123,7 +136,7 @@ __global__ __launch_bounds__(RB) void loop_head_kernel(const float* __restrict__
   }
 }
 
-template <typename TO>
+template <typename TO, int NJ>
 __global__ __launch_bounds__(RB) void rmsnorm_kernel(const float* __restrict__ x, int64_t ldx,
                                                      const float* __restrict__ g, float eps, TO* __restrict__ out,
                                                      int64_t ldo, int D, const int32_t* live) {
@@ -133,20 +146,23 @@ __global__ __launch_bounds__(RB) void rmsnorm_kernel(const float* __restrict__ x
   TO* orow = out + (int64_t)blockIdx.x * ldo;
   const int D4 = D >> 2;
   float4 v[MAXV4];
+#pragma unroll
+  for (int j = 0; j < (NJ ? NJ : MAXV4); ++j) {
+    const int i4 = threadIdx.x + j * RB;
+    if (NJ || i4 < D4) v[j] = ld4(xr + i4 * 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < MAXV4; ++j) {
+  for (int j = 0; j < (NJ ? NJ : MAXV4); ++j) {
     const int i4 = threadIdx.x + j * RB;
-    if (i4 < D4) {
-      v[j] = ld4(xr + i4 * 4);
-      ss += dot4(v[j], v[j]);
-    }
+    if (NJ || i4 < D4) ss += dot4(v[j], v[j]);
   }
-  const float r = 1.0f / sqrtf(block_sum(ss, red) / D + eps);
+  const float r = 1.0f / sqrtf(block_sum_dpp(ss, red) / D + eps);
 #pragma unroll
-  for (int j = 0; j < MAXV4; ++j) {
+  for (int j = 0; j < (NJ ? NJ : MAXV4); ++j) {
     const int i4 = threadIdx.x + j * RB;
-    if (i4 < D4) {
+    if (NJ || i4 < D4) {
       const float4 gg = ld4(g + i4 * 4);
       const float4 y = v[j];
       st4(orow + i4 * 4, make_float4(y.x * r * gg.x, y.y * r * gg.y, y.z * r * gg.z, y.w * r * gg.w));
@@ -985,19 +1001,38 @@ void launch_make_A(const float* log_A, const float* log_dt, float* A, int D, hip
 void launch_loop_head(int act_bf16, const float* h, const float* e, const float* emb_t, int loop_dim,
                       const float* g_rec, const float* g_attn, float eps, float* c, void* a, int N, int D,
                       hipStream_t s, const int32_t* live_prev, int32_t* live_cur) {
-  if (act_bf16)
-    loop_head_kernel<bf16_t><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (bf16_t*)a, D, live_prev,
-                                              live_cur);
-  else
-    loop_head_kernel<float><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (float*)a, D, live_prev,
-                                             live_cur);
+#define RDT_LOOP_HEAD(TA, NJ) \
+  loop_head_kernel<TA, NJ><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (TA*)a, D, live_prev, live_cur)
+  const int nj = D % (4 * RB) == 0 ? D / (4 * RB) : 0;
+  if (act_bf16) {
+    switch (nj) {
+      case 1: RDT_LOOP_HEAD(bf16_t, 1); break;
+      case 2: RDT_LOOP_HEAD(bf16_t, 2); break;
+      case 3: RDT_LOOP_HEAD(bf16_t, 3); break;
+      case 4: RDT_LOOP_HEAD(bf16_t, 4); break;
+      default: RDT_LOOP_HEAD(bf16_t, 0); break;
+    }
+  } else {
+    RDT_LOOP_HEAD(float, 0);
+  }
+#undef RDT_LOOP_HEAD
 }
 
 void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, float eps, void* out, int64_t ldo,
                     int rows, int D, hipStream_t s, const int32_t* live) {
   if (rows <= 0) return;
-  if (out_bf16) rmsnorm_kernel<bf16_t><<<rows, RB, 0, s>>>(x, ldx, g, eps, (bf16_t*)out, ldo, D, live);
-  else rmsnorm_kernel<float><<<rows, RB, 0, s>>>(x, ldx, g, eps, (float*)out, ldo, D, live);
+  const int nj = D % (4 * RB) == 0 ? D / (4 * RB) : 0;
+  if (out_bf16) {
+    switch (nj) {
+      case 1: rmsnorm_kernel<bf16_t, 1><<<rows, RB, 0, s>>>(x, ldx, g, eps, (bf16_t*)out, ldo, D, live); break;
+      case 2: rmsnorm_kernel<bf16_t, 2><<<rows, RB, 0, s>>>(x, ldx, g, eps, (bf16_t*)out, ldo, D, live); break;
+      case 3: rmsnorm_kernel<bf16_t, 3><<<rows, RB, 0, s>>>(x, ldx, g, eps, (bf16_t*)out, ldo, D, live); break;
+      case 4: rmsnorm_kernel<bf16_t, 4><<<rows, RB, 0, s>>>(x, ldx, g, eps, (bf16_t*)out, ldo, D, live); break;
+      default: rmsnorm_kernel<bf16_t, 0><<<rows, RB, 0, s>>>(x, ldx, g, eps, (bf16_t*)out, ldo, D, live); break;
+    }
+  } else {
+    rmsnorm_kernel<float, 0><<<rows, RB, 0, s>>>(x, ldx, g, eps, (float*)out, ldo, D, live);
+  }
 }
 
 void launch_router_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* sel, float* gate,
