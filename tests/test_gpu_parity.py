@@ -81,6 +81,15 @@ def test_end_to_end_large_terms(name):
         assert len(np.unique(g["halt"])) > 1
 
 
+def test_end_to_end_groups_split_over_xcds():
+    """batch 4 x 2 kv heads = 8 (batch, kv head) groups: flash attention
+    gives each XCD its own group (the ordering the large prefill takes),
+    with a ragged sequence."""
+    cfg, W, e, h0 = _inputs("small_bf16", batch=4, seq=150)
+    assert cfg["batch"] * cfg["n_kv_heads"] % 8 == 0
+    _e2e(cfg, W, e, h0)
+
+
 @pytest.mark.parametrize("act", [0.99, 0.0])
 def test_end_to_end_wide_rows(act):
     """dim 1024 with rank-16 LoRA, top-2 plus one shared expert: the batched
