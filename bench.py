@@ -135,8 +135,9 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "copies": 4}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the single-GPU recurrent-block forward; runs on more than one GPU are not "
-              "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
+        print("bench.py measures the single-GPU recurrent-block forward; it does not run on more than one GPU "
+              "(the block shards over independent sequences, or over experts with an all-to-all per loop, "
+              "neither of which is built).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -14,7 +14,7 @@ Pages cited (title, then section):
        (zero.shotlearni.ng)
   [RC] "OpenMythos" (runchr.com, Korean copy of the project README)
 
-Readings of what the pages leave open (listed again in the design doc):
+Readings of what the pages leave open:
   * h0 = e: the recurrent stage receives the prelude output both as its state
     and as the frozen anchor ([ZS §Core Structure]).
   * loop-index embedding: frequencies theta^(-2j/loop_dim) for

@@ -62,7 +62,7 @@ def kv_capacity(cfg):
     return cfg["start_pos"] + cfg["seq"]
 
 
-class GpuRun:
+class DeviceRun:
     """One forward (or decode) through the C ABI with per-loop capture."""
 
     def __init__(self, cfg, W, e, h0, n_loops=None, thr=None, start_pos=None, kv=None, capture=True,

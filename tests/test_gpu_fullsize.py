@@ -21,7 +21,7 @@ import pytest
 from oracle import rdt_oracle as O
 from workloads import configs, generate
 
-from gpu_support import EPS_ROUTE, TOL, GpuRun, fill_cache, kv_capacity, rel_err
+from gpu_support import EPS_ROUTE, TOL, DeviceRun, fill_cache, kv_capacity, rel_err
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -93,7 +93,7 @@ def _dispatch_and_router(cfg, P, run):
 
 
 def _gpu(cfg, W, e, h0, **kw):
-    g = GpuRun(cfg, W, e, h0, **kw)
+    g = DeviceRun(cfg, W, e, h0, **kw)
     r = g.np()
     r["h0"] = h0
     return g, r

@@ -18,7 +18,7 @@ import pytest
 from oracle import rdt_oracle as O
 from workloads import configs, generate
 
-from gpu_support import EPS_HALT, EPS_ROUTE, TOL, GpuRun, fill_cache, kv_capacity, read_cache, rel_err
+from gpu_support import EPS_HALT, EPS_ROUTE, TOL, DeviceRun, fill_cache, kv_capacity, read_cache, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def _inputs(name, scales=None, **over):
 def _e2e(cfg, W, e, h0, **kw):
     print(f"[e2e] {cfg['name']} B={cfg['batch']} T={cfg['seq']} loops={cfg['n_loops']} thr={cfg['act_threshold']}",
           flush=True)
-    g = GpuRun(cfg, W, e, h0, **kw).np()
+    g = DeviceRun(cfg, W, e, h0, **kw).np()
     N = e.shape[0] * e.shape[1]
     dt = cfg["dtype"]
     adopt = O.Adoption(sel=g["sel"], halt_counts=g["halt"], eps_route=EPS_ROUTE[dt], eps_halt=EPS_HALT[dt])
@@ -127,7 +127,7 @@ def test_router_and_dispatch_stage(name):
     """Oracle router on the GPU's own f: bit-identical choices; dispatch
     tables equal a brute-force stable sort of the choices."""
     cfg, W, e, h0 = _inputs(name, n_loops=1, act_threshold=0.0)
-    run = GpuRun(cfg, W, e, h0)
+    run = DeviceRun(cfg, W, e, h0)
     import torch
     B, T, D = e.shape
     N, k, E = B * T, cfg["top_k"], cfg["n_experts"]
@@ -159,7 +159,7 @@ def test_router_ties_go_to_lower_index():
     rw[5] = rw[2]
     rw[7] = rw[0]
     W["router_w"] = rw
-    g = GpuRun(cfg, W, e, h0).np()
+    g = DeviceRun(cfg, W, e, h0).np()
     sel = g["sel"][0]
     for row in sel:
         row = list(row)
@@ -172,8 +172,8 @@ def test_router_ties_go_to_lower_index():
 
 def test_deterministic_bitwise():
     cfg, W, e, h0 = _inputs("small_bf16")
-    a = GpuRun(cfg, W, e, h0).np()
-    b = GpuRun(cfg, W, e, h0).np()
+    a = DeviceRun(cfg, W, e, h0).np()
+    b = DeviceRun(cfg, W, e, h0).np()
     for key in ("out", "halt", "h", "sel", "p"):
         np.testing.assert_array_equal(a[key], b[key])
 
@@ -223,7 +223,7 @@ def test_mla_decode_against_random_latent_cache(start_pos):
         oc[t]["c_kv"][:, :P] = ckv
         oc[t]["k_rope"][:, :P] = kr
     print(f"[mla decode] B={B} pos={P} loops={n}", flush=True)
-    g = GpuRun(cfg, W, e, h0, kv=kv, decode=True).np()
+    g = DeviceRun(cfg, W, e, h0, kv=kv, decode=True).np()
     assert np.all(np.isfinite(g["out"]))
     thr = cfg["act_threshold"]
     adopt = O.Adoption(sel=g["sel"], halt_counts=g["halt"], eps_route=EPS_ROUTE["f32"], eps_halt=EPS_HALT["f32"])
@@ -263,7 +263,7 @@ def test_decode_against_random_cache(start_pos, kv_heads, nan_past_end):
         oc[t]["v"][:, :, :P] = O.as_f64(V)
     print(f"[decode] {cfg['name']} B={B} pos={P} kv_heads={kv_heads} loops={n} nan_past_end={nan_past_end}",
           flush=True)
-    g = GpuRun(cfg, W, e, h0, kv=kv, decode=True).np()
+    g = DeviceRun(cfg, W, e, h0, kv=kv, decode=True).np()
     assert np.all(np.isfinite(g["out"]))
     adopt = O.Adoption(sel=g["sel"], halt_counts=g["halt"], eps_route=EPS_ROUTE["bf16"], eps_halt=EPS_HALT["bf16"])
     ref = O.recurrent_forward(cfg, O.Params(W), e, h0, n, 0.0, start_pos=P, cache=oc, adopt=adopt, record=True)
@@ -290,11 +290,11 @@ def test_prefill_then_decode_matches_full_prefill(name):
     B, T, n = cfg["batch"], cfg["seq"], cfg["n_loops"]
     cfgc = dict(cfg, start_pos=0)
     kv = torch.zeros(binding.kv_cache_bytes(cfg, B, T, n), dtype=torch.uint8, device="cuda")
-    full = GpuRun(cfg, W, e, h0).np()
+    full = DeviceRun(cfg, W, e, h0).np()
     pre_cfg = dict(cfgc, seq=T - 1)
-    GpuRun(pre_cfg, W, e[:, :T - 1].copy(), h0[:, :T - 1].copy(), kv=kv, start_pos=0, capture=False, kv_cap=T)
+    DeviceRun(pre_cfg, W, e[:, :T - 1].copy(), h0[:, :T - 1].copy(), kv=kv, start_pos=0, capture=False, kv_cap=T)
     step_cfg = dict(cfgc, seq=1, start_pos=T - 1)
-    g = GpuRun(step_cfg, W, e[:, T - 1:].copy(), h0[:, T - 1:].copy(), kv=kv, decode=True, kv_cap=T).np()
+    g = DeviceRun(step_cfg, W, e[:, T - 1:].copy(), h0[:, T - 1:].copy(), kv=kv, decode=True, kv_cap=T).np()
     tol = TOL[cfg["dtype"]]
     assert rel_err(g["out"][:, 0], full["out"][:, T - 1]) < tol
     ref = O.recurrent_forward(cfg, O.Params(W), e, h0, n, 0.0)["out"]
@@ -315,12 +315,12 @@ def test_chained_decode_steps_match_full_prefill(name, act):
     steps = 4
     cfgc = dict(cfg, start_pos=0)
     kv = torch.zeros(binding.kv_cache_bytes(cfg, B, T, n), dtype=torch.uint8, device="cuda")
-    full = GpuRun(cfg, W, e, h0).np()
+    full = DeviceRun(cfg, W, e, h0).np()
     P0 = T - steps
-    GpuRun(dict(cfgc, seq=P0), W, e[:, :P0].copy(), h0[:, :P0].copy(), kv=kv, start_pos=0, capture=False, kv_cap=T)
+    DeviceRun(dict(cfgc, seq=P0), W, e[:, :P0].copy(), h0[:, :P0].copy(), kv=kv, start_pos=0, capture=False, kv_cap=T)
     tol = TOL[cfg["dtype"]]
     for i in range(P0, T):
-        g = GpuRun(dict(cfgc, seq=1, start_pos=i), W, e[:, i:i + 1].copy(), h0[:, i:i + 1].copy(), kv=kv,
+        g = DeviceRun(dict(cfgc, seq=1, start_pos=i), W, e[:, i:i + 1].copy(), h0[:, i:i + 1].copy(), kv=kv,
                    decode=True, kv_cap=T).np()
         print(f"[chained decode] {name} position {i}: max|d|/rms {rel_err(g['out'][:, 0], full['out'][:, i]):.2e}",
               flush=True)

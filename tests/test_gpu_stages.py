@@ -14,7 +14,7 @@ import pytest
 from oracle import rdt_oracle as O
 from workloads import configs, generate
 
-from gpu_support import GpuRun
+from gpu_support import DeviceRun
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def stage_run(request):
     W = generate.make_weights(cfg)
     e, h0 = generate.make_inputs(cfg)
     print(f"[stages] {name}", flush=True)
-    run = GpuRun(cfg, W, e, h0)
+    run = DeviceRun(cfg, W, e, h0)
     return cfg, W, e, h0, run
 
 
