@@ -195,16 +195,20 @@ rdt_status rdt_workspace_offset(const rdt_block* blk, int32_t B, int32_t T, cons
                                 size_t* offset, size_t* bytes);
 
 /* Per-stage kernel timing with HIP events recorded on the call's stream
- * around each stage's launches (for benchmarks; off by default, and a small
- * host-side cost per launch when on).  rdt_set_timing(1) clears the totals;
- * rdt_read_timing waits for the recorded events and returns, per stage, the
- * summed milliseconds and the number of timed launches since then. */
+ * around each stage's launches (for benchmarks; off by default; each timed
+ * launch costs two event records on the stream and some host time).
+ * rdt_set_timing(1) times every stage, rdt_set_timing_stages(mask) only the
+ * stages whose bit (1 << rdt_stage) is set, 0 turns timing off; both clear
+ * the totals.  rdt_read_timing waits for the recorded events and returns,
+ * per stage, the summed milliseconds and the number of timed launches since
+ * then (RDT_STAGE_COUNT entries each). */
 enum rdt_stage {
   RDT_STAGE_LOOP_HEAD = 0, RDT_STAGE_QKV, RDT_STAGE_ATTN, RDT_STAGE_OPROJ, RDT_STAGE_FFN_NORM,
   RDT_STAGE_ROUTER, RDT_STAGE_DISPATCH, RDT_STAGE_EXPERT_GATEUP, RDT_STAGE_EXPERT_DOWN,
   RDT_STAGE_SHARED_GATEUP, RDT_STAGE_SHARED_DOWN, RDT_STAGE_TAIL, RDT_STAGE_COUNT
 };
 rdt_status rdt_set_timing(rdt_block* blk, int32_t enable);
+rdt_status rdt_set_timing_stages(rdt_block* blk, uint32_t stage_mask);
 rdt_status rdt_read_timing(rdt_block* blk, double* total_ms, int64_t* launches);
 
 /* Host-only variants that take the configuration instead of a handle, so a

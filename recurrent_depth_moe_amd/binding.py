@@ -76,6 +76,7 @@ def lib():
         "rdt_get_A": ([vp, vp], i32),
         "rdt_set_capture": ([vp, vp, vp, vp, i32], i32),
         "rdt_set_timing": ([vp, i32], i32),
+        "rdt_set_timing_stages": ([vp, ctypes.c_uint32], i32),
         "rdt_read_timing": ([vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
@@ -197,6 +198,10 @@ class Block:
 
     def set_timing(self, enable=True):
         check(lib().rdt_set_timing(self._h, 1 if enable else 0))
+
+    def set_timing_stages(self, stages):
+        """Time only the named stages (an empty list turns timing off)."""
+        check(lib().rdt_set_timing_stages(self._h, sum(1 << STAGES.index(s) for s in stages)))
 
     def read_timing(self):
         """{stage: (total_ms, launches)} since set_timing(True)."""

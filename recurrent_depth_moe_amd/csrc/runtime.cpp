@@ -249,8 +249,9 @@ struct rdt_block {
   int32_t* cap_sel = nullptr;
   float* cap_p = nullptr;
   int cap_loops = 0;
-  // stage timing
+  // stage timing (stages whose bit is set in timing_mask)
   bool timing = false;
+  uint32_t timing_mask = 0;
   struct Pending {
     int stage;
     hipEvent_t a, b;
@@ -281,7 +282,9 @@ struct StageTimer {
   int stage;
   hipEvent_t a = nullptr;
   StageTimer(rdt_block* b_, hipStream_t s_, int st) : b(b_), s(s_), stage(st) {
-    if (b->timing && (a = take_event(b)) != nullptr && hipEventRecord(a, s) != hipSuccess) a = nullptr;
+    if (b->timing && ((b->timing_mask >> st) & 1u) && (a = take_event(b)) != nullptr &&
+        hipEventRecord(a, s) != hipSuccess)
+      a = nullptr;
   }
   ~StageTimer() {
     if (!a) return;
@@ -586,8 +589,13 @@ rdt_status rdt_set_capture(rdt_block* b, float* h_loops, int32_t* sel_loops, flo
 }
 
 rdt_status rdt_set_timing(rdt_block* b, int32_t enable) {
+  return rdt_set_timing_stages(b, enable != 0 ? (1u << RDT_STAGE_COUNT) - 1u : 0u);
+}
+
+rdt_status rdt_set_timing_stages(rdt_block* b, uint32_t stage_mask) {
   if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
-  b->timing = enable != 0;
+  b->timing_mask = stage_mask & ((1u << RDT_STAGE_COUNT) - 1u);
+  b->timing = b->timing_mask != 0;
   for (int i = 0; i < RDT_STAGE_COUNT; ++i) {
     b->stage_ms[i] = 0.0;
     b->stage_n[i] = 0;
