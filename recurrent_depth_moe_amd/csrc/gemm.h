@@ -48,7 +48,6 @@ struct GemmParams {
   const int32_t* grp_end;    // [E+1] offsets: rows of group e are [grp_end[e], grp_end[e+1])
   int n_groups;
   int dense_gm;              // dense raster: m-tiles per group of the tile order
-  int skinny_mt_cap;         // skinny kernel: m-tiles its grid is sized for
   const int32_t* live;       // running positions after the previous loop (null: always run)
   // big kernel, grouped products: RDT_NUM_XCD tile-claim counters, zero at
   // launch (null: static round-robin over each XCD's share of the tiles)

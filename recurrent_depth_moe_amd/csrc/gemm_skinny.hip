@@ -2,27 +2,27 @@
 // router logits (32 tokens x all experts per block) and every matrix
 // product of a decode step (32 sequences, or the 1-2 rows an expert gets).
 //
-// Block = 4 wave64s over one 32-row x NC-column tile (x2 for the fused
-// gate|up product).  The K range is split in four; each wave runs
-// v_mfma_f32_32x32x16_bf16 over its quarter with both operands streamed
+// Block = NW wave64s over one 32-row x NC-column tile (x2 for the fused
+// gate|up product).  The K range is split NW ways; each wave runs
+// v_mfma_f32_32x32x16_bf16 over its share with both operands streamed
 // straight from global memory (lane l reads 16 bytes of row / column l % 32
-// at k offset 8 * (l / 32)), four k-steps in flight.  Partial accumulators
-// meet in LDS, are summed in a fixed order (deterministic) and go through
-// the same epilogues as the large kernels.  These products are bound by
-// weight streaming, not by MFMA.
+// at k offset 8 * (l / 32)), the next U k-steps loading while the current U
+// multiply.  Partial accumulators meet in LDS, are summed in a fixed order
+// (deterministic) and go through the same epilogues as the large kernels.
+// These products are bound by weight streaming, not by MFMA.
 #include "gemm_device.h"
 
 namespace {
 
-template <int NC, bool DUAL, int EPI, typename TO>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
+template <int NC, bool DUAL, int EPI, typename TO, int NW, int U>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmParams p) {
   RDT_SKIP_IF_ALL_HALTED(p.live);
   constexpr int NF = NC / 32, NB = DUAL ? 2 : 1, NA = NB * NF;
-  __shared__ float red[4][NA][16 * 64];
+  __shared__ float red[NW][NA][16 * 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ntn = (p.N + NC - 1) / NC;
   const int n_mt = p.mt_start ? p.mt_start[p.n_groups] : (p.M + 31) / 32;
-  const int mt = blockIdx.x % p.skinny_mt_cap, nt = blockIdx.x / p.skinny_mt_cap;
+  const int nt = blockIdx.x % ntn, mt = blockIdx.x / ntn;
   if (mt >= n_mt || nt >= ntn) return;   // grouped grids are sized for the worst case
   int row0, rows, grp;
   tile_rows(p, mt, 32, row0, rows, grp);
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
   Wb[0] = (const bf16_t*)p.W0 + (int64_t)grp * p.w_stride;
   if constexpr (DUAL) Wb[NB - 1] = (const bf16_t*)p.W1 + (int64_t)grp * p.w_stride;
 
-  const int kq = p.K / 4, kbeg = w * kq, kk = 8 * (lane >> 5);
+  const int kq = p.K / NW, kbeg = w * kq, kk = 8 * (lane >> 5);
   const int r = lane & 31;
   const int m = row0 + (r < rows ? r : 0);
   const int arow = p.a_rows ? p.a_rows[m] : m;
@@ -52,20 +52,43 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 
   const int steps = kq / 16;
   int s = 0;
-  for (; s + 4 <= steps; s += 4) {
-    uint4 av[4], bv[4][NA];
+  auto load = [&](int s0, uint4 (&av)[U], uint4 (&bv)[U][NA]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      av[u] = *(const uint4*)(ap + (s + u) * 16);
+    for (int u = 0; u < U; ++u) {
+      av[u] = *(const uint4*)(ap + (s0 + u) * 16);
 #pragma unroll
-      for (int i = 0; i < NA; ++i) bv[u][i] = *(const uint4*)(bp[i] + (s + u) * 16);
+      for (int i = 0; i < NA; ++i) bv[u][i] = *(const uint4*)(bp[i] + (s0 + u) * 16);
     }
+  };
+  auto mma = [&](const uint4 (&av)[U], const uint4 (&bv)[U][NA]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < NA; ++i)
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
                                                          __builtin_bit_cast(bf16x8_t, bv[u][i]), acc[i], 0, 0, 0);
+  };
+  // two register buffers: the loads of the next U steps are in flight while
+  // the MFMAs of the current ones run.  The scheduling barriers keep the
+  // compiler from sinking loads between the MFMAs (it would otherwise trade
+  // the loads in flight for registers, which halves the streaming rate).
+  {
+    uint4 a0[U], b0[U][NA], a1[U], b1[U][NA];
+    if (U <= steps) load(0, a0, b0);
+    for (; s + 2 * U <= steps; s += 2 * U) {
+      load(s + U, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 3 * U <= steps) load(s + 2 * U, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (s + U <= steps) {
+      mma(a0, b0);
+      s += U;
+    }
   }
   for (; s < steps; ++s) {
     const uint4 a1 = *(const uint4*)(ap + s * 16);
@@ -81,13 +104,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
     for (int e = 0; e < 16; ++e) red[w][i][e * 64 + lane] = acc[i][e];
   __syncthreads();
   // accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32
-  for (int idx = threadIdx.x; idx < NF * 16 * 64; idx += 256) {
+  for (int idx = threadIdx.x; idx < NF * 16 * 64; idx += 64 * NW) {
     const int f = idx / (16 * 64), rem = idx - f * 16 * 64, e = rem >> 6, l = rem & 63;
     const int row = 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
     const int n = n0 + f * 32 + (l & 31);
     float v = 0.f, v2 = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       v += red[ww][f][e * 64 + l];
       v2 += DUAL ? red[ww][NF + f][e * 64 + l] : red[ww][f][e * 64 + (l ^ 1)];
     }
@@ -97,18 +120,18 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 
 }  // namespace
 
-// grid = (m-tiles the grid is sized for) x (n-tiles); grouped products size
-// it for the worst case and surplus blocks exit at once
+// grid = (m-tiles the grid is sized for) x (n-tiles), n-tile fastest, so the
+// live m-tiles come first in dispatch order; grouped products size the grid
+// for the worst case and the surplus blocks at its end exit at once
 template <int NC, bool DUAL, int EPI, typename TO>
 static void launch_skinny_t(const GemmParams& p, int mt_cap, hipStream_t s) {
   const int ntn = (p.N + NC - 1) / NC;
-  gemm_skinny_kernel<NC, DUAL, EPI, TO><<<mt_cap * ntn, 256, 0, s>>>(p);
+  gemm_skinny_kernel<NC, DUAL, EPI, TO, 4, 4><<<mt_cap * ntn, 256, 0, s>>>(p);
 }
 
 void launch_gemm_bf16_skinny(const GemmParams& p0, int epi, bool dual, int out_is_bf16, int mt_cap, int nc,
                              hipStream_t s) {
-  GemmParams p = p0;
-  p.skinny_mt_cap = mt_cap;
+  const GemmParams& p = p0;
   if (dual) {
     if (out_is_bf16) launch_skinny_t<32, true, EPI_SWIGLU, bf16_t>(p, mt_cap, s);
     else launch_skinny_t<32, true, EPI_SWIGLU, float>(p, mt_cap, s);
