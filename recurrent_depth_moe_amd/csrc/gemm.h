@@ -63,9 +63,11 @@ struct GemmParams {
 void launch_gemm_bf16_big(const GemmParams& p, int epi, bool dual, int out_is_bf16, int n_cu, hipStream_t s,
                           int bn = 256);
 // at most 32 rows per m-tile (grouped schedules built with RDT_BM_SKINNY),
-// nc = 32 or 64 output columns per block; mt_cap bounds the m-tile count
+// nc = 32 or 64 output columns per block; mt_cap bounds the m-tile count;
+// nw = 8 splits K over eight waves instead of four (fp32 EPI_STORE
+// products with K a multiple of 128; others ignore it)
 void launch_gemm_bf16_skinny(const GemmParams& p, int epi, bool dual, int out_is_bf16, int mt_cap, int nc,
-                             hipStream_t s);
+                             hipStream_t s, int nw = 4);
 void launch_gemm_f32(const GemmParams& p, int epi, bool dual, int n_cu, hipStream_t s);
 
 // m-tile heights the kernels are built with (the dispatch builds schedules

@@ -123,15 +123,22 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmParams p) {
 // grid = (m-tiles the grid is sized for) x (n-tiles), n-tile fastest, so the
 // live m-tiles come first in dispatch order; grouped products size the grid
 // for the worst case and the surplus blocks at its end exit at once
-template <int NC, bool DUAL, int EPI, typename TO>
+template <int NC, bool DUAL, int EPI, typename TO, int NW = 4, int U = 4>
 static void launch_skinny_t(const GemmParams& p, int mt_cap, hipStream_t s) {
   const int ntn = (p.N + NC - 1) / NC;
-  gemm_skinny_kernel<NC, DUAL, EPI, TO, 4, 4><<<mt_cap * ntn, 256, 0, s>>>(p);
+  gemm_skinny_kernel<NC, DUAL, EPI, TO, NW, U><<<mt_cap * ntn, 64 * NW, 0, s>>>(p);
 }
 
 void launch_gemm_bf16_skinny(const GemmParams& p0, int epi, bool dual, int out_is_bf16, int mt_cap, int nc,
-                             hipStream_t s) {
+                             hipStream_t s, int nw) {
   const GemmParams& p = p0;
+  // eight waves, eight k-steps per buffer: fp32 products with few blocks
+  // (router logits), where the waves' sequential load round trips set the time
+  if (nw == 8 && !dual && epi == EPI_STORE && !out_is_bf16 && p.K % (8 * 16) == 0) {
+    if (nc == 64) launch_skinny_t<64, false, EPI_STORE, float, 8, 8>(p, mt_cap, s);
+    else launch_skinny_t<32, false, EPI_STORE, float, 8, 8>(p, mt_cap, s);
+    return;
+  }
   if (dual) {
     if (out_is_bf16) launch_skinny_t<32, true, EPI_SWIGLU, bf16_t>(p, mt_cap, s);
     else launch_skinny_t<32, true, EPI_SWIGLU, float>(p, mt_cap, s);

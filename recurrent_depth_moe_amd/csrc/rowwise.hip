@@ -171,23 +171,47 @@ __global__ __launch_bounds__(RB) void rmsnorm_kernel(const float* __restrict__ x
 }
 
 // ------------------------------------------------------------ router
-// One wave per token.  [ZS §MoE]: softmax scores over all experts; top-k
-// taken on logits + router_bias; gates = chosen scores renormalised.
+// Sixteen lanes (one DPP row) per token, lane j holding experts j, j + 16,
+// ...  [ZS §MoE]: softmax scores over all experts; top-k taken on
+// logits + router_bias (ties to the lower expert index); gates = chosen
+// scores renormalised.  Every reduction stays inside the 16-lane row
+// (quad_perm / row mirror DPP moves), so no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ int dpp_row_mov(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& best, int& bi, float& bz) {
+  const float ob = __builtin_bit_cast(float, dpp_row_mov<CTRL>(__builtin_bit_cast(int, best)));
+  const int oi = dpp_row_mov<CTRL>(bi);
+  const float oz = __builtin_bit_cast(float, dpp_row_mov<CTRL>(__builtin_bit_cast(int, bz)));
+  if (ob > best || (ob == best && oi < bi)) {
+    best = ob;
+    bi = oi;
+    bz = oz;
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ float max_step(float m) {
+  return fmaxf(m, __builtin_bit_cast(float, dpp_row_mov<CTRL>(__builtin_bit_cast(int, m))));
+}
+
+template <int EPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
                                                           const float* __restrict__ bias, int N, int E, int k,
                                                           int32_t* __restrict__ sel, float* __restrict__ gate,
                                                           int32_t* __restrict__ cap_sel, const int32_t* live) {
   RDT_SKIP_IF_ALL_HALTED(live);
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= N) return;
+  const int l16 = threadIdx.x & 15;
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= N) return;   // whole 16-lane rows leave together
   const float* z = logits + (int64_t)row * E;
-  float zv[4], bv[4];
+  float zv[EPL], bv[EPL];
   unsigned taken = 0;
   float m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ex = lane + 64 * j;
+  for (int j = 0; j < EPL; ++j) {
+    const int ex = l16 + 16 * j;
     if (ex < E) {
       zv[j] = z[ex];
       const float b = zv[j] + bias[ex];
@@ -199,7 +223,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       taken |= 1u << j;
     }
   }
-  m = wave_max(m);
+  m = max_step<0xB1>(m);    // quad_perm [1, 0, 3, 2]
+  m = max_step<0x4E>(m);    // quad_perm [2, 3, 0, 1]
+  m = max_step<0x141>(m);   // row_half_mirror
+  m = max_step<0x140>(m);   // row_mirror
   float num[8];
   int idx[8];
   float den = 0.f;
@@ -207,31 +234,24 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     float best = -INFINITY, bz = 0.f;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ex = lane + 64 * j;
+    for (int j = 0; j < EPL; ++j) {
+      const int ex = l16 + 16 * j;
       if (!((taken >> j) & 1u) && (bv[j] > best || (bv[j] == best && ex < bi))) {
         best = bv[j];
         bi = ex;
         bz = zv[j];
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      const float oz = __shfl_xor(bz, o, 64);
-      if (ob > best || (ob == best && oi < bi)) {
-        best = ob;
-        bi = oi;
-        bz = oz;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    argmax_step<0xB1>(best, bi, bz);
+    argmax_step<0x4E>(best, bi, bz);
+    argmax_step<0x141>(best, bi, bz);
+    argmax_step<0x140>(best, bi, bz);
+    if ((bi & 15) == l16) taken |= 1u << (bi >> 4);
     num[kk] = expf(bz - m);
     idx[kk] = bi;
     den += num[kk];
   }
-  if (lane == 0) {
+  if (l16 == 0) {
     for (int kk = 0; kk < k; ++kk) {
       sel[(int64_t)row * k + kk] = idx[kk];
       gate[(int64_t)row * k + kk] = num[kk] / den;
@@ -256,7 +276,9 @@ __global__ __launch_bounds__(RDT_DISP_TILE) void dispatch_count_kernel(const int
 }
 
 // per expert: exclusive scan over tiles (tile base), totals -> offsets,
-// m-tile schedule of height bm
+// m-tile schedule of height bm.  Thread ex owns expert ex; the scans over
+// experts are wave scans plus the totals of the earlier waves.
+constexpr int RDT_SCAN_BATCH = 64;   // tile counts one thread holds in registers
 __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t* __restrict__ tile_counts,
                                                                         int ntiles, int E, int bm,
                                                                         int32_t* __restrict__ offsets,
@@ -267,56 +289,80 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
                                                                         int n_claim, const int32_t* live) {
   RDT_SKIP_IF_ALL_HALTED(live);
   if ((int)threadIdx.x < n_claim) tile_claim[threadIdx.x] = 0;
-  __shared__ int tot[RDT_MAX_EXPERTS];
-  __shared__ int off[RDT_MAX_EXPERTS + 1];
-  __shared__ int mts[RDT_MAX_EXPERTS + 1];
-  const int ex = threadIdx.x;
-  if (ex < E) {
-    // exclusive scan down the tiles, 16 counts loaded before any is used
-    // (the loads are independent; one at a time they would serialise)
-    int run = 0;
-    for (int t0 = 0; t0 < ntiles; t0 += 16) {
-      int c[16];
+  __shared__ int wsum[RDT_MAX_EXPERTS / 64][2];
+  const int ex = threadIdx.x, lane = ex & 63, wv = ex >> 6;
+  const bool own = ex < E;
+  // exclusive scan down the tiles; with at most RDT_SCAN_BATCH tiles every
+  // count is loaded before any is used and the prefixes stay in registers
+  const bool one_batch = ntiles <= RDT_SCAN_BATCH;
+  int pre[RDT_SCAN_BATCH];
+  int run = 0;
+  if (own) {
+    if (one_batch) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) c[u] = t0 + u < ntiles ? tile_counts[(int64_t)(t0 + u) * E + ex] : 0;
+      for (int u = 0; u < RDT_SCAN_BATCH; ++u) pre[u] = u < ntiles ? tile_counts[(int64_t)u * E + ex] : 0;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (t0 + u < ntiles) tile_counts[(int64_t)(t0 + u) * E + ex] = run;
-        run += c[u];
+      for (int u = 0; u < RDT_SCAN_BATCH; ++u) {
+        const int c = pre[u];
+        pre[u] = run;
+        run += c;
+      }
+    } else {
+      for (int t0 = 0; t0 < ntiles; t0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) c[u] = t0 + u < ntiles ? tile_counts[(int64_t)(t0 + u) * E + ex] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (t0 + u < ntiles) tile_counts[(int64_t)(t0 + u) * E + ex] = run;
+          run += c[u];
+        }
       }
     }
-    tot[ex] = run;
+  }
+  // exclusive scans over experts of the row totals and of the m-tile counts
+  const int tot = own ? run : 0, nmt = own ? (run + bm - 1) / bm : 0;
+  int it = tot, im = nmt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(it, o, 64), b = __shfl_up(im, o, 64);
+    if (lane >= o) {
+      it += a;
+      im += b;
+    }
+  }
+  if (lane == 63) {
+    wsum[wv][0] = it;
+    wsum[wv][1] = im;
   }
   __syncthreads();
-  if (ex == 0) {
-    int o = 0, m = 0;
-    for (int i = 0; i < E; ++i) {
-      off[i] = o;
-      mts[i] = m;
-      o += tot[i];
-      m += (tot[i] + bm - 1) / bm;
-    }
-    off[E] = o;
-    mts[E] = m;
+  int off = it - tot, mts = im - nmt;
+  for (int w = 0; w < wv; ++w) {
+    off += wsum[w][0];
+    mts += wsum[w][1];
   }
-  __syncthreads();
-  if (ex <= E) {
-    offsets[ex] = off[ex];
-    mt_start[ex] = mts[ex];
+  if (ex <= E) {   // thread E writes the totals
+    offsets[ex] = off;
+    mt_start[ex] = mts;
   }
-  if (ex < E) {
-    for (int t0 = 0; t0 < ntiles; t0 += 16) {
-      int c[16];
+  if (own) {
+    if (one_batch) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) c[u] = t0 + u < ntiles ? tile_counts[(int64_t)(t0 + u) * E + ex] : 0;
+      for (int u = 0; u < RDT_SCAN_BATCH; ++u)
+        if (u < ntiles) tile_counts[(int64_t)u * E + ex] = pre[u] + off;
+    } else {
+      for (int t0 = 0; t0 < ntiles; t0 += 16) {
+        int c[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (t0 + u < ntiles) tile_counts[(int64_t)(t0 + u) * E + ex] = c[u] + off[ex];
+        for (int u = 0; u < 16; ++u) c[u] = t0 + u < ntiles ? tile_counts[(int64_t)(t0 + u) * E + ex] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (t0 + u < ntiles) tile_counts[(int64_t)(t0 + u) * E + ex] = c[u] + off;
+      }
     }
-    const int nt = mts[ex + 1] - mts[ex];
-    for (int i = 0; i < nt; ++i) {
-      tile_grp[mts[ex] + i] = ex;
-      tile_row0[mts[ex] + i] = off[ex] + i * bm;
+    for (int i = 0; i < nmt; ++i) {
+      tile_grp[mts + i] = ex;
+      tile_row0[mts + i] = off + i * bm;
     }
   }
 }
@@ -1037,7 +1083,12 @@ void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, f
 
 void launch_router_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* sel, float* gate,
                         int32_t* cap_sel, hipStream_t s, const int32_t* live) {
-  router_topk_kernel<<<(N + 3) / 4, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
+  const dim3 grid((N + 15) / 16);
+  if (E <= 16) router_topk_kernel<1><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
+  else if (E <= 32) router_topk_kernel<2><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
+  else if (E <= 64) router_topk_kernel<4><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
+  else if (E <= 128) router_topk_kernel<8><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
+  else router_topk_kernel<16><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
 }
 
 void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,

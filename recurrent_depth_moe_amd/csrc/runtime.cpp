@@ -670,7 +670,10 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     const bool grouped = gp.mt_start != nullptr;
     if (T == 1 || narrow) {
       const int cap = grouped ? p.max_mt : (gp.M + RDT_BM_SKINNY - 1) / RDT_BM_SKINNY;
-      launch_gemm_bf16_skinny(gp, epi, dual, out_bf16, cap, narrow ? 64 : 32, s);
+      // narrow outputs (router logits): 64-column blocks while they still
+      // give every CU one, eight waves per block
+      const int nc = narrow && cap * ((gp.N + 63) / 64) >= b->n_cu ? 64 : 32;
+      launch_gemm_bf16_skinny(gp, epi, dual, out_bf16, cap, nc, s, narrow ? 8 : 4);
     } else {
       // 192-column tiles where they fill the rounds of CUs markedly better
       // than 256-column ones (e.g. dense N = 3072 on 256 CUs)
