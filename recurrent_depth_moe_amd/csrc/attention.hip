@@ -334,8 +334,9 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
 //   S^T = K Q^T : A = 16 keys x 32 dims, B = Q^T (heads on the column axis),
 //                 lane l gets keys 4*(l/16)+i of the 16-key group for head l%16;
 //   O   = P V   : A = P with lane l holding head l%16 at the eight keys it
-//                 already scored in two adjacent groups, B = V read from V^T
-//                 in that same key order (two 8-byte pieces per lane).
+//                 already scored in two adjacent groups (the key slots are
+//                 ordered so those eight are consecutive), B = V read from
+//                 V^T in that same key order (one 16-byte piece per lane).
 // Each wave takes an exact softmax over its keys (scores stay in registers),
 // the four waves merge through LDS, and the block leaves one partial
 // (max, sum, unnormalised o) per head; a second kernel merges the partials
@@ -377,27 +378,49 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16_t* __
     }
   }
 
-  // scores of 8 groups of 16 keys; element i of group gi is key j0 + 16 gi + 4 qd + i
+  // Scores of 8 groups of 16 key slots.  Slot s of group gi = 2 c + h is key
+  // j0 + 32 c + 8 (s / 4) + 4 h + s % 4, so accumulator element i of lane
+  // (qd, c16) in groups 2c and 2c+1 holds keys j0 + 32 c + 8 qd + i and
+  // + 4 + i: eight consecutive keys, which is the k order P takes into the
+  // P V product and lets each lane read V^T in 16-byte pieces.  All K loads
+  // are issued before the first product, the V^T loads right after the
+  // products (they do not depend on the scores), so the waits come once.
+  uint4 kv4[8][4];
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi) {
+    const int key = min(j0 + 32 * (gi >> 1) + 8 * (c16 >> 2) + 4 * (gi & 1) + (c16 & 3), cap - 1);
+    const bf16_t* kr = kb + (int64_t)key * DEC_D + 8 * qd;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) kv4[gi][ds] = *(const uint4*)(kr + 32 * ds);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   floatx4_t sc[8];
 #pragma unroll
   for (int gi = 0; gi < 8; ++gi) {
-    const int key = min(j0 + 16 * gi + c16, cap - 1);
-    const bf16_t* kr = kb + (int64_t)key * DEC_D + 8 * qd;
-    uint4 kv4[4];
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) kv4[ds] = *(const uint4*)(kr + 32 * ds);
     floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv4[ds]), qf[ds], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv4[gi][ds]), qf[ds], acc, 0, 0, 0);
     sc[gi] = acc;
   }
+  // V^T: dim 16 db + c16, keys j0 + 32 c + 8 qd .. + 7 (cap is a multiple of
+  // 64, so the clamped start stays 16-byte aligned; a clamped piece lies
+  // wholly past the last key and is zeroed below)
+  uint4 vv[4][8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int ka = min(j0 + 32 * c + 8 * qd, cap - 8);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) vv[c][db] = *(const uint4*)(vb + (int64_t)(16 * db + c16) * cap + ka);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   float m = -INFINITY;
 #pragma unroll
   for (int gi = 0; gi < 8; ++gi)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float v = (j0 + 16 * gi + 4 * qd + i < nk) ? sc[gi][i] * scale_log2 : -INFINITY;
+      const int key = j0 + 32 * (gi >> 1) + 8 * qd + 4 * (gi & 1) + i;
+      const float v = key < nk ? sc[gi][i] * scale_log2 : -INFINITY;
       sc[gi][i] = v;
       m = fmaxf(m, v);
     }
@@ -432,22 +455,14 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16_t* __
   for (int db = 0; db < 8; ++db) o[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int k1 = j0 + 32 * c + 4 * qd, k2 = k1 + 16;
-    const int a1 = min(k1, cap - 4), a2 = min(k2, cap - 4);
-    uint2 vv[8][2];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const bf16_t* vr = vb + (int64_t)(16 * db + c16) * cap;
-      vv[db][0] = *(const uint2*)(vr + a1);
-      vv[db][1] = *(const uint2*)(vr + a2);
-    }
+    const int k0 = j0 + 32 * c + 8 * qd;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       uint4 u;
-      u.x = keep_keys(vv[db][0].x, k1, nk);
-      u.y = keep_keys(vv[db][0].y, k1 + 2, nk);
-      u.z = keep_keys(vv[db][1].x, k2, nk);
-      u.w = keep_keys(vv[db][1].y, k2 + 2, nk);
+      u.x = keep_keys(vv[c][db].x, k0, nk);
+      u.y = keep_keys(vv[c][db].y, k0 + 2, nk);
+      u.z = keep_keys(vv[c][db].z, k0 + 4, nk);
+      u.w = keep_keys(vv[c][db].w, k0 + 6, nk);
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[c], __builtin_bit_cast(bf16x8_t, u), o[db], 0, 0, 0);
     }
   }
