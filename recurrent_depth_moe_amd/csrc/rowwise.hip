@@ -1113,9 +1113,8 @@ static void launch_tail_rows(const TailArgs& a, int nj, hipStream_t s) {
   }
 }
 
-template <int NJ>
+template <int NJ, int R>
 static bool launch_tail_fast_nj(const TailArgs& a, int ns, hipStream_t s) {
-  constexpr int R = 4;
   const int grid = a.N / R;
   switch (ns) {
     case 1: loop_tail_fast_kernel<R, NJ, 1><<<grid, RB, 0, s>>>(a); return true;
@@ -1128,17 +1127,29 @@ static bool launch_tail_fast_nj(const TailArgs& a, int ns, hipStream_t s) {
 
 void launch_loop_tail(const TailArgs& a, hipStream_t s) {
   // batched form: bf16 LoRA, whole float4 columns per thread (D a multiple
-  // of 4 RB, at most 4 of them), 4-row blocks, k + S <= 4, rank a multiple
-  // of 4 up to 16
-  if (a.w_bf16 && a.N % 4 == 0 && a.D % (4 * RB) == 0 && a.D <= 16 * RB && a.r % 4 == 0 && a.r <= 16 &&
+  // of 4 RB, at most 4 of them), 4-row blocks (1-row ones below 1024 rows),
+  // k + S <= 4, rank a multiple of 4 up to 16
+  if (a.w_bf16 && (a.N % 4 == 0 || a.N < 1024) && a.D % (4 * RB) == 0 && a.D <= 16 * RB && a.r % 4 == 0 && a.r <= 16 &&
       a.r > 0) {
     const int ns = a.k + a.S;
     bool ok = false;
-    switch (a.D / (4 * RB)) {
-      case 1: ok = launch_tail_fast_nj<1>(a, ns, s); break;
-      case 2: ok = launch_tail_fast_nj<2>(a, ns, s); break;
-      case 3: ok = launch_tail_fast_nj<3>(a, ns, s); break;
-      default: ok = launch_tail_fast_nj<4>(a, ns, s); break;
+    // one row per block when four-row blocks would leave most CUs idle
+    // (single-token steps): the LoRA weights are re-read per row from L2,
+    // but the block count, not bandwidth, sets the time there
+    if (a.N < 1024) {
+      switch (a.D / (4 * RB)) {
+        case 1: ok = launch_tail_fast_nj<1, 1>(a, ns, s); break;
+        case 2: ok = launch_tail_fast_nj<2, 1>(a, ns, s); break;
+        case 3: ok = launch_tail_fast_nj<3, 1>(a, ns, s); break;
+        default: ok = launch_tail_fast_nj<4, 1>(a, ns, s); break;
+      }
+    } else {
+      switch (a.D / (4 * RB)) {
+        case 1: ok = launch_tail_fast_nj<1, 4>(a, ns, s); break;
+        case 2: ok = launch_tail_fast_nj<2, 4>(a, ns, s); break;
+        case 3: ok = launch_tail_fast_nj<3, 4>(a, ns, s); break;
+        default: ok = launch_tail_fast_nj<4, 4>(a, ns, s); break;
+      }
     }
     if (ok) return;
   }
