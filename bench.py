@@ -46,6 +46,7 @@ def stage_work(cfg, touched=None):
                             cfg["expert_dim"], cfg["top_k"], cfg["n_shared_experts"])
     sp = cfg["start_pos"]
     NK = N * k
+    es = 2.0 if cfg["dtype"] == "bf16" else 4.0   # stored width of matrix-product outputs
     Et = E if touched is None else touched
     w = {}
     w["qkv"] = dict(flops=2.0 * N * D * (H + 2 * G) * dh)
@@ -53,13 +54,13 @@ def stage_work(cfg, touched=None):
     w["o_proj"] = dict(flops=2.0 * N * D * H * dh)
     w["router"] = dict(flops=2.0 * N * D * E)
     w["expert_gate_up"] = dict(flops=2.0 * NK * 2 * F * D, bytes=2.0 * Et * 2 * F * D + 2.0 * NK * D + 2.0 * NK * F)
-    w["expert_down"] = dict(flops=2.0 * NK * F * D, bytes=2.0 * Et * F * D + 2.0 * NK * F + 4.0 * NK * D)
+    w["expert_down"] = dict(flops=2.0 * NK * F * D, bytes=2.0 * Et * F * D + 2.0 * NK * F + es * NK * D)
     w["shared_gate_up"] = dict(flops=2.0 * N * 2 * F * D * S)
     w["shared_down"] = dict(flops=2.0 * N * F * D * S)
     # row-wise kernels: each tensor read / written once at its stored width
     w["loop_head"] = dict(bytes=N * D * (4 + 4 + 4 + 2))             # h, e in; c fp32, a bf16 out
     w["ffn_norm"] = dict(bytes=N * D * (4 + 2))                       # x1 in, f out
-    w["tail"] = dict(bytes=N * D * (4 + 4 * k + 4 * S + 4 + 4 + 4 + 4))   # x1, y (k rows), y_s, h, e in; h, h_out
+    w["tail"] = dict(bytes=N * D * (4 + es * k + es * S + 4 + 4 + 4 + 4))   # x1, y (k rows), y_s, h, e in; h, h_out
     return w
 
 

@@ -190,7 +190,9 @@ rdt_status rdt_set_capture(rdt_block* blk, float* h_loops, int32_t* sel_loops, f
  * "cq_raw", "cq_norm", "lat_ckv", "lat_krope", "ckv_norm", plus for MLA
  * decode steps (T = 1, attention over the latent with absorbed
  * up-projections) "q_lat", "k_lat", "vt_lat", "o_lat" (0 bytes otherwise).
- * INVALID_ARG for other names. */
+ * Matrix-product inputs and outputs ("a", "f", "q", "k", "vt", "o", "act",
+ * "act_s", "y", "y_s") are stored in the weight dtype; "c", "x1", "logits",
+ * "gate", "h", "cum" are fp32.  INVALID_ARG for other names. */
 rdt_status rdt_workspace_offset(const rdt_block* blk, int32_t B, int32_t T, const char* name,
                                 size_t* offset, size_t* bytes);
 

@@ -58,8 +58,8 @@ struct GemmParams {
 // Launch helpers (stream-ordered, no sync).
 // 256x256 tiles, direct-to-LDS loads; K must be a multiple of 64 and a
 // grouped schedule must be built with m-tile height RDT_BM_BIG
-// bn = 256, or 192 for dense fp32-output products (EPI_STORE, EPI_RESID)
-// whose 256-wide tiles would leave part of the last round of CUs idle
+// bn = 256, or 192 for single-B products (EPI_STORE, EPI_RESID) whose
+// 256-wide tiles would leave part of the last round of CUs idle
 void launch_gemm_bf16_big(const GemmParams& p, int epi, bool dual, int out_is_bf16, int n_cu, hipStream_t s,
                           int bn = 256);
 // at most 32 rows per m-tile (grouped schedules built with RDT_BM_SKINNY),

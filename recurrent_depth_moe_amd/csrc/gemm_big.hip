@@ -536,8 +536,9 @@ void launch_gemm_bf16_big(const GemmParams& p, int epi, bool dual, int out_is_bf
     else launch_big<true, EPI_SWIGLU, float>(p, n_cu, s);
     return;
   }
-  if (bn == 192 && ((epi == EPI_STORE && !out_is_bf16) || epi == EPI_RESID)) {
+  if (bn == 192 && (epi == EPI_STORE || epi == EPI_RESID)) {
     if (epi == EPI_RESID) launch_big<false, EPI_RESID, float, 3>(p, n_cu, s);
+    else if (out_is_bf16) launch_big<false, EPI_STORE, bf16_t, 3>(p, n_cu, s);
     else launch_big<false, EPI_STORE, float, 3>(p, n_cu, s);
     return;
   }

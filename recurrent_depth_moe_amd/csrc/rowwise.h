@@ -35,10 +35,10 @@ void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* 
 
 struct TailArgs {
   const float* x1;        // [N][D]
-  const float* y;         // routed expert outputs in dispatch order [NK][D]
+  const void* y;          // routed expert outputs in dispatch order [NK][D], weight dtype
   const int32_t* inv;     // [N*k] slot -> dispatch row
   const float* gate;      // [N*k]
-  const float* y_s;       // shared expert outputs [S][N][D]
+  const void* y_s;        // shared expert outputs [S][N][D], weight dtype
   int S;
   const void* lora_down;  // [r][D] weight dtype
   const void* lora_B;     // [r][D]

@@ -432,9 +432,9 @@ __global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
     if (i4 < D4) {
       const int d = i4 * 4;
       float4 x = ld4(a.x1 + base + d);
-      for (int s = 0; s < a.k; ++s) x = fma4(gw[s], ld4(a.y + (int64_t)drow[s] * D + d), x);
+      for (int s = 0; s < a.k; ++s) x = fma4(gw[s], ld4((const TW*)a.y + (int64_t)drow[s] * D + d), x);
       for (int s = 0; s < a.S; ++s) {
-        const float4 ys = ld4(a.y_s + (int64_t)s * a.N * D + base + d);
+        const float4 ys = ld4((const TW*)a.y_s + (int64_t)s * a.N * D + base + d);
         x.x += ys.x; x.y += ys.y; x.z += ys.z; x.w += ys.w;
       }
       tau[j] = x;
@@ -559,9 +559,9 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
         float4 x = ld4(a.x1 + (int64_t)n * D + d);
 #pragma unroll
         for (int s = 0; s < 8; ++s)
-          if (s < a.k) x = fma4(gw[s], ld4(a.y + (int64_t)drow[s] * D + d), x);
+          if (s < a.k) x = fma4(gw[s], ld4((const TW*)a.y + (int64_t)drow[s] * D + d), x);
         for (int s = 0; s < a.S; ++s) {
-          const float4 ys = ld4(a.y_s + ((int64_t)s * a.N + n) * D + d);
+          const float4 ys = ld4((const TW*)a.y_s + ((int64_t)s * a.N + n) * D + d);
           x.x += ys.x; x.y += ys.y; x.z += ys.z; x.w += ys.w;
         }
         tau[i][j] = x;
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
   const bf16_t* Wd = (const bf16_t*)a.lora_down;
   const bf16_t* Wb = (const bf16_t*)a.lora_B;
   // source rows: the k routed slots (gate-weighted), then the S shared experts
-  const float* src[R][NS];
+  const bf16_t* src[R][NS];
   float wt[R][NS];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
@@ -727,10 +727,10 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
       if (q < k) {
-        src[i][q] = a.y + (int64_t)a.inv[(int64_t)n * k + q] * D;
+        src[i][q] = (const bf16_t*)a.y + (int64_t)a.inv[(int64_t)n * k + q] * D;
         wt[i][q] = a.gate[(int64_t)n * k + q];
       } else {
-        src[i][q] = a.y_s + ((int64_t)(q - k) * a.N + n) * D;
+        src[i][q] = (const bf16_t*)a.y_s + ((int64_t)(q - k) * a.N + n) * D;
         wt[i][q] = 1.f;
       }
     }

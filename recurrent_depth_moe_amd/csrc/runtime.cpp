@@ -164,9 +164,9 @@ Plan make_plan(const rdt_config& c, int B, int T) {
   s[WS_PERM] = NK * 4;
   s[WS_INV] = NK * 4;
   s[WS_ACT] = NK * F * es;
-  s[WS_Y] = NK * D * 4;
+  s[WS_Y] = NK * D * es;
   s[WS_ACTS] = N * F * es;
-  s[WS_YS] = (size_t)c.n_shared_experts * N * D * 4;
+  s[WS_YS] = (size_t)c.n_shared_experts * N * D * es;
   s[WS_CUM] = N * 4;
   if (!is_gqa(c)) {
     const size_t ql = c.q_lora_rank, kvl = c.kv_lora_rank, rope = c.qk_rope_head_dim;
@@ -678,12 +678,11 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       // 192-column tiles where they fill the rounds of CUs markedly better
       // than 256-column ones (e.g. dense N = 3072 on 256 CUs)
       int bn = 256;
-      if (grouped && !dual && gp.N % 192 == 0 && epi == EPI_STORE && !out_bf16) {
+      if (grouped && !dual && gp.N % 192 == 0 && epi == EPI_STORE) {
         // routed down projection: its m-tile count is only known on the
         // device; a third more (narrower) tiles levels the rounds of CUs
         bn = 192;
-      } else if (!grouped && !dual && gp.N % 192 == 0 && !(epi == EPI_STORE && out_bf16) &&
-          (epi == EPI_STORE || epi == EPI_RESID)) {
+      } else if (!grouped && !dual && gp.N % 192 == 0 && (epi == EPI_STORE || epi == EPI_RESID)) {
         const int mt = (gp.M + 255) / 256;
         auto eff = [&](int tiles) {
           const int rounds = (tiles + b->n_cu - 1) / b->n_cu;
@@ -877,7 +876,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gd.epi.out = W(WS_Y);
       gd.epi.ldo = D;
       StageTimer st_(b, s, RDT_STAGE_EXPERT_DOWN);
-      gemm(gd, EPI_STORE, false, 0);
+      gemm(gd, EPI_STORE, false, bf);
     }
     // a13: shared experts on every row
     for (int si = 0; si < c.n_shared_experts; ++si) {
@@ -890,19 +889,19 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
         gemm(gp, EPI_SWIGLU, true, bf);
       }
       GemmParams gd = dense(W(WS_ACTS), F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, N, D, F);
-      gd.epi.out = WF(WS_YS) + (size_t)si * N * D;
+      gd.epi.out = (char*)W(WS_YS) + (size_t)si * N * D * es;
       gd.epi.ldo = D;
       StageTimer st_(b, s, RDT_STAGE_SHARED_DOWN);
-      gemm(gd, EPI_STORE, false, 0);
+      gemm(gd, EPI_STORE, false, bf);
     }
     // a14-a17: combine, depth-wise LoRA, LTI injection, ACT
     {
       TailArgs ta{};
       ta.x1 = WF(WS_X1);
-      ta.y = WF(WS_Y);
+      ta.y = W(WS_Y);
       ta.inv = WI(WS_INV);
       ta.gate = WF(WS_GATE);
-      ta.y_s = WF(WS_YS);
+      ta.y_s = W(WS_YS);
       ta.S = c.n_shared_experts;
       ta.lora_down = b->lora_down;
       ta.lora_B = b->lora_B;

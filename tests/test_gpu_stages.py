@@ -142,7 +142,7 @@ def test_stage_experts(stage_run):
     perm = _get(run, cfg, "perm", (N * k,), "i32")
     inv = _get(run, cfg, "inv", (N * k,), "i32")
     act = _get(run, cfg, "act", (N * k, F))
-    y = _get(run, cfg, "y", (N * k, D), "f32")
+    y = _get(run, cfg, "y", (N * k, D))
     for a in range(N * k):
         assert perm[inv[a]] == a // k
     # per dispatch row: expert of the slot, token row
@@ -159,13 +159,23 @@ def test_stage_experts(stage_run):
     for ex in np.unique(ex_of_row):
         rows = np.nonzero(ex_of_row == ex)[0]
         ref_y[rows] = act[rows] @ P.expert("w_down", ex).T
-    assert _max_rel(y, ref_y) < 1e-5
+    # y is stored in the activation dtype (bf16 configs: its own rounding)
+    if cfg["dtype"] == "bf16":
+        nbad, where = _elem_bf16_ok(y, ref_y, abs_=1e-4)
+        assert nbad == 0, where
+    else:
+        assert _max_rel(y, ref_y) < 1e-5
     acts = _get(run, cfg, "act_s", (N, F))
-    ys = _get(run, cfg, "y_s", (S, N, D), "f32")
+    ys = _get(run, cfg, "y_s", (S, N, D))
     ref_as = O.silu(f @ P.expert("s_gate", S - 1).T) * (f @ P.expert("s_up", S - 1).T)
     nbad, where = _elem_bf16_ok(acts, ref_as, abs_=1e-4)
     assert nbad == 0, where
-    assert _max_rel(ys[S - 1], acts @ P.expert("s_down", S - 1).T) < 1e-5
+    ref_ys = acts @ P.expert("s_down", S - 1).T
+    if cfg["dtype"] == "bf16":
+        nbad, where = _elem_bf16_ok(ys[S - 1], ref_ys, abs_=1e-4)
+        assert nbad == 0, where
+    else:
+        assert _max_rel(ys[S - 1], ref_ys) < 1e-5
 
 
 def test_stage_tail(stage_run):
@@ -174,8 +184,8 @@ def test_stage_tail(stage_run):
     B, T, D = e.shape
     N, k, S = B * T, cfg["top_k"], cfg["n_shared_experts"]
     x1 = _get(run, cfg, "x1", (N, D), "f32")
-    y = _get(run, cfg, "y", (N * k, D), "f32")
-    ys = _get(run, cfg, "y_s", (S, N, D), "f32")
+    y = _get(run, cfg, "y", (N * k, D))
+    ys = _get(run, cfg, "y_s", (S, N, D))
     inv = _get(run, cfg, "inv", (N * k,), "i32")
     gate = _get(run, cfg, "gate", (N * k,), "f32")
     tau = x1 + (gate[:, None] * y[inv]).reshape(N, k, D).sum(1) + ys.sum(0)
