@@ -52,6 +52,10 @@ struct GemmParams {
   // big kernel, grouped products: RDT_NUM_XCD tile-claim counters, zero at
   // launch (null: static round-robin over each XCD's share of the tiles)
   int32_t* tile_ctr;
+  // big kernel, 192-column single-B grouped products: the schedule may give
+  // an m-tile up to this many rows beyond 256 (0 or 32, a merged schedule
+  // from the dispatch), computed as a 32-row strip of the same tile
+  int strip_rows;
   EpiParams epi;
 };
 

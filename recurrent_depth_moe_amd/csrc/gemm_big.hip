@@ -30,6 +30,8 @@
 // accumulators.
 #include "gemm_device.h"
 
+#include <type_traits>
+
 namespace {
 
 // Issue order of the first half of a stage: a fragment read of the second
@@ -134,7 +136,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the loads set the pace, so the smaller stages (A 8 or 16 KB + B 32 KB)
 // run in a deeper ring: 4 stages for 64 rows, 3 for 128.
 template <int SR, bool DUAL, int EPI, typename TO>
-__device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, const bf16_t* const (&asrc)[8],
+__device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, const bf16_t* const* asrc,
                                            const bf16_t* const (&bsrc)[8], int w, int lane, int rows, int row0,
                                            int n0, int KT) {
   constexpr int FM = SR / 32;                  // 32-row fragments
@@ -266,6 +268,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
   constexpr int WTM = 128, WTN = 32 * WNF;
   constexpr int A_CH = BM * (BK / 8), B_CH = BN * (BK / 8);   // 16-byte chunks per stage
   constexpr int A_IT = A_CH / 256, B_IT = B_CH / 256;
+  // 192-column single-B tiles also take a strip of up to 32 rows past the
+  // 256 (the remainder of a routed expert's rows in a merged schedule): its
+  // A rows follow the tile's in each A stage, and it reuses the B fragments
+  // the waves already hold, so the expert's weights stream once
+  constexpr bool HAS_STRIP = WNF == 3 && !DUAL;
+  constexpr int SROWS = HAS_STRIP ? 32 : 0;
+  constexpr int A_CHS = (BM + SROWS) * (BK / 8), A_ITS = A_CHS / 256;   // A stage stride / loads with the strip
+  static_assert((2 * A_CHS + 3 * B_CH) * 16 <= LDS_BYTES, "stages fit in LDS");
   constexpr int NCOL = DUAL ? BN / 2 : BN;       // output columns per tile
   extern __shared__ uint4 smem[];
 
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
   for (int L = next_tile(-1); L >= 0; L = next_tile(L)) {
     int mt, nt, row0, rows, grp;
     tile_coords(p, L, ntn, n_mt, mt, nt);
-    tile_rows(p, mt, BM, row0, rows, grp);
+    tile_rows(p, mt, BM, row0, rows, grp, HAS_STRIP ? p.strip_rows : 0);
     const int n0 = nt * NCOL;
     const bf16_t* W0 = (const bf16_t*)p.W0 + (int64_t)grp * p.w_stride;
     const bf16_t* W1 = DUAL ? (const bf16_t*)p.W1 + (int64_t)grp * p.w_stride : W0;
@@ -326,9 +336,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     // source pointers of this thread's chunks (k offset added per stage):
     // LDS slot s = (j*4 + w)*64 + lane holds row s/8, logical chunk
     // (s%8) ^ ((row >> 1) & 7)
-    const bf16_t* asrc[A_IT];
+    const bf16_t* asrc[A_ITS];
 #pragma unroll
-    for (int j = 0; j < A_IT; ++j) {
+    for (int j = 0; j < A_ITS; ++j) {
       const int s = (j * 4 + w) * 64 + lane, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
       const int m = row0 + (r < rows ? r : 0);
       const int arow = p.a_rows ? p.a_rows[m] : m;
@@ -356,10 +366,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     // expert's weights stream from HBM, so they are requested one stage
     // earlier)
     uint4* const sAbuf = smem;
-    uint4* const sBbuf = smem + 2 * A_CH;
-    auto issueA = [&](int buf, int k0) {
+    uint4* const sBbuf = smem + 2 * A_CHS;
+    auto issueA = [&](int buf, int k0, auto strip_c) {
+      constexpr int n = decltype(strip_c)::value ? A_ITS : A_IT;
 #pragma unroll
-      for (int j = 0; j < A_IT; ++j) g2lds(asrc[j] + k0, sAbuf + buf * A_CH + (j * 4 + w) * 64);
+      for (int j = 0; j < n; ++j) g2lds(asrc[j] + k0, sAbuf + buf * A_CHS + (j * 4 + w) * 64);
     };
     auto issueB = [&](int buf, int k0) {
 #pragma unroll
@@ -377,6 +388,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       }
     }
 
+    auto full_tile = [&](auto strip_c) {
+    constexpr bool S = decltype(strip_c)::value;
+    constexpr int NMS = S ? 4 : 0, NDS = S ? 2 : 0;   // strip MFMAs / fragment reads per half stage
     floatx16_t acc[4][WNF];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -384,29 +398,56 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       for (int j = 0; j < WNF; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    // strip: 32 rows x this wave's B fragments 0 and 1 (wm = 0) or 2 (wm =
+    // 1; its second accumulator repeats fragment 2 and is never stored, so
+    // every wave issues the same MFMAs)
+    floatx16_t accs[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) accs[j][e] = 0.f;
+    auto read_strip = [&](const uint4* sA, int hh, bf16x8_t (&fs)[2]) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int c = 4 * hh + 2 * x + (lane >> 5), r = BM + (lane & 31);
+        fs[x] = __builtin_bit_cast(bf16x8_t, sA[r * 8 + (c ^ ((r >> 1) & 7))]);
+      }
+    };
+    auto strip_mfma = [&](const bf16x8_t (&fs)[2], const bf16x8_t (&fb)[2 * WNF]) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const bf16x8_t b0 = wm ? fb[x * WNF + 2] : fb[x * WNF + 0];
+        const bf16x8_t b1 = wm ? fb[x * WNF + 2] : fb[x * WNF + 1];
+        accs[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[x], b0, accs[0], 0, 0, 0);
+        accs[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[x], b1, accs[1], 0, 0, 0);
+      }
+    };
     // 32-row fragments of this wave that hold at least one valid row
     const int fm_valid = max(0, min(4, (rows - wm * WTM + 31) / 32));
 
     // prologue: A stages 0, 1 and B stages 0, 1, 2 in flight, first half
     // of stage 0 read (past the end of K, loads repeat the last stage into
     // a buffer nobody reads)
-    issueA(0, 0);
+    issueA(0, 0, strip_c);
     issueB(0, 0);
-    issueA(1, min(1, KT - 1) * BK);
+    issueA(1, min(1, KT - 1) * BK, strip_c);
     issueB(1, min(1, KT - 1) * BK);
     issueB(2, min(2, KT - 1) * BK);
-    bf16x8_t fa0[8], fb0[2 * WNF], fa1[8], fb1[2 * WNF];
-    wait_vmcnt<A_IT + 2 * B_IT>();
+    bf16x8_t fa0[8], fb0[2 * WNF], fa1[8], fb1[2 * WNF], fs0[2], fs1[2];
+    wait_vmcnt<(S ? A_ITS : A_IT) + 2 * B_IT>();
     __syncthreads();
     read_frags<WNF>(sAbuf, sBbuf, wm, wn, lane, 0, fa0, fb0);
+    if constexpr (S) read_strip(sAbuf, 0, fs0);
     int b3 = 0;   // kt % 3
     for (int kt = 0; kt < KT; ++kt) {
       const int b3n = b3 == 2 ? 0 : b3 + 1;
       {
         // first half of stage kt (registers fa0/fb0); read its second half
-        read_frags<WNF>(sAbuf + (kt & 1) * A_CH, sBbuf + b3 * B_CH, wm, wn, lane, 1, fa1, fb1);
+        read_frags<WNF>(sAbuf + (kt & 1) * A_CHS, sBbuf + b3 * B_CH, wm, wn, lane, 1, fa1, fb1);
+        if constexpr (S) read_strip(sAbuf + (kt & 1) * A_CHS, 1, fs1);
         mfma_stage<WNF>(fa0, fb0, acc);
-        interleave_first_half<8 * WNF, 8 + 2 * WNF>();
+        if constexpr (S) strip_mfma(fs0, fb0);
+        interleave_first_half<8 * WNF + NMS, 8 + 2 * WNF + NDS>();
         __builtin_amdgcn_sched_barrier(0);
       }
       {
@@ -418,11 +459,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        issueA(kt & 1, min(kt + 2, KT - 1) * BK);
+        issueA(kt & 1, min(kt + 2, KT - 1) * BK, strip_c);
         issueB(b3, min(kt + 3, KT - 1) * BK);
-        read_frags<WNF>(sAbuf + ((kt + 1) & 1) * A_CH, sBbuf + b3n * B_CH, wm, wn, lane, 0, fa0, fb0);
+        read_frags<WNF>(sAbuf + ((kt + 1) & 1) * A_CHS, sBbuf + b3n * B_CH, wm, wn, lane, 0, fa0, fb0);
+        if constexpr (S) read_strip(sAbuf + ((kt + 1) & 1) * A_CHS, 0, fs0);
         mfma_stage<WNF>(fa1, fb1, acc);
-        interleave_second_half<8 * WNF, 8 + 2 * WNF, A_IT + B_IT>();
+        if constexpr (S) strip_mfma(fs1, fb1);
+        interleave_second_half<8 * WNF + NMS, 8 + 2 * WNF + NDS, (S ? A_ITS : A_IT) + B_IT>();
         __builtin_amdgcn_sched_barrier(0);
       }
       b3 = b3n;
@@ -507,6 +550,37 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
           __builtin_amdgcn_wave_barrier();
         }
       }
+      if constexpr (S) {
+        // strip rows 256 .. rows-1: 32 x 64 (wm = 0) or 32 x 32 (wm = 1) columns
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = accs[j][e];
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        const int cg = wm ? 4 : 8, ncol0 = n0 + wn * WTN + (wm ? 64 : 0);
+#pragma unroll 1
+        for (int it = 0; it < 4; ++it) {
+          const int idx = it * 64 + lane, rl = idx / cg, c8 = (idx - rl * cg) * 8;
+          const int ml = BM + rl;
+          if (rl < 32 && ml < rows) {
+            float v[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
+            epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, ncol0 + c8, v, v);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    };
+    if constexpr (HAS_STRIP) {
+      if (rows > BM) full_tile(std::true_type{});
+      else full_tile(std::false_type{});
+    } else {
+      full_tile(std::false_type{});
     }
     __syncthreads();   // the next tile's loads reuse this LDS
   }

@@ -78,11 +78,15 @@ static __device__ __forceinline__ void tile_coords(const GemmParams& p, int L, i
   }
 }
 
-static __device__ __forceinline__ void tile_rows(const GemmParams& p, int mt, int bm, int& row0, int& rows, int& grp) {
+static __device__ __forceinline__ void tile_rows(const GemmParams& p, int mt, int bm, int& row0, int& rows, int& grp,
+                                                 int extra = 0) {
   if (p.mt_start) {
     grp = p.tile_grp[mt];
     row0 = p.tile_row0[mt];
-    rows = min(bm, p.grp_end[grp + 1] - row0);
+    // a merged schedule gives a group's last m-tile up to `extra` more rows;
+    // every other m-tile of it has bm rows
+    const int left = p.grp_end[grp + 1] - row0;
+    rows = left <= bm + extra ? left : bm;
   } else {
     grp = 0;
     row0 = mt * bm;

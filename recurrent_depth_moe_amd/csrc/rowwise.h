@@ -28,10 +28,15 @@ void launch_router_topk(const float* logits, const float* bias, int N, int E, in
                         int32_t* cap_sel, hipStream_t s, const int32_t* live = nullptr);
 // dropless dispatch: stable order (token, slot) inside each expert
 // (also zeroes the n_claim tile-claim counters the grouped products of the
-// same loop draw from, n_claim <= RDT_MAX_EXPERTS)
+// same loop draw from, n_claim <= RDT_MAX_EXPERTS).  With merge_extra > 0 a
+// second m-tile schedule (mt_start_m, tile_row0_m, tile_grp_m) is built in
+// which an expert's last m-tile also takes a remainder of at most
+// merge_extra rows instead of leaving it to a tile of its own.
 void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,
                      int32_t* mt_start, int32_t* tile_row0, int32_t* tile_grp, int32_t* perm_src, int32_t* inv,
-                     int32_t* tile_claim, int n_claim, hipStream_t s, const int32_t* live = nullptr);
+                     int32_t* tile_claim, int n_claim, hipStream_t s, const int32_t* live = nullptr,
+                     int merge_extra = 0, int32_t* mt_start_m = nullptr, int32_t* tile_row0_m = nullptr,
+                     int32_t* tile_grp_m = nullptr);
 
 struct TailArgs {
   const float* x1;        // [N][D]

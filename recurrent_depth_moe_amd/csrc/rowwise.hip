@@ -286,10 +286,14 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
                                                                         int32_t* __restrict__ tile_row0,
                                                                         int32_t* __restrict__ tile_grp,
                                                                         int32_t* __restrict__ tile_claim,
-                                                                        int n_claim, const int32_t* live) {
+                                                                        int n_claim, int merge_extra,
+                                                                        int32_t* __restrict__ mt_start_m,
+                                                                        int32_t* __restrict__ tile_row0_m,
+                                                                        int32_t* __restrict__ tile_grp_m,
+                                                                        const int32_t* live) {
   RDT_SKIP_IF_ALL_HALTED(live);
   if ((int)threadIdx.x < n_claim) tile_claim[threadIdx.x] = 0;
-  __shared__ int wsum[RDT_MAX_EXPERTS / 64][2];
+  __shared__ int wsum[RDT_MAX_EXPERTS / 64][3];
   const int ex = threadIdx.x, lane = ex & 63, wv = ex >> 6;
   const bool own = ex < E;
   // exclusive scan down the tiles; with at most RDT_SCAN_BATCH tiles every
@@ -321,29 +325,36 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
     }
   }
   // exclusive scans over experts of the row totals and of the m-tile counts
+  // (plain and merged schedule)
   const int tot = own ? run : 0, nmt = own ? (run + bm - 1) / bm : 0;
-  int it = tot, im = nmt;
+  const int rem = tot - (tot / bm) * bm;
+  const int nmm = (merge_extra > 0 && tot > bm && rem > 0 && rem <= merge_extra) ? tot / bm : nmt;
+  int it = tot, im = nmt, imm = nmm;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int a = __shfl_up(it, o, 64), b = __shfl_up(im, o, 64);
+    const int a = __shfl_up(it, o, 64), b = __shfl_up(im, o, 64), c = __shfl_up(imm, o, 64);
     if (lane >= o) {
       it += a;
       im += b;
+      imm += c;
     }
   }
   if (lane == 63) {
     wsum[wv][0] = it;
     wsum[wv][1] = im;
+    wsum[wv][2] = imm;
   }
   __syncthreads();
-  int off = it - tot, mts = im - nmt;
+  int off = it - tot, mts = im - nmt, mtm = imm - nmm;
   for (int w = 0; w < wv; ++w) {
     off += wsum[w][0];
     mts += wsum[w][1];
+    mtm += wsum[w][2];
   }
   if (ex <= E) {   // thread E writes the totals
     offsets[ex] = off;
     mt_start[ex] = mts;
+    if (merge_extra > 0) mt_start_m[ex] = mtm;
   }
   if (own) {
     if (one_batch) {
@@ -363,6 +374,12 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
     for (int i = 0; i < nmt; ++i) {
       tile_grp[mts + i] = ex;
       tile_row0[mts + i] = off + i * bm;
+    }
+    if (merge_extra > 0) {
+      for (int i = 0; i < nmm; ++i) {
+        tile_grp_m[mtm + i] = ex;
+        tile_row0_m[mtm + i] = off + i * bm;
+      }
     }
   }
 }
@@ -1093,11 +1110,14 @@ void launch_router_topk(const float* logits, const float* bias, int N, int E, in
 
 void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,
                      int32_t* mt_start, int32_t* tile_row0, int32_t* tile_grp, int32_t* perm_src, int32_t* inv,
-                     int32_t* tile_claim, int n_claim, hipStream_t s, const int32_t* live) {
+                     int32_t* tile_claim, int n_claim, hipStream_t s, const int32_t* live, int merge_extra,
+                     int32_t* mt_start_m, int32_t* tile_row0_m, int32_t* tile_grp_m) {
   const int ntiles = (NK + RDT_DISP_TILE - 1) / RDT_DISP_TILE;
   dispatch_count_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, E, tile_counts, live);
+  if (!(mt_start_m && tile_row0_m && tile_grp_m)) merge_extra = 0;
   dispatch_scan_kernel<<<1, RDT_MAX_EXPERTS, 0, s>>>(tile_counts, ntiles, E, bm, offsets, mt_start, tile_row0,
-                                                     tile_grp, tile_claim, n_claim, live);
+                                                     tile_grp, tile_claim, n_claim, merge_extra, mt_start_m,
+                                                     tile_row0_m, tile_grp_m, live);
   dispatch_scatter_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, k, E, tile_counts, perm_src, inv, live);
 }
 

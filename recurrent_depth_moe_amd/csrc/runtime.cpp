@@ -97,13 +97,22 @@ enum WsId {
   WS_H, WS_C, WS_A, WS_Q, WS_K, WS_VT, WS_O, WS_X1, WS_F, WS_LOGITS, WS_SEL, WS_GATE, WS_TILECNT, WS_OFFSETS,
   WS_MTSTART, WS_TROW0, WS_TGRP, WS_PERM, WS_INV, WS_ACT, WS_Y, WS_ACTS, WS_YS, WS_CUM,
   WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_DPART, WS_LIVE, WS_TCLAIM,
-  WS_QLAT, WS_KLAT, WS_VLAT, WS_OLAT, WS_COUNT
+  WS_QLAT, WS_KLAT, WS_VLAT, WS_OLAT, WS_MTSTART_M, WS_TROW0_M, WS_TGRP_M, WS_COUNT
 };
 const char* kWsNames[WS_COUNT] = {"h", "c", "a", "q", "k", "vt", "o", "x1", "f", "logits", "sel", "gate",
                                   "tile_counts", "offsets", "mt_start", "tile_row0", "tile_grp", "perm", "inv",
                                   "act", "y", "act_s", "y_s", "cum", "kv_raw", "cq_raw", "cq_norm", "lat_ckv",
                                   "lat_krope", "ckv_norm", "attn_part", "live",
-                                  "tile_claim", "q_lat", "k_lat", "vt_lat", "o_lat"};
+                                  "tile_claim", "q_lat", "k_lat", "vt_lat", "o_lat", "mt_start_merged",
+                                  "tile_row0_merged", "tile_grp_merged"};
+
+// Prefill with bf16 weights runs the routed down product on 192-column
+// tiles of the large kernel when dim is a multiple of 192; those tiles also
+// compute up to 32 rows past their 256, so that product uses a schedule in
+// which an expert's last m-tile absorbs a remainder of at most 32 rows.
+static bool merged_down_schedule(const rdt_config& c, int T) {
+  return c.weight_dtype == RDT_BF16 && T > 1 && c.dim % 192 == 0;
+}
 
 struct Plan {
   int B, T, N, NK, kvcap, kvlen_max, bm, max_mt, disp_tiles;
@@ -186,6 +195,11 @@ Plan make_plan(const rdt_config& c, int B, int T) {
   if (use_decode_attn(c, T)) s[WS_DPART] = attn_decode_part_floats(B, c.n_heads, p.kvlen_max) * 4;
   s[WS_LIVE] = 2 * 4;   // running-position counts of the previous and the current loop
   s[WS_TCLAIM] = 2 * RDT_NUM_XCD * 4;   // tile-claim counters of the two routed products
+  if (merged_down_schedule(c, T)) {       // m-tile schedule of the routed down product
+    s[WS_MTSTART_M] = (E + 1) * 4;
+    s[WS_TROW0_M] = (size_t)p.max_mt * 4;
+    s[WS_TGRP_M] = (size_t)p.max_mt * 4;
+  }
   size_t o = 0;
   for (int i = 0; i < WS_COUNT; ++i) {
     p.off[i] = o;
@@ -645,6 +659,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   auto WF = [&](int id) -> float* { return (float*)(w + p.off[id]); };
   auto WI = [&](int id) -> int32_t* { return (int32_t*)(w + p.off[id]); };
   const bool bf = c.weight_dtype == RDT_BF16;
+  const bool merged = merged_down_schedule(c, T);
   const int N = p.N, D = c.dim, E = c.n_experts, F = c.expert_dim, k = c.top_k, H = c.n_heads;
   const int G = kv_heads(c), dq = qk_dim(c), dv = v_dim(c);
   const size_t es = esize(c);
@@ -835,7 +850,8 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       StageTimer st_(b, s, RDT_STAGE_DISPATCH);
       launch_dispatch(WI(WS_SEL), p.NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART),
                       WI(WS_TROW0), WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), WI(WS_TCLAIM), 2 * RDT_NUM_XCD, s,
-                      live_prev);
+                      live_prev, merged ? 32 : 0, merged ? WI(WS_MTSTART_M) : nullptr,
+                      merged ? WI(WS_TROW0_M) : nullptr, merged ? WI(WS_TGRP_M) : nullptr);
     }
     // a11: routed gate|up + SwiGLU, rows gathered from f
     {
@@ -870,6 +886,12 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gd.W1 = nullptr;
       gd.w_stride = (int64_t)D * F;
       gd.tile_ctr = WI(WS_TCLAIM) + RDT_NUM_XCD;
+      if (merged) {
+        gd.mt_start = WI(WS_MTSTART_M);
+        gd.tile_row0 = WI(WS_TROW0_M);
+        gd.tile_grp = WI(WS_TGRP_M);
+        gd.strip_rows = 32;
+      }
       gd.N = D;
       gd.K = F;
       gd.epi = EpiParams{};

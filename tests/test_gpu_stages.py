@@ -33,7 +33,7 @@ def _elem_bf16_ok(got, ref, rel=2 ** -7, abs_=1e-6):
     return int(bad.sum()), np.argwhere(bad)[:5]
 
 
-@pytest.fixture(scope="module", params=["small_bf16", "small_bf16_k3", "small_f32"])
+@pytest.fixture(scope="module", params=["small_bf16", "small_bf16_k3", "small_f32", "small_bf16_strip"])
 def stage_run(request):
     name = request.param
     cfg = configs.get(name, n_loops=1, act_threshold=0.0)

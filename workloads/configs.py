@@ -116,6 +116,15 @@ CONFIGS = {
         lora_rank=4, max_loop_iters=2, max_seq_len=512,
         dtype="bf16", batch=3, seq=77, n_loops=3, act_threshold=0.0,
         seed=12),
+    # bf16, dim a multiple of 192 with ~270 routed rows per expert: the
+    # routed down product's 192-column tiles and merged m-tile schedule
+    # (experts 1-32 rows past 256 computed as a strip of the same tile)
+    "small_bf16_strip": _cfg(
+        dim=768, n_heads=6, n_kv_heads=2, attn="gqa",
+        n_experts=8, n_shared_experts=1, top_k=2, expert_dim=384,
+        lora_rank=8, max_loop_iters=4, max_seq_len=1088,
+        dtype="bf16", batch=2, seq=540, n_loops=2, act_threshold=0.0,
+        seed=15),
     # bf16 decode against a cache: 4 sequences, 1 token at position 300
     "small_bf16_decode": _cfg(
         dim=512, n_heads=4, n_kv_heads=2, attn="gqa",
