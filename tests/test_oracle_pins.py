@@ -353,8 +353,8 @@ BIG = {"lora_scale": 1.0, "lora_B": 0.3, "wo": 0.1, "w_down": 0.1, "s_down": 0.1
 @pytest.mark.parametrize("name", ["tiny_gqa", "tiny_mla", "small_f32", "small_bf16_k3"])
 def test_single_loop_matches_independent_torch_block(name):
     """n_loops = 1 equals one application of the block, written independently
-    with library routines (north star special case).  Larger LoRA / output
-    scales keep every term visible above the tolerance."""
+    with library routines (the single-loop special case).  Larger LoRA /
+    output scales keep every term visible above the tolerance."""
     cfg, W, P, e, h0 = _setup(name, scales=BIG)
     e64 = e.astype(np.float64)
     h = e64 * 0.7 + 0.1
