@@ -53,8 +53,8 @@ struct GemmParams {
   // launch (null: static round-robin over each XCD's share of the tiles)
   int32_t* tile_ctr;
   // big kernel, 192-column single-B grouped products: the schedule may give
-  // an m-tile up to this many rows beyond 256 (0 or 32, a merged schedule
-  // from the dispatch), computed as a 32-row strip of the same tile
+  // an m-tile up to this many rows beyond 256 (0 or 64, a merged schedule
+  // from the dispatch), computed as 32-row strips of the same tile
   int strip_rows;
   EpiParams epi;
 };

@@ -268,12 +268,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
   constexpr int WTM = 128, WTN = 32 * WNF;
   constexpr int A_CH = BM * (BK / 8), B_CH = BN * (BK / 8);   // 16-byte chunks per stage
   constexpr int A_IT = A_CH / 256, B_IT = B_CH / 256;
-  // 192-column single-B tiles also take a strip of up to 32 rows past the
-  // 256 (the remainder of a routed expert's rows in a merged schedule): its
-  // A rows follow the tile's in each A stage, and it reuses the B fragments
-  // the waves already hold, so the expert's weights stream once
+  // 192-column single-B tiles also take up to two 32-row strips past the
+  // 256 rows (the remainder of a routed expert's rows in a merged
+  // schedule): their A rows follow the tile's in each A stage, and they
+  // reuse the B fragments the waves already hold, so the expert's weights
+  // stream once
   constexpr bool HAS_STRIP = WNF == 3 && !DUAL;
-  constexpr int SROWS = HAS_STRIP ? 32 : 0;
+  constexpr int SROWS = HAS_STRIP ? 64 : 0;
   constexpr int A_CHS = (BM + SROWS) * (BK / 8), A_ITS = A_CHS / 256;   // A stage stride / loads with the strip
   static_assert((2 * A_CHS + 3 * B_CH) * 16 <= LDS_BYTES, "stages fit in LDS");
   constexpr int NCOL = DUAL ? BN / 2 : BN;       // output columns per tile
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     uint4* const sAbuf = smem;
     uint4* const sBbuf = smem + 2 * A_CHS;
     auto issueA = [&](int buf, int k0, auto strip_c) {
-      constexpr int n = decltype(strip_c)::value ? A_ITS : A_IT;
+      constexpr int n = A_IT + decltype(strip_c)::value;   // one load per thread and 32-row strip
 #pragma unroll
       for (int j = 0; j < n; ++j) g2lds(asrc[j] + k0, sAbuf + buf * A_CHS + (j * 4 + w) * 64);
     };
@@ -389,8 +390,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     }
 
     auto full_tile = [&](auto strip_c) {
-    constexpr bool S = decltype(strip_c)::value;
-    constexpr int NMS = S ? 4 : 0, NDS = S ? 2 : 0;   // strip MFMAs / fragment reads per half stage
+    constexpr int NSTR = decltype(strip_c)::value;   // 32-row strips (0, 1, 2)
+    constexpr bool S = NSTR > 0;
+    constexpr int NMS = 4 * NSTR, NDS = 2 * NSTR;   // strip MFMAs / fragment reads per half stage
+    constexpr int NSA = NSTR > 0 ? NSTR : 1;        // array extents
     floatx16_t acc[4][WNF];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -398,28 +401,35 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       for (int j = 0; j < WNF; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    // strip: 32 rows x this wave's B fragments 0 and 1 (wm = 0) or 2 (wm =
-    // 1; its second accumulator repeats fragment 2 and is never stored, so
-    // every wave issues the same MFMAs)
-    floatx16_t accs[2];
+    // strip st: 32 rows x this wave's B fragments 0 and 1 (wm = 0) or 2
+    // (wm = 1; its second accumulator repeats fragment 2 and is never
+    // stored, so every wave issues the same MFMAs)
+    floatx16_t accs[NSA][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int st = 0; st < NSA; ++st)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) accs[j][e] = 0.f;
-    auto read_strip = [&](const uint4* sA, int hh, bf16x8_t (&fs)[2]) {
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int c = 4 * hh + 2 * x + (lane >> 5), r = BM + (lane & 31);
-        fs[x] = __builtin_bit_cast(bf16x8_t, sA[r * 8 + (c ^ ((r >> 1) & 7))]);
-      }
+        for (int e = 0; e < 16; ++e) accs[st][j][e] = 0.f;
+    auto read_strip = [&](const uint4* sA, int hh, bf16x8_t (&fs)[NSA][2]) {
+#pragma unroll
+      for (int st = 0; st < NSTR; ++st)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int c = 4 * hh + 2 * x + (lane >> 5), r = BM + 32 * st + (lane & 31);
+          fs[st][x] = __builtin_bit_cast(bf16x8_t, sA[r * 8 + (c ^ ((r >> 1) & 7))]);
+        }
     };
-    auto strip_mfma = [&](const bf16x8_t (&fs)[2], const bf16x8_t (&fb)[2 * WNF]) {
+    auto strip_mfma = [&](const bf16x8_t (&fs)[NSA][2], const bf16x8_t (&fb)[2 * WNF]) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const bf16x8_t b0 = wm ? fb[x * WNF + 2] : fb[x * WNF + 0];
         const bf16x8_t b1 = wm ? fb[x * WNF + 2] : fb[x * WNF + 1];
-        accs[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[x], b0, accs[0], 0, 0, 0);
-        accs[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[x], b1, accs[1], 0, 0, 0);
+#pragma unroll
+        for (int st = 0; st < NSTR; ++st) {
+          accs[st][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[st][x], b0, accs[st][0], 0, 0, 0);
+          accs[st][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[st][x], b1, accs[st][1], 0, 0, 0);
+        }
       }
     };
     // 32-row fragments of this wave that hold at least one valid row
@@ -433,8 +443,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     issueA(1, min(1, KT - 1) * BK, strip_c);
     issueB(1, min(1, KT - 1) * BK);
     issueB(2, min(2, KT - 1) * BK);
-    bf16x8_t fa0[8], fb0[2 * WNF], fa1[8], fb1[2 * WNF], fs0[2], fs1[2];
-    wait_vmcnt<(S ? A_ITS : A_IT) + 2 * B_IT>();
+    bf16x8_t fa0[8], fb0[2 * WNF], fa1[8], fb1[2 * WNF], fs0[NSA][2], fs1[NSA][2];
+    wait_vmcnt<A_IT + NSTR + 2 * B_IT>();
     __syncthreads();
     read_frags<WNF>(sAbuf, sBbuf, wm, wn, lane, 0, fa0, fb0);
     if constexpr (S) read_strip(sAbuf, 0, fs0);
@@ -465,7 +475,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
         if constexpr (S) read_strip(sAbuf + ((kt + 1) & 1) * A_CHS, 0, fs0);
         mfma_stage<WNF>(fa1, fb1, acc);
         if constexpr (S) strip_mfma(fs1, fb1);
-        interleave_second_half<8 * WNF + NMS, 8 + 2 * WNF + NDS, (S ? A_ITS : A_IT) + B_IT>();
+        interleave_second_half<8 * WNF + NMS, 8 + 2 * WNF + NDS, A_IT + NSTR + B_IT>();
         __builtin_amdgcn_sched_barrier(0);
       }
       b3 = b3n;
@@ -551,36 +561,41 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
         }
       }
       if constexpr (S) {
-        // strip rows 256 .. rows-1: 32 x 64 (wm = 0) or 32 x 32 (wm = 1) columns
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = accs[j][e];
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
+        // strip rows 256 .. rows-1: per strip 32 x 64 (wm = 0) or 32 x 32
+        // (wm = 1) columns
         const int cg = wm ? 4 : 8, ncol0 = n0 + wn * WTN + (wm ? 64 : 0);
-#pragma unroll 1
-        for (int it = 0; it < 4; ++it) {
-          const int idx = it * 64 + lane, rl = idx / cg, c8 = (idx - rl * cg) * 8;
-          const int ml = BM + rl;
-          if (rl < 32 && ml < rows) {
-            float v[8];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
-            epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, ncol0 + c8, v, v);
+        for (int st = 0; st < NSTR; ++st) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = accs[st][j][e];
+          __builtin_amdgcn_s_waitcnt(0);
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+          for (int it = 0; it < 4; ++it) {
+            const int idx = it * 64 + lane, rl = idx / cg, c8 = (idx - rl * cg) * 8;
+            const int ml = BM + 32 * st + rl;
+            if (rl < 32 && ml < rows) {
+              float v[8];
+#pragma unroll
+              for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
+              epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, ncol0 + c8, v, v);
+            }
           }
+          __builtin_amdgcn_s_waitcnt(0);
+          __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
       }
     }
     };
     if constexpr (HAS_STRIP) {
-      if (rows > BM) full_tile(std::true_type{});
-      else full_tile(std::false_type{});
+      if (rows > BM + 32) full_tile(std::integral_constant<int, 2>{});
+      else if (rows > BM) full_tile(std::integral_constant<int, 1>{});
+      else full_tile(std::integral_constant<int, 0>{});
     } else {
-      full_tile(std::false_type{});
+      full_tile(std::integral_constant<int, 0>{});
     }
     __syncthreads();   // the next tile's loads reuse this LDS
   }

@@ -108,8 +108,8 @@ const char* kWsNames[WS_COUNT] = {"h", "c", "a", "q", "k", "vt", "o", "x1", "f",
 
 // Prefill with bf16 weights runs the routed down product on 192-column
 // tiles of the large kernel when dim is a multiple of 192; those tiles also
-// compute up to 32 rows past their 256, so that product uses a schedule in
-// which an expert's last m-tile absorbs a remainder of at most 32 rows.
+// compute up to 64 rows past their 256, so that product uses a schedule in
+// which an expert's last m-tile absorbs a remainder of at most 64 rows.
 static bool merged_down_schedule(const rdt_config& c, int T) {
   return c.weight_dtype == RDT_BF16 && T > 1 && c.dim % 192 == 0;
 }
@@ -850,7 +850,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       StageTimer st_(b, s, RDT_STAGE_DISPATCH);
       launch_dispatch(WI(WS_SEL), p.NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART),
                       WI(WS_TROW0), WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), WI(WS_TCLAIM), 2 * RDT_NUM_XCD, s,
-                      live_prev, merged ? 32 : 0, merged ? WI(WS_MTSTART_M) : nullptr,
+                      live_prev, merged ? 64 : 0, merged ? WI(WS_MTSTART_M) : nullptr,
                       merged ? WI(WS_TROW0_M) : nullptr, merged ? WI(WS_TGRP_M) : nullptr);
     }
     // a11: routed gate|up + SwiGLU, rows gathered from f
@@ -890,7 +890,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
         gd.mt_start = WI(WS_MTSTART_M);
         gd.tile_row0 = WI(WS_TROW0_M);
         gd.tile_grp = WI(WS_TGRP_M);
-        gd.strip_rows = 32;
+        gd.strip_rows = 64;
       }
       gd.N = D;
       gd.K = F;

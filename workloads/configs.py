@@ -118,7 +118,7 @@ CONFIGS = {
         seed=12),
     # bf16, dim a multiple of 192 with ~270 routed rows per expert: the
     # routed down product's 192-column tiles and merged m-tile schedule
-    # (experts 1-32 rows past 256 computed as a strip of the same tile)
+    # (experts 1-64 rows past 256 computed as strips of the same tile)
     "small_bf16_strip": _cfg(
         dim=768, n_heads=6, n_kv_heads=2, attn="gqa",
         n_experts=8, n_shared_experts=1, top_k=2, expert_dim=384,
