@@ -390,205 +390,205 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     }
 
     auto full_tile = [&](auto strip_c) {
-    constexpr int NSTR = decltype(strip_c)::value;   // 32-row strips (0, 1, 2)
-    constexpr bool S = NSTR > 0;
-    constexpr int NMS = 4 * NSTR, NDS = 2 * NSTR;   // strip MFMAs / fragment reads per half stage
-    constexpr int NSA = NSTR > 0 ? NSTR : 1;        // array extents
-    floatx16_t acc[4][WNF];
+      constexpr int NSTR = decltype(strip_c)::value;   // 32-row strips (0, 1, 2)
+      constexpr bool S = NSTR > 0;
+      constexpr int NMS = 4 * NSTR, NDS = 2 * NSTR;   // strip MFMAs / fragment reads per half stage
+      constexpr int NSA = NSTR > 0 ? NSTR : 1;        // array extents
+      floatx16_t acc[4][WNF];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < WNF; ++j)
+        for (int j = 0; j < WNF; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    // strip st: 32 rows x this wave's B fragments 0 and 1 (wm = 0) or 2
-    // (wm = 1; its second accumulator repeats fragment 2 and is never
-    // stored, so every wave issues the same MFMAs)
-    floatx16_t accs[NSA][2];
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      // strip st: 32 rows x this wave's B fragments 0 and 1 (wm = 0) or 2
+      // (wm = 1; its second accumulator repeats fragment 2 and is never
+      // stored, so every wave issues the same MFMAs)
+      floatx16_t accs[NSA][2];
 #pragma unroll
-    for (int st = 0; st < NSA; ++st)
+      for (int st = 0; st < NSA; ++st)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) accs[st][j][e] = 0.f;
-    auto read_strip = [&](const uint4* sA, int hh, bf16x8_t (&fs)[NSA][2]) {
+          for (int e = 0; e < 16; ++e) accs[st][j][e] = 0.f;
+      auto read_strip = [&](const uint4* sA, int hh, bf16x8_t (&fs)[NSA][2]) {
 #pragma unroll
-      for (int st = 0; st < NSTR; ++st)
+        for (int st = 0; st < NSTR; ++st)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int c = 4 * hh + 2 * x + (lane >> 5), r = BM + 32 * st + (lane & 31);
+            fs[st][x] = __builtin_bit_cast(bf16x8_t, sA[r * 8 + (c ^ ((r >> 1) & 7))]);
+          }
+      };
+      auto strip_mfma = [&](const bf16x8_t (&fs)[NSA][2], const bf16x8_t (&fb)[2 * WNF]) {
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-          const int c = 4 * hh + 2 * x + (lane >> 5), r = BM + 32 * st + (lane & 31);
-          fs[st][x] = __builtin_bit_cast(bf16x8_t, sA[r * 8 + (c ^ ((r >> 1) & 7))]);
+          const bf16x8_t b0 = wm ? fb[x * WNF + 2] : fb[x * WNF + 0];
+          const bf16x8_t b1 = wm ? fb[x * WNF + 2] : fb[x * WNF + 1];
+#pragma unroll
+          for (int st = 0; st < NSTR; ++st) {
+            accs[st][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[st][x], b0, accs[st][0], 0, 0, 0);
+            accs[st][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[st][x], b1, accs[st][1], 0, 0, 0);
+          }
         }
-    };
-    auto strip_mfma = [&](const bf16x8_t (&fs)[NSA][2], const bf16x8_t (&fb)[2 * WNF]) {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const bf16x8_t b0 = wm ? fb[x * WNF + 2] : fb[x * WNF + 0];
-        const bf16x8_t b1 = wm ? fb[x * WNF + 2] : fb[x * WNF + 1];
-#pragma unroll
-        for (int st = 0; st < NSTR; ++st) {
-          accs[st][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[st][x], b0, accs[st][0], 0, 0, 0);
-          accs[st][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[st][x], b1, accs[st][1], 0, 0, 0);
+      };
+      // 32-row fragments of this wave that hold at least one valid row
+      const int fm_valid = max(0, min(4, (rows - wm * WTM + 31) / 32));
+
+      // prologue: A stages 0, 1 and B stages 0, 1, 2 in flight, first half
+      // of stage 0 read (past the end of K, loads repeat the last stage into
+      // a buffer nobody reads)
+      issueA(0, 0, strip_c);
+      issueB(0, 0);
+      issueA(1, min(1, KT - 1) * BK, strip_c);
+      issueB(1, min(1, KT - 1) * BK);
+      issueB(2, min(2, KT - 1) * BK);
+      bf16x8_t fa0[8], fb0[2 * WNF], fa1[8], fb1[2 * WNF], fs0[NSA][2], fs1[NSA][2];
+      wait_vmcnt<A_IT + NSTR + 2 * B_IT>();
+      __syncthreads();
+      read_frags<WNF>(sAbuf, sBbuf, wm, wn, lane, 0, fa0, fb0);
+      if constexpr (S) read_strip(sAbuf, 0, fs0);
+      int b3 = 0;   // kt % 3
+      for (int kt = 0; kt < KT; ++kt) {
+        const int b3n = b3 == 2 ? 0 : b3 + 1;
+        {
+          // first half of stage kt (registers fa0/fb0); read its second half
+          read_frags<WNF>(sAbuf + (kt & 1) * A_CHS, sBbuf + b3 * B_CH, wm, wn, lane, 1, fa1, fb1);
+          if constexpr (S) read_strip(sAbuf + (kt & 1) * A_CHS, 1, fs1);
+          mfma_stage<WNF>(fa0, fb0, acc);
+          if constexpr (S) strip_mfma(fs0, fb0);
+          interleave_first_half<8 * WNF + NMS, 8 + 2 * WNF + NDS>();
+          __builtin_amdgcn_sched_barrier(0);
         }
+        {
+          // second half: stage kt+1 landed (only B of stage kt+2 may still be
+          // in flight) and every wave is done reading stage kt, so its
+          // buffers take A of stage kt+2 and B of stage kt+3; read stage
+          // kt+1's first half (past the end: unused)
+          wait_vmcnt<B_IT>();
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+          __syncthreads();
+          __builtin_amdgcn_sched_barrier(0);
+          issueA(kt & 1, min(kt + 2, KT - 1) * BK, strip_c);
+          issueB(b3, min(kt + 3, KT - 1) * BK);
+          read_frags<WNF>(sAbuf + ((kt + 1) & 1) * A_CHS, sBbuf + b3n * B_CH, wm, wn, lane, 0, fa0, fb0);
+          if constexpr (S) read_strip(sAbuf + ((kt + 1) & 1) * A_CHS, 0, fs0);
+          mfma_stage<WNF>(fa1, fb1, acc);
+          if constexpr (S) strip_mfma(fs1, fb1);
+          interleave_second_half<8 * WNF + NMS, 8 + 2 * WNF + NDS, A_IT + NSTR + B_IT>();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        b3 = b3n;
       }
-    };
-    // 32-row fragments of this wave that hold at least one valid row
-    const int fm_valid = max(0, min(4, (rows - wm * WTM + 31) / 32));
+      wait_vm(0);   // the trailing reloads land before the epilogue reuses LDS
+      __syncthreads();   // every wave done with the stages before the epilogue reuses LDS
 
-    // prologue: A stages 0, 1 and B stages 0, 1, 2 in flight, first half
-    // of stage 0 read (past the end of K, loads repeat the last stage into
-    // a buffer nobody reads)
-    issueA(0, 0, strip_c);
-    issueB(0, 0);
-    issueA(1, min(1, KT - 1) * BK, strip_c);
-    issueB(1, min(1, KT - 1) * BK);
-    issueB(2, min(2, KT - 1) * BK);
-    bf16x8_t fa0[8], fb0[2 * WNF], fa1[8], fb1[2 * WNF], fs0[NSA][2], fs1[NSA][2];
-    wait_vmcnt<A_IT + NSTR + 2 * B_IT>();
-    __syncthreads();
-    read_frags<WNF>(sAbuf, sBbuf, wm, wn, lane, 0, fa0, fb0);
-    if constexpr (S) read_strip(sAbuf, 0, fs0);
-    int b3 = 0;   // kt % 3
-    for (int kt = 0; kt < KT; ++kt) {
-      const int b3n = b3 == 2 ? 0 : b3 + 1;
+      // Epilogue through LDS, four passes of 32 rows per wave (one fragment
+      // row each): a 32x32 accumulator holds, in lane l and element e, row
+      // 8*(e/4) + 4*(l/32) + e%4 and column l%32.  The values go to a
+      // row-major 32 x 128 fp32 patch of the wave's own LDS region, then each
+      // lane takes 8 consecutive columns of one row, so stores are 16-byte
+      // vectors and RoPE pairs sit in one lane.
       {
-        // first half of stage kt (registers fa0/fb0); read its second half
-        read_frags<WNF>(sAbuf + (kt & 1) * A_CHS, sBbuf + b3 * B_CH, wm, wn, lane, 1, fa1, fb1);
-        if constexpr (S) read_strip(sAbuf + (kt & 1) * A_CHS, 1, fs1);
-        mfma_stage<WNF>(fa0, fb0, acc);
-        if constexpr (S) strip_mfma(fs0, fb0);
-        interleave_first_half<8 * WNF + NMS, 8 + 2 * WNF + NDS>();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      {
-        // second half: stage kt+1 landed (only B of stage kt+2 may still be
-        // in flight) and every wave is done reading stage kt, so its
-        // buffers take A of stage kt+2 and B of stage kt+3; read stage
-        // kt+1's first half (past the end: unused)
-        wait_vmcnt<B_IT>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        issueA(kt & 1, min(kt + 2, KT - 1) * BK, strip_c);
-        issueB(b3, min(kt + 3, KT - 1) * BK);
-        read_frags<WNF>(sAbuf + ((kt + 1) & 1) * A_CHS, sBbuf + b3n * B_CH, wm, wn, lane, 0, fa0, fb0);
-        if constexpr (S) read_strip(sAbuf + ((kt + 1) & 1) * A_CHS, 0, fs0);
-        mfma_stage<WNF>(fa1, fb1, acc);
-        if constexpr (S) strip_mfma(fs1, fb1);
-        interleave_second_half<8 * WNF + NMS, 8 + 2 * WNF + NDS, A_IT + NSTR + B_IT>();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      b3 = b3n;
-    }
-    wait_vm(0);   // the trailing reloads land before the epilogue reuses LDS
-    __syncthreads();   // every wave done with the stages before the epilogue reuses LDS
-
-    // Epilogue through LDS, four passes of 32 rows per wave (one fragment
-    // row each): a 32x32 accumulator holds, in lane l and element e, row
-    // 8*(e/4) + 4*(l/32) + e%4 and column l%32.  The values go to a
-    // row-major 32 x 128 fp32 patch of the wave's own LDS region, then each
-    // lane takes 8 consecutive columns of one row, so stores are 16-byte
-    // vectors and RoPE pairs sit in one lane.
-    {
-      float* ep = (float*)smem + w * (32 * EP_LD);
+        float* ep = (float*)smem + w * (32 * EP_LD);
 #pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        if (pass < fm_valid) {
+        for (int pass = 0; pass < 4; ++pass) {
+          if (pass < fm_valid) {
 #pragma unroll
-          for (int j = 0; j < WNF; ++j)
+            for (int j = 0; j < WNF; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = acc[pass][j][e];
-          __builtin_amdgcn_s_waitcnt(0);
-          __builtin_amdgcn_wave_barrier();
-          if constexpr (DUAL) {
-            // 64 output columns: gate at patch columns 0..63, up at 64..127
+              for (int e = 0; e < 16; ++e)
+                ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = acc[pass][j][e];
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+            if constexpr (DUAL) {
+              // 64 output columns: gate at patch columns 0..63, up at 64..127
 #pragma unroll 1
-            for (int it = 0; it < 4; ++it) {
-              const int rl = it * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-              const int ml = wm * WTM + pass * 32 + rl;
-              float g[8], u[8];
+              for (int it = 0; it < 4; ++it) {
+                const int rl = it * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+                const int ml = wm * WTM + pass * 32 + rl;
+                float g[8], u[8];
 #pragma unroll
-              for (int x = 0; x < 8; ++x) {
-                g[x] = ep[rl * EP_LD + c8 + x];
-                u[x] = ep[rl * EP_LD + 64 + c8 + x];
+                for (int x = 0; x < 8; ++x) {
+                  g[x] = ep[rl * EP_LD + c8 + x];
+                  u[x] = ep[rl * EP_LD + 64 + c8 + x];
+                }
+                if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + wn * 64 + c8, g, u);
               }
-              if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + wn * 64 + c8, g, u);
-            }
-          } else if (EPI == EPI_QKV && n0 + wn * WTN >= p.epi.H * p.epi.dq + p.epi.G * p.epi.dq) {
-            // every column of this wave is a V channel, stored transposed
-            // (V^T [b][g][d][position]): a lane takes 8 consecutive rows of
-            // one column and stores them as one 16-byte run of positions
-            const EpiParams& e = p.epi;
-            const int hqk = e.H * e.dq + e.G * e.dq;
+            } else if (EPI == EPI_QKV && n0 + wn * WTN >= p.epi.H * p.epi.dq + p.epi.G * p.epi.dq) {
+              // every column of this wave is a V channel, stored transposed
+              // (V^T [b][g][d][position]): a lane takes 8 consecutive rows of
+              // one column and stores them as one 16-byte run of positions
+              const EpiParams& e = p.epi;
+              const int hqk = e.H * e.dq + e.G * e.dq;
 #pragma unroll 1
-            for (int it = 0; it < 32 * WTN / (8 * 64); ++it) {
-              const int idx = it * 64 + lane, c = idx % WTN, rg = idx / WTN;
-              const int ml = wm * WTM + pass * 32 + rg * 8;
-              const int n = n0 + wn * WTN + c;
-              if (ml >= rows || n >= p.N) continue;
-              const int m = row0 + ml, b = m / e.T, i = m - b * e.T;
-              const int nn = n - hqk, g = nn / e.dv, d = nn - g * e.dv;
-              TO* col = (TO*)e.vt + ((int64_t)(b * e.G + g) * e.dv + d) * e.cap + e.kbase + i;
-              float v[8];
+              for (int it = 0; it < 32 * WTN / (8 * 64); ++it) {
+                const int idx = it * 64 + lane, c = idx % WTN, rg = idx / WTN;
+                const int ml = wm * WTM + pass * 32 + rg * 8;
+                const int n = n0 + wn * WTN + c;
+                if (ml >= rows || n >= p.N) continue;
+                const int m = row0 + ml, b = m / e.T, i = m - b * e.T;
+                const int nn = n - hqk, g = nn / e.dv, d = nn - g * e.dv;
+                TO* col = (TO*)e.vt + ((int64_t)(b * e.G + g) * e.dv + d) * e.cap + e.kbase + i;
+                float v[8];
 #pragma unroll
-              for (int x = 0; x < 8; ++x) v[x] = ep[(rg * 8 + x) * EP_LD + c];
-              if (ml + 8 <= rows && i + 8 <= e.T && ((e.kbase + i) & 7) == 0) {
-                store8<EPI, TO>(col, v);
-              } else {
-                // rows past the tile, a sequence boundary or an unaligned run
-                for (int x = 0; x < 8 && ml + x < rows; ++x) {
-                  const int mx = m + x, bx = mx / e.T, ix = mx - bx * e.T;
-                  St<TO>::st((TO*)e.vt + ((int64_t)(bx * e.G + g) * e.dv + d) * e.cap + e.kbase + ix, v[x]);
+                for (int x = 0; x < 8; ++x) v[x] = ep[(rg * 8 + x) * EP_LD + c];
+                if (ml + 8 <= rows && i + 8 <= e.T && ((e.kbase + i) & 7) == 0) {
+                  store8<EPI, TO>(col, v);
+                } else {
+                  // rows past the tile, a sequence boundary or an unaligned run
+                  for (int x = 0; x < 8 && ml + x < rows; ++x) {
+                    const int mx = m + x, bx = mx / e.T, ix = mx - bx * e.T;
+                    St<TO>::st((TO*)e.vt + ((int64_t)(bx * e.G + g) * e.dv + d) * e.cap + e.kbase + ix, v[x]);
+                  }
                 }
               }
-            }
-          } else {
-            // 32 rows x WTN columns in groups of 8 columns, one group per lane
-            constexpr int CG = WTN / 8;
+            } else {
+              // 32 rows x WTN columns in groups of 8 columns, one group per lane
+              constexpr int CG = WTN / 8;
 #pragma unroll 1
-            for (int it = 0; it < 32 * CG / 64; ++it) {
-              const int idx = it * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
-              const int ml = wm * WTM + pass * 32 + rl;
-              float v[8];
+              for (int it = 0; it < 32 * CG / 64; ++it) {
+                const int idx = it * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
+                const int ml = wm * WTM + pass * 32 + rl;
+                float v[8];
 #pragma unroll
-              for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
-              if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + wn * WTN + c8, v, v);
+                for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
+                if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + wn * WTN + c8, v, v);
+              }
             }
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
           }
-          __builtin_amdgcn_s_waitcnt(0);
-          __builtin_amdgcn_wave_barrier();
+        }
+        if constexpr (S) {
+          // strip rows 256 .. rows-1: per strip 32 x 64 (wm = 0) or 32 x 32
+          // (wm = 1) columns
+          const int cg = wm ? 4 : 8, ncol0 = n0 + wn * WTN + (wm ? 64 : 0);
+#pragma unroll
+          for (int st = 0; st < NSTR; ++st) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = accs[st][j][e];
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+            for (int it = 0; it < 4; ++it) {
+              const int idx = it * 64 + lane, rl = idx / cg, c8 = (idx - rl * cg) * 8;
+              const int ml = BM + 32 * st + rl;
+              if (rl < 32 && ml < rows) {
+                float v[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
+                epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, ncol0 + c8, v, v);
+              }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+          }
         }
       }
-      if constexpr (S) {
-        // strip rows 256 .. rows-1: per strip 32 x 64 (wm = 0) or 32 x 32
-        // (wm = 1) columns
-        const int cg = wm ? 4 : 8, ncol0 = n0 + wn * WTN + (wm ? 64 : 0);
-#pragma unroll
-        for (int st = 0; st < NSTR; ++st) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-              ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = accs[st][j][e];
-          __builtin_amdgcn_s_waitcnt(0);
-          __builtin_amdgcn_wave_barrier();
-#pragma unroll 1
-          for (int it = 0; it < 4; ++it) {
-            const int idx = it * 64 + lane, rl = idx / cg, c8 = (idx - rl * cg) * 8;
-            const int ml = BM + 32 * st + rl;
-            if (rl < 32 && ml < rows) {
-              float v[8];
-#pragma unroll
-              for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
-              epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, ncol0 + c8, v, v);
-            }
-          }
-          __builtin_amdgcn_s_waitcnt(0);
-          __builtin_amdgcn_wave_barrier();
-        }
-      }
-    }
     };
     if constexpr (HAS_STRIP) {
       if (rows > BM + 32) full_tile(std::integral_constant<int, 2>{});
