@@ -545,15 +545,55 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
               }
             } else {
               // 32 rows x WTN columns in groups of 8 columns, one group per lane
-              constexpr int CG = WTN / 8;
+              constexpr int CG = WTN / 8, NIT = 32 * CG / 64;
+              if constexpr (EPI == EPI_RESID) {
+                // the residual rows of PG groups are requested before their
+                // stores, so the load latencies overlap instead of each store
+                // waiting on its own
+                const EpiParams& e = p.epi;
+                constexpr int PG = NIT % 4 == 0 ? 4 : 3;   // 8 groups per pass (256 columns) or 6 (192)
+                static_assert(NIT % PG == 0, "whole load batches per pass");
 #pragma unroll 1
-              for (int it = 0; it < 32 * CG / 64; ++it) {
-                const int idx = it * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
-                const int ml = wm * WTM + pass * 32 + rl;
-                float v[8];
+                for (int g0 = 0; g0 < NIT; g0 += PG) {
+                  float4 r[PG][2];
 #pragma unroll
-                for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
-                if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + wn * WTN + c8, v, v);
+                  for (int u = 0; u < PG; ++u) {
+                    const int idx = (g0 + u) * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
+                    const int ml = wm * WTM + pass * 32 + rl, n = n0 + wn * WTN + c8;
+                    r[u][0] = r[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (ml < rows && n + 8 <= p.N) {
+                      const float* src = e.resid + (int64_t)(row0 + ml) * e.ldo + n;
+                      r[u][0] = *(const float4*)src;
+                      r[u][1] = *(const float4*)(src + 4);
+                    }
+                  }
+#pragma unroll
+                  for (int u = 0; u < PG; ++u) {
+                    const int idx = (g0 + u) * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
+                    const int ml = wm * WTM + pass * 32 + rl, n = n0 + wn * WTN + c8;
+                    if (ml >= rows) continue;
+                    float v[8];
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
+                    if (n + 8 > p.N) {
+                      epi_store8<EPI, TO>(e, p.N, row0 + ml, n, v, v);   // ragged column end
+                    } else {
+                      const float o[8] = {r[u][0].x + v[0], r[u][0].y + v[1], r[u][0].z + v[2], r[u][0].w + v[3],
+                                          r[u][1].x + v[4], r[u][1].y + v[5], r[u][1].z + v[6], r[u][1].w + v[7]};
+                      store8<EPI, float>((float*)e.out + (int64_t)(row0 + ml) * e.ldo + n, o);
+                    }
+                  }
+                }
+              } else {
+#pragma unroll 1
+                for (int it = 0; it < NIT; ++it) {
+                  const int idx = it * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
+                  const int ml = wm * WTM + pass * 32 + rl;
+                  float v[8];
+#pragma unroll
+                  for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
+                  if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + wn * WTN + c8, v, v);
+                }
               }
             }
             __builtin_amdgcn_s_waitcnt(0);
