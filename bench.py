@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="mythos_3b")
-    ap.add_argument("--cpu-prefix", type=int, default=2048)
+    ap.add_argument("--cpu-prefix", type=int, default=4096)   # 3b: one whole loop of the workload
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run plain device copies of this many MiB (calibrates HBM byte counters)")
