@@ -111,6 +111,21 @@ def test_end_to_end_merged_expert_tails():
     _e2e(cfg, W, e, h0)
 
 
+@pytest.mark.parametrize("name, over", [
+    ("small_bf16", dict(batch=3, seq=1, n_loops=2)),                         # single-token prefill, no cache
+    ("small_bf16", dict(batch=1, seq=5)),                                    # one short sequence
+    ("small_bf16", dict(n_experts=2, top_k=2)),                              # every token to every expert
+    ("small_bf16", dict(n_experts=1, top_k=1, n_shared_experts=0)),          # one expert, no shared expert
+    ("small_f32", dict(act_threshold=1.0)),                                  # halting only by the last-loop rule
+], ids=["T1-no-cache", "B1-T5", "top2-of-2", "one-expert", "thr-1.0"])
+def test_end_to_end_degenerate_shapes(name, over):
+    """Degenerate shapes and routing: every step of the path against the
+    oracle where tiles are mostly padding, routing has no choice, or the
+    shared expert is absent."""
+    cfg, W, e, h0 = _inputs(name, **over)
+    _e2e(cfg, W, e, h0)
+
+
 @pytest.mark.parametrize("act", [0.99, 0.0])
 def test_end_to_end_wide_rows(act):
     """dim 1024 with rank-16 LoRA, top-2 plus one shared expert: the batched
