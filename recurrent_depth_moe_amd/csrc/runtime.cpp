@@ -274,6 +274,9 @@ struct rdt_block {
   std::vector<hipEvent_t> free_events;
   double stage_ms[RDT_STAGE_COUNT] = {0};
   int64_t stage_n[RDT_STAGE_COUNT] = {0};
+  // side stream for single-token steps (created on first use)
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 namespace {
@@ -558,6 +561,9 @@ rdt_status rdt_block_destroy(rdt_block* b) {
     (void)hipEventDestroy(p.b);
   }
   for (auto e : b->free_events) (void)hipEventDestroy(e);
+  if (b->ev_fork) (void)hipEventDestroy(b->ev_fork);
+  if (b->ev_join) (void)hipEventDestroy(b->ev_join);
+  if (b->aux) (void)hipStreamDestroy(b->aux);
   if (b->mem) (void)hipFree(b->mem);
   delete b;
   if (he != hipSuccess) return fail(RDT_E_HIP, "destroy: %s", hipGetErrorString(he));
@@ -653,6 +659,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   if (b->cap_loops && n_loops > b->cap_loops)
     return fail(RDT_E_INVALID_ARG, "n_loops %d exceeds the capture buffers (%d loops)", n_loops, b->cap_loops);
   hipStream_t s = (hipStream_t)stream;
+  const hipStream_t s_main = s;
   const Plan p = make_plan(c, B, T);
   char* w = (char*)ws;
   auto W = [&](int id) -> void* { return w + p.off[id]; };
@@ -676,8 +683,9 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
 
   // bf16: the 256x256 kernel for prefill products, the skinny kernel for
   // single-token steps and for narrow outputs (router logits)
-  auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16, bool narrow = false) {
+  auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16, bool narrow = false, hipStream_t on = nullptr) {
     gp.live = live_prev;
+    const hipStream_t s = on ? on : s_main;
     if (!bf) {
       launch_gemm_f32(gp, epi, dual, b->n_cu, s);
       return;
@@ -720,6 +728,41 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     gp.dense_gm = 4;
     return gp;
   };
+  auto shared_experts = [&](hipStream_t on) {
+    for (int si = 0; si < c.n_shared_experts; ++si) {
+      GemmParams gp = dense(W(WS_F), D, (const char*)b->s_gate + (size_t)si * F * D * es,
+                            (const char*)b->s_up + (size_t)si * F * D * es, N, F, D);
+      gp.epi.out = W(WS_ACTS);
+      gp.epi.ldo = F;
+      {
+        StageTimer st_(b, on, RDT_STAGE_SHARED_GATEUP);
+        gemm(gp, EPI_SWIGLU, true, bf, false, on);
+      }
+      GemmParams gd = dense(W(WS_ACTS), F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, N, D, F);
+      gd.epi.out = (char*)W(WS_YS) + (size_t)si * N * D * es;
+      gd.epi.ldo = D;
+      StageTimer st_(b, on, RDT_STAGE_SHARED_DOWN);
+      gemm(gd, EPI_STORE, false, bf, false, on);
+    }
+  };
+  // Single-token bf16 steps are launch- and latency-bound: the shared experts
+  // (which need only f) go to a side stream of the handle's, forked after the
+  // FFN norm and joined before the tail.  They write act_s and y_s, which
+  // nothing on the main stream touches in between.
+  const bool side = bf && T == 1 && c.n_shared_experts > 0;
+  hipError_t he = hipSuccess;
+  if (side && !b->aux) {
+    if ((he = hipStreamCreateWithFlags(&b->aux, hipStreamNonBlocking)) != hipSuccess) {
+      b->aux = nullptr;
+      return fail(RDT_E_HIP, "side stream: %s", hipGetErrorString(he));
+    }
+    if ((he = hipEventCreateWithFlags(&b->ev_fork, hipEventDisableTiming)) != hipSuccess ||
+        (he = hipEventCreateWithFlags(&b->ev_join, hipEventDisableTiming)) != hipSuccess) {
+      (void)hipStreamDestroy(b->aux);
+      b->aux = nullptr;
+      return fail(RDT_E_HIP, "side stream events: %s", hipGetErrorString(he));
+    }
+  }
 
   for (int t = 0; t < n_loops; ++t) {
     const float* hp = t == 0 ? h0 : WF(WS_H);
@@ -835,6 +878,15 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       StageTimer st_(b, s, RDT_STAGE_FFN_NORM);
       launch_rmsnorm(bf, WF(WS_X1), D, b->g_ffn, c.norm_eps, W(WS_F), D, N, D, s, live_prev);
     }
+    if (side) {
+      // fork: the side stream starts once f is written; the tail joins it
+      if ((he = hipEventRecord(b->ev_fork, s)) != hipSuccess ||
+          (he = hipStreamWaitEvent(b->aux, b->ev_fork, 0)) != hipSuccess)
+        return fail(RDT_E_HIP, "stream fork: %s", hipGetErrorString(he));
+      shared_experts(b->aux);
+      if ((he = hipEventRecord(b->ev_join, b->aux)) != hipSuccess)
+        return fail(RDT_E_HIP, "stream join: %s", hipGetErrorString(he));
+    }
     // a9: router logits, softmax, top-k
     {
       StageTimer st_(b, s, RDT_STAGE_ROUTER);
@@ -900,22 +952,12 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       StageTimer st_(b, s, RDT_STAGE_EXPERT_DOWN);
       gemm(gd, EPI_STORE, false, bf);
     }
-    // a13: shared experts on every row
-    for (int si = 0; si < c.n_shared_experts; ++si) {
-      GemmParams gp = dense(W(WS_F), D, (const char*)b->s_gate + (size_t)si * F * D * es,
-                            (const char*)b->s_up + (size_t)si * F * D * es, N, F, D);
-      gp.epi.out = W(WS_ACTS);
-      gp.epi.ldo = F;
-      {
-        StageTimer st_(b, s, RDT_STAGE_SHARED_GATEUP);
-        gemm(gp, EPI_SWIGLU, true, bf);
-      }
-      GemmParams gd = dense(W(WS_ACTS), F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, N, D, F);
-      gd.epi.out = (char*)W(WS_YS) + (size_t)si * N * D * es;
-      gd.epi.ldo = D;
-      StageTimer st_(b, s, RDT_STAGE_SHARED_DOWN);
-      gemm(gd, EPI_STORE, false, bf);
-    }
+    // a13: shared experts on every row (on the side stream for single-token
+    // steps, where they ran beside the router and the routed experts)
+    if (!side)
+      shared_experts(s);
+    else if ((he = hipStreamWaitEvent(s, b->ev_join, 0)) != hipSuccess)
+      return fail(RDT_E_HIP, "stream wait: %s", hipGetErrorString(he));
     // a14-a17: combine, depth-wise LoRA, LTI injection, ACT
     {
       TailArgs ta{};
@@ -954,7 +996,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       launch_loop_tail(ta, s);
     }
   }
-  hipError_t he = hipGetLastError();
+  he = hipGetLastError();
   if (he != hipSuccess) return fail(RDT_E_HIP, "kernel launch: %s", hipGetErrorString(he));
   return RDT_OK;
 }
