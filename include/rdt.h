@@ -18,8 +18,15 @@
  *   - A handle must not be used from two threads at once.  Results are
  *     bitwise reproducible run to run (no floating-point atomics).
  *   - Only rdt_block_create allocates device memory (the handle's own copy
- *     of the weights and tables).  Forward and decode allocate nothing: the
- *     caller passes the workspace.
+ *     of the weights and tables) or creates HIP objects (for bf16 configs
+ *     with shared experts, a side stream of default priority and two
+ *     events).  Forward and decode allocate nothing: the caller passes the
+ *     workspace.
+ *   - Single-token bf16 calls run the shared-expert products on the
+ *     handle's side stream, forked from `stream` after the FFN norm and
+ *     joined back before the loop tail with events, so the call stays
+ *     ordered on `stream`; calls of one handle on different streams then
+ *     share (and serialise on) that side stream.
  */
 #ifndef RDT_H
 #define RDT_H

@@ -274,7 +274,8 @@ struct rdt_block {
   std::vector<hipEvent_t> free_events;
   double stage_ms[RDT_STAGE_COUNT] = {0};
   int64_t stage_n[RDT_STAGE_COUNT] = {0};
-  // side stream for single-token steps (created on first use)
+  // side stream for single-token bf16 steps with shared experts (created
+  // with the handle)
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
@@ -544,7 +545,16 @@ rdt_status rdt_block_create(const rdt_config* cfg, const void* const* weights, v
     he = hipGetLastError();
   }
   if (he == hipSuccess) he = hipStreamSynchronize(s);
+  // side stream (default priority) and its fork / join events for the
+  // shared-expert products of single-token bf16 steps
+  if (he == hipSuccess && c.weight_dtype == RDT_BF16 && c.n_shared_experts > 0) {
+    he = hipStreamCreateWithFlags(&b->aux, hipStreamNonBlocking);
+    if (he == hipSuccess) he = hipEventCreateWithFlags(&b->ev_fork, hipEventDisableTiming);
+    if (he == hipSuccess) he = hipEventCreateWithFlags(&b->ev_join, hipEventDisableTiming);
+  }
   if (he != hipSuccess) {
+    if (b->ev_fork) (void)hipEventDestroy(b->ev_fork);
+    if (b->aux) (void)hipStreamDestroy(b->aux);
     (void)hipFree(b->mem);
     delete b;
     return fail(RDT_E_HIP, "create: %s", hipGetErrorString(he));
@@ -749,20 +759,8 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   // (which need only f) go to a side stream of the handle's, forked after the
   // FFN norm and joined before the tail.  They write act_s and y_s, which
   // nothing on the main stream touches in between.
-  const bool side = bf && T == 1 && c.n_shared_experts > 0;
+  const bool side = bf && T == 1 && b->aux != nullptr;
   hipError_t he = hipSuccess;
-  if (side && !b->aux) {
-    if ((he = hipStreamCreateWithFlags(&b->aux, hipStreamNonBlocking)) != hipSuccess) {
-      b->aux = nullptr;
-      return fail(RDT_E_HIP, "side stream: %s", hipGetErrorString(he));
-    }
-    if ((he = hipEventCreateWithFlags(&b->ev_fork, hipEventDisableTiming)) != hipSuccess ||
-        (he = hipEventCreateWithFlags(&b->ev_join, hipEventDisableTiming)) != hipSuccess) {
-      (void)hipStreamDestroy(b->aux);
-      b->aux = nullptr;
-      return fail(RDT_E_HIP, "side stream events: %s", hipGetErrorString(he));
-    }
-  }
 
   for (int t = 0; t < n_loops; ++t) {
     const float* hp = t == 0 ? h0 : WF(WS_H);
