@@ -315,6 +315,38 @@ def test_decode_against_random_cache(start_pos, kv_heads, nan_past_end):
         assert rel_err(v_gpu[:, :, P], oc[t]["v"][:, :, P]) < TOL["bf16"]
 
 
+def test_decode_on_a_non_default_stream():
+    """A bf16 decode step with a shared expert, enqueued on a fresh stream
+    (its shared-expert products fork to the handle's side stream and join
+    back before the loop tail), gives bitwise the outputs and cache writes
+    of the same step on the default stream, twice in a row."""
+    import torch
+    from recurrent_depth_moe_amd import binding
+    cfg, W, e, h0 = _inputs("small_bf16_decode")
+    assert cfg["n_shared_experts"] > 0
+    B, n = cfg["batch"], cfg["n_loops"]
+    cap = kv_capacity(cfg)
+
+    def cache():
+        kv = torch.zeros((binding.kv_cache_bytes(cfg, B, cap, n),), dtype=torch.uint8, device="cuda")
+        for t in range(n):
+            fill_cache(cfg, None, kv, t, generate.make_cache_loop(cfg, t, "k"), generate.make_cache_loop(cfg, t, "v"))
+        return kv
+
+    print(f"[decode stream] {cfg['name']} B={B} pos={cfg['start_pos']} loops={n}", flush=True)
+    kv0 = cache()
+    ref = DeviceRun(cfg, W, e, h0, kv=kv0, decode=True).np()
+    side = torch.cuda.Stream()
+    for _ in range(2):
+        kv1 = cache()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            got = DeviceRun(cfg, W, e, h0, kv=kv1, decode=True).np()
+        np.testing.assert_array_equal(got["out"], ref["out"])
+        np.testing.assert_array_equal(got["sel"], ref["sel"])
+        assert torch.equal(kv1, kv0)
+
+
 @pytest.mark.parametrize("name", ["tiny_gqa", "tiny_mla", "small_bf16"])
 def test_prefill_then_decode_matches_full_prefill(name):
     """Prefill of positions 0..T-2 into the per-loop caches, then a decode
