@@ -415,7 +415,7 @@ class Adoption:
 
 
 def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=None,
-                      adopt=None, record=False, stop_when_halted=True):
+                      adopt=None, record=False, stop_when_halted=True, on_loop=None):
     """The looped Recurrent Block ([ZS §Recurrent Block]; [RC §아키텍처]).
 
     e, h0: [B, T, D].  Returns dict(out=[B, T, D] float64, halt_counts=[B, T]
@@ -423,7 +423,9 @@ def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=
     act_threshold == 0 the output is the final state; otherwise the
     ACT-weighted sum of the states, and the loop stops once every position
     has halted (nothing returned can change after that) unless a cache is
-    being filled or ``stop_when_halted`` is False.
+    being filled or ``stop_when_halted`` is False.  ``on_loop(t, state)``,
+    when given, is called after each loop with the new state (progress
+    reports of long runs; it cannot change anything).
     """
     e = as_f64(e)
     h = as_f64(h0)
@@ -482,6 +484,8 @@ def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=
             rec["sel"].append(step["sel"].copy())
             rec["margin"].append(step["margin"].copy())
         loops_run = t + 1
+        if on_loop is not None:
+            on_loop(t, h)
         if act and stop_when_halted and cache is None and halted.all():
             break
     out = h_out if act else h

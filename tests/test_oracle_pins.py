@@ -32,6 +32,16 @@ def _setup(name, scales=None, **over):
     return cfg, W, O.Params(W), e, h0
 
 
+def _t64(a):
+    """float64 torch tensor of a weight array, decoded by torch itself:
+    uint16 arrays are bfloat16 bit patterns (reinterpreted as torch.bfloat16),
+    so this path shares no decoding with the oracle's as_f64."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).double()
+    return torch.from_numpy(a.astype(np.float64))
+
+
 # ---------------------------------------------------------------- injection
 
 def test_A_matches_zoh_discretisation_and_clamp():
@@ -200,8 +210,7 @@ def test_moe_equals_dense_masked_sum():
     got = O.moe_ffn(cfg, P, f, sel, gate)
     ft = torch.from_numpy(f)
     def expert(wg, wu, wd):
-        return F.linear(F.silu(F.linear(ft, torch.from_numpy(O.as_f64(wg)))) * F.linear(ft, torch.from_numpy(O.as_f64(wu))),
-                        torch.from_numpy(O.as_f64(wd)))
+        return F.linear(F.silu(F.linear(ft, _t64(wg))) * F.linear(ft, _t64(wu)), _t64(wd))
     dense = torch.stack([expert(W["w_gate"][x], W["w_up"][x], W["w_down"][x]) for x in range(cfg["n_experts"])], 1)
     mask = torch.zeros(24, cfg["n_experts"], dtype=torch.float64)
     for n in range(24):
@@ -287,12 +296,57 @@ def test_act_weights_sum_to_one_and_first_crossing(name):
     np.testing.assert_allclose(on["out"], ref, rtol=1e-13)
 
 
+def test_halting_probability_matches_torch_and_closed_form():
+    """[ZS §ACT]: the halting head is a linear map of h to one logit followed
+    by a sigmoid, p = sigmoid(h . w + b).  Checked against torch's
+    sigmoid(F.linear(h, w) + b) on random states, and against the closed
+    form sigmoid(b) = 1 / (1 + exp(-b)) for states orthogonal to w (b = 0
+    gives exactly 1/2), so a flipped sign, a dropped bias or a transposed
+    product fails."""
+    rng = np.random.default_rng(11)
+    D = 48
+    w = rng.standard_normal(D) * 0.3
+    for b in (0.0, -1.7, 2.3):
+        P = O.Params({"halt_w": w, "halt_b": np.array([b])})
+        h = rng.standard_normal((37, D))
+        got = O.halting_probability(P, h)
+        ref = torch.sigmoid(F.linear(torch.from_numpy(h), torch.from_numpy(w)[None, :]) + b)[:, 0].numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-14, atol=0)
+        # states orthogonal to w: the logit is the bias alone
+        hp = h - np.outer(h @ w / (w @ w), w)
+        np.testing.assert_allclose(O.halting_probability(P, hp), 1.0 / (1.0 + math.exp(-b)), rtol=1e-13)
+    P0 = O.Params({"halt_w": w, "halt_b": np.array([0.0])})
+    assert O.halting_probability(P0, np.zeros((3, D))).tolist() == [0.5, 0.5, 0.5]
+    # monotone in the logit and in (0, 1)
+    ramp = np.outer(np.linspace(-30, 30, 61), w / (w @ w))
+    p = O.halting_probability(P0, ramp)
+    assert np.all(np.diff(p) > 0) and p[0] > 0 and p[-1] < 1
+
+
+def test_bf16_decode_matches_torch_on_every_bit_pattern():
+    """as_f64 reads uint16 arrays as bfloat16 bit patterns.  All 65536
+    patterns decode to what torch's own bfloat16 gives (NaN patterns to NaN),
+    so a wrong shift, byte order or sign bit fails."""
+    u16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):      # NaN patterns widen with a warning
+        got = O.as_f64(u16)
+    ref = torch.from_numpy(u16.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))     # -0.0 included
+    # a few values fixed by the format itself: 1.0 = 0x3F80, -2.0 = 0xC000,
+    # the smallest subnormal 2^-133 = 0x0001, +inf = 0x7F80
+    assert O.as_f64(np.array([0x3F80, 0xC000, 0x0001, 0x7F80], dtype=np.uint16)).tolist() == \
+        [1.0, -2.0, 2.0 ** -133, math.inf]
+
+
 # ---------------------------------------------------------------- whole block
 
 def _torch_one_loop(cfg, W, h, e, t, start_pos=0):
     """One loop written independently with torch CPU library routines:
     F.rms_norm, complex-number RoPE, SDPA with GQA, a dense masked MoE."""
-    T64 = lambda a: torch.from_numpy(O.as_f64(a))
+    T64 = _t64
     h, e = torch.from_numpy(h), torch.from_numpy(e)
     B, T, D = h.shape
     eps = cfg["norm_eps"]
