@@ -21,7 +21,11 @@
  *     of the weights and tables) or creates HIP objects (for bf16 configs
  *     with shared experts, a side stream of default priority and two
  *     events).  Forward and decode allocate nothing: the caller passes the
- *     workspace.
+ *     workspace.  The one exception is opt-in stage timing
+ *     (rdt_set_timing*): while it is on, forward and decode create the HIP
+ *     events they record on demand; rdt_read_timing returns them to a pool
+ *     of the handle that later calls reuse, and rdt_block_destroy frees
+ *     them.
  *   - Single-token bf16 calls run the shared-expert products on the
  *     handle's side stream, forked from `stream` after the FFN norm and
  *     joined back before the loop tail with events, so the call stays

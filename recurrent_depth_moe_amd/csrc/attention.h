@@ -3,7 +3,16 @@
 
 #include "common.h"
 
-// Any head widths (dq, dv <= 128), fp32 or bf16 storage.
+// Generic kernel's LDS: the query row (dq floats, rounded up to 4) then one
+// score per visible key.  The runtime refuses configurations whose longest
+// call would need more than RDT_GENERIC_LDS_MAX bytes.
+constexpr size_t RDT_GENERIC_LDS_MAX = 64 * 1024;
+__host__ __device__ inline int attn_generic_qslots(int dq) { return (dq + 3) & ~3; }
+inline size_t attn_generic_lds_bytes(int dq, int nk) {
+  return ((size_t)attn_generic_qslots(dq) + (size_t)nk) * sizeof(float);
+}
+// Any query width dq (the query row and the scores share the dynamic LDS,
+// see above), fp32 or bf16 storage.
 // `live` (nullable): skip the launch when it points to 0 (every position
 // halted in the previous loop).
 void launch_attn_generic(int dtype_bf16, const void* q, const void* k, const void* vt, void* o, int B, int H,

@@ -31,8 +31,8 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
                                                           int kbase, float scale, const int32_t* live) {
   RDT_SKIP_IF_ALL_HALTED(live);
   extern __shared__ float sm[];
-  float* qs = sm;          // [dq]
-  float* sc = sm + 128;    // [nk]
+  float* qs = sm;                     // [dq]
+  float* sc = sm + attn_generic_qslots(dq);   // [nk]
   const int i = blockIdx.x, bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H, g = h / (H / G);
   const int lane = threadIdx.x;
@@ -521,7 +521,7 @@ void launch_attn_generic(int dtype_bf16, const void* q, const void* k, const voi
                          int G, int Tq, int cap, int dq, int dv, int kbase, float scale, hipStream_t s,
                          const int32_t* live) {
   const dim3 grid(Tq, B * H), block(64);
-  const size_t shm = (128 + (size_t)(kbase + Tq)) * sizeof(float);
+  const size_t shm = attn_generic_lds_bytes(dq, kbase + Tq);
   if (dtype_bf16)
     attn_generic_kernel<bf16_t><<<grid, block, shm, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt,
                                                          (bf16_t*)o, H, G, Tq, cap, dq, dv, kbase, scale, live);

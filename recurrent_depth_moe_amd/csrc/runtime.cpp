@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -86,6 +87,18 @@ rdt_status check_config(const rdt_config* c) {
   if (c->loop_dim < 0 || c->loop_dim > c->dim || c->loop_dim % 4)
     return fail(RDT_E_INVALID_ARG, "loop_dim must be a multiple of 4 in [0, dim]");
   if (c->max_seq_len < 1) return fail(RDT_E_INVALID_ARG, "max_seq_len");
+  // configurations that can reach the generic attention kernel (fp32, MLA,
+  // bf16 single-token steps with more than 16 query heads per KV head) hold
+  // one score per visible key in LDS: bound the longest sequence up front
+  if (c->weight_dtype != RDT_BF16 || !is_gqa(*c) || c->n_heads / c->n_kv_heads > 16) {
+    const int dq = is_gqa(*c) ? c->head_dim
+                              : std::max(c->qk_nope_head_dim + c->qk_rope_head_dim,
+                                         c->kv_lora_rank + c->qk_rope_head_dim);
+    const size_t need = attn_generic_lds_bytes(dq, c->max_seq_len);
+    if (need > RDT_GENERIC_LDS_MAX)
+      return fail(RDT_E_UNSUPPORTED, "max_seq_len %d: generic attention needs %zu bytes of LDS (limit %zu)",
+                  c->max_seq_len, need, RDT_GENERIC_LDS_MAX);
+  }
   if (!(c->norm_eps > 0.f) || !(c->rope_theta > 0.f) || !(c->loop_theta > 0.f))
     return fail(RDT_E_INVALID_ARG, "norm_eps, rope_theta and loop_theta must be positive");
   return RDT_OK;

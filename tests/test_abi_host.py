@@ -70,6 +70,23 @@ def test_unsupported_combinations():
         assert L.rdt_check_config(ctypes.byref(_cfg(name))) == 0, name
 
 
+def test_generic_attention_lds_bound_refused_up_front():
+    """Configurations that reach the generic attention kernel keep the query
+    row and one score per visible key in 64 KB of LDS: a longer max_seq_len
+    is refused by the config check (UNSUPPORTED) before any device work,
+    and a wide MLA latent (kv_lora_rank 512 + rope 16 query slots in decode)
+    is accepted while it fits."""
+    from recurrent_depth_moe_amd import binding
+    L = binding.lib()
+    assert L.rdt_check_config(ctypes.byref(_cfg("tiny_gqa", max_seq_len=16000))) == 0
+    assert L.rdt_check_config(ctypes.byref(_cfg("tiny_gqa", max_seq_len=16380))) == 2
+    assert "LDS" in L.rdt_last_error().decode()
+    assert L.rdt_check_config(ctypes.byref(_cfg("tiny_mla", kv_lora_rank=512, max_seq_len=15800))) == 0
+    assert L.rdt_check_config(ctypes.byref(_cfg("tiny_mla", kv_lora_rank=512, max_seq_len=15900))) == 2
+    # bf16 GQA with at most 16 query heads per KV head never uses it
+    assert L.rdt_check_config(ctypes.byref(_cfg("mythos_3b", max_seq_len=1 << 20))) == 0
+
+
 def test_call_checks():
     from recurrent_depth_moe_amd import binding
     L = binding.lib()
