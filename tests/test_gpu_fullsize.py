@@ -21,7 +21,7 @@ import pytest
 from oracle import rdt_oracle as O
 from workloads import configs, generate
 
-from gpu_support import EPS_ROUTE, TOL, DeviceRun, fill_cache, kv_capacity, rel_err
+from gpu_support import EPS_HALT, EPS_ROUTE, TOL, DeviceRun, fill_cache, kv_capacity, rel_err
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -92,6 +92,48 @@ def _dispatch_and_router(cfg, P, run):
     np.testing.assert_array_equal(inv[order], np.arange(N * k))
 
 
+def _free_running(cfg, W, e, h0, r, seqs=None, cache=None):
+    """The oracle runs every loop from the same e and h0 as the GPU (no
+    teacher forcing), on whole sequences (``seqs``: all when None; each
+    sequence is independent of the others, so a subset is exact).  Router
+    and halting decisions within the bf16 tie margins are taken from the
+    GPU; any other difference fails.  Checks, on every row of those
+    sequences: halt counts equal, expert choices equal outside the margins,
+    and the output within max|d|/RMS <= 3e-2; prints the per-loop error of
+    the state (GPU h_t against the oracle's h_t)."""
+    import time
+    B, T, D = e.shape
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    Bs, N, L = len(seqs), len(seqs) * T, cfg["n_loops"]
+    sub = dict(cfg, batch=Bs)
+    rows = np.concatenate([np.arange(b * T, (b + 1) * T) for b in seqs])
+    sel = r["sel"].reshape(L, B * T, -1)[:, rows]
+    halt = r["halt"].reshape(B, T)[seqs]
+    adopt = O.Adoption(sel=sel, halt_counts=halt, eps_route=EPS_ROUTE["bf16"], eps_halt=EPS_HALT["bf16"])
+    gh = r["h"].reshape(L, B * T, D)
+    curve = []
+    t0 = time.time()
+
+    def on_loop(t, h):
+        err = rel_err(gh[t][rows], h.reshape(N, D))
+        curve.append(err)
+        print(f"[{cfg['name']}] free-running loop {t}: state max|d|/rms = {err:.3e} "
+              f"(routes adopted {adopt.route_adopted}, disagree {adopt.route_disagree}; "
+              f"{time.time() - t0:.0f} s)", flush=True)
+
+    ref = O.recurrent_forward(sub, O.Params(W), e[seqs], h0[seqs], L, cfg["act_threshold"],
+                              start_pos=cfg["start_pos"], cache=cache, adopt=adopt, on_loop=on_loop)
+    err = rel_err(r["out"].reshape(B, T, D)[seqs], ref["out"])
+    print(f"[{cfg['name']}] free-running over {L} loops on {N} rows: output max|d|/rms = {err:.3e}; "
+          f"per-loop state error {[round(x, 5) for x in curve]}; routes adopted {adopt.route_adopted}, "
+          f"halts adopted {adopt.halt_adopted}", flush=True)
+    for (lp, n, m) in adopt.disagree_rows[:10]:
+        print(f"  route disagreement: loop {lp} row {n} margin {m:.3e}", flush=True)
+    assert adopt.route_disagree == 0 and adopt.halt_disagree == 0
+    np.testing.assert_array_equal(halt, ref["halt_counts"])
+    assert err <= TOL["bf16"]
+
+
 def _gpu(cfg, W, e, h0, **kw):
     g = DeviceRun(cfg, W, e, h0, **kw)
     r = g.np()
@@ -154,6 +196,14 @@ def test_3b_act_on_every_row(run_3b):
     assert err <= TOL["f32"]
 
 
+def test_3b_free_running_all_loops(run_3b):
+    """Every loop of the full mythos_3b workload (both sequences, all 4096
+    positions, ACT at 0.99) against the oracle run free from the same
+    inputs."""
+    cfg, W, e, h0, g, r = run_3b
+    _free_running(cfg, W, e, h0, r)
+
+
 @pytest.mark.parametrize("t", [0, 15])
 def test_3b_teacher_forced_loop(run_3b, t):
     cfg, W, e, h0, g, r = run_3b
@@ -164,7 +214,8 @@ def test_3b_teacher_forced_loop(run_3b, t):
 
 def test_1b_full_size():
     """ACT off: the output is the last captured state; loops 0 and 15
-    teacher-forced on sampled rows; router and dispatch on every row."""
+    teacher-forced on sampled rows; router and dispatch on every row; all
+    16 loops free-running against the oracle on every row."""
     cfg = configs.get("mythos_1b")
     W = generate.make_weights(cfg)
     e, h0 = generate.make_inputs(cfg)
@@ -176,16 +227,20 @@ def test_1b_full_size():
     _dispatch_and_router(cfg, P, g)
     for t in (0, cfg["n_loops"] - 1):
         _teacher_forced(cfg, P, r, e, t, _sample_rows(cfg["batch"], cfg["seq"], N_SAMPLE, 200 + t))
+    _free_running(cfg, W, e, h0, r)
 
 
 # ---------------------------------------------------------- mythos_10b decode
 
+FREE_SEQS_10B = (0, 11, 22, 31)
+
+
 def test_10b_decode_full_size():
     """One decode step of 32 sequences at position 8192 against 8192 cached
-    N(0,1) positions, 24 loops.  Loops 0 and 23 hold the seeded cache the
-    oracle also reads and are teacher-forced on every sequence; the other
-    slots hold GPU-drawn N(0,1) values (they only shape the GPU's own
-    states, which enter the oracle as inputs)."""
+    N(0,1) positions in every one of the 24 loop slots (seeded, the same
+    values the oracle reads).  Loops 0 and 23 are teacher-forced on every
+    sequence; four whole sequences run free through all 24 loops against
+    the oracle (sequences are independent, so the subset is exact)."""
     import torch
     from recurrent_depth_moe_amd import binding
     cfg = configs.get("mythos_10b_decode")
@@ -194,22 +249,26 @@ def test_10b_decode_full_size():
     B, P, L = cfg["batch"], cfg["start_pos"], cfg["n_loops"]
     G, dh = cfg["n_kv_heads"], cfg["head_dim"]
     cap = kv_capacity(cfg)
-    kv = torch.empty(binding.kv_cache_bytes(cfg, B, cap, L), dtype=torch.uint8, device="cuda")
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(cfg["seed"])
-    kv.view(torch.bfloat16).normal_(0.0, 1.0, generator=gen)
+    kv = torch.zeros(binding.kv_cache_bytes(cfg, B, cap, L), dtype=torch.uint8, device="cuda")
     checked = (0, L - 1)
-    oc = {}
-    for t in checked:
+    free = list(FREE_SEQS_10B)
+    oc, ocf = {}, []
+    for t in range(L):
         K = generate.make_cache_loop(cfg, t, "k")
         V = generate.make_cache_loop(cfg, t, "v")
         fill_cache(cfg, None, kv, t, K, V)
-        oc[t] = dict(k=np.zeros((B, G, cap, dh)), v=np.zeros((B, G, cap, dh)))
-        oc[t]["k"][:, :, :P] = O.as_f64(K)
-        oc[t]["v"][:, :, :P] = O.as_f64(V)
+        fk = np.zeros((len(free), G, cap, dh))
+        fv = np.zeros((len(free), G, cap, dh))
+        fk[:, :, :P] = O.as_f64(K[free])
+        fv[:, :, :P] = O.as_f64(V[free])
+        ocf.append(dict(k=fk, v=fv))
+        if t in checked:
+            oc[t] = dict(k=np.zeros((B, G, cap, dh)), v=np.zeros((B, G, cap, dh)))
+            oc[t]["k"][:, :, :P] = O.as_f64(K)
+            oc[t]["v"][:, :, :P] = O.as_f64(V)
         del K, V
     torch.cuda.synchronize()
-    print(f"[mythos_10b_decode] B={B} pos={P} loops={L}", flush=True)
+    print(f"[mythos_10b_decode] B={B} pos={P} loops={L}; every cache slot seeded", flush=True)
     g, r = _gpu(cfg, W, e, h0, kv=kv)
     np.testing.assert_array_equal(r["out"].reshape(-1), r["h"][-1].reshape(-1))
     Pm = O.Params(W)
@@ -217,3 +276,4 @@ def test_10b_decode_full_size():
     for t in checked:
         _teacher_forced(cfg, Pm, r, e, t, rows, cache=oc[t])
         del oc[t]
+    _free_running(cfg, W, e, h0, r, seqs=free, cache=ocf)

@@ -374,7 +374,8 @@ def test_chained_decode_steps_match_full_prefill(name, act):
     """Prefill of positions 0..T-5, then four chained decode steps at
     T-4 .. T-1, each appending to the same per-loop caches, reproduce the
     last four rows of a full prefill, ACT output and halt counts included
-    ([ZS §RoPE & generation cache])."""
+    ([ZS §RoPE & generation cache]); each step is also compared with the
+    oracle's full prefill at that position."""
     import torch
     from recurrent_depth_moe_amd import binding
     over = {} if act else {"act_threshold": 0.0}
@@ -384,13 +385,21 @@ def test_chained_decode_steps_match_full_prefill(name, act):
     cfgc = dict(cfg, start_pos=0)
     kv = torch.zeros(binding.kv_cache_bytes(cfg, B, T, n), dtype=torch.uint8, device="cuda")
     full = DeviceRun(cfg, W, e, h0).np()
+    # the oracle's full prefill, decisions within the tie margins taken
+    # from the GPU's full prefill
+    dt = cfg["dtype"]
+    adopt = O.Adoption(sel=full["sel"], halt_counts=full["halt"], eps_route=EPS_ROUTE[dt], eps_halt=EPS_HALT[dt])
+    ref = O.recurrent_forward(cfg, O.Params(W), e, h0, n, cfg["act_threshold"], adopt=adopt)
+    assert adopt.route_disagree == 0 and adopt.halt_disagree == 0
     P0 = T - steps
     DeviceRun(dict(cfgc, seq=P0), W, e[:, :P0].copy(), h0[:, :P0].copy(), kv=kv, start_pos=0, capture=False, kv_cap=T)
-    tol = TOL[cfg["dtype"]]
+    tol = TOL[dt]
     for i in range(P0, T):
         g = DeviceRun(dict(cfgc, seq=1, start_pos=i), W, e[:, i:i + 1].copy(), h0[:, i:i + 1].copy(), kv=kv,
                    decode=True, kv_cap=T).np()
-        print(f"[chained decode] {name} position {i}: max|d|/rms {rel_err(g['out'][:, 0], full['out'][:, i]):.2e}",
-              flush=True)
+        print(f"[chained decode] {name} position {i}: max|d|/rms {rel_err(g['out'][:, 0], full['out'][:, i]):.2e} "
+              f"vs the GPU prefill, {rel_err(g['out'][:, 0], ref['out'][:, i]):.2e} vs the oracle", flush=True)
         assert rel_err(g["out"][:, 0], full["out"][:, i]) < tol
         np.testing.assert_array_equal(g["halt"][:, 0], full["halt"][:, i])
+        assert rel_err(g["out"][:, 0], ref["out"][:, i]) < tol
+        np.testing.assert_array_equal(g["halt"][:, 0], ref["halt_counts"][:, i])
