@@ -151,7 +151,7 @@ def attend(q, k, v, q_pos, k_pos, scale):
     return p @ v
 
 
-def gqa_attention(cfg, P, a, start_pos, cache, rows):
+def gqa_attention(cfg, P, a, start_pos, cache, rows, kv_state=None):
     """Grouped-query attention with RoPE, output projection included.
 
     [RC §Attention 구현]: fewer KV heads than query heads, RoPE applied to q
@@ -159,14 +159,31 @@ def gqa_attention(cfg, P, a, start_pos, cache, rows):
     (b, i) query rows to produce.  ``cache`` (or None) is a dict with 'k',
     'v' arrays [B, Hkv, capacity, dh] that this call fills at positions
     start_pos .. start_pos+T-1 and then reads from position 0.
+
+    ``kv_state`` (ACT compute skipping, no cache): a dict with 'k', 'v'
+    arrays [B, Hkv, T, dh] that persists over the loops of one call.  Only
+    the ``rows`` (the positions still running) get new keys and values,
+    written into it; every other position keeps the keys and values of the
+    last loop it ran.  Attention reads all T positions of it, causally.
     """
     B, T, D = a.shape
     H, G, dh = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     pos = start_pos + np.arange(T)
     cos, sin = rope_cos_sin(pos, dh, cfg["rope_theta"])
-    k = (a @ P["wk"].T).reshape(B, T, G, dh).transpose(0, 2, 1, 3)
-    v = (a @ P["wv"].T).reshape(B, T, G, dh).transpose(0, 2, 1, 3)
-    k = apply_rope(k, cos, sin)
+    if kv_state is not None:
+        bi = np.array(rows)
+        ar = a[bi[:, 0], bi[:, 1]]                                  # [M, D]
+        kr = (ar @ P["wk"].T).reshape(len(rows), G, dh)
+        vr = (ar @ P["wv"].T).reshape(len(rows), G, dh)
+        kr = apply_rope(kr.transpose(1, 0, 2), cos[bi[:, 1]], sin[bi[:, 1]]).transpose(1, 0, 2)
+        for n, (b, i) in enumerate(rows):
+            kv_state["k"][b, :, i] = kr[n]
+            kv_state["v"][b, :, i] = vr[n]
+        k, v = kv_state["k"], kv_state["v"]
+    else:
+        k = (a @ P["wk"].T).reshape(B, T, G, dh).transpose(0, 2, 1, 3)
+        v = (a @ P["wv"].T).reshape(B, T, G, dh).transpose(0, 2, 1, 3)
+        k = apply_rope(k, cos, sin)
     if cache is not None:
         cache["k"][:, :, start_pos:start_pos + T] = k
         cache["v"][:, :, start_pos:start_pos + T] = v
@@ -346,13 +363,14 @@ def act_weights(cum, running, p, halt_now):
     return np.where(halt_now, np.maximum(1.0 - cum, 0.0), p) * running
 
 
-def run_loop(cfg, P, h, e, t, start_pos=0, cache=None, rows=None, route_hook=None):
+def run_loop(cfg, P, h, e, t, start_pos=0, cache=None, rows=None, route_hook=None, kv_state=None):
     """One pass of the recurrent block at loop index t ([ZS §Recurrent Block]).
 
     h, e: [B, T, D] float64.  Returns the new state for ``rows`` (all rows
     when None) and the intermediates callers check.  ``route_hook(sel,
     margin, rows)`` may return a replacement expert choice (used by the
     tie-adoption protocol); the gates are then taken for that choice.
+    ``kv_state``: see gqa_attention (ACT compute skipping).
     """
     B, T, D = h.shape
     eps = cfg["norm_eps"]
@@ -362,7 +380,12 @@ def run_loop(cfg, P, h, e, t, start_pos=0, cache=None, rows=None, route_hook=Non
     c = rms_norm(u + e, P["g_rec"], eps)
     a = rms_norm(c, P["g_attn"], eps)
     attn = gqa_attention if cfg["attn"] == "gqa" else mla_attention
-    o = attn(cfg, P, a, start_pos, cache, rows)
+    if kv_state is not None:
+        if cfg["attn"] != "gqa" or cache is not None:
+            raise NotImplementedError("ACT compute skipping is defined for GQA without a cache")
+        o = gqa_attention(cfg, P, a, start_pos, None, rows, kv_state=kv_state)
+    else:
+        o = attn(cfg, P, a, start_pos, cache, rows)
     ridx = tuple(np.array(rows).T)
     x1 = c[ridx] + np.stack([o[r] for r in rows])
     f = rms_norm(x1, P["g_ffn"], eps)
@@ -490,6 +513,97 @@ def recurrent_forward(cfg, P, e, h0, n_loops, act_threshold, start_pos=0, cache=
             break
     out = h_out if act else h
     res = dict(out=out, halt_counts=counts.reshape(B, T), state=h, loops_run=loops_run)
+    if record:
+        res["record"] = rec
+    return res
+
+
+def recurrent_forward_act_skip(cfg, P, e, h0, n_loops, act_threshold, adopt=None, record=False, on_loop=None):
+    """ACT with compute skipping: a position that has halted leaves the
+    batch ([GN §6], continuous depth-wise batching: halted tokens stop
+    taking compute).
+
+    Reading of what the pages leave open: a halted position's state is
+    frozen (its output is already complete), it is not run again, and in
+    later loops the other positions attend to the keys and values it had in
+    the last loop it ran (its K/V freeze with it).  Everything else is the
+    rule of ``recurrent_forward``: the same block, the same ACT weights and
+    halt counts, threshold in (0, 1], GQA, no cache.
+
+    ``adopt`` (an Adoption with per-loop expert choices [n_loops, N, k]
+    indexed by position and halt counts [N]) takes another implementation's
+    decisions where the oracle's own are within its tie margins.  Returns
+    dict(out, halt_counts, loops_run[, record]).
+    """
+    if act_threshold <= 0:
+        raise ValueError("compute skipping needs ACT on")
+    e = as_f64(e)
+    h = as_f64(h0).copy()
+    B, T, D = h.shape
+    N = B * T
+    G, dh = cfg["n_kv_heads"], cfg["head_dim"]
+    kv = dict(k=np.zeros((B, G, T, dh)), v=np.zeros((B, G, T, dh)))
+    thr32 = np.float32(act_threshold)
+    hf = h.reshape(N, D)
+    h_out = np.zeros((N, D))
+    cum = np.zeros(N)
+    cum32 = np.zeros(N, dtype=np.float32)
+    halted = np.zeros(N, dtype=bool)
+    counts = np.full(N, n_loops, dtype=np.int64)
+    rec = dict(sel=[], p=[], running=[])
+    loops_run = 0
+    for t in range(n_loops):
+        run_idx = np.nonzero(~halted)[0]
+        if len(run_idx) == 0:
+            break
+        rows = [(int(n) // T, int(n) % T) for n in run_idx]
+        hook = None
+        if adopt is not None and adopt.sel is not None:
+            gpu = np.asarray(adopt.sel[t]).reshape(N, -1)
+
+            def hook(sel, margin, rr, gpu=gpu, t=t, run_idx=run_idx):
+                out = sel.copy()
+                for m in range(len(rr)):
+                    want = gpu[run_idx[m]]
+                    if not np.array_equal(sel[m], want):
+                        if margin[m] < adopt.eps_route:
+                            out[m] = want
+                            adopt.route_adopted += 1
+                        else:
+                            adopt.route_disagree += 1
+                            adopt.disagree_rows.append((t, int(run_idx[m]), float(margin[m])))
+                return out
+        step = run_loop(cfg, P, hf.reshape(B, T, D), e, t, rows=rows, route_hook=hook, kv_state=kv)
+        hr = step["h"]
+        hf[run_idx] = hr
+        p = halting_probability(P, hr)
+        p32 = p.astype(np.float32)
+        sub_cum32 = cum32[run_idx]
+        running = np.ones(len(run_idx), dtype=bool)
+        halt_now = act_halts(sub_cum32, running, p, t, n_loops, act_threshold)
+        if adopt is not None and adopt.halt_counts is not None:
+            gpu_halt = np.asarray(adopt.halt_counts).reshape(N)[run_idx] == t + 1
+            near = (np.abs((sub_cum32 + p32).astype(np.float64) - float(thr32)) < adopt.eps_halt) & \
+                (t != n_loops - 1)
+            diff = gpu_halt != halt_now
+            adopt.halt_adopted += int(np.sum(diff & near))
+            adopt.halt_disagree += int(np.sum(diff & ~near))
+            halt_now = np.where(near, gpu_halt, halt_now)
+        weight = act_weights(cum[run_idx], running, p, halt_now)
+        h_out[run_idx] += weight[:, None] * hr
+        cum[run_idx] += p
+        cum32[run_idx] = (sub_cum32 + p32).astype(np.float32)
+        counts[run_idx[halt_now]] = t + 1
+        halted[run_idx[halt_now]] = True
+        loops_run = t + 1
+        if record:
+            rec["sel"].append((run_idx.copy(), step["sel"].copy()))
+            rec["p"].append((run_idx.copy(), p))
+            rec["running"].append(run_idx.copy())
+        if on_loop is not None:
+            on_loop(t, hf.reshape(B, T, D))
+    res = dict(out=h_out.reshape(B, T, D), halt_counts=counts.reshape(B, T), state=hf.reshape(B, T, D),
+               loops_run=loops_run)
     if record:
         res["record"] = rec
     return res

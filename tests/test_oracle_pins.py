@@ -343,9 +343,15 @@ def test_bf16_decode_matches_torch_on_every_bit_pattern():
 
 # ---------------------------------------------------------------- whole block
 
-def _torch_one_loop(cfg, W, h, e, t, start_pos=0):
+def _torch_one_loop(cfg, W, h, e, t, start_pos=0, frozen=None, running=None):
     """One loop written independently with torch CPU library routines:
-    F.rms_norm, complex-number RoPE, SDPA with GQA, a dense masked MoE."""
+    F.rms_norm, complex-number RoPE, SDPA with GQA, a dense masked MoE.
+
+    With ``frozen`` (dict of k, v [B, G, T, dh] float64 arrays) and
+    ``running`` (bool [B, T]): keys and values are computed for every
+    position and then replaced by the frozen ones where a position is not
+    running (a dense masked form of ACT compute skipping); the keys and
+    values used are returned in ``frozen``."""
     T64 = _t64
     h, e = torch.from_numpy(h), torch.from_numpy(e)
     B, T, D = h.shape
@@ -369,6 +375,11 @@ def _torch_one_loop(cfg, W, h, e, t, start_pos=0):
         q = rot(F.linear(a, T64(W["wq"])).reshape(B, T, H, dh), dh).transpose(1, 2)
         k = rot(F.linear(a, T64(W["wk"])).reshape(B, T, G, dh), dh).transpose(1, 2)
         v = F.linear(a, T64(W["wv"])).reshape(B, T, G, dh).transpose(1, 2)
+        if frozen is not None:
+            keep = torch.from_numpy(np.asarray(running))[:, None, :, None]
+            k = torch.where(keep, k, torch.from_numpy(frozen["k"]))
+            v = torch.where(keep, v, torch.from_numpy(frozen["v"]))
+            frozen["k"], frozen["v"] = k.numpy().copy(), v.numpy().copy()
         o = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
     else:
         kvl, rp, nope, vd = cfg["kv_lora_rank"], cfg["qk_rope_head_dim"], cfg["qk_nope_head_dim"], cfg["v_head_dim"]
@@ -457,3 +468,88 @@ def test_row_subset_equals_full_loop():
     idx = [b * T + i for b, i in rows]
     np.testing.assert_allclose(part["h"], full["h"][idx], rtol=1e-13, atol=1e-14)
     np.testing.assert_array_equal(part["sel"], full["sel"][idx])
+
+
+# ---------------------------------------------------------------- ACT compute skipping
+
+def test_act_skip_loop_matches_dense_masked_torch():
+    """One loop of the compute-skipping mode (only the running positions are
+    computed, halted positions keep their keys and values) equals a dense
+    masked form written with torch: K/V for every position, replaced by the
+    frozen ones where a position is not running, attention and the rest of
+    the block for every position, read on the running rows."""
+    cfg, W, P, e, h0 = _setup("small_f32", scales=BIG)
+    B, T, D = e.shape
+    G, dh = cfg["n_kv_heads"], cfg["head_dim"]
+    rng = np.random.default_rng(21)
+    e64 = e.astype(np.float64)
+    h = e64 * 0.6 + 0.05 * rng.standard_normal(e.shape)
+    running = rng.random((B, T)) < 0.55
+    running[0, 0] = False
+    frozen = dict(k=rng.standard_normal((B, G, T, dh)), v=rng.standard_normal((B, G, T, dh)))
+    kv = dict(k=frozen["k"].copy(), v=frozen["v"].copy())
+    rows = [(b, i) for b in range(B) for i in range(T) if running[b, i]]
+    t = 2
+    got = O.run_loop(cfg, P, h, e64, t, rows=rows, kv_state=kv)["h"]
+    tf = dict(frozen)
+    ref = _torch_one_loop(cfg, W, h, e64, t, frozen=tf, running=running)
+    bi = np.array(rows)
+    np.testing.assert_allclose(got, ref[bi[:, 0], bi[:, 1]], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(kv["k"], tf["k"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(kv["v"], tf["v"], rtol=1e-12, atol=1e-13)
+
+
+def test_act_skip_equals_full_path_when_nothing_halts_early():
+    """With the halting head far negative no position halts before the last
+    loop, so nothing is ever skipped and the mode reduces to the plain path."""
+    cfg, W, P, e, h0 = _setup("small_f32", scales={"halt_w": 0.0, "halt_b": -30.0})
+    n = cfg["n_loops"]
+    a = O.recurrent_forward(cfg, P, e, h0, n, cfg["act_threshold"])
+    b = O.recurrent_forward_act_skip(cfg, P, e, h0, n, cfg["act_threshold"])
+    assert np.all(a["halt_counts"] == n)
+    np.testing.assert_array_equal(a["halt_counts"], b["halt_counts"])
+    np.testing.assert_allclose(b["out"], a["out"], rtol=1e-11, atol=1e-12)
+
+
+def test_act_skip_equals_full_path_on_single_token_sequences():
+    """Sequences of one token attend only to themselves, so skipping a halted
+    position changes nothing it returns: output and halt counts equal the
+    plain path even with halting spread over the loops."""
+    cfg, W, P, e, h0 = _setup("tiny_gqa", scales={"halt_w": 0.05, "halt_b": -0.8}, batch=12, seq=1)
+    n = cfg["n_loops"]
+    a = O.recurrent_forward(cfg, P, e, h0, n, cfg["act_threshold"])
+    b = O.recurrent_forward_act_skip(cfg, P, e, h0, n, cfg["act_threshold"])
+    assert len(np.unique(a["halt_counts"])) > 1
+    np.testing.assert_array_equal(a["halt_counts"], b["halt_counts"])
+    np.testing.assert_allclose(b["out"], a["out"], rtol=1e-11, atol=1e-12)
+
+
+def test_act_skip_weights_sum_to_one_and_halted_rows_stop():
+    """In the skipping mode too the ACT weights of a position sum to 1, its
+    halt count is the first loop where the float32 running sum of its p
+    reaches the threshold, and a halted position is never computed again."""
+    cfg, W, P, e, h0 = _setup("small_f32", scales={"halt_w": 0.05, "halt_b": -0.8})
+    n = cfg["n_loops"]
+    r = O.recurrent_forward_act_skip(cfg, P, e, h0, n, cfg["act_threshold"], record=True)
+    N = e.shape[0] * e.shape[1]
+    counts = r["halt_counts"].ravel()
+    assert len(np.unique(counts)) > 1
+    ps = {}
+    for t, (idx, p) in enumerate(r["record"]["p"]):
+        assert np.all(counts[idx] > t)                 # only running positions run
+        for m, nn in enumerate(idx):
+            ps.setdefault(int(nn), []).append(p[m])
+    thr = np.float32(cfg["act_threshold"])
+    for nn in range(N):
+        seq = ps[nn]
+        assert len(seq) == counts[nn]
+        cum = np.float32(0)
+        want = n
+        for t, pv in enumerate(seq):
+            if np.float32(cum + np.float32(pv)) >= thr:
+                want = t + 1
+                break
+            cum = np.float32(cum + np.float32(pv))
+        assert counts[nn] == want
+        wsum = sum(seq[:-1]) + max(1.0 - sum(seq[:-1]), 0.0)
+        assert abs(wsum - 1.0) < 1e-12
