@@ -97,6 +97,24 @@ def measured_traffic(config):
         return None
 
 
+def sample_sclk(stop, out):
+    """GPU core clock (MHz) read with rocm-smi every ~0.2 s until `stop` is
+    set (the sustained clock under load; MFMA-heavy phases run below the
+    2.4 GHz peak clock)."""
+    import re
+    import subprocess
+    while not stop.is_set():
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                               text=True, timeout=10)
+            m = re.search(r"sclk clock level:\s*\S+:?\s*\((\d+)Mhz\)", r.stdout)
+            if m:
+                out.append(int(m.group(1)))
+        except (OSError, subprocess.SubprocessError):
+            return
+        stop.wait(0.2)
+
+
 def cpu_baseline(cfg, W, e, h0, prefix):
     """The fp64 oracle as it stands, on the first `prefix` tokens of each
     sequence for one loop (causal attention and per-token routing make this
@@ -122,6 +140,9 @@ def main():
     ap.add_argument("--config", default="mythos_3b")
     ap.add_argument("--cpu-prefix", type=int, default=4096)   # 3b: one whole loop of the workload
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--act-skip", action="store_true",
+                    help="ACT with compute skipping (halted positions leave the batch; "
+                         "rdt_recurrent_forward_act_skip); value = token-loops actually run per second")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run plain device copies of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -166,8 +187,15 @@ def main():
         kv = torch.zeros(blk.kv_cache_bytes(B, cap, n_loops), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
+    if args.act_skip and (thr <= 0 or cfg["use_cache"]):
+        print("--act-skip needs a prefill workload with ACT on", file=sys.stderr)
+        sys.exit(2)
+
     def step():
-        blk.forward(et, ht, n_loops, thr, cfg["start_pos"], kv, cap, ws, h_out, hc)
+        if args.act_skip:
+            blk.forward_act_skip(et, ht, n_loops, thr, cfg["start_pos"], ws, h_out, hc)
+        else:
+            blk.forward(et, ht, n_loops, thr, cfg["start_pos"], kv, cap, ws, h_out, hc)
 
     for i in range(args.warmup):
         step()
@@ -177,12 +205,22 @@ def main():
     # event records per launch on the stream; timing every stage costs ~2.5%)
     dom = "expert_gate_up"
     blk.set_timing_stages([dom])
+    import threading
+    clocks, stop = [], threading.Event()
+    sampler = threading.Thread(target=sample_sclk, args=(stop, clocks), daemon=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
+    sampler.start()
     t0 = time.perf_counter()
+    ev[0].record(stream)
     for i in range(args.steps):
         step()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    stop.set()
+    sampler.join(timeout=15)
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     dom_timing = blk.read_timing()[dom]
     # per-stage breakdown from one more step with every stage timed
     blk.set_timing(True)
@@ -198,13 +236,24 @@ def main():
     # position has halted, i.e. after max(halt_counts) loops
     loops_exec = int(halt.max()) if (thr > 0 and not cfg["use_cache"]) else n_loops
     ms_step = elapsed / args.steps * 1e3
-    value = B * T * loops_exec * args.steps / elapsed
+    if args.act_skip:
+        # every position runs exactly its halt count of loops
+        value = float(halt.sum()) * args.steps / elapsed
+    else:
+        value = B * T * loops_exec * args.steps / elapsed
 
     E = cfg["n_experts"]
     offs = blk.workspace_view(ws, B, T, "offsets", torch.int32, (E + 1,)).cpu().numpy()
     counts = np.diff(offs)
     touched = int(np.sum(counts > 0))
     work = stage_work(cfg, touched)
+    if args.act_skip:
+        # per-launch work averaged over the loops: loop t runs the positions
+        # whose halt count exceeds t
+        rows_t = [int(np.sum(halt > t)) for t in range(loops_exec)]
+        frac_rows = float(np.mean(rows_t)) / (B * T)
+        work = stage_work(dict(cfg, seq=max(1, int(round(T * frac_rows)))), touched)
+        log(f"[bench] act-skip rows per loop: {rows_t}")
     kernels = {}
     # milliseconds per step of each stage (the dominant one was timed over
     # args.steps steps, the others over one)
@@ -260,11 +309,14 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "token·loops/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 3), "ms_per_step_min": round(step_ms[0], 3),
+        "sclk_mhz_samples": clocks,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
         "data": "synthetic (seeded N(0,0.02) weights, RMS-normalised N(0,1) inputs)",
         "config": {"workload": f"{args.config}-shaped recurrent block, {cfg['dtype']} "
                                f"{'decode' if cfg['use_cache'] else 'prefill'}, batch {B} x seq {T}, "
-                               f"{n_loops} loops, ACT {'off' if thr == 0 else thr}",
+                               f"{n_loops} loops, ACT {'off' if thr == 0 else thr}"
+                               f"{' with compute skipping' if args.act_skip else ''}",
                    "dim": D, "heads": cfg["n_heads"], "kv_heads": cfg["n_kv_heads"], "experts": cfg["n_experts"],
                    "expert_dim": cfg["expert_dim"], "top_k": cfg["top_k"], "loops_executed": loops_exec},
         "useful_token_loops_per_s": round(float(halt.sum()) * args.steps / elapsed, 1),

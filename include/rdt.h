@@ -6,6 +6,8 @@
  *   [ZS] "OpenMythos 분석: Mythos Preview의 장기 추론 성능과 OpenMythos의 계산 모델링"
  *        (zero.shotlearni.ng)
  *   [RC] "OpenMythos" (runchr.com, Korean copy of the project README)
+ *   [GN] "[GeekNews 요약] OpenMythos: Claude Mythos 아키텍처를 역설계한 오픈소스
+ *        Recurrent-Depth Transformer 구현" (aisleshub.com)
  *
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers, caller-owned, row-major,
@@ -162,6 +164,28 @@ rdt_status rdt_recurrent_forward(rdt_block* blk, const float* e, const float* h0
                                  void* kv_cache, int32_t kv_capacity, size_t kv_bytes,
                                  void* workspace, size_t ws_bytes,
                                  float* h_out, int32_t* halt_counts, void* stream);
+
+/* ACT with compute skipping ([GN §6]: continuous depth-wise batching, a
+ * halted position leaves the batch).  Same arguments and outputs as
+ * rdt_recurrent_forward without a cache, ACT on (act_threshold in (0, 1]),
+ * GQA attention.  Loop t runs the block only on the positions that have not
+ * halted before it; a halted position's state freezes, and in later loops
+ * the running positions attend to the keys and values it had in the last
+ * loop it ran (the reading these pages leave open: its K/V freeze with it).
+ * With nothing halting before the last loop the result equals
+ * rdt_recurrent_forward's.  The loop stops once no position runs.
+ * The call synchronises `stream` once per loop after the first (the host
+ * reads the running count to size that loop's launches), so it returns
+ * after the last loop's kernels are enqueued.  The capture buffers, when
+ * set, receive loop t's values only at the positions that ran it.
+ * Errors: those of rdt_recurrent_forward; INVALID_ARG if act_threshold is
+ * 0; UNSUPPORTED for MLA attention.
+ * Source: [GN] "[GeekNews 요약] OpenMythos: …" (aisleshub.com), section 6
+ * (deployment: depth-wise batching); ACT rule of [ZS §Recurrent Block]. */
+rdt_status rdt_recurrent_forward_act_skip(rdt_block* blk, const float* e, const float* h0, int32_t B, int32_t T,
+                                          int32_t start_pos, int32_t n_loops, float act_threshold,
+                                          void* workspace, size_t ws_bytes, float* h_out, int32_t* halt_counts,
+                                          void* stream);
 
 /* One generation step of the recurrent stage ([ZS §RoPE & generation
  * cache]): each of B sequences brings one new token at absolute position

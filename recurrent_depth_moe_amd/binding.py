@@ -73,6 +73,7 @@ def lib():
         "rdt_workspace_offset": ([vp, i32, i32, ctypes.c_char_p, ctypes.POINTER(sz), ctypes.POINTER(sz)], i32),
         "rdt_recurrent_forward": ([vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, sz, vp, sz, vp, vp, vp], i32),
         "rdt_decode_step": ([vp, vp, vp, i32, i32, i32, f32, vp, i32, sz, vp, sz, vp, vp, vp], i32),
+        "rdt_recurrent_forward_act_skip": ([vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp, vp, vp], i32),
         "rdt_get_A": ([vp, vp], i32),
         "rdt_set_capture": ([vp, vp, vp, vp, i32], i32),
         "rdt_set_timing": ([vp, i32], i32),
@@ -224,6 +225,21 @@ class Block:
                                           float(act_threshold), _ptr(kv_cache), kv_capacity, kvb,
                                           _ptr(workspace), workspace.numel(), _ptr(h_out), _ptr(halt_counts),
                                           _stream(stream)))
+        return h_out, halt_counts
+
+    def forward_act_skip(self, e, h0, n_loops, act_threshold, start_pos=0, workspace=None, h_out=None,
+                         halt_counts=None, stream=None):
+        """ACT with compute skipping (rdt_recurrent_forward_act_skip)."""
+        B, T, D = e.shape
+        if workspace is None:
+            workspace = self.new_workspace(B, T)
+        if h_out is None:
+            h_out = torch.empty_like(e)
+        if halt_counts is None:
+            halt_counts = torch.empty((B, T), dtype=torch.int32, device=e.device)
+        check(lib().rdt_recurrent_forward_act_skip(self._h, _ptr(e), _ptr(h0), B, T, start_pos, n_loops,
+                                                   float(act_threshold), _ptr(workspace), workspace.numel(),
+                                                   _ptr(h_out), _ptr(halt_counts), _stream(stream)))
         return h_out, halt_counts
 
     def decode_step(self, e_new, h0_new, start_pos, n_loops, act_threshold, kv_cache, kv_capacity,

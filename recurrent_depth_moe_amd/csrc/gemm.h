@@ -31,6 +31,9 @@ struct EpiParams {
   const float* rcos;  // RoPE tables [position][rot_half]
   const float* rsin;
   int rot_half;
+  // EPI_QKV with ACT compute skipping: output row m is sequence position
+  // tok[m] (b = tok[m] / T, i = tok[m] % T); null: row m is position m
+  const int32_t* tok;
 };
 
 struct GemmParams {

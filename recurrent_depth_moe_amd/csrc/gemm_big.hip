@@ -527,18 +527,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
                 const int ml = wm * WTM + pass * 32 + rg * 8;
                 const int n = n0 + wn * WTN + c;
                 if (ml >= rows || n >= p.N) continue;
-                const int m = row0 + ml, b = m / e.T, i = m - b * e.T;
+                const int m = row0 + ml, mp = e.tok ? e.tok[m] : m, b = mp / e.T, i = mp - b * e.T;
                 const int nn = n - hqk, g = nn / e.dv, d = nn - g * e.dv;
                 TO* col = (TO*)e.vt + ((int64_t)(b * e.G + g) * e.dv + d) * e.cap + e.kbase + i;
                 float v[8];
 #pragma unroll
                 for (int x = 0; x < 8; ++x) v[x] = ep[(rg * 8 + x) * EP_LD + c];
-                if (ml + 8 <= rows && i + 8 <= e.T && ((e.kbase + i) & 7) == 0) {
+                if (!e.tok && ml + 8 <= rows && i + 8 <= e.T && ((e.kbase + i) & 7) == 0) {
                   store8<EPI, TO>(col, v);
                 } else {
-                  // rows past the tile, a sequence boundary or an unaligned run
+                  // rows past the tile, a sequence boundary, an unaligned run
+                  // or positions from a map
                   for (int x = 0; x < 8 && ml + x < rows; ++x) {
-                    const int mx = m + x, bx = mx / e.T, ix = mx - bx * e.T;
+                    const int mx = e.tok ? e.tok[m + x] : m + x, bx = mx / e.T, ix = mx - bx * e.T;
                     St<TO>::st((TO*)e.vt + ((int64_t)(bx * e.G + g) * e.dv + d) * e.cap + e.kbase + ix, v[x]);
                   }
                 }

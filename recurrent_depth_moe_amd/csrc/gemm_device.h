@@ -14,7 +14,8 @@ static __device__ __forceinline__ void epi_store(const EpiParams& e, int m, int 
   } else if constexpr (EPI == EPI_SWIGLU) {
     St<TO>::st((TO*)e.out + (int64_t)m * e.ldo + n, silu_f(v) * v2);
   } else if constexpr (EPI == EPI_QKV) {
-    const int b = m / e.T, i = m - b * e.T;
+    const int mp = e.tok ? e.tok[m] : m;
+    const int b = mp / e.T, i = mp - b * e.T;
     const int hq = e.H * e.dq, hk = e.G * e.dq;
     if (n < hq + hk) {
       // adjacent channels (2j, 2j+1) are one complex number; v2 holds the
@@ -133,7 +134,8 @@ static __device__ __forceinline__ void epi_store8(const EpiParams& e, int N, int
                         r1.x + v[4], r1.y + v[5], r1.z + v[6], r1.w + v[7]};
     store8<EPI, float>((float*)e.out + i, o);
   } else if constexpr (EPI == EPI_QKV) {
-    const int b = m / e.T, i = m - b * e.T;
+    const int mp = e.tok ? e.tok[m] : m;
+    const int b = mp / e.T, i = mp - b * e.T;
     const int hq = e.H * e.dq, hk = e.G * e.dq;
     if (n < hq + hk) {
       const int d = n % e.dq;

@@ -14,9 +14,14 @@ void launch_make_loop_table(float* emb, int n_loops_max, int loop_dim, double th
 void launch_make_A(const float* log_A, const float* log_dt, float* A, int D, hipStream_t s);
 
 // c = RMSNorm(h + emb_t + e) * g_rec (fp32); a = RMSNorm(c) * g_attn (bf16 or fp32)
+// Row n of c and a reads position tok[n] of h and e (tok null: position n).
 void launch_loop_head(int act_bf16, const float* h, const float* e, const float* emb_t, int loop_dim,
                       const float* g_rec, const float* g_attn, float eps, float* c, void* a, int N, int D,
-                      hipStream_t s, const int32_t* live_prev = nullptr, int32_t* live_cur = nullptr);
+                      hipStream_t s, const int32_t* live_prev = nullptr, int32_t* live_cur = nullptr,
+                      const int32_t* tok = nullptr);
+// ACT compute skipping: tok[0 .. count) = the positions whose halt count is
+// still 0 (running), in ascending order; *count written on the device.
+void launch_compact_running(const int32_t* halt_counts, int N, int32_t* tok, int32_t* count, hipStream_t s);
 // out[r] = RMSNorm(x[r]) * g for rows r < rows; x fp32 with row stride ldx,
 // out (bf16 or fp32) with stride ldo
 void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, float eps, void* out, int64_t ldo,
@@ -24,8 +29,11 @@ void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, f
 
 // softmax over E logits, top-k of logits + bias (descending, ties to the
 // lower index), gates renormalised over the chosen experts
+// (cap_sel, when set, receives row n's choice at position tok[n]; tok null:
+// position n)
 void launch_router_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* sel, float* gate,
-                        int32_t* cap_sel, hipStream_t s, const int32_t* live = nullptr);
+                        int32_t* cap_sel, hipStream_t s, const int32_t* live = nullptr,
+                        const int32_t* tok = nullptr);
 // dropless dispatch: stable order (token, slot) inside each expert
 // (also zeroes the n_claim tile-claim counters the grouped products of the
 // same loop draw from, n_claim <= RDT_MAX_EXPERTS).  With merge_extra > 0 a
@@ -66,6 +74,11 @@ struct TailArgs {
   int w_bf16;
   const int32_t* live_prev;  // running positions after loop t-1, or null (never skip)
   int32_t* live_cur;         // running positions after this loop are added here, or null
+  // ACT compute skipping: the N rows are the running positions only, row n
+  // is position tok[n] (null: row n is position n).  x1, y, inv, gate and
+  // y_s are per row; e, h_prev, h_next, h_out, cum, halt_counts, cap_h and
+  // cap_p are per position.
+  const int32_t* tok;
 };
 void launch_loop_tail(const TailArgs& a, hipStream_t s);
 

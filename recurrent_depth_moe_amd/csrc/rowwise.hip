@@ -71,13 +71,15 @@ __global__ __launch_bounds__(RB) void loop_head_kernel(const float* __restrict__
                                                        const float* __restrict__ g_rec,
                                                        const float* __restrict__ g_attn, float eps,
                                                        float* __restrict__ c, TA* __restrict__ a, int D,
-                                                       const int32_t* live_prev, int32_t* live_cur) {
+                                                       const int32_t* live_prev, int32_t* live_cur,
+                                                       const int32_t* __restrict__ tok) {
   // this loop's running count starts at 0 (the tail adds to it), also when
   // the loop itself is skipped, so a skip carries on to every later loop
   if (live_cur && blockIdx.x == 0 && threadIdx.x == 0) *live_cur = 0;
   RDT_SKIP_IF_ALL_HALTED(live_prev);
   __shared__ float red[RB / 64];
-  const int64_t base = (int64_t)blockIdx.x * D;
+  const int64_t base = (int64_t)blockIdx.x * D;                                   // rows of c, a
+  const int64_t pbase = (int64_t)(tok ? tok[blockIdx.x] : (int)blockIdx.x) * D;   // position of h, e
   const int D4 = D >> 2;
   float4 v[MAXV4], y[MAXV4], m[MAXV4];
   // every load first (the loop embedding from a clamped, always valid
@@ -87,8 +89,8 @@ __global__ __launch_bounds__(RB) void loop_head_kernel(const float* __restrict__
     const int i4 = threadIdx.x + j * RB;
     if (NJ || i4 < D4) {
       const int d = i4 * 4;
-      v[j] = ld4(h + base + d);
-      y[j] = ld4(e + base + d);
+      v[j] = ld4(h + pbase + d);
+      y[j] = ld4(e + pbase + d);
       if (loop_dim > 0) m[j] = ld4(emb + min(d, loop_dim - 4));
     }
   }
@@ -200,7 +202,8 @@ template <int EPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
                                                           const float* __restrict__ bias, int N, int E, int k,
                                                           int32_t* __restrict__ sel, float* __restrict__ gate,
-                                                          int32_t* __restrict__ cap_sel, const int32_t* live) {
+                                                          int32_t* __restrict__ cap_sel, const int32_t* live,
+                                                          const int32_t* __restrict__ tok) {
   RDT_SKIP_IF_ALL_HALTED(live);
   const int l16 = threadIdx.x & 15;
   const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     for (int kk = 0; kk < k; ++kk) {
       sel[(int64_t)row * k + kk] = idx[kk];
       gate[(int64_t)row * k + kk] = num[kk] / den;
-      if (cap_sel) cap_sel[(int64_t)row * k + kk] = idx[kk];
+      if (cap_sel) cap_sel[(int64_t)(tok ? tok[row] : row) * k + kk] = idx[kk];
     }
   }
 }
@@ -429,7 +432,9 @@ __global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
   __shared__ float red[RDT_MAX_LORA + 1][RB / 64];
   const int n = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int D = a.D, D4 = D >> 2;
-  const int64_t base = (int64_t)n * D;
+  const int64_t base = (int64_t)n * D;                    // per-row tensors
+  const int np = a.tok ? a.tok[n] : n;                    // this row's position
+  const int64_t pbase = (int64_t)np * D;                  // per-position tensors
   const TW* Wd = (const TW*)a.lora_down;
   const TW* Wb = (const TW*)a.lora_B;
 
@@ -487,15 +492,15 @@ __global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
 #pragma unroll
       for (int r = 0; r < RDT_MAX_LORA; ++r)
         if (r < a.r) x = fma4(lo[r], ld4(Wb + (int64_t)r * D + d), x);
-      const float4 A = ld4(a.A + d), Bv = ld4(a.Bv + d), hp = ld4(a.h_prev + base + d), ee = ld4(a.e + base + d);
+      const float4 A = ld4(a.A + d), Bv = ld4(a.Bv + d), hp = ld4(a.h_prev + pbase + d), ee = ld4(a.e + pbase + d);
       float4 hn;
       hn.x = A.x * hp.x + Bv.x * ee.x + x.x;
       hn.y = A.y * hp.y + Bv.y * ee.y + x.y;
       hn.z = A.z * hp.z + Bv.z * ee.z + x.z;
       hn.w = A.w * hp.w + Bv.w * ee.w + x.w;
       tau[j] = hn;
-      st4(a.h_next + base + d, hn);
-      if (a.cap_h) st4(a.cap_h + base + d, hn);
+      st4(a.h_next + pbase + d, hn);
+      if (a.cap_h) st4(a.cap_h + pbase + d, hn);
       zs += dot4(hn, ld4(a.halt_w + d));
     }
   }
@@ -506,16 +511,16 @@ __global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
 #pragma unroll
       for (int j = 0; j < MAXV4; ++j) {
         const int i4 = threadIdx.x + j * RB;
-        if (i4 < D4) st4(a.h_out + base + i4 * 4, tau[j]);
+        if (i4 < D4) st4(a.h_out + pbase + i4 * 4, tau[j]);
       }
     }
-    if (threadIdx.x == 0) a.halt_counts[n] = a.t + 1;
+    if (threadIdx.x == 0) a.halt_counts[np] = a.t + 1;
     return;
   }
   const float z = block_sum(zs, &red[RDT_MAX_LORA][0]) + a.halt_b[0];
   const float p = sigmoid_f(z);
-  const float cum = a.t == 0 ? 0.f : a.cum[n];
-  const int hc = a.t == 0 ? 0 : a.halt_counts[n];
+  const float cum = a.t == 0 ? 0.f : a.cum[np];
+  const int hc = a.t == 0 ? 0 : a.halt_counts[np];
   const bool running = hc == 0;
   float wgt = 0.f;
   bool halt_now = false;
@@ -530,16 +535,16 @@ __global__ __launch_bounds__(RB) void loop_tail_kernel(TailArgs a) {
       const int i4 = threadIdx.x + j * RB;
       if (i4 < D4) {
         const int d = i4 * 4;
-        const float4 prev = a.t == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : ld4(a.h_out + base + d);
-        st4(a.h_out + base + d, fma4(wgt, tau[j], prev));
+        const float4 prev = a.t == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : ld4(a.h_out + pbase + d);
+        st4(a.h_out + pbase + d, fma4(wgt, tau[j], prev));
       }
     }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    a.cum[n] = running ? cum + p : cum;
-    a.halt_counts[n] = halt_now ? a.t + 1 : hc;
-    if (a.cap_p) a.cap_p[n] = p;
+    a.cum[np] = running ? cum + p : cum;
+    a.halt_counts[np] = halt_now ? a.t + 1 : hc;
+    if (a.cap_p) a.cap_p[np] = p;
     if (a.live_cur && running && !halt_now) atomicAdd(a.live_cur, 1);
   }
 }
@@ -642,7 +647,7 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
       const float4 A = ld4(a.A + d), Bv = ld4(a.Bv + d), hw = ld4(a.halt_w + d);
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const int64_t off = (int64_t)(n0 + i) * D + d;
+        const int64_t off = (int64_t)(a.tok ? a.tok[n0 + i] : n0 + i) * D + d;   // position
         const float4 hp = ld4(a.h_prev + off), ee = ld4(a.e + off), x = tau[i][j];
         float4 hn;
         hn.x = A.x * hp.x + Bv.x * ee.x + x.x;
@@ -665,10 +670,10 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const int i4 = threadIdx.x + j * RB;
-          if (i4 < D4) st4(a.h_out + (int64_t)(n0 + i) * D + i4 * 4, tau[i][j]);
+          if (i4 < D4) st4(a.h_out + (int64_t)(a.tok ? a.tok[n0 + i] : n0 + i) * D + i4 * 4, tau[i][j]);
         }
     }
-    if (threadIdx.x < R) a.halt_counts[n0 + threadIdx.x] = a.t + 1;
+    if (threadIdx.x < R) a.halt_counts[a.tok ? a.tok[n0 + threadIdx.x] : n0 + threadIdx.x] = a.t + 1;
     return;
   }
   __syncthreads();   // red reused
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(RB) void loop_tail_rows_kernel(TailArgs a) {
   int still = 0;   // rows of this block still running after this loop
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const int n = n0 + i;
+    const int n = a.tok ? a.tok[n0 + i] : n0 + i;   // position of row n0 + i
     float z = a.halt_b[0];
     for (int ww = 0; ww < RB / 64; ++ww) z += red[ww][LR * R + i];
     const float p = sigmoid_f(z);
@@ -735,12 +740,22 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
   const int D = a.D, k = a.k;
   const bf16_t* Wd = (const bf16_t*)a.lora_down;
   const bf16_t* Wb = (const bf16_t*)a.lora_B;
+  // row n0 + i (rows past N, in a last block of a row count that is not a
+  // multiple of R, load row N - 1 and store nothing) and its position
+  int nr[R], np[R];
+  bool valid[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    valid[i] = n0 + i < a.N;
+    nr[i] = valid[i] ? n0 + i : a.N - 1;
+    np[i] = a.tok ? a.tok[nr[i]] : nr[i];
+  }
   // source rows: the k routed slots (gate-weighted), then the S shared experts
   const bf16_t* src[R][NS];
   float wt[R][NS];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const int n = n0 + i;
+    const int n = nr[i];
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
       if (q < k) {
@@ -759,7 +774,7 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int d = (threadIdx.x + j * RB) * 4;
-      v[j][0] = ld4(a.x1 + (int64_t)(n0 + i) * D + d);
+      v[j][0] = ld4(a.x1 + (int64_t)nr[i] * D + d);
 #pragma unroll
       for (int q = 0; q < NS; ++q) v[j][q + 1] = ld4(src[i][q] + d);
     }
@@ -822,14 +837,14 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
     float4 hp[NJ], ee[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int64_t off = (int64_t)(n0 + i) * D + (threadIdx.x + j * RB) * 4;
+      const int64_t off = (int64_t)np[i] * D + (threadIdx.x + j * RB) * 4;
       hp[j] = ld4(a.h_prev + off);
       ee[j] = ld4(a.e + off);
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int d = (threadIdx.x + j * RB) * 4;
-      const int64_t off = (int64_t)(n0 + i) * D + d;
+      const int64_t off = (int64_t)np[i] * D + d;
       const float4 A = ld4(a.A + d), Bv = ld4(a.Bv + d), x = tau[i][j];
       float4 hn;
       hn.x = A.x * hp[j].x + Bv.x * ee[j].x + x.x;
@@ -837,8 +852,10 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
       hn.z = A.z * hp[j].z + Bv.z * ee[j].z + x.z;
       hn.w = A.w * hp[j].w + Bv.w * ee[j].w + x.w;
       tau[i][j] = hn;
-      st4(a.h_next + off, hn);
-      if (a.cap_h) st4(a.cap_h + off, hn);
+      if (valid[i]) {
+        st4(a.h_next + off, hn);
+        if (a.cap_h) st4(a.cap_h + off, hn);
+      }
       zs[i] += dot4(hn, ld4(a.halt_w + d));
     }
   }
@@ -848,11 +865,14 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
     if (last) {
 #pragma unroll
       for (int i = 0; i < R; ++i)
+        if (valid[i])
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          st4(a.h_out + (int64_t)(n0 + i) * D + (threadIdx.x + j * RB) * 4, tau[i][j]);
+          for (int j = 0; j < NJ; ++j)
+            st4(a.h_out + (int64_t)np[i] * D + (threadIdx.x + j * RB) * 4, tau[i][j]);
     }
-    if (threadIdx.x < R) a.halt_counts[n0 + threadIdx.x] = a.t + 1;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (threadIdx.x == i && valid[i]) a.halt_counts[np[i]] = a.t + 1;
     return;
   }
   // ACT: halting logit of every row (block sum), then the decisions
@@ -867,14 +887,14 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
   bool run[R], halt[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const int n = n0 + i;
+    const int n = np[i];
     float z = a.halt_b[0];
 #pragma unroll
     for (int ww = 0; ww < RB / 64; ++ww) z += red[ww][RDT_MAX_LORA * R + i];
     pv[i] = sigmoid_f(z);
     cumv[i] = a.t == 0 ? 0.f : a.cum[n];
     hcv[i] = a.t == 0 ? 0 : a.halt_counts[n];
-    run[i] = hcv[i] == 0;
+    run[i] = hcv[i] == 0 && valid[i];
     halt[i] = false;
     float wgt = 0.f;
     if (run[i]) {
@@ -896,8 +916,8 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
   int still = 0;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    if (threadIdx.x == i) {
-      const int n = n0 + i;
+    if (threadIdx.x == i && valid[i]) {
+      const int n = np[i];
       a.cum[n] = run[i] ? cumv[i] + pv[i] : cumv[i];
       a.halt_counts[n] = halt[i] ? a.t + 1 : hcv[i];
       if (a.cap_p) a.cap_p[n] = pv[i];
@@ -905,6 +925,36 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
     still += (run[i] && !halt[i]) ? 1 : 0;
   }
   if (a.live_cur && threadIdx.x == 0 && still > 0) atomicAdd(a.live_cur, still);
+}
+
+// ------------------------------------------------------------ compaction
+// ACT compute skipping: the positions still running (halt count 0) in
+// ascending order, by one block: each wave ballots its 64 positions, the
+// wave totals are scanned in LDS, and the block walks N in 1024-position
+// chunks carrying the running offset.
+__global__ __launch_bounds__(1024) void compact_running_kernel(const int32_t* __restrict__ halt_counts, int N,
+                                                               int32_t* __restrict__ tok, int32_t* __restrict__ count) {
+  __shared__ int wtot[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int base = 0;
+  for (int c0 = 0; c0 < N; c0 += 1024) {
+    const int n = c0 + threadIdx.x;
+    const bool run = n < N && halt_counts[n] == 0;
+    const uint64_t m = __ballot(run);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wtot[w] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    int total = 0;
+    for (int j = 0; j < 16; ++j) {
+      if (j < w) off += wtot[j];
+      total += wtot[j];
+    }
+    if (run) tok[off + before] = n;
+    base += total;
+    __syncthreads();   // wtot is rewritten by the next chunk
+  }
+  if (threadIdx.x == 0) *count = base;
 }
 
 // ------------------------------------------------------------ MLA glue
@@ -1063,9 +1113,10 @@ void launch_make_A(const float* log_A, const float* log_dt, float* A, int D, hip
 
 void launch_loop_head(int act_bf16, const float* h, const float* e, const float* emb_t, int loop_dim,
                       const float* g_rec, const float* g_attn, float eps, float* c, void* a, int N, int D,
-                      hipStream_t s, const int32_t* live_prev, int32_t* live_cur) {
+                      hipStream_t s, const int32_t* live_prev, int32_t* live_cur, const int32_t* tok) {
 #define RDT_LOOP_HEAD(TA, NJ) \
-  loop_head_kernel<TA, NJ><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (TA*)a, D, live_prev, live_cur)
+  loop_head_kernel<TA, NJ><<<N, RB, 0, s>>>(h, e, emb_t, loop_dim, g_rec, g_attn, eps, c, (TA*)a, D, live_prev, \
+                                            live_cur, tok)
   const int nj = D % (4 * RB) == 0 ? D / (4 * RB) : 0;
   if (act_bf16) {
     switch (nj) {
@@ -1099,13 +1150,13 @@ void launch_rmsnorm(int out_bf16, const float* x, int64_t ldx, const float* g, f
 }
 
 void launch_router_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* sel, float* gate,
-                        int32_t* cap_sel, hipStream_t s, const int32_t* live) {
+                        int32_t* cap_sel, hipStream_t s, const int32_t* live, const int32_t* tok) {
   const dim3 grid((N + 15) / 16);
-  if (E <= 16) router_topk_kernel<1><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
-  else if (E <= 32) router_topk_kernel<2><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
-  else if (E <= 64) router_topk_kernel<4><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
-  else if (E <= 128) router_topk_kernel<8><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
-  else router_topk_kernel<16><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live);
+  if (E <= 16) router_topk_kernel<1><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live, tok);
+  else if (E <= 32) router_topk_kernel<2><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live, tok);
+  else if (E <= 64) router_topk_kernel<4><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live, tok);
+  else if (E <= 128) router_topk_kernel<8><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live, tok);
+  else router_topk_kernel<16><<<grid, 256, 0, s>>>(logits, bias, N, E, k, sel, gate, cap_sel, live, tok);
 }
 
 void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* tile_counts, int32_t* offsets,
@@ -1135,7 +1186,7 @@ static void launch_tail_rows(const TailArgs& a, int nj, hipStream_t s) {
 
 template <int NJ, int R>
 static bool launch_tail_fast_nj(const TailArgs& a, int ns, hipStream_t s) {
-  const int grid = a.N / R;
+  const int grid = (a.N + R - 1) / R;
   switch (ns) {
     case 1: loop_tail_fast_kernel<R, NJ, 1><<<grid, RB, 0, s>>>(a); return true;
     case 2: loop_tail_fast_kernel<R, NJ, 2><<<grid, RB, 0, s>>>(a); return true;
@@ -1147,10 +1198,10 @@ static bool launch_tail_fast_nj(const TailArgs& a, int ns, hipStream_t s) {
 
 void launch_loop_tail(const TailArgs& a, hipStream_t s) {
   // batched form: bf16 LoRA, whole float4 columns per thread (D a multiple
-  // of 4 RB, at most 4 of them), 4-row blocks (1-row ones below 1024 rows),
-  // k + S <= 4, rank a multiple of 4 up to 16
-  if (a.w_bf16 && (a.N % 4 == 0 || a.N < 1024) && a.D % (4 * RB) == 0 && a.D <= 16 * RB && a.r % 4 == 0 && a.r <= 16 &&
-      a.r > 0) {
+  // of 4 RB, at most 4 of them), 4-row blocks (1-row ones below 1024 rows;
+  // a ragged last block masks its extra rows), k + S <= 4, rank a multiple
+  // of 4 up to 16
+  if (a.w_bf16 && a.D % (4 * RB) == 0 && a.D <= 16 * RB && a.r % 4 == 0 && a.r <= 16 && a.r > 0) {
     const int ns = a.k + a.S;
     bool ok = false;
     // one row per block when four-row blocks would leave most CUs idle
@@ -1209,4 +1260,8 @@ void launch_mla_kv_prep(int act_bf16, const void* lat_ckv, const void* lat_krope
     mla_kv_prep_kernel<float><<<B * kvlen, 64, 0, s>>>((const float*)lat_ckv, (const float*)lat_krope, lat_cap,
                                                        gkv, eps, kvlen, kvl, rope, H, dq, (float*)ckv_norm,
                                                        (float*)K, live);
+}
+
+void launch_compact_running(const int32_t* halt_counts, int N, int32_t* tok, int32_t* count, hipStream_t s) {
+  compact_running_kernel<<<1, 1024, 0, s>>>(halt_counts, N, tok, count);
 }

@@ -110,14 +110,14 @@ enum WsId {
   WS_H, WS_C, WS_A, WS_Q, WS_K, WS_VT, WS_O, WS_X1, WS_F, WS_LOGITS, WS_SEL, WS_GATE, WS_TILECNT, WS_OFFSETS,
   WS_MTSTART, WS_TROW0, WS_TGRP, WS_PERM, WS_INV, WS_ACT, WS_Y, WS_ACTS, WS_YS, WS_CUM,
   WS_KVRAW, WS_CQRAW, WS_CQN, WS_LATC, WS_LATR, WS_CKVN, WS_DPART, WS_LIVE, WS_TCLAIM,
-  WS_QLAT, WS_KLAT, WS_VLAT, WS_OLAT, WS_MTSTART_M, WS_TROW0_M, WS_TGRP_M, WS_COUNT
+  WS_QLAT, WS_KLAT, WS_VLAT, WS_OLAT, WS_MTSTART_M, WS_TROW0_M, WS_TGRP_M, WS_TOK, WS_NRUN, WS_COUNT
 };
 const char* kWsNames[WS_COUNT] = {"h", "c", "a", "q", "k", "vt", "o", "x1", "f", "logits", "sel", "gate",
                                   "tile_counts", "offsets", "mt_start", "tile_row0", "tile_grp", "perm", "inv",
                                   "act", "y", "act_s", "y_s", "cum", "kv_raw", "cq_raw", "cq_norm", "lat_ckv",
                                   "lat_krope", "ckv_norm", "attn_part", "live",
                                   "tile_claim", "q_lat", "k_lat", "vt_lat", "o_lat", "mt_start_merged",
-                                  "tile_row0_merged", "tile_grp_merged"};
+                                  "tile_row0_merged", "tile_grp_merged", "tok", "n_running"};
 
 // Prefill with bf16 weights runs the routed down product on 192-column
 // tiles of the large kernel when dim is a multiple of 192; those tiles also
@@ -208,6 +208,8 @@ Plan make_plan(const rdt_config& c, int B, int T) {
   if (use_decode_attn(c, T)) s[WS_DPART] = attn_decode_part_floats(B, c.n_heads, p.kvlen_max) * 4;
   s[WS_LIVE] = 2 * 4;   // running-position counts of the previous and the current loop
   s[WS_TCLAIM] = 2 * RDT_NUM_XCD * 4;   // tile-claim counters of the two routed products
+  s[WS_TOK] = N * 4;     // ACT compute skipping: running row -> position
+  s[WS_NRUN] = 4;        // and the running count
   if (merged_down_schedule(c, T)) {       // m-tile schedule of the routed down product
     s[WS_MTSTART_M] = (E + 1) * 4;
     s[WS_TROW0_M] = (size_t)p.max_mt * 4;
@@ -672,13 +674,17 @@ rdt_status rdt_read_timing(rdt_block* b, double* total_ms, int64_t* launches) {
 
 static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int T, int start_pos, int n_loops,
                       float thr, void* kv, int kv_capacity, size_t kv_bytes, void* ws, size_t ws_bytes,
-                      float* h_out, int32_t* halt_counts, void* stream, bool decode) {
+                      float* h_out, int32_t* halt_counts, void* stream, bool decode, bool act_skip = false) {
   g_err.clear();
   if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
   const rdt_config& c = b->cfg;
   rdt_status st = check_call(c, e, h0, B, T, start_pos, n_loops, thr, kv, kv_capacity, kv_bytes, ws, ws_bytes,
                              h_out, halt_counts, decode);
   if (st) return st;
+  if (act_skip) {
+    if (!(thr > 0.f)) return fail(RDT_E_INVALID_ARG, "ACT compute skipping needs act_threshold in (0, 1]");
+    if (!is_gqa(c)) return fail(RDT_E_UNSUPPORTED, "ACT compute skipping is built for GQA attention");
+  }
   if (b->cap_loops && n_loops > b->cap_loops)
     return fail(RDT_E_INVALID_ARG, "n_loops %d exceeds the capture buffers (%d loops)", n_loops, b->cap_loops);
   hipStream_t s = (hipStream_t)stream;
@@ -700,7 +706,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   // with ACT on and no cache to fill every kernel of the later loops exits
   // at once: loop t's kernels read the count of positions still running
   // after loop t-1 (two alternating counters in the workspace).
-  int32_t* const live_buf = (thr > 0.f && !kv) ? WI(WS_LIVE) : nullptr;
+  int32_t* const live_buf = (thr > 0.f && !kv && !act_skip) ? WI(WS_LIVE) : nullptr;
   const int32_t* live_prev = nullptr;
   int32_t* live_cur = nullptr;
 
@@ -751,18 +757,22 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     gp.dense_gm = 4;
     return gp;
   };
+  // rows of this loop: every position, or with ACT compute skipping the
+  // positions still running (row m is position tok[m])
+  int Mr = N;
+  const int32_t* tok = nullptr;
   auto shared_experts = [&](hipStream_t on) {
     for (int si = 0; si < c.n_shared_experts; ++si) {
       GemmParams gp = dense(W(WS_F), D, (const char*)b->s_gate + (size_t)si * F * D * es,
-                            (const char*)b->s_up + (size_t)si * F * D * es, N, F, D);
+                            (const char*)b->s_up + (size_t)si * F * D * es, Mr, F, D);
       gp.epi.out = W(WS_ACTS);
       gp.epi.ldo = F;
       {
         StageTimer st_(b, on, RDT_STAGE_SHARED_GATEUP);
         gemm(gp, EPI_SWIGLU, true, bf, false, on);
       }
-      GemmParams gd = dense(W(WS_ACTS), F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, N, D, F);
-      gd.epi.out = (char*)W(WS_YS) + (size_t)si * N * D * es;
+      GemmParams gd = dense(W(WS_ACTS), F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, Mr, D, F);
+      gd.epi.out = (char*)W(WS_YS) + (size_t)si * Mr * D * es;
       gd.epi.ldo = D;
       StageTimer st_(b, on, RDT_STAGE_SHARED_DOWN);
       gemm(gd, EPI_STORE, false, bf, false, on);
@@ -776,6 +786,18 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   hipError_t he = hipSuccess;
 
   for (int t = 0; t < n_loops; ++t) {
+    if (act_skip && t > 0) {
+      // the positions still running after loop t-1 become this loop's rows;
+      // the host reads their count to size the launches
+      launch_compact_running(halt_counts, N, WI(WS_TOK), WI(WS_NRUN), s);
+      int32_t nrun = 0;
+      if ((he = hipMemcpyAsync(&nrun, WI(WS_NRUN), sizeof nrun, hipMemcpyDeviceToHost, s)) != hipSuccess ||
+          (he = hipStreamSynchronize(s)) != hipSuccess)
+        return fail(RDT_E_HIP, "running count: %s", hipGetErrorString(he));
+      if (nrun <= 0) break;
+      Mr = nrun;
+      tok = WI(WS_TOK);
+    }
     const float* hp = t == 0 ? h0 : WF(WS_H);
     live_prev = (live_buf && t > 0) ? live_buf + ((t - 1) & 1) : nullptr;
     live_cur = live_buf ? live_buf + (t & 1) : nullptr;
@@ -783,7 +805,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     {
       StageTimer st_(b, s, RDT_STAGE_LOOP_HEAD);
       launch_loop_head(bf, hp, e, b->loop_emb + (size_t)t * c.loop_dim, c.loop_dim, b->g_rec, b->g_attn, c.norm_eps,
-                     WF(WS_C), W(WS_A), N, D, s, live_prev, live_cur);
+                     WF(WS_C), W(WS_A), Mr, D, s, live_prev, live_cur, tok);
     }
     // a4-a6: attention
     char* kslot = kv ? (char*)kv + slot * t : nullptr;
@@ -792,7 +814,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       void* VT = kv ? (void*)(kslot + (size_t)B * G * cap_pad * dq * es) : W(WS_VT);
       const int cap = kv ? cap_pad : p.kvcap;
       const int kbase = kv ? start_pos : 0;
-      GemmParams gp = dense(W(WS_A), D, b->wqkv, nullptr, N, (H + 2 * G) * dq, D);
+      GemmParams gp = dense(W(WS_A), D, b->wqkv, nullptr, Mr, (H + 2 * G) * dq, D);
       EpiParams& ep = gp.epi;
       ep.q = W(WS_Q);
       ep.k = K;
@@ -808,6 +830,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       ep.rcos = b->rope_cos;
       ep.rsin = b->rope_sin;
       ep.rot_half = dq / 2;
+      ep.tok = tok;
       {
         StageTimer st_(b, s, RDT_STAGE_QKV);
         gemm(gp, EPI_QKV, false, bf);
@@ -878,7 +901,8 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     // a7: x1 = c + o Wo^T
     {
       StageTimer st_(b, s, RDT_STAGE_OPROJ);
-      GemmParams gp = dense(W(WS_O), (int64_t)H * dv, b->wo, nullptr, N, D, H * dv);
+      GemmParams gp = dense(W(WS_O), (int64_t)H * dv, b->wo, nullptr, Mr, D, H * dv);
+      gp.a_rows = tok;   // attention output rows are positions
       gp.epi.out = W(WS_X1);
       gp.epi.ldo = D;
       gp.epi.resid = WF(WS_C);
@@ -887,7 +911,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     // a8: f = RMSNorm(x1) * g_ffn
     {
       StageTimer st_(b, s, RDT_STAGE_FFN_NORM);
-      launch_rmsnorm(bf, WF(WS_X1), D, b->g_ffn, c.norm_eps, W(WS_F), D, N, D, s, live_prev);
+      launch_rmsnorm(bf, WF(WS_X1), D, b->g_ffn, c.norm_eps, W(WS_F), D, Mr, D, s, live_prev);
     }
     if (side) {
       // fork: the side stream starts once f is written; the tail joins it
@@ -901,17 +925,17 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
     // a9: router logits, softmax, top-k
     {
       StageTimer st_(b, s, RDT_STAGE_ROUTER);
-      GemmParams gp = dense(W(WS_F), D, b->router, nullptr, N, E, D);
+      GemmParams gp = dense(W(WS_F), D, b->router, nullptr, Mr, E, D);
       gp.epi.out = W(WS_LOGITS);
       gp.epi.ldo = E;
       gemm(gp, EPI_STORE, false, 0, true);
-      launch_router_topk(WF(WS_LOGITS), b->router_bias, N, E, k, WI(WS_SEL), WF(WS_GATE),
-                         b->cap_sel ? b->cap_sel + (size_t)t * N * k : nullptr, s, live_prev);
+      launch_router_topk(WF(WS_LOGITS), b->router_bias, Mr, E, k, WI(WS_SEL), WF(WS_GATE),
+                         b->cap_sel ? b->cap_sel + (size_t)t * N * k : nullptr, s, live_prev, tok);
     }
     // a10: dispatch
     {
       StageTimer st_(b, s, RDT_STAGE_DISPATCH);
-      launch_dispatch(WI(WS_SEL), p.NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART),
+      launch_dispatch(WI(WS_SEL), Mr * k, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART),
                       WI(WS_TROW0), WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), WI(WS_TCLAIM), 2 * RDT_NUM_XCD, s,
                       live_prev, merged ? 64 : 0, merged ? WI(WS_MTSTART_M) : nullptr,
                       merged ? WI(WS_TROW0_M) : nullptr, merged ? WI(WS_TGRP_M) : nullptr);
@@ -925,7 +949,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gp.W0 = b->w_gate;
       gp.W1 = b->w_up;
       gp.w_stride = (int64_t)F * D;
-      gp.M = p.NK;
+      gp.M = Mr * k;
       gp.N = F;
       gp.K = D;
       gp.mt_start = WI(WS_MTSTART);
@@ -995,7 +1019,8 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       ta.halt_counts = halt_counts;
       ta.t = t;
       ta.n_loops = n_loops;
-      ta.N = N;
+      ta.N = Mr;
+      ta.tok = tok;
       ta.D = D;
       ta.k = k;
       ta.cap_h = b->cap_h ? b->cap_h + (size_t)t * N * D : nullptr;
@@ -1018,6 +1043,13 @@ rdt_status rdt_recurrent_forward(rdt_block* b, const float* e, const float* h0, 
                                  float* h_out, int32_t* halt_counts, void* stream) {
   return run(b, e, h0, B, T, start_pos, n_loops, act_threshold, kv_cache, kv_capacity, kv_bytes, workspace,
              ws_bytes, h_out, halt_counts, stream, false);
+}
+
+rdt_status rdt_recurrent_forward_act_skip(rdt_block* b, const float* e, const float* h0, int32_t B, int32_t T,
+                                          int32_t start_pos, int32_t n_loops, float act_threshold, void* workspace,
+                                          size_t ws_bytes, float* h_out, int32_t* halt_counts, void* stream) {
+  return run(b, e, h0, B, T, start_pos, n_loops, act_threshold, nullptr, 0, 0, workspace, ws_bytes, h_out,
+             halt_counts, stream, false, true);
 }
 
 rdt_status rdt_decode_step(rdt_block* b, const float* e_new, const float* h0_new, int32_t B, int32_t start_pos,

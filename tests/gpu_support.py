@@ -66,7 +66,7 @@ class DeviceRun:
     """One forward (or decode) through the C ABI with per-loop capture."""
 
     def __init__(self, cfg, W, e, h0, n_loops=None, thr=None, start_pos=None, kv=None, capture=True,
-                 decode=False, kv_cap=None):
+                 decode=False, kv_cap=None, act_skip=False):
         import torch
         from recurrent_depth_moe_amd import binding
         self.cfg = cfg
@@ -88,7 +88,9 @@ class DeviceRun:
         self.ws = self.blk.new_workspace(B, T)
         self.kv = kv
         cap = (kv_capacity(cfg) if kv_cap is None else kv_cap) if kv is not None else 0
-        if decode:
+        if act_skip:
+            self.out, self.halt = self.blk.forward_act_skip(self.e, self.h0, n_loops, thr, start_pos, self.ws)
+        elif decode:
             self.out, self.halt = self.blk.decode_step(self.e, self.h0, start_pos, n_loops, thr, kv, cap, self.ws)
         else:
             self.out, self.halt = self.blk.forward(self.e, self.h0, n_loops, thr, start_pos, kv, cap, self.ws)
