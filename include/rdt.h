@@ -202,6 +202,26 @@ rdt_status rdt_decode_step(rdt_block* blk, const float* e_new, const float* h0_n
                            void* workspace, size_t ws_bytes,
                            float* h_out, int32_t* halt_counts, void* stream);
 
+/* rdt_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, arguments and outputs without the workspace,
+ * which comes from a static device array of RDT_NOALLOC_MAX_WORKSPACE bytes
+ * that the library holds on each device until the process ends (its
+ * address is looked up once per device, in rdt_block_create).  The call
+ * allocates nothing and calls no allocating routine.  Every call on one
+ * device shares that array: calls that overlap on one device (on several
+ * streams, or from several threads or handles) race and must be ordered by
+ * the caller.  Nothing in it has to start at zero: each call writes every
+ * part of it it reads.  Errors: those of rdt_decode_step;
+ * WORKSPACE_TOO_SMALL when rdt_workspace_bytes(B, 1) exceeds the array
+ * (32 MiB holds a 4096-wide, 128-expert block at 32 sequences);
+ * BAD_STATE while stage timing is on (timing creates events). */
+#define RDT_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+rdt_status rdt_decode_step_noalloc(rdt_block* blk, const float* e_new, const float* h0_new, int32_t B,
+                                   int32_t start_pos, int32_t n_loops, float act_threshold, void* kv_cache,
+                                   int32_t kv_capacity, size_t kv_bytes, float* h_out, int32_t* halt_counts,
+                                   void* stream);
+
 /* Copies A (fp32, [D]) to host memory, for the rho(A) < 1 check of
  * [RC §사용법] (A is diagonal, so rho(A) = max A_i).  Synchronous. */
 rdt_status rdt_get_A(const rdt_block* blk, float* A_host);

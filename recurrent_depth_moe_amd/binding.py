@@ -74,6 +74,7 @@ def lib():
         "rdt_recurrent_forward": ([vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, sz, vp, sz, vp, vp, vp], i32),
         "rdt_decode_step": ([vp, vp, vp, i32, i32, i32, f32, vp, i32, sz, vp, sz, vp, vp, vp], i32),
         "rdt_recurrent_forward_act_skip": ([vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp, vp, vp], i32),
+        "rdt_decode_step_noalloc": ([vp, vp, vp, i32, i32, i32, f32, vp, i32, sz, vp, vp, vp], i32),
         "rdt_get_A": ([vp, vp], i32),
         "rdt_set_capture": ([vp, vp, vp, vp, i32], i32),
         "rdt_set_timing": ([vp, i32], i32),
@@ -256,6 +257,17 @@ class Block:
                                     float(act_threshold), _ptr(kv_cache), kv_capacity, kvb, _ptr(workspace),
                                     workspace.numel(), _ptr(h_out), _ptr(halt_counts), _stream(stream)))
         return h_out, halt_counts
+
+
+def decode_step_noalloc(blk, e_new, h0_new, start_pos, n_loops, act_threshold, kv_cache, kv_capacity, h_out,
+                        halt_counts, stream=None):
+    """rdt_decode_step_noalloc: a decode step whose workspace is the
+    library's static scratch array (outputs are caller tensors)."""
+    kvb = kv_cache.numel() * kv_cache.element_size()
+    check(lib().rdt_decode_step_noalloc(blk._h, _ptr(e_new), _ptr(h0_new), e_new.shape[0], start_pos, n_loops,
+                                        float(act_threshold), _ptr(kv_cache), kv_capacity, kvb, _ptr(h_out),
+                                        _ptr(halt_counts), _stream(stream)))
+    return h_out, halt_counts
 
 
 def weights_to_device(W, device="cuda"):

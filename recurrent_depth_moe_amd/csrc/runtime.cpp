@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -101,6 +102,39 @@ rdt_status check_config(const rdt_config* c) {
   }
   if (!(c->norm_eps > 0.f) || !(c->rope_theta > 0.f) || !(c->loop_theta > 0.f))
     return fail(RDT_E_INVALID_ARG, "norm_eps, rope_theta and loop_theta must be positive");
+  return RDT_OK;
+}
+
+// ------------------------------------------------------------ allocation-free scratch
+// rdt_decode_step_noalloc takes its workspace from this array instead of a
+// caller buffer.  Each device that loads the library holds its own copy
+// until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[RDT_NOALLOC_MAX_WORKSPACE];
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (rdt_block_create calls this with the handle's device current).
+rdt_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return fail(RDT_E_HIP, "hipGetDevice: %s", hipGetErrorString(he));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RDT_E_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    he = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (he != hipSuccess || !p)
+      return fail(RDT_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(he));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return RDT_OK;
 }
 
@@ -502,6 +536,14 @@ rdt_status rdt_block_create(const rdt_config* cfg, const void* const* weights, v
   if (he != hipSuccess) {
     delete b;
     return fail(RDT_E_HIP, "hipGetDevice/hipDeviceGetAttribute: %s", hipGetErrorString(he));
+  }
+  {
+    // set-up of the allocation-free entry point's scratch on this device
+    void* sp = nullptr;
+    if (scratch_address(&sp) != RDT_OK) {
+      delete b;
+      return RDT_E_HIP;
+    }
   }
   he = hipMalloc((void**)&b->mem, o);
   if (he != hipSuccess) {
@@ -1050,6 +1092,25 @@ rdt_status rdt_recurrent_forward_act_skip(rdt_block* b, const float* e, const fl
                                           size_t ws_bytes, float* h_out, int32_t* halt_counts, void* stream) {
   return run(b, e, h0, B, T, start_pos, n_loops, act_threshold, nullptr, 0, 0, workspace, ws_bytes, h_out,
              halt_counts, stream, false, true);
+}
+
+rdt_status rdt_decode_step_noalloc(rdt_block* b, const float* e_new, const float* h0_new, int32_t B,
+                                   int32_t start_pos, int32_t n_loops, float act_threshold, void* kv_cache,
+                                   int32_t kv_capacity, size_t kv_bytes, float* h_out, int32_t* halt_counts,
+                                   void* stream) {
+  g_err.clear();
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  if (b->timing) return fail(RDT_E_BAD_STATE, "stage timing creates events: turn it off for this entry point");
+  if (B < 1) return fail(RDT_E_INVALID_ARG, "B must be >= 1 (got %d)", B);
+  const size_t need = make_plan(b->cfg, B, 1).total;
+  if (need > RDT_NOALLOC_MAX_WORKSPACE)
+    return fail(RDT_E_WORKSPACE_TOO_SMALL, "a decode step of %d sequences needs %zu bytes of scratch; the "
+                "allocation-free entry point holds %zu", B, need, (size_t)RDT_NOALLOC_MAX_WORKSPACE);
+  void* ws = nullptr;
+  rdt_status st = scratch_address(&ws);
+  if (st) return st;
+  return run(b, e_new, h0_new, B, 1, start_pos, n_loops, act_threshold, kv_cache, kv_capacity, kv_bytes, ws,
+             RDT_NOALLOC_MAX_WORKSPACE, h_out, halt_counts, stream, true);
 }
 
 rdt_status rdt_decode_step(rdt_block* b, const float* e_new, const float* h0_new, int32_t B, int32_t start_pos,
