@@ -64,7 +64,8 @@ def stage_work(cfg, touched=None):
     return w
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_expert_gate_up_mythos_3b.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_per_kernel_{}_prefill.md")
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "mfma_counters_{}_prefill.md")
 GEMM_SOURCES = ["gemm_big.hip", "gemm_device.h", "gemm.h", "common.h"]
 
 
@@ -77,24 +78,36 @@ def gemm_source_hash():
     return hsh.hexdigest()
 
 
-def measured_traffic(config):
-    """HBM bytes per launch of the routed gate|up kernel from the committed
-    rocprofv3 counter summary, or None when that summary was taken on
-    another workload or on a different kernel source."""
-    if config != "mythos_3b" or not os.path.exists(TRAFFIC_PROFILE):
+def profile_value(path, key):
+    """A machine-readable `key: value` line of a committed rocprofv3 counter
+    summary, or None when the file is absent or was taken on a different
+    GEMM kernel source (its kernel_source_sha256 line)."""
+    if not os.path.exists(path):
         return None
     fields = {}
-    with open(TRAFFIC_PROFILE) as f:
+    with open(path) as f:
         for line in f:
-            if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch", "kernel_source_sha256"):
-                key, val = line.split(":", 1)
-                fields[key.strip()] = val.strip().strip("`")
+            if ":" in line and line.split(":", 1)[0].strip() in (key, "kernel_source_sha256"):
+                k, val = line.split(":", 1)
+                fields[k.strip()] = val.strip().strip("`")
     if fields.get("kernel_source_sha256") != gemm_source_hash():
         return None
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the routed gate|up kernel (FETCH_SIZE and
+    WRITE_SIZE passes, copy-calibrated) for this workload, or None."""
+    return profile_value(TRAFFIC_PROFILE.format(config), "traffic_bytes_per_launch")
+
+
+def counter_mfma_frac(config):
+    """Executed bf16 MFMA flops of the routed gate|up launch
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) / (its duration x 2.5 PF), or None."""
+    return profile_value(MFMA_PROFILE.format(config), "mfma_frac_counter_expert_gate_up")
 
 
 def sample_sclk(stop, out):
@@ -143,6 +156,8 @@ def main():
     ap.add_argument("--act-skip", action="store_true",
                     help="ACT with compute skipping (halted positions leave the batch; "
                          "rdt_recurrent_forward_act_skip); value = token-loops actually run per second")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the core clock with rocm-smi (for runs under a profiler)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run plain device copies of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -210,7 +225,8 @@ def main():
     sampler = threading.Thread(target=sample_sclk, args=(stop, clocks), daemon=True)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    sampler.start()
+    if not args.no_clock:
+        sampler.start()
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
@@ -219,7 +235,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     stop.set()
-    sampler.join(timeout=15)
+    if not args.no_clock:
+        sampler.join(timeout=15)
     step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     dom_timing = blk.read_timing()[dom]
     # per-stage breakdown from one more step with every stage timed
@@ -289,10 +306,11 @@ def main():
         roof = dict(bound="mfma", achieved=round(wk["flops"] / avg_s / 1e12, 2) if avg_s else None,
                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4) if roof["achieved"] else None
-    roof["traffic"] = measured_traffic(args.config)
+    roof["traffic"] = None if args.act_skip else measured_traffic(args.config)
     roof.update(kernel="routed expert gate|up grouped GEMM (SwiGLU epilogue)",
                 per_launch_flops=wk["flops"], per_launch_bytes=wk["bytes"], avg_launch_ms=d.get("avg_ms"),
-                mfma_frac=d.get("mfma_frac"))
+                mfma_frac=d.get("mfma_frac"),
+                mfma_frac_counter=None if args.act_skip else counter_mfma_frac(args.config))
     tiles = int(np.sum((counts + 255) // 256)) if T > 1 else int(np.sum((counts + 31) // 32))
     log(f"[bench] routed rows per expert (last loop): min {counts.min()} mean {counts.mean():.1f} "
         f"max {counts.max()}, experts touched {int(np.sum(counts > 0))}, m-tiles {tiles}, "
