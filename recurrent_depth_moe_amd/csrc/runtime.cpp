@@ -295,8 +295,17 @@ rdt_status check_call(const rdt_config& c, const void* e, const void* h0, int B,
 
 // ------------------------------------------------------------ handle
 
+// Attention weights of one layer (the recurrent block, or a dense layer of
+// a model): GQA uses wqkv ([(H + 2G) dh, D], q, k, v rows back to back) and
+// wo; MLA the latent projections, their norm gains and wo.
+struct AttnW {
+  const void *wqkv = nullptr, *wo = nullptr, *wdq = nullptr, *wuq = nullptr, *wdkv = nullptr, *wukv = nullptr;
+  const float *gq = nullptr, *gkv = nullptr;
+};
+
 struct rdt_block {
   rdt_config cfg;
+  AttnW aw;
   int n_cu = 0;
   int64_t params = 0;
   char* mem = nullptr;
@@ -591,6 +600,14 @@ rdt_status rdt_block_create(const rdt_config* cfg, const void* const* weights, v
   b->Bv = PF(RDT_W_B);
   b->halt_w = PF(RDT_W_HALT_W);
   b->halt_b = PF(RDT_W_HALT_B);
+  b->aw.wqkv = b->wqkv;
+  b->aw.wo = b->wo;
+  b->aw.wdq = b->wdq;
+  b->aw.wuq = b->wuq;
+  b->aw.wdkv = b->wdkv;
+  b->aw.wukv = b->wukv;
+  b->aw.gq = b->gq;
+  b->aw.gkv = b->gkv;
   b->rope_cos = (float*)(b->mem + rope_off);
   b->rope_sin = (float*)(b->mem + rope_off + align256((size_t)c.max_seq_len * (rot / 2) * 4));
   b->loop_emb = (float*)(b->mem + loop_off);
@@ -714,6 +731,198 @@ rdt_status rdt_read_timing(rdt_block* b, double* total_ms, int64_t* launches) {
   return RDT_OK;
 }
 
+namespace {
+
+// Launch context of one call: the handle, the workspace plan, the rows of
+// the current loop and the stream.
+struct Ctx {
+  rdt_block* b;
+  const rdt_config* c;
+  const Plan* p;
+  char* w;
+  hipStream_t s;
+  bool bf;
+  int B, T, start_pos;
+  int Mr;                    // rows of this loop
+  const int32_t* tok;        // row -> position (null: row m is position m)
+  const int32_t* live_prev;  // running count of the previous loop (null: always run)
+  void* W(int id) const { return w + p->off[id]; }
+  float* WF(int id) const { return (float*)(w + p->off[id]); }
+  int32_t* WI(int id) const { return (int32_t*)(w + p->off[id]); }
+  // bf16: the 256x256 kernel for prefill products, the skinny kernel for
+  // single-token steps and for narrow outputs (router logits)
+  void gemm(GemmParams gp, int epi, bool dual, int out_bf16, bool narrow = false, hipStream_t on = nullptr) const {
+    gp.live = live_prev;
+    const hipStream_t st = on ? on : s;
+    if (!bf) {
+      launch_gemm_f32(gp, epi, dual, b->n_cu, st);
+      return;
+    }
+    const bool grouped = gp.mt_start != nullptr;
+    if (T == 1 || narrow) {
+      const int cap = grouped ? p->max_mt : (gp.M + RDT_BM_SKINNY - 1) / RDT_BM_SKINNY;
+      // narrow outputs (router logits): 64-column blocks while they still
+      // give every CU one, eight waves per block
+      const int nc = narrow && cap * ((gp.N + 63) / 64) >= b->n_cu ? 64 : 32;
+      launch_gemm_bf16_skinny(gp, epi, dual, out_bf16, cap, nc, st, narrow ? 8 : 4);
+    } else {
+      // 192-column tiles where they fill the rounds of CUs markedly better
+      // than 256-column ones (e.g. dense N = 3072 on 256 CUs)
+      int bn = 256;
+      if (grouped && !dual && gp.N % 192 == 0 && epi == EPI_STORE) {
+        // routed down projection: its m-tile count is only known on the
+        // device; a third more (narrower) tiles levels the rounds of CUs
+        bn = 192;
+      } else if (!grouped && !dual && gp.N % 192 == 0 && (epi == EPI_STORE || epi == EPI_RESID)) {
+        const int mt = (gp.M + 255) / 256;
+        auto eff = [&](int tiles) {
+          const int rounds = (tiles + b->n_cu - 1) / b->n_cu;
+          return (double)tiles / ((double)rounds * b->n_cu);
+        };
+        if (eff(mt * (gp.N / 192)) > eff(mt * ((gp.N + 255) / 256)) + 0.05) bn = 192;
+      }
+      launch_gemm_bf16_big(gp, epi, dual, out_bf16, b->n_cu, st, bn);
+    }
+  }
+};
+
+GemmParams dense_params(const void* A, int64_t lda, const void* W0, const void* W1, int M, int Nn, int K) {
+  GemmParams gp{};
+  gp.A = A;
+  gp.lda = lda;
+  gp.W0 = W0;
+  gp.W1 = W1;
+  gp.M = M;
+  gp.N = Nn;
+  gp.K = K;
+  gp.dense_gm = 4;
+  return gp;
+}
+
+// a4-a7 of one layer (the recurrent block or a dense layer around it):
+// QKV projection with RoPE (writing this call's positions into the layer's
+// cache slot `kslot` when there is one), causal attention, then the
+// O-projection with its residual, x1 = resid + o Wo^T.  The normalised
+// input rows are W(WS_A); rows are x.Mr, row m at position x.tok[m].
+void attention_sublayer(const Ctx& x, const AttnW& aw, char* kslot, int cap_pad, const float* resid, float* x1) {
+  rdt_block* b = x.b;
+  const rdt_config& c = *x.c;
+  const Plan& p = *x.p;
+  const hipStream_t s = x.s;
+  const bool bf = x.bf, kv = kslot != nullptr;
+  const int B = x.B, T = x.T, N = p.N, Mr = x.Mr, start_pos = x.start_pos;
+  const int D = c.dim, H = c.n_heads, G = kv_heads(c), dq = qk_dim(c), dv = v_dim(c);
+  const size_t es = esize(c);
+  const int32_t* tok = x.tok;
+  const int32_t* live_prev = x.live_prev;
+  const float scale = 1.0f / sqrtf((float)dq);
+  auto W = [&](int id) { return x.W(id); };
+  auto WF = [&](int id) { return x.WF(id); };
+  auto gemm = [&](const GemmParams& gp, int epi, bool dual, int out_bf16) { x.gemm(gp, epi, dual, out_bf16); };
+  auto dense = dense_params;
+  if (is_gqa(c)) {
+    void* K = kv ? (void*)kslot : W(WS_K);
+    void* VT = kv ? (void*)(kslot + (size_t)B * G * cap_pad * dq * es) : W(WS_VT);
+    const int cap = kv ? cap_pad : p.kvcap;
+    const int kbase = kv ? start_pos : 0;
+    GemmParams gp = dense(W(WS_A), D, aw.wqkv, nullptr, Mr, (H + 2 * G) * dq, D);
+    EpiParams& ep = gp.epi;
+    ep.q = W(WS_Q);
+    ep.k = K;
+    ep.vt = VT;
+    ep.T = T;
+    ep.H = H;
+    ep.G = G;
+    ep.dq = dq;
+    ep.dv = dv;
+    ep.cap = cap;
+    ep.kbase = kbase;
+    ep.start_pos = start_pos;
+    ep.rcos = b->rope_cos;
+    ep.rsin = b->rope_sin;
+    ep.rot_half = dq / 2;
+    ep.tok = tok;
+    {
+      StageTimer st_(b, s, RDT_STAGE_QKV);
+      gemm(gp, EPI_QKV, false, bf);
+    }
+    StageTimer st_(b, s, RDT_STAGE_ATTN);
+    if (bf && T > 1)
+      launch_attn_flash_bf16(W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, kbase, scale, s, live_prev);
+    else if (kv && use_decode_attn(c, T))
+      launch_attn_decode_bf16(W(WS_Q), K, VT, W(WS_O), WF(WS_DPART), B, H, G, cap, kbase + 1, scale, s);
+    else
+      launch_attn_generic(bf, W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, dq, dv, kbase, scale, s, live_prev);
+  } else {
+    StageTimer st_(b, s, RDT_STAGE_ATTN);
+    const int ql = c.q_lora_rank, kvl = c.kv_lora_rank, rope = c.qk_rope_head_dim, nope = c.qk_nope_head_dim;
+    const int lat_cap = kv ? cap_pad : T;
+    const int kbase = kv ? start_pos : 0;
+    const int kvlen = kbase + T;
+    void* lat_c = kv ? (void*)kslot : W(WS_LATC);
+    void* lat_r = kv ? (void*)(kslot + (size_t)B * cap_pad * kvl * es) : W(WS_LATR);
+    GemmParams g1 = dense(W(WS_A), D, aw.wdkv, nullptr, N, kvl + rope, D);
+    g1.epi.out = W(WS_KVRAW);
+    g1.epi.ldo = kvl + rope;
+    gemm(g1, EPI_STORE, false, 0);
+    GemmParams g2 = dense(W(WS_A), D, aw.wdq, nullptr, N, ql, D);
+    g2.epi.out = W(WS_CQRAW);
+    g2.epi.ldo = ql;
+    gemm(g2, EPI_STORE, false, 0);
+    launch_mla_latent(bf, WF(WS_KVRAW), WF(WS_CQRAW), aw.gq, c.norm_eps, N, T, ql, kvl, rope, start_pos,
+                      b->rope_cos, b->rope_sin, W(WS_CQN), lat_c, lat_r, lat_cap, kbase, s, live_prev);
+    GemmParams g3 = dense(W(WS_CQN), ql, aw.wuq, nullptr, N, H * dq, ql);
+    g3.epi.q = W(WS_Q);
+    g3.epi.T = T;
+    g3.epi.H = H;
+    g3.epi.dq = dq;
+    g3.epi.nope = nope;
+    g3.epi.start_pos = start_pos;
+    g3.epi.rcos = b->rope_cos;
+    g3.epi.rsin = b->rope_sin;
+    g3.epi.rot_half = rope / 2;
+    gemm(g3, EPI_MLA_Q, false, bf);
+    if (T == 1 && kv) {
+      // decode step: attention over the cached latent, up-projections
+      // absorbed into the query and the output
+      launch_mla_absorbed_decode_prep((const float*)lat_c, (const float*)lat_r, lat_cap, aw.gkv, c.norm_eps, B,
+                                      kvlen, kvl, rope, WF(WS_Q), (const float*)aw.wukv, H, nope, dv,
+                                      WF(WS_KLAT), WF(WS_VLAT), WF(WS_QLAT), s, live_prev);
+      launch_attn_generic(bf, W(WS_QLAT), W(WS_KLAT), W(WS_VLAT), W(WS_OLAT), B, H, 1, T, kvlen, kvl + rope, kvl,
+                          kbase, scale, s, live_prev);
+      launch_mla_absorb_o(WF(WS_OLAT), (const float*)aw.wukv, B, H, nope, dv, kvl, WF(WS_O), s, live_prev);
+    } else {
+      // prefill: rebuild k_nope and v of every visible position from the latent
+      launch_mla_kv_prep(bf, lat_c, lat_r, lat_cap, aw.gkv, c.norm_eps, B, kvlen, kvl, rope, H, dq, W(WS_CKVN),
+                         W(WS_K), s, live_prev);
+      GemmParams g4 = dense(W(WS_CKVN), kvl, aw.wukv, nullptr, B * kvlen, H * (nope + dv), kvl);
+      g4.epi.k = W(WS_K);
+      g4.epi.vt = W(WS_VT);
+      g4.epi.T = kvlen;
+      g4.epi.H = H;
+      g4.epi.dq = dq;
+      g4.epi.dv = dv;
+      g4.epi.nope = nope;
+      g4.epi.cap = kvlen;
+      gemm(g4, EPI_MLA_KV, false, bf);
+      launch_attn_generic(bf, W(WS_Q), W(WS_K), W(WS_VT), W(WS_O), B, H, H, T, kvlen, dq, dv, kbase, scale, s,
+                          live_prev);
+    }
+  }
+  // a7: x1 = resid + o Wo^T
+  {
+    StageTimer st_(b, s, RDT_STAGE_OPROJ);
+    GemmParams gp = dense(W(WS_O), (int64_t)H * dv, aw.wo, nullptr, Mr, D, H * dv);
+    gp.a_rows = tok;   // attention output rows are positions
+    gp.epi.out = x1;
+    gp.epi.ldo = D;
+    gp.epi.resid = resid;
+    gemm(gp, EPI_RESID, false, 0);
+  }
+}
+
+}  // namespace
+
 static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int T, int start_pos, int n_loops,
                       float thr, void* kv, int kv_capacity, size_t kv_bytes, void* ws, size_t ws_bytes,
                       float* h_out, int32_t* halt_counts, void* stream, bool decode, bool act_skip = false) {
@@ -738,12 +947,10 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   auto WI = [&](int id) -> int32_t* { return (int32_t*)(w + p.off[id]); };
   const bool bf = c.weight_dtype == RDT_BF16;
   const bool merged = merged_down_schedule(c, T);
-  const int N = p.N, D = c.dim, E = c.n_experts, F = c.expert_dim, k = c.top_k, H = c.n_heads;
-  const int G = kv_heads(c), dq = qk_dim(c), dv = v_dim(c);
+  const int N = p.N, D = c.dim, E = c.n_experts, F = c.expert_dim, k = c.top_k;
   const size_t es = esize(c);
   const int cap_pad = round_up(kv_capacity > 0 ? kv_capacity : 1, 64);
   const size_t slot = kv ? kv_slot_bytes(c, B, kv_capacity) : 0;
-  const float scale = 1.0f / sqrtf((float)dq);
   // Once every position has halted nothing the call returns can change, so
   // with ACT on and no cache to fill every kernel of the later loops exits
   // at once: loop t's kernels read the count of positions still running
@@ -752,53 +959,12 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   const int32_t* live_prev = nullptr;
   int32_t* live_cur = nullptr;
 
-  // bf16: the 256x256 kernel for prefill products, the skinny kernel for
-  // single-token steps and for narrow outputs (router logits)
+  Ctx x{b, &c, &p, w, s_main, bf, B, T, start_pos, N, nullptr, nullptr};
   auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16, bool narrow = false, hipStream_t on = nullptr) {
-    gp.live = live_prev;
-    const hipStream_t s = on ? on : s_main;
-    if (!bf) {
-      launch_gemm_f32(gp, epi, dual, b->n_cu, s);
-      return;
-    }
-    const bool grouped = gp.mt_start != nullptr;
-    if (T == 1 || narrow) {
-      const int cap = grouped ? p.max_mt : (gp.M + RDT_BM_SKINNY - 1) / RDT_BM_SKINNY;
-      // narrow outputs (router logits): 64-column blocks while they still
-      // give every CU one, eight waves per block
-      const int nc = narrow && cap * ((gp.N + 63) / 64) >= b->n_cu ? 64 : 32;
-      launch_gemm_bf16_skinny(gp, epi, dual, out_bf16, cap, nc, s, narrow ? 8 : 4);
-    } else {
-      // 192-column tiles where they fill the rounds of CUs markedly better
-      // than 256-column ones (e.g. dense N = 3072 on 256 CUs)
-      int bn = 256;
-      if (grouped && !dual && gp.N % 192 == 0 && epi == EPI_STORE) {
-        // routed down projection: its m-tile count is only known on the
-        // device; a third more (narrower) tiles levels the rounds of CUs
-        bn = 192;
-      } else if (!grouped && !dual && gp.N % 192 == 0 && (epi == EPI_STORE || epi == EPI_RESID)) {
-        const int mt = (gp.M + 255) / 256;
-        auto eff = [&](int tiles) {
-          const int rounds = (tiles + b->n_cu - 1) / b->n_cu;
-          return (double)tiles / ((double)rounds * b->n_cu);
-        };
-        if (eff(mt * (gp.N / 192)) > eff(mt * ((gp.N + 255) / 256)) + 0.05) bn = 192;
-      }
-      launch_gemm_bf16_big(gp, epi, dual, out_bf16, b->n_cu, s, bn);
-    }
+    x.live_prev = live_prev;
+    x.gemm(gp, epi, dual, out_bf16, narrow, on);
   };
-  auto dense = [&](const void* A, int64_t lda, const void* W0, const void* W1, int M, int Nn, int K) {
-    GemmParams gp{};
-    gp.A = A;
-    gp.lda = lda;
-    gp.W0 = W0;
-    gp.W1 = W1;
-    gp.M = M;
-    gp.N = Nn;
-    gp.K = K;
-    gp.dense_gm = 4;
-    return gp;
-  };
+  auto dense = dense_params;
   // rows of this loop: every position, or with ACT compute skipping the
   // positions still running (row m is position tok[m])
   int Mr = N;
@@ -849,107 +1015,11 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       launch_loop_head(bf, hp, e, b->loop_emb + (size_t)t * c.loop_dim, c.loop_dim, b->g_rec, b->g_attn, c.norm_eps,
                      WF(WS_C), W(WS_A), Mr, D, s, live_prev, live_cur, tok);
     }
-    // a4-a6: attention
-    char* kslot = kv ? (char*)kv + slot * t : nullptr;
-    if (is_gqa(c)) {
-      void* K = kv ? (void*)kslot : W(WS_K);
-      void* VT = kv ? (void*)(kslot + (size_t)B * G * cap_pad * dq * es) : W(WS_VT);
-      const int cap = kv ? cap_pad : p.kvcap;
-      const int kbase = kv ? start_pos : 0;
-      GemmParams gp = dense(W(WS_A), D, b->wqkv, nullptr, Mr, (H + 2 * G) * dq, D);
-      EpiParams& ep = gp.epi;
-      ep.q = W(WS_Q);
-      ep.k = K;
-      ep.vt = VT;
-      ep.T = T;
-      ep.H = H;
-      ep.G = G;
-      ep.dq = dq;
-      ep.dv = dv;
-      ep.cap = cap;
-      ep.kbase = kbase;
-      ep.start_pos = start_pos;
-      ep.rcos = b->rope_cos;
-      ep.rsin = b->rope_sin;
-      ep.rot_half = dq / 2;
-      ep.tok = tok;
-      {
-        StageTimer st_(b, s, RDT_STAGE_QKV);
-        gemm(gp, EPI_QKV, false, bf);
-      }
-      StageTimer st_(b, s, RDT_STAGE_ATTN);
-      if (bf && T > 1)
-        launch_attn_flash_bf16(W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, kbase, scale, s, live_prev);
-      else if (kv && use_decode_attn(c, T))
-        launch_attn_decode_bf16(W(WS_Q), K, VT, W(WS_O), WF(WS_DPART), B, H, G, cap, kbase + 1, scale, s);
-      else
-        launch_attn_generic(bf, W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, dq, dv, kbase, scale, s, live_prev);
-    } else {
-      StageTimer st_(b, s, RDT_STAGE_ATTN);
-      const int ql = c.q_lora_rank, kvl = c.kv_lora_rank, rope = c.qk_rope_head_dim, nope = c.qk_nope_head_dim;
-      const int lat_cap = kv ? cap_pad : T;
-      const int kbase = kv ? start_pos : 0;
-      const int kvlen = kbase + T;
-      void* lat_c = kv ? (void*)kslot : W(WS_LATC);
-      void* lat_r = kv ? (void*)(kslot + (size_t)B * cap_pad * kvl * es) : W(WS_LATR);
-      GemmParams g1 = dense(W(WS_A), D, b->wdkv, nullptr, N, kvl + rope, D);
-      g1.epi.out = W(WS_KVRAW);
-      g1.epi.ldo = kvl + rope;
-      gemm(g1, EPI_STORE, false, 0);
-      GemmParams g2 = dense(W(WS_A), D, b->wdq, nullptr, N, ql, D);
-      g2.epi.out = W(WS_CQRAW);
-      g2.epi.ldo = ql;
-      gemm(g2, EPI_STORE, false, 0);
-      launch_mla_latent(bf, WF(WS_KVRAW), WF(WS_CQRAW), b->gq, c.norm_eps, N, T, ql, kvl, rope, start_pos,
-                        b->rope_cos, b->rope_sin, W(WS_CQN), lat_c, lat_r, lat_cap, kbase, s, live_prev);
-      GemmParams g3 = dense(W(WS_CQN), ql, b->wuq, nullptr, N, H * dq, ql);
-      g3.epi.q = W(WS_Q);
-      g3.epi.T = T;
-      g3.epi.H = H;
-      g3.epi.dq = dq;
-      g3.epi.nope = nope;
-      g3.epi.start_pos = start_pos;
-      g3.epi.rcos = b->rope_cos;
-      g3.epi.rsin = b->rope_sin;
-      g3.epi.rot_half = rope / 2;
-      gemm(g3, EPI_MLA_Q, false, bf);
-      if (T == 1 && kv) {
-        // decode step: attention over the cached latent, up-projections
-        // absorbed into the query and the output
-        launch_mla_absorbed_decode_prep((const float*)lat_c, (const float*)lat_r, lat_cap, b->gkv, c.norm_eps, B,
-                                        kvlen, kvl, rope, WF(WS_Q), (const float*)b->wukv, H, nope, dv,
-                                        WF(WS_KLAT), WF(WS_VLAT), WF(WS_QLAT), s, live_prev);
-        launch_attn_generic(bf, W(WS_QLAT), W(WS_KLAT), W(WS_VLAT), W(WS_OLAT), B, H, 1, T, kvlen, kvl + rope, kvl,
-                            kbase, scale, s, live_prev);
-        launch_mla_absorb_o(WF(WS_OLAT), (const float*)b->wukv, B, H, nope, dv, kvl, WF(WS_O), s, live_prev);
-      } else {
-        // prefill: rebuild k_nope and v of every visible position from the latent
-        launch_mla_kv_prep(bf, lat_c, lat_r, lat_cap, b->gkv, c.norm_eps, B, kvlen, kvl, rope, H, dq, W(WS_CKVN),
-                           W(WS_K), s, live_prev);
-        GemmParams g4 = dense(W(WS_CKVN), kvl, b->wukv, nullptr, B * kvlen, H * (nope + dv), kvl);
-        g4.epi.k = W(WS_K);
-        g4.epi.vt = W(WS_VT);
-        g4.epi.T = kvlen;
-        g4.epi.H = H;
-        g4.epi.dq = dq;
-        g4.epi.dv = dv;
-        g4.epi.nope = nope;
-        g4.epi.cap = kvlen;
-        gemm(g4, EPI_MLA_KV, false, bf);
-        launch_attn_generic(bf, W(WS_Q), W(WS_K), W(WS_VT), W(WS_O), B, H, H, T, kvlen, dq, dv, kbase, scale, s,
-                            live_prev);
-      }
-    }
-    // a7: x1 = c + o Wo^T
-    {
-      StageTimer st_(b, s, RDT_STAGE_OPROJ);
-      GemmParams gp = dense(W(WS_O), (int64_t)H * dv, b->wo, nullptr, Mr, D, H * dv);
-      gp.a_rows = tok;   // attention output rows are positions
-      gp.epi.out = W(WS_X1);
-      gp.epi.ldo = D;
-      gp.epi.resid = WF(WS_C);
-      gemm(gp, EPI_RESID, false, 0);
-    }
+    // a4-a7: attention sub-layer, x1 = c + Attn(a)
+    x.Mr = Mr;
+    x.tok = tok;
+    x.live_prev = live_prev;
+    attention_sublayer(x, b->aw, kv ? (char*)kv + slot * t : nullptr, cap_pad, WF(WS_C), WF(WS_X1));
     // a8: f = RMSNorm(x1) * g_ffn
     {
       StageTimer st_(b, s, RDT_STAGE_FFN_NORM);
