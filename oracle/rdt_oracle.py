@@ -607,3 +607,108 @@ def recurrent_forward_act_skip(cfg, P, e, h0, n_loops, act_threshold, adopt=None
     if record:
         res["record"] = rec
     return res
+
+
+# --------------------------------------------------------------------------
+# the whole model around the recurrent stage
+# --------------------------------------------------------------------------
+
+def dense_hidden(cfg):
+    """Hidden width of the prelude / coda feed-forward: the dense SwiGLU
+    expert of width dim * 4 // 3 ([ZS §MoE]: only the recurrent block's FFN
+    is a MoE)."""
+    return cfg["dim"] * 4 // 3
+
+
+class LayerParams:
+    """The weights of one prelude or coda layer under the names the
+    attention functions read ("wq", "wk", ...), stored as ``prefix + name``."""
+
+    def __init__(self, P, prefix):
+        self.P = P
+        self.prefix = prefix
+        self.arrays = {k[len(prefix):]: v for k, v in P.arrays.items() if k.startswith(prefix)}
+
+    def __getitem__(self, name):
+        return self.P[self.prefix + name]
+
+
+def dense_layer(cfg, LP, x, start_pos=0, cache=None):
+    """One prelude / coda layer: the pre-norm Transformer block with a dense
+    SwiGLU feed-forward ([ZS §MoE]), x1 = x + Attn(RMSNorm(x)),
+    out = x1 + FFN(RMSNorm(x1)).  x: [B, T, D]; ``cache`` is this layer's
+    cache (or None) as in recurrent_forward."""
+    B, T, D = x.shape
+    eps = cfg["norm_eps"]
+    rows = [(b, i) for b in range(B) for i in range(T)]
+    a = rms_norm(x, LP["attn_norm"], eps)
+    attn = gqa_attention if cfg["attn"] == "gqa" else mla_attention
+    o = attn(cfg, LP, a, start_pos, cache, rows)
+    x1 = x.reshape(B * T, D) + np.stack([o[r] for r in rows])
+    f = rms_norm(x1, LP["ffn_norm"], eps)
+    return (x1 + swiglu(f, LP["w1"], LP["w3"], LP["w2"])).reshape(B, T, D)
+
+
+def new_model_cache(cfg, batch, capacity, n_loops):
+    """Caches of every layer of the model: one per prelude layer, one per
+    loop of the recurrent stage, one per coda layer ([ZS §Core Structure]:
+    each layer and loop has its own cache key)."""
+    one = lambda: new_cache(cfg, batch, capacity, 1)[0]
+    return dict(prelude=[one() for _ in range(cfg["prelude_layers"])],
+                loops=new_cache(cfg, batch, capacity, n_loops),
+                coda=[one() for _ in range(cfg["coda_layers"])])
+
+
+def model_forward(cfg, P, ids, n_loops, act_threshold, start_pos=0, cache=None):
+    """The model forward of [ZS §Core Structure]: token embedding, the
+    prelude layers, e = x frozen as the anchor, the recurrent stage with
+    h0 = e, the coda layers, the final RMSNorm and the LM head.
+
+    ids: [B, T] ints.  Returns (logits [B, T, vocab] float64, the recurrent
+    stage's result dict)."""
+    x = P["embed"][np.asarray(ids)]
+    for i in range(cfg["prelude_layers"]):
+        x = dense_layer(cfg, LayerParams(P, f"prelude_{i}."), x, start_pos,
+                        None if cache is None else cache["prelude"][i])
+    e = x
+    r = recurrent_forward(cfg, P, e, e, n_loops, act_threshold, start_pos=start_pos,
+                          cache=None if cache is None else cache["loops"])
+    x = r["out"]
+    for i in range(cfg["coda_layers"]):
+        x = dense_layer(cfg, LayerParams(P, f"coda_{i}."), x, start_pos,
+                        None if cache is None else cache["coda"][i])
+    x = rms_norm(x, P["final_norm"], cfg["norm_eps"])
+    return x @ P["head"].T, r
+
+
+def argmax_lowest(v):
+    """Index of the largest entry of each row, the lowest index on ties, and
+    the gap to the runner-up (the decision margin)."""
+    v = np.asarray(v, dtype=np.float64)
+    idx = np.argmax(v, axis=-1)                      # first maximum
+    top = np.take_along_axis(v, idx[..., None], -1)[..., 0]
+    rest = v.copy()
+    np.put_along_axis(rest, idx[..., None], -np.inf, -1)
+    return idx, top - rest.max(axis=-1)
+
+
+def generate(cfg, P, ids, max_new, n_loops, act_threshold, choose=None):
+    """Greedy decoding with per-layer caches ([ZS §RoPE & generation cache]):
+    step 0 feeds the whole prompt at start_pos 0, every later step only the
+    last token at start_pos = prompt_len + step - 1; the next token is the
+    argmax of the last position's logits (lowest index on ties; the pages
+    show no sampling rule).  ``choose(step, idx, margin)``, when given, may
+    replace the choice (the tie-adoption protocol of the tests).  Returns the
+    [B, prompt_len + max_new] token array."""
+    ids = np.asarray(ids)
+    B, T0 = ids.shape
+    cache = new_model_cache(cfg, B, T0 + max_new, n_loops)
+    out = ids.copy()
+    for step in range(max_new):
+        cur, sp = (ids, 0) if step == 0 else (out[:, -1:], T0 + step - 1)
+        logits, _ = model_forward(cfg, P, cur, n_loops, act_threshold, start_pos=sp, cache=cache)
+        idx, margin = argmax_lowest(logits[:, -1])
+        if choose is not None:
+            idx = choose(step, idx, margin)
+        out = np.concatenate([out, np.asarray(idx).reshape(B, 1)], axis=1)
+    return out

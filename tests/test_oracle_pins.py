@@ -343,25 +343,13 @@ def test_bf16_decode_matches_torch_on_every_bit_pattern():
 
 # ---------------------------------------------------------------- whole block
 
-def _torch_one_loop(cfg, W, h, e, t, start_pos=0, frozen=None, running=None):
-    """One loop written independently with torch CPU library routines:
-    F.rms_norm, complex-number RoPE, SDPA with GQA, a dense masked MoE.
-
-    With ``frozen`` (dict of k, v [B, G, T, dh] float64 arrays) and
-    ``running`` (bool [B, T]): keys and values are computed for every
-    position and then replaced by the frozen ones where a position is not
-    running (a dense masked form of ACT compute skipping); the keys and
-    values used are returned in ``frozen``."""
+def _torch_attn(cfg, W, a, start_pos=0, frozen=None, running=None):
+    """Causal attention of one layer with torch routines (complex-number
+    RoPE, SDPA): GQA or MLA by cfg["attn"]; returns o [B, heads, T, dv].
+    ``frozen`` / ``running``: see _torch_one_loop."""
     T64 = _t64
-    h, e = torch.from_numpy(h), torch.from_numpy(e)
-    B, T, D = h.shape
+    B, T, D = a.shape
     eps = cfg["norm_eps"]
-    half = cfg["loop_dim"] // 2
-    fr = cfg["loop_theta"] ** (-torch.arange(0, cfg["loop_dim"], 2, dtype=torch.float64) / cfg["loop_dim"])
-    emb = torch.zeros(D, dtype=torch.float64)
-    emb[:half], emb[half:2 * half] = torch.sin(t * fr), torch.cos(t * fr)
-    c = F.rms_norm(h + emb + e, (D,), T64(W["g_rec"]), eps)
-    a = F.rms_norm(c, (D,), T64(W["g_attn"]), eps)
 
     def rot(x, d):                                 # x [B, T, heads, d]
         inv = cfg["rope_theta"] ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
@@ -392,6 +380,30 @@ def _torch_one_loop(cfg, W, h, e, t, start_pos=0, frozen=None, running=None):
         k = torch.cat([kv[..., :nope], kr], -1)
         v = kv[..., nope:]
         o = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), is_causal=True)
+    return o
+
+
+def _torch_one_loop(cfg, W, h, e, t, start_pos=0, frozen=None, running=None):
+    """One loop written independently with torch CPU library routines:
+    F.rms_norm, complex-number RoPE, SDPA with GQA, a dense masked MoE.
+
+    With ``frozen`` (dict of k, v [B, G, T, dh] float64 arrays) and
+    ``running`` (bool [B, T]): keys and values are computed for every
+    position and then replaced by the frozen ones where a position is not
+    running (a dense masked form of ACT compute skipping); the keys and
+    values used are returned in ``frozen``."""
+    T64 = _t64
+    h, e = torch.from_numpy(h), torch.from_numpy(e)
+    B, T, D = h.shape
+    eps = cfg["norm_eps"]
+    half = cfg["loop_dim"] // 2
+    fr = cfg["loop_theta"] ** (-torch.arange(0, cfg["loop_dim"], 2, dtype=torch.float64) / cfg["loop_dim"])
+    emb = torch.zeros(D, dtype=torch.float64)
+    emb[:half], emb[half:2 * half] = torch.sin(t * fr), torch.cos(t * fr)
+    c = F.rms_norm(h + emb + e, (D,), T64(W["g_rec"]), eps)
+    a = F.rms_norm(c, (D,), T64(W["g_attn"]), eps)
+
+    o = _torch_attn(cfg, W, a, start_pos, frozen, running)
     x1 = c + F.linear(o.transpose(1, 2).reshape(B, T, -1), T64(W["wo"]))
     f = F.rms_norm(x1, (D,), T64(W["g_ffn"]), eps).reshape(B * T, D)
     z = F.linear(f, T64(W["router_w"]))
@@ -553,3 +565,94 @@ def test_act_skip_weights_sum_to_one_and_halted_rows_stop():
         assert counts[nn] == want
         wsum = sum(seq[:-1]) + max(1.0 - sum(seq[:-1]), 0.0)
         assert abs(wsum - 1.0) < 1e-12
+
+
+# ---------------------------------------------------------------- the whole model
+
+def _layer_weights(W, prefix):
+    return {k[len(prefix):]: v for k, v in W.items() if k.startswith(prefix)}
+
+
+def _torch_dense_layer(cfg, LW, x):
+    """A prelude / coda layer with torch routines: x1 = x + Attn(rms_norm(x)),
+    out = x1 + silu(f W1^T) * (f W3^T) W2^T with f = rms_norm(x1)."""
+    B, T, D = x.shape
+    eps = cfg["norm_eps"]
+    a = F.rms_norm(x, (D,), _t64(LW["attn_norm"]), eps)
+    o = _torch_attn(cfg, LW, a)
+    x1 = x + F.linear(o.transpose(1, 2).reshape(B, T, -1), _t64(LW["wo"]))
+    f = F.rms_norm(x1, (D,), _t64(LW["ffn_norm"]), eps)
+    return x1 + F.linear(F.silu(F.linear(f, _t64(LW["w1"]))) * F.linear(f, _t64(LW["w3"])), _t64(LW["w2"]))
+
+
+@pytest.mark.parametrize("name", ["tiny_model_gqa", "tiny_model_mla"])
+def test_dense_layer_matches_torch(name):
+    """[ZS §MoE]: prelude and coda layers are the pre-norm block with a dense
+    SwiGLU feed-forward of width dim * 4 // 3 (341 at dim 256)."""
+    cfg = configs.get(name)
+    W = generate.make_weights(cfg, scales={"prelude_0.wo": 0.1, "prelude_0.w2": 0.1})
+    P = O.Params(W)
+    assert W["prelude_0.w1"].shape == (O.dense_hidden(cfg), cfg["dim"]) == (341, 256)
+    x = np.random.default_rng(31).standard_normal((cfg["batch"], cfg["seq"], cfg["dim"]))
+    got = O.dense_layer(cfg, O.LayerParams(P, "prelude_0."), x)
+    ref = _torch_dense_layer(cfg, _layer_weights(W, "prelude_0."), torch.from_numpy(x)).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+
+
+@pytest.mark.parametrize("name", ["tiny_model_gqa", "tiny_model_mla"])
+def test_model_forward_wiring(name):
+    """[ZS §Core Structure]: embed, prelude, e = x as both anchor and initial
+    state of the recurrent stage, coda, final norm, head -- written here with
+    torch for every part but the recurrent stage (pinned on its own above).
+    The usage example prints logits of shape (2, 16, vocab 1000)."""
+    cfg = configs.get(name)
+    W = generate.make_weights(cfg, scales={"prelude_0.wo": 0.1, "coda_0.wo": 0.1})
+    P = O.Params(W)
+    ids = generate.make_ids(cfg)
+    logits, r = O.model_forward(cfg, P, ids, cfg["n_loops"], cfg["act_threshold"])
+    assert logits.shape == (2, 16, 1000)
+    x = _t64(W["embed"])[torch.from_numpy(ids.astype(np.int64))]
+    x = _torch_dense_layer(cfg, _layer_weights(W, "prelude_0."), x)
+    rr = O.recurrent_forward(cfg, P, x.numpy(), x.numpy(), cfg["n_loops"], cfg["act_threshold"])
+    y = _torch_dense_layer(cfg, _layer_weights(W, "coda_0."), torch.from_numpy(rr["out"]))
+    y = F.rms_norm(y, (cfg["dim"],), _t64(W["final_norm"]), cfg["norm_eps"])
+    ref = F.linear(y, _t64(W["head"])).numpy()
+    np.testing.assert_array_equal(r["halt_counts"], rr["halt_counts"])
+    np.testing.assert_allclose(logits, ref, rtol=1e-9, atol=1e-11)
+
+
+def test_argmax_lowest_index_brute_force():
+    rng = np.random.default_rng(32)
+    v = rng.integers(0, 4, size=(50, 9)).astype(np.float64)      # many exact ties
+    idx, margin = O.argmax_lowest(v)
+    for r in range(50):
+        best = max(v[r])
+        assert idx[r] == min(j for j in range(9) if v[r, j] == best)
+        others = sorted(v[r], reverse=True)
+        assert margin[r] == others[0] - others[1]
+
+
+@pytest.mark.parametrize("name", ["tiny_model_gqa", "tiny_model_mla"])
+def test_generate_with_caches_equals_full_recompute(name):
+    """[ZS §RoPE & generation cache]: greedy generation that feeds the prompt
+    once and then one token per step at start_pos = prompt_len + step - 1
+    against the per-layer caches gives the tokens of recomputing the whole
+    growing sequence every step (no cache).  The usage example generates 8
+    tokens with 8 loops: output shape (2, 24)."""
+    cfg = configs.get(name, seq=6)
+    W = generate.make_weights(cfg)
+    P = O.Params(W)
+    ids = generate.make_ids(cfg)
+    n_new, L = 4, 8
+    out = O.generate(cfg, P, ids, n_new, L, cfg["act_threshold"])
+    assert out.shape == (2, 6 + n_new)
+    np.testing.assert_array_equal(out[:, :6], ids)
+    seq = ids.copy()
+    for _ in range(n_new):
+        logits, _ = O.model_forward(cfg, P, seq, L, cfg["act_threshold"])
+        nxt, margin = O.argmax_lowest(logits[:, -1])
+        assert np.all(margin > 1e-9)
+        seq = np.concatenate([seq, nxt[:, None]], axis=1)
+    np.testing.assert_array_equal(out, seq)
+    full = O.generate(configs.get(name), P, generate.make_ids(configs.get(name)), 8, 8, 0.99)
+    assert full.shape == (2, 24)

@@ -40,6 +40,10 @@ _COMMON = dict(
     qk_nope_head_dim=0,
     v_head_dim=0,
     use_cache=False,
+    # the model around the recurrent stage (token embedding, prelude and
+    # coda layers, final norm, LM head); the block-only workloads have none
+    prelude_layers=0,
+    coda_layers=0,
     # how e is made: "embed" = lookup of uniform token ids in an N(0, 0.02)
     # table (toy example); "rmsnorm_normal" = N(0,1) rows, RMS-normalised.
     e_kind="rmsnorm_normal",
@@ -139,6 +143,32 @@ CONFIGS = {
         lora_rank=8, max_loop_iters=4, max_seq_len=256,
         dtype="f32", batch=2, seq=150, n_loops=3, act_threshold=0.99,
         seed=14),
+
+    # ---- whole model: the usage example of [RC] (vocabulary 1000, one
+    # prelude and one coda layer, prompt of 2 x 16 token ids, 4 loops; 8 new
+    # tokens generated with 8 loops) ----
+    "tiny_model_gqa": _cfg(
+        dim=256, n_heads=8, n_kv_heads=2, attn="gqa",
+        n_experts=8, n_shared_experts=1, top_k=2, expert_dim=64,
+        lora_rank=8, max_loop_iters=4, max_seq_len=128,
+        dtype="f32", batch=2, seq=16, n_loops=4, act_threshold=0.99,
+        seed=21, vocab=1000, prelude_layers=1, coda_layers=1),
+    "tiny_model_mla": _cfg(
+        dim=256, n_heads=8, n_kv_heads=8, attn="mla",
+        q_lora_rank=64, kv_lora_rank=32, qk_rope_head_dim=16,
+        qk_nope_head_dim=16, v_head_dim=16,
+        n_experts=8, n_shared_experts=1, top_k=2, expert_dim=64,
+        lora_rank=8, max_loop_iters=4, max_seq_len=128,
+        dtype="f32", batch=2, seq=16, n_loops=4, act_threshold=0.99,
+        seed=22, vocab=1000, prelude_layers=1, coda_layers=1),
+    # bf16 model shape with head_dim 128 (large-tile GEMMs, flash and split-KV
+    # attention in every layer), two prelude layers, ragged prompt
+    "small_model_bf16": _cfg(
+        dim=512, n_heads=4, n_kv_heads=2, attn="gqa",
+        n_experts=8, n_shared_experts=1, top_k=2, expert_dim=384,
+        lora_rank=8, max_loop_iters=4, max_seq_len=256,
+        dtype="bf16", batch=2, seq=70, n_loops=3, act_threshold=0.99,
+        seed=23, vocab=3000, prelude_layers=2, coda_layers=1),
 }
 
 

@@ -104,6 +104,37 @@ def tensor_specs(cfg):
     vec("B", [D], "uniform", 1.0)
     vec("halt_w", [D], "normal", 0.02)
     vec("halt_b", [1], "const", cfg["halt_b"])
+    # the model around the recurrent stage: token embedding, prelude and
+    # coda layers (pre-norm attention + dense SwiGLU of width dim * 4 // 3),
+    # final norm, LM head
+    if cfg.get("prelude_layers", 0) or cfg.get("coda_layers", 0):
+        V, Fd = cfg["vocab"], D * 4 // 3
+        mat("embed", [V, D])
+        for pre, n in (("prelude", cfg["prelude_layers"]), ("coda", cfg["coda_layers"])):
+            for i in range(n):
+                p = f"{pre}_{i}."
+                vec(p + "attn_norm", [D], "const", 1.0)
+                if cfg["attn"] == "gqa":
+                    mat(p + "wq", [H * dh, D])
+                    mat(p + "wk", [Hkv * dh, D])
+                    mat(p + "wv", [Hkv * dh, D])
+                    mat(p + "wo", [D, H * dh])
+                else:
+                    ql, kvl = cfg["q_lora_rank"], cfg["kv_lora_rank"]
+                    rope, nope, vd = cfg["qk_rope_head_dim"], cfg["qk_nope_head_dim"], cfg["v_head_dim"]
+                    mat(p + "wdq", [ql, D])
+                    vec(p + "gq", [ql], "const", 1.0)
+                    mat(p + "wuq", [H * (nope + rope), ql])
+                    mat(p + "wdkv", [kvl + rope, D])
+                    vec(p + "gkv", [kvl], "const", 1.0)
+                    mat(p + "wukv", [H * (nope + vd), kvl])
+                    mat(p + "wo", [D, H * vd])
+                vec(p + "ffn_norm", [D], "const", 1.0)
+                mat(p + "w1", [Fd, D])
+                mat(p + "w3", [Fd, D])
+                mat(p + "w2", [D, Fd])
+        vec("final_norm", [D], "const", 1.0)
+        mat("head", [V, D])
     return sp
 
 
@@ -190,6 +221,13 @@ def make_inputs(cfg):
         e = (x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True))).astype(np.float32)
     e = np.ascontiguousarray(e, dtype=np.float32)
     return e, e.copy()
+
+
+def make_ids(cfg):
+    """Prompt token ids [B, T], uniform in [0, vocab) (the usage example of
+    the pages draws them the same way)."""
+    B, T = cfg["batch"], cfg["seq"]
+    return draw(cfg["seed"], "ids", (B, T), "int", cfg["vocab"]).reshape(B, T).astype(np.int32)
 
 
 def make_cache_loop(cfg, t, which, b_range=None):
