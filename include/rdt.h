@@ -222,6 +222,85 @@ rdt_status rdt_decode_step_noalloc(rdt_block* blk, const float* e_new, const flo
                                    int32_t kv_capacity, size_t kv_bytes, float* h_out, int32_t* halt_counts,
                                    void* stream);
 
+/* ------------------------------------------------------------------------
+ * The whole model around the recurrent stage ([ZS §Core Structure]): token
+ * embedding, prelude layers, e = x frozen as the anchor and initial state
+ * of the recurrent stage, coda layers, final RMSNorm, LM head; greedy
+ * generation with per-layer caches ([ZS §RoPE & generation cache]).
+ * Prelude and coda layers are pre-norm blocks with the block's attention
+ * type and shapes and a dense SwiGLU feed-forward of width dim * 4 / 3
+ * (integer division, [ZS §MoE]): x1 = x + Attn(RMSNorm(x)), out = x1 +
+ * W2 (silu(W1 f) * (W3 f)), f = RMSNorm(x1).  No biases.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  rdt_config block;        /* the recurrent block; its attention shape is every layer's */
+  int32_t vocab_size;
+  int32_t prelude_layers;  /* 0 .. 64 */
+  int32_t coda_layers;     /* 0 .. 64 */
+} rdt_model_config;
+
+/* Model-level tensors (device pointers, "M" = block.weight_dtype):
+ *   EMBED M [V, D]   FINAL_NORM f32 [D]   HEAD M [V, D] */
+enum rdt_model_weight_id { RDT_MW_EMBED = 0, RDT_MW_FINAL_NORM, RDT_MW_HEAD, RDT_MW_COUNT };
+/* Tensors of one prelude / coda layer (Fd = dim * 4 / 3):
+ *   ATTN_NORM, FFN_NORM f32 [D]; attention as the block's (GQA: WQ WK WV
+ *   WO; MLA: WDQ GQ WUQ WDKV GKV WUKV WO, shapes as RDT_W_*);
+ *   W1 (gate), W3 (up) M [Fd, D]; W2 (down) M [D, Fd].
+ * Entries of the other attention type may be NULL. */
+enum rdt_layer_weight_id {
+  RDT_LW_ATTN_NORM = 0, RDT_LW_WQ, RDT_LW_WK, RDT_LW_WV, RDT_LW_WO,
+  RDT_LW_WDQ, RDT_LW_GQ, RDT_LW_WUQ, RDT_LW_WDKV, RDT_LW_GKV, RDT_LW_WUKV,
+  RDT_LW_FFN_NORM, RDT_LW_W1, RDT_LW_W3, RDT_LW_W2, RDT_LW_COUNT
+};
+
+typedef struct rdt_model rdt_model; /* opaque */
+
+/* Build a model: the recurrent block from `block_weights` (as
+ * rdt_block_create), the model tensors from `model_weights` (RDT_MW_COUNT
+ * pointers) and the layers from `layer_weights` ((prelude_layers +
+ * coda_layers) * RDT_LW_COUNT pointers, prelude layers first, layer l's
+ * tensor id at l * RDT_LW_COUNT + id).  Weights are copied into
+ * handle-owned memory (the dense hidden width padded with zero rows /
+ * columns to the matrix-product granularity, which changes no value).
+ * Errors: those of rdt_block_create; INVALID_ARG for vocab_size < 1 or a
+ * layer count outside [0, 64]. */
+rdt_status rdt_model_create(const rdt_model_config* cfg, const void* const* block_weights,
+                            const void* const* model_weights, const void* const* layer_weights, void* stream,
+                            rdt_model** out);
+rdt_status rdt_model_destroy(rdt_model* m);
+/* The model's recurrent-stage handle (owned by the model), e.g. for
+ * rdt_set_capture or stage timing of the recurrent stage. */
+rdt_status rdt_model_block(const rdt_model* m, rdt_block** blk);
+/* Workspace bytes of a model call on B sequences of T tokens. */
+rdt_status rdt_model_workspace_bytes(const rdt_model* m, int32_t B, int32_t T, size_t* bytes);
+/* Bytes of the model's cache: prelude_layers + n_loops + coda_layers slots
+ * of rdt_kv_cache_bytes' layout, in that order (prelude layer i in slot i,
+ * loop t in slot prelude_layers + t, coda layer j after the loops). */
+rdt_status rdt_model_kv_cache_bytes(const rdt_model* m, int32_t B, int32_t capacity, int32_t n_loops,
+                                    size_t* bytes);
+/* The model forward ([ZS §Core Structure]).  ids: device int32, token i of
+ * sequence b at ids[b * ids_ld + i]; logits: fp32 [B, T, vocab_size].
+ * start_pos, n_loops, act_threshold, the cache and the workspace as for
+ * rdt_recurrent_forward (a single-token call with a cache runs the decode
+ * kernels).  An id outside [0, vocab_size) makes its rows' logits NaN.
+ * Errors: those of rdt_recurrent_forward. */
+rdt_status rdt_model_forward(rdt_model* m, const int32_t* ids, int64_t ids_ld, int32_t B, int32_t T,
+                             int32_t start_pos, int32_t n_loops, float act_threshold, void* kv_cache,
+                             int32_t kv_capacity, size_t kv_bytes, void* workspace, size_t ws_bytes,
+                             float* logits, void* stream);
+/* Greedy generation ([ZS §RoPE & generation cache]): out_ids [B, T0 +
+ * max_new] (device int32) receives the prompt [B, T0] then max_new tokens;
+ * step 0 runs the prompt at start_pos 0, step s > 0 the last token at
+ * start_pos T0 + s - 1, each token the argmax of the last position's
+ * logits (lowest id on ties).  The cache needs capacity >= T0 + max_new and
+ * the workspace rdt_model_workspace_bytes(B, T0).  Stream-ordered: the
+ * chosen ids never leave the device.  Errors: those of rdt_model_forward;
+ * INVALID_ARG for max_new < 1. */
+rdt_status rdt_model_generate(rdt_model* m, const int32_t* prompt, int32_t B, int32_t T0, int32_t max_new,
+                              int32_t n_loops, float act_threshold, void* kv_cache, int32_t kv_capacity,
+                              size_t kv_bytes, void* workspace, size_t ws_bytes, int32_t* out_ids,
+                              void* stream);
+
 /* Copies A (fp32, [D]) to host memory, for the rho(A) < 1 check of
  * [RC §사용법] (A is diagonal, so rho(A) = max A_i).  Synchronous. */
 rdt_status rdt_get_A(const rdt_block* blk, float* A_host);

@@ -659,20 +659,21 @@ def new_model_cache(cfg, batch, capacity, n_loops):
                 coda=[one() for _ in range(cfg["coda_layers"])])
 
 
-def model_forward(cfg, P, ids, n_loops, act_threshold, start_pos=0, cache=None):
+def model_forward(cfg, P, ids, n_loops, act_threshold, start_pos=0, cache=None, adopt=None):
     """The model forward of [ZS §Core Structure]: token embedding, the
     prelude layers, e = x frozen as the anchor, the recurrent stage with
     h0 = e, the coda layers, the final RMSNorm and the LM head.
 
-    ids: [B, T] ints.  Returns (logits [B, T, vocab] float64, the recurrent
-    stage's result dict)."""
+    ids: [B, T] ints.  ``adopt`` is passed to the recurrent stage (see
+    recurrent_forward).  Returns (logits [B, T, vocab] float64, the
+    recurrent stage's result dict)."""
     x = P["embed"][np.asarray(ids)]
     for i in range(cfg["prelude_layers"]):
         x = dense_layer(cfg, LayerParams(P, f"prelude_{i}."), x, start_pos,
                         None if cache is None else cache["prelude"][i])
     e = x
     r = recurrent_forward(cfg, P, e, e, n_loops, act_threshold, start_pos=start_pos,
-                          cache=None if cache is None else cache["loops"])
+                          cache=None if cache is None else cache["loops"], adopt=adopt)
     x = r["out"]
     for i in range(cfg["coda_layers"]):
         x = dense_layer(cfg, LayerParams(P, f"coda_{i}."), x, start_pos,

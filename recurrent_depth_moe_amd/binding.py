@@ -37,6 +37,16 @@ class RdtConfig(ctypes.Structure):
          ("weight_dtype", ctypes.c_int32)]
 
 
+class RdtModelConfig(ctypes.Structure):
+    _fields_ = [("block", RdtConfig), ("vocab_size", ctypes.c_int32), ("prelude_layers", ctypes.c_int32),
+                ("coda_layers", ctypes.c_int32)]
+
+
+MODEL_WEIGHT_NAMES = ["embed", "final_norm", "head"]
+LAYER_WEIGHT_NAMES = ["attn_norm", "wq", "wk", "wv", "wo", "wdq", "gq", "wuq", "wdkv", "gkv", "wukv",
+                      "ffn_norm", "w1", "w3", "w2"]
+
+
 class RdtError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
@@ -75,6 +85,14 @@ def lib():
         "rdt_decode_step": ([vp, vp, vp, i32, i32, i32, f32, vp, i32, sz, vp, sz, vp, vp, vp], i32),
         "rdt_recurrent_forward_act_skip": ([vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp, vp, vp], i32),
         "rdt_decode_step_noalloc": ([vp, vp, vp, i32, i32, i32, f32, vp, i32, sz, vp, vp, vp], i32),
+        "rdt_model_create": ([ctypes.c_void_p, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
+                              ctypes.POINTER(vp)], i32),
+        "rdt_model_destroy": ([vp], i32),
+        "rdt_model_block": ([vp, ctypes.POINTER(vp)], i32),
+        "rdt_model_workspace_bytes": ([vp, i32, i32, ctypes.POINTER(sz)], i32),
+        "rdt_model_kv_cache_bytes": ([vp, i32, i32, i32, ctypes.POINTER(sz)], i32),
+        "rdt_model_forward": ([vp, vp, ctypes.c_int64, i32, i32, i32, i32, f32, vp, i32, sz, vp, sz, vp, vp], i32),
+        "rdt_model_generate": ([vp, vp, i32, i32, i32, i32, f32, vp, i32, sz, vp, sz, vp, vp], i32),
         "rdt_get_A": ([vp, vp], i32),
         "rdt_set_capture": ([vp, vp, vp, vp, i32], i32),
         "rdt_set_timing": ([vp, i32], i32),
@@ -268,6 +286,111 @@ def decode_step_noalloc(blk, e_new, h0_new, start_pos, n_loops, act_threshold, k
                                         float(act_threshold), _ptr(kv_cache), kv_capacity, kvb, _ptr(h_out),
                                         _ptr(halt_counts), _stream(stream)))
     return h_out, halt_counts
+
+
+class _BlockView(Block):
+    """The recurrent-stage handle a Model owns (not destroyed by this view)."""
+
+    def __init__(self, cfg, handle):
+        self.cfg = cfg
+        self._c = make_config(cfg)
+        self._h = handle
+
+    def close(self):
+        self._h = ctypes.c_void_p()
+
+
+class Model:
+    """Owns an rdt_model handle: token embedding, prelude / coda layers, the
+    recurrent stage, final norm, LM head.  ``weights`` maps the block's names,
+    "embed", "final_norm", "head" and "prelude_<i>.<name>" /
+    "coda_<j>.<name>" layer tensors to device tensors."""
+
+    def __init__(self, cfg, weights, stream=None):
+        self.cfg = cfg
+        mc = RdtModelConfig()
+        mc.block = make_config(cfg)
+        mc.vocab_size = int(cfg["vocab"])
+        mc.prelude_layers = int(cfg["prelude_layers"])
+        mc.coda_layers = int(cfg["coda_layers"])
+        self._mc = mc
+
+        def ptrs(names, prefix=""):
+            arr = (ctypes.c_void_p * len(names))()
+            for i, n in enumerate(names):
+                t = weights.get(prefix + n)
+                if t is not None:
+                    assert t.is_cuda and t.is_contiguous(), prefix + n
+                    arr[i] = t.data_ptr()
+            return arr
+        bw = ptrs(WEIGHT_NAMES)
+        mw = ptrs(MODEL_WEIGHT_NAMES)
+        prefixes = [f"prelude_{i}." for i in range(mc.prelude_layers)] + [f"coda_{j}." for j in range(mc.coda_layers)]
+        lw = (ctypes.c_void_p * max(1, len(prefixes) * len(LAYER_WEIGHT_NAMES)))()
+        for l, pre in enumerate(prefixes):
+            one = ptrs(LAYER_WEIGHT_NAMES, pre)
+            for i in range(len(LAYER_WEIGHT_NAMES)):
+                lw[l * len(LAYER_WEIGHT_NAMES) + i] = one[i]
+        h = ctypes.c_void_p()
+        check(lib().rdt_model_create(ctypes.byref(mc), bw, mw, lw, _stream(stream), ctypes.byref(h)))
+        self._h = h
+        bh = ctypes.c_void_p()
+        check(lib().rdt_model_block(self._h, ctypes.byref(bh)))
+        self.block = _BlockView(cfg, bh)
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self.block.close()
+            check(lib().rdt_model_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, B, T):
+        n = ctypes.c_size_t()
+        check(lib().rdt_model_workspace_bytes(self._h, B, T, ctypes.byref(n)))
+        return n.value
+
+    def kv_cache_bytes(self, B, capacity, n_loops):
+        n = ctypes.c_size_t()
+        check(lib().rdt_model_kv_cache_bytes(self._h, B, capacity, n_loops, ctypes.byref(n)))
+        return n.value
+
+    def new_workspace(self, B, T):
+        return torch.empty(self.workspace_bytes(B, T), dtype=torch.uint8, device="cuda")
+
+    def forward(self, ids, n_loops, act_threshold, start_pos=0, kv_cache=None, kv_capacity=0, workspace=None,
+                logits=None, stream=None):
+        """ids: int32 device tensor [B, T] (a view with unit column stride)."""
+        B, T = ids.shape
+        assert ids.dtype == torch.int32 and ids.stride(1) == 1
+        if workspace is None:
+            workspace = self.new_workspace(B, T)
+        if logits is None:
+            logits = torch.empty((B, T, self.cfg["vocab"]), dtype=torch.float32, device=ids.device)
+        kvb = 0 if kv_cache is None else kv_cache.numel() * kv_cache.element_size()
+        check(lib().rdt_model_forward(self._h, _ptr(ids), ids.stride(0), B, T, start_pos, n_loops,
+                                      float(act_threshold), _ptr(kv_cache), kv_capacity, kvb, _ptr(workspace),
+                                      workspace.numel(), _ptr(logits), _stream(stream)))
+        return logits
+
+    def generate(self, prompt, max_new, n_loops, act_threshold, kv_cache=None, workspace=None, stream=None):
+        B, T0 = prompt.shape
+        cap = T0 + max_new
+        if kv_cache is None:
+            kv_cache = torch.zeros(self.kv_cache_bytes(B, cap, n_loops), dtype=torch.uint8, device=prompt.device)
+        if workspace is None:
+            workspace = self.new_workspace(B, T0)
+        out = torch.empty((B, cap), dtype=torch.int32, device=prompt.device)
+        kvb = kv_cache.numel() * kv_cache.element_size()
+        check(lib().rdt_model_generate(self._h, _ptr(prompt.contiguous()), B, T0, max_new, n_loops,
+                                       float(act_threshold), _ptr(kv_cache), cap, kvb, _ptr(workspace),
+                                       workspace.numel(), _ptr(out), _stream(stream)))
+        return out
 
 
 def weights_to_device(W, device="cuda"):

@@ -19,6 +19,15 @@ void launch_loop_head(int act_bf16, const float* h, const float* e, const float*
                       const float* g_rec, const float* g_attn, float eps, float* c, void* a, int N, int D,
                       hipStream_t s, const int32_t* live_prev = nullptr, int32_t* live_cur = nullptr,
                       const int32_t* tok = nullptr);
+// Token embedding ([ZS §Core Structure], the model's first step): row
+// n = b T + i of x (fp32 [B T, D]) is row ids[b ids_ld + i] of the table
+// ([V, D], bf16 or fp32); an id outside [0, V) gives a row of NaN.
+void launch_embed(int table_bf16, const int32_t* ids, int64_t ids_ld, int B, int T, const void* table, int V, int D,
+                  float* x, hipStream_t s);
+// Greedy choice: out[r * out_ld] = the column of the largest logit of row r
+// (fp32 [rows, V]), the lowest column among equal maxima; NaN never wins
+// (a row of NaN gives 0).
+void launch_argmax_rows(const float* logits, int rows, int V, int32_t* out, int64_t out_ld, hipStream_t s);
 // ACT compute skipping: tok[0 .. count) = the positions whose halt count is
 // still 0 (running), in ascending order; *count written on the device.
 void launch_compact_running(const int32_t* halt_counts, int N, int32_t* tok, int32_t* count, hipStream_t s);

@@ -927,6 +927,55 @@ __global__ __launch_bounds__(RB) void loop_tail_fast_kernel(TailArgs a) {
   if (a.live_cur && threadIdx.x == 0 && still > 0) atomicAdd(a.live_cur, still);
 }
 
+// ------------------------------------------------------------ embedding, argmax
+template <typename TT>
+__global__ __launch_bounds__(RB) void embed_kernel(const int32_t* __restrict__ ids, int64_t ids_ld, int T,
+                                                    const TT* __restrict__ table, int V, int D,
+                                                    float* __restrict__ x) {
+  const int n = blockIdx.x, b = n / T, i = n - b * T;
+  const int id = ids[(int64_t)b * ids_ld + i];
+  float* xr = x + (int64_t)n * D;
+  if (id < 0 || id >= V) {
+    for (int d = threadIdx.x; d < D; d += RB) xr[d] = __builtin_nanf("");
+    return;
+  }
+  const TT* tr = table + (int64_t)id * D;
+  for (int d4 = threadIdx.x; d4 < (D >> 2); d4 += RB) st4(xr + 4 * d4, ld4(tr + 4 * d4));
+}
+
+// one block per row: each thread scans a strided share, then a block
+// reduction keeps the larger value and, on equal values, the lower column
+__global__ __launch_bounds__(RB) void argmax_rows_kernel(const float* __restrict__ logits, int V,
+                                                         int32_t* __restrict__ out, int64_t out_ld) {
+  __shared__ float bv[RB];
+  __shared__ int bi[RB];
+  const float* row = logits + (int64_t)blockIdx.x * V;
+  float best = -INFINITY;
+  int besti = 0x7fffffff;
+  for (int j = threadIdx.x; j < V; j += RB) {
+    const float v = row[j];
+    if (v > best) {   // NaN compares false: never taken; ascending j keeps the first maximum
+      best = v;
+      besti = j;
+    }
+  }
+  bv[threadIdx.x] = best;
+  bi[threadIdx.x] = besti;
+  __syncthreads();
+  for (int w = RB / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      const float ov = bv[threadIdx.x + w];
+      const int oi = bi[threadIdx.x + w];
+      if (ov > bv[threadIdx.x] || (ov == bv[threadIdx.x] && oi < bi[threadIdx.x])) {
+        bv[threadIdx.x] = ov;
+        bi[threadIdx.x] = oi;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[(int64_t)blockIdx.x * out_ld] = bi[0] == 0x7fffffff ? 0 : bi[0];
+}
+
 // ------------------------------------------------------------ compaction
 // ACT compute skipping: the positions still running (halt count 0) in
 // ascending order, by one block: each wave ballots its 64 positions, the
@@ -1264,4 +1313,16 @@ void launch_mla_kv_prep(int act_bf16, const void* lat_ckv, const void* lat_krope
 
 void launch_compact_running(const int32_t* halt_counts, int N, int32_t* tok, int32_t* count, hipStream_t s) {
   compact_running_kernel<<<1, 1024, 0, s>>>(halt_counts, N, tok, count);
+}
+
+void launch_embed(int table_bf16, const int32_t* ids, int64_t ids_ld, int B, int T, const void* table, int V, int D,
+                  float* x, hipStream_t s) {
+  if (table_bf16)
+    embed_kernel<bf16_t><<<B * T, RB, 0, s>>>(ids, ids_ld, T, (const bf16_t*)table, V, D, x);
+  else
+    embed_kernel<float><<<B * T, RB, 0, s>>>(ids, ids_ld, T, (const float*)table, V, D, x);
+}
+
+void launch_argmax_rows(const float* logits, int rows, int V, int32_t* out, int64_t out_ld, hipStream_t s) {
+  argmax_rows_kernel<<<rows, RB, 0, s>>>(logits, V, out, out_ld);
 }

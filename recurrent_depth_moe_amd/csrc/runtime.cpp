@@ -1192,3 +1192,379 @@ rdt_status rdt_decode_step(rdt_block* b, const float* e_new, const float* h0_new
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ the model
+// Token embedding, prelude layers, the recurrent stage, coda layers, final
+// norm and LM head ([ZS §Core Structure]); greedy generation ([ZS §RoPE &
+// generation cache]).
+
+namespace {
+
+struct ModelLayer {
+  AttnW aw;
+  const float* attn_norm = nullptr;
+  const float* ffn_norm = nullptr;
+  const void *w1 = nullptr, *w3 = nullptr, *w2 = nullptr;   // [fd_pad, D], [fd_pad, D], [D, fd_pad]
+};
+
+constexpr int kMaxLayers = 64;
+
+// the dense feed-forward's hidden width (dim * 4 / 3, [ZS §MoE]) and the
+// width it is stored with: zero rows / columns up to the matrix-product
+// granularity (K multiple of 64 for bf16, 4 for fp32)
+int dense_width(const rdt_config& c) { return c.dim * 4 / 3; }
+int dense_width_padded(const rdt_config& c) { return round_up(dense_width(c), c.weight_dtype == RDT_BF16 ? 64 : 4); }
+
+enum MwsId { MWS_X, MWS_Y, MWS_HOUT, MWS_HALT, MWS_ACTD, MWS_NORM, MWS_LAST, MWS_COUNT };
+
+struct ModelPlan {
+  Plan blk;   // the recurrent stage's plan, also used by the dense layers, at offset 0
+  size_t off[MWS_COUNT];
+  size_t total;
+};
+
+ModelPlan make_model_plan(const rdt_model_config& mc, int B, int T) {
+  ModelPlan mp;
+  mp.blk = make_plan(mc.block, B, T);
+  const size_t N = (size_t)B * T, D = mc.block.dim, es = esize(mc.block), V = mc.vocab_size;
+  const size_t sz[MWS_COUNT] = {N * D * 4, N * D * 4, N * D * 4, N * 4, N * dense_width_padded(mc.block) * es,
+                                N * D * es, (size_t)B * V * 4};
+  size_t o = align256(mp.blk.total);
+  for (int i = 0; i < MWS_COUNT; ++i) {
+    mp.off[i] = o;
+    o += align256(sz[i]);
+  }
+  mp.total = o;
+  return mp;
+}
+
+rdt_status check_model_config(const rdt_model_config* mc) {
+  if (!mc) return fail(RDT_E_INVALID_ARG, "model config is NULL");
+  rdt_status st = check_config(&mc->block);
+  if (st) return st;
+  if (mc->vocab_size < 1) return fail(RDT_E_INVALID_ARG, "vocab_size must be >= 1");
+  if (mc->prelude_layers < 0 || mc->prelude_layers > kMaxLayers || mc->coda_layers < 0 ||
+      mc->coda_layers > kMaxLayers)
+    return fail(RDT_E_INVALID_ARG, "prelude_layers and coda_layers must be in [0, %d]", kMaxLayers);
+  return RDT_OK;
+}
+
+}  // namespace
+
+struct rdt_model {
+  rdt_model_config cfg;
+  rdt_block* blk = nullptr;
+  char* mem = nullptr;
+  const void* embed = nullptr;
+  const float* final_norm = nullptr;
+  const void* head = nullptr;
+  std::vector<ModelLayer> layers;   // prelude layers, then coda layers
+};
+
+namespace {
+
+// One prelude / coda layer on x.Mr rows: x1 = xin + Attn(RMSNorm(xin)),
+// xout = x1 + W2 (silu(W1 f) * (W3 f)), f = RMSNorm(x1).
+void dense_layer(const rdt_model* m, const ModelLayer& L, const Ctx& x, const float* xin, float* xout, char* kslot,
+                 int cap_pad, void* actd) {
+  const rdt_config& c = m->cfg.block;
+  const int D = c.dim, N = x.Mr, fp = dense_width_padded(c);
+  launch_rmsnorm(x.bf, xin, D, L.attn_norm, c.norm_eps, x.W(WS_A), D, N, D, x.s);
+  attention_sublayer(x, L.aw, kslot, cap_pad, xin, x.WF(WS_X1));
+  launch_rmsnorm(x.bf, x.WF(WS_X1), D, L.ffn_norm, c.norm_eps, x.W(WS_F), D, N, D, x.s);
+  GemmParams gu = dense_params(x.W(WS_F), D, L.w1, L.w3, N, fp, D);
+  gu.epi.out = actd;
+  gu.epi.ldo = fp;
+  x.gemm(gu, EPI_SWIGLU, true, x.bf);
+  GemmParams gd = dense_params(actd, fp, L.w2, nullptr, N, D, fp);
+  gd.epi.out = xout;
+  gd.epi.ldo = D;
+  gd.epi.resid = x.WF(WS_X1);
+  x.gemm(gd, EPI_RESID, false, 0);
+}
+
+// The model forward on B sequences of T tokens.  logits: [B T, V] fp32, or
+// null; with `choose` set only the last position of each sequence goes
+// through the final norm and the head, and its argmax is written to
+// choose[b * choose_ld].
+rdt_status model_run(rdt_model* m, const int32_t* ids, int64_t ids_ld, int B, int T, int start_pos, int n_loops,
+                     float thr, void* kv, int kv_capacity, size_t kv_bytes, void* ws, size_t ws_bytes,
+                     float* logits, int32_t* choose, int64_t choose_ld, hipStream_t s) {
+  const rdt_model_config& mc = m->cfg;
+  const rdt_config& c = mc.block;
+  if (!ids || (!logits && !choose)) return fail(RDT_E_INVALID_ARG, "ids and logits must be non-NULL");
+  if (B < 1 || T < 1) return fail(RDT_E_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
+  if (ids_ld < T) return fail(RDT_E_INVALID_ARG, "ids_ld %lld below T %d", (long long)ids_ld, T);
+  if (n_loops < 1 || n_loops > RDT_MAX_LOOPS) return fail(RDT_E_INVALID_ARG, "n_loops must be in [1, %d]", RDT_MAX_LOOPS);
+  const int P = mc.prelude_layers, C = mc.coda_layers;
+  size_t slot = 0;
+  if (kv) {
+    slot = kv_slot_bytes(c, B, kv_capacity);
+    if ((int64_t)start_pos + T > kv_capacity)
+      return fail(RDT_E_INVALID_ARG, "start_pos + T exceeds kv_capacity %d", kv_capacity);
+    const size_t need = slot * (size_t)(P + n_loops + C);
+    if (kv_bytes < need)
+      return fail(RDT_E_INVALID_ARG, "model cache holds %zu bytes, %d slots need %zu", kv_bytes, P + n_loops + C, need);
+  }
+  if ((int64_t)start_pos + T > c.max_seq_len)
+    return fail(RDT_E_INVALID_ARG, "start_pos + T exceeds max_seq_len %d", c.max_seq_len);
+  if (!ws) return fail(RDT_E_INVALID_ARG, "workspace is NULL");
+  const ModelPlan mp = make_model_plan(mc, B, T);
+  if (ws_bytes < mp.total) return fail(RDT_E_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, mp.total);
+  if (((uintptr_t)ws) & 255) return fail(RDT_E_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  char* w = (char*)ws;
+  auto MW = [&](int id) { return w + mp.off[id]; };
+  const bool bf = c.weight_dtype == RDT_BF16;
+  const int N = B * T, D = c.dim, V = mc.vocab_size;
+  const int cap_pad = round_up(kv_capacity > 0 ? kv_capacity : 1, 64);
+  Ctx x{m->blk, &c, &mp.blk, w, s, bf, B, T, start_pos, N, nullptr, nullptr};
+  float* cur = (float*)MW(MWS_X);
+  float* nxt = (float*)MW(MWS_Y);
+  launch_embed(bf, ids, ids_ld, B, T, m->embed, V, D, cur, s);
+  for (int l = 0; l < P; ++l) {
+    dense_layer(m, m->layers[l], x, cur, nxt, kv ? (char*)kv + slot * l : nullptr, cap_pad, MW(MWS_ACTD));
+    std::swap(cur, nxt);
+  }
+  // e = x: the prelude output is both the anchor and the initial state
+  float* hout = (float*)MW(MWS_HOUT);
+  rdt_status st = run(m->blk, cur, cur, B, T, start_pos, n_loops, thr, kv ? (char*)kv + slot * P : nullptr,
+                      kv_capacity, kv ? slot * (size_t)n_loops : 0, ws, mp.blk.total, hout, (int32_t*)MW(MWS_HALT),
+                      s, kv != nullptr && T == 1);
+  if (st) return st;
+  cur = hout;
+  nxt = (float*)MW(MWS_X);
+  for (int j = 0; j < C; ++j) {
+    dense_layer(m, m->layers[P + j], x, cur, nxt, kv ? (char*)kv + slot * (P + n_loops + j) : nullptr, cap_pad,
+                MW(MWS_ACTD));
+    cur = nxt;
+    nxt = (float*)MW(j % 2 == 0 ? MWS_Y : MWS_X);
+  }
+  // final norm and LM head: every position, or the last of each sequence
+  const int rows = choose ? B : N;
+  if (choose)
+    launch_rmsnorm(bf, cur + (size_t)(T - 1) * D, (int64_t)T * D, m->final_norm, c.norm_eps, MW(MWS_NORM), D, B, D, s);
+  else
+    launch_rmsnorm(bf, cur, D, m->final_norm, c.norm_eps, MW(MWS_NORM), D, N, D, s);
+  float* out = choose ? (float*)MW(MWS_LAST) : logits;
+  GemmParams gh = dense_params(MW(MWS_NORM), D, m->head, nullptr, rows, V, D);
+  gh.epi.out = out;
+  gh.epi.ldo = V;
+  x.Mr = rows;
+  x.gemm(gh, EPI_STORE, false, 0);
+  if (choose) launch_argmax_rows(out, B, V, choose, choose_ld, s);
+  hipError_t he = hipGetLastError();
+  if (he != hipSuccess) return fail(RDT_E_HIP, "kernel launch: %s", hipGetErrorString(he));
+  return RDT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rdt_status rdt_model_create(const rdt_model_config* cfg, const void* const* block_weights,
+                            const void* const* model_weights, const void* const* layer_weights, void* stream,
+                            rdt_model** out) {
+  g_err.clear();
+  if (!out) return fail(RDT_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  rdt_status st = check_model_config(cfg);
+  if (st) return st;
+  if (!model_weights || (!layer_weights && cfg->prelude_layers + cfg->coda_layers > 0))
+    return fail(RDT_E_INVALID_ARG, "model_weights / layer_weights is NULL");
+  const rdt_config& c = cfg->block;
+  const int nl = cfg->prelude_layers + cfg->coda_layers;
+  const size_t es = esize(c), D = c.dim, V = cfg->vocab_size, H = c.n_heads;
+  const size_t fd = dense_width(c), fp = dense_width_padded(c);
+  for (int i = 0; i < RDT_MW_COUNT; ++i)
+    if (!model_weights[i]) return fail(RDT_E_INVALID_ARG, "model tensor %d is NULL", i);
+  // per-layer tensors: (id, elements, matrix?)
+  struct LT { int id; size_t numel; bool matrix; };
+  std::vector<LT> lt;
+  lt.push_back({RDT_LW_ATTN_NORM, D, false});
+  if (is_gqa(c)) {
+    const size_t dh = c.head_dim, G = c.n_kv_heads;
+    lt.push_back({RDT_LW_WQ, H * dh * D, true});
+    lt.push_back({RDT_LW_WK, G * dh * D, true});
+    lt.push_back({RDT_LW_WV, G * dh * D, true});
+    lt.push_back({RDT_LW_WO, D * H * dh, true});
+  } else {
+    const size_t ql = c.q_lora_rank, kvl = c.kv_lora_rank, rope = c.qk_rope_head_dim, nope = c.qk_nope_head_dim,
+                 vd = c.v_head_dim;
+    lt.push_back({RDT_LW_WDQ, ql * D, true});
+    lt.push_back({RDT_LW_GQ, ql, false});
+    lt.push_back({RDT_LW_WUQ, H * (nope + rope) * ql, true});
+    lt.push_back({RDT_LW_WDKV, (kvl + rope) * D, true});
+    lt.push_back({RDT_LW_GKV, kvl, false});
+    lt.push_back({RDT_LW_WUKV, H * (nope + vd) * kvl, true});
+    lt.push_back({RDT_LW_WO, D * H * vd, true});
+  }
+  lt.push_back({RDT_LW_FFN_NORM, D, false});
+  for (int l = 0; l < nl; ++l)
+    for (const LT& t : lt)
+      if (!layer_weights[(size_t)l * RDT_LW_COUNT + t.id])
+        return fail(RDT_E_INVALID_ARG, "layer %d tensor %d is NULL", l, t.id);
+  for (int l = 0; l < nl; ++l)
+    for (int id : {RDT_LW_W1, RDT_LW_W3, RDT_LW_W2})
+      if (!layer_weights[(size_t)l * RDT_LW_COUNT + id]) return fail(RDT_E_INVALID_ARG, "layer %d tensor %d is NULL", l, id);
+
+  // layout: embed, final norm, head, then per layer its tensors (q, k, v
+  // back to back) and the padded feed-forward matrices
+  size_t o = 0;
+  const size_t off_embed = o;
+  o = align256(o + V * D * es);
+  const size_t off_fnorm = o;
+  o = align256(o + D * 4);
+  const size_t off_head = o;
+  o = align256(o + V * D * es);
+  std::vector<std::vector<size_t>> loff(nl, std::vector<size_t>(RDT_LW_COUNT, 0));
+  for (int l = 0; l < nl; ++l) {
+    for (const LT& t : lt) {
+      const bool packed = t.id == RDT_LW_WK || t.id == RDT_LW_WV;
+      if (!packed) o = align256(o);
+      loff[l][t.id] = o;
+      o += t.numel * (t.matrix ? es : 4);
+    }
+    o = align256(o);
+    loff[l][RDT_LW_W1] = o;
+    o = align256(o + fp * D * es);
+    loff[l][RDT_LW_W3] = o;
+    o = align256(o + fp * D * es);
+    loff[l][RDT_LW_W2] = o;
+    o = align256(o + D * fp * es);
+  }
+  rdt_model* m = new rdt_model();
+  m->cfg = *cfg;
+  st = rdt_block_create(&c, block_weights, stream, &m->blk);
+  if (st) {
+    delete m;
+    return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t he = hipMalloc((void**)&m->mem, o);
+  if (he != hipSuccess) {
+    (void)rdt_block_destroy(m->blk);
+    delete m;
+    return fail(he == hipErrorOutOfMemory ? RDT_E_OUT_OF_MEMORY : RDT_E_HIP, "hipMalloc(%zu): %s", o,
+                hipGetErrorString(he));
+  }
+  auto cp = [&](size_t off, const void* src, size_t bytes) {
+    if (he == hipSuccess) he = hipMemcpyAsync(m->mem + off, src, bytes, hipMemcpyDeviceToDevice, s);
+  };
+  cp(off_embed, model_weights[RDT_MW_EMBED], V * D * es);
+  cp(off_fnorm, model_weights[RDT_MW_FINAL_NORM], D * 4);
+  cp(off_head, model_weights[RDT_MW_HEAD], V * D * es);
+  m->embed = m->mem + off_embed;
+  m->final_norm = (const float*)(m->mem + off_fnorm);
+  m->head = m->mem + off_head;
+  m->layers.resize(nl);
+  for (int l = 0; l < nl; ++l) {
+    const void* const* lw = layer_weights + (size_t)l * RDT_LW_COUNT;
+    for (const LT& t : lt) cp(loff[l][t.id], lw[t.id], t.numel * (t.matrix ? es : 4));
+    // gate and up: fd rows, then zero rows to fp; down: fd columns of each
+    // of the D rows, then zero columns to fp
+    for (int id : {RDT_LW_W1, RDT_LW_W3}) {
+      cp(loff[l][id], lw[id], fd * D * es);
+      if (he == hipSuccess && fp > fd) he = hipMemsetAsync(m->mem + loff[l][id] + fd * D * es, 0, (fp - fd) * D * es, s);
+    }
+    if (he == hipSuccess)
+      he = hipMemcpy2DAsync(m->mem + loff[l][RDT_LW_W2], fp * es, lw[RDT_LW_W2], fd * es, fd * es, D,
+                            hipMemcpyDeviceToDevice, s);
+    if (he == hipSuccess && fp > fd)
+      he = hipMemset2DAsync(m->mem + loff[l][RDT_LW_W2] + fd * es, fp * es, 0, (fp - fd) * es, D, s);
+    ModelLayer& L = m->layers[l];
+    auto at = [&](int id) -> const void* { return m->mem + loff[l][id]; };
+    L.attn_norm = (const float*)at(RDT_LW_ATTN_NORM);
+    L.ffn_norm = (const float*)at(RDT_LW_FFN_NORM);
+    L.w1 = at(RDT_LW_W1);
+    L.w3 = at(RDT_LW_W3);
+    L.w2 = at(RDT_LW_W2);
+    L.aw.wo = at(RDT_LW_WO);
+    if (is_gqa(c)) {
+      L.aw.wqkv = at(RDT_LW_WQ);
+    } else {
+      L.aw.wdq = at(RDT_LW_WDQ);
+      L.aw.gq = (const float*)at(RDT_LW_GQ);
+      L.aw.wuq = at(RDT_LW_WUQ);
+      L.aw.wdkv = at(RDT_LW_WDKV);
+      L.aw.gkv = (const float*)at(RDT_LW_GKV);
+      L.aw.wukv = at(RDT_LW_WUKV);
+    }
+  }
+  if (he == hipSuccess) he = hipStreamSynchronize(s);
+  if (he != hipSuccess) {
+    (void)hipFree(m->mem);
+    (void)rdt_block_destroy(m->blk);
+    delete m;
+    return fail(RDT_E_HIP, "model create: %s", hipGetErrorString(he));
+  }
+  *out = m;
+  return RDT_OK;
+}
+
+rdt_status rdt_model_destroy(rdt_model* m) {
+  if (!m) return RDT_OK;
+  rdt_status st = rdt_block_destroy(m->blk);
+  if (m->mem) (void)hipFree(m->mem);
+  delete m;
+  return st;
+}
+
+rdt_status rdt_model_block(const rdt_model* m, rdt_block** blk) {
+  if (!m || !blk) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  *blk = m->blk;
+  return RDT_OK;
+}
+
+rdt_status rdt_model_workspace_bytes(const rdt_model* m, int32_t B, int32_t T, size_t* bytes) {
+  if (!m || !bytes) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  if (B < 1 || T < 1) return fail(RDT_E_INVALID_ARG, "B and T must be >= 1");
+  *bytes = make_model_plan(m->cfg, B, T).total;
+  return RDT_OK;
+}
+
+rdt_status rdt_model_kv_cache_bytes(const rdt_model* m, int32_t B, int32_t capacity, int32_t n_loops,
+                                    size_t* bytes) {
+  if (!m || !bytes) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  if (B < 1 || capacity < 1 || n_loops < 1) return fail(RDT_E_INVALID_ARG, "B, capacity and n_loops must be >= 1");
+  *bytes = kv_slot_bytes(m->cfg.block, B, capacity) *
+           (size_t)(m->cfg.prelude_layers + n_loops + m->cfg.coda_layers);
+  return RDT_OK;
+}
+
+rdt_status rdt_model_forward(rdt_model* m, const int32_t* ids, int64_t ids_ld, int32_t B, int32_t T,
+                             int32_t start_pos, int32_t n_loops, float act_threshold, void* kv_cache,
+                             int32_t kv_capacity, size_t kv_bytes, void* workspace, size_t ws_bytes,
+                             float* logits, void* stream) {
+  g_err.clear();
+  if (!m) return fail(RDT_E_INVALID_ARG, "model is NULL");
+  if (!logits) return fail(RDT_E_INVALID_ARG, "logits is NULL");
+  return model_run(m, ids, ids_ld, B, T, start_pos, n_loops, act_threshold, kv_cache, kv_capacity, kv_bytes,
+                   workspace, ws_bytes, logits, nullptr, 0, (hipStream_t)stream);
+}
+
+rdt_status rdt_model_generate(rdt_model* m, const int32_t* prompt, int32_t B, int32_t T0, int32_t max_new,
+                              int32_t n_loops, float act_threshold, void* kv_cache, int32_t kv_capacity,
+                              size_t kv_bytes, void* workspace, size_t ws_bytes, int32_t* out_ids,
+                              void* stream) {
+  g_err.clear();
+  if (!m || !prompt || !out_ids) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  if (max_new < 1) return fail(RDT_E_INVALID_ARG, "max_new must be >= 1");
+  if (B < 1 || T0 < 1) return fail(RDT_E_INVALID_ARG, "B and T0 must be >= 1");
+  if (!kv_cache) return fail(RDT_E_BAD_STATE, "generation needs the model cache");
+  const int64_t L = (int64_t)T0 + max_new;
+  if (L > kv_capacity) return fail(RDT_E_INVALID_ARG, "T0 + max_new exceeds kv_capacity %d", kv_capacity);
+  if (L > m->cfg.block.max_seq_len) return fail(RDT_E_INVALID_ARG, "T0 + max_new exceeds max_seq_len");
+  const size_t need = make_model_plan(m->cfg, B, T0).total;
+  if (ws_bytes < need) return fail(RDT_E_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipMemcpy2DAsync(out_ids, L * 4, prompt, (size_t)T0 * 4, (size_t)T0 * 4, B, hipMemcpyDeviceToDevice, s));
+  rdt_status st = model_run(m, prompt, T0, B, T0, 0, n_loops, act_threshold, kv_cache, kv_capacity, kv_bytes,
+                            workspace, ws_bytes, nullptr, out_ids + T0, L, s);
+  for (int step = 1; st == RDT_OK && step < max_new; ++step)
+    st = model_run(m, out_ids + T0 + step - 1, L, B, 1, T0 + step - 1, n_loops, act_threshold, kv_cache,
+                   kv_capacity, kv_bytes, workspace, ws_bytes, nullptr, out_ids + T0 + step, L, s);
+  return st;
+}
+
+}  // extern "C"
