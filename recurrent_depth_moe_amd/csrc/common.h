@@ -99,5 +99,10 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU with the hardware exponential and reciprocal (v_exp_f32, v_rcp_f32,
+// each within about one ulp): an IEEE-rounded division costs a dozen
+// instructions per element, which the GEMM epilogues that apply it to every
+// gate value cannot hide.  For x below about -88 the exponential overflows
+// to +inf and the reciprocal to 0, so the result is -0, as the limit is.
+__device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }

@@ -76,15 +76,15 @@ __device__ __forceinline__ void g2lds(const void* src, uint4* lds_slot0) {
 }
 
 // Fragments of one 32-deep half (hh = 0, 1) of a 64-deep stage for this
-// wave, for v_mfma_f32_32x32x16_bf16 (two 16-deep k-steps): 4 A fragments
-// (32 rows each) and 4 B fragments (32 columns each) per k-step; lane l
+// wave, for v_mfma_f32_32x32x16_bf16 (two 16-deep k-steps): FMW A fragments
+// (32 rows each) and WNF B fragments (32 columns each) per k-step; lane l
 // holds row/column l % 32 and k values 8 * (l / 32) .. +7 of the k-step.
 // Rows hold 8 chunks of 8 k (128 bytes); chunk c of row r sits at position
 // c ^ ((r >> 1) & 7), so the 8 rows a quarter-wave reads land in distinct
 // banks.
-template <int WNF>
+template <int WNF, int FMW>
 __device__ __forceinline__ void read_frags(const uint4* sA, const uint4* sB, int wm, int wn, int lane, int hh,
-                                           bf16x8_t (&af)[8], bf16x8_t (&bf)[2 * WNF]) {
+                                           bf16x8_t (&af)[2 * FMW], bf16x8_t (&bf)[2 * WNF]) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int c = 4 * hh + 2 * s + (lane >> 5);
@@ -94,23 +94,23 @@ __device__ __forceinline__ void read_frags(const uint4* sA, const uint4* sB, int
       bf[s * WNF + j] = __builtin_bit_cast(bf16x8_t, sB[r * 8 + (c ^ ((r >> 1) & 7))]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + (lane & 31);
-      af[s * 4 + i] = __builtin_bit_cast(bf16x8_t, sA[r * 8 + (c ^ ((r >> 1) & 7))]);
+    for (int i = 0; i < FMW; ++i) {
+      const int r = wm * (32 * FMW) + i * 32 + (lane & 31);
+      af[s * FMW + i] = __builtin_bit_cast(bf16x8_t, sA[r * 8 + (c ^ ((r >> 1) & 7))]);
     }
   }
 }
 
-template <int WNF>
-__device__ __forceinline__ void mfma_stage(const bf16x8_t (&af)[8], const bf16x8_t (&bf)[2 * WNF],
-                                           floatx16_t (&acc)[4][WNF]) {
+template <int WNF, int FMW>
+__device__ __forceinline__ void mfma_stage(const bf16x8_t (&af)[2 * FMW], const bf16x8_t (&bf)[2 * WNF],
+                                           floatx16_t (&acc)[FMW][WNF]) {
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FMW; ++i)
 #pragma unroll
       for (int j = 0; j < WNF; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s * 4 + i], bf[s * WNF + j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s * FMW + i], bf[s * WNF + j], acc[i][j], 0, 0, 0);
 }
 
 // wait until at most `n` direct-to-LDS loads of this wave are in flight
@@ -121,6 +121,12 @@ __device__ __forceinline__ void wait_vm(int n) {
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at max: the epilogues
+// pass accumulators between lanes through LDS and wait for those LDS
+// accesses only, so the global stores of one 32-row pass stay in flight
+// while the next pass runs
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at max
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -130,20 +136,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // A tile with at most SR (64 or 128) valid rows: the tail of a routed
 // expert's rows, or the last rows of a dense product.  Only A rows 0..SR-1
-// are loaded and each wave computes those rows for a quarter of the
-// columns (for gate|up: 32 gate and the matching 32 up columns), so the
-// tile costs SR/256 of a full tile's MFMAs.  With so little math per stage
-// the loads set the pace, so the smaller stages (A 8 or 16 KB + B 32 KB)
-// run in a deeper ring: 4 stages for 64 rows, 3 for 128.
-template <int SR, bool DUAL, int EPI, typename TO>
+// are loaded and each wave computes those rows for 64 of the columns (for
+// gate|up: 32 gate and the matching 32 up columns), so the tile costs
+// SR/256 of a full tile's MFMAs.  192-column tiles (WNF = 3) give waves 0-2
+// 64 columns each; wave 3 repeats wave 2's columns and stores nothing, so
+// every wave issues the same instructions.  With so little math per stage
+// the loads set the pace, so the smaller stages (A 8 or 16 KB + B 24 or 32
+// KB) run in a deeper ring: 4 stages for 64 rows, 3 for 128.
+template <int SR, bool DUAL, int EPI, typename TO, int WNF>
 __device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, const bf16_t* const* asrc,
-                                           const bf16_t* const (&bsrc)[8], int w, int lane, int rows, int row0,
-                                           int n0, int KT) {
+                                           const bf16_t* const (&bsrc)[2 * WNF], int w, int lane, int rows,
+                                           int row0, int n0, int KT) {
+  static_assert(WNF == 4 || (WNF == 3 && !DUAL), "gate|up tiles are 256 columns wide");
   constexpr int FM = SR / 32;                  // 32-row fragments
   constexpr int SA_IT = SR / 32;               // A rows 0..SR-1 sit in LDS slots 0..SR*8-1
-  constexpr int B_IT = 8;
+  constexpr int B_IT = 2 * WNF;                // B rows 64 WNF: 512 WNF chunks over 256 threads
   constexpr int IT = SA_IT + B_IT;             // loads per thread and stage
-  constexpr int SA_CH = SR * 8, STG = SA_CH + 2048;
+  constexpr int SA_CH = SR * 8, STG = SA_CH + 512 * WNF;
   constexpr int NS = SR == 64 ? 4 : 3;
   static_assert(NS * STG * 16 <= LDS_BYTES, "stages fit in LDS");
   auto issue = [&](int stage, int k0) {
@@ -153,7 +162,9 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, con
 #pragma unroll
     for (int j = 0; j < B_IT; ++j) g2lds(bsrc[j] + k0, base + SA_CH + (j * 4 + w) * 64);
   };
-  const int brow0 = DUAL ? (w >> 1) * 128 + (w & 1) * 32 : 64 * w;
+  const int wc = WNF == 3 ? min(w, 2) : w;    // this wave's 64-column group
+  const bool wstore = WNF == 4 || w < 3;
+  const int brow0 = DUAL ? (w >> 1) * 128 + (w & 1) * 32 : 64 * wc;
   const int brow1 = DUAL ? brow0 + 64 : brow0 + 32;
   auto read = [&](int stage, int hh, bf16x8_t (&af)[2 * FM], bf16x8_t (&bf)[4]) {
     const uint4* sA = smem + stage * STG;
@@ -223,7 +234,7 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, con
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = acc[pass][j][e];
-      __builtin_amdgcn_s_waitcnt(0);
+      wait_lgkm0();
       __builtin_amdgcn_wave_barrier();
       if constexpr (DUAL) {
         // 32 output columns: gate at patch columns 0..31, up at 32..63
@@ -247,10 +258,10 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, con
           float val[8];
 #pragma unroll
           for (int x = 0; x < 8; ++x) val[x] = ep[rl * EP_LD + c8 + x];
-          if (ml < rows) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + 64 * w + c8, val, val);
+          if (ml < rows && wstore) epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, n0 + 64 * wc + c8, val, val);
         }
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      wait_lgkm0();
       __builtin_amdgcn_wave_barrier();
     }
   }
@@ -368,8 +379,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     // earlier)
     uint4* const sAbuf = smem;
     uint4* const sBbuf = smem + 2 * A_CHS;
-    auto issueA = [&](int buf, int k0, auto strip_c) {
-      constexpr int n = A_IT + decltype(strip_c)::value;   // one load per thread and 32-row strip
+    auto issueA = [&](int buf, int k0, auto n_c) {
+      constexpr int n = decltype(n_c)::value;   // A_IT (+ one per 32-row strip), or fewer for a 192-row tile
 #pragma unroll
       for (int j = 0; j < n; ++j) g2lds(asrc[j] + k0, sAbuf + buf * A_CHS + (j * 4 + w) * 64);
     };
@@ -378,25 +389,30 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       for (int j = 0; j < B_IT; ++j) g2lds(bsrc[j] + k0, sBbuf + buf * B_CH + (j * 4 + w) * 64);
     };
 
-    if constexpr (EPI != EPI_QKV && WNF == 4) {   // (QKV rows come in full tiles but the last; its epilogue is the heaviest)
+    if constexpr (EPI != EPI_QKV) {   // (QKV rows come in full tiles but the last; its epilogue is the heaviest)
       if (rows <= 64) {
-        small_tile<64, DUAL, EPI, TO>(p, smem, asrc, bsrc, w, lane, rows, row0, n0, KT);
+        small_tile<64, DUAL, EPI, TO, WNF>(p, smem, asrc, bsrc, w, lane, rows, row0, n0, KT);
         continue;
       }
       if (rows <= 128) {
-        small_tile<128, DUAL, EPI, TO>(p, smem, asrc, bsrc, w, lane, rows, row0, n0, KT);
+        small_tile<128, DUAL, EPI, TO, WNF>(p, smem, asrc, bsrc, w, lane, rows, row0, n0, KT);
         continue;
       }
     }
 
-    auto full_tile = [&](auto strip_c) {
+    auto full_tile = [&](auto strip_c, auto fmw_c) {
       constexpr int NSTR = decltype(strip_c)::value;   // 32-row strips (0, 1, 2)
+      constexpr int FMW = decltype(fmw_c)::value;      // 32-row fragments per wave: 4 (256-row tile) or 3 (192)
+      constexpr int WTMF = 32 * FMW;                   // rows per wave
+      constexpr int A_ITF = 2 * FMW;                   // A loads per thread and stage (rows 0 .. 64 FMW - 1)
+      static_assert(FMW == 4 || NSTR == 0, "strips follow 256-row tiles");
+      constexpr std::integral_constant<int, A_ITF + NSTR> na_c{};
       constexpr bool S = NSTR > 0;
       constexpr int NMS = 4 * NSTR, NDS = 2 * NSTR;   // strip MFMAs / fragment reads per half stage
       constexpr int NSA = NSTR > 0 ? NSTR : 1;        // array extents
-      floatx16_t acc[4][WNF];
+      floatx16_t acc[FMW][WNF];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FMW; ++i)
 #pragma unroll
         for (int j = 0; j < WNF; ++j)
 #pragma unroll
@@ -433,31 +449,31 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
         }
       };
       // 32-row fragments of this wave that hold at least one valid row
-      const int fm_valid = max(0, min(4, (rows - wm * WTM + 31) / 32));
+      const int fm_valid = max(0, min(FMW, (rows - wm * WTMF + 31) / 32));
 
       // prologue: A stages 0, 1 and B stages 0, 1, 2 in flight, first half
       // of stage 0 read (past the end of K, loads repeat the last stage into
       // a buffer nobody reads)
-      issueA(0, 0, strip_c);
+      issueA(0, 0, na_c);
       issueB(0, 0);
-      issueA(1, min(1, KT - 1) * BK, strip_c);
+      issueA(1, min(1, KT - 1) * BK, na_c);
       issueB(1, min(1, KT - 1) * BK);
       issueB(2, min(2, KT - 1) * BK);
-      bf16x8_t fa0[8], fb0[2 * WNF], fa1[8], fb1[2 * WNF], fs0[NSA][2], fs1[NSA][2];
-      wait_vmcnt<A_IT + NSTR + 2 * B_IT>();
+      bf16x8_t fa0[2 * FMW], fb0[2 * WNF], fa1[2 * FMW], fb1[2 * WNF], fs0[NSA][2], fs1[NSA][2];
+      wait_vmcnt<A_ITF + NSTR + 2 * B_IT>();
       __syncthreads();
-      read_frags<WNF>(sAbuf, sBbuf, wm, wn, lane, 0, fa0, fb0);
+      read_frags<WNF, FMW>(sAbuf, sBbuf, wm, wn, lane, 0, fa0, fb0);
       if constexpr (S) read_strip(sAbuf, 0, fs0);
       int b3 = 0;   // kt % 3
       for (int kt = 0; kt < KT; ++kt) {
         const int b3n = b3 == 2 ? 0 : b3 + 1;
         {
           // first half of stage kt (registers fa0/fb0); read its second half
-          read_frags<WNF>(sAbuf + (kt & 1) * A_CHS, sBbuf + b3 * B_CH, wm, wn, lane, 1, fa1, fb1);
+          read_frags<WNF, FMW>(sAbuf + (kt & 1) * A_CHS, sBbuf + b3 * B_CH, wm, wn, lane, 1, fa1, fb1);
           if constexpr (S) read_strip(sAbuf + (kt & 1) * A_CHS, 1, fs1);
-          mfma_stage<WNF>(fa0, fb0, acc);
+          mfma_stage<WNF, FMW>(fa0, fb0, acc);
           if constexpr (S) strip_mfma(fs0, fb0);
-          interleave_first_half<8 * WNF + NMS, 8 + 2 * WNF + NDS>();
+          interleave_first_half<2 * FMW * WNF + NMS, 2 * FMW + 2 * WNF + NDS>();
           __builtin_amdgcn_sched_barrier(0);
         }
         {
@@ -469,13 +485,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
           __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
           __syncthreads();
           __builtin_amdgcn_sched_barrier(0);
-          issueA(kt & 1, min(kt + 2, KT - 1) * BK, strip_c);
+          issueA(kt & 1, min(kt + 2, KT - 1) * BK, na_c);
           issueB(b3, min(kt + 3, KT - 1) * BK);
-          read_frags<WNF>(sAbuf + ((kt + 1) & 1) * A_CHS, sBbuf + b3n * B_CH, wm, wn, lane, 0, fa0, fb0);
+          read_frags<WNF, FMW>(sAbuf + ((kt + 1) & 1) * A_CHS, sBbuf + b3n * B_CH, wm, wn, lane, 0, fa0, fb0);
           if constexpr (S) read_strip(sAbuf + ((kt + 1) & 1) * A_CHS, 0, fs0);
-          mfma_stage<WNF>(fa1, fb1, acc);
+          mfma_stage<WNF, FMW>(fa1, fb1, acc);
           if constexpr (S) strip_mfma(fs1, fb1);
-          interleave_second_half<8 * WNF + NMS, 8 + 2 * WNF + NDS, A_IT + NSTR + B_IT>();
+          interleave_second_half<2 * FMW * WNF + NMS, 2 * FMW + 2 * WNF + NDS, A_ITF + NSTR + B_IT>();
           __builtin_amdgcn_sched_barrier(0);
         }
         b3 = b3n;
@@ -492,21 +508,21 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       {
         float* ep = (float*)smem + w * (32 * EP_LD);
 #pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
+        for (int pass = 0; pass < FMW; ++pass) {
           if (pass < fm_valid) {
 #pragma unroll
             for (int j = 0; j < WNF; ++j)
 #pragma unroll
               for (int e = 0; e < 16; ++e)
                 ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = acc[pass][j][e];
-            __builtin_amdgcn_s_waitcnt(0);
+            wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
             if constexpr (DUAL) {
               // 64 output columns: gate at patch columns 0..63, up at 64..127
 #pragma unroll 1
               for (int it = 0; it < 4; ++it) {
                 const int rl = it * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-                const int ml = wm * WTM + pass * 32 + rl;
+                const int ml = wm * WTMF + pass * 32 + rl;
                 float g[8], u[8];
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
@@ -524,7 +540,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
 #pragma unroll 1
               for (int it = 0; it < 32 * WTN / (8 * 64); ++it) {
                 const int idx = it * 64 + lane, c = idx % WTN, rg = idx / WTN;
-                const int ml = wm * WTM + pass * 32 + rg * 8;
+                const int ml = wm * WTMF + pass * 32 + rg * 8;
                 const int n = n0 + wn * WTN + c;
                 if (ml >= rows || n >= p.N) continue;
                 const int m = row0 + ml, mp = e.tok ? e.tok[m] : m, b = mp / e.T, i = mp - b * e.T;
@@ -560,7 +576,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
 #pragma unroll
                   for (int u = 0; u < PG; ++u) {
                     const int idx = (g0 + u) * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
-                    const int ml = wm * WTM + pass * 32 + rl, n = n0 + wn * WTN + c8;
+                    const int ml = wm * WTMF + pass * 32 + rl, n = n0 + wn * WTN + c8;
                     r[u][0] = r[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
                     if (ml < rows && n + 8 <= p.N) {
                       const float* src = e.resid + (int64_t)(row0 + ml) * e.ldo + n;
@@ -571,7 +587,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
 #pragma unroll
                   for (int u = 0; u < PG; ++u) {
                     const int idx = (g0 + u) * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
-                    const int ml = wm * WTM + pass * 32 + rl, n = n0 + wn * WTN + c8;
+                    const int ml = wm * WTMF + pass * 32 + rl, n = n0 + wn * WTN + c8;
                     if (ml >= rows) continue;
                     float v[8];
 #pragma unroll
@@ -589,7 +605,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
 #pragma unroll 1
                 for (int it = 0; it < NIT; ++it) {
                   const int idx = it * 64 + lane, rl = idx / CG, c8 = (idx - rl * CG) * 8;
-                  const int ml = wm * WTM + pass * 32 + rl;
+                  const int ml = wm * WTMF + pass * 32 + rl;
                   float v[8];
 #pragma unroll
                   for (int x = 0; x < 8; ++x) v[x] = ep[rl * EP_LD + c8 + x];
@@ -597,7 +613,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
                 }
               }
             }
-            __builtin_amdgcn_s_waitcnt(0);
+            wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
           }
         }
@@ -612,7 +628,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
 #pragma unroll
               for (int e = 0; e < 16; ++e)
                 ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = accs[st][j][e];
-            __builtin_amdgcn_s_waitcnt(0);
+            wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
 #pragma unroll 1
             for (int it = 0; it < 4; ++it) {
@@ -625,18 +641,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
                 epi_store8<EPI, TO>(p.epi, p.N, row0 + ml, ncol0 + c8, v, v);
               }
             }
-            __builtin_amdgcn_s_waitcnt(0);
+            wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
           }
         }
       }
     };
-    if constexpr (HAS_STRIP) {
-      if (rows > BM + 32) full_tile(std::integral_constant<int, 2>{});
-      else if (rows > BM) full_tile(std::integral_constant<int, 1>{});
-      else full_tile(std::integral_constant<int, 0>{});
+    using I0 = std::integral_constant<int, 0>;
+    using F4 = std::integral_constant<int, 4>;
+    constexpr bool ROUTED = EPI == EPI_SWIGLU || EPI == EPI_STORE;   // the routed expert products
+    if (ROUTED && rows <= 192) {
+      // 129-192 rows (the last tile of a routed expert): three 32-row
+      // fragments per wave, so the tile costs 3/4 of a full one
+      if constexpr (ROUTED) full_tile(I0{}, std::integral_constant<int, 3>{});
+    } else if constexpr (HAS_STRIP) {
+      if (rows > BM + 32) full_tile(std::integral_constant<int, 2>{}, F4{});
+      else if (rows > BM) full_tile(std::integral_constant<int, 1>{}, F4{});
+      else full_tile(I0{}, F4{});
     } else {
-      full_tile(std::integral_constant<int, 0>{});
+      full_tile(I0{}, F4{});
     }
     __syncthreads();   // the next tile's loads reuse this LDS
   }

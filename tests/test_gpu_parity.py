@@ -111,6 +111,43 @@ def test_end_to_end_merged_expert_tails():
     _e2e(cfg, W, e, h0)
 
 
+def test_end_to_end_short_tiles_of_192_column_products():
+    """dim 768 with 24 experts (about 60 routed rows each): every expert's
+    rows fit one short tile (<= 64 or <= 128 rows) of the routed down
+    product's 192-column tiles, which then loads and multiplies only those
+    rows (three waves store 64 columns each)."""
+    import torch
+    scales = {"w_down": 0.1, "s_down": 0.1}
+    cfg, W, e, h0 = _inputs("small_bf16_strip", scales=scales, n_experts=24, seq=360)
+    run = DeviceRun(cfg, W, e, h0)
+    E = cfg["n_experts"]
+    counts = np.diff(run.ws_np("offsets", torch.int32, (E + 1,)))
+    print(f"  rows per expert {counts.tolist()}", flush=True)
+    assert np.sum(counts <= 64) > 0 and np.sum((counts > 64) & (counts <= 128)) > 0
+    _e2e(cfg, W, e, h0)
+
+
+@pytest.mark.parametrize("over, where", [
+    (dict(seq=300), "only"),                  # 112-212 rows per expert
+    (dict(seq=420, n_experts=4), "second"),   # 371-465 rows: a 256-row tile, then 115-209
+], ids=["only-tile", "second-tile"])
+def test_end_to_end_192_row_tiles(over, where):
+    """Routed tiles of 129-192 rows run with three 32-row fragments per wave
+    (gate|up on 256-column tiles, down on 192-column ones): as an expert's
+    only tile, and as the tile after a full 256-row one."""
+    import torch
+    scales = {"w_down": 0.1, "s_down": 0.1}
+    cfg, W, e, h0 = _inputs("small_bf16_strip", scales=scales, **over)
+    run = DeviceRun(cfg, W, e, h0)
+    E = cfg["n_experts"]
+    counts = np.diff(run.ws_np("offsets", torch.int32, (E + 1,)))
+    print(f"  rows per expert {counts.tolist()}", flush=True)
+    tail = counts % 256 if where == "second" else counts
+    hit = (tail > 128) & (tail <= 192) & ((counts > 256) if where == "second" else (counts <= 256))
+    assert hit.any(), counts
+    _e2e(cfg, W, e, h0)
+
+
 @pytest.mark.parametrize("name, over", [
     ("small_bf16", dict(batch=3, seq=1, n_loops=2)),                         # single-token prefill, no cache
     ("small_bf16", dict(batch=1, seq=5)),                                    # one short sequence
