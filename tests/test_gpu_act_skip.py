@@ -18,7 +18,7 @@ import pytest
 from oracle import rdt_oracle as O
 from workloads import configs, generate
 
-from gpu_support import EPS_HALT, EPS_ROUTE, TOL, DeviceRun, rel_err
+from gpu_support import EPS_HALT, EPS_ROUTE, DeviceRun, loop_tol, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -55,9 +55,9 @@ def _skip_e2e(cfg, W, e, h0):
             idx, osel = ref["record"]["sel"][t]
             np.testing.assert_array_equal(idx, np.nonzero(ran)[0])
             np.testing.assert_array_equal(osel, sel[idx])
-    err = rel_err(g["out"], ref["out"])
-    print(f"  rows per loop {rows_per_loop}; max|d|/rms = {err:.3e} (tol {TOL[dt]})", flush=True)
-    assert err <= TOL[dt]
+    err, tol = rel_err(g["out"], ref["out"]), loop_tol(dt, L)
+    print(f"  rows per loop {rows_per_loop}; max|d|/rms = {err:.3e} (tol {tol:.3g})", flush=True)
+    assert err <= tol
     return g, ref, rows_per_loop
 
 

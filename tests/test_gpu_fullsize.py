@@ -21,7 +21,7 @@ import pytest
 from oracle import rdt_oracle as O
 from workloads import configs, generate
 
-from gpu_support import EPS_HALT, EPS_ROUTE, TOL, DeviceRun, fill_cache, kv_capacity, rel_err
+from gpu_support import EPS_HALT, EPS_ROUTE, TOL, DeviceRun, fill_cache, free_running_tol, kv_capacity, rel_err
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -90,20 +90,6 @@ def _dispatch_and_router(cfg, P, run):
     inv = run.ws_np("inv", torch.int32, (N * k,))
     np.testing.assert_array_equal(perm, order // k)
     np.testing.assert_array_equal(inv[order], np.arange(N * k))
-
-
-def free_running_tol(n_loops):
-    """Tolerance of the final state after n_loops free-running bf16 loops.
-
-    Each loop rounds its matrix-product operands (a, q, k, v, P, o, f, act)
-    and its expert outputs to bf16, which the teacher-forced single-loop
-    check bounds by 3e-2 (max|d| / RMS).  Those per-loop errors then travel
-    with the state: h <- A h + B e + block(h) keeps a fraction A_i of each
-    channel's error, and the channels with A_i near 1 (A = exp(-exp(log_A)),
-    log_A ~ N(0, 1)) barely damp it, so independent per-loop errors add up
-    like a random walk.  The bound is therefore 3e-2 * sqrt(n_loops), and the
-    single-loop 3e-2 where that is smaller."""
-    return max(TOL["bf16"], TOL["bf16"] * float(np.sqrt(n_loops)))
 
 
 def _free_running(cfg, W, e, h0, r, seqs=None, cache=None, state_tol=None):
