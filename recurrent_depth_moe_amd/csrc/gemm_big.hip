@@ -69,6 +69,17 @@ constexpr int LDS_BYTES = 160 * 1024;                // two 64 KB stages; short 
 constexpr int EP_LD = 128 + 4;                      // epilogue patch row stride (floats)
 static_assert(4 * 32 * EP_LD * 4 <= LDS_BYTES, "epilogue patches fit in the tile LDS");
 
+// One 32x32 accumulator into columns 32 j .. 32 j + 31 of a wave's
+// row-major fp32 patch.  The MFMAs take their operands in (B, A) order, so
+// lane l holds output row l % 32 and, in elements 4g .. 4g+3, the four
+// consecutive columns 8g + 4 (l / 32) .. +3: one 16-byte LDS write each
+// (rows 528 bytes apart, so sixteen lanes cover all 64 banks once).
+__device__ __forceinline__ void patch_write(float* ep, int lane, int j, const floatx16_t& a) {
+  float* row = ep + (lane & 31) * EP_LD + j * 32 + 4 * (lane >> 5);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) *(float4*)(row + 8 * g) = make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ void g2lds(const void* src, uint4* lds_slot0) {
@@ -110,7 +121,7 @@ __device__ __forceinline__ void mfma_stage(const bf16x8_t (&af)[2 * FMW], const 
     for (int i = 0; i < FMW; ++i)
 #pragma unroll
       for (int j = 0; j < WNF; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s * FMW + i], bf[s * WNF + j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s * WNF + j], af[s * FMW + i], acc[i][j], 0, 0, 0);
 }
 
 // wait until at most `n` direct-to-LDS loads of this wave are in flight
@@ -198,7 +209,7 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, con
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s * FM + i], bf[s * 2 + j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s * 2 + j], af[s * FM + i], acc[i][j], 0, 0, 0);
   };
   // every buffer loading (past the end of K: repeats of the last stage)
 #pragma unroll
@@ -230,10 +241,7 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, uint4* smem, con
   for (int pass = 0; pass < FM; ++pass) {
     if (pass * 32 < rows) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = acc[pass][j][e];
+      for (int j = 0; j < 2; ++j) patch_write(ep, lane, j, acc[pass][j]);
       wait_lgkm0();
       __builtin_amdgcn_wave_barrier();
       if constexpr (DUAL) {
@@ -443,8 +451,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
           const bf16x8_t b1 = wm ? fb[x * WNF + 2] : fb[x * WNF + 1];
 #pragma unroll
           for (int st = 0; st < NSTR; ++st) {
-            accs[st][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[st][x], b0, accs[st][0], 0, 0, 0);
-            accs[st][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fs[st][x], b1, accs[st][1], 0, 0, 0);
+            accs[st][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, fs[st][x], accs[st][0], 0, 0, 0);
+            accs[st][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, fs[st][x], accs[st][1], 0, 0, 0);
           }
         }
       };
@@ -499,22 +507,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       wait_vm(0);   // the trailing reloads land before the epilogue reuses LDS
       __syncthreads();   // every wave done with the stages before the epilogue reuses LDS
 
-      // Epilogue through LDS, four passes of 32 rows per wave (one fragment
-      // row each): a 32x32 accumulator holds, in lane l and element e, row
-      // 8*(e/4) + 4*(l/32) + e%4 and column l%32.  The values go to a
-      // row-major 32 x 128 fp32 patch of the wave's own LDS region, then each
-      // lane takes 8 consecutive columns of one row, so stores are 16-byte
-      // vectors and RoPE pairs sit in one lane.
+      // Epilogue through LDS, one pass of 32 rows per wave fragment row:
+      // the accumulators go to a row-major 32 x 128 fp32 patch of the
+      // wave's own LDS region with 16-byte writes straight from the
+      // accumulator registers (patch_write), then each lane takes 8
+      // consecutive columns of one row, so stores are 16-byte vectors and
+      // RoPE pairs sit in one lane.
       {
         float* ep = (float*)smem + w * (32 * EP_LD);
 #pragma unroll
         for (int pass = 0; pass < FMW; ++pass) {
           if (pass < fm_valid) {
 #pragma unroll
-            for (int j = 0; j < WNF; ++j)
-#pragma unroll
-              for (int e = 0; e < 16; ++e)
-                ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = acc[pass][j][e];
+            for (int j = 0; j < WNF; ++j) patch_write(ep, lane, j, acc[pass][j]);
             wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
             if constexpr (DUAL) {
@@ -624,10 +629,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
 #pragma unroll
           for (int st = 0; st < NSTR; ++st) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-              for (int e = 0; e < 16; ++e)
-                ep[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * EP_LD + j * 32 + (lane & 31)] = accs[st][j][e];
+            for (int j = 0; j < 2; ++j) patch_write(ep, lane, j, accs[st][j]);
             wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
 #pragma unroll 1
