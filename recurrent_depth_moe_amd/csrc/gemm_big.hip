@@ -314,17 +314,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
 
   // XCD x owns tiles [x * chunk, (x + 1) * chunk), so tiles that share an
   // A or B panel meet in one L2.  Static order: slot s of the XCD takes
-  // every per_xcd-th tile of its share.  Claimed order (tile_ctr): blocks
+  // every per_xcd-th work unit of its share, a unit being a whole tile or,
+  // when the share's last round would leave at least half of the XCD's
+  // blocks idle (e.g. 640 QKV tiles on 256 CUs), one 128-row half of each
+  // of the share's last tiles: every block then ends with a half-cost unit
+  // instead of half the blocks with a whole one.  Claimed order (tile_ctr): blocks
   // take their XCD's tiles one at a time from its counter, then help the
   // other XCDs in turn, so tiles of unequal cost (the short tail tiles of
   // routed experts) level out over the CUs.  The claimed tile index passes
   // through LDS word 0, which no tile uses between its closing barrier and
   // the next tile's first load.
+  const int c0 = xcd * chunk, cnt = max(0, t_end - c0);
+  const int rem = cnt % per_xcd;
+  const int n_split = (p.tile_ctr == nullptr && p.mt_start == nullptr && rem > 0 && 2 * rem <= per_xcd) ? rem : 0;
+  const int n_whole = cnt - n_split, n_units = n_whole + 2 * n_split;
   int src = xcd;   // claimed order: the share thread 0 currently draws from
   auto next_tile = [&](int L) -> int {
     if (p.tile_ctr == nullptr) {
-      L = L < 0 ? xcd * chunk + slot : L + per_xcd;
-      return L < t_end ? L : -1;
+      L = L < 0 ? slot : L + per_xcd;   // a unit of this XCD's share
+      return L < n_units ? L : -1;
     }
     int* const bc = (int*)smem;
     if (tid == 0) {
@@ -345,10 +353,21 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     return got;
   };
 
-  for (int L = next_tile(-1); L >= 0; L = next_tile(L)) {
+  for (int U = next_tile(-1); U >= 0; U = next_tile(U)) {
+    // unit -> tile (and half: -1 for a whole tile)
+    int L = U, half = -1;
+    if (p.tile_ctr == nullptr) {
+      L = c0 + (U < n_whole ? U : n_whole + ((U - n_whole) >> 1));
+      if (U >= n_whole) half = (U - n_whole) & 1;
+    }
     int mt, nt, row0, rows, grp;
     tile_coords(p, L, ntn, n_mt, mt, nt);
     tile_rows(p, mt, BM, row0, rows, grp, HAS_STRIP ? p.strip_rows : 0);
+    if (half >= 0) {
+      row0 += 128 * half;
+      rows = min(rows - 128 * half, 128);
+      if (rows <= 0) continue;   // (uniform: a tile of at most 128 rows has no second half)
+    }
     const int n0 = nt * NCOL;
     const bf16_t* W0 = (const bf16_t*)p.W0 + (int64_t)grp * p.w_stride;
     const bf16_t* W1 = DUAL ? (const bf16_t*)p.W1 + (int64_t)grp * p.w_stride : W0;
@@ -656,6 +675,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
       // 129-192 rows (the last tile of a routed expert): three 32-row
       // fragments per wave, so the tile costs 3/4 of a full one
       if constexpr (ROUTED) full_tile(I0{}, std::integral_constant<int, 3>{});
+    } else if (EPI == EPI_QKV && rows <= 128) {
+      // a half unit or the short last m-tile of the QKV product (which has
+      // no short-tile path): two 32-row fragments per wave
+      if constexpr (EPI == EPI_QKV) full_tile(I0{}, std::integral_constant<int, 2>{});
     } else if constexpr (HAS_STRIP) {
       if (rows > BM + 32) full_tile(std::integral_constant<int, 2>{}, F4{});
       else if (rows > BM) full_tile(std::integral_constant<int, 1>{}, F4{});
