@@ -301,6 +301,73 @@ rdt_status rdt_model_generate(rdt_model* m, const int32_t* prompt, int32_t B, in
                               size_t kv_bytes, void* workspace, size_t ws_bytes, int32_t* out_ids,
                               void* stream);
 
+/* ------------------------------------------------------------------------
+ * Training of the recurrent stage: its backward pass and the router-bias
+ * balancing step ([ZS §Tokenizer & training script] trains with AdamW in
+ * bf16; [ZS §MoE] notes the selection-only router bias that no step
+ * updates).  Built for bf16 GQA blocks (head_dim 128) on sequences of
+ * T >= 2 tokens without a cache.
+ *
+ * The gradient is that of the stage's output with the discrete decisions
+ * of the forward held fixed (the expert choice of every loop and position,
+ * the halting loop of every position): the derivative of the piece of the
+ * output map the forward took.  The router bias only enters the choice and
+ * gets no gradient.  Matrix products take bf16 operands (activations,
+ * their gradients and the weights) with fp32 accumulation; states, norms,
+ * the residual stream and every reduction stay fp32.
+ * ------------------------------------------------------------------------ */
+#define RDT_MAX_TRAIN_LOOPS 64
+
+/* Bytes of the tape a training forward records (the state after each loop,
+ * fp32 [n_loops][B T][D]) and of the backward workspace for B x T and
+ * n_loops (every loop's saved matrix-product operands, the working buffers
+ * of one loop and transposed copies of the weights). */
+rdt_status rdt_train_tape_bytes(const rdt_block* blk, int32_t B, int32_t T, int32_t n_loops, size_t* bytes);
+rdt_status rdt_train_workspace_bytes(const rdt_block* blk, int32_t B, int32_t T, int32_t n_loops, size_t* bytes);
+
+/* Layout of the gradient buffer (fp32): tensor `id` (RDT_W_*, shapes as in
+ * the weights table) starts at element *offset and holds *numel elements
+ * (0 for tensors the block does not use).  WQ, WK, WV are back to back.
+ * rdt_grad_numel gives the buffer's total element count. */
+rdt_status rdt_grad_layout(const rdt_block* blk, int32_t id, int64_t* offset, int64_t* numel);
+rdt_status rdt_grad_numel(const rdt_block* blk, int64_t* numel);
+
+/* Training forward: rdt_recurrent_forward without a cache (same arguments,
+ * outputs and stop once every position has halted), which also writes the
+ * state after each loop run into `tape` (>= rdt_train_tape_bytes). */
+rdt_status rdt_train_forward(rdt_block* blk, const float* e, const float* h0, int32_t B, int32_t T, int32_t n_loops,
+                             float act_threshold, void* workspace, size_t ws_bytes, float* tape, size_t tape_bytes,
+                             float* h_out, int32_t* halt_counts, void* stream);
+
+/* Backward pass ([ZS §Recurrent Block] forward): given dy = dL/dh_out
+ * (fp32 [B, T, D]) for the output of the rdt_train_forward call that wrote
+ * `tape` and `halt_counts` with the same e, h0, n_loops and act_threshold,
+ * writes the gradient of every trained tensor into `grad` (fp32, layout of
+ * rdt_grad_layout; the router bias's entry is 0), dL/de and dL/dh0 (fp32
+ * [B, T, D]), and expert_load (int32 [n_experts]): the (position, slot)
+ * assignments of each expert summed over the loops run.  Each loop is
+ * recomputed from its recorded input state, in reverse order; weight
+ * gradients are accumulated over all loops' rows at the end.  The handle's
+ * weights (router bias included) must not change between the two calls.
+ * The call synchronises `stream` once (to read the number of loops run).
+ * Errors: INVALID_ARG (nulls, sizes, n_loops > RDT_MAX_TRAIN_LOOPS),
+ * UNSUPPORTED (not bf16 GQA with head_dim 128, T < 2),
+ * WORKSPACE_TOO_SMALL (tape, workspace or gradient buffer). */
+rdt_status rdt_train_backward(rdt_block* blk, const float* e, const float* h0, int32_t B, int32_t T,
+                              int32_t n_loops, float act_threshold, const float* tape, size_t tape_bytes,
+                              const int32_t* halt_counts, const float* dy, float* grad, int64_t grad_numel,
+                              float* de, float* dh0, int32_t* expert_load, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* Router-bias balancing step on the handle's bias (aux-loss-free routing,
+ * the rule [ZS §MoE] finds missing): bias_i += gamma * sign(mean load -
+ * load_i), with load = expert_load of rdt_train_backward (device int32
+ * [n_experts]); an expert at the mean load keeps its bias. */
+rdt_status rdt_router_bias_update(rdt_block* blk, const int32_t* expert_load, float gamma, void* stream);
+/* Copies the handle's router bias (fp32, [n_experts]) to host memory.
+ * Synchronous. */
+rdt_status rdt_get_router_bias(const rdt_block* blk, float* bias_host);
+
 /* Copies A (fp32, [D]) to host memory, for the rho(A) < 1 check of
  * [RC §사용법] (A is diagonal, so rho(A) = max A_i).  Synchronous. */
 rdt_status rdt_get_A(const rdt_block* blk, float* A_host);

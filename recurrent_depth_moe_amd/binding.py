@@ -98,6 +98,15 @@ def lib():
         "rdt_set_timing": ([vp, i32], i32),
         "rdt_set_timing_stages": ([vp, ctypes.c_uint32], i32),
         "rdt_read_timing": ([vp, vp, vp], i32),
+        "rdt_train_tape_bytes": ([vp, i32, i32, i32, ctypes.POINTER(sz)], i32),
+        "rdt_train_workspace_bytes": ([vp, i32, i32, i32, ctypes.POINTER(sz)], i32),
+        "rdt_grad_layout": ([vp, i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)], i32),
+        "rdt_grad_numel": ([vp, ctypes.POINTER(ctypes.c_int64)], i32),
+        "rdt_train_forward": ([vp, vp, vp, i32, i32, i32, f32, vp, sz, vp, sz, vp, vp, vp], i32),
+        "rdt_train_backward": ([vp, vp, vp, i32, i32, i32, f32, vp, sz, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
+                                vp, sz, vp], i32),
+        "rdt_router_bias_update": ([vp, vp, f32, vp], i32),
+        "rdt_get_router_bias": ([vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -260,6 +269,74 @@ class Block:
                                                    float(act_threshold), _ptr(workspace), workspace.numel(),
                                                    _ptr(h_out), _ptr(halt_counts), _stream(stream)))
         return h_out, halt_counts
+
+    # ---- training (rdt_train_forward / rdt_train_backward)
+    def grad_layout(self):
+        """{weight name: (offset, numel)} of the fp32 gradient buffer."""
+        out = {}
+        for i, n in enumerate(WEIGHT_NAMES):
+            off, num = ctypes.c_int64(), ctypes.c_int64()
+            check(lib().rdt_grad_layout(self._h, i, ctypes.byref(off), ctypes.byref(num)))
+            if num.value:
+                out[n] = (off.value, num.value)
+        return out
+
+    def grad_numel(self):
+        n = ctypes.c_int64()
+        check(lib().rdt_grad_numel(self._h, ctypes.byref(n)))
+        return n.value
+
+    def train_tape_bytes(self, B, T, n_loops):
+        n = ctypes.c_size_t()
+        check(lib().rdt_train_tape_bytes(self._h, B, T, n_loops, ctypes.byref(n)))
+        return n.value
+
+    def train_workspace_bytes(self, B, T, n_loops):
+        n = ctypes.c_size_t()
+        check(lib().rdt_train_workspace_bytes(self._h, B, T, n_loops, ctypes.byref(n)))
+        return n.value
+
+    def train_forward(self, e, h0, n_loops, act_threshold, tape, workspace=None, h_out=None, halt_counts=None,
+                      stream=None):
+        B, T, D = e.shape
+        if workspace is None:
+            workspace = self.new_workspace(B, T)
+        if h_out is None:
+            h_out = torch.empty_like(e)
+        if halt_counts is None:
+            halt_counts = torch.empty((B, T), dtype=torch.int32, device=e.device)
+        check(lib().rdt_train_forward(self._h, _ptr(e), _ptr(h0), B, T, n_loops, float(act_threshold),
+                                      _ptr(workspace), workspace.numel(), _ptr(tape),
+                                      tape.numel() * tape.element_size(), _ptr(h_out), _ptr(halt_counts),
+                                      _stream(stream)))
+        return h_out, halt_counts
+
+    def train_backward(self, e, h0, n_loops, act_threshold, tape, halt_counts, dy, workspace, grad=None, de=None,
+                       dh0=None, expert_load=None, stream=None):
+        """Returns (grad, de, dh0, expert_load); grad is the flat fp32
+        buffer of grad_layout()."""
+        B, T, D = e.shape
+        if grad is None:
+            grad = torch.empty(self.grad_numel(), dtype=torch.float32, device=e.device)
+        if de is None:
+            de = torch.empty_like(e)
+        if dh0 is None:
+            dh0 = torch.empty_like(e)
+        if expert_load is None:
+            expert_load = torch.empty(self.cfg["n_experts"], dtype=torch.int32, device=e.device)
+        check(lib().rdt_train_backward(self._h, _ptr(e), _ptr(h0), B, T, n_loops, float(act_threshold), _ptr(tape),
+                                       tape.numel() * tape.element_size(), _ptr(halt_counts), _ptr(dy), _ptr(grad),
+                                       grad.numel(), _ptr(de), _ptr(dh0), _ptr(expert_load), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
+        return grad, de, dh0, expert_load
+
+    def router_bias_update(self, expert_load, gamma, stream=None):
+        check(lib().rdt_router_bias_update(self._h, _ptr(expert_load), float(gamma), _stream(stream)))
+
+    def get_router_bias(self):
+        out = torch.empty(self.cfg["n_experts"], dtype=torch.float32)
+        check(lib().rdt_get_router_bias(self._h, ctypes.c_void_p(out.data_ptr())))
+        return out
 
     def decode_step(self, e_new, h0_new, start_pos, n_loops, act_threshold, kv_cache, kv_capacity,
                     workspace=None, h_out=None, halt_counts=None, stream=None):

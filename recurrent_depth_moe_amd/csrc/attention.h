@@ -19,9 +19,11 @@ void launch_attn_generic(int dtype_bf16, const void* q, const void* k, const voi
                          int G, int Tq, int cap, int dq, int dv, int kbase, float scale, hipStream_t s,
                          const int32_t* live = nullptr);
 // bf16, head width 128, MFMA flash kernel (prefill).  `cap` must be a
-// multiple of 8.
+// multiple of 8.  lse2 (nullable, fp32 [B][H][Tq]) receives each query row's
+// log2 softmax normaliser: p = exp2(score * scale * log2(e) - lse2).
 void launch_attn_flash_bf16(const void* q, const void* k, const void* vt, void* o, int B, int H, int G, int Tq,
-                            int cap, int kbase, float scale, hipStream_t s, const int32_t* live = nullptr);
+                            int cap, int kbase, float scale, hipStream_t s, const int32_t* live = nullptr,
+                            float* lse2 = nullptr);
 // bf16, head width 128, one query per sequence against the cache (decode
 // step), H / G <= 16, cap >= 4.  Keys are split over blocks of 512; `part`
 // is fp32 scratch of attn_decode_part_floats(B, H, nk) floats.

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
                                                                   const bf16_t* __restrict__ vt,
                                                                   bf16_t* __restrict__ o, int H, int G, int Tq,
                                                                   int cap, int kbase, float scale_log2,
-                                                                  const int32_t* live) {
+                                                                  const int32_t* live, float* __restrict__ lse2) {
   RDT_SKIP_IF_ALL_HALTED(live);
   __shared__ uint4 sK[2][FBK * 16];   // [key][16 chunks of 8 d], chunk ^ (key & 15)
   __shared__ uint4 sV[2][FD * 8];     // [d][8 chunks of 8 keys], chunk ^ ((d >> 1) & 7)
@@ -319,6 +319,12 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16_kernel(const bf16_t* _
                           pack_bf16x2(oacc[db][e4 * 4 + 2] * inv, oacc[db][e4 * 4 + 3] * inv)};
         *(uint2*)(orow + db * 32 + 8 * e4 + 4 * half) = ov;
       }
+    // log2 of the row's softmax normaliser in the exp2 domain of the scores
+    // (p = exp2(s * scale_log2 - lse2)), kept for the backward pass
+    if (lse2 != nullptr && half == 0) {
+      const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * scale_log2;
+      lse2[(int64_t)(b * H + h) * Tq + myq] = mc + __log2f(l_run);
+    }
   }
 }
 
@@ -531,11 +537,11 @@ void launch_attn_generic(int dtype_bf16, const void* q, const void* k, const voi
 }
 
 void launch_attn_flash_bf16(const void* q, const void* k, const void* vt, void* o, int B, int H, int G, int Tq,
-                            int cap, int kbase, float scale, hipStream_t s, const int32_t* live) {
+                            int cap, int kbase, float scale, hipStream_t s, const int32_t* live, float* lse2) {
   const dim3 grid((Tq + FBQ - 1) / FBQ * B * H), block(256);
   const float scale_log2 = scale * 1.4426950408889634f;
   attn_flash_bf16_kernel<<<grid, block, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)vt, (bf16_t*)o,
-                                                H, G, Tq, cap, kbase, scale_log2, live);
+                                                H, G, Tq, cap, kbase, scale_log2, live, lse2);
 }
 
 int attn_decode_blocks(int nk) { return (nk + DEC_BLK - 1) / DEC_BLK; }

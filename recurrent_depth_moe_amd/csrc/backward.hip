@@ -1,0 +1,948 @@
+// Backward pass of the recurrent block ([ZS §Recurrent Block] forward,
+// differentiated with the expert choices and halting loops held fixed).
+//
+// Pages: [ZS] "OpenMythos 분석: …의 계산 모델링" (zero.shotlearni.ng).
+//
+// MFMA v_mfma_f32_32x32x16_bf16 layout used throughout: with operands
+// (a, b), lane l supplies a row A[l % 32][8 (l / 32) .. +7] and a column
+// B[8 (l / 32) .. +7][l % 32]; the result lane l holds column l % 32 of rows
+// 8 (r / 4) + 4 (l / 32) + r % 4, r = 0 .. 15.  Any permutation of the 16
+// contraction slots works as long as both operands use it: the products
+// that contract over queries or keys use the order in which a lane already
+// holds its scores (slot 8 h + x <-> index 8 (x / 4) + 4 h + x % 4).
+#include "backward.h"
+
+#include <algorithm>
+
+namespace {
+
+__device__ __forceinline__ floatx16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const floatx16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t bf_elem(const uint4& v, int j) {
+  const uint32_t d = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+  return (j & 1) ? (d >> 16) : (d & 0xffffu);
+}
+
+// 8 bf16 from p, the first `nvalid` of them (the rest zero)
+__device__ __forceinline__ uint4 load8(const bf16_t* p, int nvalid) {
+  if (nvalid >= 8) return *(const uint4*)p;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < nvalid; ++i) w[i >> 1] |= (uint32_t)p[i] << (16 * (i & 1));
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ bf16x8_t as_frag(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// eight fp32 scores -> one bf16 fragment
+__device__ __forceinline__ bf16x8_t pack8(const float* p) {
+  const uint4 v = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                   pack_bf16x2(p[6], p[7])};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ void st4(float* p, float4 v) { *(float4*)p = v; }
+__device__ __forceinline__ float4 ldbf4(const bf16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                __uint_as_float(u.y & 0xffff0000u)};
+}
+__device__ __forceinline__ void stbf4(bf16_t* p, float4 v) {
+  *(uint2*)p = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+}
+__device__ __forceinline__ float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+__device__ __forceinline__ float4 fma4(float s, float4 a, float4 b) {
+  return float4{fmaf(s, a.x, b.x), fmaf(s, a.y, b.y), fmaf(s, a.z, b.z), fmaf(s, a.w, b.w)};
+}
+__device__ __forceinline__ float4 add4(float4 a, float4 b) { return float4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w}; }
+__device__ __forceinline__ float4 mul4(float4 a, float4 b) { return float4{a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w}; }
+__device__ __forceinline__ float4 scl4(float s, float4 a) { return float4{s * a.x, s * a.y, s * a.z, s * a.w}; }
+
+// ------------------------------------------------------------ transpose
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ in, int64_t isb1,
+                                                             int64_t isb2, int nb2, int64_t ldi,
+                                                             bf16_t* __restrict__ out, int64_t osb, int64_t ldo,
+                                                             int R, int Rp, int C, int Cv) {
+  __shared__ bf16_t tile[64][66];
+  const int bi = blockIdx.z, b1 = bi / nb2, b2 = bi - b1 * nb2;
+  const bf16_t* src = in + b1 * isb1 + b2 * isb2;
+  bf16_t* dst = out + bi * osb;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < Cv && c < C) ? src[(int64_t)r * ldi + c] : (bf16_t)0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < Rp) dst[(int64_t)c * ldo + r] = tile[tx][i];
+  }
+}
+
+// ------------------------------------------------------------ weight gradients
+// 128 x 128 output tile per block (four waves of 64 x 64), 64 stacked rows
+// per step.  Each thread loads 4 rows x 8 columns of both operands, turns
+// them into 8 columns x 4 rows in registers and writes them to LDS as
+// [column][row] (rows contiguous), so the MFMA fragments (8 consecutive
+// rows of one column) are single 16-byte LDS reads.  The next step's global
+// loads are in flight while the current step computes.
+constexpr int WG_LD = 72;   // 64 rows + 8 pad (bf16) per LDS column
+
+__device__ __forceinline__ void wg_store_t(bf16_t* s, const uint4* v, int rg, int cc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint2 u = {bf_elem(v[0], j) | (bf_elem(v[1], j) << 16), bf_elem(v[2], j) | (bf_elem(v[3], j) << 16)};
+    *(uint2*)&s[(8 * cc + j) * WG_LD + 4 * rg] = u;
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[128 * WG_LD];
+  __shared__ __attribute__((aligned(16))) bf16_t sX[128 * WG_LD];
+  const int tilesN = (a.Nc + 127) / 128;
+  const int tn = blockIdx.x % tilesN, tk = blockIdx.x / tilesN;
+  const int g = blockIdx.y, z = blockIdx.z;
+  const int n0 = tn * 128, k0 = tk * 128;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
+  const int wn = w >> 1, wk = w & 1;
+  const int rg = tid & 15, cc = tid >> 4;
+  const int na = a.Nc - (n0 + 8 * cc), nx = a.Kc - (k0 + 8 * cc);
+  const bf16_t* Ab = (const bf16_t*)a.A + n0 + 8 * cc;
+  const bf16_t* Xb = (const bf16_t*)a.X + k0 + 8 * cc;
+  floatx16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int t_lo = (int)((int64_t)z * a.n_loops / a.splits), t_hi = (int)((int64_t)(z + 1) * a.n_loops / a.splits);
+  // chunk iterator over (loop, 64-row step) of this group
+  int t = t_lo - 1;
+  int64_t m0 = 0, r1 = 0;
+  auto advance = [&]() -> bool {
+    m0 += 64;
+    while (m0 >= r1) {
+      if (++t >= t_hi) return false;
+      const int64_t base = (int64_t)t * a.loop_rows;
+      if (a.off) {
+        const int32_t* o = a.off + (int64_t)t * (a.G + 1) + g;
+        m0 = base + o[0];
+        r1 = base + o[1];
+      } else {
+        m0 = base;
+        r1 = base + a.rows;
+      }
+    }
+    return true;
+  };
+  uint4 va[4], vx[4];
+  auto load = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + 4 * rg + i;
+      const bool ok = m < r1;
+      const int64_t xm = ok ? (a.xrow ? (int64_t)a.xrow[m] : m) : 0;
+      va[i] = load8(Ab + (ok ? m : 0) * a.lda, ok ? na : 0);
+      vx[i] = load8(Xb + xm * a.ldx, ok ? nx : 0);
+    }
+  };
+  m0 = -64;
+  bool more = advance();
+  if (more) load();
+  while (more) {
+    __syncthreads();
+    wg_store_t(sA, va, rg, cc);
+    wg_store_t(sX, vx, rg, cc);
+    __syncthreads();
+    more = advance();
+    if (more) load();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t af[2], xf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *(const bf16x8_t*)&sA[(wn * 64 + i * 32 + (lane & 31)) * WG_LD + 16 * ks + 8 * half];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        xf[j] = *(const bf16x8_t*)&sX[(wk * 64 + j * 32 + (lane & 31)) * WG_LD + 16 * ks + 8 * half];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], xf[j], acc[i][j]);
+    }
+  }
+  float* Cb = a.C + (int64_t)g * a.c_gstride + (int64_t)z * a.c_split_stride;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int k = k0 + wk * 64 + j * 32 + (lane & 31);
+      if (k >= a.Kc) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = n0 + wn * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (n < a.Nc) {
+          float* p = Cb + (int64_t)n * a.ldc + k;
+          *p = a.accumulate ? *p + acc[i][j][r] : acc[i][j][r];
+        }
+      }
+    }
+}
+
+// dWr[e][c]: one block per (expert, 256 columns), loops and rows in order
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dz, const bf16_t* __restrict__ f,
+                                                           const int32_t* __restrict__ gidx,
+                                                           const int32_t* __restrict__ off, int n_loops, int NK,
+                                                           int E, int D, float* __restrict__ dWr) {
+  const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= D) return;
+  float acc = 0.f;
+  for (int t = 0; t < n_loops; ++t) {
+    const int32_t* o = off + (int64_t)t * (E + 1);
+    for (int m = o[e]; m < o[e + 1]; ++m) {
+      const int64_t row = (int64_t)t * NK + m;
+      acc = fmaf(dz[row], bf2f(f[(int64_t)gidx[row] * D + c]), acc);
+    }
+  }
+  dWr[(int64_t)e * D + c] = acc;
+}
+
+// ------------------------------------------------------------ attention backward
+constexpr int AQ = 64;      // queries per tile (dK / dV kernel), keys per tile (dQ kernel)
+constexpr int LQ = 136;     // row stride of [row][128 d] LDS tiles (bf16)
+constexpr int LT = 72;      // row stride of [d][64] transposed LDS tiles (bf16)
+
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const bf16_t* __restrict__ o,
+                                                            const bf16_t* __restrict__ dO, int N, int H, int T,
+                                                            float* __restrict__ Dq) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= N * H) return;
+  const int n = idx / H, h = idx - n * H;
+  const bf16_t* po = o + (int64_t)n * H * 128 + h * 128;
+  const bf16_t* pd = dO + (int64_t)n * H * 128 + h * 128;
+  float s = 0.f;
+  for (int d = 0; d < 128; d += 4) s += dot4(ldbf4(po + d), ldbf4(pd + d));
+  const int b = n / T, i = n - b * T;
+  Dq[((int64_t)b * H + h) * T + i] = s;
+}
+
+// one block per (key tile of 128 keys, b, kv head g); wave w owns keys
+// 32 w .. 32 w + 31 of the tile with dK and dV for all 128 d in registers,
+// and walks the query tiles at and after its keys for every query head of
+// the group.
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dO, const bf16_t* __restrict__ qt, const bf16_t* __restrict__ dOt,
+    const float* __restrict__ lse2, const float* __restrict__ Dq, float* __restrict__ dK, float* __restrict__ dV,
+    int B, int H, int G, int T, int Tp, int cap, float scale_log2, float scale) {
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[AQ * LQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sdO[AQ * LQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sQt[128 * LT];
+  __shared__ __attribute__((aligned(16))) bf16_t sdOt[128 * LT];
+  __shared__ float sL[AQ], sD[AQ];
+  const int BG = B * G, kt = blockIdx.x / BG, bg = blockIdx.x - kt * BG;
+  const int b = bg / G, g = bg - b * G, rep = H / G;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
+  const int kw0 = kt * 128 + w * 32, kl = kw0 + (lane & 31);
+  bf16x8_t kf[8], vf[8];
+  {
+    const bf16_t* kr = k + ((int64_t)bg * cap + kl) * 128;
+    const bf16_t* vr = v + ((int64_t)bg * cap + kl) * 128;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      uint4 a = uint4{0u, 0u, 0u, 0u}, c = a;
+      if (kl < T) {
+        a = *(const uint4*)(kr + 16 * ds + 8 * half);
+        c = *(const uint4*)(vr + 16 * ds + 8 * half);
+      }
+      kf[ds] = as_frag(a);
+      vf[ds] = as_frag(c);
+    }
+  }
+  floatx16_t accK[4], accV[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) accK[i][e] = accV[i][e] = 0.f;
+  const int nqt = (T + AQ - 1) / AQ;
+  for (int hr = 0; hr < rep; ++hr) {
+    const int h = g * rep + hr;
+    const bf16_t* qh = q + (int64_t)(b * H + h) * T * 128;
+    const bf16_t* qth = qt + (int64_t)(b * H + h) * 128 * Tp;
+    const bf16_t* dOth = dOt + (int64_t)(b * H + h) * 128 * Tp;
+    const float* Lh = lse2 + (int64_t)(b * H + h) * T;
+    const float* Dh = Dq + (int64_t)(b * H + h) * T;
+    for (int qti = (kt * 128) / AQ; qti < nqt; ++qti) {
+      const int q0 = qti * AQ;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + 256 * j;
+        const int row = idx >> 4, ch = idx & 15, qq = q0 + row;
+        uint4 a = uint4{0u, 0u, 0u, 0u}, c = a;
+        if (qq < T) {
+          a = *(const uint4*)(qh + (int64_t)qq * 128 + ch * 8);
+          c = *(const uint4*)(dO + ((int64_t)(b * T + qq) * H + h) * 128 + ch * 8);
+        }
+        *(uint4*)&sQ[row * LQ + ch * 8] = a;
+        *(uint4*)&sdO[row * LQ + ch * 8] = c;
+        const int d = idx >> 3, c8 = idx & 7;
+        *(uint4*)&sQt[d * LT + c8 * 8] = *(const uint4*)(qth + (int64_t)d * Tp + q0 + c8 * 8);
+        *(uint4*)&sdOt[d * LT + c8 * 8] = *(const uint4*)(dOth + (int64_t)d * Tp + q0 + c8 * 8);
+      }
+      if (tid < AQ) {
+        const int qq = q0 + tid;
+        sL[tid] = qq < T ? Lh[qq] : 0.f;
+        sD[tid] = qq < T ? Dh[qq] : 0.f;
+      }
+      __syncthreads();
+      if (kw0 > q0 + AQ - 1) continue;   // every query of the tile precedes this wave's keys
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        floatx16_t S, dP;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
+        const int qrow = qb * 32 + (lane & 31);
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds) {
+          const bf16x8_t qa = *(const bf16x8_t*)&sQ[qrow * LQ + 16 * ds + 8 * half];
+          const bf16x8_t da = *(const bf16x8_t*)&sdO[qrow * LQ + 16 * ds + 8 * half];
+          S = mfma32(qa, kf[ds], S);
+          dP = mfma32(da, vf[ds], dP);
+        }
+        float p[16], dsv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = qb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int qq = q0 + ql;
+          const bool ok = qq < T && kl <= qq && kl < T;
+          const float pr = ok ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - sL[ql]) : 0.f;
+          p[r] = pr;
+          dsv[r] = pr * (dP[r] - sD[ql]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8_t pa = pack8(p + 8 * ks), sa = pack8(dsv + 8 * ks);
+          const int qo = qb * 32 + 16 * ks + 4 * half;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int d = db * 32 + (lane & 31);
+            const uint2 o0 = *(const uint2*)&sdOt[d * LT + qo], o1 = *(const uint2*)&sdOt[d * LT + qo + 8];
+            const uint2 t0 = *(const uint2*)&sQt[d * LT + qo], t1 = *(const uint2*)&sQt[d * LT + qo + 8];
+            accV[db] = mfma32(pa, as_frag(uint4{o0.x, o0.y, o1.x, o1.y}), accV[db]);
+            accK[db] = mfma32(sa, as_frag(uint4{t0.x, t0.y, t1.x, t1.y}), accK[db]);
+          }
+        }
+      }
+    }
+  }
+  float* dKb = dK + (int64_t)bg * T * 128;
+  float* dVb = dV + (int64_t)bg * T * 128;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (key < T) {
+        const int64_t i = (int64_t)key * 128 + db * 32 + (lane & 31);
+        dKb[i] = accK[db][r] * scale;
+        dVb[i] = accV[db][r];
+      }
+    }
+}
+
+// one block per (query tile of 128, b, head h); wave w owns queries
+// 32 w .. 32 w + 31 and walks the key tiles up to its diagonal
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dO, const bf16_t* __restrict__ kt, const float* __restrict__ lse2,
+    const float* __restrict__ Dq, float* __restrict__ dQ, int B, int H, int G, int T, int cap, float scale_log2,
+    float scale) {
+  __shared__ __attribute__((aligned(16))) bf16_t sK[AQ * LQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[AQ * LQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sKt[128 * LT];
+  const int BH = B * H, nqt = (T + 127) / 128;
+  const int qti = nqt - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+  const int b = bh / H, h = bh - b * H, g = h / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
+  const int qw0 = qti * 128 + w * 32, ql = qw0 + (lane & 31);
+  bf16x8_t qf[8], df[8];
+  {
+    const bf16_t* qr = q + ((int64_t)bh * T + ql) * 128;
+    const bf16_t* dr = dO + ((int64_t)(b * T + ql) * H + h) * 128;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      uint4 a = uint4{0u, 0u, 0u, 0u}, c = a;
+      if (ql < T) {
+        a = *(const uint4*)(qr + 16 * ds + 8 * half);
+        c = *(const uint4*)(dr + 16 * ds + 8 * half);
+      }
+      qf[ds] = as_frag(a);
+      df[ds] = as_frag(c);
+    }
+  }
+  const float Lq = ql < T ? lse2[(int64_t)bh * T + ql] : 0.f;
+  const float Dqq = ql < T ? Dq[(int64_t)bh * T + ql] : 0.f;
+  floatx16_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  const int bg = b * G + g;
+  const bf16_t* kb = k + (int64_t)bg * cap * 128;
+  const bf16_t* vb = v + (int64_t)bg * cap * 128;
+  const bf16_t* ktb = kt + (int64_t)bg * 128 * cap;
+  const int kend = min(T, qti * 128 + 128);
+  const int nkt = (kend + AQ - 1) / AQ;
+  for (int kti = 0; kti < nkt; ++kti) {
+    const int k0 = kti * AQ;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + 256 * j;
+      const int row = idx >> 4, ch = idx & 15, kk = k0 + row;
+      uint4 a = uint4{0u, 0u, 0u, 0u}, c = a;
+      if (kk < T) {
+        a = *(const uint4*)(kb + (int64_t)kk * 128 + ch * 8);
+        c = *(const uint4*)(vb + (int64_t)kk * 128 + ch * 8);
+      }
+      *(uint4*)&sK[row * LQ + ch * 8] = a;
+      *(uint4*)&sV[row * LQ + ch * 8] = c;
+      const int d = idx >> 3, c8 = idx & 7;
+      *(uint4*)&sKt[d * LT + c8 * 8] = *(const uint4*)(ktb + (int64_t)d * cap + k0 + c8 * 8);
+    }
+    __syncthreads();
+    if (k0 > qw0 + 31) continue;   // every key of the tile follows this wave's queries
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      floatx16_t S, dP;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
+      const int krow = kb2 * 32 + (lane & 31);
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds) {
+        const bf16x8_t ka = *(const bf16x8_t*)&sK[krow * LQ + 16 * ds + 8 * half];
+        const bf16x8_t va = *(const bf16x8_t*)&sV[krow * LQ + 16 * ds + 8 * half];
+        S = mfma32(ka, qf[ds], S);
+        dP = mfma32(va, df[ds], dP);
+      }
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb2 * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool ok = ql < T && key <= ql;
+        const float pr = ok ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - Lq) : 0.f;
+        dsv[r] = pr * (dP[r] - Dqq);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t sa = pack8(dsv + 8 * ks);
+        const int ko = kb2 * 32 + 16 * ks + 4 * half;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = db * 32 + (lane & 31);
+          const uint2 t0 = *(const uint2*)&sKt[d * LT + ko], t1 = *(const uint2*)&sKt[d * LT + ko + 8];
+          acc[db] = mfma32(sa, as_frag(uint4{t0.x, t0.y, t1.x, t1.y}), acc[db]);
+        }
+      }
+    }
+  }
+  float* dQb = dQ + (int64_t)bh * T * 128;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = qw0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (qq < T) dQb[(int64_t)qq * 128 + db * 32 + (lane & 31)] = acc[db][r] * scale;
+    }
+}
+
+// dqkv row n = b T + i: [dq heads | dk heads | dv heads], RoPE taken back
+// on the q and k parts (pairs rotated by minus the angle)
+__global__ __launch_bounds__(256) void qkv_bwd_kernel(const float* __restrict__ dQ, const float* __restrict__ dK,
+                                                      const float* __restrict__ dV, const float* __restrict__ rcos,
+                                                      const float* __restrict__ rsin, int B, int T, int H, int G,
+                                                      bf16_t* __restrict__ dqkv) {
+  const int W = (H + 2 * G) * 128, pairs = W / 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)B * T * pairs) return;
+  const int n = (int)(idx / pairs), col = 2 * (int)(idx - (int64_t)n * pairs);
+  const int b = n / T, i = n - b * T;
+  const int hd = col >> 7, d = col & 127;
+  float x0, x1;
+  bool rot = true;
+  if (hd < H) {
+    const float* p = dQ + (((int64_t)b * H + hd) * T + i) * 128 + d;
+    x0 = p[0];
+    x1 = p[1];
+  } else if (hd < H + G) {
+    const float* p = dK + (((int64_t)b * G + (hd - H)) * T + i) * 128 + d;
+    x0 = p[0];
+    x1 = p[1];
+  } else {
+    const float* p = dV + (((int64_t)b * G + (hd - H - G)) * T + i) * 128 + d;
+    x0 = p[0];
+    x1 = p[1];
+    rot = false;
+  }
+  if (rot) {
+    const float c = rcos[(int64_t)i * 64 + (d >> 1)], s = rsin[(int64_t)i * 64 + (d >> 1)];
+    const float y0 = x0 * c + x1 * s, y1 = x1 * c - x0 * s;
+    x0 = y0;
+    x1 = y1;
+  }
+  *(uint32_t*)(dqkv + (int64_t)n * W + col) = pack_bf16x2(x0, x1);
+}
+
+// ------------------------------------------------------------ SwiGLU
+__global__ __launch_bounds__(256) void swiglu_fwd_kernel(const bf16_t* __restrict__ gu, int M, int F,
+                                                         bf16_t* __restrict__ act) {
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (idx >= (int64_t)M * F) return;
+  const int64_t m = idx / F;
+  const int f = (int)(idx - m * F);
+  const float4 G = ldbf4(gu + m * 2 * F + f), U = ldbf4(gu + m * 2 * F + F + f);
+  stbf4(act + m * F + f, float4{silu_f(G.x) * U.x, silu_f(G.y) * U.y, silu_f(G.z) * U.z, silu_f(G.w) * U.w});
+}
+
+__device__ __forceinline__ void swiglu_grad(float g, float u, float da, float& dg, float& du) {
+  const float sg = 1.0f / (1.0f + __expf(-g));
+  du = da * g * sg;
+  dg = da * u * sg * (1.0f + g * (1.0f - sg));
+}
+
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16_t* __restrict__ gu, const float* __restrict__ dact,
+                                                         int M, int F, bf16_t* __restrict__ dgu) {
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (idx >= (int64_t)M * F) return;
+  const int64_t m = idx / F;
+  const int f = (int)(idx - m * F);
+  const float4 G = ldbf4(gu + m * 2 * F + f), U = ldbf4(gu + m * 2 * F + F + f), dA = ld4(dact + m * F + f);
+  float4 dG, dU;
+  swiglu_grad(G.x, U.x, dA.x, dG.x, dU.x);
+  swiglu_grad(G.y, U.y, dA.y, dG.y, dU.y);
+  swiglu_grad(G.z, U.z, dA.z, dG.z, dU.z);
+  swiglu_grad(G.w, U.w, dA.w, dG.w, dU.w);
+  stbf4(dgu + m * 2 * F + f, dG);
+  stbf4(dgu + m * 2 * F + F + f, dU);
+}
+
+// ------------------------------------------------------------ row-wise passes
+// One wave per row (rows n = wave, wave + RDT_BWD_WAVES, ...); lane l owns
+// the float4 columns 4 l + 256 j.
+
+#define ROW_LOOP_BEGIN                                                  \
+  const int lane = threadIdx.x & 63;                                   \
+  const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);                  \
+  for (int n = wg; n < N; n += RDT_BWD_WAVES) {
+#define ROW_LOOP_END }
+
+__global__ __launch_bounds__(256) void act_prep_kernel(const float* __restrict__ states, const float* __restrict__ dy,
+                                                       const float* __restrict__ hw, const float* __restrict__ hb,
+                                                       const int32_t* __restrict__ hc, int L, int N, int D,
+                                                       float* __restrict__ w_act, float* __restrict__ z_act,
+                                                       float* __restrict__ part_hw, float* __restrict__ part_hb) {
+  ROW_LOOP_BEGIN
+  // lane t keeps p_t and G_t = <dy, h_{t+1}>
+  float my_p = 0.f, my_G = 0.f;
+  const float* dyr = dy + (int64_t)n * D;
+  for (int t = 0; t < L; ++t) {
+    const float* sr = states + ((int64_t)t * N + n) * D;
+    float zp = 0.f, gp = 0.f;
+    for (int c = 4 * lane; c < D; c += 256) {
+      const float4 x = ld4(sr + c);
+      zp += dot4(x, ld4(hw + c));
+      gp += dot4(x, ld4(dyr + c));
+    }
+    zp = wave_sum(zp);
+    gp = wave_sum(gp);
+    if (lane == t) {
+      my_p = 1.0f / (1.0f + expf(-(zp + hb[0])));
+      my_G = gp;
+    }
+  }
+  const int th = hc[n] - 1;   // halting loop
+  float cum_th = 0.f, G_th = 0.f;
+  for (int t = 0; t < L; ++t) {
+    const float pt = __shfl(my_p, t, 64), Gt = __shfl(my_G, t, 64);
+    if (t < th) cum_th += pt;
+    if (t == th) G_th = Gt;
+  }
+  const float rem = 1.0f - cum_th;
+  if (lane < L) {
+    const int t = lane;
+    float wv = 0.f, zv = 0.f;
+    if (t < th) {
+      wv = my_p;
+      const float dp = my_G - (rem > 0.f ? G_th : 0.f);
+      zv = dp * my_p * (1.0f - my_p);
+    } else if (t == th) {
+      wv = rem > 0.f ? rem : 0.f;
+    }
+    w_act[(int64_t)t * N + n] = wv;
+    z_act[(int64_t)t * N + n] = zv;
+  }
+  // d halt_w += sum_t z_t h_{t+1}; d halt_b += sum_t z_t
+  float zsum = 0.f;
+  float* ph = part_hw + (int64_t)wg * D;
+  for (int t = 0; t < L && t < th; ++t) {
+    const float zt = __shfl(my_p, t, 64) * (1.0f - __shfl(my_p, t, 64)) *
+                     (__shfl(my_G, t, 64) - (rem > 0.f ? G_th : 0.f));
+    zsum += zt;
+    const float* sr = states + ((int64_t)t * N + n) * D;
+    for (int c = 4 * lane; c < D; c += 256) st4(ph + c, fma4(zt, ld4(sr + c), ld4(ph + c)));
+  }
+  if (lane == 0) part_hb[wg] += zsum;
+  ROW_LOOP_END
+}
+
+__global__ __launch_bounds__(256) void tail_bwd_kernel(TailBwdArgs a) {
+  const int N = a.N, D = a.D, k = a.k, r = a.r;
+  ROW_LOOP_BEGIN
+  const int64_t ro = (int64_t)n * D;
+  const float wa = a.w_act ? a.w_act[n] : 0.f, za = a.z_act ? a.z_act[n] : 0.f;
+  const bf16_t* yb = (const bf16_t*)a.y;
+  const bf16_t* ysb = (const bf16_t*)a.ys;
+  const bf16_t* Ld = (const bf16_t*)a.lora_down;
+  const bf16_t* LB = (const bf16_t*)a.lora_B;
+  int rows_j[8];
+  float gates[8];
+  for (int j = 0; j < k; ++j) {
+    rows_j[j] = a.inv[(int64_t)n * k + j];
+    gates[j] = a.gate[(int64_t)n * k + j];
+  }
+  auto g_full = [&](int c) {
+    float4 gf = ld4(a.g + ro + c);
+    if (a.w_act) gf = fma4(wa, ld4(a.dy + ro + c), gf);
+    if (a.z_act) gf = fma4(za, ld4(a.halt_w + c), gf);
+    return gf;
+  };
+  auto tau_at = [&](int c) {
+    float4 tv = ld4(a.x1 + ro + c);
+    for (int j = 0; j < k; ++j) tv = fma4(gates[j], ldbf4(yb + (int64_t)rows_j[j] * D + c), tv);
+    for (int s2 = 0; s2 < a.S; ++s2) tv = add4(tv, ldbf4(ysb + ((int64_t)s2 * N + n) * D + c));
+    return tv;
+  };
+  // pass 1: v = tau Ld^T and dw = g_full LB^T (r values each)
+  float vv[RDT_LORA_LD], dw[RDT_LORA_LD];
+  for (int i = 0; i < r; ++i) vv[i] = dw[i] = 0.f;
+  for (int c = 4 * lane; c < D; c += 256) {
+    const float4 tv = tau_at(c), gf = g_full(c);
+    for (int i = 0; i < r; ++i) {
+      vv[i] += dot4(tv, ldbf4(Ld + (int64_t)i * D + c));
+      dw[i] += dot4(gf, ldbf4(LB + (int64_t)i * D + c));
+    }
+  }
+  float dv[RDT_LORA_LD];
+  float* ps = a.part_s + (int64_t)wg * RDT_LORA_LD;
+  for (int i = 0; i < r; ++i) {
+    vv[i] = wave_sum(vv[i]);
+    dw[i] = wave_sum(dw[i]);
+    dv[i] = dw[i] * a.scale_row[i];
+    if (lane == 0) {
+      ps[i] += dw[i] * vv[i];
+      ((bf16_t*)a.sv_wl)[(int64_t)n * RDT_LORA_LD + i] = f2bf(vv[i] * a.scale_row[i]);
+      ((bf16_t*)a.sv_dv)[(int64_t)n * RDT_LORA_LD + i] = f2bf(dv[i]);
+    }
+  }
+  // pass 2: dtau = g_full + dv Ld; outputs
+  float dg[8];
+  for (int j = 0; j < k; ++j) dg[j] = 0.f;
+  for (int c = 4 * lane; c < D; c += 256) {
+    const float4 gf = g_full(c), tv = tau_at(c);
+    float4 dt = gf;
+    for (int i = 0; i < r; ++i) dt = fma4(dv[i], ldbf4(Ld + (int64_t)i * D + c), dt);
+    for (int j = 0; j < k; ++j) {
+      const float4 yv = ldbf4(yb + (int64_t)rows_j[j] * D + c);
+      dg[j] += dot4(dt, yv);
+      stbf4((bf16_t*)a.dY + (int64_t)rows_j[j] * D + c, scl4(gates[j], dt));
+    }
+    st4(a.dtau + ro + c, dt);
+    stbf4((bf16_t*)a.dtau_bf + ro + c, dt);
+    stbf4((bf16_t*)a.sv_g + ro + c, gf);
+    stbf4((bf16_t*)a.sv_tau + ro + c, tv);
+    const float4 Av = ld4(a.A + c), Bv = ld4(a.Bv + c), hp = ld4(a.h_prev + ro + c), ev = ld4(a.e + ro + c);
+    st4(a.de + ro + c, fma4(1.f, mul4(Bv, gf), ld4(a.de + ro + c)));
+    float* pA = a.part_A + (int64_t)wg * D + c;
+    float* pB = a.part_B + (int64_t)wg * D + c;
+    st4(pA, add4(ld4(pA), mul4(gf, hp)));
+    st4(pB, add4(ld4(pB), mul4(gf, ev)));
+    st4(a.g_next + ro + c, mul4(Av, gf));
+  }
+  // router: the gates are the softmax of the chosen logits, so
+  // d z_j = gate_j (dgate_j - sum_i gate_i dgate_i) and 0 elsewhere
+  float gd = 0.f;
+  for (int j = 0; j < k; ++j) {
+    dg[j] = wave_sum(dg[j]);
+    gd += gates[j] * dg[j];
+  }
+  if (lane == 0)
+    for (int j = 0; j < k; ++j) {
+      const float dz = gates[j] * (dg[j] - gd);
+      a.dz[(int64_t)n * k + j] = dz;
+      a.dz_perm[rows_j[j]] = dz;
+    }
+  ROW_LOOP_END
+}
+
+__global__ __launch_bounds__(256) void ffn_norm_bwd_kernel(int N, int D, int k, float eps, const float* __restrict__ df,
+                                                           const float* __restrict__ dfp,
+                                                           const int32_t* __restrict__ inv,
+                                                           const int32_t* __restrict__ sel,
+                                                           const float* __restrict__ dz, const bf16_t* __restrict__ Wr,
+                                                           const float* __restrict__ x1,
+                                                           const float* __restrict__ gf, float* __restrict__ dx1,
+                                                           bf16_t* __restrict__ dx1_bf, float* __restrict__ part_g) {
+  ROW_LOOP_BEGIN
+  const int64_t ro = (int64_t)n * D;
+  int rj[8], sj[8];
+  float zj[8];
+  for (int j = 0; j < k; ++j) {
+    rj[j] = inv[(int64_t)n * k + j];
+    sj[j] = sel[(int64_t)n * k + j];
+    zj[j] = dz[(int64_t)n * k + j];
+  }
+  auto dft_at = [&](int c) {
+    float4 v = df ? ld4(df + ro + c) : float4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      v = add4(v, ld4(dfp + (int64_t)rj[j] * D + c));
+      v = fma4(zj[j], ldbf4(Wr + (int64_t)sj[j] * D + c), v);
+    }
+    return v;
+  };
+  float ss = 0.f, dd = 0.f;
+  for (int c = 4 * lane; c < D; c += 256) {
+    const float4 x = ld4(x1 + ro + c);
+    ss += dot4(x, x);
+    dd += dot4(mul4(dft_at(c), ld4(gf + c)), x);
+  }
+  ss = wave_sum(ss);
+  dd = wave_sum(dd);
+  const float rstd = rsqrtf(ss / D + eps), m = dd * rstd * rstd / D;
+  float* pg = part_g + (int64_t)wg * D;
+  for (int c = 4 * lane; c < D; c += 256) {
+    const float4 x = ld4(x1 + ro + c), dft = dft_at(c), g4 = ld4(gf + c);
+    const float4 xh = scl4(rstd, x);
+    const float4 dx = scl4(rstd, float4{dft.x * g4.x - x.x * m, dft.y * g4.y - x.y * m, dft.z * g4.z - x.z * m,
+                                        dft.w * g4.w - x.w * m});
+    const float4 o = add4(ld4(dx1 + ro + c), dx);
+    st4(dx1 + ro + c, o);
+    stbf4(dx1_bf + ro + c, o);
+    st4(pg + c, add4(ld4(pg + c), mul4(dft, xh)));
+  }
+  ROW_LOOP_END
+}
+
+__global__ __launch_bounds__(256) void head_bwd_kernel(int N, int D, float eps, const float* __restrict__ dx1,
+                                                       const float* __restrict__ da, const float* __restrict__ c_,
+                                                       const float* __restrict__ ga, const float* __restrict__ gr,
+                                                       const float* __restrict__ hp, const float* __restrict__ e,
+                                                       const float* __restrict__ emb, int loop_dim,
+                                                       float* __restrict__ gcarry, float* __restrict__ de,
+                                                       float* __restrict__ part_ga, float* __restrict__ part_gr) {
+  ROW_LOOP_BEGIN
+  const int64_t ro = (int64_t)n * D;
+  auto r_at = [&](int c) {
+    float4 v = add4(ld4(hp + ro + c), ld4(e + ro + c));
+    if (c < loop_dim) v = add4(v, ld4(emb + c));
+    return v;
+  };
+  float sc = 0.f, sac = 0.f, sr = 0.f;
+  for (int c = 4 * lane; c < D; c += 256) {
+    const float4 cv = ld4(c_ + ro + c), rv = r_at(c);
+    sc += dot4(cv, cv);
+    sac += dot4(mul4(ld4(da + ro + c), ld4(ga + c)), cv);
+    sr += dot4(rv, rv);
+  }
+  sc = wave_sum(sc);
+  sac = wave_sum(sac);
+  sr = wave_sum(sr);
+  const float rc = rsqrtf(sc / D + eps), mc = sac * rc * rc / D;
+  const float rr = rsqrtf(sr / D + eps);
+  auto dc_at = [&](int c) {
+    const float4 cv = ld4(c_ + ro + c), dav = mul4(ld4(da + ro + c), ld4(ga + c));
+    const float4 t = float4{dav.x - cv.x * mc, dav.y - cv.y * mc, dav.z - cv.z * mc, dav.w - cv.w * mc};
+    return fma4(rc, t, ld4(dx1 + ro + c));
+  };
+  float scr = 0.f;
+  for (int c = 4 * lane; c < D; c += 256) scr += dot4(mul4(dc_at(c), ld4(gr + c)), r_at(c));
+  scr = wave_sum(scr);
+  const float mr = scr * rr * rr / D;
+  float* pa = part_ga + (int64_t)wg * D;
+  float* pr = part_gr + (int64_t)wg * D;
+  for (int c = 4 * lane; c < D; c += 256) {
+    const float4 dc = dc_at(c), rv = r_at(c), g4 = ld4(gr + c);
+    const float4 t = float4{dc.x * g4.x - rv.x * mr, dc.y * g4.y - rv.y * mr, dc.z * g4.z - rv.z * mr,
+                            dc.w * g4.w - rv.w * mr};
+    const float4 dr = scl4(rr, t);
+    st4(gcarry + ro + c, add4(ld4(gcarry + ro + c), dr));
+    st4(de + ro + c, add4(ld4(de + ro + c), dr));
+    st4(pa + c, add4(ld4(pa + c), mul4(ld4(da + ro + c), scl4(rc, ld4(c_ + ro + c)))));
+    st4(pr + c, add4(ld4(pr + c), mul4(dc, scl4(rr, rv))));
+  }
+  ROW_LOOP_END
+}
+
+__global__ __launch_bounds__(256) void loop_index_kernel(const int32_t* __restrict__ perm,
+                                                         const int32_t* __restrict__ off, int t, int NK, int N, int E,
+                                                         int32_t* __restrict__ gidx, int32_t* __restrict__ load) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < NK) gidx[(int64_t)t * NK + i] = t * N + perm[i];
+  if (blockIdx.x == 0 && threadIdx.x < E) load[threadIdx.x] += off[threadIdx.x + 1] - off[threadIdx.x];
+}
+
+__global__ __launch_bounds__(256) void col_reduce_kernel(const float* __restrict__ part, int rows, int64_t ld, int len,
+                                                         float* __restrict__ out, int accumulate) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= len) return;
+  float s = 0.f;
+  for (int w = 0; w < rows; ++w) s += part[(int64_t)w * ld + c];
+  out[c] = accumulate ? out[c] + s : s;
+}
+
+__global__ __launch_bounds__(256) void lti_param_grad_kernel(const float* __restrict__ dA, const float* __restrict__ A,
+                                                             const float* __restrict__ log_A,
+                                                             const float* __restrict__ log_dt, int D,
+                                                             float* __restrict__ dlog_A, float* __restrict__ dlog_dt) {
+  __shared__ float red[4];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) {
+    const float x = log_dt[0] + log_A[i];
+    // A = exp(-exp(x)): dA/dx = -A exp(x); no gradient outside the clamp
+    const float g = (x >= -20.f && x <= 20.f) ? dA[i] * A[i] * -expf(x) : 0.f;
+    dlog_A[i] = g;
+    s += g;
+  }
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) dlog_dt[0] = s;
+}
+
+__global__ __launch_bounds__(256) void router_bias_update_kernel(float* __restrict__ bias,
+                                                                 const int32_t* __restrict__ load, int E,
+                                                                 float gamma) {
+  __shared__ int tot[256];
+  const int e = threadIdx.x;
+  tot[e] = e < E ? load[e] : 0;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (e < o) tot[e] += tot[e + o];
+    __syncthreads();
+  }
+  if (e < E) {
+    const long long d = (long long)tot[0] - (long long)E * load[e];
+    bias[e] += gamma * (float)((d > 0) - (d < 0));
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ launchers
+
+void launch_transpose_bf16(const void* in, int64_t isb1, int64_t isb2, int nb2, int64_t ldi, void* out, int64_t osb,
+                           int64_t ldo, int nbatch, int R, int Rp, int C, int Cv, hipStream_t s) {
+  const dim3 grid((C + 63) / 64, (Rp + 63) / 64, nbatch);
+  transpose_bf16_kernel<<<grid, 256, 0, s>>>((const bf16_t*)in, isb1, isb2, nb2, ldi, (bf16_t*)out, osb, ldo, R, Rp,
+                                             C, Cv);
+}
+
+void launch_wgrad(const WgradArgs& a, hipStream_t s) {
+  const dim3 grid(((a.Nc + 127) / 128) * ((a.Kc + 127) / 128), a.G, a.splits);
+  wgrad_kernel<<<grid, 256, 0, s>>>(a);
+}
+
+void launch_router_wgrad(const float* dz, const void* f, const int32_t* gidx, const int32_t* off, int n_loops,
+                         int NK, int E, int D, float* dWr, hipStream_t s) {
+  router_wgrad_kernel<<<dim3((D + 255) / 256, E), 256, 0, s>>>(dz, (const bf16_t*)f, gidx, off, n_loops, NK, E, D,
+                                                                dWr);
+}
+
+void launch_attn_bwd_prep(const void* o, const void* dO, int N, int H, int T, float* Dq, hipStream_t s) {
+  attn_bwd_prep_kernel<<<(N * H + 255) / 256, 256, 0, s>>>((const bf16_t*)o, (const bf16_t*)dO, N, H, T, Dq);
+}
+
+void launch_attn_bwd(const void* q, const void* k, const void* v, const void* dO, const void* qt, const void* dOt,
+                     const void* kt, const float* lse2, const float* Dq, float* dQ, float* dK, float* dV, int B,
+                     int H, int G, int T, int Tp, int cap, float scale, hipStream_t s) {
+  const float sl2 = scale * 1.4426950408889634f;
+  const int nkt = (T + 127) / 128;
+  attn_bwd_dkdv_kernel<<<nkt * B * G, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+                                                   (const bf16_t*)dO, (const bf16_t*)qt, (const bf16_t*)dOt, lse2, Dq,
+                                                   dK, dV, B, H, G, T, Tp, cap, sl2, scale);
+  attn_bwd_dq_kernel<<<nkt * B * H, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+                                                 (const bf16_t*)dO, (const bf16_t*)kt, lse2, Dq, dQ, B, H, G, T, cap,
+                                                 sl2, scale);
+}
+
+void launch_qkv_bwd(const float* dQ, const float* dK, const float* dV, const float* rcos, const float* rsin, int B,
+                    int T, int H, int G, void* dqkv, hipStream_t s) {
+  const int64_t n = (int64_t)B * T * (H + 2 * G) * 64;
+  qkv_bwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(dQ, dK, dV, rcos, rsin, B, T, H, G, (bf16_t*)dqkv);
+}
+
+void launch_swiglu_fwd(const void* gu, int M, int F, void* act, hipStream_t s) {
+  const int64_t n = (int64_t)M * F / 4;
+  swiglu_fwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const bf16_t*)gu, M, F, (bf16_t*)act);
+}
+
+void launch_swiglu_bwd(const void* gu, const float* dact, int M, int F, void* dgu, hipStream_t s) {
+  const int64_t n = (int64_t)M * F / 4;
+  swiglu_bwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const bf16_t*)gu, dact, M, F, (bf16_t*)dgu);
+}
+
+void launch_act_prep(const float* states, const float* dy, const float* halt_w, const float* halt_b,
+                     const int32_t* halt_counts, int L, int N, int D, float* w_act, float* z_act, float* part_hw,
+                     float* part_hb, hipStream_t s) {
+  act_prep_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(states, dy, halt_w, halt_b, halt_counts, L, N, D, w_act, z_act,
+                                                 part_hw, part_hb);
+}
+
+void launch_tail_bwd(const TailBwdArgs& a, hipStream_t s) { tail_bwd_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(a); }
+
+void launch_ffn_norm_bwd(int N, int D, int k, float eps, const float* df, const float* dfp, const int32_t* inv,
+                         const int32_t* sel, const float* dz, const void* Wr, const float* x1, const float* g_ffn,
+                         float* dx1, void* dx1_bf, float* part_g, hipStream_t s) {
+  ffn_norm_bwd_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, k, eps, df, dfp, inv, sel, dz, (const bf16_t*)Wr, x1,
+                                                     g_ffn, dx1, (bf16_t*)dx1_bf, part_g);
+}
+
+void launch_head_bwd(int N, int D, float eps, const float* dx1, const float* da, const float* c,
+                     const float* g_attn, const float* g_rec, const float* h_prev, const float* e, const float* emb_t,
+                     int loop_dim, float* g_carry, float* de, float* part_ga, float* part_gr, hipStream_t s) {
+  head_bwd_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, eps, dx1, da, c, g_attn, g_rec, h_prev, e, emb_t, loop_dim,
+                                                 g_carry, de, part_ga, part_gr);
+}
+
+void launch_loop_index(const int32_t* perm, const int32_t* off, int t, int NK, int N, int E, int32_t* gidx,
+                       int32_t* load, hipStream_t s) {
+  loop_index_kernel<<<(NK + 255) / 256, 256, 0, s>>>(perm, off, t, NK, N, E, gidx, load);
+}
+
+void launch_col_reduce(const float* part, int rows, int64_t ld, int len, float* out, int accumulate, hipStream_t s) {
+  col_reduce_kernel<<<(len + 255) / 256, 256, 0, s>>>(part, rows, ld, len, out, accumulate);
+}
+
+void launch_lti_param_grad(const float* dA, const float* A, const float* log_A, const float* log_dt, int D,
+                           float* dlog_A, float* dlog_dt, hipStream_t s) {
+  lti_param_grad_kernel<<<1, 256, 0, s>>>(dA, A, log_A, log_dt, D, dlog_A, dlog_dt);
+}
+
+void launch_router_bias_update(float* bias, const int32_t* load, int E, float gamma, hipStream_t s) {
+  router_bias_update_kernel<<<1, 256, 0, s>>>(bias, load, E, gamma);
+}
+
+namespace {
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+}  // namespace
+
+void launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (n == 0) return;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 4096);
+  fill_zero_kernel<<<(unsigned)blocks, 256, 0, s>>>((uint32_t*)p, n);
+}

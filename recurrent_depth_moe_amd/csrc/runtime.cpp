@@ -17,6 +17,7 @@
 
 #include "../../include/rdt.h"
 #include "attention.h"
+#include "backward.h"
 #include "gemm.h"
 #include "rowwise.h"
 
@@ -746,6 +747,7 @@ struct Ctx {
   int Mr;                    // rows of this loop
   const int32_t* tok;        // row -> position (null: row m is position m)
   const int32_t* live_prev;  // running count of the previous loop (null: always run)
+  float* lse2 = nullptr;     // bf16 prefill attention: log2 softmax normalisers (training recompute)
   void* W(int id) const { return w + p->off[id]; }
   float* WF(int id) const { return (float*)(w + p->off[id]); }
   int32_t* WI(int id) const { return (int32_t*)(w + p->off[id]); }
@@ -848,7 +850,7 @@ void attention_sublayer(const Ctx& x, const AttnW& aw, char* kslot, int cap_pad,
     }
     StageTimer st_(b, s, RDT_STAGE_ATTN);
     if (bf && T > 1)
-      launch_attn_flash_bf16(W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, kbase, scale, s, live_prev);
+      launch_attn_flash_bf16(W(WS_Q), K, VT, W(WS_O), B, H, G, T, cap, kbase, scale, s, live_prev, x.lse2);
     else if (kv && use_decode_attn(c, T))
       launch_attn_decode_bf16(W(WS_Q), K, VT, W(WS_O), WF(WS_DPART), B, H, G, cap, kbase + 1, scale, s);
     else
@@ -925,7 +927,8 @@ void attention_sublayer(const Ctx& x, const AttnW& aw, char* kslot, int cap_pad,
 
 static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int T, int start_pos, int n_loops,
                       float thr, void* kv, int kv_capacity, size_t kv_bytes, void* ws, size_t ws_bytes,
-                      float* h_out, int32_t* halt_counts, void* stream, bool decode, bool act_skip = false) {
+                      float* h_out, int32_t* halt_counts, void* stream, bool decode, bool act_skip = false,
+                      float* tape_h = nullptr) {
   g_err.clear();
   if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
   const rdt_config& c = b->cfg;
@@ -1135,7 +1138,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       ta.tok = tok;
       ta.D = D;
       ta.k = k;
-      ta.cap_h = b->cap_h ? b->cap_h + (size_t)t * N * D : nullptr;
+      ta.cap_h = tape_h ? tape_h + (size_t)t * N * D : b->cap_h ? b->cap_h + (size_t)t * N * D : nullptr;
       ta.cap_p = (b->cap_p && thr > 0.f) ? b->cap_p + (size_t)t * N : nullptr;
       ta.w_bf16 = bf;
       ta.live_prev = live_prev;
@@ -1565,6 +1568,529 @@ rdt_status rdt_model_generate(rdt_model* m, const int32_t* prompt, int32_t B, in
     st = model_run(m, out_ids + T0 + step - 1, L, B, 1, T0 + step - 1, n_loops, act_threshold, kv_cache,
                    kv_capacity, kv_bytes, workspace, ws_bytes, nullptr, out_ids + T0 + step, L, s);
   return st;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ training
+// The backward pass of the recurrent stage ([ZS §Recurrent Block] forward
+// with its expert choices and halting loops held fixed) and the router-bias
+// balancing step.  Each loop is recomputed from its recorded input state in
+// reverse order; the operands of every weight-gradient product are kept for
+// all loops (HBM holds them easily) so each weight gradient is one product
+// contracting over every loop's rows at the end.
+
+namespace {
+
+enum BwId {
+  // per loop, stacked over the loops: operands of the weight-gradient products
+  SV_A, SV_DQKV, SV_O, SV_DX1, SV_F, SV_GIDX, SV_OFF, SV_DZP, SV_DGU, SV_ACT, SV_DY, SV_ACTS, SV_DGUS, SV_DTAU,
+  SV_G, SV_TAU, SV_WL, SV_DV,
+  // working buffers of one loop
+  BW_G, BW_DX1, BW_DF, BW_DA, BW_DZ, BW_GU, BW_DACT, BW_DFP, BW_GUS, BW_DACTS, BW_DO, BW_LSE, BW_DELTA, BW_QT,
+  BW_DOT, BW_KT, BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC,
+  // per-wave partial column sums (contiguous: cleared together)
+  BP_A, BP_B, BP_GF, BP_GA, BP_GR, BP_HW, BP_HB, BP_S,
+  // transposed weights
+  TW_WO, TW_WQKV, TW_WD, TW_WGU, TW_WSD, TW_WSGU,
+  BW_COUNT
+};
+
+struct BwPlan {
+  Plan fwd;   // the recompute's forward workspace, at offset 0
+  size_t off[BW_COUNT], size[BW_COUNT], total;
+};
+
+BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
+  BwPlan q{};
+  q.fwd = make_plan(c, B, T);
+  const size_t N = (size_t)B * T, D = c.dim, E = c.n_experts, F = c.expert_dim, S = c.n_shared_experts;
+  const size_t NK = N * c.top_k, H = c.n_heads, G = c.n_kv_heads, QKV = (H + 2 * G) * 128, HD = H * 128;
+  const size_t Tp = round_up(T, 64), cap = q.fwd.kvcap, Ls = L, W = RDT_BWD_WAVES, r = c.lora_rank;
+  size_t* s = q.size;
+  s[SV_A] = Ls * N * D * 2;
+  s[SV_DQKV] = Ls * N * QKV * 2;
+  s[SV_O] = Ls * N * HD * 2;
+  s[SV_DX1] = Ls * N * D * 2;
+  s[SV_F] = Ls * N * D * 2;
+  s[SV_GIDX] = Ls * NK * 4;
+  s[SV_OFF] = Ls * (E + 1) * 4;
+  s[SV_DZP] = Ls * NK * 4;
+  s[SV_DGU] = Ls * NK * 2 * F * 2;
+  s[SV_ACT] = Ls * NK * F * 2;
+  s[SV_DY] = Ls * NK * D * 2;
+  s[SV_ACTS] = S * Ls * N * F * 2;
+  s[SV_DGUS] = S * Ls * N * 2 * F * 2;
+  s[SV_DTAU] = Ls * N * D * 2;
+  s[SV_G] = Ls * N * D * 2;
+  s[SV_TAU] = Ls * N * D * 2;
+  s[SV_WL] = Ls * N * RDT_LORA_LD * 2;
+  s[SV_DV] = Ls * N * RDT_LORA_LD * 2;
+  s[BW_G] = s[BW_DX1] = s[BW_DF] = s[BW_DA] = N * D * 4;
+  s[BW_DZ] = N * c.top_k * 4;
+  s[BW_GU] = NK * 2 * F * 2;
+  s[BW_DACT] = NK * F * 4;
+  s[BW_DFP] = NK * D * 4;
+  s[BW_GUS] = S * N * 2 * F * 2;
+  s[BW_DACTS] = N * F * 4;
+  s[BW_DO] = N * HD * 2;
+  s[BW_LSE] = s[BW_DELTA] = N * H * 4;
+  s[BW_QT] = s[BW_DOT] = (size_t)B * H * 128 * Tp * 2;
+  s[BW_KT] = s[BW_VN] = (size_t)B * G * 128 * cap * 2;
+  s[BW_GQ] = N * H * 128 * 4;
+  s[BW_GK] = s[BW_GV] = N * G * 128 * 4;
+  s[BW_WACT] = s[BW_ZACT] = Ls * N * 4;
+  s[BW_SPLIT] = Ls * r * D * 4;
+  s[BW_DAVEC] = D * 4;
+  s[BP_A] = s[BP_B] = s[BP_GF] = s[BP_GA] = s[BP_GR] = s[BP_HW] = W * D * 4;
+  s[BP_HB] = W * 4;
+  s[BP_S] = Ls * W * RDT_LORA_LD * 4;
+  s[TW_WO] = HD * D * 2;
+  s[TW_WQKV] = D * QKV * 2;
+  s[TW_WD] = E * F * D * 2;
+  s[TW_WGU] = E * D * 2 * F * 2;
+  s[TW_WSD] = S * F * D * 2;
+  s[TW_WSGU] = S * D * 2 * F * 2;
+  size_t o = align256(q.fwd.total);
+  for (int i = 0; i < BW_COUNT; ++i) {
+    q.off[i] = o;
+    o += align256(q.size[i]);
+  }
+  q.total = o;
+  return q;
+}
+
+// gradient buffer: the block's tensors in weight-table order, fp32, each
+// starting on a multiple of 64 elements except WK and WV, which follow WQ
+void grad_offsets(const rdt_config& c, int64_t* off, int64_t* numel, int64_t* total) {
+  TensorDesc td[RDT_W_COUNT];
+  int nt = 0;
+  tensor_list(c, td, &nt);
+  for (int i = 0; i < RDT_W_COUNT; ++i) off[i] = numel[i] = 0;
+  int64_t o = 0;
+  for (int i = 0; i < nt; ++i) {
+    if (td[i].id != RDT_W_WK && td[i].id != RDT_W_WV) o = (o + 63) / 64 * 64;
+    off[td[i].id] = o;
+    numel[td[i].id] = (int64_t)td[i].numel;
+    o += (int64_t)td[i].numel;
+  }
+  *total = (o + 63) / 64 * 64;
+}
+
+rdt_status check_train(const rdt_config& c, int B, int T, int n_loops, float thr) {
+  if (c.weight_dtype != RDT_BF16 || !is_gqa(c))
+    return fail(RDT_E_UNSUPPORTED, "training is built for bf16 blocks with GQA attention");
+  if (B < 1 || T < 1) return fail(RDT_E_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
+  if (T < 2) return fail(RDT_E_UNSUPPORTED, "training is built for sequences of T >= 2 tokens");
+  if (T > c.max_seq_len) return fail(RDT_E_INVALID_ARG, "T %d exceeds max_seq_len %d", T, c.max_seq_len);
+  if (n_loops < 1 || n_loops > RDT_MAX_TRAIN_LOOPS)
+    return fail(RDT_E_INVALID_ARG, "n_loops must be in [1, %d] for training", RDT_MAX_TRAIN_LOOPS);
+  if (!(thr == 0.f || (thr > 0.f && thr <= 1.f))) return fail(RDT_E_INVALID_ARG, "act_threshold must be 0 or in (0, 1]");
+  return RDT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rdt_status rdt_train_tape_bytes(const rdt_block* b, int32_t B, int32_t T, int32_t n_loops, size_t* bytes) {
+  g_err.clear();
+  if (!b || !bytes) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  rdt_status st = check_train(b->cfg, B, T, n_loops, 0.f);
+  if (st) return st;
+  *bytes = (size_t)n_loops * B * T * b->cfg.dim * 4;
+  return RDT_OK;
+}
+
+rdt_status rdt_train_workspace_bytes(const rdt_block* b, int32_t B, int32_t T, int32_t n_loops, size_t* bytes) {
+  g_err.clear();
+  if (!b || !bytes) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  rdt_status st = check_train(b->cfg, B, T, n_loops, 0.f);
+  if (st) return st;
+  *bytes = make_bw_plan(b->cfg, B, T, n_loops).total;
+  return RDT_OK;
+}
+
+rdt_status rdt_grad_layout(const rdt_block* b, int32_t id, int64_t* offset, int64_t* numel) {
+  g_err.clear();
+  if (!b || !offset || !numel) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  if (id < 0 || id >= RDT_W_COUNT) return fail(RDT_E_INVALID_ARG, "tensor id %d", id);
+  int64_t off[RDT_W_COUNT], n[RDT_W_COUNT], total = 0;
+  grad_offsets(b->cfg, off, n, &total);
+  *offset = off[id];
+  *numel = n[id];
+  return RDT_OK;
+}
+
+rdt_status rdt_grad_numel(const rdt_block* b, int64_t* numel) {
+  g_err.clear();
+  if (!b || !numel) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  int64_t off[RDT_W_COUNT], n[RDT_W_COUNT];
+  grad_offsets(b->cfg, off, n, numel);
+  return RDT_OK;
+}
+
+rdt_status rdt_train_forward(rdt_block* b, const float* e, const float* h0, int32_t B, int32_t T, int32_t n_loops,
+                             float act_threshold, void* workspace, size_t ws_bytes, float* tape, size_t tape_bytes,
+                             float* h_out, int32_t* halt_counts, void* stream) {
+  g_err.clear();
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  rdt_status st = check_train(b->cfg, B, T, n_loops, act_threshold);
+  if (st) return st;
+  if (!tape) return fail(RDT_E_INVALID_ARG, "tape is NULL");
+  const size_t need = (size_t)n_loops * B * T * b->cfg.dim * 4;
+  if (tape_bytes < need) return fail(RDT_E_WORKSPACE_TOO_SMALL, "tape %zu bytes, need %zu", tape_bytes, need);
+  return run(b, e, h0, B, T, 0, n_loops, act_threshold, nullptr, 0, 0, workspace, ws_bytes, h_out, halt_counts, stream,
+             false, false, tape);
+}
+
+rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int32_t B, int32_t T, int32_t n_loops,
+                              float thr, const float* tape, size_t tape_bytes, const int32_t* hc, const float* dy,
+                              float* grad, int64_t grad_numel, float* de, float* dh0, int32_t* load, void* ws,
+                              size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  const rdt_config& c = b->cfg;
+  rdt_status st = check_train(c, B, T, n_loops, thr);
+  if (st) return st;
+  if (!e || !h0 || !tape || !hc || !dy || !grad || !de || !dh0 || !load || !ws)
+    return fail(RDT_E_INVALID_ARG, "NULL argument");
+  const int N = B * T, D = c.dim, E = c.n_experts, F = c.expert_dim, S = c.n_shared_experts, k = c.top_k;
+  const int NK = N * k, H = c.n_heads, G = c.n_kv_heads, QKV = (H + 2 * G) * 128, HD = H * 128, r = c.lora_rank;
+  const int ld = c.loop_dim;
+  if (tape_bytes < (size_t)n_loops * N * D * 4) return fail(RDT_E_WORKSPACE_TOO_SMALL, "tape too small");
+  int64_t goff[RDT_W_COUNT], gnum[RDT_W_COUNT], gtotal = 0;
+  grad_offsets(c, goff, gnum, &gtotal);
+  if (grad_numel < gtotal)
+    return fail(RDT_E_WORKSPACE_TOO_SMALL, "gradient buffer of %lld elements, need %lld", (long long)grad_numel,
+                (long long)gtotal);
+  const BwPlan q = make_bw_plan(c, B, T, n_loops);
+  if (ws_bytes < q.total) return fail(RDT_E_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, q.total);
+  if (((uintptr_t)ws) & 255) return fail(RDT_E_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const bool act = thr > 0.f;
+  // loops run: with ACT on the forward stopped after the last halting loop
+  int L = n_loops;
+  if (act) {
+    std::vector<int32_t> hh(N);
+    HIP_TRY(hipMemcpyAsync(hh.data(), hc, (size_t)N * 4, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    L = 0;
+    for (int v : hh) {
+      if (v < 1 || v > n_loops) return fail(RDT_E_INVALID_ARG, "halt count %d outside [1, %d]", v, n_loops);
+      L = std::max(L, v);
+    }
+  }
+  const Plan& p = q.fwd;
+  char* w = (char*)ws;
+  auto W = [&](int id) -> void* { return w + p.off[id]; };
+  auto WF = [&](int id) -> float* { return (float*)(w + p.off[id]); };
+  auto WI = [&](int id) -> int32_t* { return (int32_t*)(w + p.off[id]); };
+  auto Q = [&](int id) -> void* { return w + q.off[id]; };
+  auto QF = [&](int id) -> float* { return (float*)(w + q.off[id]); };
+  auto QI = [&](int id) -> int32_t* { return (int32_t*)(w + q.off[id]); };
+  auto QB = [&](int id) -> bf16_t* { return (bf16_t*)(w + q.off[id]); };
+  const bf16_t* wb = nullptr;
+  (void)wb;
+  const int cap = p.kvcap, Tp = round_up(T, 64);
+  const float eps = c.norm_eps, scale = 1.0f / sqrtf(128.f);
+  const size_t NDs = (size_t)N * D;
+
+  // what accumulates starts at zero
+  launch_fill_zero(grad, (size_t)gtotal * 4, s);
+  launch_fill_zero(de, NDs * 4, s);
+  launch_fill_zero(load, (size_t)E * 4, s);
+  launch_fill_zero(Q(BP_A), q.off[BP_S] + q.size[BP_S] - q.off[BP_A], s);
+  // transposed weights: W^T of every product whose input gradient is taken
+  {
+    const bf16_t* wqkv = (const bf16_t*)b->wqkv;
+    launch_transpose_bf16(b->wo, 0, 0, 1, HD, Q(TW_WO), 0, D, 1, D, D, HD, HD, s);              // [HD][D]
+    launch_transpose_bf16(wqkv, 0, 0, 1, D, Q(TW_WQKV), 0, QKV, 1, QKV, QKV, D, D, s);          // [D][QKV]
+    launch_transpose_bf16(b->w_down, (int64_t)D * F, 0, 1, F, Q(TW_WD), (int64_t)F * D, D, E, D, D, F, F, s);
+    launch_transpose_bf16(b->w_gate, (int64_t)F * D, 0, 1, D, Q(TW_WGU), (int64_t)D * 2 * F, 2 * F, E, F, F, D, D, s);
+    launch_transpose_bf16(b->w_up, (int64_t)F * D, 0, 1, D, QB(TW_WGU) + F, (int64_t)D * 2 * F, 2 * F, E, F, F, D, D,
+                          s);
+    if (S) {
+      launch_transpose_bf16(b->s_down, (int64_t)D * F, 0, 1, F, Q(TW_WSD), (int64_t)F * D, D, S, D, D, F, F, s);
+      launch_transpose_bf16(b->s_gate, (int64_t)F * D, 0, 1, D, Q(TW_WSGU), (int64_t)D * 2 * F, 2 * F, S, F, F, D,
+                            D, s);
+      launch_transpose_bf16(b->s_up, (int64_t)F * D, 0, 1, D, QB(TW_WSGU) + F, (int64_t)D * 2 * F, 2 * F, S, F, F, D,
+                            D, s);
+    }
+  }
+  // ACT: the weight of each loop's state in the output and the gradient of
+  // each halting logit; without ACT the output is the last state
+  if (act) {
+    launch_fill_zero(Q(BW_G), NDs * 4, s);
+    launch_act_prep(tape, dy, b->halt_w, b->halt_b, hc, L, N, D, QF(BW_WACT), QF(BW_ZACT), QF(BP_HW), QF(BP_HB), s);
+  } else {
+    HIP_TRY(hipMemcpyAsync(Q(BW_G), dy, NDs * 4, hipMemcpyDeviceToDevice, s));
+  }
+  Ctx x{b, &c, &p, w, s, true, B, T, 0, N, nullptr, nullptr};
+  x.lse2 = QF(BW_LSE);
+  const size_t es = 2;
+  for (int t = L - 1; t >= 0; --t) {
+    const float* hp = t == 0 ? h0 : tape + (size_t)(t - 1) * NDs;
+    const float* emb_t = b->loop_emb + (size_t)t * ld;
+    // ---- recompute loop t (same kernels and schedules as the forward up
+    // to the routed products, so the expert choice is the forward's)
+    launch_loop_head(1, hp, e, emb_t, ld, b->g_rec, b->g_attn, eps, WF(WS_C), W(WS_A), N, D, s);
+    attention_sublayer(x, b->aw, nullptr, 0, WF(WS_C), WF(WS_X1));
+    launch_rmsnorm(1, WF(WS_X1), D, b->g_ffn, eps, W(WS_F), D, N, D, s);
+    {
+      GemmParams gp = dense_params(W(WS_F), D, b->router, nullptr, N, E, D);
+      gp.epi.out = W(WS_LOGITS);
+      gp.epi.ldo = E;
+      x.gemm(gp, EPI_STORE, false, 0, true);
+      launch_router_topk(WF(WS_LOGITS), b->router_bias, N, E, k, WI(WS_SEL), WF(WS_GATE), nullptr, s);
+    }
+    launch_dispatch(WI(WS_SEL), NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART), WI(WS_TROW0),
+                    WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), WI(WS_TCLAIM), 2 * RDT_NUM_XCD, s);
+    launch_loop_index(WI(WS_PERM), WI(WS_OFFSETS), t, NK, N, E, QI(SV_GIDX), load, s);
+    HIP_TRY(hipMemcpyAsync(QI(SV_OFF) + (size_t)t * (E + 1), WI(WS_OFFSETS), (size_t)(E + 1) * 4,
+                           hipMemcpyDeviceToDevice, s));
+    // routed gate and up pre-activations (kept for the SwiGLU backward),
+    // the activation and the routed outputs
+    GemmParams gp{};
+    gp.A = W(WS_F);
+    gp.lda = D;
+    gp.a_rows = WI(WS_PERM);
+    gp.W0 = b->w_gate;
+    gp.w_stride = (int64_t)F * D;
+    gp.M = NK;
+    gp.N = F;
+    gp.K = D;
+    gp.mt_start = WI(WS_MTSTART);
+    gp.tile_row0 = WI(WS_TROW0);
+    gp.tile_grp = WI(WS_TGRP);
+    gp.grp_end = WI(WS_OFFSETS);
+    gp.n_groups = E;
+    gp.epi.out = Q(BW_GU);
+    gp.epi.ldo = 2 * F;
+    launch_gemm_bf16_big(gp, EPI_STORE, false, 1, b->n_cu, s, 256);
+    gp.W0 = b->w_up;
+    gp.epi.out = QB(BW_GU) + F;
+    launch_gemm_bf16_big(gp, EPI_STORE, false, 1, b->n_cu, s, 256);
+    bf16_t* act_t = QB(SV_ACT) + (size_t)t * NK * F;
+    launch_swiglu_fwd(Q(BW_GU), NK, F, act_t, s);
+    {
+      GemmParams gd = gp;
+      gd.A = act_t;
+      gd.lda = F;
+      gd.a_rows = nullptr;
+      gd.W0 = b->w_down;
+      gd.w_stride = (int64_t)D * F;
+      gd.N = D;
+      gd.K = F;
+      gd.epi = EpiParams{};
+      gd.epi.out = W(WS_Y);
+      gd.epi.ldo = D;
+      launch_gemm_bf16_big(gd, EPI_STORE, false, 1, b->n_cu, s, 256);
+    }
+    for (int si = 0; si < S; ++si) {
+      bf16_t* gus = QB(BW_GUS) + (size_t)si * N * 2 * F;
+      GemmParams gs = dense_params(W(WS_F), D, (const char*)b->s_gate + (size_t)si * F * D * es, nullptr, N, F, D);
+      gs.epi.out = gus;
+      gs.epi.ldo = 2 * F;
+      x.gemm(gs, EPI_STORE, false, 1);
+      gs.W0 = (const char*)b->s_up + (size_t)si * F * D * es;
+      gs.epi.out = gus + F;
+      x.gemm(gs, EPI_STORE, false, 1);
+      bf16_t* acts = QB(SV_ACTS) + ((size_t)si * n_loops + t) * N * F;
+      launch_swiglu_fwd(gus, N, F, acts, s);
+      GemmParams gd = dense_params(acts, F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, N, D, F);
+      gd.epi.out = (bf16_t*)W(WS_YS) + (size_t)si * NDs;
+      gd.epi.ldo = D;
+      x.gemm(gd, EPI_STORE, false, 1);
+    }
+    HIP_TRY(hipMemcpyAsync(QB(SV_A) + (size_t)t * NDs, W(WS_A), NDs * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(hipMemcpyAsync(QB(SV_O) + (size_t)t * N * HD, W(WS_O), (size_t)N * HD * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(hipMemcpyAsync(QB(SV_F) + (size_t)t * NDs, W(WS_F), NDs * 2, hipMemcpyDeviceToDevice, s));
+
+    // ---- backward of loop t
+    {
+      TailBwdArgs ta{};
+      ta.N = N;
+      ta.D = D;
+      ta.k = k;
+      ta.S = S;
+      ta.r = r;
+      ta.g = QF(BW_G);
+      ta.dy = dy;
+      ta.w_act = act ? QF(BW_WACT) + (size_t)t * N : nullptr;
+      ta.z_act = act ? QF(BW_ZACT) + (size_t)t * N : nullptr;
+      ta.halt_w = b->halt_w;
+      ta.x1 = WF(WS_X1);
+      ta.y = W(WS_Y);
+      ta.inv = WI(WS_INV);
+      ta.gate = WF(WS_GATE);
+      ta.ys = W(WS_YS);
+      ta.lora_down = b->lora_down;
+      ta.lora_B = b->lora_B;
+      ta.scale_row = b->lora_scale + (size_t)std::min(t, c.max_loop_iters - 1) * r;
+      ta.A = b->A;
+      ta.Bv = b->Bv;
+      ta.h_prev = hp;
+      ta.e = e;
+      ta.g_next = QF(BW_G);
+      ta.de = de;
+      ta.dtau = QF(BW_DX1);
+      ta.dtau_bf = QB(SV_DTAU) + (size_t)t * NDs;
+      ta.dY = QB(SV_DY) + (size_t)t * NK * D;
+      ta.dz = QF(BW_DZ);
+      ta.dz_perm = QF(SV_DZP) + (size_t)t * NK;
+      ta.sv_g = QB(SV_G) + (size_t)t * NDs;
+      ta.sv_tau = QB(SV_TAU) + (size_t)t * NDs;
+      ta.sv_wl = QB(SV_WL) + (size_t)t * N * RDT_LORA_LD;
+      ta.sv_dv = QB(SV_DV) + (size_t)t * N * RDT_LORA_LD;
+      ta.part_A = QF(BP_A);
+      ta.part_B = QF(BP_B);
+      ta.part_s = QF(BP_S) + (size_t)t * RDT_BWD_WAVES * RDT_LORA_LD;
+      launch_tail_bwd(ta, s);
+    }
+    // shared experts: d act_s = dtau Wsd, SwiGLU backward, df (+)= dGU_s [Wsg; Wsu]
+    for (int si = 0; si < S; ++si) {
+      const bf16_t* gus = QB(BW_GUS) + (size_t)si * N * 2 * F;
+      GemmParams g1 = dense_params(QB(SV_DTAU) + (size_t)t * NDs, D, QB(TW_WSD) + (size_t)si * F * D, nullptr, N, F, D);
+      g1.epi.out = QF(BW_DACTS);
+      g1.epi.ldo = F;
+      x.gemm(g1, EPI_STORE, false, 0);
+      bf16_t* dgus = QB(SV_DGUS) + ((size_t)si * n_loops + t) * N * 2 * F;
+      launch_swiglu_bwd(gus, QF(BW_DACTS), N, F, dgus, s);
+      GemmParams g2 = dense_params(dgus, 2 * F, QB(TW_WSGU) + (size_t)si * D * 2 * F, nullptr, N, D, 2 * F);
+      g2.epi.out = QF(BW_DF);
+      g2.epi.ldo = D;
+      if (si == 0) {
+        x.gemm(g2, EPI_STORE, false, 0);
+      } else {
+        g2.epi.resid = QF(BW_DF);
+        x.gemm(g2, EPI_RESID, false, 0);
+      }
+    }
+    // routed experts: d act = dY Wd_e, SwiGLU backward, dfp = dGU [Wg; Wu]_e
+    {
+      GemmParams r1 = gp;
+      r1.A = QB(SV_DY) + (size_t)t * NK * D;
+      r1.lda = D;
+      r1.a_rows = nullptr;
+      r1.W0 = Q(TW_WD);
+      r1.w_stride = (int64_t)F * D;
+      r1.N = F;
+      r1.K = D;
+      r1.epi = EpiParams{};
+      r1.epi.out = QF(BW_DACT);
+      r1.epi.ldo = F;
+      launch_gemm_bf16_big(r1, EPI_STORE, false, 0, b->n_cu, s, 256);
+      bf16_t* dgu = QB(SV_DGU) + (size_t)t * NK * 2 * F;
+      launch_swiglu_bwd(Q(BW_GU), QF(BW_DACT), NK, F, dgu, s);
+      GemmParams r2 = r1;
+      r2.A = dgu;
+      r2.lda = 2 * F;
+      r2.W0 = Q(TW_WGU);
+      r2.w_stride = (int64_t)D * 2 * F;
+      r2.N = D;
+      r2.K = 2 * F;
+      r2.epi.out = QF(BW_DFP);
+      r2.epi.ldo = D;
+      launch_gemm_bf16_big(r2, EPI_STORE, false, 0, b->n_cu, s, 256);
+    }
+    launch_ffn_norm_bwd(N, D, k, eps, S ? QF(BW_DF) : nullptr, QF(BW_DFP), WI(WS_INV), WI(WS_SEL), QF(BW_DZ), b->router,
+                        WF(WS_X1), b->g_ffn, QF(BW_DX1), QB(SV_DX1) + (size_t)t * NDs, QF(BP_GF), s);
+    // attention: dO = dx1 Wo, flash backward, dqkv (RoPE taken back), da = dqkv Wqkv
+    {
+      GemmParams a1 = dense_params(QB(SV_DX1) + (size_t)t * NDs, D, Q(TW_WO), nullptr, N, HD, D);
+      a1.epi.out = Q(BW_DO);
+      a1.epi.ldo = HD;
+      x.gemm(a1, EPI_STORE, false, 1);
+      launch_attn_bwd_prep(W(WS_O), Q(BW_DO), N, H, T, QF(BW_DELTA), s);
+      launch_transpose_bf16(W(WS_Q), (int64_t)T * 128, 0, 1, 128, Q(BW_QT), (int64_t)128 * Tp, Tp, B * H, T, Tp, 128,
+                            128, s);
+      launch_transpose_bf16(Q(BW_DO), (int64_t)T * HD, 128, H, HD, Q(BW_DOT), (int64_t)128 * Tp, Tp, B * H, T, Tp,
+                            128, 128, s);
+      launch_transpose_bf16(W(WS_K), (int64_t)cap * 128, 0, 1, 128, Q(BW_KT), (int64_t)128 * cap, cap, B * G, T, cap,
+                            128, 128, s);
+      launch_transpose_bf16(W(WS_VT), (int64_t)128 * cap, 0, 1, cap, Q(BW_VN), (int64_t)cap * 128, 128, B * G, 128,
+                            128, cap, T, s);
+      launch_attn_bwd(W(WS_Q), W(WS_K), Q(BW_VN), Q(BW_DO), Q(BW_QT), Q(BW_DOT), Q(BW_KT), QF(BW_LSE), QF(BW_DELTA),
+                      QF(BW_GQ), QF(BW_GK), QF(BW_GV), B, H, G, T, Tp, cap, scale, s);
+      bf16_t* dqkv = QB(SV_DQKV) + (size_t)t * N * QKV;
+      launch_qkv_bwd(QF(BW_GQ), QF(BW_GK), QF(BW_GV), b->rope_cos, b->rope_sin, B, T, H, G, dqkv, s);
+      GemmParams a2 = dense_params(dqkv, QKV, Q(TW_WQKV), nullptr, N, D, QKV);
+      a2.epi.out = QF(BW_DA);
+      a2.epi.ldo = D;
+      x.gemm(a2, EPI_STORE, false, 0);
+    }
+    launch_head_bwd(N, D, eps, QF(BW_DX1), QF(BW_DA), WF(WS_C), b->g_attn, b->g_rec, hp, e, emb_t, ld, QF(BW_G), de,
+                    QF(BP_GA), QF(BP_GR), s);
+  }
+  HIP_TRY(hipMemcpyAsync(dh0, Q(BW_G), NDs * 4, hipMemcpyDeviceToDevice, s));
+
+  // ---- weight gradients: one product per tensor over every loop's rows
+  auto wgrad = [&](const void* A, int64_t lda, const void* X, int64_t ldx, const int32_t* xrow, const int32_t* off,
+                   int64_t loop_rows, int rows, int groups, int Nc, int Kc, float* C, int64_t ldc, int64_t cg,
+                   int splits, int64_t css) {
+    WgradArgs a{A, lda, X, ldx, xrow, off, L, loop_rows, rows, groups, Nc, Kc, C, ldc, cg, splits, css, 0};
+    launch_wgrad(a, s);
+  };
+  float* gb = grad;
+  wgrad(Q(SV_DQKV), QKV, Q(SV_A), D, nullptr, nullptr, N, N, 1, QKV, D, gb + goff[RDT_W_WQ], D, 0, 1, 0);
+  wgrad(Q(SV_DX1), D, Q(SV_O), HD, nullptr, nullptr, N, N, 1, D, HD, gb + goff[RDT_W_WO], HD, 0, 1, 0);
+  launch_router_wgrad(QF(SV_DZP), Q(SV_F), QI(SV_GIDX), QI(SV_OFF), L, NK, E, D, gb + goff[RDT_W_ROUTER], s);
+  wgrad(Q(SV_DGU), 2 * F, Q(SV_F), D, QI(SV_GIDX), QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_GATE], D,
+        (int64_t)F * D, 1, 0);
+  wgrad(QB(SV_DGU) + F, 2 * F, Q(SV_F), D, QI(SV_GIDX), QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_UP], D,
+        (int64_t)F * D, 1, 0);
+  wgrad(Q(SV_DY), D, Q(SV_ACT), F, nullptr, QI(SV_OFF), NK, 0, E, D, F, gb + goff[RDT_W_DOWN], F, (int64_t)D * F, 1,
+        0);
+  for (int si = 0; si < S; ++si) {
+    const bf16_t* dgus = QB(SV_DGUS) + (size_t)si * n_loops * N * 2 * F;
+    const bf16_t* acts = QB(SV_ACTS) + (size_t)si * n_loops * N * F;
+    wgrad(dgus, 2 * F, Q(SV_F), D, nullptr, nullptr, N, N, 1, F, D, gb + goff[RDT_W_S_GATE] + (size_t)si * F * D, D,
+          0, 1, 0);
+    wgrad(dgus + F, 2 * F, Q(SV_F), D, nullptr, nullptr, N, N, 1, F, D, gb + goff[RDT_W_S_UP] + (size_t)si * F * D,
+          D, 0, 1, 0);
+    wgrad(Q(SV_DTAU), D, acts, F, nullptr, nullptr, N, N, 1, D, F, gb + goff[RDT_W_S_DOWN] + (size_t)si * D * F, F,
+          0, 1, 0);
+  }
+  // depth-wise LoRA: split over the loops, then summed
+  const int64_t rD = (int64_t)r * D;
+  wgrad(Q(SV_WL), RDT_LORA_LD, Q(SV_G), D, nullptr, nullptr, N, N, 1, r, D, QF(BW_SPLIT), D, 0, L, rD);
+  launch_col_reduce(QF(BW_SPLIT), L, rD, (int)rD, gb + goff[RDT_W_LORA_B], 0, s);
+  wgrad(Q(SV_DV), RDT_LORA_LD, Q(SV_TAU), D, nullptr, nullptr, N, N, 1, r, D, QF(BW_SPLIT), D, 0, L, rD);
+  launch_col_reduce(QF(BW_SPLIT), L, rD, (int)rD, gb + goff[RDT_W_LORA_DOWN], 0, s);
+  for (int t = 0; t < L; ++t)
+    launch_col_reduce(QF(BP_S) + (size_t)t * RDT_BWD_WAVES * RDT_LORA_LD, RDT_BWD_WAVES, RDT_LORA_LD, r,
+                      gb + goff[RDT_W_LORA_SCALE] + (size_t)std::min(t, c.max_loop_iters - 1) * r, 1, s);
+  // vectors: norm gains, B, halting head, A's parameters
+  launch_col_reduce(QF(BP_GR), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_G_REC], 0, s);
+  launch_col_reduce(QF(BP_GA), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_G_ATTN], 0, s);
+  launch_col_reduce(QF(BP_GF), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_G_FFN], 0, s);
+  launch_col_reduce(QF(BP_B), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_B], 0, s);
+  launch_col_reduce(QF(BP_HW), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_HALT_W], 0, s);
+  launch_col_reduce(QF(BP_HB), RDT_BWD_WAVES, 1, 1, gb + goff[RDT_W_HALT_B], 0, s);
+  launch_col_reduce(QF(BP_A), RDT_BWD_WAVES, D, D, QF(BW_DAVEC), 0, s);
+  launch_lti_param_grad(QF(BW_DAVEC), b->A, b->log_A, b->log_dt, D, gb + goff[RDT_W_LOG_A], gb + goff[RDT_W_LOG_DT],
+                        s);
+  hipError_t he = hipGetLastError();
+  if (he != hipSuccess) return fail(RDT_E_HIP, "kernel launch: %s", hipGetErrorString(he));
+  return RDT_OK;
+}
+
+rdt_status rdt_get_router_bias(const rdt_block* b, float* bias_host) {
+  g_err.clear();
+  if (!b || !bias_host) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  HIP_TRY(hipMemcpy(bias_host, b->router_bias, (size_t)b->cfg.n_experts * 4, hipMemcpyDeviceToHost));
+  return RDT_OK;
+}
+
+rdt_status rdt_router_bias_update(rdt_block* b, const int32_t* expert_load, float gamma, void* stream) {
+  g_err.clear();
+  if (!b || !expert_load) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  if (!std::isfinite(gamma)) return fail(RDT_E_INVALID_ARG, "gamma must be finite");
+  launch_router_bias_update((float*)b->router_bias, expert_load, b->cfg.n_experts, gamma, (hipStream_t)stream);
+  hipError_t he = hipGetLastError();
+  if (he != hipSuccess) return fail(RDT_E_HIP, "kernel launch: %s", hipGetErrorString(he));
+  return RDT_OK;
 }
 
 }  // extern "C"
