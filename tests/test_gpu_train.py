@@ -15,7 +15,9 @@ bf16 roundings that it differentiates; independent roundings add in
 quadrature, so a norm-relative error of a few 1e-3 per loop, growing like
 the square root of the loops, is expected.  The bound is
 2e-2 * sqrt(loops) (the free-running forward's 3e-2 * sqrt(loops) scaled by
-the ratio of norm-wise to max-wise error), checked on every tensor.
+the ratio of norm-wise to max-wise error), checked on every tensor; the
+scalar d log_dt, a sum of the D log_A gradients, against the sum of their
+magnitudes.
 
 Pages: [ZS] "OpenMythos 분석: …의 계산 모델링" (zero.shotlearni.ng),
 §Recurrent Block, §ACT, §MoE.
@@ -33,6 +35,9 @@ from gpu_support import EPS_HALT, EPS_ROUTE, to_np
 pytestmark = pytest.mark.gpu
 
 SPREAD = {"halt_w": 0.05, "halt_b": -0.8}
+# O(1) LoRA and output scales, so the LoRA and residual terms of every
+# input gradient are far above the tolerance
+BIG = {"lora_scale": 1.0, "lora_B": 0.3, "wo": 0.1, "w_down": 0.1, "s_down": 0.1, "halt_w": 0.05, "halt_b": -0.8}
 
 
 def _grad_tol(n_loops):
@@ -88,6 +93,10 @@ def _check(cfg, W, e, h0):
         want = np.asarray(ref[name], dtype=np.float64).reshape(-1)
         got = np.asarray(got, dtype=np.float64).reshape(-1)
         nrm = np.linalg.norm(want)
+        if name == "log_dt":
+            # the sum of the log_A gradients: with each term off by a
+            # relative e, the sum is off by at most e * sum |terms|
+            nrm = np.abs(np.asarray(ref["log_A"], dtype=np.float64)).sum()
         err = np.linalg.norm(got - want) / nrm if nrm > 0 else np.linalg.norm(got)
         print(f"  {name:11s} |ref| {nrm:.3e}  rel err {err:.3e}", flush=True)
         worst = max(worst, err)
@@ -100,12 +109,16 @@ def _check(cfg, W, e, h0):
 @pytest.mark.parametrize("name, scales, over", [
     ("small_bf16", SPREAD, dict(n_loops=4)),
     ("small_bf16_k3", None, dict()),
-], ids=["small_bf16_act", "small_bf16_k3"])
+    ("small_bf16", BIG, dict(n_loops=3)),
+    ("small_bf16_strip", None, dict()),
+], ids=["small_bf16_act", "small_bf16_k3", "large_terms", "strip_540_tokens"])
 def test_backward_matches_gradient_oracle(name, scales, over):
     """small_bf16: ACT on with halting spread over the loops (remainder
     weights, positions running on after others halted), 200 tokens (ragged
     attention tiles); small_bf16_k3: ACT off, top-3 of 12 experts, two
-    shared experts, 77 tokens."""
+    shared experts, 77 tokens; large_terms: O(1) LoRA and projections;
+    strip_540_tokens: dim 768, 1080 rows (several 128-row attention and
+    weight-gradient tiles, ~270 routed rows per expert)."""
     cfg = configs.get(name, **over)
     W = generate.make_weights(cfg, scales=scales)
     e, h0 = generate.make_inputs(cfg)
@@ -130,3 +143,14 @@ def test_router_bias_balancing_step():
     after = blk.get_router_bias().numpy()
     np.testing.assert_array_equal(after, OB.router_bias_update(before, g["load"], 0.03125))
     assert np.any(after != before)
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_size_mythos_1b_one_loop():
+    """mythos_1b at full size (dim 2048, 16 heads, 64 experts of 2048,
+    4096 tokens), one loop: every kernel at the shapes the training bench
+    runs (many tiles, real routing skew, 32 attention tiles per head)."""
+    cfg = configs.get("mythos_1b", n_loops=1)
+    W = generate.make_weights(cfg)
+    e, h0 = generate.make_inputs(cfg)
+    _check(cfg, W, e, h0)
