@@ -145,6 +145,93 @@ def cpu_baseline(cfg, W, e, h0, prefix):
                        f"({cfg['batch'] * prefix} token-loops, {dt:.1f} s)")
 
 
+def train_flops(cfg, loops):
+    """Algorithmic flops of one training step: the forward, then per loop the
+    input-gradient and weight-gradient products (each the forward product's
+    flops) and the attention backward (dV, dP, dQ, dK: twice the forward's
+    two products)."""
+    w = stage_work(cfg)
+    fwd = sum(v["flops"] for v in w.values() if "flops" in v)
+    att = w["attention"]["flops"]
+    return loops * (fwd + 2 * (fwd - att) + 2 * att)
+
+
+def train_bench(args, cfg):
+    import threading
+
+    import numpy as np
+    import torch
+
+    from recurrent_depth_moe_amd import binding
+    from workloads import generate
+    B, T, D, L, thr = cfg["batch"], cfg["seq"], cfg["dim"], cfg["n_loops"], cfg["act_threshold"]
+    t0 = time.time()
+    W = generate.make_weights(cfg)
+    e, h0 = generate.make_inputs(cfg)
+    log(f"[bench] {args.config} training step: inputs generated in {time.time() - t0:.1f}s")
+    blk = binding.Block(cfg, binding.weights_to_device(W))
+    et = torch.from_numpy(e).cuda()
+    ht = torch.from_numpy(h0).cuda()
+    dy = torch.from_numpy(np.random.default_rng(5).standard_normal(e.shape).astype(np.float32)).cuda()
+    ws = blk.new_workspace(B, T)
+    tape = torch.empty(blk.train_tape_bytes(B, T, L) // 4, dtype=torch.float32, device="cuda")
+    bws = torch.empty(blk.train_workspace_bytes(B, T, L), dtype=torch.uint8, device="cuda")
+    grad = torch.empty(blk.grad_numel(), dtype=torch.float32, device="cuda")
+    de, dh0 = torch.empty_like(et), torch.empty_like(et)
+    load = torch.empty(cfg["n_experts"], dtype=torch.int32, device="cuda")
+    h_out = torch.empty_like(et)
+    hc = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    log(f"[bench] training workspace {bws.numel() / 2**30:.1f} GiB, tape {tape.numel() * 4 / 2**30:.2f} GiB")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        blk.train_forward(et, ht, L, thr, tape, ws, h_out, hc)
+        blk.train_backward(et, ht, L, thr, tape, hc, dy, bws, grad, de, dh0, load)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    clocks, stop = [], threading.Event()
+    sampler = threading.Thread(target=sample_sclk, args=(stop, clocks), daemon=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    if not args.no_clock:
+        sampler.start()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+        log(f"[bench] step {i + 1}/{args.steps} enqueued")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stop.set()
+    if not args.no_clock:
+        sampler.join(timeout=15)
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    halt = hc.cpu().numpy()
+    loops = int(halt.max()) if thr > 0 else L
+    value = B * T * loops * args.steps / elapsed
+    fl = train_flops(cfg, loops)
+    ms_step = elapsed / args.steps * 1e3
+    out = {
+        "metric": "recurrent-block training token·loops/sec (1 GPU; forward + backward)", "value": round(value, 1),
+        "unit": "token·loops/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3), "ms_per_step_median": round(step_ms[len(step_ms) // 2], 3),
+        "ms_per_step_min": round(step_ms[0], 3), "sclk_mhz_samples": clocks, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
+        "data": "synthetic (seeded N(0,0.02) weights, RMS-normalised N(0,1) inputs, N(0,1) upstream gradient)",
+        "config": {"workload": f"{args.config}-shaped recurrent block, training step (forward + backward), "
+                               f"{cfg['dtype']}, batch {B} x seq {T}, {L} loops, ACT {'off' if thr == 0 else thr}",
+                   "loops_executed": loops},
+        "algorithmic_tflops_per_step": round(fl / 1e12, 1),
+        "achieved_tflops": round(fl / (ms_step * 1e-3) / 1e12, 1),
+        "mfma_frac_of_step": round(fl / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +243,9 @@ def main():
     ap.add_argument("--act-skip", action="store_true",
                     help="ACT with compute skipping (halted positions leave the batch; "
                          "rdt_recurrent_forward_act_skip); value = token-loops actually run per second")
+    ap.add_argument("--train", action="store_true",
+                    help="training step: rdt_train_forward + rdt_train_backward (gradients of every trained "
+                         "tensor, e and h0 for a seeded upstream gradient); value = token-loops trained per second")
     ap.add_argument("--no-clock", action="store_true",
                     help="do not sample the core clock with rocm-smi (for runs under a profiler)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -184,6 +274,9 @@ def main():
     from workloads import configs, generate
 
     cfg = configs.get(args.config)
+    if args.train:
+        train_bench(args, cfg)
+        return
     B, T, D, n_loops, thr = cfg["batch"], cfg["seq"], cfg["dim"], cfg["n_loops"], cfg["act_threshold"]
     t0 = time.time()
     W = generate.make_weights(cfg)

@@ -9,10 +9,12 @@
 // RDT_BWD_BLOCKS blocks of four waves; wave w of block b owns partial row
 // 4 b + w and adds its rows' contributions there, so every sum is formed in
 // a fixed order.
-#define RDT_BWD_BLOCKS 256
+#define RDT_BWD_BLOCKS 1024
 #define RDT_BWD_WAVES (RDT_BWD_BLOCKS * 4)
 // row stride of the saved LoRA vectors (lora_rank <= 32)
 #define RDT_LORA_LD 32
+// loops a weight-gradient product may stack (the training loop limit)
+#define RDT_MAX_WGRAD_LOOPS 64
 
 // out[bi][c][r] = in(bi)[r][c] for r < R and c < Cv, 0 for R <= r < Rp or
 // Cv <= c < C, where bi = b1 * nb2 + b2 and in(bi) = in + b1 * isb1 + b2 * isb2
@@ -47,9 +49,11 @@ struct WgradArgs {
 void launch_wgrad(const WgradArgs& a, hipStream_t s);
 
 // dWr[e][c] = sum over loops t and dispatch rows m of expert e of
-// dz[t][m] * f[gidx[t][m]][c]   (f bf16 rows stacked over loops)
-void launch_router_wgrad(const float* dz, const void* f, const int32_t* gidx, const int32_t* off, int n_loops,
-                         int NK, int E, int D, float* dWr, hipStream_t s);
+// dz[t][m] * fperm[t][m][c]   (f in dispatch order, bf16, stacked over loops)
+void launch_router_wgrad(const float* dz, const void* fperm, const int32_t* off, int n_loops, int NK, int E, int D,
+                         float* dWr, hipStream_t s);
+// dst[m] = src[perm[m]] for m < M (bf16 rows of D, D a multiple of 8)
+void launch_gather_rows_bf16(const void* src, const int32_t* perm, int M, int D, void* dst, hipStream_t s);
 
 // Flash-attention backward (bf16, head width 128, causal, GQA).
 // Dq[b][h][i] = sum_d dO[b i][h d] o[b i][h d]
@@ -99,7 +103,7 @@ struct TailBwdArgs {
   const float* e;          // [N][D]
   float* g_next;           // A * g_full (may alias g)
   float* de;               // += B * g_full
-  float* dtau;             // fp32 [N][D]
+  float* dtau;             // fp32 [N][D]: g_full after the rows pass, dtau after the LoRA product
   void* dtau_bf;           // bf16 [N][D]
   void* dY;                // bf16 [NK][D], row inv[n k + j] = gate_j dtau
   float* dz;               // [N][k] d loss / d router logit of each chosen expert
@@ -110,9 +114,17 @@ struct TailBwdArgs {
   void* sv_dv;             // bf16 [N][RDT_LORA_LD] d(tau Ld^T)
   float* part_A;           // [waves][D] += g_full * h_prev
   float* part_B;           // [waves][D] += g_full * e
-  float* part_s;           // [waves][RDT_LORA_LD] = sum of dw * v (this loop)
 };
-void launch_tail_bwd(const TailBwdArgs& a, hipStream_t s);
+// Three passes: rows (g_full, tau, carry, de, dA / dB partials; dtau =
+// g_full), then after v = tau Ld^T and dw = g_full LB^T (products)
+// launch_lora_bwd, then after dtau += dv Ld (product) the gates pass (dY,
+// dz, bf16 dtau).  sv_wl, sv_dv and part_s are written by launch_lora_bwd.
+void launch_tail_bwd_rows(const TailBwdArgs& a, hipStream_t s);
+// dv = dw * scale, saved (tau Ld^T) * scale and dv ([N][RDT_LORA_LD] bf16),
+// dv_pad [N][64] bf16 (zero past r), part_s [waves][RDT_LORA_LD] += dw * v
+void launch_lora_bwd(int N, int r, const float* v, const float* dw, const float* scale, void* sv_wl, void* sv_dv,
+                     void* dv_pad, float* part_s, hipStream_t s);
+void launch_tail_bwd_gates(const TailBwdArgs& a, hipStream_t s);
 
 // dx1 += RMSNorm backward of f = RMSNorm(x1) g_ffn at df_total = df (null:
 // 0) + sum_j dfp[inv j] + sum_j dz_j Wr[sel_j]; dx1_bf = bf16(dx1);

@@ -83,44 +83,78 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __res
 }
 
 // ------------------------------------------------------------ weight gradients
-// 128 x 128 output tile per block (four waves of 64 x 64), 64 stacked rows
-// per step.  Each thread loads 4 rows x 8 columns of both operands, turns
-// them into 8 columns x 4 rows in registers and writes them to LDS as
-// [column][row] (rows contiguous), so the MFMA fragments (8 consecutive
-// rows of one column) are single 16-byte LDS reads.  The next step's global
-// loads are in flight while the current step computes.
+// Block tile 64 WF x 64 WF of the output (four waves in 2 x 2, each
+// 32 WF x 32 WF: WF x WF MFMA blocks), 64 stacked rows per step.  Each
+// thread loads 4 rows x 8 columns of each operand per 128 columns of the
+// tile, turns them into 8 columns x 4 rows in registers and writes them to
+// LDS as [column][row] (rows contiguous), so the MFMA fragments (8
+// consecutive rows of one column) are single 16-byte LDS reads.  The next
+// step's global loads are in flight while the current step computes.  With
+// WF = 4 each fragment feeds four MFMAs, which keeps the LDS reads under the
+// MFMA time; WF = 2 serves narrow products.
 constexpr int WG_LD = 72;   // 64 rows + 8 pad (bf16) per LDS column
 
-__device__ __forceinline__ void wg_store_t(bf16_t* s, const uint4* v, int rg, int cc) {
+__device__ __forceinline__ void wg_store_t(bf16_t* s, const uint4* v, int col0, int rg) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint2 u = {bf_elem(v[0], j) | (bf_elem(v[1], j) << 16), bf_elem(v[2], j) | (bf_elem(v[3], j) << 16)};
-    *(uint2*)&s[(8 * cc + j) * WG_LD + 4 * rg] = u;
+    *(uint2*)&s[(col0 + j) * WG_LD + 4 * rg] = u;
   }
 }
 
-__global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[128 * WG_LD];
-  __shared__ __attribute__((aligned(16))) bf16_t sX[128 * WG_LD];
-  const int tilesN = (a.Nc + 127) / 128;
-  const int tn = blockIdx.x % tilesN, tk = blockIdx.x / tilesN;
-  const int g = blockIdx.y, z = blockIdx.z;
-  const int n0 = tn * 128, k0 = tk * 128;
+template <int WF>
+__global__ __launch_bounds__(256, WF == 4 ? 1 : 2) void wgrad_kernel(WgradArgs a) {
+  constexpr int TILE = 64 * WF, NP = TILE / 128;
+  __shared__ __attribute__((aligned(16))) bf16_t sA[TILE * WG_LD];
+  __shared__ __attribute__((aligned(16))) bf16_t sX[TILE * WG_LD];
+  const int tilesN = (a.Nc + TILE - 1) / TILE, tilesK = (a.Kc + TILE - 1) / TILE, nt = tilesN * tilesK;
+  // blocks go to the XCDs round-robin by linear index; a single product
+  // gives each XCD a rectangle of tiles (its blocks share row slabs in its
+  // L2); grouped products take the tiles of one group after another
+  int g, tn, tk;
+  {
+    const int bid = blockIdx.x, xcd = bid % RDT_NUM_XCD, j = bid / RDT_NUM_XCD;
+    int px = 0;
+    if (a.G == 1 && nt % RDT_NUM_XCD == 0) {
+      if (tilesN % 4 == 0 && tilesK % 2 == 0) px = 4;
+      else if (tilesN % 2 == 0 && tilesK % 4 == 0) px = 2;
+      else if (tilesN % 8 == 0) px = 8;
+      else if (tilesK % 8 == 0) px = 1;
+    }
+    if (px) {
+      const int py = RDT_NUM_XCD / px, wn_ = tilesN / px, wk_ = tilesK / py;
+      g = 0;
+      tn = (xcd % px) * wn_ + j % wn_;
+      tk = (xcd / px) * wk_ + j / wn_;
+    } else {
+      g = bid / nt;
+      tn = (bid % nt) % tilesN;
+      tk = (bid % nt) / tilesN;
+    }
+  }
+  const int z = blockIdx.z;
+  const int n0 = tn * TILE, k0 = tk * TILE;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
   const int wn = w >> 1, wk = w & 1;
   const int rg = tid & 15, cc = tid >> 4;
-  const int na = a.Nc - (n0 + 8 * cc), nx = a.Kc - (k0 + 8 * cc);
-  const bf16_t* Ab = (const bf16_t*)a.A + n0 + 8 * cc;
-  const bf16_t* Xb = (const bf16_t*)a.X + k0 + 8 * cc;
-  floatx16_t acc[2][2];
+  floatx16_t acc[WF][WF];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WF; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WF; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   const int t_lo = (int)((int64_t)z * a.n_loops / a.splits), t_hi = (int)((int64_t)(z + 1) * a.n_loops / a.splits);
   // chunk iterator over (loop, 64-row step) of this group
+  // this group's row range in every loop, read once (a global read at each
+  // segment change would stall the load stream)
+  __shared__ int s_lo[RDT_MAX_WGRAD_LOOPS], s_hi[RDT_MAX_WGRAD_LOOPS];
+  for (int i = tid; i < t_hi - t_lo; i += blockDim.x) {
+    const int32_t* o = a.off ? a.off + (int64_t)(t_lo + i) * (a.G + 1) + g : nullptr;
+    s_lo[i] = o ? o[0] : 0;
+    s_hi[i] = o ? o[1] : a.rows;
+  }
+  __syncthreads();
   int t = t_lo - 1;
   int64_t m0 = 0, r1 = 0;
   auto advance = [&]() -> bool {
@@ -128,26 +162,35 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a) {
     while (m0 >= r1) {
       if (++t >= t_hi) return false;
       const int64_t base = (int64_t)t * a.loop_rows;
-      if (a.off) {
-        const int32_t* o = a.off + (int64_t)t * (a.G + 1) + g;
-        m0 = base + o[0];
-        r1 = base + o[1];
-      } else {
-        m0 = base;
-        r1 = base + a.rows;
-      }
+      m0 = base + s_lo[t - t_lo];
+      r1 = base + s_hi[t - t_lo];
     }
     return true;
   };
-  uint4 va[4], vx[4];
+  uint4 va[NP][4], vx[NP][4];
+  // tiles wholly inside the output take plain 16-byte loads
+  const bool full = n0 + TILE <= a.Nc && k0 + TILE <= a.Kc;
+  const bf16_t* Ab = (const bf16_t*)a.A + n0 + 8 * cc;
+  const bf16_t* Xb = (const bf16_t*)a.X + k0 + 8 * cc;
   auto load = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t m = m0 + 4 * rg + i;
       const bool ok = m < r1;
-      const int64_t xm = ok ? (a.xrow ? (int64_t)a.xrow[m] : m) : 0;
-      va[i] = load8(Ab + (ok ? m : 0) * a.lda, ok ? na : 0);
-      vx[i] = load8(Xb + xm * a.ldx, ok ? nx : 0);
+      const int64_t mm = ok ? m : r1 - 1;   // a row of the chunk; zeroed below when past its end
+      const bf16_t* ar = Ab + mm * a.lda;
+      const bf16_t* xr = Xb + (a.xrow ? (int64_t)a.xrow[mm] : mm) * a.ldx;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (full) {
+          va[p][i] = *(const uint4*)(ar + 128 * p);
+          vx[p][i] = *(const uint4*)(xr + 128 * p);
+        } else {
+          va[p][i] = load8(ar + 128 * p, a.Nc - (n0 + 8 * cc + 128 * p));
+          vx[p][i] = load8(xr + 128 * p, a.Kc - (k0 + 8 * cc + 128 * p));
+        }
+        if (!ok) va[p][i] = vx[p][i] = uint4{0u, 0u, 0u, 0u};
+      }
     }
   };
   m0 = -64;
@@ -155,36 +198,191 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a) {
   if (more) load();
   while (more) {
     __syncthreads();
-    wg_store_t(sA, va, rg, cc);
-    wg_store_t(sX, vx, rg, cc);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      wg_store_t(sA, va[p], 8 * cc + 128 * p, rg);
+      wg_store_t(sX, vx[p], 8 * cc + 128 * p, rg);
+    }
     __syncthreads();
     more = advance();
     if (more) load();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t af[2], xf[2];
+      bf16x8_t af[WF], xf[WF];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *(const bf16x8_t*)&sA[(wn * 64 + i * 32 + (lane & 31)) * WG_LD + 16 * ks + 8 * half];
+      for (int i = 0; i < WF; ++i)
+        af[i] = *(const bf16x8_t*)&sA[(wn * 32 * WF + i * 32 + (lane & 31)) * WG_LD + 16 * ks + 8 * half];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        xf[j] = *(const bf16x8_t*)&sX[(wk * 64 + j * 32 + (lane & 31)) * WG_LD + 16 * ks + 8 * half];
+      for (int j = 0; j < WF; ++j)
+        xf[j] = *(const bf16x8_t*)&sX[(wk * 32 * WF + j * 32 + (lane & 31)) * WG_LD + 16 * ks + 8 * half];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WF; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], xf[j], acc[i][j]);
+        for (int j = 0; j < WF; ++j) acc[i][j] = mfma32(af[i], xf[j], acc[i][j]);
+      // one k-step's fragments live at a time (the 4 x 4 accumulators fill
+      // the AGPRs)
+      if constexpr (WF == 4) __builtin_amdgcn_sched_barrier(0);
     }
   }
   float* Cb = a.C + (int64_t)g * a.c_gstride + (int64_t)z * a.c_split_stride;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WF; ++i)
+#pragma unroll
+    for (int j = 0; j < WF; ++j) {
+      const int k = k0 + wk * 32 * WF + j * 32 + (lane & 31);
+      if (k >= a.Kc) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = n0 + wn * 32 * WF + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (n < a.Nc) {
+          float* p = Cb + (int64_t)n * a.ldc + k;
+          *p = a.accumulate ? *p + acc[i][j][r] : acc[i][j][r];
+        }
+      }
+    }
+}
+
+// Large products: 256 x 256 output tile, eight waves (2 along n x 4 along
+// k, each 128 x 64: 4 x 2 MFMA blocks), two per SIMD.  LDS is
+// double-buffered: step i computes from one buffer while the rows of step
+// i + 1 (already in registers) are transposed into the other and those of
+// step i + 2 are loaded from memory, with one barrier per step; the
+// transposition's VALU and LDS writes run under the MFMAs queued before it.
+__global__ __launch_bounds__(512, 1) void wgrad8_kernel(WgradArgs a) {
+  constexpr int TILE = 256;
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][TILE * WG_LD];
+  __shared__ __attribute__((aligned(16))) bf16_t sX[2][TILE * WG_LD];
+  const int tilesN = (a.Nc + TILE - 1) / TILE, tilesK = (a.Kc + TILE - 1) / TILE, nt = tilesN * tilesK;
+  int g, tn, tk;
+  {
+    const int bid = blockIdx.x, xcd = bid % RDT_NUM_XCD, j = bid / RDT_NUM_XCD;
+    int px = 0;
+    if (a.G == 1 && nt % RDT_NUM_XCD == 0) {
+      if (tilesN % 4 == 0 && tilesK % 2 == 0) px = 4;
+      else if (tilesN % 2 == 0 && tilesK % 4 == 0) px = 2;
+      else if (tilesN % 8 == 0) px = 8;
+      else if (tilesK % 8 == 0) px = 1;
+    }
+    if (px) {
+      const int py = RDT_NUM_XCD / px, wn_ = tilesN / px, wk_ = tilesK / py;
+      g = 0;
+      tn = (xcd % px) * wn_ + j % wn_;
+      tk = (xcd / px) * wk_ + j / wn_;
+    } else {
+      g = bid / nt;
+      tn = (bid % nt) % tilesN;
+      tk = (bid % nt) / tilesN;
+    }
+  }
+  const int z = blockIdx.z;
+  const int n0 = tn * TILE, k0 = tk * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
+  const int wn = w >> 2, wk = w & 3;
+  const int rg = tid & 15, cc = tid >> 4;   // rows 4 rg .. +3, columns 8 cc .. +7
+  floatx16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int t_lo = (int)((int64_t)z * a.n_loops / a.splits), t_hi = (int)((int64_t)(z + 1) * a.n_loops / a.splits);
+  __shared__ int s_lo[RDT_MAX_WGRAD_LOOPS], s_hi[RDT_MAX_WGRAD_LOOPS];
+  for (int i = tid; i < t_hi - t_lo; i += blockDim.x) {
+    const int32_t* o = a.off ? a.off + (int64_t)(t_lo + i) * (a.G + 1) + g : nullptr;
+    s_lo[i] = o ? o[0] : 0;
+    s_hi[i] = o ? o[1] : a.rows;
+  }
+  __syncthreads();
+  int t = t_lo - 1;
+  int64_t m0 = -64, r1 = 0;
+  auto advance = [&]() -> bool {
+    m0 += 64;
+    while (m0 >= r1) {
+      if (++t >= t_hi) return false;
+      const int64_t base = (int64_t)t * a.loop_rows;
+      m0 = base + s_lo[t - t_lo];
+      r1 = base + s_hi[t - t_lo];
+    }
+    return true;
+  };
+  const bool full = n0 + TILE <= a.Nc && k0 + TILE <= a.Kc;
+  const bf16_t* Ab = (const bf16_t*)a.A + n0 + 8 * cc;
+  const bf16_t* Xb = (const bf16_t*)a.X + k0 + 8 * cc;
+  const int na = a.Nc - (n0 + 8 * cc), nx = a.Kc - (k0 + 8 * cc);
+  uint4 va[4], vx[4];
+  auto load = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + 4 * rg + i;
+      const bool ok = m < r1;
+      const int64_t mm = ok ? m : r1 - 1;
+      const bf16_t* ar = Ab + mm * a.lda;
+      const bf16_t* xr = Xb + (a.xrow ? (int64_t)a.xrow[mm] : mm) * a.ldx;
+      if (full) {
+        va[i] = *(const uint4*)ar;
+        vx[i] = *(const uint4*)xr;
+      } else {
+        va[i] = load8(ar, na);
+        vx[i] = load8(xr, nx);
+      }
+      if (!ok) va[i] = vx[i] = uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  bool have = advance();
+  if (have) {
+    load();
+    wg_store_t(sA[0], va, 8 * cc, rg);
+    wg_store_t(sX[0], vx, 8 * cc, rg);
+  }
+  bool more = have && advance();
+  if (more) load();
+  __syncthreads();
+  int cur = 0;
+  while (have) {
+    bool more2 = false;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t af[4], xf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *(const bf16x8_t*)&sA[cur][(wn * 128 + i * 32 + (lane & 31)) * WG_LD + 16 * ks + 8 * half];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        xf[j] = *(const bf16x8_t*)&sX[cur][(wk * 64 + j * 32 + (lane & 31)) * WG_LD + 16 * ks + 8 * half];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], xf[j], acc[i][j]);
+      if (ks == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+          wg_store_t(sA[cur ^ 1], va, 8 * cc, rg);
+          wg_store_t(sX[cur ^ 1], vx, 8 * cc, rg);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (ks == 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        more2 = more && advance();
+        if (more2) load();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    have = more;
+    more = more2;
+    cur ^= 1;
+  }
+  float* Cb = a.C + (int64_t)g * a.c_gstride + (int64_t)z * a.c_split_stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int k = k0 + wk * 64 + j * 32 + (lane & 31);
       if (k >= a.Kc) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int n = n0 + wn * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int n = n0 + wn * 128 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         if (n < a.Nc) {
           float* p = Cb + (int64_t)n * a.ldc + k;
           *p = a.accumulate ? *p + acc[i][j][r] : acc[i][j][r];
@@ -194,8 +392,8 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a) {
 }
 
 // dWr[e][c]: one block per (expert, 256 columns), loops and rows in order
-__global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dz, const bf16_t* __restrict__ f,
-                                                           const int32_t* __restrict__ gidx,
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dz,
+                                                           const bf16_t* __restrict__ fperm,
                                                            const int32_t* __restrict__ off, int n_loops, int NK,
                                                            int E, int D, float* __restrict__ dWr) {
   const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
@@ -205,10 +403,21 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restri
     const int32_t* o = off + (int64_t)t * (E + 1);
     for (int m = o[e]; m < o[e + 1]; ++m) {
       const int64_t row = (int64_t)t * NK + m;
-      acc = fmaf(dz[row], bf2f(f[(int64_t)gidx[row] * D + c]), acc);
+      acc = fmaf(dz[row], bf2f(fperm[row * D + c]), acc);
     }
   }
   dWr[(int64_t)e * D + c] = acc;
+}
+
+// dst[m] = src[perm[m]] (bf16 rows of D)
+__global__ __launch_bounds__(256) void gather_rows_kernel(const bf16_t* __restrict__ src,
+                                                          const int32_t* __restrict__ perm, int M, int D,
+                                                          bf16_t* __restrict__ dst) {
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (idx >= (int64_t)M * D) return;
+  const int64_t m = idx / D;
+  const int c = (int)(idx - m * D);
+  *(uint4*)(dst + idx) = *(const uint4*)(src + (int64_t)perm[m] * D + c);
 }
 
 // ------------------------------------------------------------ attention backward
@@ -600,81 +809,92 @@ __global__ __launch_bounds__(256) void act_prep_kernel(const float* __restrict__
   ROW_LOOP_END
 }
 
-__global__ __launch_bounds__(256) void tail_bwd_kernel(TailBwdArgs a) {
-  const int N = a.N, D = a.D, k = a.k, r = a.r;
+// Tail backward, first pass (no reductions): the state gradient with this
+// loop's ACT terms, g_full = g + w dy + z halt_w; tau recomputed from its
+// parts; dtau = g_full (the LoRA term is added by a product afterwards);
+// the carry A g_full, de += B g_full and the partial sums of g_full h_prev
+// (dA) and g_full e (dB).
+__global__ __launch_bounds__(256) void tail_bwd_rows_kernel(TailBwdArgs a) {
+  const int N = a.N, D = a.D, k = a.k;
   ROW_LOOP_BEGIN
   const int64_t ro = (int64_t)n * D;
   const float wa = a.w_act ? a.w_act[n] : 0.f, za = a.z_act ? a.z_act[n] : 0.f;
   const bf16_t* yb = (const bf16_t*)a.y;
   const bf16_t* ysb = (const bf16_t*)a.ys;
-  const bf16_t* Ld = (const bf16_t*)a.lora_down;
-  const bf16_t* LB = (const bf16_t*)a.lora_B;
   int rows_j[8];
   float gates[8];
   for (int j = 0; j < k; ++j) {
     rows_j[j] = a.inv[(int64_t)n * k + j];
     gates[j] = a.gate[(int64_t)n * k + j];
   }
-  auto g_full = [&](int c) {
+  float* pA = a.part_A + (int64_t)wg * D;
+  float* pB = a.part_B + (int64_t)wg * D;
+  for (int c = 4 * lane; c < D; c += 256) {
     float4 gf = ld4(a.g + ro + c);
     if (a.w_act) gf = fma4(wa, ld4(a.dy + ro + c), gf);
     if (a.z_act) gf = fma4(za, ld4(a.halt_w + c), gf);
-    return gf;
-  };
-  auto tau_at = [&](int c) {
     float4 tv = ld4(a.x1 + ro + c);
     for (int j = 0; j < k; ++j) tv = fma4(gates[j], ldbf4(yb + (int64_t)rows_j[j] * D + c), tv);
     for (int s2 = 0; s2 < a.S; ++s2) tv = add4(tv, ldbf4(ysb + ((int64_t)s2 * N + n) * D + c));
-    return tv;
-  };
-  // pass 1: v = tau Ld^T and dw = g_full LB^T (r values each)
-  float vv[RDT_LORA_LD], dw[RDT_LORA_LD];
-  for (int i = 0; i < r; ++i) vv[i] = dw[i] = 0.f;
-  for (int c = 4 * lane; c < D; c += 256) {
-    const float4 tv = tau_at(c), gf = g_full(c);
-    for (int i = 0; i < r; ++i) {
-      vv[i] += dot4(tv, ldbf4(Ld + (int64_t)i * D + c));
-      dw[i] += dot4(gf, ldbf4(LB + (int64_t)i * D + c));
-    }
-  }
-  float dv[RDT_LORA_LD];
-  float* ps = a.part_s + (int64_t)wg * RDT_LORA_LD;
-  for (int i = 0; i < r; ++i) {
-    vv[i] = wave_sum(vv[i]);
-    dw[i] = wave_sum(dw[i]);
-    dv[i] = dw[i] * a.scale_row[i];
-    if (lane == 0) {
-      ps[i] += dw[i] * vv[i];
-      ((bf16_t*)a.sv_wl)[(int64_t)n * RDT_LORA_LD + i] = f2bf(vv[i] * a.scale_row[i]);
-      ((bf16_t*)a.sv_dv)[(int64_t)n * RDT_LORA_LD + i] = f2bf(dv[i]);
-    }
-  }
-  // pass 2: dtau = g_full + dv Ld; outputs
-  float dg[8];
-  for (int j = 0; j < k; ++j) dg[j] = 0.f;
-  for (int c = 4 * lane; c < D; c += 256) {
-    const float4 gf = g_full(c), tv = tau_at(c);
-    float4 dt = gf;
-    for (int i = 0; i < r; ++i) dt = fma4(dv[i], ldbf4(Ld + (int64_t)i * D + c), dt);
-    for (int j = 0; j < k; ++j) {
-      const float4 yv = ldbf4(yb + (int64_t)rows_j[j] * D + c);
-      dg[j] += dot4(dt, yv);
-      stbf4((bf16_t*)a.dY + (int64_t)rows_j[j] * D + c, scl4(gates[j], dt));
-    }
-    st4(a.dtau + ro + c, dt);
-    stbf4((bf16_t*)a.dtau_bf + ro + c, dt);
     stbf4((bf16_t*)a.sv_g + ro + c, gf);
     stbf4((bf16_t*)a.sv_tau + ro + c, tv);
-    const float4 Av = ld4(a.A + c), Bv = ld4(a.Bv + c), hp = ld4(a.h_prev + ro + c), ev = ld4(a.e + ro + c);
-    st4(a.de + ro + c, fma4(1.f, mul4(Bv, gf), ld4(a.de + ro + c)));
-    float* pA = a.part_A + (int64_t)wg * D + c;
-    float* pB = a.part_B + (int64_t)wg * D + c;
-    st4(pA, add4(ld4(pA), mul4(gf, hp)));
-    st4(pB, add4(ld4(pB), mul4(gf, ev)));
-    st4(a.g_next + ro + c, mul4(Av, gf));
+    st4(a.dtau + ro + c, gf);
+    const float4 hp = ld4(a.h_prev + ro + c), ev = ld4(a.e + ro + c);
+    st4(a.de + ro + c, add4(ld4(a.de + ro + c), mul4(ld4(a.Bv + c), gf)));
+    st4(pA + c, add4(ld4(pA + c), mul4(gf, hp)));
+    st4(pB + c, add4(ld4(pB + c), mul4(gf, ev)));
+    st4(a.g_next + ro + c, mul4(ld4(a.A + c), gf));
   }
-  // router: the gates are the softmax of the chosen logits, so
-  // d z_j = gate_j (dgate_j - sum_i gate_i dgate_i) and 0 elsewhere
+  ROW_LOOP_END
+}
+
+// LoRA backward per row from v = tau Ld^T and dw = g_full LB^T ([N][r]
+// fp32): dv = dw * scale (saved, and zero-padded to 64 columns for the
+// product dtau += dv Ld), the saved (tau Ld^T) * scale, and the partial
+// sums of dw * v (d scale of this loop)
+__global__ __launch_bounds__(256) void lora_bwd_kernel(int N, int r, const float* __restrict__ v,
+                                                       const float* __restrict__ dw,
+                                                       const float* __restrict__ scale, bf16_t* __restrict__ sv_wl,
+                                                       bf16_t* __restrict__ sv_dv, bf16_t* __restrict__ dv_pad,
+                                                       float* __restrict__ part_s) {
+  ROW_LOOP_BEGIN
+  const int i = lane;
+  const bool in = i < r;
+  const float vi = in ? v[(int64_t)n * r + i] : 0.f, dwi = in ? dw[(int64_t)n * r + i] : 0.f;
+  const float si = in ? scale[i] : 0.f, dvi = dwi * si;
+  if (i < RDT_LORA_LD) {
+    sv_wl[(int64_t)n * RDT_LORA_LD + i] = f2bf(vi * si);
+    sv_dv[(int64_t)n * RDT_LORA_LD + i] = f2bf(dvi);
+  }
+  dv_pad[(int64_t)n * 64 + i] = f2bf(dvi);
+  if (in) part_s[(int64_t)wg * RDT_LORA_LD + i] += dwi * vi;
+  ROW_LOOP_END
+}
+
+// Tail backward, last pass: with dtau complete, the gate gradients
+// dgate_j = <dtau, y_j>, the routed outputs' gradient dY[inv j] = gate_j
+// dtau, bf16 dtau, and the router: the gates are the softmax of the chosen
+// logits, so d z_j = gate_j (dgate_j - sum_i gate_i dgate_i), 0 elsewhere.
+__global__ __launch_bounds__(256) void tail_bwd_gates_kernel(TailBwdArgs a) {
+  const int N = a.N, D = a.D, k = a.k;
+  ROW_LOOP_BEGIN
+  const int64_t ro = (int64_t)n * D;
+  const bf16_t* yb = (const bf16_t*)a.y;
+  int rows_j[8];
+  float gates[8], dg[8];
+  for (int j = 0; j < k; ++j) {
+    rows_j[j] = a.inv[(int64_t)n * k + j];
+    gates[j] = a.gate[(int64_t)n * k + j];
+    dg[j] = 0.f;
+  }
+  for (int c = 4 * lane; c < D; c += 256) {
+    const float4 dt = ld4(a.dtau + ro + c);
+    for (int j = 0; j < k; ++j) {
+      dg[j] += dot4(dt, ldbf4(yb + (int64_t)rows_j[j] * D + c));
+      stbf4((bf16_t*)a.dY + (int64_t)rows_j[j] * D + c, scl4(gates[j], dt));
+    }
+    stbf4((bf16_t*)a.dtau_bf + ro + c, dt);
+  }
   float gd = 0.f;
   for (int j = 0; j < k; ++j) {
     dg[j] = wave_sum(dg[j]);
@@ -795,13 +1015,29 @@ __global__ __launch_bounds__(256) void loop_index_kernel(const int32_t* __restri
   if (blockIdx.x == 0 && threadIdx.x < E) load[threadIdx.x] += off[threadIdx.x + 1] - off[threadIdx.x];
 }
 
+// CW columns per block (64, or fewer for narrow sums); the 256 / CW row
+// slices of each column are summed by their threads, then added in a
+// fixed order
 __global__ __launch_bounds__(256) void col_reduce_kernel(const float* __restrict__ part, int rows, int64_t ld, int len,
-                                                         float* __restrict__ out, int accumulate) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= len) return;
-  float s = 0.f;
-  for (int w = 0; w < rows; ++w) s += part[(int64_t)w * ld + c];
-  out[c] = accumulate ? out[c] + s : s;
+                                                         float* __restrict__ out, int accumulate, int CW) {
+  __shared__ float red[256];
+  const int cl = threadIdx.x % CW, rs = threadIdx.x / CW, RS = 256 / CW, c = blockIdx.x * CW + cl;
+  float s0 = 0.f, s1 = 0.f;
+  if (c < len) {
+    int w = rs;
+    for (; w + RS < rows; w += 2 * RS) {
+      s0 += part[(int64_t)w * ld + c];
+      s1 += part[(int64_t)(w + RS) * ld + c];
+    }
+    if (w < rows) s0 += part[(int64_t)w * ld + c];
+  }
+  red[threadIdx.x] = s0 + s1;
+  __syncthreads();
+  if (rs == 0 && c < len) {
+    float t = 0.f;
+    for (int i = 0; i < RS; ++i) t += red[i * CW + cl];
+    out[c] = accumulate ? out[c] + t : t;
+  }
 }
 
 __global__ __launch_bounds__(256) void lti_param_grad_kernel(const float* __restrict__ dA, const float* __restrict__ A,
@@ -850,14 +1086,24 @@ void launch_transpose_bf16(const void* in, int64_t isb1, int64_t isb2, int nb2, 
 }
 
 void launch_wgrad(const WgradArgs& a, hipStream_t s) {
-  const dim3 grid(((a.Nc + 127) / 128) * ((a.Kc + 127) / 128), a.G, a.splits);
-  wgrad_kernel<<<grid, 256, 0, s>>>(a);
+  // 256-wide tiles unless the product is narrow (LoRA rank, small shapes)
+  if (a.Nc >= 256 && a.Kc >= 256) {
+    const dim3 grid(((a.Nc + 255) / 256) * ((a.Kc + 255) / 256) * a.G, 1, a.splits);
+    wgrad8_kernel<<<grid, 512, 0, s>>>(a);
+  } else {
+    const dim3 grid(((a.Nc + 127) / 128) * ((a.Kc + 127) / 128) * a.G, 1, a.splits);
+    wgrad_kernel<2><<<grid, 256, 0, s>>>(a);
+  }
 }
 
-void launch_router_wgrad(const float* dz, const void* f, const int32_t* gidx, const int32_t* off, int n_loops,
-                         int NK, int E, int D, float* dWr, hipStream_t s) {
-  router_wgrad_kernel<<<dim3((D + 255) / 256, E), 256, 0, s>>>(dz, (const bf16_t*)f, gidx, off, n_loops, NK, E, D,
-                                                                dWr);
+void launch_router_wgrad(const float* dz, const void* fperm, const int32_t* off, int n_loops, int NK, int E, int D,
+                         float* dWr, hipStream_t s) {
+  router_wgrad_kernel<<<dim3((D + 255) / 256, E), 256, 0, s>>>(dz, (const bf16_t*)fperm, off, n_loops, NK, E, D, dWr);
+}
+
+void launch_gather_rows_bf16(const void* src, const int32_t* perm, int M, int D, void* dst, hipStream_t s) {
+  const int64_t n = (int64_t)M * D / 8;
+  gather_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const bf16_t*)src, perm, M, D, (bf16_t*)dst);
 }
 
 void launch_attn_bwd_prep(const void* o, const void* dO, int N, int H, int T, float* Dq, hipStream_t s) {
@@ -900,7 +1146,19 @@ void launch_act_prep(const float* states, const float* dy, const float* halt_w, 
                                                  part_hw, part_hb);
 }
 
-void launch_tail_bwd(const TailBwdArgs& a, hipStream_t s) { tail_bwd_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(a); }
+void launch_tail_bwd_rows(const TailBwdArgs& a, hipStream_t s) {
+  tail_bwd_rows_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(a);
+}
+
+void launch_lora_bwd(int N, int r, const float* v, const float* dw, const float* scale, void* sv_wl, void* sv_dv,
+                     void* dv_pad, float* part_s, hipStream_t s) {
+  lora_bwd_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, r, v, dw, scale, (bf16_t*)sv_wl, (bf16_t*)sv_dv, (bf16_t*)dv_pad,
+                                                 part_s);
+}
+
+void launch_tail_bwd_gates(const TailBwdArgs& a, hipStream_t s) {
+  tail_bwd_gates_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(a);
+}
 
 void launch_ffn_norm_bwd(int N, int D, int k, float eps, const float* df, const float* dfp, const int32_t* inv,
                          const int32_t* sel, const float* dz, const void* Wr, const float* x1, const float* g_ffn,
@@ -922,7 +1180,8 @@ void launch_loop_index(const int32_t* perm, const int32_t* off, int t, int NK, i
 }
 
 void launch_col_reduce(const float* part, int rows, int64_t ld, int len, float* out, int accumulate, hipStream_t s) {
-  col_reduce_kernel<<<(len + 255) / 256, 256, 0, s>>>(part, rows, ld, len, out, accumulate);
+  const int CW = len >= 64 ? 64 : len >= 16 ? 16 : 4;
+  col_reduce_kernel<<<(len + CW - 1) / CW, 256, 0, s>>>(part, rows, ld, len, out, accumulate, CW);
 }
 
 void launch_lti_param_grad(const float* dA, const float* A, const float* log_A, const float* log_dt, int D,

@@ -1584,15 +1584,15 @@ namespace {
 
 enum BwId {
   // per loop, stacked over the loops: operands of the weight-gradient products
-  SV_A, SV_DQKV, SV_O, SV_DX1, SV_F, SV_GIDX, SV_OFF, SV_DZP, SV_DGU, SV_ACT, SV_DY, SV_ACTS, SV_DGUS, SV_DTAU,
+  SV_A, SV_DQKV, SV_O, SV_DX1, SV_F, SV_FPERM, SV_GIDX, SV_OFF, SV_DZP, SV_DGU, SV_ACT, SV_DY, SV_ACTS, SV_DGUS, SV_DTAU,
   SV_G, SV_TAU, SV_WL, SV_DV,
   // working buffers of one loop
   BW_G, BW_DX1, BW_DF, BW_DA, BW_DZ, BW_GU, BW_DACT, BW_DFP, BW_GUS, BW_DACTS, BW_DO, BW_LSE, BW_DELTA, BW_QT,
-  BW_DOT, BW_KT, BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC,
+  BW_DOT, BW_KT, BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD,
   // per-wave partial column sums (contiguous: cleared together)
   BP_A, BP_B, BP_GF, BP_GA, BP_GR, BP_HW, BP_HB, BP_S,
   // transposed weights
-  TW_WO, TW_WQKV, TW_WD, TW_WGU, TW_WSD, TW_WSGU,
+  TW_WO, TW_WQKV, TW_WD, TW_WGU, TW_WSD, TW_WSGU, TW_LDT,
   BW_COUNT
 };
 
@@ -1613,6 +1613,7 @@ BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   s[SV_O] = Ls * N * HD * 2;
   s[SV_DX1] = Ls * N * D * 2;
   s[SV_F] = Ls * N * D * 2;
+  s[SV_FPERM] = Ls * NK * D * 2;
   s[SV_GIDX] = Ls * NK * 4;
   s[SV_OFF] = Ls * (E + 1) * 4;
   s[SV_DZP] = Ls * NK * 4;
@@ -1642,6 +1643,8 @@ BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   s[BW_WACT] = s[BW_ZACT] = Ls * N * 4;
   s[BW_SPLIT] = Ls * r * D * 4;
   s[BW_DAVEC] = D * 4;
+  s[BW_LV] = s[BW_LDW] = N * r * 4;
+  s[BW_DVPAD] = N * 64 * 2;
   s[BP_A] = s[BP_B] = s[BP_GF] = s[BP_GA] = s[BP_GR] = s[BP_HW] = W * D * 4;
   s[BP_HB] = W * 4;
   s[BP_S] = Ls * W * RDT_LORA_LD * 4;
@@ -1651,6 +1654,7 @@ BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   s[TW_WGU] = E * D * 2 * F * 2;
   s[TW_WSD] = S * F * D * 2;
   s[TW_WSGU] = S * D * 2 * F * 2;
+  s[TW_LDT] = D * 64 * 2;
   size_t o = align256(q.fwd.total);
   for (int i = 0; i < BW_COUNT; ++i) {
     q.off[i] = o;
@@ -1805,6 +1809,7 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   {
     const bf16_t* wqkv = (const bf16_t*)b->wqkv;
     launch_transpose_bf16(b->wo, 0, 0, 1, HD, Q(TW_WO), 0, D, 1, D, D, HD, HD, s);              // [HD][D]
+    launch_transpose_bf16(b->lora_down, 0, 0, 1, D, Q(TW_LDT), 0, 64, 1, r, 64, D, D, s);        // [D][64], 0 past r
     launch_transpose_bf16(wqkv, 0, 0, 1, D, Q(TW_WQKV), 0, QKV, 1, QKV, QKV, D, D, s);          // [D][QKV]
     launch_transpose_bf16(b->w_down, (int64_t)D * F, 0, 1, F, Q(TW_WD), (int64_t)F * D, D, E, D, D, F, F, s);
     launch_transpose_bf16(b->w_gate, (int64_t)F * D, 0, 1, D, Q(TW_WGU), (int64_t)D * 2 * F, 2 * F, E, F, F, D, D, s);
@@ -1906,6 +1911,7 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
     HIP_TRY(hipMemcpyAsync(QB(SV_A) + (size_t)t * NDs, W(WS_A), NDs * 2, hipMemcpyDeviceToDevice, s));
     HIP_TRY(hipMemcpyAsync(QB(SV_O) + (size_t)t * N * HD, W(WS_O), (size_t)N * HD * 2, hipMemcpyDeviceToDevice, s));
     HIP_TRY(hipMemcpyAsync(QB(SV_F) + (size_t)t * NDs, W(WS_F), NDs * 2, hipMemcpyDeviceToDevice, s));
+    launch_gather_rows_bf16(W(WS_F), WI(WS_PERM), NK, D, QB(SV_FPERM) + (size_t)t * NK * D, s);
 
     // ---- backward of loop t
     {
@@ -1945,8 +1951,24 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
       ta.sv_dv = QB(SV_DV) + (size_t)t * N * RDT_LORA_LD;
       ta.part_A = QF(BP_A);
       ta.part_B = QF(BP_B);
-      ta.part_s = QF(BP_S) + (size_t)t * RDT_BWD_WAVES * RDT_LORA_LD;
-      launch_tail_bwd(ta, s);
+      launch_tail_bwd_rows(ta, s);
+      // LoRA: v = tau Ld^T, dw = g_full LB^T; dtau += (dw * scale) Ld
+      GemmParams l1 = dense_params(ta.sv_tau, D, b->lora_down, nullptr, N, r, D);
+      l1.epi.out = QF(BW_LV);
+      l1.epi.ldo = r;
+      x.gemm(l1, EPI_STORE, false, 0, true);
+      GemmParams l2 = dense_params(ta.sv_g, D, b->lora_B, nullptr, N, r, D);
+      l2.epi.out = QF(BW_LDW);
+      l2.epi.ldo = r;
+      x.gemm(l2, EPI_STORE, false, 0, true);
+      launch_lora_bwd(N, r, QF(BW_LV), QF(BW_LDW), ta.scale_row, ta.sv_wl, ta.sv_dv, Q(BW_DVPAD),
+                      QF(BP_S) + (size_t)t * RDT_BWD_WAVES * RDT_LORA_LD, s);
+      GemmParams l3 = dense_params(Q(BW_DVPAD), 64, Q(TW_LDT), nullptr, N, D, 64);
+      l3.epi.out = QF(BW_DX1);
+      l3.epi.ldo = D;
+      l3.epi.resid = QF(BW_DX1);
+      x.gemm(l3, EPI_RESID, false, 0);
+      launch_tail_bwd_gates(ta, s);
     }
     // shared experts: d act_s = dtau Wsd, SwiGLU backward, df (+)= dGU_s [Wsg; Wsu]
     for (int si = 0; si < S; ++si) {
@@ -2035,10 +2057,10 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   float* gb = grad;
   wgrad(Q(SV_DQKV), QKV, Q(SV_A), D, nullptr, nullptr, N, N, 1, QKV, D, gb + goff[RDT_W_WQ], D, 0, 1, 0);
   wgrad(Q(SV_DX1), D, Q(SV_O), HD, nullptr, nullptr, N, N, 1, D, HD, gb + goff[RDT_W_WO], HD, 0, 1, 0);
-  launch_router_wgrad(QF(SV_DZP), Q(SV_F), QI(SV_GIDX), QI(SV_OFF), L, NK, E, D, gb + goff[RDT_W_ROUTER], s);
-  wgrad(Q(SV_DGU), 2 * F, Q(SV_F), D, QI(SV_GIDX), QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_GATE], D,
+  launch_router_wgrad(QF(SV_DZP), Q(SV_FPERM), QI(SV_OFF), L, NK, E, D, gb + goff[RDT_W_ROUTER], s);
+  wgrad(Q(SV_DGU), 2 * F, Q(SV_FPERM), D, nullptr, QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_GATE], D,
         (int64_t)F * D, 1, 0);
-  wgrad(QB(SV_DGU) + F, 2 * F, Q(SV_F), D, QI(SV_GIDX), QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_UP], D,
+  wgrad(QB(SV_DGU) + F, 2 * F, Q(SV_FPERM), D, nullptr, QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_UP], D,
         (int64_t)F * D, 1, 0);
   wgrad(Q(SV_DY), D, Q(SV_ACT), F, nullptr, QI(SV_OFF), NK, 0, E, D, F, gb + goff[RDT_W_DOWN], F, (int64_t)D * F, 1,
         0);
