@@ -49,9 +49,11 @@ struct WgradArgs {
 void launch_wgrad(const WgradArgs& a, hipStream_t s);
 
 // dWr[e][c] = sum over loops t and dispatch rows m of expert e of
-// dz[t][m] * fperm[t][m][c]   (f in dispatch order, bf16, stacked over loops)
+// dz[t][m] * fperm[t][m][c]   (f in dispatch order, bf16, stacked over loops);
+// part: fp32 scratch of 16 E D floats (row-slice partial sums)
+#define RDT_ROUTER_WGRAD_PART(E, D) ((size_t)16 * (E) * (D))
 void launch_router_wgrad(const float* dz, const void* fperm, const int32_t* off, int n_loops, int NK, int E, int D,
-                         float* dWr, hipStream_t s);
+                         float* part, float* dWr, hipStream_t s);
 // dst[m] = src[perm[m]] for m < M (bf16 rows of D, D a multiple of 8)
 void launch_gather_rows_bf16(const void* src, const int32_t* perm, int M, int D, void* dst, hipStream_t s);
 

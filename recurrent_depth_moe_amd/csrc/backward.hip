@@ -61,15 +61,39 @@ __device__ __forceinline__ float4 mul4(float4 a, float4 b) { return float4{a.x *
 __device__ __forceinline__ float4 scl4(float s, float4 a) { return float4{s * a.x, s * a.y, s * a.z, s * a.w}; }
 
 // ------------------------------------------------------------ transpose
+// 64 x 64 tile per block; 16-byte global reads and writes where the tile
+// lies inside the matrix and the strides allow, element-wise at the edges
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ in, int64_t isb1,
                                                              int64_t isb2, int nb2, int64_t ldi,
                                                              bf16_t* __restrict__ out, int64_t osb, int64_t ldo,
-                                                             int R, int Rp, int C, int Cv) {
-  __shared__ bf16_t tile[64][66];
+                                                             int R, int Rp, int C, int Cv, int vec) {
+  __shared__ bf16_t tile[64][72];
   const int bi = blockIdx.z, b1 = bi / nb2, b2 = bi - b1 * nb2;
   const bf16_t* src = in + b1 * isb1 + b2 * isb2;
   bf16_t* dst = out + bi * osb;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const bool inside = vec && r0 + 64 <= R && c0 + 64 <= Cv && c0 + 64 <= C && r0 + 64 <= Rp;
+  if (inside) {
+    // thread: row i = tid / 8 (+ 32), columns 8 (tid % 8) .. +7
+    const int i = threadIdx.x >> 3, cc = (threadIdx.x & 7) * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 v = *(const uint4*)(src + (int64_t)(r0 + i + 32 * h) * ldi + c0 + cc);
+      *(uint4*)&tile[i + 32 * h][cc] = v;
+    }
+    __syncthreads();
+    // thread: output row (column c0 + i), rows r0 + rr .. +7 of the input
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = i + 32 * h;
+      uint32_t w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        w[x] = (uint32_t)tile[cc + 2 * x][c] | ((uint32_t)tile[cc + 2 * x + 1][c] << 16);
+      *(uint4*)(dst + (int64_t)(c0 + c) * ldo + r0 + cc) = uint4{w[0], w[1], w[2], w[3]};
+    }
+    return;
+  }
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int i = ty; i < 64; i += 4) {
     const int r = r0 + i, c = c0 + tx;
@@ -391,22 +415,32 @@ __global__ __launch_bounds__(512, 1) void wgrad8_kernel(WgradArgs a) {
     }
 }
 
-// dWr[e][c]: one block per (expert, 256 columns), loops and rows in order
+// dWr[e][c] partial sums: block (256 columns, expert e, row slice z) takes
+// rows z, z + RW_SLICES, ... of each loop's rows of e; the slices are added
+// afterwards in order
+#define RW_SLICES 16
 __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dz,
                                                            const bf16_t* __restrict__ fperm,
                                                            const int32_t* __restrict__ off, int n_loops, int NK,
-                                                           int E, int D, float* __restrict__ dWr) {
-  const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+                                                           int E, int D, float* __restrict__ part) {
+  const int e = blockIdx.y, z = blockIdx.z, c = blockIdx.x * 256 + threadIdx.x;
   if (c >= D) return;
-  float acc = 0.f;
+  float acc0 = 0.f, acc1 = 0.f;
   for (int t = 0; t < n_loops; ++t) {
     const int32_t* o = off + (int64_t)t * (E + 1);
-    for (int m = o[e]; m < o[e + 1]; ++m) {
+    const int m1 = o[e + 1];
+    int m = o[e] + z;
+    for (; m + RW_SLICES < m1; m += 2 * RW_SLICES) {
       const int64_t row = (int64_t)t * NK + m;
-      acc = fmaf(dz[row], bf2f(fperm[row * D + c]), acc);
+      acc0 = fmaf(dz[row], bf2f(fperm[row * D + c]), acc0);
+      acc1 = fmaf(dz[row + RW_SLICES], bf2f(fperm[(row + RW_SLICES) * D + c]), acc1);
+    }
+    if (m < m1) {
+      const int64_t row = (int64_t)t * NK + m;
+      acc0 = fmaf(dz[row], bf2f(fperm[row * D + c]), acc0);
     }
   }
-  dWr[(int64_t)e * D + c] = acc;
+  part[((int64_t)z * E + e) * D + c] = acc0 + acc1;
 }
 
 // dst[m] = src[perm[m]] (bf16 rows of D)
@@ -1081,8 +1115,11 @@ __global__ __launch_bounds__(256) void router_bias_update_kernel(float* __restri
 void launch_transpose_bf16(const void* in, int64_t isb1, int64_t isb2, int nb2, int64_t ldi, void* out, int64_t osb,
                            int64_t ldo, int nbatch, int R, int Rp, int C, int Cv, hipStream_t s) {
   const dim3 grid((C + 63) / 64, (Rp + 63) / 64, nbatch);
+  // 16-byte accesses need 8-element aligned bases and strides
+  const int vec = ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0) && isb1 % 8 == 0 && isb2 % 8 == 0 &&
+                  ldi % 8 == 0 && osb % 8 == 0 && ldo % 8 == 0;
   transpose_bf16_kernel<<<grid, 256, 0, s>>>((const bf16_t*)in, isb1, isb2, nb2, ldi, (bf16_t*)out, osb, ldo, R, Rp,
-                                             C, Cv);
+                                             C, Cv, vec);
 }
 
 void launch_wgrad(const WgradArgs& a, hipStream_t s) {
@@ -1097,8 +1134,10 @@ void launch_wgrad(const WgradArgs& a, hipStream_t s) {
 }
 
 void launch_router_wgrad(const float* dz, const void* fperm, const int32_t* off, int n_loops, int NK, int E, int D,
-                         float* dWr, hipStream_t s) {
-  router_wgrad_kernel<<<dim3((D + 255) / 256, E), 256, 0, s>>>(dz, (const bf16_t*)fperm, off, n_loops, NK, E, D, dWr);
+                         float* part, float* dWr, hipStream_t s) {
+  router_wgrad_kernel<<<dim3((D + 255) / 256, E, RW_SLICES), 256, 0, s>>>(dz, (const bf16_t*)fperm, off, n_loops, NK,
+                                                                           E, D, part);
+  launch_col_reduce(part, RW_SLICES, (int64_t)E * D, E * D, dWr, 0, s);
 }
 
 void launch_gather_rows_bf16(const void* src, const int32_t* perm, int M, int D, void* dst, hipStream_t s) {

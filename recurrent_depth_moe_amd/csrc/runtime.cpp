@@ -1588,7 +1588,7 @@ enum BwId {
   SV_G, SV_TAU, SV_WL, SV_DV,
   // working buffers of one loop
   BW_G, BW_DX1, BW_DF, BW_DA, BW_DZ, BW_GU, BW_DACT, BW_DFP, BW_GUS, BW_DACTS, BW_DO, BW_LSE, BW_DELTA, BW_QT,
-  BW_DOT, BW_KT, BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD,
+  BW_DOT, BW_KT, BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD, BW_RWP,
   // per-wave partial column sums (contiguous: cleared together)
   BP_A, BP_B, BP_GF, BP_GA, BP_GR, BP_HW, BP_HB, BP_S,
   // transposed weights
@@ -1645,6 +1645,7 @@ BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   s[BW_DAVEC] = D * 4;
   s[BW_LV] = s[BW_LDW] = N * r * 4;
   s[BW_DVPAD] = N * 64 * 2;
+  s[BW_RWP] = RDT_ROUTER_WGRAD_PART(E, D) * 4;
   s[BP_A] = s[BP_B] = s[BP_GF] = s[BP_GA] = s[BP_GR] = s[BP_HW] = W * D * 4;
   s[BP_HB] = W * 4;
   s[BP_S] = Ls * W * RDT_LORA_LD * 4;
@@ -2057,7 +2058,7 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   float* gb = grad;
   wgrad(Q(SV_DQKV), QKV, Q(SV_A), D, nullptr, nullptr, N, N, 1, QKV, D, gb + goff[RDT_W_WQ], D, 0, 1, 0);
   wgrad(Q(SV_DX1), D, Q(SV_O), HD, nullptr, nullptr, N, N, 1, D, HD, gb + goff[RDT_W_WO], HD, 0, 1, 0);
-  launch_router_wgrad(QF(SV_DZP), Q(SV_FPERM), QI(SV_OFF), L, NK, E, D, gb + goff[RDT_W_ROUTER], s);
+  launch_router_wgrad(QF(SV_DZP), Q(SV_FPERM), QI(SV_OFF), L, NK, E, D, QF(BW_RWP), gb + goff[RDT_W_ROUTER], s);
   wgrad(Q(SV_DGU), 2 * F, Q(SV_FPERM), D, nullptr, QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_GATE], D,
         (int64_t)F * D, 1, 0);
   wgrad(QB(SV_DGU) + F, 2 * F, Q(SV_FPERM), D, nullptr, QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_UP], D,
