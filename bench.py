@@ -173,19 +173,18 @@ def train_bench(args, cfg):
     et = torch.from_numpy(e).cuda()
     ht = torch.from_numpy(h0).cuda()
     dy = torch.from_numpy(np.random.default_rng(5).standard_normal(e.shape).astype(np.float32)).cuda()
-    ws = blk.new_workspace(B, T)
-    tape = torch.empty(blk.train_tape_bytes(B, T, L) // 4, dtype=torch.float32, device="cuda")
+    tape = blk.new_tape(B, T, L)
     bws = torch.empty(blk.train_workspace_bytes(B, T, L), dtype=torch.uint8, device="cuda")
     grad = torch.empty(blk.grad_numel(), dtype=torch.float32, device="cuda")
     de, dh0 = torch.empty_like(et), torch.empty_like(et)
     load = torch.empty(cfg["n_experts"], dtype=torch.int32, device="cuda")
     h_out = torch.empty_like(et)
     hc = torch.empty((B, T), dtype=torch.int32, device="cuda")
-    log(f"[bench] training workspace {bws.numel() / 2**30:.1f} GiB, tape {tape.numel() * 4 / 2**30:.2f} GiB")
+    log(f"[bench] training workspace {bws.numel() / 2**30:.1f} GiB, tape {tape.numel() / 2**30:.2f} GiB")
     stream = torch.cuda.current_stream()
 
     def step():
-        blk.train_forward(et, ht, L, thr, tape, ws, h_out, hc)
+        blk.train_forward(et, ht, L, thr, tape, h_out, hc)
         blk.train_backward(et, ht, L, thr, tape, hc, dy, bws, grad, de, dh0, load)
 
     for i in range(args.warmup):

@@ -318,10 +318,11 @@ rdt_status rdt_model_generate(rdt_model* m, const int32_t* prompt, int32_t B, in
  * ------------------------------------------------------------------------ */
 #define RDT_MAX_TRAIN_LOOPS 64
 
-/* Bytes of the tape a training forward records (the state after each loop,
- * fp32 [n_loops][B T][D]) and of the backward workspace for B x T and
- * n_loops (every loop's saved matrix-product operands, the working buffers
- * of one loop and transposed copies of the weights). */
+/* Bytes of the tape a training forward records (every loop's forward
+ * intermediates: one forward workspace per loop, plus the attention's
+ * softmax normalisers) and of the backward workspace for B x T and n_loops
+ * (every loop's saved gradient operands, the working buffers of one loop
+ * and transposed copies of the weights). */
 rdt_status rdt_train_tape_bytes(const rdt_block* blk, int32_t B, int32_t T, int32_t n_loops, size_t* bytes);
 rdt_status rdt_train_workspace_bytes(const rdt_block* blk, int32_t B, int32_t T, int32_t n_loops, size_t* bytes);
 
@@ -332,12 +333,13 @@ rdt_status rdt_train_workspace_bytes(const rdt_block* blk, int32_t B, int32_t T,
 rdt_status rdt_grad_layout(const rdt_block* blk, int32_t id, int64_t* offset, int64_t* numel);
 rdt_status rdt_grad_numel(const rdt_block* blk, int64_t* numel);
 
-/* Training forward: rdt_recurrent_forward without a cache (same arguments,
- * outputs and stop once every position has halted), which also writes the
- * state after each loop run into `tape` (>= rdt_train_tape_bytes). */
+/* Training forward: rdt_recurrent_forward without a cache (same outputs,
+ * same stop once every position has halted), each loop running in its own
+ * frame of `tape` (>= rdt_train_tape_bytes, 256-byte aligned), which then
+ * holds what the backward pass reads; no other workspace is needed. */
 rdt_status rdt_train_forward(rdt_block* blk, const float* e, const float* h0, int32_t B, int32_t T, int32_t n_loops,
-                             float act_threshold, void* workspace, size_t ws_bytes, float* tape, size_t tape_bytes,
-                             float* h_out, int32_t* halt_counts, void* stream);
+                             float act_threshold, void* tape, size_t tape_bytes, float* h_out, int32_t* halt_counts,
+                             void* stream);
 
 /* Backward pass ([ZS §Recurrent Block] forward): given dy = dL/dh_out
  * (fp32 [B, T, D]) for the output of the rdt_train_forward call that wrote
@@ -345,16 +347,17 @@ rdt_status rdt_train_forward(rdt_block* blk, const float* e, const float* h0, in
  * writes the gradient of every trained tensor into `grad` (fp32, layout of
  * rdt_grad_layout; the router bias's entry is 0), dL/de and dL/dh0 (fp32
  * [B, T, D]), and expert_load (int32 [n_experts]): the (position, slot)
- * assignments of each expert summed over the loops run.  Each loop is
- * recomputed from its recorded input state, in reverse order; weight
- * gradients are accumulated over all loops' rows at the end.  The handle's
+ * assignments of each expert summed over the loops run.  The loops are
+ * taken in reverse order from their frames of the tape (only the gate / up
+ * pre-activations of the experts are recomputed); weight gradients are
+ * formed over all loops' rows at the end.  The handle's
  * weights (router bias included) must not change between the two calls.
  * The call synchronises `stream` once (to read the number of loops run).
  * Errors: INVALID_ARG (nulls, sizes, n_loops > RDT_MAX_TRAIN_LOOPS),
  * UNSUPPORTED (not bf16 GQA with head_dim 128, T < 2),
  * WORKSPACE_TOO_SMALL (tape, workspace or gradient buffer). */
 rdt_status rdt_train_backward(rdt_block* blk, const float* e, const float* h0, int32_t B, int32_t T,
-                              int32_t n_loops, float act_threshold, const float* tape, size_t tape_bytes,
+                              int32_t n_loops, float act_threshold, const void* tape, size_t tape_bytes,
                               const int32_t* halt_counts, const float* dy, float* grad, int64_t grad_numel,
                               float* de, float* dh0, int32_t* expert_load, void* workspace, size_t ws_bytes,
                               void* stream);

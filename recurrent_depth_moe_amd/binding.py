@@ -102,7 +102,7 @@ def lib():
         "rdt_train_workspace_bytes": ([vp, i32, i32, i32, ctypes.POINTER(sz)], i32),
         "rdt_grad_layout": ([vp, i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)], i32),
         "rdt_grad_numel": ([vp, ctypes.POINTER(ctypes.c_int64)], i32),
-        "rdt_train_forward": ([vp, vp, vp, i32, i32, i32, f32, vp, sz, vp, sz, vp, vp, vp], i32),
+        "rdt_train_forward": ([vp, vp, vp, i32, i32, i32, f32, vp, sz, vp, vp, vp], i32),
         "rdt_train_backward": ([vp, vp, vp, i32, i32, i32, f32, vp, sz, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
                                 vp, sz, vp], i32),
         "rdt_router_bias_update": ([vp, vp, f32, vp], i32),
@@ -296,17 +296,16 @@ class Block:
         check(lib().rdt_train_workspace_bytes(self._h, B, T, n_loops, ctypes.byref(n)))
         return n.value
 
-    def train_forward(self, e, h0, n_loops, act_threshold, tape, workspace=None, h_out=None, halt_counts=None,
-                      stream=None):
+    def new_tape(self, B, T, n_loops):
+        return torch.empty(self.train_tape_bytes(B, T, n_loops), dtype=torch.uint8, device="cuda")
+
+    def train_forward(self, e, h0, n_loops, act_threshold, tape, h_out=None, halt_counts=None, stream=None):
         B, T, D = e.shape
-        if workspace is None:
-            workspace = self.new_workspace(B, T)
         if h_out is None:
             h_out = torch.empty_like(e)
         if halt_counts is None:
             halt_counts = torch.empty((B, T), dtype=torch.int32, device=e.device)
-        check(lib().rdt_train_forward(self._h, _ptr(e), _ptr(h0), B, T, n_loops, float(act_threshold),
-                                      _ptr(workspace), workspace.numel(), _ptr(tape),
+        check(lib().rdt_train_forward(self._h, _ptr(e), _ptr(h0), B, T, n_loops, float(act_threshold), _ptr(tape),
                                       tape.numel() * tape.element_size(), _ptr(h_out), _ptr(halt_counts),
                                       _stream(stream)))
         return h_out, halt_counts

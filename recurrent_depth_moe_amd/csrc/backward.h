@@ -22,20 +22,21 @@
 void launch_transpose_bf16(const void* in, int64_t isb1, int64_t isb2, int nb2, int64_t ldi, void* out, int64_t osb,
                            int64_t ldo, int nbatch, int R, int Rp, int C, int Cv, hipStream_t s);
 
-// Weight gradient C_g[n][k] (+)= sum over rows m of group g of A[m][n] X[xrow(m)][k]
-// (bf16 operands, fp32 result).  Rows are stacked per loop: row (t, i) is
-// t * loop_rows + i; group g of loop t holds rows off[t][g] .. off[t][g+1]
-// (off null: one group of `rows` rows).  Loops split over `splits` slices
-// along grid z, slice z writing C + z * c_split_stride.
+// Weight gradient C_g[n][k] (+)= sum over loops t and rows m of group g
+// of A_t[m][n] X_t[m][k] (bf16 operands, fp32 result), A_t = A + t a_loop_stride
+// (elements), row m at A_t + m lda, likewise X; group g of loop t holds
+// rows off[t][g] .. off[t][g+1] (off null: one group of `rows` rows).
+// Loops split over `splits` slices along grid z, slice z writing
+// C + z * c_split_stride.
 struct WgradArgs {
   const void* A;
   int64_t lda;
+  int64_t a_loop_stride;
   const void* X;
   int64_t ldx;
-  const int32_t* xrow;   // nullable: X row of each stacked row
+  int64_t x_loop_stride;
   const int32_t* off;    // nullable: [n_loops][G + 1]
   int n_loops;
-  int64_t loop_rows;
   int rows;
   int G;
   int Nc, Kc;
@@ -78,11 +79,11 @@ void launch_swiglu_bwd(const void* gu, const float* dact, int M, int F, void* dg
 
 // ACT: per position n and loop t < L, w[t][n] = weight of h_{t+1} in the
 // output and z[t][n] = d loss / d halting logit, from the recorded states
-// (states[t] = h_{t+1}), dy and the halting loops; partial sums of
-// z * h_{t+1} (d halt_w) and of z (d halt_b) per wave.
-void launch_act_prep(const float* states, const float* dy, const float* halt_w, const float* halt_b,
-                     const int32_t* halt_counts, int L, int N, int D, float* w_act, float* z_act, float* part_hw,
-                     float* part_hb, hipStream_t s);
+// (h_{t+1} = states + t state_stride, [N][D] fp32), dy and the halting
+// loops; partial sums of z * h_{t+1} (d halt_w) and of z (d halt_b) per wave.
+void launch_act_prep(const float* states, int64_t state_stride, const float* dy, const float* halt_w,
+                     const float* halt_b, const int32_t* halt_counts, int L, int N, int D, float* w_act, float* z_act,
+                     float* part_hw, float* part_hb, hipStream_t s);
 
 struct TailBwdArgs {
   int N, D, k, S, r;
@@ -142,7 +143,7 @@ void launch_head_bwd(int N, int D, float eps, const float* dx1, const float* da,
                      const float* g_attn, const float* g_rec, const float* h_prev, const float* e, const float* emb_t,
                      int loop_dim, float* g_carry, float* de, float* part_ga, float* part_gr, hipStream_t s);
 
-// gidx[t NK + m] = t N + perm[m]; load[e] += off[e+1] - off[e]
+// gidx[t NK + m] = t N + perm[m] (gidx nullable); load[e] += off[e+1] - off[e]
 void launch_loop_index(const int32_t* perm, const int32_t* off, int t, int NK, int N, int E, int32_t* gidx,
                        int32_t* load, hipStream_t s);
 // out[c] (+)= sum_w part[w][c] for c < len, w < rows

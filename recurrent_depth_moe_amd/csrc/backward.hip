@@ -179,31 +179,33 @@ __global__ __launch_bounds__(256, WF == 4 ? 1 : 2) void wgrad_kernel(WgradArgs a
     s_hi[i] = o ? o[1] : a.rows;
   }
   __syncthreads();
+  const bf16_t* Ab = (const bf16_t*)a.A + n0 + 8 * cc;
+  const bf16_t* Xb = (const bf16_t*)a.X + k0 + 8 * cc;
+  const bf16_t *Abt = Ab, *Xbt = Xb;   // this loop's rows
   int t = t_lo - 1;
   int64_t m0 = 0, r1 = 0;
   auto advance = [&]() -> bool {
     m0 += 64;
     while (m0 >= r1) {
       if (++t >= t_hi) return false;
-      const int64_t base = (int64_t)t * a.loop_rows;
-      m0 = base + s_lo[t - t_lo];
-      r1 = base + s_hi[t - t_lo];
+      m0 = s_lo[t - t_lo];
+      r1 = s_hi[t - t_lo];
+      Abt = Ab + (int64_t)t * a.a_loop_stride;
+      Xbt = Xb + (int64_t)t * a.x_loop_stride;
     }
     return true;
   };
   uint4 va[NP][4], vx[NP][4];
   // tiles wholly inside the output take plain 16-byte loads
   const bool full = n0 + TILE <= a.Nc && k0 + TILE <= a.Kc;
-  const bf16_t* Ab = (const bf16_t*)a.A + n0 + 8 * cc;
-  const bf16_t* Xb = (const bf16_t*)a.X + k0 + 8 * cc;
   auto load = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t m = m0 + 4 * rg + i;
       const bool ok = m < r1;
       const int64_t mm = ok ? m : r1 - 1;   // a row of the chunk; zeroed below when past its end
-      const bf16_t* ar = Ab + mm * a.lda;
-      const bf16_t* xr = Xb + (a.xrow ? (int64_t)a.xrow[mm] : mm) * a.ldx;
+      const bf16_t* ar = Abt + mm * a.lda;
+      const bf16_t* xr = Xbt + mm * a.ldx;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (full) {
@@ -318,21 +320,23 @@ __global__ __launch_bounds__(512, 1) void wgrad8_kernel(WgradArgs a) {
     s_hi[i] = o ? o[1] : a.rows;
   }
   __syncthreads();
+  const bf16_t* Ab = (const bf16_t*)a.A + n0 + 8 * cc;
+  const bf16_t* Xb = (const bf16_t*)a.X + k0 + 8 * cc;
+  const bf16_t *Abt = Ab, *Xbt = Xb;   // this loop's rows
   int t = t_lo - 1;
   int64_t m0 = -64, r1 = 0;
   auto advance = [&]() -> bool {
     m0 += 64;
     while (m0 >= r1) {
       if (++t >= t_hi) return false;
-      const int64_t base = (int64_t)t * a.loop_rows;
-      m0 = base + s_lo[t - t_lo];
-      r1 = base + s_hi[t - t_lo];
+      m0 = s_lo[t - t_lo];
+      r1 = s_hi[t - t_lo];
+      Abt = Ab + (int64_t)t * a.a_loop_stride;
+      Xbt = Xb + (int64_t)t * a.x_loop_stride;
     }
     return true;
   };
   const bool full = n0 + TILE <= a.Nc && k0 + TILE <= a.Kc;
-  const bf16_t* Ab = (const bf16_t*)a.A + n0 + 8 * cc;
-  const bf16_t* Xb = (const bf16_t*)a.X + k0 + 8 * cc;
   const int na = a.Nc - (n0 + 8 * cc), nx = a.Kc - (k0 + 8 * cc);
   uint4 va[4], vx[4];
   auto load = [&]() {
@@ -341,8 +345,8 @@ __global__ __launch_bounds__(512, 1) void wgrad8_kernel(WgradArgs a) {
       const int64_t m = m0 + 4 * rg + i;
       const bool ok = m < r1;
       const int64_t mm = ok ? m : r1 - 1;
-      const bf16_t* ar = Ab + mm * a.lda;
-      const bf16_t* xr = Xb + (a.xrow ? (int64_t)a.xrow[mm] : mm) * a.ldx;
+      const bf16_t* ar = Abt + mm * a.lda;
+      const bf16_t* xr = Xbt + mm * a.ldx;
       if (full) {
         va[i] = *(const uint4*)ar;
         vx[i] = *(const uint4*)xr;
@@ -784,7 +788,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16_t* __restric
   for (int n = wg; n < N; n += RDT_BWD_WAVES) {
 #define ROW_LOOP_END }
 
-__global__ __launch_bounds__(256) void act_prep_kernel(const float* __restrict__ states, const float* __restrict__ dy,
+__global__ __launch_bounds__(256) void act_prep_kernel(const float* __restrict__ states, int64_t sstride,
+                                                       const float* __restrict__ dy,
                                                        const float* __restrict__ hw, const float* __restrict__ hb,
                                                        const int32_t* __restrict__ hc, int L, int N, int D,
                                                        float* __restrict__ w_act, float* __restrict__ z_act,
@@ -794,7 +799,7 @@ __global__ __launch_bounds__(256) void act_prep_kernel(const float* __restrict__
   float my_p = 0.f, my_G = 0.f;
   const float* dyr = dy + (int64_t)n * D;
   for (int t = 0; t < L; ++t) {
-    const float* sr = states + ((int64_t)t * N + n) * D;
+    const float* sr = states + (int64_t)t * sstride + (int64_t)n * D;
     float zp = 0.f, gp = 0.f;
     for (int c = 4 * lane; c < D; c += 256) {
       const float4 x = ld4(sr + c);
@@ -836,7 +841,7 @@ __global__ __launch_bounds__(256) void act_prep_kernel(const float* __restrict__
     const float zt = __shfl(my_p, t, 64) * (1.0f - __shfl(my_p, t, 64)) *
                      (__shfl(my_G, t, 64) - (rem > 0.f ? G_th : 0.f));
     zsum += zt;
-    const float* sr = states + ((int64_t)t * N + n) * D;
+    const float* sr = states + (int64_t)t * sstride + (int64_t)n * D;
     for (int c = 4 * lane; c < D; c += 256) st4(ph + c, fma4(zt, ld4(sr + c), ld4(ph + c)));
   }
   if (lane == 0) part_hb[wg] += zsum;
@@ -1045,7 +1050,7 @@ __global__ __launch_bounds__(256) void loop_index_kernel(const int32_t* __restri
                                                          const int32_t* __restrict__ off, int t, int NK, int N, int E,
                                                          int32_t* __restrict__ gidx, int32_t* __restrict__ load) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < NK) gidx[(int64_t)t * NK + i] = t * N + perm[i];
+  if (gidx && i < NK) gidx[(int64_t)t * NK + i] = t * N + perm[i];
   if (blockIdx.x == 0 && threadIdx.x < E) load[threadIdx.x] += off[threadIdx.x + 1] - off[threadIdx.x];
 }
 
@@ -1178,11 +1183,11 @@ void launch_swiglu_bwd(const void* gu, const float* dact, int M, int F, void* dg
   swiglu_bwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const bf16_t*)gu, dact, M, F, (bf16_t*)dgu);
 }
 
-void launch_act_prep(const float* states, const float* dy, const float* halt_w, const float* halt_b,
-                     const int32_t* halt_counts, int L, int N, int D, float* w_act, float* z_act, float* part_hw,
-                     float* part_hb, hipStream_t s) {
-  act_prep_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(states, dy, halt_w, halt_b, halt_counts, L, N, D, w_act, z_act,
-                                                 part_hw, part_hb);
+void launch_act_prep(const float* states, int64_t state_stride, const float* dy, const float* halt_w,
+                     const float* halt_b, const int32_t* halt_counts, int L, int N, int D, float* w_act, float* z_act,
+                     float* part_hw, float* part_hb, hipStream_t s) {
+  act_prep_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(states, state_stride, dy, halt_w, halt_b, halt_counts, L, N, D,
+                                                 w_act, z_act, part_hw, part_hb);
 }
 
 void launch_tail_bwd_rows(const TailBwdArgs& a, hipStream_t s) {

@@ -928,7 +928,7 @@ void attention_sublayer(const Ctx& x, const AttnW& aw, char* kslot, int cap_pad,
 static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int T, int start_pos, int n_loops,
                       float thr, void* kv, int kv_capacity, size_t kv_bytes, void* ws, size_t ws_bytes,
                       float* h_out, int32_t* halt_counts, void* stream, bool decode, bool act_skip = false,
-                      float* tape_h = nullptr) {
+                      size_t frame = 0, float* lse2_frames = nullptr) {
   g_err.clear();
   if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
   const rdt_config& c = b->cfg;
@@ -963,6 +963,10 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   int32_t* live_cur = nullptr;
 
   Ctx x{b, &c, &p, w, s_main, bf, B, T, start_pos, N, nullptr, nullptr};
+  // training forward: loop t runs in its own frame of the workspace (frame
+  // bytes apart), which keeps every loop's intermediates for the backward
+  // pass; the ACT running sums and counters stay in frame 0
+  char* const base = w;
   auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16, bool narrow = false, hipStream_t on = nullptr) {
     x.live_prev = live_prev;
     x.gemm(gp, epi, dual, out_bf16, narrow, on);
@@ -1009,7 +1013,12 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       Mr = nrun;
       tok = WI(WS_TOK);
     }
-    const float* hp = t == 0 ? h0 : WF(WS_H);
+    if (frame) {
+      w = base + (size_t)t * frame;
+      x.w = w;
+      x.lse2 = lse2_frames + (size_t)t * N * c.n_heads;
+    }
+    const float* hp = t == 0 ? h0 : frame ? (const float*)(base + (size_t)(t - 1) * frame + p.off[WS_H]) : WF(WS_H);
     live_prev = (live_buf && t > 0) ? live_buf + ((t - 1) & 1) : nullptr;
     live_cur = live_buf ? live_buf + (t & 1) : nullptr;
     // a1-a3: loop-index embedding, re-injection of e, RMSNorms
@@ -1130,7 +1139,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       ta.halt_b = b->halt_b;
       ta.act_threshold = thr;
       ta.h_out = h_out;
-      ta.cum = WF(WS_CUM);
+      ta.cum = (float*)(base + p.off[WS_CUM]);
       ta.halt_counts = halt_counts;
       ta.t = t;
       ta.n_loops = n_loops;
@@ -1138,7 +1147,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       ta.tok = tok;
       ta.D = D;
       ta.k = k;
-      ta.cap_h = tape_h ? tape_h + (size_t)t * N * D : b->cap_h ? b->cap_h + (size_t)t * N * D : nullptr;
+      ta.cap_h = b->cap_h ? b->cap_h + (size_t)t * N * D : nullptr;
       ta.cap_p = (b->cap_p && thr > 0.f) ? b->cap_p + (size_t)t * N : nullptr;
       ta.w_bf16 = bf;
       ta.live_prev = live_prev;
@@ -1583,12 +1592,12 @@ rdt_status rdt_model_generate(rdt_model* m, const int32_t* prompt, int32_t B, in
 namespace {
 
 enum BwId {
-  // per loop, stacked over the loops: operands of the weight-gradient products
-  SV_A, SV_DQKV, SV_O, SV_DX1, SV_F, SV_FPERM, SV_GIDX, SV_OFF, SV_DZP, SV_DGU, SV_ACT, SV_DY, SV_ACTS, SV_DGUS, SV_DTAU,
-  SV_G, SV_TAU, SV_WL, SV_DV,
+  // per loop, stacked over the loops: operands of the weight-gradient
+  // products that the forward frames do not already hold
+  SV_DQKV, SV_DX1, SV_FPERM, SV_OFF, SV_DZP, SV_DGU, SV_DY, SV_ACTS, SV_DGUS, SV_DTAU, SV_G, SV_TAU, SV_WL, SV_DV,
   // working buffers of one loop
-  BW_G, BW_DX1, BW_DF, BW_DA, BW_DZ, BW_GU, BW_DACT, BW_DFP, BW_GUS, BW_DACTS, BW_DO, BW_LSE, BW_DELTA, BW_QT,
-  BW_DOT, BW_KT, BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD, BW_RWP,
+  BW_G, BW_DX1, BW_DF, BW_DA, BW_DZ, BW_GU, BW_DACT, BW_DFP, BW_GUS, BW_DACTS, BW_DO, BW_DELTA, BW_QT, BW_DOT, BW_KT,
+  BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD, BW_RWP,
   // per-wave partial column sums (contiguous: cleared together)
   BP_A, BP_B, BP_GF, BP_GA, BP_GR, BP_HW, BP_HB, BP_S,
   // transposed weights
@@ -1596,29 +1605,39 @@ enum BwId {
   BW_COUNT
 };
 
+// The tape of a training forward: one frame (a whole forward workspace)
+// per loop, then the loops' attention log2 normalisers [L][B H T].
+struct TapePlan {
+  Plan fwd;
+  size_t frame, lse_off, total;
+};
+
+TapePlan make_tape_plan(const rdt_config& c, int B, int T, int L) {
+  TapePlan tp{};
+  tp.fwd = make_plan(c, B, T);
+  tp.frame = align256(tp.fwd.total);
+  tp.lse_off = tp.frame * (size_t)L;
+  tp.total = tp.lse_off + align256((size_t)L * B * T * c.n_heads * 4);
+  return tp;
+}
+
 struct BwPlan {
-  Plan fwd;   // the recompute's forward workspace, at offset 0
   size_t off[BW_COUNT], size[BW_COUNT], total;
 };
 
 BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   BwPlan q{};
-  q.fwd = make_plan(c, B, T);
+  const Plan fwd = make_plan(c, B, T);
   const size_t N = (size_t)B * T, D = c.dim, E = c.n_experts, F = c.expert_dim, S = c.n_shared_experts;
   const size_t NK = N * c.top_k, H = c.n_heads, G = c.n_kv_heads, QKV = (H + 2 * G) * 128, HD = H * 128;
-  const size_t Tp = round_up(T, 64), cap = q.fwd.kvcap, Ls = L, W = RDT_BWD_WAVES, r = c.lora_rank;
+  const size_t Tp = round_up(T, 64), cap = fwd.kvcap, Ls = L, W = RDT_BWD_WAVES, r = c.lora_rank;
   size_t* s = q.size;
-  s[SV_A] = Ls * N * D * 2;
   s[SV_DQKV] = Ls * N * QKV * 2;
-  s[SV_O] = Ls * N * HD * 2;
   s[SV_DX1] = Ls * N * D * 2;
-  s[SV_F] = Ls * N * D * 2;
   s[SV_FPERM] = Ls * NK * D * 2;
-  s[SV_GIDX] = Ls * NK * 4;
   s[SV_OFF] = Ls * (E + 1) * 4;
   s[SV_DZP] = Ls * NK * 4;
   s[SV_DGU] = Ls * NK * 2 * F * 2;
-  s[SV_ACT] = Ls * NK * F * 2;
   s[SV_DY] = Ls * NK * D * 2;
   s[SV_ACTS] = S * Ls * N * F * 2;
   s[SV_DGUS] = S * Ls * N * 2 * F * 2;
@@ -1635,7 +1654,7 @@ BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   s[BW_GUS] = S * N * 2 * F * 2;
   s[BW_DACTS] = N * F * 4;
   s[BW_DO] = N * HD * 2;
-  s[BW_LSE] = s[BW_DELTA] = N * H * 4;
+  s[BW_DELTA] = N * H * 4;
   s[BW_QT] = s[BW_DOT] = (size_t)B * H * 128 * Tp * 2;
   s[BW_KT] = s[BW_VN] = (size_t)B * G * 128 * cap * 2;
   s[BW_GQ] = N * H * 128 * 4;
@@ -1656,7 +1675,7 @@ BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   s[TW_WSD] = S * F * D * 2;
   s[TW_WSGU] = S * D * 2 * F * 2;
   s[TW_LDT] = D * 64 * 2;
-  size_t o = align256(q.fwd.total);
+  size_t o = 0;
   for (int i = 0; i < BW_COUNT; ++i) {
     q.off[i] = o;
     o += align256(q.size[i]);
@@ -1703,7 +1722,7 @@ rdt_status rdt_train_tape_bytes(const rdt_block* b, int32_t B, int32_t T, int32_
   if (!b || !bytes) return fail(RDT_E_INVALID_ARG, "NULL argument");
   rdt_status st = check_train(b->cfg, B, T, n_loops, 0.f);
   if (st) return st;
-  *bytes = (size_t)n_loops * B * T * b->cfg.dim * 4;
+  *bytes = make_tape_plan(b->cfg, B, T, n_loops).total;
   return RDT_OK;
 }
 
@@ -1736,21 +1755,21 @@ rdt_status rdt_grad_numel(const rdt_block* b, int64_t* numel) {
 }
 
 rdt_status rdt_train_forward(rdt_block* b, const float* e, const float* h0, int32_t B, int32_t T, int32_t n_loops,
-                             float act_threshold, void* workspace, size_t ws_bytes, float* tape, size_t tape_bytes,
-                             float* h_out, int32_t* halt_counts, void* stream) {
+                             float act_threshold, void* tape, size_t tape_bytes, float* h_out, int32_t* halt_counts,
+                             void* stream) {
   g_err.clear();
   if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
   rdt_status st = check_train(b->cfg, B, T, n_loops, act_threshold);
   if (st) return st;
   if (!tape) return fail(RDT_E_INVALID_ARG, "tape is NULL");
-  const size_t need = (size_t)n_loops * B * T * b->cfg.dim * 4;
-  if (tape_bytes < need) return fail(RDT_E_WORKSPACE_TOO_SMALL, "tape %zu bytes, need %zu", tape_bytes, need);
-  return run(b, e, h0, B, T, 0, n_loops, act_threshold, nullptr, 0, 0, workspace, ws_bytes, h_out, halt_counts, stream,
-             false, false, tape);
+  const TapePlan tp = make_tape_plan(b->cfg, B, T, n_loops);
+  if (tape_bytes < tp.total) return fail(RDT_E_WORKSPACE_TOO_SMALL, "tape %zu bytes, need %zu", tape_bytes, tp.total);
+  return run(b, e, h0, B, T, 0, n_loops, act_threshold, nullptr, 0, 0, tape, tape_bytes, h_out, halt_counts, stream,
+             false, false, tp.frame, (float*)((char*)tape + tp.lse_off));
 }
 
 rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int32_t B, int32_t T, int32_t n_loops,
-                              float thr, const float* tape, size_t tape_bytes, const int32_t* hc, const float* dy,
+                              float thr, const void* tape, size_t tape_bytes, const int32_t* hc, const float* dy,
                               float* grad, int64_t grad_numel, float* de, float* dh0, int32_t* load, void* ws,
                               size_t ws_bytes, void* stream) {
   g_err.clear();
@@ -1763,7 +1782,8 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   const int N = B * T, D = c.dim, E = c.n_experts, F = c.expert_dim, S = c.n_shared_experts, k = c.top_k;
   const int NK = N * k, H = c.n_heads, G = c.n_kv_heads, QKV = (H + 2 * G) * 128, HD = H * 128, r = c.lora_rank;
   const int ld = c.loop_dim;
-  if (tape_bytes < (size_t)n_loops * N * D * 4) return fail(RDT_E_WORKSPACE_TOO_SMALL, "tape too small");
+  const TapePlan tp = make_tape_plan(c, B, T, n_loops);
+  if (tape_bytes < tp.total) return fail(RDT_E_WORKSPACE_TOO_SMALL, "tape %zu bytes, need %zu", tape_bytes, tp.total);
   int64_t goff[RDT_W_COUNT], gnum[RDT_W_COUNT], gtotal = 0;
   grad_offsets(c, goff, gnum, &gtotal);
   if (grad_numel < gtotal)
@@ -1771,7 +1791,8 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
                 (long long)gtotal);
   const BwPlan q = make_bw_plan(c, B, T, n_loops);
   if (ws_bytes < q.total) return fail(RDT_E_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", ws_bytes, q.total);
-  if (((uintptr_t)ws) & 255) return fail(RDT_E_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (((uintptr_t)ws) & 255 || ((uintptr_t)tape) & 255)
+    return fail(RDT_E_INVALID_ARG, "workspace and tape must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   const bool act = thr > 0.f;
   // loops run: with ACT on the forward stopped after the last halting loop
@@ -1786,20 +1807,22 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
       L = std::max(L, v);
     }
   }
-  const Plan& p = q.fwd;
+  const Plan& p = tp.fwd;
+  const char* tb = (const char*)tape;
+  // loop t's forward intermediates, in its frame of the tape
+  auto FR = [&](int t, int id) -> void* { return (void*)(tb + (size_t)t * tp.frame + p.off[id]); };
+  auto FRF = [&](int t, int id) -> float* { return (float*)FR(t, id); };
+  auto FRI = [&](int t, int id) -> int32_t* { return (int32_t*)FR(t, id); };
+  const float* lse_all = (const float*)(tb + tp.lse_off);
   char* w = (char*)ws;
-  auto W = [&](int id) -> void* { return w + p.off[id]; };
-  auto WF = [&](int id) -> float* { return (float*)(w + p.off[id]); };
-  auto WI = [&](int id) -> int32_t* { return (int32_t*)(w + p.off[id]); };
   auto Q = [&](int id) -> void* { return w + q.off[id]; };
   auto QF = [&](int id) -> float* { return (float*)(w + q.off[id]); };
   auto QI = [&](int id) -> int32_t* { return (int32_t*)(w + q.off[id]); };
   auto QB = [&](int id) -> bf16_t* { return (bf16_t*)(w + q.off[id]); };
-  const bf16_t* wb = nullptr;
-  (void)wb;
   const int cap = p.kvcap, Tp = round_up(T, 64);
   const float eps = c.norm_eps, scale = 1.0f / sqrtf(128.f);
-  const size_t NDs = (size_t)N * D;
+  const size_t NDs = (size_t)N * D, es = 2;
+  const int64_t fr_bf = (int64_t)(tp.frame / 2);   // frame stride in bf16 elements
 
   // what accumulates starts at zero
   launch_fill_zero(grad, (size_t)gtotal * 4, s);
@@ -1828,48 +1851,36 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   // each halting logit; without ACT the output is the last state
   if (act) {
     launch_fill_zero(Q(BW_G), NDs * 4, s);
-    launch_act_prep(tape, dy, b->halt_w, b->halt_b, hc, L, N, D, QF(BW_WACT), QF(BW_ZACT), QF(BP_HW), QF(BP_HB), s);
+    launch_act_prep(FRF(0, WS_H), (int64_t)(tp.frame / 4), dy, b->halt_w, b->halt_b, hc, L, N, D, QF(BW_WACT),
+                    QF(BW_ZACT), QF(BP_HW), QF(BP_HB), s);
   } else {
     HIP_TRY(hipMemcpyAsync(Q(BW_G), dy, NDs * 4, hipMemcpyDeviceToDevice, s));
   }
-  Ctx x{b, &c, &p, w, s, true, B, T, 0, N, nullptr, nullptr};
-  x.lse2 = QF(BW_LSE);
-  const size_t es = 2;
+  // products go through the forward's dispatcher (workspace pointer unused)
+  Ctx x{b, &c, &p, (char*)ws, s, true, B, T, 0, N, nullptr, nullptr};
   for (int t = L - 1; t >= 0; --t) {
-    const float* hp = t == 0 ? h0 : tape + (size_t)(t - 1) * NDs;
+    const float* hp = t == 0 ? h0 : FRF(t - 1, WS_H);
     const float* emb_t = b->loop_emb + (size_t)t * ld;
-    // ---- recompute loop t (same kernels and schedules as the forward up
-    // to the routed products, so the expert choice is the forward's)
-    launch_loop_head(1, hp, e, emb_t, ld, b->g_rec, b->g_attn, eps, WF(WS_C), W(WS_A), N, D, s);
-    attention_sublayer(x, b->aw, nullptr, 0, WF(WS_C), WF(WS_X1));
-    launch_rmsnorm(1, WF(WS_X1), D, b->g_ffn, eps, W(WS_F), D, N, D, s);
-    {
-      GemmParams gp = dense_params(W(WS_F), D, b->router, nullptr, N, E, D);
-      gp.epi.out = W(WS_LOGITS);
-      gp.epi.ldo = E;
-      x.gemm(gp, EPI_STORE, false, 0, true);
-      launch_router_topk(WF(WS_LOGITS), b->router_bias, N, E, k, WI(WS_SEL), WF(WS_GATE), nullptr, s);
-    }
-    launch_dispatch(WI(WS_SEL), NK, k, E, p.bm, WI(WS_TILECNT), WI(WS_OFFSETS), WI(WS_MTSTART), WI(WS_TROW0),
-                    WI(WS_TGRP), WI(WS_PERM), WI(WS_INV), WI(WS_TCLAIM), 2 * RDT_NUM_XCD, s);
-    launch_loop_index(WI(WS_PERM), WI(WS_OFFSETS), t, NK, N, E, QI(SV_GIDX), load, s);
-    HIP_TRY(hipMemcpyAsync(QI(SV_OFF) + (size_t)t * (E + 1), WI(WS_OFFSETS), (size_t)(E + 1) * 4,
+    // ---- from the forward's frame: the routing of loop t; recomputed: the
+    // routed and shared gate / up pre-activations (the forward's fused
+    // SwiGLU epilogue keeps only their product) and the shared activations
+    launch_loop_index(FRI(t, WS_PERM), FRI(t, WS_OFFSETS), t, NK, N, E, nullptr, load, s);
+    HIP_TRY(hipMemcpyAsync(QI(SV_OFF) + (size_t)t * (E + 1), FRI(t, WS_OFFSETS), (size_t)(E + 1) * 4,
                            hipMemcpyDeviceToDevice, s));
-    // routed gate and up pre-activations (kept for the SwiGLU backward),
-    // the activation and the routed outputs
+    launch_gather_rows_bf16(FR(t, WS_F), FRI(t, WS_PERM), NK, D, QB(SV_FPERM) + (size_t)t * NK * D, s);
     GemmParams gp{};
-    gp.A = W(WS_F);
+    gp.A = FR(t, WS_F);
     gp.lda = D;
-    gp.a_rows = WI(WS_PERM);
+    gp.a_rows = FRI(t, WS_PERM);
     gp.W0 = b->w_gate;
     gp.w_stride = (int64_t)F * D;
     gp.M = NK;
     gp.N = F;
     gp.K = D;
-    gp.mt_start = WI(WS_MTSTART);
-    gp.tile_row0 = WI(WS_TROW0);
-    gp.tile_grp = WI(WS_TGRP);
-    gp.grp_end = WI(WS_OFFSETS);
+    gp.mt_start = FRI(t, WS_MTSTART);
+    gp.tile_row0 = FRI(t, WS_TROW0);
+    gp.tile_grp = FRI(t, WS_TGRP);
+    gp.grp_end = FRI(t, WS_OFFSETS);
     gp.n_groups = E;
     gp.epi.out = Q(BW_GU);
     gp.epi.ldo = 2 * F;
@@ -1877,42 +1888,17 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
     gp.W0 = b->w_up;
     gp.epi.out = QB(BW_GU) + F;
     launch_gemm_bf16_big(gp, EPI_STORE, false, 1, b->n_cu, s, 256);
-    bf16_t* act_t = QB(SV_ACT) + (size_t)t * NK * F;
-    launch_swiglu_fwd(Q(BW_GU), NK, F, act_t, s);
-    {
-      GemmParams gd = gp;
-      gd.A = act_t;
-      gd.lda = F;
-      gd.a_rows = nullptr;
-      gd.W0 = b->w_down;
-      gd.w_stride = (int64_t)D * F;
-      gd.N = D;
-      gd.K = F;
-      gd.epi = EpiParams{};
-      gd.epi.out = W(WS_Y);
-      gd.epi.ldo = D;
-      launch_gemm_bf16_big(gd, EPI_STORE, false, 1, b->n_cu, s, 256);
-    }
     for (int si = 0; si < S; ++si) {
       bf16_t* gus = QB(BW_GUS) + (size_t)si * N * 2 * F;
-      GemmParams gs = dense_params(W(WS_F), D, (const char*)b->s_gate + (size_t)si * F * D * es, nullptr, N, F, D);
+      GemmParams gs = dense_params(FR(t, WS_F), D, (const char*)b->s_gate + (size_t)si * F * D * es, nullptr, N, F, D);
       gs.epi.out = gus;
       gs.epi.ldo = 2 * F;
       x.gemm(gs, EPI_STORE, false, 1);
       gs.W0 = (const char*)b->s_up + (size_t)si * F * D * es;
       gs.epi.out = gus + F;
       x.gemm(gs, EPI_STORE, false, 1);
-      bf16_t* acts = QB(SV_ACTS) + ((size_t)si * n_loops + t) * N * F;
-      launch_swiglu_fwd(gus, N, F, acts, s);
-      GemmParams gd = dense_params(acts, F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, N, D, F);
-      gd.epi.out = (bf16_t*)W(WS_YS) + (size_t)si * NDs;
-      gd.epi.ldo = D;
-      x.gemm(gd, EPI_STORE, false, 1);
+      launch_swiglu_fwd(gus, N, F, QB(SV_ACTS) + ((size_t)si * n_loops + t) * N * F, s);
     }
-    HIP_TRY(hipMemcpyAsync(QB(SV_A) + (size_t)t * NDs, W(WS_A), NDs * 2, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(hipMemcpyAsync(QB(SV_O) + (size_t)t * N * HD, W(WS_O), (size_t)N * HD * 2, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(hipMemcpyAsync(QB(SV_F) + (size_t)t * NDs, W(WS_F), NDs * 2, hipMemcpyDeviceToDevice, s));
-    launch_gather_rows_bf16(W(WS_F), WI(WS_PERM), NK, D, QB(SV_FPERM) + (size_t)t * NK * D, s);
 
     // ---- backward of loop t
     {
@@ -1927,11 +1913,11 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
       ta.w_act = act ? QF(BW_WACT) + (size_t)t * N : nullptr;
       ta.z_act = act ? QF(BW_ZACT) + (size_t)t * N : nullptr;
       ta.halt_w = b->halt_w;
-      ta.x1 = WF(WS_X1);
-      ta.y = W(WS_Y);
-      ta.inv = WI(WS_INV);
-      ta.gate = WF(WS_GATE);
-      ta.ys = W(WS_YS);
+      ta.x1 = FRF(t, WS_X1);
+      ta.y = FR(t, WS_Y);
+      ta.inv = FRI(t, WS_INV);
+      ta.gate = FRF(t, WS_GATE);
+      ta.ys = FR(t, WS_YS);
       ta.lora_down = b->lora_down;
       ta.lora_B = b->lora_B;
       ta.scale_row = b->lora_scale + (size_t)std::min(t, c.max_loop_iters - 1) * r;
@@ -2017,25 +2003,26 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
       r2.epi.ldo = D;
       launch_gemm_bf16_big(r2, EPI_STORE, false, 0, b->n_cu, s, 256);
     }
-    launch_ffn_norm_bwd(N, D, k, eps, S ? QF(BW_DF) : nullptr, QF(BW_DFP), WI(WS_INV), WI(WS_SEL), QF(BW_DZ), b->router,
-                        WF(WS_X1), b->g_ffn, QF(BW_DX1), QB(SV_DX1) + (size_t)t * NDs, QF(BP_GF), s);
+    launch_ffn_norm_bwd(N, D, k, eps, S ? QF(BW_DF) : nullptr, QF(BW_DFP), FRI(t, WS_INV), FRI(t, WS_SEL), QF(BW_DZ),
+                        b->router, FRF(t, WS_X1), b->g_ffn, QF(BW_DX1), QB(SV_DX1) + (size_t)t * NDs, QF(BP_GF), s);
     // attention: dO = dx1 Wo, flash backward, dqkv (RoPE taken back), da = dqkv Wqkv
     {
       GemmParams a1 = dense_params(QB(SV_DX1) + (size_t)t * NDs, D, Q(TW_WO), nullptr, N, HD, D);
       a1.epi.out = Q(BW_DO);
       a1.epi.ldo = HD;
       x.gemm(a1, EPI_STORE, false, 1);
-      launch_attn_bwd_prep(W(WS_O), Q(BW_DO), N, H, T, QF(BW_DELTA), s);
-      launch_transpose_bf16(W(WS_Q), (int64_t)T * 128, 0, 1, 128, Q(BW_QT), (int64_t)128 * Tp, Tp, B * H, T, Tp, 128,
-                            128, s);
+      launch_attn_bwd_prep(FR(t, WS_O), Q(BW_DO), N, H, T, QF(BW_DELTA), s);
+      launch_transpose_bf16(FR(t, WS_Q), (int64_t)T * 128, 0, 1, 128, Q(BW_QT), (int64_t)128 * Tp, Tp, B * H, T, Tp,
+                            128, 128, s);
       launch_transpose_bf16(Q(BW_DO), (int64_t)T * HD, 128, H, HD, Q(BW_DOT), (int64_t)128 * Tp, Tp, B * H, T, Tp,
                             128, 128, s);
-      launch_transpose_bf16(W(WS_K), (int64_t)cap * 128, 0, 1, 128, Q(BW_KT), (int64_t)128 * cap, cap, B * G, T, cap,
-                            128, 128, s);
-      launch_transpose_bf16(W(WS_VT), (int64_t)128 * cap, 0, 1, cap, Q(BW_VN), (int64_t)cap * 128, 128, B * G, 128,
-                            128, cap, T, s);
-      launch_attn_bwd(W(WS_Q), W(WS_K), Q(BW_VN), Q(BW_DO), Q(BW_QT), Q(BW_DOT), Q(BW_KT), QF(BW_LSE), QF(BW_DELTA),
-                      QF(BW_GQ), QF(BW_GK), QF(BW_GV), B, H, G, T, Tp, cap, scale, s);
+      launch_transpose_bf16(FR(t, WS_K), (int64_t)cap * 128, 0, 1, 128, Q(BW_KT), (int64_t)128 * cap, cap, B * G, T,
+                            cap, 128, 128, s);
+      launch_transpose_bf16(FR(t, WS_VT), (int64_t)128 * cap, 0, 1, cap, Q(BW_VN), (int64_t)cap * 128, 128, B * G,
+                            128, 128, cap, T, s);
+      launch_attn_bwd(FR(t, WS_Q), FR(t, WS_K), Q(BW_VN), Q(BW_DO), Q(BW_QT), Q(BW_DOT), Q(BW_KT),
+                      lse_all + (size_t)t * N * H, QF(BW_DELTA), QF(BW_GQ), QF(BW_GK), QF(BW_GV), B, H, G, T, Tp, cap,
+                      scale, s);
       bf16_t* dqkv = QB(SV_DQKV) + (size_t)t * N * QKV;
       launch_qkv_bwd(QF(BW_GQ), QF(BW_GK), QF(BW_GV), b->rope_cos, b->rope_sin, B, T, H, G, dqkv, s);
       GemmParams a2 = dense_params(dqkv, QKV, Q(TW_WQKV), nullptr, N, D, QKV);
@@ -2043,43 +2030,63 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
       a2.epi.ldo = D;
       x.gemm(a2, EPI_STORE, false, 0);
     }
-    launch_head_bwd(N, D, eps, QF(BW_DX1), QF(BW_DA), WF(WS_C), b->g_attn, b->g_rec, hp, e, emb_t, ld, QF(BW_G), de,
-                    QF(BP_GA), QF(BP_GR), s);
+    launch_head_bwd(N, D, eps, QF(BW_DX1), QF(BW_DA), FRF(t, WS_C), b->g_attn, b->g_rec, hp, e, emb_t, ld, QF(BW_G),
+                    de, QF(BP_GA), QF(BP_GR), s);
   }
   HIP_TRY(hipMemcpyAsync(dh0, Q(BW_G), NDs * 4, hipMemcpyDeviceToDevice, s));
 
   // ---- weight gradients: one product per tensor over every loop's rows
-  auto wgrad = [&](const void* A, int64_t lda, const void* X, int64_t ldx, const int32_t* xrow, const int32_t* off,
-                   int64_t loop_rows, int rows, int groups, int Nc, int Kc, float* C, int64_t ldc, int64_t cg,
+  // (a_ls / x_ls: elements between consecutive loops' rows of each operand)
+  auto wgrad = [&](const void* A, int64_t lda, int64_t a_ls, const void* X, int64_t ldx, int64_t x_ls,
+                   const int32_t* off, int rows, int groups, int Nc, int Kc, float* C, int64_t ldc, int64_t cg,
                    int splits, int64_t css) {
-    WgradArgs a{A, lda, X, ldx, xrow, off, L, loop_rows, rows, groups, Nc, Kc, C, ldc, cg, splits, css, 0};
+    WgradArgs a{};
+    a.A = A;
+    a.lda = lda;
+    a.a_loop_stride = a_ls;
+    a.X = X;
+    a.ldx = ldx;
+    a.x_loop_stride = x_ls;
+    a.off = off;
+    a.n_loops = L;
+    a.rows = rows;
+    a.G = groups;
+    a.Nc = Nc;
+    a.Kc = Kc;
+    a.C = C;
+    a.ldc = ldc;
+    a.c_gstride = cg;
+    a.splits = splits;
+    a.c_split_stride = css;
     launch_wgrad(a, s);
   };
   float* gb = grad;
-  wgrad(Q(SV_DQKV), QKV, Q(SV_A), D, nullptr, nullptr, N, N, 1, QKV, D, gb + goff[RDT_W_WQ], D, 0, 1, 0);
-  wgrad(Q(SV_DX1), D, Q(SV_O), HD, nullptr, nullptr, N, N, 1, D, HD, gb + goff[RDT_W_WO], HD, 0, 1, 0);
+  const int64_t nd = (int64_t)N * D, nkd = (int64_t)NK * D;
+  wgrad(Q(SV_DQKV), QKV, (int64_t)N * QKV, FR(0, WS_A), D, fr_bf, nullptr, N, 1, QKV, D, gb + goff[RDT_W_WQ], D, 0,
+        1, 0);
+  wgrad(Q(SV_DX1), D, nd, FR(0, WS_O), HD, fr_bf, nullptr, N, 1, D, HD, gb + goff[RDT_W_WO], HD, 0, 1, 0);
   launch_router_wgrad(QF(SV_DZP), Q(SV_FPERM), QI(SV_OFF), L, NK, E, D, QF(BW_RWP), gb + goff[RDT_W_ROUTER], s);
-  wgrad(Q(SV_DGU), 2 * F, Q(SV_FPERM), D, nullptr, QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_GATE], D,
+  wgrad(Q(SV_DGU), 2 * F, (int64_t)NK * 2 * F, Q(SV_FPERM), D, nkd, QI(SV_OFF), 0, E, F, D, gb + goff[RDT_W_GATE], D,
         (int64_t)F * D, 1, 0);
-  wgrad(QB(SV_DGU) + F, 2 * F, Q(SV_FPERM), D, nullptr, QI(SV_OFF), NK, 0, E, F, D, gb + goff[RDT_W_UP], D,
-        (int64_t)F * D, 1, 0);
-  wgrad(Q(SV_DY), D, Q(SV_ACT), F, nullptr, QI(SV_OFF), NK, 0, E, D, F, gb + goff[RDT_W_DOWN], F, (int64_t)D * F, 1,
-        0);
+  wgrad(QB(SV_DGU) + F, 2 * F, (int64_t)NK * 2 * F, Q(SV_FPERM), D, nkd, QI(SV_OFF), 0, E, F, D, gb + goff[RDT_W_UP],
+        D, (int64_t)F * D, 1, 0);
+  wgrad(Q(SV_DY), D, nkd, FR(0, WS_ACT), F, fr_bf, QI(SV_OFF), 0, E, D, F, gb + goff[RDT_W_DOWN], F, (int64_t)D * F,
+        1, 0);
   for (int si = 0; si < S; ++si) {
     const bf16_t* dgus = QB(SV_DGUS) + (size_t)si * n_loops * N * 2 * F;
     const bf16_t* acts = QB(SV_ACTS) + (size_t)si * n_loops * N * F;
-    wgrad(dgus, 2 * F, Q(SV_F), D, nullptr, nullptr, N, N, 1, F, D, gb + goff[RDT_W_S_GATE] + (size_t)si * F * D, D,
-          0, 1, 0);
-    wgrad(dgus + F, 2 * F, Q(SV_F), D, nullptr, nullptr, N, N, 1, F, D, gb + goff[RDT_W_S_UP] + (size_t)si * F * D,
-          D, 0, 1, 0);
-    wgrad(Q(SV_DTAU), D, acts, F, nullptr, nullptr, N, N, 1, D, F, gb + goff[RDT_W_S_DOWN] + (size_t)si * D * F, F,
-          0, 1, 0);
+    wgrad(dgus, 2 * F, (int64_t)N * 2 * F, FR(0, WS_F), D, fr_bf, nullptr, N, 1, F, D,
+          gb + goff[RDT_W_S_GATE] + (size_t)si * F * D, D, 0, 1, 0);
+    wgrad(dgus + F, 2 * F, (int64_t)N * 2 * F, FR(0, WS_F), D, fr_bf, nullptr, N, 1, F, D,
+          gb + goff[RDT_W_S_UP] + (size_t)si * F * D, D, 0, 1, 0);
+    wgrad(Q(SV_DTAU), D, nd, acts, F, (int64_t)N * F, nullptr, N, 1, D, F, gb + goff[RDT_W_S_DOWN] + (size_t)si * D * F,
+          F, 0, 1, 0);
   }
   // depth-wise LoRA: split over the loops, then summed
-  const int64_t rD = (int64_t)r * D;
-  wgrad(Q(SV_WL), RDT_LORA_LD, Q(SV_G), D, nullptr, nullptr, N, N, 1, r, D, QF(BW_SPLIT), D, 0, L, rD);
+  const int64_t rD = (int64_t)r * D, nl = (int64_t)N * RDT_LORA_LD;
+  wgrad(Q(SV_WL), RDT_LORA_LD, nl, Q(SV_G), D, nd, nullptr, N, 1, r, D, QF(BW_SPLIT), D, 0, L, rD);
   launch_col_reduce(QF(BW_SPLIT), L, rD, (int)rD, gb + goff[RDT_W_LORA_B], 0, s);
-  wgrad(Q(SV_DV), RDT_LORA_LD, Q(SV_TAU), D, nullptr, nullptr, N, N, 1, r, D, QF(BW_SPLIT), D, 0, L, rD);
+  wgrad(Q(SV_DV), RDT_LORA_LD, nl, Q(SV_TAU), D, nd, nullptr, N, 1, r, D, QF(BW_SPLIT), D, 0, L, rD);
   launch_col_reduce(QF(BW_SPLIT), L, rD, (int)rD, gb + goff[RDT_W_LORA_DOWN], 0, s);
   for (int t = 0; t < L; ++t)
     launch_col_reduce(QF(BP_S) + (size_t)t * RDT_BWD_WAVES * RDT_LORA_LD, RDT_BWD_WAVES, RDT_LORA_LD, r,
@@ -2099,13 +2106,6 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   return RDT_OK;
 }
 
-rdt_status rdt_get_router_bias(const rdt_block* b, float* bias_host) {
-  g_err.clear();
-  if (!b || !bias_host) return fail(RDT_E_INVALID_ARG, "NULL argument");
-  HIP_TRY(hipMemcpy(bias_host, b->router_bias, (size_t)b->cfg.n_experts * 4, hipMemcpyDeviceToHost));
-  return RDT_OK;
-}
-
 rdt_status rdt_router_bias_update(rdt_block* b, const int32_t* expert_load, float gamma, void* stream) {
   g_err.clear();
   if (!b || !expert_load) return fail(RDT_E_INVALID_ARG, "NULL argument");
@@ -2115,5 +2115,13 @@ rdt_status rdt_router_bias_update(rdt_block* b, const int32_t* expert_load, floa
   if (he != hipSuccess) return fail(RDT_E_HIP, "kernel launch: %s", hipGetErrorString(he));
   return RDT_OK;
 }
+
+rdt_status rdt_get_router_bias(const rdt_block* b, float* bias_host) {
+  g_err.clear();
+  if (!b || !bias_host) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  HIP_TRY(hipMemcpy(bias_host, b->router_bias, (size_t)b->cfg.n_experts * 4, hipMemcpyDeviceToHost));
+  return RDT_OK;
+}
+
 
 }  // extern "C"

@@ -55,7 +55,7 @@ def _run(cfg, W, e, h0, seed=5):
     blk.set_capture(None, cap_sel, None, L)
     e_d = torch.from_numpy(np.ascontiguousarray(e)).cuda()
     h_d = torch.from_numpy(np.ascontiguousarray(h0)).cuda()
-    tape = torch.empty(blk.train_tape_bytes(B, T, L) // 4, dtype=torch.float32, device="cuda")
+    tape = blk.new_tape(B, T, L)
     out, halt = blk.train_forward(e_d, h_d, L, thr, tape)
     dy = np.random.default_rng(seed).standard_normal(e.shape).astype(np.float32)
     dy_d = torch.from_numpy(dy).cuda()
