@@ -477,20 +477,42 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const bf16_t* __rest
   Dq[((int64_t)b * H + h) * T + i] = s;
 }
 
+// global -> LDS copy of 16 bytes per lane into the 1 KB window at lds (lane
+// i fills bytes 16 i .. 16 i + 15), as asm so the compiler adds no wait of
+// its own before later LDS reads: the kernels wait explicitly before the
+// barrier that publishes a buffer.
+__device__ __forceinline__ void dma16(const void* src, const void* lds) {
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m) : "memory", "m0");
+}
+
+// Row tiles [row][16 chunks of 8 d] keep chunk c at c ^ rswz(row): the
+// lanes of a quarter-wave read rows in the permuted order of kperm, which
+// this sends to 16 distinct positions.  Transposed tiles [d][8 chunks of 8]
+// keep chunk c at c ^ tswz(d).
+__device__ __forceinline__ int rswz(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
+__device__ __forceinline__ int tswz(int d) { return (d >> 1) & 7; }
+// score row read by lane i of a 32-row block: lane half h of the result
+// then holds rows 16 h .. 16 h + 15 in order
+__device__ __forceinline__ int kperm(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
 // one block per (key tile of 128 keys, b, kv head g); wave w owns keys
-// 32 w .. 32 w + 31 of the tile with dK and dV for all 128 d in registers,
-// and walks the query tiles at and after its keys for every query head of
-// the group.
+// 32 w .. 32 w + 31 of the tile with dK and dV for all 128 d in registers
+// and walks the 64-query tiles at and after its keys for every query head
+// of the group.  The next query tile streams into the other LDS buffer
+// while the current one is used.
+struct alignas(16) DkdvBuf {
+  uint4 q[AQ * 16], dO[AQ * 16], qt[128 * 8], dOt[128 * 8];
+  float L[AQ], Dl[AQ];
+};
+
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dO, const bf16_t* __restrict__ qt, const bf16_t* __restrict__ dOt,
     const float* __restrict__ lse2, const float* __restrict__ Dq, float* __restrict__ dK, float* __restrict__ dV,
     int B, int H, int G, int T, int Tp, int cap, float scale_log2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[AQ * LQ];
-  __shared__ __attribute__((aligned(16))) bf16_t sdO[AQ * LQ];
-  __shared__ __attribute__((aligned(16))) bf16_t sQt[128 * LT];
-  __shared__ __attribute__((aligned(16))) bf16_t sdOt[128 * LT];
-  __shared__ float sL[AQ], sD[AQ];
+  __shared__ DkdvBuf buf[2];
   const int BG = B * G, kt = blockIdx.x / BG, bg = blockIdx.x - kt * BG;
   const int b = bg / G, g = bg - b * G, rep = H / G;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
@@ -515,77 +537,93 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) accK[i][e] = accV[i][e] = 0.f;
-  const int nqt = (T + AQ - 1) / AQ;
-  for (int hr = 0; hr < rep; ++hr) {
-    const int h = g * rep + hr;
+  const int nqt = (T + AQ - 1) / AQ, qt0 = (kt * 128) / AQ, nq = nqt - qt0, ntile = rep * nq;
+  float Lr = 0.f, Dr = 0.f;
+  // issue tile i (query head g rep + i / nq, query tile qt0 + i % nq) into buffer bb
+  auto issue = [&](int i, int bb) {
+    const int h = g * rep + i / nq, q0 = (qt0 + i % nq) * AQ;
     const bf16_t* qh = q + (int64_t)(b * H + h) * T * 128;
     const bf16_t* qth = qt + (int64_t)(b * H + h) * 128 * Tp;
     const bf16_t* dOth = dOt + (int64_t)(b * H + h) * 128 * Tp;
-    const float* Lh = lse2 + (int64_t)(b * H + h) * T;
-    const float* Dh = Dq + (int64_t)(b * H + h) * T;
-    for (int qti = (kt * 128) / AQ; qti < nqt; ++qti) {
-      const int q0 = qti * AQ;
-      __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = tid + 256 * j;
-        const int row = idx >> 4, ch = idx & 15, qq = q0 + row;
-        uint4 a = uint4{0u, 0u, 0u, 0u}, c = a;
-        if (qq < T) {
-          a = *(const uint4*)(qh + (int64_t)qq * 128 + ch * 8);
-          c = *(const uint4*)(dO + ((int64_t)(b * T + qq) * H + h) * 128 + ch * 8);
-        }
-        *(uint4*)&sQ[row * LQ + ch * 8] = a;
-        *(uint4*)&sdO[row * LQ + ch * 8] = c;
-        const int d = idx >> 3, c8 = idx & 7;
-        *(uint4*)&sQt[d * LT + c8 * 8] = *(const uint4*)(qth + (int64_t)d * Tp + q0 + c8 * 8);
-        *(uint4*)&sdOt[d * LT + c8 * 8] = *(const uint4*)(dOth + (int64_t)d * Tp + q0 + c8 * 8);
-      }
-      if (tid < AQ) {
-        const int qq = q0 + tid;
-        sL[tid] = qq < T ? Lh[qq] : 0.f;
-        sD[tid] = qq < T ? Dh[qq] : 0.f;
-      }
-      __syncthreads();
-      if (kw0 > q0 + AQ - 1) continue;   // every query of the tile precedes this wave's keys
+    for (int j = 0; j < 4; ++j) {
+      const int sl = (j * 4 + w) * 64 + lane;
+      const int row = sl >> 4, lc = (sl & 15) ^ rswz(row), qq = min(q0 + row, T - 1);
+      dma16(qh + (int64_t)qq * 128 + lc * 8, &buf[bb].q[(j * 4 + w) * 64]);
+      dma16(dO + ((int64_t)(b * T + qq) * H + h) * 128 + lc * 8, &buf[bb].dO[(j * 4 + w) * 64]);
+      const int d = sl >> 3, tc = (sl & 7) ^ tswz(d);
+      dma16(qth + (int64_t)d * Tp + q0 + tc * 8, &buf[bb].qt[(j * 4 + w) * 64]);
+      dma16(dOth + (int64_t)d * Tp + q0 + tc * 8, &buf[bb].dOt[(j * 4 + w) * 64]);
+    }
+    if (tid < AQ) {
+      const int qq = q0 + tid;
+      const int64_t o = (int64_t)(b * H + h) * T + qq;
+      Lr = qq < T ? lse2[o] : 0.f;
+      Dr = qq < T ? Dq[o] : 0.f;
+    }
+  };
+  if (ntile > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (tid < AQ) {
+    buf[0].L[tid] = Lr;
+    buf[0].Dl[tid] = Dr;
+  }
+  __syncthreads();
+  const int myrow = kperm(lane & 31);
+  for (int i = 0; i < ntile; ++i) {
+    const int bb = i & 1;
+    if (i + 1 < ntile) issue(i + 1, bb ^ 1);
+    const int q0 = (qt0 + i % nq) * AQ;
+    const DkdvBuf& cb = buf[bb];
+    if (kw0 <= q0 + AQ - 1) {   // else every query of the tile precedes this wave's keys
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         floatx16_t S, dP;
 #pragma unroll
         for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
-        const int qrow = qb * 32 + (lane & 31);
+        const int qrow = qb * 32 + myrow;
 #pragma unroll
         for (int ds = 0; ds < 8; ++ds) {
-          const bf16x8_t qa = *(const bf16x8_t*)&sQ[qrow * LQ + 16 * ds + 8 * half];
-          const bf16x8_t da = *(const bf16x8_t*)&sdO[qrow * LQ + 16 * ds + 8 * half];
-          S = mfma32(qa, kf[ds], S);
-          dP = mfma32(da, vf[ds], dP);
+          const int pc = (2 * ds + half) ^ rswz(qrow);
+          S = mfma32(as_frag(cb.q[qrow * 16 + pc]), kf[ds], S);
+          dP = mfma32(as_frag(cb.dO[qrow * 16 + pc]), vf[ds], dP);
         }
+        // this lane: key kl, queries q0 + 32 qb + 16 half + r
+        const int qbase = qb * 32 + 16 * half;
         float p[16], dsv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = qb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int qq = q0 + ql;
-          const bool ok = qq < T && kl <= qq && kl < T;
-          const float pr = ok ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - sL[ql]) : 0.f;
-          p[r] = pr;
-          dsv[r] = pr * (dP[r] - sD[ql]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 L4 = *(const float4*)&cb.L[qbase + 4 * r4];
+          const float4 D4 = *(const float4*)&cb.Dl[qbase + 4 * r4];
+          const float Ls[4] = {L4.x, L4.y, L4.z, L4.w}, Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int r = 4 * r4 + x, qq = q0 + qbase + r;
+            const bool ok = qq < T && kl <= qq && kl < T;
+            const float pr = ok ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - Ls[x]) : 0.f;
+            p[r] = pr;
+            dsv[r] = pr * (dP[r] - Ds[x]);
+          }
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const bf16x8_t pa = pack8(p + 8 * ks), sa = pack8(dsv + 8 * ks);
-          const int qo = qb * 32 + 16 * ks + 4 * half;
+          const int lc = 4 * qb + 2 * half + ks;
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            const int d = db * 32 + (lane & 31);
-            const uint2 o0 = *(const uint2*)&sdOt[d * LT + qo], o1 = *(const uint2*)&sdOt[d * LT + qo + 8];
-            const uint2 t0 = *(const uint2*)&sQt[d * LT + qo], t1 = *(const uint2*)&sQt[d * LT + qo + 8];
-            accV[db] = mfma32(pa, as_frag(uint4{o0.x, o0.y, o1.x, o1.y}), accV[db]);
-            accK[db] = mfma32(sa, as_frag(uint4{t0.x, t0.y, t1.x, t1.y}), accK[db]);
+            const int d = db * 32 + (lane & 31), pc = lc ^ tswz(d);
+            accV[db] = mfma32(pa, as_frag(cb.dOt[d * 8 + pc]), accV[db]);
+            accK[db] = mfma32(sa, as_frag(cb.qt[d * 8 + pc]), accK[db]);
           }
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (i + 1 < ntile && tid < AQ) {
+      buf[bb ^ 1].L[tid] = Lr;
+      buf[bb ^ 1].Dl[tid] = Dr;
+    }
+    __syncthreads();
   }
   float* dKb = dK + (int64_t)bg * T * 128;
   float* dVb = dV + (int64_t)bg * T * 128;
@@ -603,15 +641,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 }
 
 // one block per (query tile of 128, b, head h); wave w owns queries
-// 32 w .. 32 w + 31 and walks the key tiles up to its diagonal
+// 32 w .. 32 w + 31 and walks the 64-key tiles up to its diagonal, the
+// next tile streaming into the other LDS buffer
+struct alignas(16) DqBuf {
+  uint4 k[AQ * 16], v[AQ * 16], kt[128 * 8];
+};
+
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dO, const bf16_t* __restrict__ kt, const float* __restrict__ lse2,
     const float* __restrict__ Dq, float* __restrict__ dQ, int B, int H, int G, int T, int cap, float scale_log2,
     float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[AQ * LQ];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[AQ * LQ];
-  __shared__ __attribute__((aligned(16))) bf16_t sKt[128 * LT];
+  __shared__ DqBuf buf[2];
   const int BH = B * H, nqt = (T + 127) / 128;
   const int qti = nqt - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
   const int b = bh / H, h = bh - b * H, g = h / (H / G);
@@ -619,15 +660,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int qw0 = qti * 128 + w * 32, ql = qw0 + (lane & 31);
   bf16x8_t qf[8], df[8];
   {
-    const bf16_t* qr = q + ((int64_t)bh * T + ql) * 128;
-    const bf16_t* dr = dO + ((int64_t)(b * T + ql) * H + h) * 128;
+    const bf16_t* qr = q + ((int64_t)bh * T + min(ql, T - 1)) * 128;
+    const bf16_t* dr = dO + ((int64_t)(b * T + min(ql, T - 1)) * H + h) * 128;
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
-      uint4 a = uint4{0u, 0u, 0u, 0u}, c = a;
-      if (ql < T) {
-        a = *(const uint4*)(qr + 16 * ds + 8 * half);
-        c = *(const uint4*)(dr + 16 * ds + 8 * half);
-      }
+      uint4 a = *(const uint4*)(qr + 16 * ds + 8 * half), c = *(const uint4*)(dr + 16 * ds + 8 * half);
+      if (ql >= T) a = c = uint4{0u, 0u, 0u, 0u};
       qf[ds] = as_frag(a);
       df[ds] = as_frag(c);
     }
@@ -645,58 +683,63 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const bf16_t* ktb = kt + (int64_t)bg * 128 * cap;
   const int kend = min(T, qti * 128 + 128);
   const int nkt = (kend + AQ - 1) / AQ;
-  for (int kti = 0; kti < nkt; ++kti) {
-    const int k0 = kti * AQ;
-    __syncthreads();
+  auto issue = [&](int i, int bb) {
+    const int k0 = i * AQ;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int idx = tid + 256 * j;
-      const int row = idx >> 4, ch = idx & 15, kk = k0 + row;
-      uint4 a = uint4{0u, 0u, 0u, 0u}, c = a;
-      if (kk < T) {
-        a = *(const uint4*)(kb + (int64_t)kk * 128 + ch * 8);
-        c = *(const uint4*)(vb + (int64_t)kk * 128 + ch * 8);
-      }
-      *(uint4*)&sK[row * LQ + ch * 8] = a;
-      *(uint4*)&sV[row * LQ + ch * 8] = c;
-      const int d = idx >> 3, c8 = idx & 7;
-      *(uint4*)&sKt[d * LT + c8 * 8] = *(const uint4*)(ktb + (int64_t)d * cap + k0 + c8 * 8);
+      const int sl = (j * 4 + w) * 64 + lane;
+      const int row = sl >> 4, lc = (sl & 15) ^ rswz(row);
+      dma16(kb + (int64_t)(k0 + row) * 128 + lc * 8, &buf[bb].k[(j * 4 + w) * 64]);
+      dma16(vb + (int64_t)(k0 + row) * 128 + lc * 8, &buf[bb].v[(j * 4 + w) * 64]);
+      const int d = sl >> 3, tc = (sl & 7) ^ tswz(d);
+      dma16(ktb + (int64_t)d * cap + k0 + tc * 8, &buf[bb].kt[(j * 4 + w) * 64]);
     }
-    __syncthreads();
-    if (k0 > qw0 + 31) continue;   // every key of the tile follows this wave's queries
+  };
+  if (nkt > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int myrow = kperm(lane & 31);
+  for (int i = 0; i < nkt; ++i) {
+    const int bb = i & 1;
+    if (i + 1 < nkt) issue(i + 1, bb ^ 1);
+    const int k0 = i * AQ;
+    const DqBuf& cb = buf[bb];
+    if (k0 <= qw0 + 31) {   // else every key of the tile follows this wave's queries
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      floatx16_t S, dP;
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        floatx16_t S, dP;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
-      const int krow = kb2 * 32 + (lane & 31);
+        for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
+        const int krow = kb2 * 32 + myrow;
 #pragma unroll
-      for (int ds = 0; ds < 8; ++ds) {
-        const bf16x8_t ka = *(const bf16x8_t*)&sK[krow * LQ + 16 * ds + 8 * half];
-        const bf16x8_t va = *(const bf16x8_t*)&sV[krow * LQ + 16 * ds + 8 * half];
-        S = mfma32(ka, qf[ds], S);
-        dP = mfma32(va, df[ds], dP);
-      }
-      float dsv[16];
+        for (int ds = 0; ds < 8; ++ds) {
+          const int pc = (2 * ds + half) ^ rswz(krow);
+          S = mfma32(as_frag(cb.k[krow * 16 + pc]), qf[ds], S);
+          dP = mfma32(as_frag(cb.v[krow * 16 + pc]), df[ds], dP);
+        }
+        // this lane: query ql, keys k0 + 32 kb2 + 16 half + r
+        float dsv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + kb2 * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool ok = ql < T && key <= ql;
-        const float pr = ok ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - Lq) : 0.f;
-        dsv[r] = pr * (dP[r] - Dqq);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb2 * 32 + 16 * half + r;
+          const bool ok = ql < T && key <= ql;
+          const float pr = ok ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - Lq) : 0.f;
+          dsv[r] = pr * (dP[r] - Dqq);
+        }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t sa = pack8(dsv + 8 * ks);
-        const int ko = kb2 * 32 + 16 * ks + 4 * half;
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8_t sa = pack8(dsv + 8 * ks);
+          const int lc = 4 * kb2 + 2 * half + ks;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int d = db * 32 + (lane & 31);
-          const uint2 t0 = *(const uint2*)&sKt[d * LT + ko], t1 = *(const uint2*)&sKt[d * LT + ko + 8];
-          acc[db] = mfma32(sa, as_frag(uint4{t0.x, t0.y, t1.x, t1.y}), acc[db]);
+          for (int db = 0; db < 4; ++db) {
+            const int d = db * 32 + (lane & 31), pc = lc ^ tswz(d);
+            acc[db] = mfma32(sa, as_frag(cb.kt[d * 8 + pc]), acc[db]);
+          }
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
   float* dQb = dQ + (int64_t)bh * T * 128;
 #pragma unroll
