@@ -156,6 +156,27 @@ def train_flops(cfg, loops):
     return loops * (fwd + 2 * (fwd - att) + 2 * att)
 
 
+def train_cpu_baseline(cfg, W, e, h0, prefix):
+    """The gradient oracle as it stands (fp64 autograd, the forward's
+    decisions taken by the numpy oracle) on the first `prefix` tokens of the
+    first sequence for one loop: a bounded sample of the training step."""
+    import numpy as np
+    from oracle import rdt_backward as OB
+    from oracle import rdt_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    sub = dict(cfg, batch=1, seq=prefix)
+    P = O.Params(W)
+    t0 = time.perf_counter()
+    r = O.recurrent_forward(sub, P, e[:1, :prefix], h0[:1, :prefix], 1, cfg["act_threshold"], record=True)
+    dy = np.random.default_rng(5).standard_normal((1, prefix, cfg["dim"]))
+    OB.recurrent_grad(sub, P, e[:1, :prefix], h0[:1, :prefix], 1, cfg["act_threshold"],
+                      np.stack(r["record"]["sel"]), r["halt_counts"], dy)
+    dt = time.perf_counter() - t0
+    return dict(value=round(prefix / dt, 3), unit="trained token·loops/s", cores=cores, kind="oracle",
+                sample=f"forward and gradient of 1 loop over the first {prefix} tokens of sequence 0 "
+                       f"({prefix} token-loops, {dt:.1f} s, every block weight in fp64 with its gradient)")
+
+
 def train_bench(args, cfg):
     import threading
 
@@ -194,6 +215,10 @@ def train_bench(args, cfg):
     clocks, stop = [], threading.Event()
     sampler = threading.Thread(target=sample_sclk, args=(stop, clocks), daemon=True)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # the dominant kernel (the routed experts' weight-gradient launches) is
+    # bracketed with HIP events by the library on the launch stream
+    dom = "train_expert_wgrad"
+    blk.set_timing_stages([dom, "train_attn_bwd"])
     torch.cuda.synchronize()
     if not args.no_clock:
         sampler.start()
@@ -209,11 +234,35 @@ def train_bench(args, cfg):
     if not args.no_clock:
         sampler.join(timeout=15)
     step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    tm = blk.read_timing()
+    blk.set_timing(False)
     halt = hc.cpu().numpy()
     loops = int(halt.max()) if thr > 0 else L
     value = B * T * loops * args.steps / elapsed
     fl = train_flops(cfg, loops)
     ms_step = elapsed / args.steps * 1e3
+    # roofline of the dominant kernel: one launch is the weight gradient of
+    # one routed matrix (gate, up or down) over every loop's rows,
+    # 2 * (loops * N * k) * F * D flops
+    N, k, F = B * T, cfg["top_k"], cfg["expert_dim"]
+    wg_flops = 2.0 * loops * N * k * F * D
+    wg_ms, wg_n = tm[dom]
+    wg_avg = wg_ms / max(wg_n, 1)
+    at_ms, at_n = tm["train_attn_bwd"]
+    at_flops = 2 * stage_work(cfg)["attention"]["flops"]
+    roof = dict(bound="mfma", achieved=round(wg_flops / (wg_avg * 1e-3) / 1e12, 2), peak=PEAK_BF16_TFLOPS,
+                unit="TFLOP/s", traffic=None,
+                kernel="routed experts' weight-gradient product (wgrad8_kernel, one routed matrix over every loop's rows)",
+                per_launch_flops=wg_flops, avg_launch_ms=round(wg_avg, 4), launches=wg_n)
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    attn = dict(avg_launch_ms=round(at_ms / max(at_n, 1), 4), launches=at_n,
+                tflops=round(at_flops / (at_ms / max(at_n, 1) * 1e-3) / 1e12, 1))
+    log(f"[bench] expert wgrad {wg_avg:.3f} ms/launch ({roof['achieved']} TFLOP/s), attention backward "
+        f"{attn['avg_launch_ms']} ms/loop ({attn['tflops']} TFLOP/s)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = train_cpu_baseline(cfg, W, e, h0, min(args.cpu_prefix, 256))
+        log(f"[bench] cpu baseline: {cpu}")
     out = {
         "metric": "recurrent-block training token·loops/sec (1 GPU; forward + backward)", "value": round(value, 1),
         "unit": "token·loops/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -227,6 +276,9 @@ def train_bench(args, cfg):
         "algorithmic_tflops_per_step": round(fl / 1e12, 1),
         "achieved_tflops": round(fl / (ms_step * 1e-3) / 1e12, 1),
         "mfma_frac_of_step": round(fl / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "attention_backward": attn,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

@@ -411,7 +411,11 @@ rdt_status rdt_workspace_offset(const rdt_block* blk, int32_t B, int32_t T, cons
 enum rdt_stage {
   RDT_STAGE_LOOP_HEAD = 0, RDT_STAGE_QKV, RDT_STAGE_ATTN, RDT_STAGE_OPROJ, RDT_STAGE_FFN_NORM,
   RDT_STAGE_ROUTER, RDT_STAGE_DISPATCH, RDT_STAGE_EXPERT_GATEUP, RDT_STAGE_EXPERT_DOWN,
-  RDT_STAGE_SHARED_GATEUP, RDT_STAGE_SHARED_DOWN, RDT_STAGE_TAIL, RDT_STAGE_COUNT
+  RDT_STAGE_SHARED_GATEUP, RDT_STAGE_SHARED_DOWN, RDT_STAGE_TAIL,
+  /* rdt_train_backward: the routed experts' weight-gradient products (three
+   * launches: gate, up, down) and the attention backward (per loop) */
+  RDT_STAGE_TRAIN_EXPERT_WGRAD, RDT_STAGE_TRAIN_ATTN_BWD,
+  RDT_STAGE_COUNT
 };
 rdt_status rdt_set_timing(rdt_block* blk, int32_t enable);
 rdt_status rdt_set_timing_stages(rdt_block* blk, uint32_t stage_mask);

@@ -20,7 +20,7 @@ STATUS = {0: "RDT_OK", 1: "RDT_E_INVALID_ARG", 2: "RDT_E_UNSUPPORTED", 3: "RDT_E
           4: "RDT_E_HIP", 5: "RDT_E_BAD_STATE", 6: "RDT_E_WORKSPACE_TOO_SMALL"}
 
 STAGES = ["loop_head", "qkv", "attention", "o_proj", "ffn_norm", "router", "dispatch", "expert_gate_up",
-          "expert_down", "shared_gate_up", "shared_down", "tail"]
+          "expert_down", "shared_gate_up", "shared_down", "tail", "train_expert_wgrad", "train_attn_bwd"]
 
 WEIGHT_NAMES = ["g_rec", "g_attn", "g_ffn", "wq", "wk", "wv", "wo", "wdq", "gq", "wuq", "wdkv", "gkv", "wukv",
                 "router_w", "router_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",

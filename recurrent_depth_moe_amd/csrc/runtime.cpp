@@ -2020,9 +2020,12 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
                             cap, 128, 128, s);
       launch_transpose_bf16(FR(t, WS_VT), (int64_t)128 * cap, 0, 1, cap, Q(BW_VN), (int64_t)cap * 128, 128, B * G,
                             128, 128, cap, T, s);
-      launch_attn_bwd(FR(t, WS_Q), FR(t, WS_K), Q(BW_VN), Q(BW_DO), Q(BW_QT), Q(BW_DOT), Q(BW_KT),
-                      lse_all + (size_t)t * N * H, QF(BW_DELTA), QF(BW_GQ), QF(BW_GK), QF(BW_GV), B, H, G, T, Tp, cap,
-                      scale, s);
+      {
+        StageTimer st_(b, s, RDT_STAGE_TRAIN_ATTN_BWD);
+        launch_attn_bwd(FR(t, WS_Q), FR(t, WS_K), Q(BW_VN), Q(BW_DO), Q(BW_QT), Q(BW_DOT), Q(BW_KT),
+                        lse_all + (size_t)t * N * H, QF(BW_DELTA), QF(BW_GQ), QF(BW_GK), QF(BW_GV), B, H, G, T, Tp,
+                        cap, scale, s);
+      }
       bf16_t* dqkv = QB(SV_DQKV) + (size_t)t * N * QKV;
       launch_qkv_bwd(QF(BW_GQ), QF(BW_GK), QF(BW_GV), b->rope_cos, b->rope_sin, B, T, H, G, dqkv, s);
       GemmParams a2 = dense_params(dqkv, QKV, Q(TW_WQKV), nullptr, N, D, QKV);
@@ -2066,12 +2069,21 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
         1, 0);
   wgrad(Q(SV_DX1), D, nd, FR(0, WS_O), HD, fr_bf, nullptr, N, 1, D, HD, gb + goff[RDT_W_WO], HD, 0, 1, 0);
   launch_router_wgrad(QF(SV_DZP), Q(SV_FPERM), QI(SV_OFF), L, NK, E, D, QF(BW_RWP), gb + goff[RDT_W_ROUTER], s);
-  wgrad(Q(SV_DGU), 2 * F, (int64_t)NK * 2 * F, Q(SV_FPERM), D, nkd, QI(SV_OFF), 0, E, F, D, gb + goff[RDT_W_GATE], D,
-        (int64_t)F * D, 1, 0);
-  wgrad(QB(SV_DGU) + F, 2 * F, (int64_t)NK * 2 * F, Q(SV_FPERM), D, nkd, QI(SV_OFF), 0, E, F, D, gb + goff[RDT_W_UP],
-        D, (int64_t)F * D, 1, 0);
-  wgrad(Q(SV_DY), D, nkd, FR(0, WS_ACT), F, fr_bf, QI(SV_OFF), 0, E, D, F, gb + goff[RDT_W_DOWN], F, (int64_t)D * F,
-        1, 0);
+  {
+    StageTimer st_(b, s, RDT_STAGE_TRAIN_EXPERT_WGRAD);
+    wgrad(Q(SV_DGU), 2 * F, (int64_t)NK * 2 * F, Q(SV_FPERM), D, nkd, QI(SV_OFF), 0, E, F, D, gb + goff[RDT_W_GATE],
+          D, (int64_t)F * D, 1, 0);
+  }
+  {
+    StageTimer st_(b, s, RDT_STAGE_TRAIN_EXPERT_WGRAD);
+    wgrad(QB(SV_DGU) + F, 2 * F, (int64_t)NK * 2 * F, Q(SV_FPERM), D, nkd, QI(SV_OFF), 0, E, F, D,
+          gb + goff[RDT_W_UP], D, (int64_t)F * D, 1, 0);
+  }
+  {
+    StageTimer st_(b, s, RDT_STAGE_TRAIN_EXPERT_WGRAD);
+    wgrad(Q(SV_DY), D, nkd, FR(0, WS_ACT), F, fr_bf, QI(SV_OFF), 0, E, D, F, gb + goff[RDT_W_DOWN], F,
+          (int64_t)D * F, 1, 0);
+  }
   for (int si = 0; si < S; ++si) {
     const bf16_t* dgus = QB(SV_DGUS) + (size_t)si * n_loops * N * 2 * F;
     const bf16_t* acts = QB(SV_ACTS) + (size_t)si * n_loops * N * F;
