@@ -1597,7 +1597,7 @@ enum BwId {
   SV_DQKV, SV_DX1, SV_FPERM, SV_OFF, SV_DZP, SV_DGU, SV_DY, SV_ACTS, SV_DGUS, SV_DTAU, SV_G, SV_TAU, SV_WL, SV_DV,
   // working buffers of one loop
   BW_G, BW_DX1, BW_DF, BW_DA, BW_DZ, BW_GU, BW_DACT, BW_DFP, BW_GUS, BW_DACTS, BW_DO, BW_DELTA, BW_QT, BW_DOT, BW_KT,
-  BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD, BW_RWP,
+  BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD, BW_RWP, BW_TCLAIM,
   // per-wave partial column sums (contiguous: cleared together)
   BP_A, BP_B, BP_GF, BP_GA, BP_GR, BP_HW, BP_HB, BP_S,
   // transposed weights
@@ -1665,6 +1665,7 @@ BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   s[BW_LV] = s[BW_LDW] = N * r * 4;
   s[BW_DVPAD] = N * 64 * 2;
   s[BW_RWP] = RDT_ROUTER_WGRAD_PART(E, D) * 4;
+  s[BW_TCLAIM] = Ls * 4 * RDT_NUM_XCD * 4;   // tile-claim counters of the four grouped products of each loop
   s[BP_A] = s[BP_B] = s[BP_GF] = s[BP_GA] = s[BP_GR] = s[BP_HW] = W * D * 4;
   s[BP_HB] = W * 4;
   s[BP_S] = Ls * W * RDT_LORA_LD * 4;
@@ -1829,6 +1830,9 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   launch_fill_zero(de, NDs * 4, s);
   launch_fill_zero(load, (size_t)E * 4, s);
   launch_fill_zero(Q(BP_A), q.off[BP_S] + q.size[BP_S] - q.off[BP_A], s);
+  launch_fill_zero(Q(BW_TCLAIM), q.size[BW_TCLAIM], s);
+  // grouped product j of loop t claims its tiles from counters that start at 0
+  auto claim = [&](int t, int j) { return QI(BW_TCLAIM) + ((size_t)t * 4 + j) * RDT_NUM_XCD; };
   // transposed weights: W^T of every product whose input gradient is taken
   {
     const bf16_t* wqkv = (const bf16_t*)b->wqkv;
@@ -1884,9 +1888,11 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
     gp.n_groups = E;
     gp.epi.out = Q(BW_GU);
     gp.epi.ldo = 2 * F;
+    gp.tile_ctr = claim(t, 0);
     launch_gemm_bf16_big(gp, EPI_STORE, false, 1, b->n_cu, s, 256);
     gp.W0 = b->w_up;
     gp.epi.out = QB(BW_GU) + F;
+    gp.tile_ctr = claim(t, 1);
     launch_gemm_bf16_big(gp, EPI_STORE, false, 1, b->n_cu, s, 256);
     for (int si = 0; si < S; ++si) {
       bf16_t* gus = QB(BW_GUS) + (size_t)si * N * 2 * F;
@@ -1989,6 +1995,7 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
       r1.epi = EpiParams{};
       r1.epi.out = QF(BW_DACT);
       r1.epi.ldo = F;
+      r1.tile_ctr = claim(t, 2);
       launch_gemm_bf16_big(r1, EPI_STORE, false, 0, b->n_cu, s, 256);
       bf16_t* dgu = QB(SV_DGU) + (size_t)t * NK * 2 * F;
       launch_swiglu_bwd(Q(BW_GU), QF(BW_DACT), NK, F, dgu, s);
@@ -2001,6 +2008,7 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
       r2.K = 2 * F;
       r2.epi.out = QF(BW_DFP);
       r2.epi.ldo = D;
+      r2.tile_ctr = claim(t, 3);
       launch_gemm_bf16_big(r2, EPI_STORE, false, 0, b->n_cu, s, 256);
     }
     launch_ffn_norm_bwd(N, D, k, eps, S ? QF(BW_DF) : nullptr, QF(BW_DFP), FRI(t, WS_INV), FRI(t, WS_SEL), QF(BW_DZ),
