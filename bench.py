@@ -145,6 +145,36 @@ def cpu_baseline(cfg, W, e, h0, prefix):
                        f"({cfg['batch'] * prefix} token-loops, {dt:.1f} s)")
 
 
+TRAIN_PROFILE = os.path.join(ROOT, "profiles", "counters_{}_train_step.md")
+BACKWARD_SOURCES = ["backward.hip", "backward.h", "common.h"]
+
+
+def train_traffic(config):
+    """HBM bytes per launch of the experts' weight-gradient product
+    (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated) from the committed
+    counter summary, or None when it was taken on other backward sources."""
+    import hashlib
+    path = TRAIN_PROFILE.format(config)
+    if not os.path.exists(path):
+        return None
+    hsh = hashlib.sha256()
+    for name in BACKWARD_SOURCES:
+        with open(os.path.join(ROOT, "recurrent_depth_moe_amd", "csrc", name), "rb") as f:
+            hsh.update(f.read())
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, val = line.split(":", 1)
+                fields[k.strip()] = val.strip().strip("`")
+    if fields.get("kernel_source_sha256") != hsh.hexdigest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch_expert_wgrad"])
+    except (KeyError, ValueError):
+        return None
+
+
 def train_flops(cfg, loops):
     """Algorithmic flops of one training step: the forward, then per loop the
     input-gradient and weight-gradient products (each the forward product's
@@ -251,7 +281,7 @@ def train_bench(args, cfg):
     at_ms, at_n = tm["train_attn_bwd"]
     at_flops = 2 * stage_work(cfg)["attention"]["flops"]
     roof = dict(bound="mfma", achieved=round(wg_flops / (wg_avg * 1e-3) / 1e12, 2), peak=PEAK_BF16_TFLOPS,
-                unit="TFLOP/s", traffic=None,
+                unit="TFLOP/s", traffic=train_traffic(args.config),
                 kernel="routed experts' weight-gradient product (wgrad8_kernel, one routed matrix over every loop's rows)",
                 per_launch_flops=wg_flops, avg_launch_ms=round(wg_avg, 4), launches=wg_n)
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
