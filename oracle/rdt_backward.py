@@ -31,6 +31,11 @@ Readings of what the pages leave open:
     b_i <- b_i + gamma * sign(mean_load - load_i), with load_i the number of
     (position, slot) assignments to expert i summed over the step's loops
     and sign(0) = 0; the sum is formed in float32, the bias's storage type.
+  * Optimizer ([ZS §Tokenizer & training script]: the training script uses
+    AdamW): decoupled weight decay (Loshchilov & Hutter) with bias-corrected
+    moments, applied to every trained tensor with the same hyper-parameters,
+    on float32 master weights; the block's matrices are the masters rounded
+    to bfloat16 (nearest, ties to even).
 """
 
 import numpy as np
@@ -179,3 +184,25 @@ def router_bias_update(bias, load, gamma):
     E = len(load)
     direction = np.sign(load.sum() - E * load)          # sign(mean - load_i), exact in integers
     return (np.asarray(bias, dtype=np.float32) + np.float32(gamma) * direction.astype(np.float32)).astype(np.float32)
+
+
+def adamw_step(param, grad, m, v, step, lr, beta1, beta2, eps, weight_decay):
+    """One AdamW step (1-based step count): moments m, v updated with grad,
+    bias-corrected, and param <- param - lr (m_hat / (sqrt(v_hat) + eps) +
+    weight_decay param), the decay on the value before the step.  Returns
+    (param, m, v) as float64."""
+    param, grad = np.asarray(param, dtype=np.float64), np.asarray(grad, dtype=np.float64)
+    m = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * grad
+    v = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * grad * grad
+    m_hat = m / (1.0 - beta1 ** step)
+    v_hat = v / (1.0 - beta2 ** step)
+    return param - lr * (m_hat / (np.sqrt(v_hat) + eps) + weight_decay * param), m, v
+
+
+def round_bf16(x):
+    """float32 values rounded to bfloat16 bit patterns (nearest, ties to
+    even; NaN stays NaN)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    return np.where(nan, np.uint16(0x7FC0), r)

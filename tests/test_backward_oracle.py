@@ -128,3 +128,43 @@ def test_router_bias_balancing_rule():
     new = OB.router_bias_update(bias, [5, 3, 0, 4], 0.125)
     np.testing.assert_array_equal(new, np.array([0.375, -0.25, 0.125, 0.875], dtype=np.float32))
     assert OB.expert_load(np.array([[[0, 1], [1, 3]], [[3, 3], [0, 1]]]), 5).tolist() == [2, 3, 0, 3, 0]
+
+
+def test_adamw_matches_torch_over_several_steps():
+    """AdamW against torch.optim.AdamW (float64), three steps with weight
+    decay on random parameters and gradients."""
+    rng = np.random.default_rng(11)
+    p0 = rng.standard_normal((7, 5))
+    grads = [rng.standard_normal((7, 5)) * s for s in (1.0, 0.1, 3.0)]
+    hp = dict(lr=1e-2, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    tp = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+    opt = torch.optim.AdamW([tp], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"])
+    p, m, v = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+    for step, g in enumerate(grads, start=1):
+        tp.grad = torch.from_numpy(g.copy())
+        opt.step()
+        p, m, v = OB.adamw_step(p, g, m, v, step, **hp)
+        np.testing.assert_allclose(p, tp.detach().numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_adamw_first_step_closed_form():
+    """Step 1: m_hat = g and v_hat = g^2, so the update is lr g / (|g| + eps)
+    plus lr * weight_decay * p."""
+    g = np.array([2.0, -0.5, 1e-3, 0.0])
+    p = np.array([1.0, -2.0, 0.5, 3.0])
+    new, m, v = OB.adamw_step(p, g, 0 * g, 0 * g, 1, 0.1, 0.9, 0.999, 1e-8, 0.01)
+    np.testing.assert_allclose(new, p - 0.1 * (g / (np.abs(g) + 1e-8) + 0.01 * p), rtol=1e-12)
+    np.testing.assert_allclose(m, 0.1 * g, rtol=1e-15)
+    np.testing.assert_allclose(v, 0.001 * g * g, rtol=1e-12)
+
+
+def test_bf16_rounding_nearest_even():
+    """round_bf16 against torch's own float32 -> bfloat16 conversion on
+    random values, exact halfway cases (ties to even) and specials."""
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 10 ** rng.uniform(-5, 5, 10000),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0, -0.0, np.inf, -np.inf],
+                                 dtype=np.float32)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(OB.round_bf16(x), ref)
