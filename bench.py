@@ -26,6 +26,10 @@ sys.path.insert(0, ROOT)
 METRIC = "recurrent-block token·loops/sec (1 GPU) + % bf16 MFMA peak / % HBM peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+# the training step's optimizer: AdamW hyper-parameters and the router-bias
+# balancing rate
+OPT_HP = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+OPT_BIAS_GAMMA = 1e-3
 # token-loops/s each workload would reach at the spec peaks: per loop the
 # larger of its MFMA time (algorithmic flops) and its HBM time (touched
 # expert weights once + the other tensors once per fused kernel)
@@ -231,12 +235,22 @@ def train_bench(args, cfg):
     load = torch.empty(cfg["n_experts"], dtype=torch.int32, device="cuda")
     h_out = torch.empty_like(et)
     hc = torch.empty((B, T), dtype=torch.int32, device="cuda")
-    log(f"[bench] training workspace {bws.numel() / 2**30:.1f} GiB, tape {tape.numel() / 2**30:.2f} GiB")
+    opt = blk.adamw_init()
+    log(f"[bench] training workspace {bws.numel() / 2**30:.1f} GiB, tape {tape.numel() / 2**30:.2f} GiB, "
+        f"optimizer state {opt.numel() * 4 / 2**30:.1f} GiB")
     stream = torch.cuda.current_stream()
+    n_steps = [0]
+    # loops each step ran (the weights move, so the halting loops may too)
+    loops_run = torch.zeros(args.warmup + args.steps, dtype=torch.int32, device="cuda")
 
     def step():
         blk.train_forward(et, ht, L, thr, tape, h_out, hc)
         blk.train_backward(et, ht, L, thr, tape, hc, dy, bws, grad, de, dh0, load)
+        n_steps[0] += 1
+        blk.adamw_step(grad, opt, n_steps[0], **OPT_HP)
+        blk.router_bias_update(load, OPT_BIAS_GAMMA)
+        if thr > 0:
+            torch.amax(hc.view(-1), 0, out=loops_run[n_steps[0] - 1])
 
     for i in range(args.warmup):
         step()
@@ -248,7 +262,7 @@ def train_bench(args, cfg):
     # the dominant kernel (the routed experts' weight-gradient launches) is
     # bracketed with HIP events by the library on the launch stream
     dom = "train_expert_wgrad"
-    blk.set_timing_stages([dom, "train_attn_bwd"])
+    blk.set_timing_stages([dom, "train_attn_bwd", "train_optimizer"])
     torch.cuda.synchronize()
     if not args.no_clock:
         sampler.start()
@@ -266,10 +280,10 @@ def train_bench(args, cfg):
     step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     tm = blk.read_timing()
     blk.set_timing(False)
-    halt = hc.cpu().numpy()
-    loops = int(halt.max()) if thr > 0 else L
-    value = B * T * loops * args.steps / elapsed
-    fl = train_flops(cfg, loops)
+    per_step = loops_run[args.warmup:].tolist() if thr > 0 else [L] * args.steps
+    loops = max(per_step)
+    value = B * T * sum(per_step) / elapsed
+    fl = sum(train_flops(cfg, x) for x in per_step) / args.steps
     ms_step = elapsed / args.steps * 1e3
     # roofline of the dominant kernel: one launch is the weight gradient of
     # one routed matrix (gate, up or down) over every loop's rows,
@@ -287,27 +301,44 @@ def train_bench(args, cfg):
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     attn = dict(avg_launch_ms=round(at_ms / max(at_n, 1), 4), launches=at_n,
                 tflops=round(at_flops / (at_ms / max(at_n, 1) * 1e-3) / 1e12, 1))
+    # the AdamW launch: per trained element it reads the gradient, master,
+    # m and v (16 B) and writes master, m, v (12 B) and the weight (bf16
+    # matrices 2 B, fp32 vectors 4 B)
+    opt_bytes = 0
+    for name, (_, m) in blk.grad_layout().items():
+        if name != "router_bias":
+            opt_bytes += m * (28 + (2 if W[name].dtype == np.uint16 else 4))
+    op_ms, op_n = tm["train_optimizer"]
+    op_avg = op_ms / max(op_n, 1)
+    optimizer = dict(bound="hbm", avg_launch_ms=round(op_avg, 4), launches=op_n, bytes_per_launch=opt_bytes,
+                     achieved=round(opt_bytes / (op_avg * 1e-3) / 1e9, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                     lr=OPT_HP["lr"], betas=[OPT_HP["beta1"], OPT_HP["beta2"]], weight_decay=OPT_HP["weight_decay"],
+                     router_bias_gamma=OPT_BIAS_GAMMA)
+    optimizer["frac"] = round(optimizer["achieved"] / PEAK_HBM_GBS, 4)
     log(f"[bench] expert wgrad {wg_avg:.3f} ms/launch ({roof['achieved']} TFLOP/s), attention backward "
-        f"{attn['avg_launch_ms']} ms/loop ({attn['tflops']} TFLOP/s)")
+        f"{attn['avg_launch_ms']} ms/loop ({attn['tflops']} TFLOP/s), AdamW {op_avg:.3f} ms "
+        f"({optimizer['achieved']} GB/s)")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = train_cpu_baseline(cfg, W, e, h0, min(args.cpu_prefix, 256))
         log(f"[bench] cpu baseline: {cpu}")
     out = {
-        "metric": "recurrent-block training token·loops/sec (1 GPU; forward + backward)", "value": round(value, 1),
+        "metric": "recurrent-block training token·loops/sec (1 GPU; forward + backward + AdamW)", "value": round(value, 1),
         "unit": "token·loops/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3), "ms_per_step_median": round(step_ms[len(step_ms) // 2], 3),
         "ms_per_step_min": round(step_ms[0], 3), "sclk_mhz_samples": clocks, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
         "data": "synthetic (seeded N(0,0.02) weights, RMS-normalised N(0,1) inputs, N(0,1) upstream gradient)",
-        "config": {"workload": f"{args.config}-shaped recurrent block, training step (forward + backward), "
+        "config": {"workload": f"{args.config}-shaped recurrent block, training step (forward, backward, "
+                               f"AdamW and router-bias step), "
                                f"{cfg['dtype']}, batch {B} x seq {T}, {L} loops, ACT {'off' if thr == 0 else thr}",
-                   "loops_executed": loops},
+                   "loops_executed": loops, "loops_per_step": per_step},
         "algorithmic_tflops_per_step": round(fl / 1e12, 1),
         "achieved_tflops": round(fl / (ms_step * 1e-3) / 1e12, 1),
         "mfma_frac_of_step": round(fl / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "attention_backward": attn,
+        "optimizer": optimizer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -371,6 +371,39 @@ rdt_status rdt_router_bias_update(rdt_block* blk, const int32_t* expert_load, fl
  * Synchronous. */
 rdt_status rdt_get_router_bias(const rdt_block* blk, float* bias_host);
 
+/* AdamW on the handle's trained tensors ([ZS §Tokenizer & training script]
+ * trains with AdamW; the rule is decoupled weight decay with bias-corrected
+ * moments).  The optimizer state is three fp32 buffers in the gradient
+ * layout, back to back in `state` (device, >= rdt_adamw_state_bytes,
+ * 16-byte aligned, caller-owned): the master weights, the first moments m
+ * and the second moments v.  rdt_adamw_init sets the masters to the
+ * handle's weights (bf16 widened exactly) and the moments to 0; the router
+ * bias's master keeps that initial value.
+ * rdt_adamw_step, for step = 1, 2, ... (the count of steps including this
+ * one), takes grad (device fp32, rdt_grad_layout, 16-byte aligned) and, for
+ * every trained tensor except the router bias (which only the balancing
+ * step moves):  m = beta1 m + (1 - beta1) g,  v = beta2 v + (1 - beta2) g^2,
+ * master -= lr (m / (1 - beta1^step) / (sqrt(v / (1 - beta2^step)) + eps)
+ * + weight_decay master);  then writes the masters into the handle's
+ * weights (matrices rounded to bf16, nearest even) and recomputes A.  fp32
+ * arithmetic throughout.  Stream-ordered, no synchronisation.
+ * Errors: INVALID_ARG (nulls, misalignment, step < 1, lr or weight_decay
+ * negative or not finite, a beta outside [0, 1), eps <= 0 or not finite),
+ * UNSUPPORTED (not a bf16 GQA block), WORKSPACE_TOO_SMALL (state or
+ * gradient buffer). */
+rdt_status rdt_adamw_state_bytes(const rdt_block* blk, size_t* bytes);
+rdt_status rdt_adamw_init(rdt_block* blk, void* state, size_t state_bytes, void* stream);
+rdt_status rdt_adamw_step(rdt_block* blk, const float* grad, int64_t grad_numel, void* state, size_t state_bytes,
+                          int32_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                          void* stream);
+/* Size in bytes of the handle's tensor `id` (RDT_W_*, shape of the weights
+ * table; bf16 for matrices of a bf16 block, else fp32), 0 for a tensor the
+ * block does not use; rdt_get_weight copies it to host memory `dst` of
+ * `bytes` >= that size (INVALID_ARG otherwise, or for an unused tensor).
+ * Synchronous. */
+rdt_status rdt_weight_bytes(const rdt_block* blk, int32_t id, size_t* bytes);
+rdt_status rdt_get_weight(const rdt_block* blk, int32_t id, void* dst, size_t bytes);
+
 /* Copies A (fp32, [D]) to host memory, for the rho(A) < 1 check of
  * [RC §사용법] (A is diagonal, so rho(A) = max A_i).  Synchronous. */
 rdt_status rdt_get_A(const rdt_block* blk, float* A_host);
@@ -413,8 +446,9 @@ enum rdt_stage {
   RDT_STAGE_ROUTER, RDT_STAGE_DISPATCH, RDT_STAGE_EXPERT_GATEUP, RDT_STAGE_EXPERT_DOWN,
   RDT_STAGE_SHARED_GATEUP, RDT_STAGE_SHARED_DOWN, RDT_STAGE_TAIL,
   /* rdt_train_backward: the routed experts' weight-gradient products (three
-   * launches: gate, up, down) and the attention backward (per loop) */
-  RDT_STAGE_TRAIN_EXPERT_WGRAD, RDT_STAGE_TRAIN_ATTN_BWD,
+   * launches: gate, up, down) and the attention backward (per loop);
+   * rdt_adamw_step's update launch */
+  RDT_STAGE_TRAIN_EXPERT_WGRAD, RDT_STAGE_TRAIN_ATTN_BWD, RDT_STAGE_TRAIN_OPTIMIZER,
   RDT_STAGE_COUNT
 };
 rdt_status rdt_set_timing(rdt_block* blk, int32_t enable);

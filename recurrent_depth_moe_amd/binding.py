@@ -20,7 +20,8 @@ STATUS = {0: "RDT_OK", 1: "RDT_E_INVALID_ARG", 2: "RDT_E_UNSUPPORTED", 3: "RDT_E
           4: "RDT_E_HIP", 5: "RDT_E_BAD_STATE", 6: "RDT_E_WORKSPACE_TOO_SMALL"}
 
 STAGES = ["loop_head", "qkv", "attention", "o_proj", "ffn_norm", "router", "dispatch", "expert_gate_up",
-          "expert_down", "shared_gate_up", "shared_down", "tail", "train_expert_wgrad", "train_attn_bwd"]
+          "expert_down", "shared_gate_up", "shared_down", "tail", "train_expert_wgrad", "train_attn_bwd",
+          "train_optimizer"]
 
 WEIGHT_NAMES = ["g_rec", "g_attn", "g_ffn", "wq", "wk", "wv", "wo", "wdq", "gq", "wuq", "wdkv", "gkv", "wukv",
                 "router_w", "router_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
@@ -107,6 +108,11 @@ def lib():
                                 vp, sz, vp], i32),
         "rdt_router_bias_update": ([vp, vp, f32, vp], i32),
         "rdt_get_router_bias": ([vp, vp], i32),
+        "rdt_adamw_state_bytes": ([vp, ctypes.POINTER(sz)], i32),
+        "rdt_adamw_init": ([vp, vp, sz, vp], i32),
+        "rdt_adamw_step": ([vp, vp, ctypes.c_int64, vp, sz, i32, f32, f32, f32, f32, f32, vp], i32),
+        "rdt_weight_bytes": ([vp, i32, ctypes.POINTER(sz)], i32),
+        "rdt_get_weight": ([vp, i32, vp, sz], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -335,6 +341,37 @@ class Block:
     def get_router_bias(self):
         out = torch.empty(self.cfg["n_experts"], dtype=torch.float32)
         check(lib().rdt_get_router_bias(self._h, ctypes.c_void_p(out.data_ptr())))
+        return out
+
+    # ---- optimizer (rdt_adamw_*)
+    def adamw_state_bytes(self):
+        n = ctypes.c_size_t()
+        check(lib().rdt_adamw_state_bytes(self._h, ctypes.byref(n)))
+        return n.value
+
+    def adamw_init(self, state=None, stream=None):
+        """The optimizer state (fp32 masters, m, v in the gradient layout,
+        one flat device tensor), set from the handle's weights."""
+        if state is None:
+            state = torch.empty(self.adamw_state_bytes() // 4, dtype=torch.float32, device="cuda")
+        check(lib().rdt_adamw_init(self._h, _ptr(state), state.numel() * state.element_size(), _stream(stream)))
+        return state
+
+    def adamw_step(self, grad, state, step, lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, stream=None):
+        check(lib().rdt_adamw_step(self._h, _ptr(grad), grad.numel(), _ptr(state),
+                                   state.numel() * state.element_size(), int(step), float(lr), float(beta1),
+                                   float(beta2), float(eps), float(weight_decay), _stream(stream)))
+
+    def get_weight(self, name):
+        """The handle's tensor as a flat numpy array (bf16 bit patterns as
+        uint16 for matrices of a bf16 block, else float32)."""
+        import numpy as np
+        i = WEIGHT_NAMES.index(name)
+        n = ctypes.c_size_t()
+        check(lib().rdt_weight_bytes(self._h, i, ctypes.byref(n)))
+        grad_n = self.grad_layout()[name][1]
+        out = np.empty(grad_n, dtype=np.uint16 if n.value == 2 * grad_n else np.float32)
+        check(lib().rdt_get_weight(self._h, i, out.ctypes.data_as(ctypes.c_void_p), out.nbytes))
         return out
 
     def decode_step(self, e_new, h0_new, start_pos, n_loops, act_threshold, kv_cache, kv_capacity,

@@ -18,6 +18,7 @@
 #include "../../include/rdt.h"
 #include "attention.h"
 #include "backward.h"
+#include "optimizer.h"
 #include "gemm.h"
 #include "rowwise.h"
 
@@ -311,6 +312,9 @@ struct rdt_block {
   int64_t params = 0;
   char* mem = nullptr;
   size_t mem_bytes = 0;
+  // byte offset in mem and size of every weight tensor (0 bytes: unused)
+  size_t woff[RDT_W_COUNT] = {0};
+  size_t wbytes[RDT_W_COUNT] = {0};
   // weights (device, handle-owned)
   const float *g_rec, *g_attn, *g_ffn, *gq, *gkv, *router_bias, *lora_scale, *log_A, *log_dt, *Bv, *halt_w, *halt_b;
   const void *wqkv, *wo, *wdq, *wuq, *wdkv, *wukv, *router, *w_gate, *w_up, *w_down, *s_gate, *s_up, *s_down,
@@ -564,6 +568,8 @@ rdt_status rdt_block_create(const rdt_config* cfg, const void* const* weights, v
   b->mem_bytes = o;
   for (int i = 0; i < nt; ++i) {
     const size_t bytes = td[i].numel * (td[i].matrix ? es : 4);
+    b->woff[td[i].id] = off[td[i].id];
+    b->wbytes[td[i].id] = bytes;
     he = hipMemcpyAsync(b->mem + off[td[i].id], weights[td[i].id], bytes, hipMemcpyDeviceToDevice, s);
     if (he != hipSuccess) break;
   }
@@ -2140,6 +2146,131 @@ rdt_status rdt_get_router_bias(const rdt_block* b, float* bias_host) {
   g_err.clear();
   if (!b || !bias_host) return fail(RDT_E_INVALID_ARG, "NULL argument");
   HIP_TRY(hipMemcpy(bias_host, b->router_bias, (size_t)b->cfg.n_experts * 4, hipMemcpyDeviceToHost));
+  return RDT_OK;
+}
+
+rdt_status rdt_weight_bytes(const rdt_block* b, int32_t id, size_t* bytes) {
+  g_err.clear();
+  if (!b || !bytes) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  if (id < 0 || id >= RDT_W_COUNT) return fail(RDT_E_INVALID_ARG, "tensor id %d", id);
+  *bytes = b->wbytes[id];
+  return RDT_OK;
+}
+
+rdt_status rdt_get_weight(const rdt_block* b, int32_t id, void* dst, size_t bytes) {
+  g_err.clear();
+  if (!b || !dst) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  if (id < 0 || id >= RDT_W_COUNT || b->wbytes[id] == 0)
+    return fail(RDT_E_INVALID_ARG, "tensor id %d is not used by this block", id);
+  if (bytes < b->wbytes[id]) return fail(RDT_E_INVALID_ARG, "tensor %d needs %zu bytes, got %zu", id, b->wbytes[id], bytes);
+  HIP_TRY(hipMemcpy(dst, b->mem + b->woff[id], b->wbytes[id], hipMemcpyDeviceToHost));
+  return RDT_OK;
+}
+
+rdt_status rdt_adamw_state_bytes(const rdt_block* b, size_t* bytes) {
+  g_err.clear();
+  if (!b || !bytes) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  int64_t off[RDT_W_COUNT], n[RDT_W_COUNT], total = 0;
+  grad_offsets(b->cfg, off, n, &total);
+  *bytes = (size_t)total * 4 * 3;
+  return RDT_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Segments of the optimizer: every tensor of the gradient layout (the
+// router bias only when with_bias is set), with its weight in the handle.
+rdt_status adamw_args(rdt_block* b, void* state, size_t state_bytes, bool with_bias, AdamwArgs* a) {
+  const rdt_config& c = b->cfg;
+  if (c.weight_dtype != RDT_BF16 || !is_gqa(c))
+    return fail(RDT_E_UNSUPPORTED, "the optimizer is built for bf16 blocks with GQA attention");
+  if (!state) return fail(RDT_E_INVALID_ARG, "state is NULL");
+  if (((uintptr_t)state) & 15) return fail(RDT_E_INVALID_ARG, "state must be 16-byte aligned");
+  int64_t off[RDT_W_COUNT], n[RDT_W_COUNT], total = 0;
+  grad_offsets(c, off, n, &total);
+  if (state_bytes < (size_t)total * 12)
+    return fail(RDT_E_WORKSPACE_TOO_SMALL, "optimizer state %zu bytes, need %zu", state_bytes, (size_t)total * 12);
+  TensorDesc td[RDT_W_COUNT];
+  int nt = 0;
+  tensor_list(c, td, &nt);
+  *a = AdamwArgs{};
+  int blocks = 0;
+  for (int i = 0; i < nt; ++i) {
+    const int id = td[i].id;
+    if ((id == RDT_W_ROUTER_BIAS && !with_bias) || n[id] == 0) continue;
+    if (a->nseg == RDT_ADAMW_MAX_SEGS) return fail(RDT_E_UNSUPPORTED, "more than %d optimizer segments", RDT_ADAMW_MAX_SEGS);
+    AdamwSeg& sg = a->seg[a->nseg++];
+    sg.off = off[id];
+    sg.numel = n[id];
+    sg.dst = b->mem + b->woff[id];
+    sg.bf16 = td[i].matrix ? 1 : 0;
+    sg.first_block = blocks;
+    const int64_t nb = (n[id] + RDT_ADAMW_BLOCK - 1) / RDT_ADAMW_BLOCK;
+    if (blocks + nb > INT32_MAX) return fail(RDT_E_INVALID_ARG, "block too large for the optimizer launch");
+    blocks += (int)nb;
+  }
+  a->nblocks = blocks;
+  a->master = (float*)state;
+  a->m = a->master + total;
+  a->v = a->m + total;
+  return RDT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rdt_status rdt_adamw_init(rdt_block* b, void* state, size_t state_bytes, void* stream) {
+  g_err.clear();
+  if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
+  AdamwArgs a;
+  rdt_status st = adamw_args(b, state, state_bytes, true, &a);
+  if (st) return st;
+  launch_adamw_init(a, (hipStream_t)stream);
+  hipError_t he = hipGetLastError();
+  if (he != hipSuccess) return fail(RDT_E_HIP, "kernel launch: %s", hipGetErrorString(he));
+  return RDT_OK;
+}
+
+rdt_status rdt_adamw_step(rdt_block* b, const float* grad, int64_t grad_numel, void* state, size_t state_bytes,
+                          int32_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                          void* stream) {
+  g_err.clear();
+  if (!b || !grad) return fail(RDT_E_INVALID_ARG, "NULL argument");
+  if (((uintptr_t)grad) & 15) return fail(RDT_E_INVALID_ARG, "grad must be 16-byte aligned");
+  if (step < 1) return fail(RDT_E_INVALID_ARG, "step must be >= 1 (got %d)", step);
+  if (!std::isfinite(lr) || lr < 0.f) return fail(RDT_E_INVALID_ARG, "lr must be finite and >= 0");
+  if (!std::isfinite(weight_decay) || weight_decay < 0.f)
+    return fail(RDT_E_INVALID_ARG, "weight_decay must be finite and >= 0");
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+    return fail(RDT_E_INVALID_ARG, "beta1 and beta2 must be in [0, 1)");
+  if (!std::isfinite(eps) || eps <= 0.f) return fail(RDT_E_INVALID_ARG, "eps must be finite and > 0");
+  int64_t off[RDT_W_COUNT], n[RDT_W_COUNT], total = 0;
+  grad_offsets(b->cfg, off, n, &total);
+  if (grad_numel < total)
+    return fail(RDT_E_WORKSPACE_TOO_SMALL, "gradient buffer of %lld elements, need %lld", (long long)grad_numel,
+                (long long)total);
+  AdamwArgs a;
+  rdt_status st = adamw_args(b, state, state_bytes, false, &a);
+  if (st) return st;
+  a.grad = grad;
+  a.lr = lr;
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.eps = eps;
+  a.weight_decay = weight_decay;
+  a.bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
+  a.bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
+  hipStream_t s = (hipStream_t)stream;
+  {
+    StageTimer st_(b, s, RDT_STAGE_TRAIN_OPTIMIZER);
+    launch_adamw_step(a, s);
+  }
+  launch_make_A(b->log_A, b->log_dt, b->A, b->cfg.dim, s);
+  hipError_t he = hipGetLastError();
+  if (he != hipSuccess) return fail(RDT_E_HIP, "kernel launch: %s", hipGetErrorString(he));
   return RDT_OK;
 }
 
