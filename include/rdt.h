@@ -320,7 +320,7 @@ rdt_status rdt_model_generate(rdt_model* m, const int32_t* prompt, int32_t B, in
 
 /* Bytes of the tape a training forward records (every loop's forward
  * intermediates: one forward workspace per loop, plus the attention's
- * softmax normalisers) and of the backward workspace for B x T and n_loops
+ * softmax normalisers and the experts' gate / up pre-activations) and of the backward workspace for B x T and n_loops
  * (every loop's saved gradient operands, the working buffers of one loop
  * and transposed copies of the weights). */
 rdt_status rdt_train_tape_bytes(const rdt_block* blk, int32_t B, int32_t T, int32_t n_loops, size_t* bytes);
@@ -348,8 +348,8 @@ rdt_status rdt_train_forward(rdt_block* blk, const float* e, const float* h0, in
  * rdt_grad_layout; the router bias's entry is 0), dL/de and dL/dh0 (fp32
  * [B, T, D]), and expert_load (int32 [n_experts]): the (position, slot)
  * assignments of each expert summed over the loops run.  The loops are
- * taken in reverse order from their frames of the tape (only the gate / up
- * pre-activations of the experts are recomputed); weight gradients are
+ * taken in reverse order from their frames of the tape (nothing of the
+ * forward is recomputed); weight gradients are
  * formed over all loops' rows at the end.  The handle's
  * weights (router bias included) must not change between the two calls.
  * The call synchronises `stream` once (to read the number of loops run).

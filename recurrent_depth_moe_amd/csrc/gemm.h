@@ -11,6 +11,8 @@ enum EpiKind {
   EPI_SWIGLU = 3,  // dual B: out[m, n] = silu(acc0) * acc1   (type TO)
   EPI_MLA_Q = 4,   // MLA query: RoPE on the rope part of each head
   EPI_MLA_KV = 5,  // MLA kv up-projection: k_nope -> K, v -> V^T
+  EPI_SWIGLU_SAVE = 6,  // EPI_SWIGLU that also stores acc0 and acc1 (type TO):
+                        // gu[m, n] = acc0, gu[m, gu_up + n] = acc1
 };
 
 struct EpiParams {
@@ -34,6 +36,10 @@ struct EpiParams {
   // EPI_QKV with ACT compute skipping: output row m is sequence position
   // tok[m] (b = tok[m] / T, i = tok[m] % T); null: row m is position m
   const int32_t* tok;
+  // EPI_SWIGLU_SAVE: the gate / up pre-activations, row stride ldgu, the
+  // up half gu_up elements after the gate half
+  void* gu;
+  int64_t ldgu, gu_up;
 };
 
 struct GemmParams {

@@ -670,7 +670,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     };
     using I0 = std::integral_constant<int, 0>;
     using F4 = std::integral_constant<int, 4>;
-    constexpr bool ROUTED = EPI == EPI_SWIGLU || EPI == EPI_STORE;   // the routed expert products
+    constexpr bool ROUTED = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE || EPI == EPI_STORE;   // the routed expert products
     if (ROUTED && rows <= 192) {
       // 129-192 rows (the last tile of a routed expert): three 32-row
       // fragments per wave, so the tile costs 3/4 of a full one
@@ -710,7 +710,8 @@ void launch_big(const GemmParams& p, int n_cu, hipStream_t s) {
 void launch_gemm_bf16_big(const GemmParams& p, int epi, bool dual, int out_is_bf16, int n_cu, hipStream_t s,
                           int bn) {
   if (dual) {
-    if (out_is_bf16) launch_big<true, EPI_SWIGLU, bf16_t>(p, n_cu, s);
+    if (epi == EPI_SWIGLU_SAVE && out_is_bf16) launch_big<true, EPI_SWIGLU_SAVE, bf16_t>(p, n_cu, s);
+    else if (out_is_bf16) launch_big<true, EPI_SWIGLU, bf16_t>(p, n_cu, s);
     else launch_big<true, EPI_SWIGLU, float>(p, n_cu, s);
     return;
   }

@@ -11,8 +11,13 @@ static __device__ __forceinline__ void epi_store(const EpiParams& e, int m, int 
   } else if constexpr (EPI == EPI_RESID) {
     const int64_t i = (int64_t)m * e.ldo + n;
     ((float*)e.out)[i] = e.resid[i] + v;
-  } else if constexpr (EPI == EPI_SWIGLU) {
+  } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) {
     St<TO>::st((TO*)e.out + (int64_t)m * e.ldo + n, silu_f(v) * v2);
+    if constexpr (EPI == EPI_SWIGLU_SAVE) {
+      TO* gu = (TO*)e.gu + (int64_t)m * e.ldgu + n;
+      St<TO>::st(gu, v);
+      St<TO>::st(gu + e.gu_up, v2);
+    }
   } else if constexpr (EPI == EPI_QKV) {
     const int mp = e.tok ? e.tok[m] : m;
     const int b = mp / e.T, i = mp - b * e.T;
@@ -117,16 +122,22 @@ static __device__ __forceinline__ void epi_store8(const EpiParams& e, int N, int
   if (n + 8 > N) {
 #pragma unroll
     for (int x = 0; x < 8; ++x)
-      if (n + x < N) epi_store<EPI, TO>(e, m, n + x, v[x], EPI == EPI_SWIGLU ? v2[x] : v[x ^ 1]);
+      if (n + x < N)
+        epi_store<EPI, TO>(e, m, n + x, v[x], (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) ? v2[x] : v[x ^ 1]);
     return;
   }
   if constexpr (EPI == EPI_STORE) {
     store8<EPI, TO>((TO*)e.out + (int64_t)m * e.ldo + n, v);
-  } else if constexpr (EPI == EPI_SWIGLU) {
+  } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) {
     float o[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) o[x] = silu_f(v[x]) * v2[x];
     store8<EPI, TO>((TO*)e.out + (int64_t)m * e.ldo + n, o);
+    if constexpr (EPI == EPI_SWIGLU_SAVE) {
+      TO* gu = (TO*)e.gu + (int64_t)m * e.ldgu + n;
+      store8<EPI, TO>(gu, v);
+      store8<EPI, TO>(gu + e.gu_up, v2);
+    }
   } else if constexpr (EPI == EPI_RESID) {
     const int64_t i = (int64_t)m * e.ldo + n;
     const float4 r0 = *(const float4*)(e.resid + i), r1 = *(const float4*)(e.resid + i + 4);

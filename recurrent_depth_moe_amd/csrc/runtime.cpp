@@ -934,7 +934,8 @@ void attention_sublayer(const Ctx& x, const AttnW& aw, char* kslot, int cap_pad,
 static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int T, int start_pos, int n_loops,
                       float thr, void* kv, int kv_capacity, size_t kv_bytes, void* ws, size_t ws_bytes,
                       float* h_out, int32_t* halt_counts, void* stream, bool decode, bool act_skip = false,
-                      size_t frame = 0, float* lse2_frames = nullptr) {
+                      size_t frame = 0, float* lse2_frames = nullptr, char* gu_frames = nullptr,
+                      size_t gu_frame = 0) {
   g_err.clear();
   if (!b) return fail(RDT_E_INVALID_ARG, "block is NULL");
   const rdt_config& c = b->cfg;
@@ -973,6 +974,10 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
   // bytes apart), which keeps every loop's intermediates for the backward
   // pass; the ACT running sums and counters stay in frame 0
   char* const base = w;
+  // training forward: loop t's gate / up pre-activations of the routed
+  // experts ([N k][2F], dispatch order) then of each shared expert ([N][2F])
+  char* gu_t = nullptr;
+  const size_t NK = (size_t)N * k;
   auto gemm = [&](GemmParams gp, int epi, bool dual, int out_bf16, bool narrow = false, hipStream_t on = nullptr) {
     x.live_prev = live_prev;
     x.gemm(gp, epi, dual, out_bf16, narrow, on);
@@ -988,9 +993,17 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
                             (const char*)b->s_up + (size_t)si * F * D * es, Mr, F, D);
       gp.epi.out = W(WS_ACTS);
       gp.epi.ldo = F;
+      int epi = EPI_SWIGLU;
+      if (gu_t) {
+        // training: the pre-activations stay in the tape for the backward
+        gp.epi.gu = gu_t + ((size_t)NK + (size_t)si * N) * 2 * F * es;
+        gp.epi.ldgu = 2 * F;
+        gp.epi.gu_up = F;
+        epi = EPI_SWIGLU_SAVE;
+      }
       {
         StageTimer st_(b, on, RDT_STAGE_SHARED_GATEUP);
-        gemm(gp, EPI_SWIGLU, true, bf, false, on);
+        gemm(gp, epi, true, bf, false, on);
       }
       GemmParams gd = dense(W(WS_ACTS), F, (const char*)b->s_down + (size_t)si * D * F * es, nullptr, Mr, D, F);
       gd.epi.out = (char*)W(WS_YS) + (size_t)si * Mr * D * es;
@@ -1023,6 +1036,7 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       w = base + (size_t)t * frame;
       x.w = w;
       x.lse2 = lse2_frames + (size_t)t * N * c.n_heads;
+      gu_t = gu_frames ? gu_frames + (size_t)t * gu_frame : nullptr;
     }
     const float* hp = t == 0 ? h0 : frame ? (const float*)(base + (size_t)(t - 1) * frame + p.off[WS_H]) : WF(WS_H);
     live_prev = (live_buf && t > 0) ? live_buf + ((t - 1) & 1) : nullptr;
@@ -1090,9 +1104,16 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
       gp.tile_ctr = WI(WS_TCLAIM);
       gp.epi.out = W(WS_ACT);
       gp.epi.ldo = F;
+      int epi = EPI_SWIGLU;
+      if (gu_t) {
+        gp.epi.gu = gu_t;
+        gp.epi.ldgu = 2 * F;
+        gp.epi.gu_up = F;
+        epi = EPI_SWIGLU_SAVE;
+      }
       {
         StageTimer st_(b, s, RDT_STAGE_EXPERT_GATEUP);
-        gemm(gp, EPI_SWIGLU, true, bf);
+        gemm(gp, epi, true, bf);
       }
       // a12: routed down
       GemmParams gd = gp;
@@ -1590,8 +1611,9 @@ rdt_status rdt_model_generate(rdt_model* m, const int32_t* prompt, int32_t B, in
 // ------------------------------------------------------------ training
 // The backward pass of the recurrent stage ([ZS §Recurrent Block] forward
 // with its expert choices and halting loops held fixed) and the router-bias
-// balancing step.  Each loop is recomputed from its recorded input state in
-// reverse order; the operands of every weight-gradient product are kept for
+// balancing step.  The loops are taken in reverse order, each from its
+// frame of the tape that the training forward wrote (its intermediates and
+// its experts' gate / up pre-activations); the operands of every weight-gradient product are kept for
 // all loops (HBM holds them easily) so each weight gradient is one product
 // contracting over every loop's rows at the end.
 
@@ -1602,7 +1624,7 @@ enum BwId {
   // products that the forward frames do not already hold
   SV_DQKV, SV_DX1, SV_FPERM, SV_OFF, SV_DZP, SV_DGU, SV_DY, SV_ACTS, SV_DGUS, SV_DTAU, SV_G, SV_TAU, SV_WL, SV_DV,
   // working buffers of one loop
-  BW_G, BW_DX1, BW_DF, BW_DA, BW_DZ, BW_GU, BW_DACT, BW_DFP, BW_GUS, BW_DACTS, BW_DO, BW_DELTA, BW_QT, BW_DOT, BW_KT,
+  BW_G, BW_DX1, BW_DF, BW_DA, BW_DZ, BW_DACT, BW_DFP, BW_DACTS, BW_DO, BW_DELTA, BW_QT, BW_DOT, BW_KT,
   BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD, BW_RWP, BW_TCLAIM,
   // per-wave partial column sums (contiguous: cleared together)
   BP_A, BP_B, BP_GF, BP_GA, BP_GR, BP_HW, BP_HB, BP_S,
@@ -1615,7 +1637,7 @@ enum BwId {
 // per loop, then the loops' attention log2 normalisers [L][B H T].
 struct TapePlan {
   Plan fwd;
-  size_t frame, lse_off, total;
+  size_t frame, lse_off, gu_off, gu_frame, total;
 };
 
 TapePlan make_tape_plan(const rdt_config& c, int B, int T, int L) {
@@ -1623,7 +1645,12 @@ TapePlan make_tape_plan(const rdt_config& c, int B, int T, int L) {
   tp.fwd = make_plan(c, B, T);
   tp.frame = align256(tp.fwd.total);
   tp.lse_off = tp.frame * (size_t)L;
-  tp.total = tp.lse_off + align256((size_t)L * B * T * c.n_heads * 4);
+  tp.gu_off = tp.lse_off + align256((size_t)L * B * T * c.n_heads * 4);
+  // per loop: the routed experts' gate / up pre-activations [N k][2F], then
+  // each shared expert's [N][2F] (bf16)
+  const size_t N = (size_t)B * T, F = c.expert_dim;
+  tp.gu_frame = align256((N * c.top_k + N * c.n_shared_experts) * 2 * F * 2);
+  tp.total = tp.gu_off + tp.gu_frame * (size_t)L;
   return tp;
 }
 
@@ -1654,10 +1681,8 @@ BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   s[SV_DV] = Ls * N * RDT_LORA_LD * 2;
   s[BW_G] = s[BW_DX1] = s[BW_DF] = s[BW_DA] = N * D * 4;
   s[BW_DZ] = N * c.top_k * 4;
-  s[BW_GU] = NK * 2 * F * 2;
   s[BW_DACT] = NK * F * 4;
   s[BW_DFP] = NK * D * 4;
-  s[BW_GUS] = S * N * 2 * F * 2;
   s[BW_DACTS] = N * F * 4;
   s[BW_DO] = N * HD * 2;
   s[BW_DELTA] = N * H * 4;
@@ -1772,7 +1797,7 @@ rdt_status rdt_train_forward(rdt_block* b, const float* e, const float* h0, int3
   const TapePlan tp = make_tape_plan(b->cfg, B, T, n_loops);
   if (tape_bytes < tp.total) return fail(RDT_E_WORKSPACE_TOO_SMALL, "tape %zu bytes, need %zu", tape_bytes, tp.total);
   return run(b, e, h0, B, T, 0, n_loops, act_threshold, nullptr, 0, 0, tape, tape_bytes, h_out, halt_counts, stream,
-             false, false, tp.frame, (float*)((char*)tape + tp.lse_off));
+             false, false, tp.frame, (float*)((char*)tape + tp.lse_off), (char*)tape + tp.gu_off, tp.gu_frame);
 }
 
 rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int32_t B, int32_t T, int32_t n_loops,
@@ -1871,46 +1896,19 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   for (int t = L - 1; t >= 0; --t) {
     const float* hp = t == 0 ? h0 : FRF(t - 1, WS_H);
     const float* emb_t = b->loop_emb + (size_t)t * ld;
-    // ---- from the forward's frame: the routing of loop t; recomputed: the
-    // routed and shared gate / up pre-activations (the forward's fused
-    // SwiGLU epilogue keeps only their product) and the shared activations
+    // ---- from the forward's frame: the routing of loop t (load counts, the
+    // offsets, f gathered into dispatch order for the router's gradient);
+    // re-formed: each shared expert's activation from its saved gate / up
     launch_loop_index(FRI(t, WS_PERM), FRI(t, WS_OFFSETS), t, NK, N, E, nullptr, load, s);
     HIP_TRY(hipMemcpyAsync(QI(SV_OFF) + (size_t)t * (E + 1), FRI(t, WS_OFFSETS), (size_t)(E + 1) * 4,
                            hipMemcpyDeviceToDevice, s));
     launch_gather_rows_bf16(FR(t, WS_F), FRI(t, WS_PERM), NK, D, QB(SV_FPERM) + (size_t)t * NK * D, s);
-    GemmParams gp{};
-    gp.A = FR(t, WS_F);
-    gp.lda = D;
-    gp.a_rows = FRI(t, WS_PERM);
-    gp.W0 = b->w_gate;
-    gp.w_stride = (int64_t)F * D;
-    gp.M = NK;
-    gp.N = F;
-    gp.K = D;
-    gp.mt_start = FRI(t, WS_MTSTART);
-    gp.tile_row0 = FRI(t, WS_TROW0);
-    gp.tile_grp = FRI(t, WS_TGRP);
-    gp.grp_end = FRI(t, WS_OFFSETS);
-    gp.n_groups = E;
-    gp.epi.out = Q(BW_GU);
-    gp.epi.ldo = 2 * F;
-    gp.tile_ctr = claim(t, 0);
-    launch_gemm_bf16_big(gp, EPI_STORE, false, 1, b->n_cu, s, 256);
-    gp.W0 = b->w_up;
-    gp.epi.out = QB(BW_GU) + F;
-    gp.tile_ctr = claim(t, 1);
-    launch_gemm_bf16_big(gp, EPI_STORE, false, 1, b->n_cu, s, 256);
-    for (int si = 0; si < S; ++si) {
-      bf16_t* gus = QB(BW_GUS) + (size_t)si * N * 2 * F;
-      GemmParams gs = dense_params(FR(t, WS_F), D, (const char*)b->s_gate + (size_t)si * F * D * es, nullptr, N, F, D);
-      gs.epi.out = gus;
-      gs.epi.ldo = 2 * F;
-      x.gemm(gs, EPI_STORE, false, 1);
-      gs.W0 = (const char*)b->s_up + (size_t)si * F * D * es;
-      gs.epi.out = gus + F;
-      x.gemm(gs, EPI_STORE, false, 1);
-      launch_swiglu_fwd(gus, N, F, QB(SV_ACTS) + ((size_t)si * n_loops + t) * N * F, s);
-    }
+    // the gate / up pre-activations the forward's SwiGLU epilogue left in
+    // the tape: routed [N k][2F] in dispatch order, then each shared expert's
+    const bf16_t* gu_rt = (const bf16_t*)((const char*)tape + tp.gu_off + (size_t)t * tp.gu_frame);
+    for (int si = 0; si < S; ++si)
+      launch_swiglu_fwd(gu_rt + ((size_t)NK + (size_t)si * N) * 2 * F, N, F,
+                        QB(SV_ACTS) + ((size_t)si * n_loops + t) * N * F, s);
 
     // ---- backward of loop t
     {
@@ -1971,7 +1969,7 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
     }
     // shared experts: d act_s = dtau Wsd, SwiGLU backward, df (+)= dGU_s [Wsg; Wsu]
     for (int si = 0; si < S; ++si) {
-      const bf16_t* gus = QB(BW_GUS) + (size_t)si * N * 2 * F;
+      const bf16_t* gus = gu_rt + ((size_t)NK + (size_t)si * N) * 2 * F;
       GemmParams g1 = dense_params(QB(SV_DTAU) + (size_t)t * NDs, D, QB(TW_WSD) + (size_t)si * F * D, nullptr, N, F, D);
       g1.epi.out = QF(BW_DACTS);
       g1.epi.ldo = F;
@@ -1990,7 +1988,14 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
     }
     // routed experts: d act = dY Wd_e, SwiGLU backward, dfp = dGU [Wg; Wu]_e
     {
-      GemmParams r1 = gp;
+      // the loop's routing schedule (dispatch-order rows, grouped by expert)
+      GemmParams r1{};
+      r1.M = NK;
+      r1.mt_start = FRI(t, WS_MTSTART);
+      r1.tile_row0 = FRI(t, WS_TROW0);
+      r1.tile_grp = FRI(t, WS_TGRP);
+      r1.grp_end = FRI(t, WS_OFFSETS);
+      r1.n_groups = E;
       r1.A = QB(SV_DY) + (size_t)t * NK * D;
       r1.lda = D;
       r1.a_rows = nullptr;
@@ -2004,7 +2009,7 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
       r1.tile_ctr = claim(t, 2);
       launch_gemm_bf16_big(r1, EPI_STORE, false, 0, b->n_cu, s, 256);
       bf16_t* dgu = QB(SV_DGU) + (size_t)t * NK * 2 * F;
-      launch_swiglu_bwd(Q(BW_GU), QF(BW_DACT), NK, F, dgu, s);
+      launch_swiglu_bwd(gu_rt, QF(BW_DACT), NK, F, dgu, s);
       GemmParams r2 = r1;
       r2.A = dgu;
       r2.lda = 2 * F;
