@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmParams p) {
     }
     int mt, nt, row0, rows, grp;
     tile_coords(p, L, ntn, n_mt, mt, nt);
-    tile_rows(p, mt, BM, row0, rows, grp, HAS_STRIP ? p.strip_rows : 0);
+    tile_rows(p, mt, BM, row0, rows, grp);
     if (half >= 0) {
       row0 += 128 * half;
       rows = min(rows - 128 * half, 128);

@@ -84,15 +84,14 @@ static __device__ __forceinline__ void tile_coords(const GemmParams& p, int L, i
   }
 }
 
-static __device__ __forceinline__ void tile_rows(const GemmParams& p, int mt, int bm, int& row0, int& rows, int& grp,
-                                                 int extra = 0) {
+static __device__ __forceinline__ void tile_rows(const GemmParams& p, int mt, int bm, int& row0, int& rows, int& grp) {
   if (p.mt_start) {
     grp = p.tile_grp[mt];
     row0 = p.tile_row0[mt];
-    // a merged schedule gives a group's last m-tile up to `extra` more rows;
-    // every other m-tile of it has bm rows
-    const int left = p.grp_end[grp + 1] - row0;
-    rows = left <= bm + extra ? left : bm;
+    // an m-tile ends where the next one of its group starts, the group's
+    // last at the group's end (a merged schedule's last m-tile may hold more
+    // than bm rows: its strip rows)
+    rows = (mt + 1 < p.mt_start[grp + 1] ? p.tile_row0[mt + 1] : p.grp_end[grp + 1]) - row0;
   } else {
     grp = 0;
     row0 = mt * bm;

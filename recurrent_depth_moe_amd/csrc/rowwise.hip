@@ -293,7 +293,7 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
                                                                         int32_t* __restrict__ mt_start_m,
                                                                         int32_t* __restrict__ tile_row0_m,
                                                                         int32_t* __restrict__ tile_grp_m,
-                                                                        const int32_t* live) {
+                                                                        const int32_t* live, int even_split) {
   RDT_SKIP_IF_ALL_HALTED(live);
   if ((int)threadIdx.x < n_claim) tile_claim[threadIdx.x] = 0;
   __shared__ int wsum[RDT_MAX_EXPERTS / 64][3];
@@ -374,9 +374,12 @@ __global__ __launch_bounds__(RDT_MAX_EXPERTS) void dispatch_scan_kernel(int32_t*
           if (t0 + u < ntiles) tile_counts[(int64_t)(t0 + u) * E + ex] = c[u] + off;
       }
     }
+    // even split: the expert's m-tiles take equal shares of its rows (within
+    // one), so they run the same tile path at the same pace and stream the
+    // expert's weight panels together
     for (int i = 0; i < nmt; ++i) {
       tile_grp[mts + i] = ex;
-      tile_row0[mts + i] = off + i * bm;
+      tile_row0[mts + i] = off + (even_split ? (int)(((int64_t)i * tot) / nmt) : i * bm);
     }
     if (merge_extra > 0) {
       for (int i = 0; i < nmm; ++i) {
@@ -1217,7 +1220,7 @@ void launch_dispatch(const int32_t* sel, int NK, int k, int E, int bm, int32_t* 
   if (!(mt_start_m && tile_row0_m && tile_grp_m)) merge_extra = 0;
   dispatch_scan_kernel<<<1, RDT_MAX_EXPERTS, 0, s>>>(tile_counts, ntiles, E, bm, offsets, mt_start, tile_row0,
                                                      tile_grp, tile_claim, n_claim, merge_extra, mt_start_m,
-                                                     tile_row0_m, tile_grp_m, live);
+                                                     tile_row0_m, tile_grp_m, live, bm >= 128 ? 1 : 0);
   dispatch_scatter_kernel<<<ntiles, RDT_DISP_TILE, 0, s>>>(sel, NK, k, E, tile_counts, perm_src, inv, live);
 }
 

@@ -1128,7 +1128,6 @@ static rdt_status run(rdt_block* b, const float* e, const float* h0, int B, int 
         gd.mt_start = WI(WS_MTSTART_M);
         gd.tile_row0 = WI(WS_TROW0_M);
         gd.tile_grp = WI(WS_TGRP_M);
-        gd.strip_rows = 64;
       }
       gd.N = D;
       gd.K = F;
