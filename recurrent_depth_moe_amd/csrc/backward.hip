@@ -322,31 +322,37 @@ __global__ __launch_bounds__(512, 1) void wgrad8_kernel(WgradArgs a) {
   __syncthreads();
   const bf16_t* Ab = (const bf16_t*)a.A + n0 + 8 * cc;
   const bf16_t* Xb = (const bf16_t*)a.X + k0 + 8 * cc;
-  const bf16_t *Abt = Ab, *Xbt = Xb;   // this loop's rows
-  int t = t_lo - 1;
-  int64_t m0 = -64, r1 = 0;
-  auto advance = [&]() -> bool {
-    m0 += 64;
-    while (m0 >= r1) {
-      if (++t >= t_hi) return false;
-      m0 = s_lo[t - t_lo];
-      r1 = s_hi[t - t_lo];
-      Abt = Ab + (int64_t)t * a.a_loop_stride;
-      Xbt = Xb + (int64_t)t * a.x_loop_stride;
+  // The rows of loops t_lo .. t_hi-1 (loop t: rows s_lo .. s_hi-1 at its own
+  // base) are taken as one sequence, 64 per step, so a step may end one
+  // loop's rows and start the next loop's; only the last step has rows past
+  // the end (zero).  A position in the sequence is (loop t, row m); `norm`
+  // moves a position that lies past its loop's end into the next loops.
+  auto norm = [&](int& t, int64_t& m) {
+    while (t < t_hi && m >= s_hi[t - t_lo]) {
+      const int64_t over = m - s_hi[t - t_lo];
+      if (++t < t_hi) m = s_lo[t - t_lo] + over;
     }
-    return true;
   };
+  int t = t_lo;                                   // first row of the next step to load
+  int64_t m0 = t_lo < t_hi ? s_lo[0] : 0;
+  norm(t, m0);
   const bool full = n0 + TILE <= a.Nc && k0 + TILE <= a.Kc;
   const int na = a.Nc - (n0 + 8 * cc), nx = a.Kc - (k0 + 8 * cc);
   uint4 va[4], vx[4];
-  auto load = [&]() {
+  // loads the thread's 4 rows (4 rg .. 4 rg + 3 of the step starting at
+  // (t, m0)) and moves (t, m0) to the next step; false when no rows are left
+  auto load_step = [&]() -> bool {
+    if (t >= t_hi) return false;
+    int tr = t;
+    int64_t mr = m0 + 4 * rg;
+    norm(tr, mr);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + 4 * rg + i;
-      const bool ok = m < r1;
-      const int64_t mm = ok ? m : r1 - 1;
-      const bf16_t* ar = Abt + mm * a.lda;
-      const bf16_t* xr = Xbt + mm * a.ldx;
+      const bool ok = tr < t_hi;
+      const int tc = ok ? tr : t;
+      const int64_t mc = ok ? mr : m0;   // a valid row; zeroed below
+      const bf16_t* ar = Ab + (int64_t)tc * a.a_loop_stride + mc * a.lda;
+      const bf16_t* xr = Xb + (int64_t)tc * a.x_loop_stride + mc * a.ldx;
       if (full) {
         va[i] = *(const uint4*)ar;
         vx[i] = *(const uint4*)xr;
@@ -355,16 +361,21 @@ __global__ __launch_bounds__(512, 1) void wgrad8_kernel(WgradArgs a) {
         vx[i] = load8(xr, nx);
       }
       if (!ok) va[i] = vx[i] = uint4{0u, 0u, 0u, 0u};
+      if (i < 3) {
+        ++mr;
+        norm(tr, mr);
+      }
     }
+    m0 += 64;
+    norm(t, m0);
+    return true;
   };
-  bool have = advance();
+  bool have = load_step();
   if (have) {
-    load();
     wg_store_t(sA[0], va, 8 * cc, rg);
     wg_store_t(sX[0], vx, 8 * cc, rg);
   }
-  bool more = have && advance();
-  if (more) load();
+  bool more = have && load_step();
   __syncthreads();
   int cur = 0;
   while (have) {
@@ -383,16 +394,14 @@ __global__ __launch_bounds__(512, 1) void wgrad8_kernel(WgradArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], xf[j], acc[i][j]);
       if (ks == 0) {
+        // the rows of step i + 1 go to the other buffer, then the loads of
+        // step i + 2 are issued at once, a whole step ahead of their use
         __builtin_amdgcn_sched_barrier(0);
         if (more) {
           wg_store_t(sA[cur ^ 1], va, 8 * cc, rg);
           wg_store_t(sX[cur ^ 1], vx, 8 * cc, rg);
         }
-        __builtin_amdgcn_sched_barrier(0);
-      } else if (ks == 1) {
-        __builtin_amdgcn_sched_barrier(0);
-        more2 = more && advance();
-        if (more2) load();
+        more2 = more && load_step();
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -134,7 +134,10 @@ def test_end_to_end_short_tiles_of_192_column_products():
 def test_end_to_end_192_row_tiles(over, where):
     """Routed tiles of 129-192 rows run with three 32-row fragments per wave
     (gate|up on 256-column tiles, down on 192-column ones): as an expert's
-    only tile, and as the tile after a full 256-row one."""
+    only tile, and as the tile after a full 256-row one (the down product's
+    merged schedule; the gate|up schedule splits an expert's rows evenly
+    over its m-tiles, 186-233 rows each here).  Both schedules are checked
+    exactly against their definitions from the dispatch offsets."""
     import torch
     scales = {"w_down": 0.1, "s_down": 0.1}
     cfg, W, e, h0 = _inputs("small_bf16_strip", scales=scales, **over)
@@ -145,6 +148,21 @@ def test_end_to_end_192_row_tiles(over, where):
     tail = counts % 256 if where == "second" else counts
     hit = (tail > 128) & (tail <= 192) & ((counts > 256) if where == "second" else (counts <= 256))
     assert hit.any(), counts
+    # plain schedule: ceil(rows / 256) m-tiles per expert starting at
+    # off + floor(i rows / n); merged: tiles of 256 rows, the last taking a
+    # remainder of at most 64 rows
+    off = run.ws_np("offsets", torch.int32, (E + 1,))
+    mts = run.ws_np("mt_start", torch.int32, (E + 1,))
+    mtm = run.ws_np("mt_start_merged", torch.int32, (E + 1,))
+    tr0 = run.ws_np("tile_row0", torch.int32, (int(mts[-1]),))
+    trm = run.ws_np("tile_row0_merged", torch.int32, (int(mtm[-1]),))
+    for x in range(E):
+        n = -(-int(counts[x]) // 256)
+        assert mts[x + 1] - mts[x] == n
+        np.testing.assert_array_equal(tr0[mts[x]:mts[x + 1]], off[x] + (np.arange(n) * int(counts[x])) // max(n, 1))
+        nm = n - 1 if counts[x] > 256 and 0 < counts[x] % 256 <= 64 else n
+        assert mtm[x + 1] - mtm[x] == nm
+        np.testing.assert_array_equal(trm[mtm[x]:mtm[x + 1]], off[x] + 256 * np.arange(nm))
     _e2e(cfg, W, e, h0)
 
 
