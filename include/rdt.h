@@ -345,7 +345,8 @@ rdt_status rdt_train_forward(rdt_block* blk, const float* e, const float* h0, in
  * (fp32 [B, T, D]) for the output of the rdt_train_forward call that wrote
  * `tape` and `halt_counts` with the same e, h0, n_loops and act_threshold,
  * writes the gradient of every trained tensor into `grad` (fp32, layout of
- * rdt_grad_layout; the router bias's entry is 0), dL/de and dL/dh0 (fp32
+ * rdt_grad_layout; the router bias's entry is 0; the padding between
+ * tensors is not written), dL/de and dL/dh0 (fp32
  * [B, T, D]), and expert_load (int32 [n_experts]): the (position, slot)
  * assignments of each expert summed over the loops run.  The loops are
  * taken in reverse order from their frames of the tape (nothing of the

@@ -1856,7 +1856,10 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   const int64_t fr_bf = (int64_t)(tp.frame / 2);   // frame stride in bf16 elements
 
   // what accumulates starts at zero
-  launch_fill_zero(grad, (size_t)gtotal * 4, s);
+  // every tensor of the gradient is overwritten at the end but the router
+  // bias (no gradient: 0) and the LoRA scales (summed over the loops run)
+  launch_fill_zero(grad + goff[RDT_W_ROUTER_BIAS], (size_t)gnum[RDT_W_ROUTER_BIAS] * 4, s);
+  launch_fill_zero(grad + goff[RDT_W_LORA_SCALE], (size_t)gnum[RDT_W_LORA_SCALE] * 4, s);
   launch_fill_zero(de, NDs * 4, s);
   launch_fill_zero(load, (size_t)E * 4, s);
   launch_fill_zero(Q(BP_A), q.off[BP_S] + q.size[BP_S] - q.off[BP_A], s);

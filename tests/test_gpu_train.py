@@ -60,10 +60,14 @@ def _run(cfg, W, e, h0, seed=5):
     dy = np.random.default_rng(seed).standard_normal(e.shape).astype(np.float32)
     dy_d = torch.from_numpy(dy).cuda()
     ws = torch.empty(blk.train_workspace_bytes(B, T, L), dtype=torch.uint8, device="cuda")
-    grad, de, dh0, load = blk.train_backward(e_d, h_d, L, thr, tape, halt, dy_d, ws)
+    # NaN everywhere first: every tensor of the layout must be written
+    grad0 = torch.full((blk.grad_numel(),), float("nan"), dtype=torch.float32, device="cuda")
+    grad, de, dh0, load = blk.train_backward(e_d, h_d, L, thr, tape, halt, dy_d, ws, grad=grad0)
     torch.cuda.synchronize()
     layout = blk.grad_layout()
     g = to_np(grad)
+    for n, (o, m) in layout.items():
+        assert np.all(np.isfinite(g[o:o + m])), f"gradient of {n} not fully written"
     res = dict(out=to_np(out), halt=to_np(halt), sel=to_np(cap_sel), dy=dy, de=to_np(de), dh0=to_np(dh0),
                load=to_np(load), blk=blk)
     res["grads"] = {n: g[o:o + m] for n, (o, m) in layout.items()}
