@@ -148,6 +148,13 @@ void launch_loop_index(const int32_t* perm, const int32_t* off, int t, int NK, i
                        int32_t* load, hipStream_t s);
 // out[c] (+)= sum_w part[w][c] for c < len, w < rows
 void launch_col_reduce(const float* part, int rows, int64_t ld, int len, float* out, int accumulate, hipStream_t s);
+// first stage of a long column sum, for nb batches (batch b at part + b
+// pstride): slices[b][z][c] = sum of part rows [z rows / RDT_COL_SLICES,
+// (z + 1) rows / RDT_COL_SLICES) of column c (len <= ld); the slices are
+// then summed in order by launch_col_reduce
+#define RDT_COL_SLICES 32
+void launch_col_slices(const float* part, int rows, int64_t ld, int len, int nb, int64_t pstride, float* slices,
+                       hipStream_t s);
 // d log_A and d log_dt from dA (A = exp(-exp(clamp(log_dt + log_A, -20, 20))))
 void launch_lti_param_grad(const float* dA, const float* A, const float* log_A, const float* log_dt, int D,
                            float* dlog_A, float* dlog_dt, hipStream_t s);

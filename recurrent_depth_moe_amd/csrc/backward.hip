@@ -1131,6 +1131,33 @@ __global__ __launch_bounds__(256) void col_reduce_kernel(const float* __restrict
   }
 }
 
+// block (column chunk, slice z, batch b): CW columns of rows [z rows / S,
+// (z + 1) rows / S), the 256 / CW row lanes of each column added in order
+__global__ __launch_bounds__(256) void col_slices_kernel(const float* __restrict__ part, int rows, int64_t ld, int len,
+                                                         int64_t pstride, float* __restrict__ slices, int CW) {
+  __shared__ float red[256];
+  const int cl = threadIdx.x % CW, rs = threadIdx.x / CW, RS = 256 / CW, c = blockIdx.x * CW + cl;
+  const int z = blockIdx.y, b = blockIdx.z;
+  const int r0 = (int)((int64_t)z * rows / RDT_COL_SLICES), r1 = (int)((int64_t)(z + 1) * rows / RDT_COL_SLICES);
+  const float* p = part + (int64_t)b * pstride;
+  float s0 = 0.f, s1 = 0.f;
+  if (c < len) {
+    int w = r0 + rs;
+    for (; w + RS < r1; w += 2 * RS) {
+      s0 += p[(int64_t)w * ld + c];
+      s1 += p[(int64_t)(w + RS) * ld + c];
+    }
+    if (w < r1) s0 += p[(int64_t)w * ld + c];
+  }
+  red[threadIdx.x] = s0 + s1;
+  __syncthreads();
+  if (rs == 0 && c < len) {
+    float t = 0.f;
+    for (int i = 0; i < RS; ++i) t += red[i * CW + cl];
+    slices[((int64_t)b * RDT_COL_SLICES + z) * len + c] = t;
+  }
+}
+
 __global__ __launch_bounds__(256) void lti_param_grad_kernel(const float* __restrict__ dA, const float* __restrict__ A,
                                                              const float* __restrict__ log_A,
                                                              const float* __restrict__ log_dt, int D,
@@ -1278,6 +1305,13 @@ void launch_loop_index(const int32_t* perm, const int32_t* off, int t, int NK, i
 void launch_col_reduce(const float* part, int rows, int64_t ld, int len, float* out, int accumulate, hipStream_t s) {
   const int CW = len >= 64 ? 64 : len >= 16 ? 16 : 4;
   col_reduce_kernel<<<(len + CW - 1) / CW, 256, 0, s>>>(part, rows, ld, len, out, accumulate, CW);
+}
+
+void launch_col_slices(const float* part, int rows, int64_t ld, int len, int nb, int64_t pstride, float* slices,
+                       hipStream_t s) {
+  const int CW = len >= 64 ? 64 : len >= 16 ? 16 : 4;
+  col_slices_kernel<<<dim3((len + CW - 1) / CW, RDT_COL_SLICES, nb), 256, 0, s>>>(part, rows, ld, len, pstride, slices,
+                                                                                    CW);
 }
 
 void launch_lti_param_grad(const float* dA, const float* A, const float* log_A, const float* log_dt, int D,

@@ -1624,7 +1624,8 @@ enum BwId {
   SV_DQKV, SV_DX1, SV_FPERM, SV_OFF, SV_DZP, SV_DGU, SV_DY, SV_ACTS, SV_DGUS, SV_DTAU, SV_G, SV_TAU, SV_WL, SV_DV,
   // working buffers of one loop
   BW_G, BW_DX1, BW_DF, BW_DA, BW_DZ, BW_DACT, BW_DFP, BW_DACTS, BW_DO, BW_DELTA, BW_QT, BW_DOT, BW_KT,
-  BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD, BW_RWP, BW_TCLAIM,
+  BW_VN, BW_GQ, BW_GK, BW_GV, BW_WACT, BW_ZACT, BW_SPLIT, BW_CSLICE, BW_DAVEC, BW_LV, BW_LDW, BW_DVPAD, BW_RWP,
+  BW_TCLAIM,
   // per-wave partial column sums (contiguous: cleared together)
   BP_A, BP_B, BP_GF, BP_GA, BP_GR, BP_HW, BP_HB, BP_S,
   // transposed weights
@@ -1691,6 +1692,7 @@ BwPlan make_bw_plan(const rdt_config& c, int B, int T, int L) {
   s[BW_GK] = s[BW_GV] = N * G * 128 * 4;
   s[BW_WACT] = s[BW_ZACT] = Ls * N * 4;
   s[BW_SPLIT] = Ls * r * D * 4;
+  s[BW_CSLICE] = (size_t)RDT_COL_SLICES * std::max(D, Ls * RDT_LORA_LD) * 4;
   s[BW_DAVEC] = D * 4;
   s[BW_LV] = s[BW_LDW] = N * r * 4;
   s[BW_DVPAD] = N * 64 * 2;
@@ -2121,17 +2123,27 @@ rdt_status rdt_train_backward(rdt_block* b, const float* e, const float* h0, int
   launch_col_reduce(QF(BW_SPLIT), L, rD, (int)rD, gb + goff[RDT_W_LORA_B], 0, s);
   wgrad(Q(SV_DV), RDT_LORA_LD, nl, Q(SV_TAU), D, nd, nullptr, N, 1, r, D, QF(BW_SPLIT), D, 0, L, rD);
   launch_col_reduce(QF(BW_SPLIT), L, rD, (int)rD, gb + goff[RDT_W_LORA_DOWN], 0, s);
+  // long column sums in two stages: RDT_COL_SLICES row slices in parallel,
+  // then the slices in order
+  float* const cs = QF(BW_CSLICE);
+  auto col_sum = [&](const float* part, int len, float* out) {
+    launch_col_slices(part, RDT_BWD_WAVES, len, len, 1, 0, cs, s);
+    launch_col_reduce(cs, RDT_COL_SLICES, len, len, out, 0, s);
+  };
+  // LoRA scales: every loop's sums at once, then added loop by loop in order
+  // (loops past max_loop_iters share the last scale row)
+  launch_col_slices(QF(BP_S), RDT_BWD_WAVES, RDT_LORA_LD, r, L, (int64_t)RDT_BWD_WAVES * RDT_LORA_LD, cs, s);
   for (int t = 0; t < L; ++t)
-    launch_col_reduce(QF(BP_S) + (size_t)t * RDT_BWD_WAVES * RDT_LORA_LD, RDT_BWD_WAVES, RDT_LORA_LD, r,
+    launch_col_reduce(cs + (size_t)t * RDT_COL_SLICES * r, RDT_COL_SLICES, r, r,
                       gb + goff[RDT_W_LORA_SCALE] + (size_t)std::min(t, c.max_loop_iters - 1) * r, 1, s);
   // vectors: norm gains, B, halting head, A's parameters
-  launch_col_reduce(QF(BP_GR), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_G_REC], 0, s);
-  launch_col_reduce(QF(BP_GA), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_G_ATTN], 0, s);
-  launch_col_reduce(QF(BP_GF), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_G_FFN], 0, s);
-  launch_col_reduce(QF(BP_B), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_B], 0, s);
-  launch_col_reduce(QF(BP_HW), RDT_BWD_WAVES, D, D, gb + goff[RDT_W_HALT_W], 0, s);
+  col_sum(QF(BP_GR), D, gb + goff[RDT_W_G_REC]);
+  col_sum(QF(BP_GA), D, gb + goff[RDT_W_G_ATTN]);
+  col_sum(QF(BP_GF), D, gb + goff[RDT_W_G_FFN]);
+  col_sum(QF(BP_B), D, gb + goff[RDT_W_B]);
+  col_sum(QF(BP_HW), D, gb + goff[RDT_W_HALT_W]);
   launch_col_reduce(QF(BP_HB), RDT_BWD_WAVES, 1, 1, gb + goff[RDT_W_HALT_B], 0, s);
-  launch_col_reduce(QF(BP_A), RDT_BWD_WAVES, D, D, QF(BW_DAVEC), 0, s);
+  col_sum(QF(BP_A), D, QF(BW_DAVEC));
   launch_lti_param_grad(QF(BW_DAVEC), b->A, b->log_A, b->log_dt, D, gb + goff[RDT_W_LOG_A], gb + goff[RDT_W_LOG_DT],
                         s);
   hipError_t he = hipGetLastError();
