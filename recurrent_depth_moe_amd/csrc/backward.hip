@@ -1000,6 +1000,69 @@ __global__ __launch_bounds__(256) void tail_bwd_gates_kernel(TailBwdArgs a) {
   ROW_LOOP_END
 }
 
+// The same with the row's slices of x1 and of the summed gradient of f held
+// in registers (NC float4 per lane, D <= 256 NC), so the second pass reads
+// none of x1, df, dfp or the router rows again; same arithmetic, same order.
+template <int NC>
+__global__ __launch_bounds__(256) void ffn_norm_bwd_reg_kernel(int N, int D, int k, float eps,
+                                                               const float* __restrict__ df,
+                                                               const float* __restrict__ dfp,
+                                                               const int32_t* __restrict__ inv,
+                                                               const int32_t* __restrict__ sel,
+                                                               const float* __restrict__ dz,
+                                                               const bf16_t* __restrict__ Wr,
+                                                               const float* __restrict__ x1,
+                                                               const float* __restrict__ gf, float* __restrict__ dx1,
+                                                               bf16_t* __restrict__ dx1_bf, float* __restrict__ part_g) {
+  ROW_LOOP_BEGIN
+  const int64_t ro = (int64_t)n * D;
+  int rj[8], sj[8];
+  float zj[8];
+  for (int j = 0; j < k; ++j) {
+    rj[j] = inv[(int64_t)n * k + j];
+    sj[j] = sel[(int64_t)n * k + j];
+    zj[j] = dz[(int64_t)n * k + j];
+  }
+  const float4 z4 = float4{0.f, 0.f, 0.f, 0.f};
+  float4 xv[NC], dfv[NC];
+  float ss = 0.f, dd = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = 4 * lane + 256 * i;
+    xv[i] = dfv[i] = z4;
+    if (c < D) {
+      float4 v = df ? ld4(df + ro + c) : z4;
+      for (int j = 0; j < k; ++j) {
+        v = add4(v, ld4(dfp + (int64_t)rj[j] * D + c));
+        v = fma4(zj[j], ldbf4(Wr + (int64_t)sj[j] * D + c), v);
+      }
+      dfv[i] = v;
+      xv[i] = ld4(x1 + ro + c);
+      ss += dot4(xv[i], xv[i]);
+      dd += dot4(mul4(v, ld4(gf + c)), xv[i]);
+    }
+  }
+  ss = wave_sum(ss);
+  dd = wave_sum(dd);
+  const float rstd = rsqrtf(ss / D + eps), m = dd * rstd * rstd / D;
+  float* pg = part_g + (int64_t)wg * D;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = 4 * lane + 256 * i;
+    if (c < D) {
+      const float4 x = xv[i], dft = dfv[i], g4 = ld4(gf + c);
+      const float4 xh = scl4(rstd, x);
+      const float4 dx = scl4(rstd, float4{dft.x * g4.x - x.x * m, dft.y * g4.y - x.y * m, dft.z * g4.z - x.z * m,
+                                          dft.w * g4.w - x.w * m});
+      const float4 o = add4(ld4(dx1 + ro + c), dx);
+      st4(dx1 + ro + c, o);
+      stbf4(dx1_bf + ro + c, o);
+      st4(pg + c, add4(ld4(pg + c), mul4(dft, xh)));
+    }
+  }
+  ROW_LOOP_END
+}
+
 __global__ __launch_bounds__(256) void ffn_norm_bwd_kernel(int N, int D, int k, float eps, const float* __restrict__ df,
                                                            const float* __restrict__ dfp,
                                                            const int32_t* __restrict__ inv,
@@ -1094,6 +1157,78 @@ __global__ __launch_bounds__(256) void head_bwd_kernel(int N, int D, float eps, 
     st4(de + ro + c, add4(ld4(de + ro + c), dr));
     st4(pa + c, add4(ld4(pa + c), mul4(ld4(da + ro + c), scl4(rc, ld4(c_ + ro + c)))));
     st4(pr + c, add4(ld4(pr + c), mul4(dc, scl4(rr, rv))));
+  }
+  ROW_LOOP_END
+}
+
+// The same with the row's slices of c and da held in registers (NC float4
+// per lane, D <= 256 NC), so the later passes read neither again; h_prev +
+// e is re-read per pass (holding it too would leave one wave per SIMD).
+// Same arithmetic, same order.
+template <int NC>
+__global__ __launch_bounds__(256) void head_bwd_reg_kernel(int N, int D, float eps, const float* __restrict__ dx1,
+                                                           const float* __restrict__ da, const float* __restrict__ c_,
+                                                           const float* __restrict__ ga, const float* __restrict__ gr,
+                                                           const float* __restrict__ hp, const float* __restrict__ e,
+                                                           const float* __restrict__ emb, int loop_dim,
+                                                           float* __restrict__ gcarry, float* __restrict__ de,
+                                                           float* __restrict__ part_ga, float* __restrict__ part_gr) {
+  ROW_LOOP_BEGIN
+  const int64_t ro = (int64_t)n * D;
+  auto r_at = [&](int c) {
+    float4 v = add4(ld4(hp + ro + c), ld4(e + ro + c));
+    if (c < loop_dim) v = add4(v, ld4(emb + c));
+    return v;
+  };
+  const float4 z4 = float4{0.f, 0.f, 0.f, 0.f};
+  float4 cv[NC], dav[NC];
+  float sc = 0.f, sac = 0.f, sr = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = 4 * lane + 256 * i;
+    cv[i] = dav[i] = z4;
+    if (c < D) {
+      cv[i] = ld4(c_ + ro + c);
+      dav[i] = ld4(da + ro + c);
+      const float4 rv = r_at(c);
+      sc += dot4(cv[i], cv[i]);
+      sac += dot4(mul4(dav[i], ld4(ga + c)), cv[i]);
+      sr += dot4(rv, rv);
+    }
+  }
+  sc = wave_sum(sc);
+  sac = wave_sum(sac);
+  sr = wave_sum(sr);
+  const float rc = rsqrtf(sc / D + eps), mc = sac * rc * rc / D;
+  const float rr = rsqrtf(sr / D + eps);
+  auto dc_at = [&](int i, int c) {
+    const float4 dg = mul4(dav[i], ld4(ga + c));
+    const float4 t = float4{dg.x - cv[i].x * mc, dg.y - cv[i].y * mc, dg.z - cv[i].z * mc, dg.w - cv[i].w * mc};
+    return fma4(rc, t, ld4(dx1 + ro + c));
+  };
+  float scr = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = 4 * lane + 256 * i;
+    if (c < D) scr += dot4(mul4(dc_at(i, c), ld4(gr + c)), r_at(c));
+  }
+  scr = wave_sum(scr);
+  const float mr = scr * rr * rr / D;
+  float* pa = part_ga + (int64_t)wg * D;
+  float* pr = part_gr + (int64_t)wg * D;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = 4 * lane + 256 * i;
+    if (c < D) {
+      const float4 dc = dc_at(i, c), rv = r_at(c), g4 = ld4(gr + c);
+      const float4 t = float4{dc.x * g4.x - rv.x * mr, dc.y * g4.y - rv.y * mr, dc.z * g4.z - rv.z * mr,
+                              dc.w * g4.w - rv.w * mr};
+      const float4 dr = scl4(rr, t);
+      st4(gcarry + ro + c, add4(ld4(gcarry + ro + c), dr));
+      st4(de + ro + c, add4(ld4(de + ro + c), dr));
+      st4(pa + c, add4(ld4(pa + c), mul4(dav[i], scl4(rc, cv[i]))));
+      st4(pr + c, add4(ld4(pr + c), mul4(dc, scl4(rr, rv))));
+    }
   }
   ROW_LOOP_END
 }
@@ -1286,15 +1421,37 @@ void launch_tail_bwd_gates(const TailBwdArgs& a, hipStream_t s) {
 void launch_ffn_norm_bwd(int N, int D, int k, float eps, const float* df, const float* dfp, const int32_t* inv,
                          const int32_t* sel, const float* dz, const void* Wr, const float* x1, const float* g_ffn,
                          float* dx1, void* dx1_bf, float* part_g, hipStream_t s) {
-  ffn_norm_bwd_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, k, eps, df, dfp, inv, sel, dz, (const bf16_t*)Wr, x1,
-                                                     g_ffn, dx1, (bf16_t*)dx1_bf, part_g);
+  const int nc = (D + 255) / 256;
+  if (nc <= 4)
+    ffn_norm_bwd_reg_kernel<4><<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, k, eps, df, dfp, inv, sel, dz, (const bf16_t*)Wr,
+                                                              x1, g_ffn, dx1, (bf16_t*)dx1_bf, part_g);
+  else if (nc <= 8)
+    ffn_norm_bwd_reg_kernel<8><<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, k, eps, df, dfp, inv, sel, dz, (const bf16_t*)Wr,
+                                                              x1, g_ffn, dx1, (bf16_t*)dx1_bf, part_g);
+  else if (nc <= 12)
+    ffn_norm_bwd_reg_kernel<12><<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, k, eps, df, dfp, inv, sel, dz, (const bf16_t*)Wr,
+                                                               x1, g_ffn, dx1, (bf16_t*)dx1_bf, part_g);
+  else
+    ffn_norm_bwd_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, k, eps, df, dfp, inv, sel, dz, (const bf16_t*)Wr, x1,
+                                                       g_ffn, dx1, (bf16_t*)dx1_bf, part_g);
 }
 
 void launch_head_bwd(int N, int D, float eps, const float* dx1, const float* da, const float* c,
                      const float* g_attn, const float* g_rec, const float* h_prev, const float* e, const float* emb_t,
                      int loop_dim, float* g_carry, float* de, float* part_ga, float* part_gr, hipStream_t s) {
-  head_bwd_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, eps, dx1, da, c, g_attn, g_rec, h_prev, e, emb_t, loop_dim,
-                                                 g_carry, de, part_ga, part_gr);
+  const int nc = (D + 255) / 256;
+  if (nc <= 4)
+    head_bwd_reg_kernel<4><<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, eps, dx1, da, c, g_attn, g_rec, h_prev, e, emb_t,
+                                                          loop_dim, g_carry, de, part_ga, part_gr);
+  else if (nc <= 8)
+    head_bwd_reg_kernel<8><<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, eps, dx1, da, c, g_attn, g_rec, h_prev, e, emb_t,
+                                                          loop_dim, g_carry, de, part_ga, part_gr);
+  else if (nc <= 12)
+    head_bwd_reg_kernel<12><<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, eps, dx1, da, c, g_attn, g_rec, h_prev, e, emb_t,
+                                                           loop_dim, g_carry, de, part_ga, part_gr);
+  else
+    head_bwd_kernel<<<RDT_BWD_BLOCKS, 256, 0, s>>>(N, D, eps, dx1, da, c, g_attn, g_rec, h_prev, e, emb_t, loop_dim,
+                                                   g_carry, de, part_ga, part_gr);
 }
 
 void launch_loop_index(const int32_t* perm, const int32_t* off, int t, int NK, int N, int E, int32_t* gidx,
