@@ -656,12 +656,12 @@ struct alignas(16) DqBuf {
   uint4 k[AQ * 16], v[AQ * 16], kt[128 * 8];
 };
 
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dO, const bf16_t* __restrict__ kt, const float* __restrict__ lse2,
     const float* __restrict__ Dq, float* __restrict__ dQ, int B, int H, int G, int T, int cap, float scale_log2,
     float scale) {
-  __shared__ DqBuf buf[2];
+  __shared__ DqBuf buf[1];
   const int BH = B * H, nqt = (T + 127) / 128;
   const int qti = nqt - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
   const int b = bh / H, h = bh - b * H, g = h / (H / G);
@@ -704,15 +704,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       dma16(ktb + (int64_t)d * cap + k0 + tc * 8, &buf[bb].kt[(j * 4 + w) * 64]);
     }
   };
-  if (nkt > 0) issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   const int myrow = kperm(lane & 31);
   for (int i = 0; i < nkt; ++i) {
-    const int bb = i & 1;
-    if (i + 1 < nkt) issue(i + 1, bb ^ 1);
+    issue(i, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     const int k0 = i * AQ;
-    const DqBuf& cb = buf[bb];
+    const DqBuf& cb = buf[0];
     if (k0 <= qw0 + 31) {   // else every key of the tile follows this wave's queries
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
