@@ -1,7 +1,8 @@
-// fp32 matrix products (fp32 configs) on gfx950: 64x64x16 tiles, 4x4 fp32
-// FMA micro-tiles, the same epilogues and the same persistent, XCD-aware
-// tile loop as the bf16 kernels (the tile list is cut into eight contiguous
-// chunks, one per XCD, since workgroup i runs on XCD i % 8).
+// fp32 matrix products (fp32 configs) on gfx950: 64x64x16 tiles, four
+// waves in 2x2, each wave one 32x32 output block on v_mfma_f32_32x32x2_f32
+// (full fp32 products and sums), the same epilogues and the same persistent,
+// XCD-aware tile loop as the bf16 kernels (the tile list is cut into eight
+// contiguous chunks, one per XCD, since workgroup i runs on XCD i % 8).
 //
 // The bf16 products live in gemm_big.hip (prefill) and gemm_skinny.hip
 // (single-token steps, router logits).
@@ -9,15 +10,17 @@
 
 namespace {
 
-// ------------------------------------------------------------ fp32 FMA
+// ------------------------------------------------------------ fp32 MFMA
 
 template <bool DUAL, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   RDT_SKIP_IF_ALL_HALTED(p.live);
   constexpr int BM = 64, BN = 64, BK = 16, NB = DUAL ? 2 : 1;
-  __shared__ float sA[BK][BM + 4];
-  __shared__ float sB[NB][BK][BN + 4];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  // rows of a k are 96 floats apart, so the two 32-lane halves of a
+  // fragment read (k and k + 1) fall in different banks
+  __shared__ float sA[BK][BM + 32];
+  __shared__ float sB[NB][BK][BN + 32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int ntn = (p.N + BN - 1) / BN;
   const int n_mt = p.mt_start ? p.mt_start[p.n_groups] : (p.M + BM - 1) / BM;
   const int total = n_mt * ntn;
@@ -45,13 +48,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     const bool bok = n0 + lr < p.N;
     const int bn = bok ? n0 + lr : 0;
 
-    float acc[NB][4][4];
+    floatx16_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[b][i][j] = 0.f;
+      for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
 
     for (int k0 = 0; k0 < p.K; k0 += BK) {
       const bool kin = k0 + lk < p.K;
@@ -69,31 +70,29 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
         sB[b][lk + 3][lr] = bv.w;
       }
       __syncthreads();
+      // k pair kk: lane l supplies A[row l % 32][k] and B[k][column l % 32]
+      // for k = 2 kk + l / 32
 #pragma unroll
-      for (int k = 0; k < BK; ++k) {
-        const float4 a4 = *(const float4*)&sA[k][ty * 4];
-        const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+      for (int kk = 0; kk < BK / 2; ++kk) {
+        const int k = 2 * kk + (lane >> 5);
+        const float a = sA[k][wm * 32 + (lane & 31)];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float4 b4 = *(const float4*)&sB[b][k][tx * 4];
-          const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[b][i][j] = fmaf(a[i], bb[j], acc[b][i][j]);
-        }
+        for (int b = 0; b < NB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sB[b][k][wn * 32 + (lane & 31)], acc[b], 0, 0, 0);
       }
       __syncthreads();
     }
+    // lane l, element e: row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 of
+    // the wave's block; the pair partner of a column (n ^ 1, for the RoPE
+    // epilogues) sits in lane l ^ 1
+    const int n = n0 + wn * 32 + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ml = ty * 4 + i, n = n0 + tx * 4 + j;
-        const float v = acc[0][i][j];
-        const float v2 = DUAL ? acc[NB - 1][i][j] : acc[0][i][j ^ 1];
-        if (ml < rows && n < p.N) epi_store<EPI, float>(p.epi, row0 + ml, n, v, v2);
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int ml = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const float v = acc[0][e];
+      const float v2 = DUAL ? acc[NB - 1][e] : __shfl_xor(v, 1, 64);
+      if (ml < rows && n < p.N) epi_store<EPI, float>(p.epi, row0 + ml, n, v, v2);
+    }
   }
 }
 
