@@ -12,6 +12,8 @@
 // holds its scores (slot 8 h + x <-> index 8 (x / 4) + 4 h + x % 4).
 #include "backward.h"
 
+#include <type_traits>
+
 #include <algorithm>
 
 namespace {
@@ -584,7 +586,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     if (i + 1 < ntile) issue(i + 1, bb ^ 1);
     const int q0 = (qt0 + i % nq) * AQ;
     const DkdvBuf& cb = buf[bb];
-    if (kw0 <= q0 + AQ - 1) {   // else every query of the tile precedes this wave's keys
+    // the scores of one query tile against this wave's keys; tiles whose
+    // queries all follow the wave's keys and end before T need no mask
+    auto tile = [&](auto masked) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         floatx16_t S, dP;
@@ -608,7 +612,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int r = 4 * r4 + x, qq = q0 + qbase + r;
-            const bool ok = qq < T && kl <= qq && kl < T;
+            const bool ok = !decltype(masked)::value || (qq < T && kl <= qq && kl < T);
             const float pr = ok ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - Ls[x]) : 0.f;
             p[r] = pr;
             dsv[r] = pr * (dP[r] - Ds[x]);
@@ -626,6 +630,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           }
         }
       }
+    };
+    if (kw0 <= q0 + AQ - 1) {   // else every query of the tile precedes this wave's keys
+      if (kw0 + 31 <= q0 && q0 + AQ <= T) tile(std::false_type{});
+      else tile(std::true_type{});
     }
     __builtin_amdgcn_s_waitcnt(0);
     if (i + 1 < ntile && tid < AQ) {
@@ -679,6 +687,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       df[ds] = as_frag(c);
     }
   }
+  const int qlim = ql < T ? ql : -1;   // last key this lane's query sees (none past T)
   const float Lq = ql < T ? lse2[(int64_t)bh * T + ql] : 0.f;
   const float Dqq = ql < T ? Dq[(int64_t)bh * T + ql] : 0.f;
   floatx16_t acc[4];
@@ -729,7 +738,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb2 * 32 + 16 * half + r;
-          const bool ok = ql < T && key <= ql;
+          const bool ok = key <= qlim;
           const float pr = ok ? __builtin_amdgcn_exp2f(S[r] * scale_log2 - Lq) : 0.f;
           dsv[r] = pr * (dP[r] - Dqq);
         }
