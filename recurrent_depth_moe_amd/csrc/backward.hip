@@ -1488,14 +1488,22 @@ void launch_router_bias_update(float* bias, const int32_t* load, int E, float ga
 }
 
 namespace {
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+// n4 16-byte words from p (16-byte aligned), then n1 4-byte words
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, size_t n4, size_t n1) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) p[i] = uint4{0u, 0u, 0u, 0u};
+  uint32_t* t = (uint32_t*)(p + n4);
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n1; i += stride) t[i] = 0u;
 }
 }  // namespace
 
 void launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  // a 4-byte aligned start that is not 16-byte aligned goes word by word
   const size_t n = bytes / 4;
   if (n == 0) return;
-  const size_t blocks = std::min<size_t>((n + 255) / 256, 4096);
-  fill_zero_kernel<<<(unsigned)blocks, 256, 0, s>>>((uint32_t*)p, n);
+  const bool a16 = ((uintptr_t)p & 15) == 0;
+  const size_t n4 = a16 ? n / 4 : 0, n1 = n - 4 * n4;
+  const size_t work = std::max(n4, n1);
+  const size_t blocks = std::min<size_t>((work + 255) / 256, 2048);
+  fill_zero_kernel<<<(unsigned)blocks, 256, 0, s>>>((uint4*)p, n4, n1);
 }
