@@ -589,18 +589,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     // the scores of one query tile against this wave's keys; tiles whose
     // queries all follow the wave's keys and end before T need no mask
     auto tile = [&](auto masked) {
+      // S and dP of both 32-query blocks first, so the exponentials of the
+      // first block can issue while the second block's products run
+      floatx16_t Sq[2], dPq[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        floatx16_t S, dP;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
+        for (int e = 0; e < 16; ++e) Sq[qb][e] = dPq[qb][e] = 0.f;
         const int qrow = qb * 32 + myrow;
 #pragma unroll
         for (int ds = 0; ds < 8; ++ds) {
           const int pc = (2 * ds + half) ^ rswz(qrow);
-          S = mfma32(as_frag(cb.q[qrow * 16 + pc]), kf[ds], S);
-          dP = mfma32(as_frag(cb.dO[qrow * 16 + pc]), vf[ds], dP);
+          Sq[qb] = mfma32(as_frag(cb.q[qrow * 16 + pc]), kf[ds], Sq[qb]);
+          dPq[qb] = mfma32(as_frag(cb.dO[qrow * 16 + pc]), vf[ds], dPq[qb]);
         }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const floatx16_t& S = Sq[qb];
+        const floatx16_t& dP = dPq[qb];
         // this lane: key kl, queries q0 + 32 qb + 16 half + r
         const int qbase = qb * 32 + 16 * half;
         float p[16], dsv[16];
