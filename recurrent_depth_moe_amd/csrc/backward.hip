@@ -139,9 +139,13 @@ __global__ __launch_bounds__(256, WF == 4 ? 1 : 2) void wgrad_kernel(WgradArgs a
   // L2); grouped products take the tiles of one group after another
   int g, tn, tk;
   {
-    const int bid = blockIdx.x, xcd = bid % RDT_NUM_XCD, j = bid / RDT_NUM_XCD;
+    // the tiles of one group (one expert, or the whole dense matrix) are
+    // dealt to the XCDs (workgroup i runs on XCD i % 8) as px x py blocks of
+    // neighbouring (n, k) tiles, so an XCD's L2 serves each dY / X slab to
+    // several of its tiles
+    const int bid = blockIdx.x, L = bid % nt, xcd = L % RDT_NUM_XCD, j = L / RDT_NUM_XCD;
     int px = 0;
-    if (a.G == 1 && nt % RDT_NUM_XCD == 0) {
+    if (nt % RDT_NUM_XCD == 0) {
       if (tilesN % 4 == 0 && tilesK % 2 == 0) px = 4;
       else if (tilesN % 2 == 0 && tilesK % 4 == 0) px = 2;
       else if (tilesN % 8 == 0) px = 8;
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(256, WF == 4 ? 1 : 2) void wgrad_kernel(WgradArgs a
     }
     if (px) {
       const int py = RDT_NUM_XCD / px, wn_ = tilesN / px, wk_ = tilesK / py;
-      g = 0;
+      g = bid / nt;
       tn = (xcd % px) * wn_ + j % wn_;
       tk = (xcd / px) * wk_ + j / wn_;
     } else {
@@ -283,9 +287,13 @@ __global__ __launch_bounds__(512, 1) void wgrad8_kernel(WgradArgs a) {
   const int tilesN = (a.Nc + TILE - 1) / TILE, tilesK = (a.Kc + TILE - 1) / TILE, nt = tilesN * tilesK;
   int g, tn, tk;
   {
-    const int bid = blockIdx.x, xcd = bid % RDT_NUM_XCD, j = bid / RDT_NUM_XCD;
+    // the tiles of one group (one expert, or the whole dense matrix) are
+    // dealt to the XCDs (workgroup i runs on XCD i % 8) as px x py blocks of
+    // neighbouring (n, k) tiles, so an XCD's L2 serves each dY / X slab to
+    // several of its tiles
+    const int bid = blockIdx.x, L = bid % nt, xcd = L % RDT_NUM_XCD, j = L / RDT_NUM_XCD;
     int px = 0;
-    if (a.G == 1 && nt % RDT_NUM_XCD == 0) {
+    if (nt % RDT_NUM_XCD == 0) {
       if (tilesN % 4 == 0 && tilesK % 2 == 0) px = 4;
       else if (tilesN % 2 == 0 && tilesK % 4 == 0) px = 2;
       else if (tilesN % 8 == 0) px = 8;
@@ -293,7 +301,7 @@ __global__ __launch_bounds__(512, 1) void wgrad8_kernel(WgradArgs a) {
     }
     if (px) {
       const int py = RDT_NUM_XCD / px, wn_ = tilesN / px, wk_ = tilesK / py;
-      g = 0;
+      g = bid / nt;
       tn = (xcd % px) * wn_ + j % wn_;
       tk = (xcd / px) * wk_ + j / wn_;
     } else {
