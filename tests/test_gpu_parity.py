@@ -81,6 +81,16 @@ def test_end_to_end_large_terms(name):
         assert len(np.unique(g["halt"])) > 1
 
 
+def test_end_to_end_f32_products_with_ragged_k():
+    """fp32 products on the MFMA tile kernel with an expert width of 100:
+    the routed and shared down products reduce over K = 100 (the last
+    16-deep k stage is a quarter full) and the gate | up outputs end inside
+    a 64-column tile; 300 rows end inside a 64-row tile."""
+    cfg, W, e, h0 = _inputs("small_f32", expert_dim=100)
+    assert cfg["expert_dim"] % 16 != 0
+    _e2e(cfg, W, e, h0)
+
+
 def test_end_to_end_groups_split_over_xcds():
     """batch 4 x 2 kv heads = 8 (batch, kv head) groups: flash attention
     gives each XCD its own group (the ordering the large prefill takes),
