@@ -144,6 +144,24 @@ def test_backward_matches_gradient_oracle(name, scales, over):
         assert np.all(g["grads"]["router_w"] == 0)
 
 
+def test_backward_deterministic_bitwise():
+    """Two training steps' backward passes on the same inputs (fresh handles,
+    so the grouped products claim their tiles in whatever order the blocks
+    arrive) give bitwise equal gradients, e / h0 gradients and expert loads:
+    every sum runs in a fixed order, with no floating-point atomics."""
+    cfg = configs.get("small_bf16")
+    W = generate.make_weights(cfg)
+    e, h0 = generate.make_inputs(cfg)
+    a = _run(cfg, W, e, h0)
+    b = _run(cfg, W, e, h0)
+    for name in a["grads"]:
+        assert np.array_equal(a["grads"][name].view(np.uint32), b["grads"][name].view(np.uint32)), name
+    for key in ("de", "dh0", "out"):
+        assert np.array_equal(a[key].view(np.uint32), b[key].view(np.uint32)), key
+    np.testing.assert_array_equal(a["load"], b["load"])
+    np.testing.assert_array_equal(a["halt"], b["halt"])
+
+
 def test_router_bias_balancing_step():
     """After a backward pass, the handle's router bias moves by gamma
     towards balance (rule in oracle/rdt_backward.py), bit for bit."""
